@@ -1,0 +1,187 @@
+/*
+ * fp64 CPU oracle for the multi-LoRA batched layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no code with the HIP library.
+ *
+ * What it computes (plain definitions, written out):
+ *
+ *   LoRA layer, row-vector convention of "Serving multiple LoRAs: segmented
+ *   matrix multiplies and adapter scheduling", section "Not merging the
+ *   weights, computing in batches":  y = x W + s * (x A) B  with
+ *   W [d_in, d_out], A [d_in, r], B [r, d_out], applied per request with that
+ *   request's own adapter (the page's per-request loop).  A request of several
+ *   tokens is several rows with one adapter id; rows of a matrix product are
+ *   independent, so the loop below runs per row.
+ *
+ *   Base-only rows (adapter id -1, "Serving many LoRA adapters",
+ *   blog.ecitis.org, section "Replay": "req C -> base only") get y = x W.
+ *   Ids outside [-1, n_adapters) are counted as errors and treated as
+ *   base-only.
+ *
+ *   The scale s is a per-adapter value that travels with the adapter
+ *   (blog.ecitis.org, section "Correctness across tenants"); it multiplies
+ *   the expanded term once.  The shrink output t = x A is returned unscaled.
+ *
+ *   Segments: the stable group-by of the same page section (stable argsort of
+ *   the per-token adapter ids, then runs of equal ids).  Rows whose id is -1
+ *   (or invalid) form the first run, with id -1.
+ *
+ * Every sum runs in fp64 over k = 0, 1, ... in order.  Inputs are the exact
+ * values the GPU sees, widened to fp64 by the caller.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int id_valid(int32_t a, int32_t n_adapters) { return a >= 0 && a < n_adapters; }
+
+/* Number of rows whose id lies outside [-1, n_adapters). */
+int64_t oracle_count_bad_ids(const int32_t* ids, int64_t n_rows, int32_t n_adapters)
+{
+    int64_t bad = 0;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (ids[i] < -1 || ids[i] >= n_adapters) ++bad;
+    return bad;
+}
+
+/*
+ * Stable group-by of adapter ids.
+ *   perm[n_rows]       : rows in ascending id order, original order inside a run
+ *   seg_ids[n_seg]     : id of each run (-1 first when present)
+ *   seg_off[n_seg + 1] : run boundaries into perm
+ * Returns the number of invalid ids (those rows are grouped with -1).
+ * Definition used: for every id value v = -1, 0, 1, ... in ascending order,
+ * append the rows carrying v in their original order.
+ */
+int64_t oracle_segments(const int32_t* ids, int64_t n_rows, int32_t n_adapters,
+                        int32_t* perm, int32_t* seg_ids, int32_t* seg_off, int32_t* n_seg)
+{
+    int64_t pos = 0;
+    int32_t s = 0;
+    for (int32_t v = -1; v < n_adapters; ++v) {
+        int64_t start = pos;
+        for (int64_t i = 0; i < n_rows; ++i) {
+            int32_t key = id_valid(ids[i], n_adapters) ? ids[i] : -1;
+            if (key == v) perm[pos++] = (int32_t)i;
+        }
+        if (pos > start) {
+            seg_ids[s] = v;
+            seg_off[s] = (int32_t)start;
+            ++s;
+        }
+    }
+    seg_off[s] = (int32_t)pos;
+    *n_seg = s;
+    return oracle_count_bad_ids(ids, n_rows, n_adapters);
+}
+
+/*
+ * The layer, one row at a time.
+ *
+ *   x      [n_rows, d_in]                  row-major
+ *   W      [d_in, d_out]                   row-major; may be NULL (no base term)
+ *   ids    [n_rows]
+ *   A, B   flat pools; adapter u is A[a_off[u] + k*ranks[u] + j]  (k < d_in, j < r_u)
+ *                                  and B[b_off[u] + j*d_out + c]   (j < r_u, c < d_out)
+ *   scales [n_adapters]
+ *
+ * Outputs (each may be NULL):
+ *   t    [n_rows, r_max]   t[i][j] = sum_k x[i][k] A_a[k][j]   (0 past r_a and on base-only rows)
+ *   lora [n_rows, d_out]   s_a * sum_j t[i][j] B_a[j][c]        (0 on base-only rows)
+ *   y    [n_rows, d_out]   sum_k x[i][k] W[k][c] + lora[i][c]
+ *
+ * ``rows`` (may be NULL) lists the rows to compute; the others are left
+ * untouched.  ``n_threads`` <= 0 keeps the OpenMP default.
+ * Returns the number of invalid ids among the computed rows.
+ */
+int64_t oracle_layer(int64_t n_rows, int64_t d_in, int64_t d_out,
+                     const double* x, const double* W,
+                     const int32_t* ids, int32_t n_adapters,
+                     const int32_t* ranks, const int64_t* a_off, const int64_t* b_off,
+                     const double* A, const double* B, const double* scales,
+                     int32_t r_max,
+                     const int64_t* rows, int64_t n_sel,
+                     double* t, double* lora, double* y, int n_threads)
+{
+    int64_t count = rows ? n_sel : n_rows;
+    int64_t bad = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+#pragma omp parallel reduction(+ : bad)
+    {
+        double* ti = (double*)malloc(sizeof(double) * (size_t)(r_max > 0 ? r_max : 1));
+        double* li = (double*)malloc(sizeof(double) * (size_t)d_out);
+        double* bi = (double*)malloc(sizeof(double) * (size_t)d_out);
+
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < count; ++q) {
+            int64_t i = rows ? rows[q] : q;
+            const double* xi = x + i * d_in;
+            int32_t a = ids[i];
+            int valid = id_valid(a, n_adapters);
+            if (a != -1 && !valid) ++bad;
+
+            /* shrink: t_i = x_i A_a */
+            for (int32_t j = 0; j < r_max; ++j) ti[j] = 0.0;
+            int32_t r = valid ? ranks[a] : 0;
+            for (int32_t j = 0; j < r; ++j) {
+                const double* Aa = A + a_off[a];
+                double acc = 0.0;
+                for (int64_t k = 0; k < d_in; ++k) acc += xi[k] * Aa[k * r + j];
+                ti[j] = acc;
+            }
+
+            /* expand: lora_i = s_a * (t_i B_a) */
+            for (int64_t c = 0; c < d_out; ++c) li[c] = 0.0;
+            if (valid) {
+                const double* Ba = B + b_off[a];
+                double s = scales[a];
+                for (int64_t c = 0; c < d_out; ++c) {
+                    double acc = 0.0;
+                    for (int32_t j = 0; j < r; ++j) acc += ti[j] * Ba[(int64_t)j * d_out + c];
+                    li[c] = s * acc;
+                }
+            }
+
+            /* base: x_i W, summed over k in order for every column */
+            if (y) {
+                for (int64_t c = 0; c < d_out; ++c) bi[c] = 0.0;
+                if (W) {
+                    for (int64_t k = 0; k < d_in; ++k) {
+                        double xk = xi[k];
+                        const double* Wk = W + k * d_out;
+                        for (int64_t c = 0; c < d_out; ++c) bi[c] += xk * Wk[c];
+                    }
+                }
+                for (int64_t c = 0; c < d_out; ++c) y[i * d_out + c] = bi[c] + li[c];
+            }
+            if (t)
+                for (int32_t j = 0; j < r_max; ++j) t[i * r_max + j] = ti[j];
+            if (lora)
+                for (int64_t c = 0; c < d_out; ++c) lora[i * d_out + c] = li[c];
+        }
+        free(ti);
+        free(li);
+        free(bi);
+    }
+    return bad;
+}
+
+/* Threads an OpenMP parallel region would use (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
