@@ -1,0 +1,237 @@
+/*
+ * lora_mi355x.h -- C ABI of the multi-LoRA batched layer for MI355X (gfx950).
+ *
+ * The layer, for a heterogeneous batch in which every row i carries an
+ * adapter id a_i (or -1 for a base-only row):
+ *
+ *     y_i = x_i W + s_{a_i} * (x_i A[a_i]) B[a_i]
+ *
+ * Row-vector convention with W [d_in, d_out], A [d_in, r], B [r, d_out]:
+ * "Serving multiple LoRAs: segmented matrix multiplies and adapter
+ * scheduling", section "Not merging the weights, computing in batches".
+ * The base product x W is computed once for the whole batch ("Multi-LoRA
+ * batching and adapter paging", section "Walking through a batch"); the
+ * low-rank term is a shrink (x -> xA, rank r) followed by an expand
+ * ((xA) -> (xA)B) that is added to the base output (same page 3 section).
+ * BGMV gathers each row's adapter by index (decode); SGMV groups rows by
+ * adapter and runs one small product per segment (prefill) (same section;
+ * also "Serving Many LoRA Adapters" (praveentn.live), section "Punica: The
+ * Segmented Gather-Scatter Kernel").
+ *
+ * Conventions shared by every entry point
+ *  - All tensors are caller-owned DEVICE memory unless marked "host".
+ *    The library never frees them.  Row-major; ld* are leading dimensions
+ *    in elements.
+ *  - Element types: x, W, A and B share one dtype (LORA_F32 or LORA_BF16);
+ *    the rank-r intermediate t is always fp32; y may be fp32 or bf16.
+ *    Products accumulate in fp32 and y is rounded once (nearest even).
+ *  - Pointers handed to the library must be 16-byte aligned, and so must
+ *    ld* times the element size; otherwise LORA_E_UNSUPPORTED.
+ *  - Every call that takes a stream only enqueues work on it and returns;
+ *    argument errors are reported synchronously, before any launch, and
+ *    nothing is enqueued then.  Nothing throws or aborts.  n_rows = 0 is a
+ *    valid no-op.
+ *  - Hot calls never allocate.  Scratch memory is a caller-provided
+ *    workspace sized by the matching *_workspace query.  A workspace must
+ *    be zero-filled once before its first use (lora_workspace_clear does
+ *    it); every call leaves it in that state again.  Calls that overlap in
+ *    time must not share a workspace.
+ *  - Ids outside [-1, n_adapters) are treated as base-only rows and set
+ *    bit 0 of the pool's device error word (see lora_pool_last_error).
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LORA_OK = 0,
+    LORA_E_INVALID = 1,     /* bad argument: null pointer, size, rank, id table */
+    LORA_E_UNSUPPORTED = 2, /* valid but not handled: alignment, rank > 64, ... */
+    LORA_E_WORKSPACE = 3,   /* workspace missing or too small */
+    LORA_E_ID_RANGE = 4,    /* reported by lora_pool_last_error only */
+    LORA_E_DEVICE = 5       /* a HIP runtime call failed */
+} lora_status_t;
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype_t;
+
+/* Pool layouts ("Serving many LoRA adapters" (blog.ecitis.org), section
+ * "Batching across different adapters": a uniform-rank pool is a dense 3-D
+ * tensor; mixed ranks need ragged indexing or padding to the maximum). */
+typedef enum { LORA_LAYOUT_UNIFORM = 0, LORA_LAYOUT_RAGGED = 1 } lora_layout_t;
+
+/* How lora_layer_apply computes the low-rank term. */
+typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode_t;
+
+/* Storage of the base weight.  LORA_W_IN_OUT: W as [d_in, d_out] (the
+ * page-3 convention y = xW).  LORA_W_OUT_IN: W stored transposed, [d_out,
+ * d_in] (the x W^T convention of "Serving Many LoRA Adapters"
+ * (praveentn.live), section "Why Naive Batching Breaks"). */
+typedef enum { LORA_W_IN_OUT = 0, LORA_W_OUT_IN = 1 } lora_w_layout_t;
+
+typedef struct lora_pool_s* lora_pool_t;
+
+/* Segment descriptor written by lora_segments_build (all device, caller-owned):
+ *   perm[n_rows]      rows in ascending adapter-id order, original order
+ *                     inside a run (a stable argsort of the ids);
+ *   seg_ids[cap]      id of each run; the run of base-only rows (id -1, and
+ *                     invalid ids) comes first when present;
+ *   seg_off[cap + 1]  run boundaries into perm; seg_off[n_seg] = n_rows;
+ *   n_seg[1]          number of runs.
+ *   cap               capacity of seg_ids, >= min(n_rows, n_adapters + 1).
+ * The group-by is the stable argsort + run detection of "Serving multiple
+ * LoRAs...", section "Not merging the weights, computing in batches". */
+typedef struct {
+    int32_t* perm;
+    int32_t* seg_ids;
+    int32_t* seg_off;
+    int32_t* n_seg;
+    int32_t cap;
+} lora_segments_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* lora_status_string(lora_status_t status);
+
+/* Parameters of one adapter of rank r on a d_in -> d_out projection:
+ * r * (d_in + d_out) ("Serving many LoRA adapters" (blog.ecitis.org),
+ * section "Low-rank structure and additivity": 131,072 at 4096/4096/16).
+ * Returns -1 for non-positive arguments.  Host only. */
+int64_t lora_adapter_param_count(int32_t rank, int32_t d_in, int32_t d_out);
+
+/* Element offsets for a ragged pool (host only, no device work).
+ * ranks[n_adapters] (host) in [1, 64].  Writes a_off/b_off[n_adapters] (host)
+ * and the total element counts of the A and B buffers.  Adapter u occupies
+ * A[a_off[u] .. a_off[u] + d_in*ranks[u]) as row-major [d_in, r_u] and
+ * B[b_off[u] .. + r_u*d_out) as row-major [r_u, d_out]; every block starts
+ * on a 256-byte boundary for either dtype. */
+lora_status_t lora_pool_ragged_offsets(int32_t n_adapters, const int32_t* ranks,
+                                       int32_t d_in, int32_t d_out,
+                                       int64_t* a_off, int64_t* b_off,
+                                       int64_t* a_total, int64_t* b_total);
+
+/* Describe a packed adapter pool over caller-owned device buffers A and B
+ * (which must outlive the pool).
+ *   UNIFORM: A is [n_adapters, d_in, r_max], B is [n_adapters, r_max, d_out];
+ *            ranks/a_off/b_off must be NULL.  Padding lower ranks to r_max
+ *            with zeros is this layout too.
+ *   RAGGED:  ranks/a_off/b_off (host, n_adapters each) give every adapter's
+ *            rank (1..r_max) and element offsets; blocks must not overlap and
+ *            must start 16-byte aligned.
+ * scales (host, n_adapters) is each adapter's s = alpha/r, which travels
+ * with the adapter ("Serving many LoRA adapters" (blog.ecitis.org), section
+ * "Correctness across tenants").  1 <= r_max <= 64.
+ * Allocates small device tables (ranks, offsets, scales, error word) and
+ * copies them synchronously on the null stream; the pool is immutable
+ * afterwards and may be used from several streams at once. */
+lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtype_t dtype,
+                               int32_t n_adapters, int32_t d_in, int32_t d_out, int32_t r_max,
+                               const int32_t* ranks, const int64_t* a_off, const int64_t* b_off,
+                               const void* A, const void* B, const float* scales);
+
+/* Free the pool's device tables (waits for the device first). NULL is a no-op. */
+lora_status_t lora_pool_destroy(lora_pool_t pool);
+
+/* r_u * (d_in + d_out) for adapter u of the pool, or -1 if u is out of range. */
+int64_t lora_pool_param_count(lora_pool_t pool, int32_t adapter);
+
+/* Synchronize `stream`, then read and clear the pool's device error word
+ * into *out (bit 0: some call saw an id outside [-1, n_adapters)).
+ * Returns LORA_E_ID_RANGE when bit 0 was set, LORA_OK otherwise. */
+lora_status_t lora_pool_last_error(lora_pool_t pool, hipStream_t stream, int32_t* out);
+
+/* Zero-fill a workspace on `stream` with a fill kernel (safe under graph
+ * capture, unlike a memset node). */
+lora_status_t lora_workspace_clear(void* ws, size_t bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Segments                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Workspace bytes for lora_segments_build (0 when none is needed). */
+lora_status_t lora_segments_workspace(int32_t n_rows, int32_t n_adapters, size_t* bytes);
+
+/* Stable group-by of ids[n_rows] (device) into *seg (one launch, integer
+ * only, bit-exact).  n_adapters <= 16383.  `status` (device, may be NULL)
+ * gets bit 0 set when an id is outside [-1, n_adapters). */
+lora_status_t lora_segments_build(const int32_t* ids, int32_t n_rows, int32_t n_adapters,
+                                  const lora_segments_t* seg, int32_t* status,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* BGMV: per-row gather of the row's adapter (decode)                     */
+/* ---------------------------------------------------------------------- */
+
+/* Workspace bytes for lora_bgmv_shrink at this batch size. */
+lora_status_t lora_bgmv_shrink_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes);
+
+/* Shrink: t[i, 0:r_max] = x_i A[a_i] (fp32, unscaled), one launch for the
+ * whole batch.  Columns [r_{a_i}, r_max) and base-only rows are written 0.
+ *   x [n_rows, ldx] (pool dtype), ids [n_rows], t [n_rows, ldt] fp32,
+ *   ldt >= r_max. */
+lora_status_t lora_bgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
+                               const int32_t* ids, int32_t n_rows,
+                               float* t, int64_t ldt,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expand: y_i (+)= s_{a_i} * t_i B[a_i], one launch for the whole batch.
+ * accumulate = 0: y_i is overwritten with the LoRA term (0 on base-only
+ * rows).  accumulate = 1: the term is added to y_i; base-only rows are not
+ * touched.  y [n_rows, ldy] of y_dtype. */
+lora_status_t lora_bgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
+                               const int32_t* ids, int32_t n_rows,
+                               void* y, lora_dtype_t y_dtype, int64_t ldy, int accumulate,
+                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* SGMV: rows grouped by adapter, one small product per segment (prefill) */
+/* ---------------------------------------------------------------------- */
+
+/* Shrink over segments from lora_segments_build (same t layout and values
+ * as lora_bgmv_shrink: original row order).  Rows of the base-only run get
+ * t = 0.  Id-range errors are reported by lora_segments_build's `status`.
+ * The grid is sized from n_rows and the pool size, so the segment count
+ * never has to come back to the host. */
+lora_status_t lora_sgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
+                               const lora_segments_t* seg, int32_t n_rows,
+                               float* t, int64_t ldt, hipStream_t stream);
+
+/* Expand over segments (same semantics as lora_bgmv_expand). */
+lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
+                               const lora_segments_t* seg, int32_t n_rows,
+                               void* y, lora_dtype_t y_dtype, int64_t ldy, int accumulate,
+                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* The fused layer                                                         */
+/* ---------------------------------------------------------------------- */
+
+/* Workspace bytes for lora_layer_apply. */
+lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t mode,
+                                   size_t* bytes);
+
+/* y = x W + s * (x A[ids]) B[ids] for the whole batch: the shrink runs in
+ * one launch (BGMV or SGMV), then one MFMA GEMM launch computes x W for all
+ * rows and adds the scaled expand in its epilogue before the single
+ * rounding of y ("Serving many LoRA adapters" (blog.ecitis.org), section
+ * "Replay": segmented gather, grouped GEMM, scatter-add, fused output).
+ *   x [n_rows, ldx]; W per w_layout with leading dimension ldw; y [n_rows,
+ *   ldy] of y_dtype.  `seg` may be NULL (SGMV builds segments in the
+ *   workspace) or a descriptor already built for these ids.
+ *   mode AUTO picks BGMV for short batches and SGMV otherwise. */
+lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx,
+                               const void* W, int64_t ldw, lora_w_layout_t w_layout,
+                               const int32_t* ids, const lora_segments_t* seg, int32_t n_rows,
+                               void* y, lora_dtype_t y_dtype, int64_t ldy,
+                               lora_mode_t mode, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

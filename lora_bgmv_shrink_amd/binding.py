@@ -1,0 +1,343 @@
+"""Thin ctypes binding over liblora_mi355x.so.
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels.  PyTorch supplies device memory (tensor ``data_ptr()``) and the
+current stream.  Output tensors and zero-filled workspaces are allocated
+here with torch when the caller does not pass them.
+
+The functions carry the C names (see include/lora_mi355x.h for the
+semantics, layouts and error behaviour of each).  A non-OK status raises
+``LoraError``.  Importing this module without the built library raises
+``ImportError``; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch  # loads the HIP runtime the library binds to
+
+from .build import LIB_PATH
+
+LORA_OK, LORA_E_INVALID, LORA_E_UNSUPPORTED, LORA_E_WORKSPACE, LORA_E_ID_RANGE, LORA_E_DEVICE = range(6)
+LORA_F32, LORA_BF16 = 0, 1
+LORA_LAYOUT_UNIFORM, LORA_LAYOUT_RAGGED = 0, 1
+LORA_MODE_AUTO, LORA_MODE_BGMV, LORA_MODE_SGMV = 0, 1, 2
+LORA_W_IN_OUT, LORA_W_OUT_IN = 0, 1
+
+# Every symbol the C header declares.
+EXPORTS = [
+    "lora_status_string", "lora_adapter_param_count", "lora_pool_ragged_offsets", "lora_pool_create",
+    "lora_pool_destroy", "lora_pool_param_count", "lora_pool_last_error", "lora_workspace_clear",
+    "lora_segments_workspace", "lora_segments_build", "lora_bgmv_shrink_workspace", "lora_bgmv_shrink",
+    "lora_bgmv_expand", "lora_sgmv_shrink", "lora_sgmv_expand", "lora_layer_workspace",
+    "lora_layer_apply",
+]
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.lora_status_string(status).decode()}")
+
+
+class SegmentsT(ctypes.Structure):
+    _fields_ = [("perm", ctypes.c_void_p), ("seg_ids", ctypes.c_void_p), ("seg_off", ctypes.c_void_p),
+                ("n_seg", ctypes.c_void_p), ("cap", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m lora_bgmv_shrink_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "lora_status_string": (ctypes.c_char_p, [st]),
+        "lora_adapter_param_count": (i64, [i32, i32, i32]),
+        "lora_pool_ragged_offsets": (st, [i32, p, i32, i32, p, p, p, p]),
+        "lora_pool_create": (st, [p, st, st, i32, i32, i32, i32, p, p, p, p, p, p]),
+        "lora_pool_destroy": (st, [p]),
+        "lora_pool_param_count": (i64, [p, i32]),
+        "lora_pool_last_error": (st, [p, p, p]),
+        "lora_workspace_clear": (st, [p, sz, p]),
+        "lora_segments_workspace": (st, [i32, i32, p]),
+        "lora_segments_build": (st, [p, i32, i32, p, p, p, sz, p]),
+        "lora_bgmv_shrink_workspace": (st, [p, i32, p]),
+        "lora_bgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p, sz, p]),
+        "lora_bgmv_expand": (st, [p, p, i64, p, i32, p, st, i64, ctypes.c_int, p]),
+        "lora_sgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p]),
+        "lora_sgmv_expand": (st, [p, p, i64, p, i32, p, st, i64, ctypes.c_int, p]),
+        "lora_layer_workspace": (st, [p, i32, st, p]),
+        "lora_layer_apply": (st, [p, p, i64, p, i64, st, p, p, i32, p, st, i64, st, p, sz, p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ctypes library (for symbol checks)."""
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != LORA_OK:
+        raise LoraError(status, where)
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return LORA_BF16
+    if t == torch.float32:
+        return LORA_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t: torch.Tensor) -> int:
+    assert t.dim() == 2 and t.stride(1) == 1, "expected a row-major 2-D tensor"
+    return t.stride(0)
+
+
+# --------------------------------------------------------------------------
+# Pools
+# --------------------------------------------------------------------------
+
+@dataclass
+class Pool:
+    handle: ctypes.c_void_p
+    dtype: torch.dtype
+    n_adapters: int
+    d_in: int
+    d_out: int
+    r_max: int
+    A: torch.Tensor
+    B: torch.Tensor
+
+    def destroy(self):
+        if self.handle:
+            _check(_lib.lora_pool_destroy(self.handle), "lora_pool_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def lora_adapter_param_count(rank: int, d_in: int, d_out: int) -> int:
+    return int(_lib.lora_adapter_param_count(rank, d_in, d_out))
+
+
+def lora_pool_ragged_offsets(ranks, d_in: int, d_out: int):
+    ranks = np.ascontiguousarray(ranks, np.int32)
+    n = ranks.shape[0]
+    a_off = np.zeros(n, np.int64)
+    b_off = np.zeros(n, np.int64)
+    ta = ctypes.c_int64()
+    tb = ctypes.c_int64()
+    _check(_lib.lora_pool_ragged_offsets(n, ranks.ctypes.data, d_in, d_out, a_off.ctypes.data,
+                                         b_off.ctypes.data, ctypes.byref(ta), ctypes.byref(tb)),
+           "lora_pool_ragged_offsets")
+    return a_off, b_off, ta.value, tb.value
+
+
+def lora_pool_create(layout: int, A: torch.Tensor, B: torch.Tensor, n_adapters: int, d_in: int,
+                     d_out: int, r_max: int, scales, ranks=None, a_off=None, b_off=None) -> Pool:
+    assert A.is_cuda and B.is_cuda and A.dtype == B.dtype and A.is_contiguous() and B.is_contiguous()
+    sc = np.ascontiguousarray(np.broadcast_to(np.asarray(scales, np.float32), (n_adapters,)))
+    h = ctypes.c_void_p()
+    args_r = [None, None, None]
+    keep = []
+    if layout == LORA_LAYOUT_RAGGED:
+        for k, arr, dt in ((0, ranks, np.int32), (1, a_off, np.int64), (2, b_off, np.int64)):
+            a = np.ascontiguousarray(arr, dt)
+            keep.append(a)
+            args_r[k] = a.ctypes.data
+    with torch.cuda.device(A.device):
+        _check(_lib.lora_pool_create(ctypes.byref(h), layout, _dt(A.dtype), n_adapters, d_in, d_out, r_max,
+                                     args_r[0], args_r[1], args_r[2], _ptr(A), _ptr(B), sc.ctypes.data),
+               "lora_pool_create")
+    return Pool(h, A.dtype, n_adapters, d_in, d_out, r_max, A, B)
+
+
+def lora_pool_destroy(pool: Pool):
+    pool.destroy()
+
+
+def lora_pool_param_count(pool: Pool, adapter: int) -> int:
+    return int(_lib.lora_pool_param_count(pool.handle, adapter))
+
+
+def lora_pool_last_error(pool: Pool) -> int:
+    """Synchronize the current stream and return (and clear) the device error word."""
+    v = ctypes.c_int32()
+    st = _lib.lora_pool_last_error(pool.handle, ctypes.c_void_p(_stream(pool.A.device)), ctypes.byref(v))
+    if st not in (LORA_OK, LORA_E_ID_RANGE):
+        _check(st, "lora_pool_last_error")
+    return int(v.value)
+
+
+def lora_workspace_clear(ws: torch.Tensor):
+    _check(_lib.lora_workspace_clear(_ptr(ws), ws.numel() * ws.element_size(),
+                                     ctypes.c_void_p(_stream(ws.device))), "lora_workspace_clear")
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------
+# Segments
+# --------------------------------------------------------------------------
+
+@dataclass
+class Segments:
+    perm: torch.Tensor
+    seg_ids: torch.Tensor
+    seg_off: torch.Tensor
+    n_seg: torch.Tensor
+    cap: int
+
+    def c_struct(self) -> SegmentsT:
+        return SegmentsT(self.perm.data_ptr(), self.seg_ids.data_ptr(), self.seg_off.data_ptr(),
+                         self.n_seg.data_ptr(), self.cap)
+
+    def host(self):
+        """(perm, seg_ids, seg_off) as numpy, trimmed to n_seg (synchronizes)."""
+        k = int(self.n_seg.item())
+        return (self.perm.cpu().numpy(), self.seg_ids[:k].cpu().numpy(), self.seg_off[:k + 1].cpu().numpy())
+
+
+def segments_alloc(n_rows: int, n_adapters: int, device) -> Segments:
+    cap = max(1, min(n_rows, n_adapters + 1))
+    z = lambda n: torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+    return Segments(z(n_rows), z(cap), z(cap + 1), z(1), cap)
+
+
+def lora_segments_build(ids: torch.Tensor, n_adapters: int, seg: Optional[Segments] = None,
+                        status: Optional[torch.Tensor] = None) -> Segments:
+    assert ids.is_cuda and ids.dtype == torch.int32 and ids.is_contiguous()
+    n = ids.numel()
+    seg = seg or segments_alloc(n, n_adapters, ids.device)
+    ws_b = ctypes.c_size_t()
+    _check(_lib.lora_segments_workspace(n, n_adapters, ctypes.byref(ws_b)), "lora_segments_workspace")
+    ws = _workspace(ws_b.value, ids.device)
+    cs = seg.c_struct()
+    _check(_lib.lora_segments_build(_ptr(ids), n, n_adapters, ctypes.byref(cs), _ptr(status), _ptr(ws),
+                                    ws_b.value, ctypes.c_void_p(_stream(ids.device))),
+           "lora_segments_build")
+    return seg
+
+
+# --------------------------------------------------------------------------
+# BGMV / SGMV
+# --------------------------------------------------------------------------
+
+def _t_out(pool: Pool, n: int, t: Optional[torch.Tensor], device) -> torch.Tensor:
+    if t is None:
+        t = torch.empty((n, pool.r_max), dtype=torch.float32, device=device)
+    assert t.dtype == torch.float32 and t.shape[0] == n
+    return t
+
+
+def lora_bgmv_shrink_workspace(pool: Pool, n_rows: int) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.lora_bgmv_shrink_workspace(pool.handle, n_rows, ctypes.byref(b)), "lora_bgmv_shrink_workspace")
+    return b.value
+
+
+def lora_bgmv_shrink(pool: Pool, x: torch.Tensor, ids: torch.Tensor, t: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    n = ids.numel()
+    t = _t_out(pool, n, t, x.device)
+    need = lora_bgmv_shrink_workspace(pool, n)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    _check(_lib.lora_bgmv_shrink(pool.handle, _ptr(x), _ld(x), _ptr(ids), n, _ptr(t), _ld(t), _ptr(ws),
+                                 0 if ws is None else ws.numel(), ctypes.c_void_p(_stream(x.device))),
+           "lora_bgmv_shrink")
+    return t
+
+
+def _y_out(pool, n, y, y_dtype, device, accumulate):
+    if y is None:
+        assert not accumulate, "accumulate needs an existing y"
+        y = torch.empty((n, pool.d_out), dtype=y_dtype or pool.dtype, device=device)
+    return y
+
+
+def lora_bgmv_expand(pool: Pool, t: torch.Tensor, ids: torch.Tensor, y: Optional[torch.Tensor] = None,
+                     y_dtype: Optional[torch.dtype] = None, accumulate: bool = False) -> torch.Tensor:
+    n = ids.numel()
+    y = _y_out(pool, n, y, y_dtype, t.device, accumulate)
+    _check(_lib.lora_bgmv_expand(pool.handle, _ptr(t), _ld(t), _ptr(ids), n, _ptr(y), _dt(y.dtype), _ld(y),
+                                 int(bool(accumulate)), ctypes.c_void_p(_stream(t.device))),
+           "lora_bgmv_expand")
+    return y
+
+
+def lora_sgmv_shrink(pool: Pool, x: torch.Tensor, seg: Segments, t: Optional[torch.Tensor] = None) -> torch.Tensor:
+    n = x.shape[0]
+    t = _t_out(pool, n, t, x.device)
+    cs = seg.c_struct()
+    _check(_lib.lora_sgmv_shrink(pool.handle, _ptr(x), _ld(x), ctypes.byref(cs), n, _ptr(t), _ld(t),
+                                 ctypes.c_void_p(_stream(x.device))), "lora_sgmv_shrink")
+    return t
+
+
+def lora_sgmv_expand(pool: Pool, t: torch.Tensor, seg: Segments, y: Optional[torch.Tensor] = None,
+                     y_dtype: Optional[torch.dtype] = None, accumulate: bool = False) -> torch.Tensor:
+    n = t.shape[0]
+    y = _y_out(pool, n, y, y_dtype, t.device, accumulate)
+    cs = seg.c_struct()
+    _check(_lib.lora_sgmv_expand(pool.handle, _ptr(t), _ld(t), ctypes.byref(cs), n, _ptr(y), _dt(y.dtype),
+                                 _ld(y), int(bool(accumulate)), ctypes.c_void_p(_stream(t.device))),
+           "lora_sgmv_expand")
+    return y
+
+
+# --------------------------------------------------------------------------
+# Layer
+# --------------------------------------------------------------------------
+
+def lora_layer_workspace(pool: Pool, n_rows: int, mode: int = LORA_MODE_AUTO) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.lora_layer_workspace(pool.handle, n_rows, mode, ctypes.byref(b)), "lora_layer_workspace")
+    return b.value
+
+
+def lora_layer_apply(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
+                     w_layout: int = LORA_W_IN_OUT, seg: Optional[Segments] = None,
+                     y: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None,
+                     mode: int = LORA_MODE_AUTO, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    n = ids.numel()
+    y = _y_out(pool, n, y, y_dtype, x.device, False)
+    need = lora_layer_workspace(pool, n, mode)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    cs = None if seg is None else seg.c_struct()
+    _check(_lib.lora_layer_apply(pool.handle, _ptr(x), _ld(x), _ptr(W), _ld(W), w_layout, _ptr(ids),
+                                 None if cs is None else ctypes.byref(cs), n, _ptr(y), _dt(y.dtype), _ld(y),
+                                 mode, _ptr(ws), 0 if ws is None else ws.numel(),
+                                 ctypes.c_void_p(_stream(x.device))), "lora_layer_apply")
+    return y

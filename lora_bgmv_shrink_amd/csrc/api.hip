@@ -1,0 +1,418 @@
+// C ABI of liblora_mi355x: argument checks, pool tables, workspace layout and
+// dispatch.  The semantics of every entry point are documented in
+// include/lora_mi355x.h.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "lora_internal.hpp"
+
+using namespace lora;
+
+struct lora_pool_s {
+    PoolDev dev;
+    lora_layout_t layout;
+    lora_dtype_t dtype;
+    std::vector<int32_t> ranks;
+    void* tables;   // one device allocation: ranks, a_off, b_off, scales, err
+};
+
+namespace {
+
+constexpr int kMaxRank = 64;
+constexpr int kMaxAdaptersSegments = 16383;
+constexpr int64_t kRaggedAlignElems = 128;   // 256 B in bf16, 512 B in fp32
+
+int elem_bytes(lora_dtype_t d) { return d == LORA_BF16 ? 2 : 4; }
+bool dtype_ok(lora_dtype_t d) { return d == LORA_F32 || d == LORA_BF16; }
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool ld_ok(int64_t ld, int64_t minv, int eb) { return ld >= minv && (ld * eb) % 16 == 0; }
+
+lora_status_t dev_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_E_DEVICE; }
+
+// Rank stride of the fp32 intermediate t inside layer workspaces.
+int64_t t_stride(int32_t r_max) { return (int64_t)align_up((size_t)r_max, 4); }
+
+__global__ void k_fill_zero(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
+                            size_t n_tail) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t k = i; k < n16; k += stride) p[k] = uint4{0u, 0u, 0u, 0u};
+    if (i < n_tail) tail[i] = 0;
+}
+
+struct SegLayout {
+    size_t perm, seg_ids, seg_off, n_seg, end;
+    int32_t cap;
+};
+
+SegLayout seg_layout(size_t base, int32_t n_rows, int32_t n_adapters) {
+    SegLayout L;
+    L.cap = std::max<int32_t>(1, std::min<int32_t>(n_rows, n_adapters + 1));
+    L.perm = align_up(base, 256);
+    L.seg_ids = align_up(L.perm + (size_t)n_rows * 4, 256);
+    L.seg_off = align_up(L.seg_ids + (size_t)L.cap * 4, 256);
+    L.n_seg = align_up(L.seg_off + (size_t)(L.cap + 1) * 4, 256);
+    L.end = align_up(L.n_seg + 4, 256);
+    return L;
+}
+
+lora_status_t check_segments(const lora_segments_t* seg, int32_t n_rows, int32_t n_adapters) {
+    if (!seg || !seg->seg_ids || !seg->seg_off || !seg->n_seg) return LORA_E_INVALID;
+    if (n_rows > 0 && !seg->perm) return LORA_E_INVALID;
+    if (seg->cap < std::min<int32_t>(n_rows, n_adapters + 1)) return LORA_E_INVALID;
+    return LORA_OK;
+}
+
+lora_status_t check_pool(lora_pool_t p) { return p ? LORA_OK : LORA_E_INVALID; }
+
+lora_mode_t resolve_mode(lora_mode_t m, int32_t n_rows) {
+    if (m != LORA_MODE_AUTO) return m;
+    return n_rows <= 64 ? LORA_MODE_BGMV : LORA_MODE_SGMV;
+}
+
+}  // namespace
+
+namespace lora {
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return hipSuccess;
+    const size_t n16 = bytes / 16;
+    const size_t n_tail = bytes - n16 * 16;
+    const size_t blocks = std::min<size_t>(std::max<size_t>(1, ceil_div((int64_t)n16, 256)), 4096);
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4*)p, n16,
+                       (uint8_t*)p + n16 * 16, n_tail);
+    return hipGetLastError();
+}
+}  // namespace lora
+
+extern "C" {
+
+const char* lora_status_string(lora_status_t s) {
+    switch (s) {
+        case LORA_OK: return "LORA_OK";
+        case LORA_E_INVALID: return "LORA_E_INVALID: invalid argument";
+        case LORA_E_UNSUPPORTED: return "LORA_E_UNSUPPORTED: valid but unsupported (alignment, rank, size)";
+        case LORA_E_WORKSPACE: return "LORA_E_WORKSPACE: workspace missing or too small";
+        case LORA_E_ID_RANGE: return "LORA_E_ID_RANGE: an adapter id was outside [-1, n_adapters)";
+        case LORA_E_DEVICE: return "LORA_E_DEVICE: a HIP runtime call failed";
+    }
+    return "unknown lora_status_t";
+}
+
+int64_t lora_adapter_param_count(int32_t rank, int32_t d_in, int32_t d_out) {
+    if (rank <= 0 || d_in <= 0 || d_out <= 0) return -1;
+    return (int64_t)rank * ((int64_t)d_in + (int64_t)d_out);
+}
+
+lora_status_t lora_pool_ragged_offsets(int32_t n_adapters, const int32_t* ranks, int32_t d_in,
+                                       int32_t d_out, int64_t* a_off, int64_t* b_off,
+                                       int64_t* a_total, int64_t* b_total) {
+    if (n_adapters <= 0 || !ranks || d_in <= 0 || d_out <= 0 || !a_off || !b_off)
+        return LORA_E_INVALID;
+    int64_t pa = 0, pb = 0;
+    for (int32_t u = 0; u < n_adapters; ++u) {
+        if (ranks[u] < 1) return LORA_E_INVALID;
+        if (ranks[u] > kMaxRank) return LORA_E_UNSUPPORTED;
+        a_off[u] = pa;
+        b_off[u] = pb;
+        pa += ceil_div((int64_t)d_in * ranks[u], kRaggedAlignElems) * kRaggedAlignElems;
+        pb += ceil_div((int64_t)ranks[u] * d_out, kRaggedAlignElems) * kRaggedAlignElems;
+    }
+    if (a_total) *a_total = pa;
+    if (b_total) *b_total = pb;
+    return LORA_OK;
+}
+
+lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtype_t dtype,
+                               int32_t n_adapters, int32_t d_in, int32_t d_out, int32_t r_max,
+                               const int32_t* ranks, const int64_t* a_off, const int64_t* b_off,
+                               const void* A, const void* B, const float* scales) {
+    if (!out) return LORA_E_INVALID;
+    *out = nullptr;
+    if (!dtype_ok(dtype) || (layout != LORA_LAYOUT_UNIFORM && layout != LORA_LAYOUT_RAGGED))
+        return LORA_E_INVALID;
+    if (n_adapters <= 0 || d_in <= 0 || d_out <= 0 || r_max <= 0 || !A || !B || !scales)
+        return LORA_E_INVALID;
+    if (r_max > kMaxRank) return LORA_E_UNSUPPORTED;
+    if (!al16(A) || !al16(B)) return LORA_E_UNSUPPORTED;
+    const int eb = elem_bytes(dtype);
+
+    std::vector<int32_t> rk(n_adapters);
+    std::vector<int64_t> ao(n_adapters), bo(n_adapters);
+    if (layout == LORA_LAYOUT_UNIFORM) {
+        if (ranks || a_off || b_off) return LORA_E_INVALID;
+        for (int32_t u = 0; u < n_adapters; ++u) {
+            rk[u] = r_max;
+            ao[u] = (int64_t)u * d_in * r_max;
+            bo[u] = (int64_t)u * r_max * d_out;
+        }
+    } else {
+        if (!ranks || !a_off || !b_off) return LORA_E_INVALID;
+        std::vector<std::pair<int64_t, int64_t>> sa, sb;
+        for (int32_t u = 0; u < n_adapters; ++u) {
+            if (ranks[u] < 1 || ranks[u] > r_max) return LORA_E_INVALID;
+            if (a_off[u] < 0 || b_off[u] < 0) return LORA_E_INVALID;
+            if ((a_off[u] * eb) % 16 != 0 || (b_off[u] * eb) % 16 != 0) return LORA_E_UNSUPPORTED;
+            rk[u] = ranks[u];
+            ao[u] = a_off[u];
+            bo[u] = b_off[u];
+            sa.push_back({a_off[u], a_off[u] + (int64_t)d_in * ranks[u]});
+            sb.push_back({b_off[u], b_off[u] + (int64_t)ranks[u] * d_out});
+        }
+        std::sort(sa.begin(), sa.end());
+        std::sort(sb.begin(), sb.end());
+        for (size_t i = 1; i < sa.size(); ++i)
+            if (sa[i].first < sa[i - 1].second || sb[i].first < sb[i - 1].second) return LORA_E_INVALID;
+    }
+    bool vec_a = true, vec_b = ((int64_t)d_out * eb) % 16 == 0;
+    for (int32_t u = 0; u < n_adapters; ++u) {
+        vec_a = vec_a && (ao[u] * eb) % 16 == 0;
+        vec_b = vec_b && (bo[u] * eb) % 16 == 0;
+    }
+
+    const size_t o_ranks = 0;
+    const size_t o_aoff = align_up(o_ranks + (size_t)n_adapters * 4, 256);
+    const size_t o_boff = align_up(o_aoff + (size_t)n_adapters * 8, 256);
+    const size_t o_scales = align_up(o_boff + (size_t)n_adapters * 8, 256);
+    const size_t o_err = align_up(o_scales + (size_t)n_adapters * 4, 256);
+    const size_t total = o_err + 256;
+    std::vector<uint8_t> host(total, 0);
+    std::memcpy(host.data() + o_ranks, rk.data(), (size_t)n_adapters * 4);
+    std::memcpy(host.data() + o_aoff, ao.data(), (size_t)n_adapters * 8);
+    std::memcpy(host.data() + o_boff, bo.data(), (size_t)n_adapters * 8);
+    std::memcpy(host.data() + o_scales, scales, (size_t)n_adapters * 4);
+
+    void* mem = nullptr;
+    if (hipMalloc(&mem, total) != hipSuccess) return LORA_E_DEVICE;
+    if (hipMemcpy(mem, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(mem);
+        return LORA_E_DEVICE;
+    }
+    lora_pool_s* p = new lora_pool_s;
+    p->layout = layout;
+    p->dtype = dtype;
+    p->ranks = rk;
+    p->tables = mem;
+    uint8_t* m = (uint8_t*)mem;
+    p->dev.A = A;
+    p->dev.B = B;
+    p->dev.ranks = (const int32_t*)(m + o_ranks);
+    p->dev.a_off = (const int64_t*)(m + o_aoff);
+    p->dev.b_off = (const int64_t*)(m + o_boff);
+    p->dev.scales = (const float*)(m + o_scales);
+    p->dev.err = (int32_t*)(m + o_err);
+    p->dev.n_adapters = n_adapters;
+    p->dev.d_in = d_in;
+    p->dev.d_out = d_out;
+    p->dev.r_max = r_max;
+    p->dev.vec_a = vec_a ? 1 : 0;
+    p->dev.vec_b = vec_b ? 1 : 0;
+    *out = p;
+    return LORA_OK;
+}
+
+lora_status_t lora_pool_destroy(lora_pool_t pool) {
+    if (!pool) return LORA_OK;
+    hipError_t e = hipDeviceSynchronize();
+    hipError_t f = hipFree(pool->tables);
+    delete pool;
+    return (e == hipSuccess && f == hipSuccess) ? LORA_OK : LORA_E_DEVICE;
+}
+
+int64_t lora_pool_param_count(lora_pool_t pool, int32_t adapter) {
+    if (!pool || adapter < 0 || adapter >= pool->dev.n_adapters) return -1;
+    return lora_adapter_param_count(pool->ranks[adapter], pool->dev.d_in, pool->dev.d_out);
+}
+
+lora_status_t lora_pool_last_error(lora_pool_t pool, hipStream_t stream, int32_t* out) {
+    if (!pool || !out) return LORA_E_INVALID;
+    if (hipStreamSynchronize(stream) != hipSuccess) return LORA_E_DEVICE;
+    int32_t v = 0, zero = 0;
+    if (hipMemcpy(&v, pool->dev.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return LORA_E_DEVICE;
+    if (hipMemcpy(pool->dev.err, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return LORA_E_DEVICE;
+    *out = v;
+    return (v & 1) ? LORA_E_ID_RANGE : LORA_OK;
+}
+
+lora_status_t lora_workspace_clear(void* ws, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return LORA_OK;
+    if (!ws || !al16(ws)) return LORA_E_INVALID;
+    return dev_status(launch_fill_zero(ws, bytes, stream));
+}
+
+lora_status_t lora_segments_workspace(int32_t n_rows, int32_t n_adapters, size_t* bytes) {
+    if (!bytes || n_rows < 0 || n_adapters <= 0) return LORA_E_INVALID;
+    if (n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
+    *bytes = 0;
+    return LORA_OK;
+}
+
+lora_status_t lora_segments_build(const int32_t* ids, int32_t n_rows, int32_t n_adapters,
+                                  const lora_segments_t* seg, int32_t* status, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (n_rows < 0 || n_adapters <= 0 || (n_rows > 0 && !ids)) return LORA_E_INVALID;
+    if (n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
+    lora_status_t st = check_segments(seg, n_rows, n_adapters);
+    if (st != LORA_OK) return st;
+    return dev_status(launch_segments(ids, n_rows, n_adapters, seg, status, stream));
+}
+
+lora_status_t lora_bgmv_shrink_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes) {
+    if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
+    BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
+    *bytes = bgmv_shrink_ws_bytes(plan, n_rows);
+    return LORA_OK;
+}
+
+lora_status_t lora_bgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx, const int32_t* ids,
+                               int32_t n_rows, float* t, int64_t ldt, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    const int eb = elem_bytes(pool->dtype);
+    if (!x || !ids || !t) return LORA_E_INVALID;
+    if (ldx < pool->dev.d_in || ldt < pool->dev.r_max) return LORA_E_INVALID;
+    if (!al16(x) || !ld_ok(ldx, pool->dev.d_in, eb)) return LORA_E_UNSUPPORTED;
+    BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, eb, n_rows);
+    const size_t need = bgmv_shrink_ws_bytes(plan, n_rows);
+    if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return LORA_E_WORKSPACE;
+    return dev_status(launch_bgmv_shrink(pool->dev, pool->dtype, x, ldx, ids, n_rows, t, ldt, ws,
+                                         plan, stream));
+}
+
+lora_status_t lora_bgmv_expand(lora_pool_t pool, const float* t, int64_t ldt, const int32_t* ids,
+                               int32_t n_rows, void* y, lora_dtype_t y_dtype, int64_t ldy,
+                               int accumulate, hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    if (!t || !ids || !y || ldt < pool->dev.r_max || ldy < pool->dev.d_out) return LORA_E_INVALID;
+    const int ey = elem_bytes(y_dtype);
+    if (!al16(y) || !ld_ok(ldy, pool->dev.d_out, ey)) return LORA_E_UNSUPPORTED;
+    return dev_status(launch_bgmv_expand(pool->dev, pool->dtype, t, ldt, ids, n_rows, y, y_dtype, ldy,
+                                         accumulate ? 1 : 0, true, stream));
+}
+
+lora_status_t lora_sgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
+                               const lora_segments_t* seg, int32_t n_rows, float* t, int64_t ldt,
+                               hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    const int eb = elem_bytes(pool->dtype);
+    if (!x || !t || ldx < pool->dev.d_in || ldt < pool->dev.r_max) return LORA_E_INVALID;
+    lora_status_t st = check_segments(seg, n_rows, pool->dev.n_adapters);
+    if (st != LORA_OK) return st;
+    if (!al16(x) || !ld_ok(ldx, pool->dev.d_in, eb)) return LORA_E_UNSUPPORTED;
+    return dev_status(launch_sgmv_shrink(pool->dev, pool->dtype, x, ldx, seg, n_rows,
+                                         pool->dev.n_adapters + 1, t, ldt, true, stream));
+}
+
+lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
+                               const lora_segments_t* seg, int32_t n_rows, void* y,
+                               lora_dtype_t y_dtype, int64_t ldy, int accumulate,
+                               hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    if (!t || !y || ldt < pool->dev.r_max || ldy < pool->dev.d_out) return LORA_E_INVALID;
+    lora_status_t st = check_segments(seg, n_rows, pool->dev.n_adapters);
+    if (st != LORA_OK) return st;
+    const int ey = elem_bytes(y_dtype);
+    if (!al16(y) || !ld_ok(ldy, pool->dev.d_out, ey)) return LORA_E_UNSUPPORTED;
+    return dev_status(launch_sgmv_expand(pool->dev, pool->dtype, t, ldt, seg, n_rows,
+                                         pool->dev.n_adapters + 1, y, y_dtype, ldy,
+                                         accumulate ? 1 : 0, stream));
+}
+
+lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t mode,
+                                   size_t* bytes) {
+    if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
+    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
+        return LORA_E_INVALID;
+    const lora_mode_t m = resolve_mode(mode, n_rows);
+    size_t off = align_up((size_t)n_rows * t_stride(pool->dev.r_max) * 4, 256);
+    if (m == LORA_MODE_BGMV) {
+        BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
+        off += bgmv_shrink_ws_bytes(plan, n_rows);
+    } else {
+        if (pool->dev.n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
+        off = seg_layout(off, n_rows, pool->dev.n_adapters).end;
+    }
+    *bytes = std::max<size_t>(off, 256);
+    return LORA_OK;
+}
+
+lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
+                               int64_t ldw, lora_w_layout_t w_layout, const int32_t* ids,
+                               const lora_segments_t* seg, int32_t n_rows, void* y,
+                               lora_dtype_t y_dtype, int64_t ldy, lora_mode_t mode, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
+    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
+        return LORA_E_INVALID;
+    if (w_layout != LORA_W_IN_OUT && w_layout != LORA_W_OUT_IN) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    const PoolDev& P = pool->dev;
+    const int eb = elem_bytes(pool->dtype);
+    const int ey = elem_bytes(y_dtype);
+    if (!x || !W || !ids || !y) return LORA_E_INVALID;
+    const int64_t w_min = (w_layout == LORA_W_IN_OUT) ? P.d_out : P.d_in;
+    if (ldx < P.d_in || ldw < w_min || ldy < P.d_out) return LORA_E_INVALID;
+    if (!al16(x) || !al16(W) || !al16(y) || !ld_ok(ldx, P.d_in, eb) || !ld_ok(ldw, w_min, eb) ||
+        !ld_ok(ldy, P.d_out, ey))
+        return LORA_E_UNSUPPORTED;
+    const lora_mode_t m = resolve_mode(mode, n_rows);
+    if (m == LORA_MODE_SGMV && seg) {
+        lora_status_t st = check_segments(seg, n_rows, P.n_adapters);
+        if (st != LORA_OK) return st;
+    }
+    size_t need = 0;
+    lora_status_t st = lora_layer_workspace(pool, n_rows, m, &need);
+    if (st != LORA_OK) return st;
+    if (!ws || ws_bytes < need || !al16(ws)) return LORA_E_WORKSPACE;
+
+    uint8_t* base = (uint8_t*)ws;
+    float* t = (float*)base;
+    const int64_t ldt = t_stride(P.r_max);
+    const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256);
+    hipError_t e = hipSuccess;
+    if (m == LORA_MODE_BGMV) {
+        BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
+        e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, base + after_t, plan,
+                               stream);
+    } else {
+        lora_segments_t own;
+        const lora_segments_t* sg = seg;
+        if (!sg) {
+            SegLayout L = seg_layout(after_t, n_rows, P.n_adapters);
+            own.perm = (int32_t*)(base + L.perm);
+            own.seg_ids = (int32_t*)(base + L.seg_ids);
+            own.seg_off = (int32_t*)(base + L.seg_off);
+            own.n_seg = (int32_t*)(base + L.n_seg);
+            own.cap = L.cap;
+            e = launch_segments(ids, n_rows, P.n_adapters, &own, P.err, stream);
+            sg = &own;
+        }
+        if (e == hipSuccess)
+            e = launch_sgmv_shrink(P, pool->dtype, x, ldx, sg, n_rows, P.n_adapters + 1, t, ldt, true,
+                                   stream);
+    }
+    if (e != hipSuccess) return LORA_E_DEVICE;
+    GemmArgs g;
+    g.x = x;
+    g.ldx = ldx;
+    g.W = W;
+    g.ldw = ldw;
+    g.w_out_in = (w_layout == LORA_W_OUT_IN) ? 1 : 0;
+    g.ids = ids;
+    g.n_rows = n_rows;
+    g.t = t;
+    g.ldt = ldt;
+    g.y = y;
+    g.ldy = ldy;
+    g.vec_x = true;
+    g.vec_w = true;
+    return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
+}
+
+}  // extern "C"

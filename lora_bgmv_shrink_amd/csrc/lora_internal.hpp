@@ -1,0 +1,120 @@
+// Internal declarations shared by the HIP translation units of liblora_mi355x.
+// Nothing here is part of the C ABI (include/lora_mi355x.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "../../include/lora_mi355x.h"
+
+namespace lora {
+
+// bf16 is carried as its raw 16-bit pattern.
+using bf16 = uint16_t;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Device view of a pool: element offsets, ranks and scales live in device
+// tables built once by lora_pool_create.
+struct PoolDev {
+    const void* A;
+    const void* B;
+    const int32_t* ranks;
+    const int64_t* a_off;
+    const int64_t* b_off;
+    const float* scales;
+    int32_t* err;        // bit 0: an id outside [-1, n_adapters) was seen
+    int32_t n_adapters;
+    int32_t d_in;
+    int32_t d_out;
+    int32_t r_max;
+    int32_t vec_a;       // every A block 16-byte aligned and rank*elem % 16 == 0
+    int32_t vec_b;       // every B block 16-byte aligned and d_out*elem % 16 == 0
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quieted).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return f32_to_bf16(v); }
+
+__device__ __forceinline__ bool id_ok(int32_t a, int32_t n_adapters) {
+    return a >= 0 && a < n_adapters;
+}
+
+__device__ __forceinline__ void flag_bad_id(int32_t* err) {
+    __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Launchers (host side, one per kernel family).  Shapes are validated by the
+// C-ABI layer before these run.
+// ---------------------------------------------------------------------------
+
+// Segments: one workgroup of 1024 threads.
+hipError_t launch_segments(const int32_t* ids, int32_t n_rows, int32_t n_adapters,
+                           const lora_segments_t* seg, int32_t* status, hipStream_t stream);
+
+// BGMV shrink: split-K over d_in with a deterministic last-arriver sum.
+struct BgmvShrinkPlan {
+    int32_t slices;   // K slices per row
+    int32_t ks;       // k-rows per slice (multiple of 8)
+};
+BgmvShrinkPlan plan_bgmv_shrink(const PoolDev& P, int elem_bytes, int32_t n_rows);
+size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan& plan, int32_t n_rows);
+hipError_t launch_bgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
+                              const int32_t* ids, int32_t n_rows, float* t, int64_t ldt,
+                              void* ws, const BgmvShrinkPlan& plan, hipStream_t stream);
+
+hipError_t launch_bgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
+                              const int32_t* ids, int32_t n_rows, void* y, lora_dtype_t ydt,
+                              int64_t ldy, int accumulate, bool vec_y, hipStream_t stream);
+
+// SGMV shrink / expand (MFMA over segment tiles).
+hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
+                              const lora_segments_t* seg, int32_t n_rows, int32_t n_bins,
+                              float* t, int64_t ldt, bool vec_x, hipStream_t stream);
+hipError_t launch_sgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
+                              const lora_segments_t* seg, int32_t n_rows, int32_t n_bins,
+                              void* y, lora_dtype_t ydt, int64_t ldy, int accumulate,
+                              hipStream_t stream);
+
+// Fused layer GEMM: y = x W (+ LoRA expand epilogue from t).
+struct GemmArgs {
+    const void* x;
+    int64_t ldx;
+    const void* W;
+    int64_t ldw;
+    int w_out_in;
+    const int32_t* ids;
+    int32_t n_rows;
+    const float* t;   // nullptr: no LoRA term
+    int64_t ldt;
+    void* y;
+    int64_t ldy;
+    bool vec_x;
+    bool vec_w;
+};
+hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt,
+                             const GemmArgs& g, hipStream_t stream);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace lora

@@ -21,9 +21,10 @@ Shapes and value distributions follow the pages:
 Values are drawn in fp32 from N(0,1), divided by a per-tensor constant and,
 for bf16 workloads, rounded to bf16 by torch (round to nearest even).
 Structure (ids, lengths, ranks) comes from ``numpy.random.default_rng(seed)``;
-values from a ``torch.Generator`` on the requested device, so a workload made
-on ``cuda`` differs numerically from one made on ``cpu`` but is equally
-seeded.  Tests always hand the oracle the exact tensors the GPU sees.
+values from a ``torch.Generator`` on the requested device (one generator per
+projection, seeded ``1000*seed + index``, so any subset of projections draws
+the same values), so a workload made on ``cuda`` differs numerically from one
+made on ``cpu`` but is equally seeded.  Tests always hand the oracle the exact tensors the GPU sees.
 """
 from __future__ import annotations
 
@@ -233,9 +234,9 @@ def walkthrough_batch(device="cpu", repeat_row0=False) -> Workload:
 # Decode / prefill workloads
 # --------------------------------------------------------------------------
 
-def decode_q_proj(device="cuda", dtype=torch.bfloat16, seed=1) -> Workload:
-    """32 decode rows, 20 distinct adapters out of a uniform rank-16 pool of 250,
-    3 base-only rows (10%), one 4096->4096 projection."""
+def decode_q_proj_ids(seed=1) -> np.ndarray:
+    """32 rows: 20 distinct ids drawn without replacement from 250, each used
+    once plus 9 more uniform draws among them, 3 base-only rows; shuffled."""
     rng = np.random.default_rng(seed)
     n_rows, n_pool, n_distinct = 32, 250, 20
     n_base = int(round(0.1 * n_rows))
@@ -243,6 +244,52 @@ def decode_q_proj(device="cuda", dtype=torch.bfloat16, seed=1) -> Workload:
     extra = rng.choice(chosen, n_rows - n_base - n_distinct)
     ids = np.concatenate([chosen, extra, np.full(n_base, -1)]).astype(np.int32)
     rng.shuffle(ids)
+    return ids
+
+
+def skewed_decode_ids(seed=2) -> np.ndarray:
+    """256 rows with ids ~ Zipf(1.1) over a pool of 1000."""
+    rng = np.random.default_rng(seed)
+    return rng.choice(1000, 256, p=zipf_probs(1000)).astype(np.int32)
+
+
+def prefill_ids(seed=3, lengths=None):
+    """16 requests, lengths ~ U{128..2048}, 8 distinct ids from 64, two
+    requests each, arrival order shuffled; rows request after request."""
+    rng = np.random.default_rng(seed)
+    n_pool, n_req = 64, 16
+    if lengths is None:
+        lengths = rng.integers(128, 2049, n_req).tolist()
+    else:
+        rng.integers(128, 2049, n_req)
+    distinct = rng.choice(n_pool, 8, replace=False)
+    req_ids = np.repeat(distinct, 2)
+    rng.shuffle(req_ids)
+    ids = np.concatenate([np.full(n, a) for a, n in zip(req_ids, lengths)]).astype(np.int32)
+    return ids, list(lengths), req_ids
+
+
+def mixed_rank_ids(seed=4):
+    """Ranks of a ragged pool of 500 and the 2218-row chunked-prefill batch."""
+    rng = np.random.default_rng(seed)
+    n_pool = 500
+    ranks = rng.choice([8, 16, 32, 64], n_pool, p=[0.4, 0.3, 0.2, 0.1]).astype(np.int32)
+    p = zipf_probs(n_pool)
+    dec_ids = rng.choice(n_pool, 64, p=p)
+    pre_ids = rng.choice(n_pool, 4, p=p)
+    n_base = int(round(0.05 * (64 + 4 * 512)))
+    block = np.full(64 + n_base, -1, np.int64)
+    pos = np.sort(rng.choice(64 + n_base, 64, replace=False))
+    block[pos] = dec_ids
+    ids = np.concatenate([block] + [np.full(512, a) for a in pre_ids]).astype(np.int32)
+    return ids, ranks, block, pre_ids
+
+
+def decode_q_proj(device="cuda", dtype=torch.bfloat16, seed=1) -> Workload:
+    """32 decode rows, 20 distinct adapters out of a uniform rank-16 pool of 250,
+    3 base-only rows (10%), one 4096->4096 projection."""
+    ids = decode_q_proj_ids(seed)
+    n_rows, n_pool, n_distinct, n_base = len(ids), 250, 20, int((ids == -1).sum())
     g = _gen(device, seed)
     d_in = d_out = 4096
     x = _randn(g, (n_rows, d_in), X_DIV, dtype, device)
@@ -255,14 +302,13 @@ def decode_q_proj(device="cuda", dtype=torch.bfloat16, seed=1) -> Workload:
 
 def skewed_decode_8b(device="cuda", dtype=torch.bfloat16, seed=2, projections=None) -> Workload:
     """256 decode rows, ids ~ Zipf(1.1) over a rank-16 pool of 1000, all seven 8B projections."""
-    rng = np.random.default_rng(seed)
-    n_rows, n_pool = 256, 1000
-    ids = rng.choice(n_pool, n_rows, p=zipf_probs(n_pool)).astype(np.int32)
-    g = _gen(device, seed)
+    ids = skewed_decode_ids(seed)
+    n_rows, n_pool = len(ids), 1000
     projs = []
-    for name, d_in, d_out in PROJ_8B:
+    for pi, (name, d_in, d_out) in enumerate(PROJ_8B):
         if projections is not None and name not in projections:
             continue
+        g = _gen(device, 1000 * seed + pi)
         x = _randn(g, (n_rows, d_in), X_DIV, dtype, device)
         W = _randn(g, (d_in, d_out), W_DIV, dtype, device)
         pool = make_uniform_pool(g, device, dtype, n_pool, d_in, d_out, 16)
@@ -275,21 +321,13 @@ def prefill_70b(device="cuda", dtype=torch.bfloat16, seed=3, projections=None,
                 lengths=None) -> Workload:
     """16 prefill requests, lengths ~ U{128..2048}, 8 distinct rank-64 adapters
     (two requests each) from a pool of 64; rows in arrival order."""
-    rng = np.random.default_rng(seed)
-    n_pool, n_req = 64, 16
-    if lengths is None:
-        lengths = rng.integers(128, 2049, n_req).tolist()
-    else:
-        rng.integers(128, 2049, n_req)
-    distinct = rng.choice(n_pool, 8, replace=False)
-    req_ids = np.repeat(distinct, 2)
-    rng.shuffle(req_ids)
-    ids = np.concatenate([np.full(n, a) for a, n in zip(req_ids, lengths)]).astype(np.int32)
-    g = _gen(device, seed)
+    ids, lengths, req_ids = prefill_ids(seed, lengths)
+    n_pool = 64
     projs = []
-    for name, d_in, d_out in PROJ_70B:
+    for pi, (name, d_in, d_out) in enumerate(PROJ_70B):
         if projections is not None and name not in projections:
             continue
+        g = _gen(device, 1000 * seed + pi)
         x = _randn(g, (len(ids), d_in), X_DIV, dtype, device)
         W = _randn(g, (d_in, d_out), W_DIV, dtype, device)
         pool = make_uniform_pool(g, device, dtype, n_pool, d_in, d_out, 64)
@@ -303,22 +341,12 @@ def mixed_rank_70b(device="cuda", dtype=torch.bfloat16, seed=4, projections=None
     """Chunked-prefill batch on a ragged pool of 500 (ranks 8/16/32/64 with
     weights .4/.3/.2/.1): 64 Zipf decode rows with 106 base-only rows
     interleaved, then 4 prefill segments of 512 rows; 2218 rows."""
-    rng = np.random.default_rng(seed)
-    n_pool = 500
-    ranks = rng.choice([8, 16, 32, 64], n_pool, p=[0.4, 0.3, 0.2, 0.1]).astype(np.int32)
-    p = zipf_probs(n_pool)
-    dec_ids = rng.choice(n_pool, 64, p=p)
-    pre_ids = rng.choice(n_pool, 4, p=p)
-    n_base = int(round(0.05 * (64 + 4 * 512)))
-    block = np.full(64 + n_base, -1, np.int64)
-    pos = np.sort(rng.choice(64 + n_base, 64, replace=False))
-    block[pos] = dec_ids
-    ids = np.concatenate([block] + [np.full(512, a) for a in pre_ids]).astype(np.int32)
-    g = _gen(device, seed)
+    ids, ranks, block, pre_ids = mixed_rank_ids(seed)
     projs = []
-    for name, d_in, d_out in PROJ_70B:
+    for pi, (name, d_in, d_out) in enumerate(PROJ_70B):
         if projections is not None and name not in projections:
             continue
+        g = _gen(device, 1000 * seed + pi)
         x = _randn(g, (len(ids), d_in), X_DIV, dtype, device)
         W = _randn(g, (d_in, d_out), W_DIV, dtype, device)
         pool = make_ragged_pool(g, device, dtype, ranks, d_in, d_out)
