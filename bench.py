@@ -1,0 +1,399 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-LoRA batched layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the layer over one synthetic batch: the shrink
+(x -> xA) for every row, then the base GEMM with the scaled expand fused into
+its epilogue.  The headline workload is the decode batch: one 4096->4096
+q projection, rank 16, a uniform pool of 250 adapters, 32 single-token rows
+on 20 distinct adapters plus 3 base-only rows, bf16 inputs with fp32
+accumulation.  Successive steps rotate over 8 replicas of the layer
+(different weights and pools, ~800 MB in all, more than the 256 MB
+Infinity Cache) so that every step reads its weights from HBM, as the
+layers of a model would.  Steps are captured in HIP graphs and replayed.
+
+The JSON line carries:
+  value        tokens/s of the whole step (wall clock around exactly K steps)
+  roofline     the dominant kernel (base GEMM + fused expand) against HBM
+               peak, from its average launch duration (HIP events)
+  adapter_term the shrink kernel's algorithmic bytes/s and the adapter
+               overhead fraction (layer time minus base-only time)
+  cpu_baseline the fp64 oracle on the host cores, on a bounded sample
+  workloads    the other four workloads (skewed 8B decode, 70B prefill,
+               mixed-rank 70B ragged and padded), measured the same way
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--kernel-reps", type=int, default=50, help="graph replays per kernel timing")
+    ap.add_argument("--workloads", default="skewed,prefill,mixed",
+                    help="comma list of extra workloads to measure (empty: none)")
+    ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def make_pool(b, p):
+    from lora_bgmv_shrink_amd import workloads as wl
+    if p.layout == wl.UNIFORM:
+        return b.lora_pool_create(b.LORA_LAYOUT_UNIFORM, p.A, p.B, p.n_adapters, p.d_in, p.d_out, p.r_max,
+                                  p.scales)
+    return b.lora_pool_create(b.LORA_LAYOUT_RAGGED, p.A, p.B, p.n_adapters, p.d_in, p.d_out, p.r_max,
+                              p.scales, ranks=p.ranks, a_off=p.a_off, b_off=p.b_off)
+
+
+def capture(torch, fn):
+    """Capture fn() into a HIP graph (after one eager run)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps):
+    """Average GPU time of one replay, from HIP events on the replay stream."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(reps):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e-3   # seconds
+
+
+def distinct_bytes(p, ids, which):
+    """Bytes of the A (or B) blocks of the distinct adapters the batch uses."""
+    import numpy as np
+    us = sorted(set(int(a) for a in ids.tolist() if 0 <= a < p.n_adapters))
+    eb = p.A.element_size()
+    if which == "A":
+        return sum(int(p.ranks[u]) * p.d_in * eb for u in us), len(us)
+    return sum(int(p.ranks[u]) * p.d_out * eb for u in us), len(us)
+
+
+# ---------------------------------------------------------------------------
+# headline: decode q_proj
+# ---------------------------------------------------------------------------
+
+def bench_decode(torch, args):
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    R = args.replicas
+    reps = []
+    for r in range(R):
+        w = wl.decode_q_proj(device=dev, value_seed=None if r == 0 else 1 + 1000 * r)
+        p = w.projections[0]
+        pool = make_pool(b, p.pool)
+        Wt = p.W.t().contiguous()
+        del p.W
+        n = w.n_rows
+        ids = torch.as_tensor(w.ids, device=dev)
+        t = torch.zeros((n, p.pool.r_max), dtype=torch.float32, device=dev)
+        y = torch.zeros((n, p.d_out), dtype=torch.bfloat16, device=dev)
+        yb = torch.zeros_like(y)
+        ws = torch.zeros(max(b.lora_bgmv_shrink_workspace(pool, n), 16), dtype=torch.uint8, device=dev)
+        reps.append(dict(w=w, p=p, pool=pool, Wt=Wt, ids=ids, t=t, y=y, yb=yb, ws=ws))
+    w0, p0 = reps[0]["w"], reps[0]["p"]
+    n = w0.n_rows
+
+    def shrink(r):
+        b.lora_bgmv_shrink(r["pool"], r["p"].x, r["ids"], t=r["t"], ws=r["ws"])
+
+    def gemm(r):
+        b.lora_base_gemm_expand(r["pool"], r["p"].x, r["Wt"], r["ids"], r["t"], w_layout=b.LORA_W_OUT_IN,
+                                y=r["y"])
+
+    def base_only(r):
+        b.lora_base_gemm_expand(r["pool"], r["p"].x, r["Wt"], r["ids"], None, w_layout=b.LORA_W_OUT_IN,
+                                y=r["yb"])
+
+    def step(r):
+        shrink(r)
+        gemm(r)
+
+    # the step is lora_layer_apply's kernel sequence; check it gives the same bits
+    r0 = reps[0]
+    step(r0)
+    y_ref = b.lora_layer_apply(r0["pool"], r0["p"].x, r0["Wt"], r0["ids"], w_layout=b.LORA_W_OUT_IN,
+                               mode=b.LORA_MODE_BGMV)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ref, r0["y"]), "step differs from lora_layer_apply"
+
+    K, W = args.steps, args.warmup
+    g_full = capture(torch, lambda: [step(r) for r in reps])
+    rem = K % R
+    g_rem = capture(torch, lambda: [step(r) for r in reps[:rem]]) if rem else None
+    for _ in range(max(1, W // R)):
+        g_full.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ----
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K // R):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_step = (t1 - t0) / K
+
+    # ---- per-kernel launch durations (graphs of R back-to-back launches) ----
+    kr = args.kernel_reps
+    g_gemm = capture(torch, lambda: [gemm(r) for r in reps])
+    g_shr = capture(torch, lambda: [shrink(r) for r in reps])
+    g_base = capture(torch, lambda: [base_only(r) for r in reps])
+    d_gemm = time_graph(torch, g_gemm, kr) / R
+    d_shr = time_graph(torch, g_shr, kr) / R
+    d_base = time_graph(torch, g_base, kr) / R
+    d_step = time_graph(torch, g_full, max(1, kr // 2)) / R
+
+    pool = p0.pool
+    bA, U = distinct_bytes(pool, w0.ids, "A")
+    bB, _ = distinct_bytes(pool, w0.ids, "B")
+    eb = 2
+    x_b = n * pool.d_in * eb
+    y_b = n * pool.d_out * eb
+    t_b = n * pool.r_max * 4
+    w_b = pool.d_in * pool.d_out * eb
+    gemm_bytes = w_b + bB + x_b + t_b + y_b + n * 4
+    shrink_bytes = bA + x_b + t_b + n * 4
+    achieved = gemm_bytes / d_gemm / 1e9
+    out = dict(
+        sec_step=sec_step,
+        tokens_per_s=n / sec_step,
+        gpu_step_s=d_step,
+        kernels_us=dict(shrink=d_shr * 1e6, base_gemm_expand=d_gemm * 1e6, base_only_gemm=d_base * 1e6),
+        roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                      kernel="k_layer_gemm (base GEMM + fused LoRA expand)",
+                      bytes_per_launch=gemm_bytes, avg_launch_us=round(d_gemm * 1e6, 3)),
+        adapter_term=dict(
+            distinct_adapters=U,
+            shrink_bytes=shrink_bytes, shrink_us=round(d_shr * 1e6, 3),
+            shrink_GBps=round(shrink_bytes / d_shr / 1e9, 1),
+            shrink_frac_hbm=round(shrink_bytes / d_shr / 1e9 / HBM_PEAK_GBS, 4),
+            adapter_bytes=bA + bB,
+            overhead_fraction=round(max(0.0, (d_step - d_base) / d_step), 4),
+        ),
+    )
+    return out, w0
+
+
+# ---------------------------------------------------------------------------
+# other workloads
+# ---------------------------------------------------------------------------
+
+def bench_multi(torch, args, name):
+    """Seven projections per step through lora_layer_apply (AUTO mode)."""
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    if name == "skewed":
+        w = wl.skewed_decode_8b(device=dev)
+        pools = [("uniform", [pp.pool for pp in w.projections])]
+    elif name == "prefill":
+        w = wl.prefill_70b(device=dev)
+        pools = [("uniform", [pp.pool for pp in w.projections])]
+    else:
+        w = wl.mixed_rank_70b(device=dev)
+        pools = [("ragged", [pp.pool for pp in w.projections]),
+                 ("padded", [pp.pool_padded for pp in w.projections])]
+    n = w.n_rows
+    ids = torch.as_tensor(w.ids, device=dev)
+    projs = []
+    for pp in w.projections:
+        Wt = pp.W.t().contiguous()
+        pp.W = None
+        projs.append(dict(p=pp, Wt=Wt, y=torch.empty((n, pp.d_out), dtype=torch.bfloat16, device=dev)))
+    res = dict(workload=w.name, rows=n, distinct_adapters=int(len(set(w.ids[w.ids >= 0].tolist()))))
+    for label, plist in pools:
+        hs = [make_pool(b, pl) for pl in plist]
+        wss = [torch.zeros(b.lora_layer_workspace(h, n), dtype=torch.uint8, device=dev) for h in hs]
+
+        def step():
+            for pr, h, ws in zip(projs, hs, wss):
+                b.lora_layer_apply(h, pr["p"].x, pr["Wt"], ids, w_layout=b.LORA_W_OUT_IN, y=pr["y"], ws=ws)
+
+        def base_step():
+            for pr, h in zip(projs, hs):
+                b.lora_base_gemm_expand(h, pr["p"].x, pr["Wt"], ids, None, w_layout=b.LORA_W_OUT_IN, y=pr["y"])
+
+        g = capture(torch, step)
+        gb = capture(torch, base_step)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        K = args.extra_steps
+        t0 = time.perf_counter()
+        for _ in range(K):
+            g.replay()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / K
+        d_base = time_graph(torch, gb, 3)
+        flops = 0
+        abytes = 0
+        wbytes = 0
+        for pr, pl in zip(projs, plist):
+            pp = pr["p"]
+            flops += 2 * n * pp.d_in * pp.d_out
+            bA, _ = distinct_bytes(pl, w.ids, "A")
+            bB, _ = distinct_bytes(pl, w.ids, "B")
+            abytes += bA + bB
+            wbytes += pp.d_in * pp.d_out * 2
+            r_true = [int(pl.ranks[a]) if a >= 0 else 0 for a in w.ids.tolist()]
+            flops += 2 * sum(r_true) * (pp.d_in + pp.d_out)
+        res[label] = dict(
+            tokens_per_s_per_projection=round(n * len(projs) / sec, 1),
+            tokens_per_s_seven_projections=round(n / sec, 1),
+            ms_per_step=round(sec * 1e3, 4),
+            tflops=round(flops / sec / 1e12, 1), mfma_frac=round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+            weight_plus_adapter_GBps=round((wbytes + abytes) / sec / 1e9, 1),
+            adapter_bytes=abytes,
+            overhead_fraction=round(max(0.0, (sec - d_base) / sec), 4),
+        )
+        for h in hs:
+            h.destroy()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, seconds):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    p = w.projections[0]
+    pool = p.pool
+    used = sorted(set(int(a) for a in w.ids.tolist() if a >= 0))
+    # marshal the batch to fp64 (outside the timed loop)
+    A, B, a_off, b_off = [], [], [], []
+    pa = pb = 0
+    for u in used:
+        a = pool.a_block(u).float().cpu().double().numpy().reshape(-1)
+        bb = pool.b_block(u).float().cpu().double().numpy().reshape(-1)
+        a_off.append(pa)
+        b_off.append(pb)
+        pa += a.size
+        pb += bb.size
+        A.append(a)
+        B.append(bb)
+    mp = {u: i for i, u in enumerate(used)}
+    ids = np.array([mp.get(int(a), -1) for a in w.ids.tolist()], np.int32)
+    op = oracle.OraclePool(len(used), pool.d_in, pool.d_out, pool.r_max,
+                           np.array([pool.ranks[u] for u in used], np.int32), np.array(a_off, np.int64),
+                           np.array(b_off, np.int64), np.concatenate(A), np.concatenate(B),
+                           pool.scales[used].astype(np.float64))
+    x = p.x.float().cpu().double().numpy()
+    Wm = p.W.float().cpu().double().numpy()
+    threads = oracle.max_threads()
+    n_done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.layer(x, Wm, ids, op, threads=threads)
+        n_done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=round(n_done * w.n_rows / el, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"full decode batch ({w.n_rows} rows, q 4096->4096, r16, 20 adapters, base + LoRA) "
+                       f"x{n_done} passes, {el:.1f} s, fp64")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this layer is built and measured on a single MI355X; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    log("bench: decode q_proj (BGMV) ...")
+    dec, w0 = bench_decode(torch, args)
+    extra = {}
+    for name in [s for s in args.workloads.split(",") if s]:
+        log(f"bench: workload {name} ...")
+        extra[name] = bench_multi(torch, args, name)
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu:
+        log("bench: cpu baseline (oracle) ...")
+        # the oracle needs W in [d_in, d_out]; regenerate replica 0's values
+        from lora_bgmv_shrink_amd import workloads as wl
+        wc = wl.decode_q_proj(device=torch.device("cuda:0"))
+        cpu = cpu_baseline(wc, args.cpu_seconds)
+
+    line = {
+        "metric": "LoRA-layer tokens/s; adapter-term HBM GB/s (% peak), BGMV decode + SGMV prefill",
+        "value": round(dec["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["sec_step"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_bgmv_q4096_r16_pool250_rows32", "rows": 32, "d_in": 4096,
+                   "d_out": 4096, "rank": 16, "pool": 250, "distinct_adapters": 20, "base_only_rows": 3,
+                   "w_layout": "out_in", "replicas": args.replicas, "graph": True},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "kernels_us": dec["kernels_us"],
+        "adapter_term": dec["adapter_term"],
+        "gpu_step_us": round(dec["gpu_step_s"] * 1e6, 3),
+        "workloads": extra,
+    }
+    if cpu:
+        line["gpu_over_cpu"] = round(line["value"] / cpu["value"], 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

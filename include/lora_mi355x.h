@@ -230,6 +230,19 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx,
                                void* y, lora_dtype_t y_dtype, int64_t ldy,
                                lora_mode_t mode, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The second half of lora_layer_apply on its own, one launch:
+ *   y = x W + s * t B[ids]   (t from lora_bgmv_shrink or lora_sgmv_shrink),
+ *   y = x W                  when t is NULL (the base-only product).
+ * Same argument rules as lora_layer_apply; t [n_rows, ldt] fp32 with
+ * ldt >= r_max.  No workspace.  The base-only form measures what the
+ * adapters add to a step ("Serving many LoRA adapters" (blog.ecitis.org),
+ * section "What to measure": adapter overhead fraction). */
+lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx,
+                                    const void* W, int64_t ldw, lora_w_layout_t w_layout,
+                                    const int32_t* ids, const float* t, int64_t ldt,
+                                    int32_t n_rows, void* y, lora_dtype_t y_dtype, int64_t ldy,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,7 @@ EXPORTS = [
     "lora_pool_destroy", "lora_pool_param_count", "lora_pool_last_error", "lora_workspace_clear",
     "lora_segments_workspace", "lora_segments_build", "lora_bgmv_shrink_workspace", "lora_bgmv_shrink",
     "lora_bgmv_expand", "lora_sgmv_shrink", "lora_sgmv_expand", "lora_layer_workspace",
-    "lora_layer_apply",
+    "lora_layer_apply", "lora_base_gemm_expand",
 ]
 
 
@@ -73,6 +73,7 @@ def _load():
         "lora_sgmv_expand": (st, [p, p, i64, p, i32, p, st, i64, ctypes.c_int, p]),
         "lora_layer_workspace": (st, [p, i32, st, p]),
         "lora_layer_apply": (st, [p, p, i64, p, i64, st, p, p, i32, p, st, i64, st, p, sz, p]),
+        "lora_base_gemm_expand": (st, [p, p, i64, p, i64, st, p, p, i64, i32, p, st, i64, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -340,4 +341,15 @@ def lora_layer_apply(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Te
                                  None if cs is None else ctypes.byref(cs), n, _ptr(y), _dt(y.dtype), _ld(y),
                                  mode, _ptr(ws), 0 if ws is None else ws.numel(),
                                  ctypes.c_void_p(_stream(x.device))), "lora_layer_apply")
+    return y
+
+
+def lora_base_gemm_expand(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
+                          t: Optional[torch.Tensor], w_layout: int = LORA_W_IN_OUT,
+                          y: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    n = ids.numel()
+    y = _y_out(pool, n, y, y_dtype, x.device, False)
+    _check(_lib.lora_base_gemm_expand(pool.handle, _ptr(x), _ld(x), _ptr(W), _ld(W), w_layout, _ptr(ids),
+                                      _ptr(t), 0 if t is None else _ld(t), n, _ptr(y), _dt(y.dtype), _ld(y),
+                                      ctypes.c_void_p(_stream(x.device))), "lora_base_gemm_expand")
     return y

@@ -164,10 +164,12 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
         for (size_t i = 1; i < sa.size(); ++i)
             if (sa[i].first < sa[i - 1].second || sb[i].first < sb[i - 1].second) return LORA_E_INVALID;
     }
-    bool vec_a = true, vec_b = ((int64_t)d_out * eb) % 16 == 0;
+    bool vec_a = true, vec_b = ((int64_t)d_out * eb) % 16 == 0, stream_ok = true;
+    const int ve = 16 / eb;
     for (int32_t u = 0; u < n_adapters; ++u) {
         vec_a = vec_a && (ao[u] * eb) % 16 == 0;
         vec_b = vec_b && (bo[u] * eb) % 16 == 0;
+        stream_ok = stream_ok && rk[u] % ve == 0 && (512 * ve) % rk[u] == 0;
     }
 
     const size_t o_ranks = 0;
@@ -207,6 +209,7 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
     p->dev.r_max = r_max;
     p->dev.vec_a = vec_a ? 1 : 0;
     p->dev.vec_b = vec_b ? 1 : 0;
+    p->dev.stream_ok = stream_ok ? 1 : 0;
     *out = p;
     return LORA_OK;
 }
@@ -398,6 +401,40 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
                                    stream);
     }
     if (e != hipSuccess) return LORA_E_DEVICE;
+    GemmArgs g;
+    g.x = x;
+    g.ldx = ldx;
+    g.W = W;
+    g.ldw = ldw;
+    g.w_out_in = (w_layout == LORA_W_OUT_IN) ? 1 : 0;
+    g.ids = ids;
+    g.n_rows = n_rows;
+    g.t = t;
+    g.ldt = ldt;
+    g.y = y;
+    g.ldy = ldy;
+    g.vec_x = true;
+    g.vec_w = true;
+    return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
+}
+
+lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
+                                    int64_t ldw, lora_w_layout_t w_layout, const int32_t* ids,
+                                    const float* t, int64_t ldt, int32_t n_rows, void* y,
+                                    lora_dtype_t y_dtype, int64_t ldy, hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
+    if (w_layout != LORA_W_IN_OUT && w_layout != LORA_W_OUT_IN) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    const PoolDev& P = pool->dev;
+    const int eb = elem_bytes(pool->dtype);
+    const int ey = elem_bytes(y_dtype);
+    if (!x || !W || !ids || !y) return LORA_E_INVALID;
+    if (t && ldt < P.r_max) return LORA_E_INVALID;
+    const int64_t w_min = (w_layout == LORA_W_IN_OUT) ? P.d_out : P.d_in;
+    if (ldx < P.d_in || ldw < w_min || ldy < P.d_out) return LORA_E_INVALID;
+    if (!al16(x) || !al16(W) || !al16(y) || !ld_ok(ldx, P.d_in, eb) || !ld_ok(ldw, w_min, eb) ||
+        !ld_ok(ldy, P.d_out, ey))
+        return LORA_E_UNSUPPORTED;
     GemmArgs g;
     g.x = x;
     g.ldx = ldx;

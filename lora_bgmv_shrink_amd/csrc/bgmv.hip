@@ -13,106 +13,153 @@
 namespace lora {
 namespace {
 
-constexpr int SHRINK_THREADS = 256;
-constexpr int SHRINK_A_BYTES = 32768;   // LDS staging of one slice of A
-constexpr int SHRINK_KS_MAX = 256;      // k-rows per slice (x staged in LDS)
-constexpr int SHRINK_PART_STRIDE = 64;  // floats per (row, slice) partial
+constexpr int SHRINK_THREADS = 512;     // one workgroup (8 waves) per row
+constexpr int SHRINK_LOADS = 16;        // 16-byte loads of A in flight per thread
+constexpr int SHRINK_X_FLOATS = 8192;   // x chunk staged in LDS (32 KiB)
+constexpr int SHRINK_A_ELEMS = 8192;    // generic path: A chunk staged in LDS
 
-// Shrink.  Workgroup b handles row i = b / S, K-slice s = b % S:
-//   partial_s[j] = sum_{k in slice} x_i[k] * A_a[k][j]
-// The slice of A is contiguous ([Ks, r] row-major) and is copied to LDS with
-// 16-byte loads; thread (j, g) then sums k = g, g + G, ... for column j, and
-// the G partial sums are added in order.  With S > 1 the slices of a row meet
-// in a last-arriver step: each slice writes its partial to the workspace, and
-// the slice that increments the row's counter last adds the S partials in
-// slice order (deterministic) and resets the counter to zero.
+// Streaming shrink, for ranks where 16-byte vectors tile every k-row
+// (r % VE == 0) and a pass of the workgroup covers whole k-rows
+// ((SHRINK_THREADS * VE) % r == 0): r in {8, 16, 32, 64} for bf16,
+// {4, 8, 16, 32, 64} for fp32.
+//
+// Row i reads A_a ([d_in, r] row-major, contiguous) once, front to back:
+// thread t owns the VE columns j0 = (t % G) * VE (G = r / VE vectors per
+// k-row) of k-rows t / G, t / G + KPT, ... (KPT = SHRINK_THREADS / G), and
+// keeps SHRINK_LOADS of those loads in flight while the matching x chunk
+// is staged in LDS.  Per-thread partial sums are folded over the lanes of a
+// wave that share j0 (butterfly), then over the waves in order; the result
+// does not depend on timing.
 template <typename T>
-__global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink(PoolDev P, const T* __restrict__ x,
-                                                               int64_t ldx,
-                                                               const int32_t* __restrict__ ids,
-                                                               float* __restrict__ t, int64_t ldt,
-                                                               int S, int Ks,
-                                                               float* __restrict__ part,
-                                                               int32_t* __restrict__ cnt) {
-    __shared__ float xs[SHRINK_KS_MAX];
-    __shared__ __attribute__((aligned(16))) T as[SHRINK_A_BYTES / sizeof(T)];
-    __shared__ float red[SHRINK_THREADS];
-    __shared__ int is_last;
+__global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_stream(PoolDev P, const T* __restrict__ x,
+                                                                      int64_t ldx,
+                                                                      const int32_t* __restrict__ ids,
+                                                                      float* __restrict__ t, int64_t ldt) {
+    constexpr int VE = 16 / sizeof(T);
+    __shared__ float xs[SHRINK_X_FLOATS];
+    __shared__ float red[SHRINK_THREADS / 64][64];
 
     const int tid = threadIdx.x;
-    const int i = blockIdx.x / S;
-    const int s = blockIdx.x - i * S;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int i = blockIdx.x;
     const int a = ids[i];
     const int r_max = P.r_max;
     float* ti = t + (int64_t)i * ldt;
-
     if (!id_ok(a, P.n_adapters)) {
-        if (s == 0) {
-            if (tid == 0 && a != -1) flag_bad_id(P.err);
-            if (tid < r_max) ti[tid] = 0.f;
-        }
+        if (tid == 0 && a != -1) flag_bad_id(P.err);
+        if (tid < r_max) ti[tid] = 0.f;
         return;
     }
     const int r = P.ranks[a];
-    const int k0 = s * Ks;
-    const int k1 = min(P.d_in, k0 + Ks);
-    const int nk = k1 - k0;
+    const int G = r / VE;
+    const int KPT = SHRINK_THREADS / G;
+    const int KC = KPT * SHRINK_LOADS;   // k-rows per chunk (<= SHRINK_X_FLOATS)
+    const int jv = tid % G;
+    const int ksub = tid / G;
+    const int d_in = P.d_in;
+    const T* Au = (const T*)P.A + P.a_off[a] + jv * VE;
+    const T* xi = x + (int64_t)i * ldx;
 
-    const T* xi = x + (int64_t)i * ldx + k0;
-    for (int k = tid; k < nk; k += SHRINK_THREADS) xs[k] = to_f32(xi[k]);
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = 0.f;
 
-    const T* src = (const T*)P.A + P.a_off[a] + (int64_t)k0 * r;
-    const int F = nk * r;
-    constexpr int VE = 16 / sizeof(T);
-    int done = 0;
-    if (P.vec_a) {
-        const int nv = F / VE;
-        for (int v = tid; v < nv; v += SHRINK_THREADS)
-            *(uint4*)(as + v * VE) = *(const uint4*)(src + v * VE);
-        done = nv * VE;
+    for (int kc0 = 0; kc0 < d_in; kc0 += KC) {
+        uint4 av[SHRINK_LOADS];
+#pragma unroll
+        for (int l = 0; l < SHRINK_LOADS; ++l) {
+            const int k = kc0 + ksub + l * KPT;
+            av[l] = (k < d_in) ? *(const uint4*)(Au + (int64_t)k * r) : uint4{0u, 0u, 0u, 0u};
+        }
+        const int kn = min(KC, d_in - kc0);
+        for (int k = tid; k < kn; k += SHRINK_THREADS) xs[k] = to_f32(xi[kc0 + k]);
+        __syncthreads();
+#pragma unroll
+        for (int l = 0; l < SHRINK_LOADS; ++l) {
+            const int kk = ksub + l * KPT;
+            const float xv = (kk < kn) ? xs[kk] : 0.f;
+            union { uint4 u; T e[VE]; } v;
+            v.u = av[l];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] += xv * to_f32(v.e[e]);
+        }
+        __syncthreads();
     }
-    for (int e = done + tid; e < F; e += SHRINK_THREADS) as[e] = src[e];
-    __syncthreads();
 
-    const int G = SHRINK_THREADS / r;
-    float acc = 0.f;
-    if (tid < G * r) {
-        const int j = tid % r;
-        const int g = tid / r;
-        for (int k = g; k < nk; k += G) acc += xs[k] * to_f32(as[k * r + j]);
+    // lanes sharing j0 differ in the lane bits >= log2(G)
+    for (int d = G; d < 64; d <<= 1)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], d, 64);
+    if (lane < G)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) red[wave][lane * VE + e] = acc[e];
+    __syncthreads();
+    if (tid < r_max) {
+        float v = 0.f;
+        if (tid < r)
+            for (int w = 0; w < SHRINK_THREADS / 64; ++w) v += red[w][tid];
+        ti[tid] = v;
     }
-    red[tid] = acc;
-    __syncthreads();
-    float v = 0.f;
-    if (tid < r)
-        for (int g = 0; g < G; ++g) v += red[g * r + tid];
+}
 
-    if (S == 1) {
-        if (tid < r_max) ti[tid] = (tid < r) ? v : 0.f;
+// Generic shrink for any rank 1..64: k-chunks of A_a are staged in LDS and
+// thread (j, g) sums column j over k = g, g + Gs, ... (Gs = threads / r),
+// then the Gs partial sums are added in order.
+template <typename T>
+__global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_lds(PoolDev P, const T* __restrict__ x,
+                                                                   int64_t ldx,
+                                                                   const int32_t* __restrict__ ids,
+                                                                   float* __restrict__ t, int64_t ldt) {
+    __shared__ __attribute__((aligned(16))) T as[SHRINK_A_ELEMS];
+    __shared__ float xs[SHRINK_A_ELEMS];
+    __shared__ float red[SHRINK_THREADS];
+
+    const int tid = threadIdx.x;
+    const int i = blockIdx.x;
+    const int a = ids[i];
+    const int r_max = P.r_max;
+    float* ti = t + (int64_t)i * ldt;
+    if (!id_ok(a, P.n_adapters)) {
+        if (tid == 0 && a != -1) flag_bad_id(P.err);
+        if (tid < r_max) ti[tid] = 0.f;
         return;
     }
-    if (tid < r) part[((int64_t)i * S + s) * SHRINK_PART_STRIDE + tid] = v;
-    __threadfence();   // every writer releases its own partial at device scope
-    __syncthreads();
-    if (tid == 0) {
-        // release our partial, acquire the others' if we arrive last
-        const int prev = __hip_atomic_fetch_add(&cnt[i], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (prev == S - 1);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __atomic_thread_fence(__ATOMIC_ACQUIRE);
-    if (tid < r_max) {
-        float sum = 0.f;
-        if (tid < r) {
-            const float* p = part + (int64_t)i * S * SHRINK_PART_STRIDE + tid;
-            for (int q = 0; q < S; ++q)
-                sum += __hip_atomic_load(p + q * SHRINK_PART_STRIDE, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+    const int r = P.ranks[a];
+    const int d_in = P.d_in;
+    const int KC = SHRINK_A_ELEMS / r / 8 * 8;   // k-rows per chunk, multiple of 8
+    const T* Au = (const T*)P.A + P.a_off[a];
+    const T* xi = x + (int64_t)i * ldx;
+    const int Gs = SHRINK_THREADS / r;
+    const int j = tid % r;
+    const int g = tid / r;
+    constexpr int VE = 16 / sizeof(T);
+    float acc = 0.f;
+    for (int k0 = 0; k0 < d_in; k0 += KC) {
+        const int nk = min(KC, d_in - k0);
+        const int F = nk * r;
+        const T* src = Au + (int64_t)k0 * r;
+        int done = 0;
+        if (P.vec_a) {   // block start 16-byte aligned and k0 * r * elem a multiple of 16
+            const int nv = F / VE;
+            for (int v = tid; v < nv; v += SHRINK_THREADS) *(uint4*)(as + v * VE) = *(const uint4*)(src + v * VE);
+            done = nv * VE;
         }
-        ti[tid] = sum;
+        for (int e = done + tid; e < F; e += SHRINK_THREADS) as[e] = src[e];
+        for (int k = tid; k < nk; k += SHRINK_THREADS) xs[k] = to_f32(xi[k0 + k]);
+        __syncthreads();
+        if (g < Gs)
+            for (int k = g; k < nk; k += Gs) acc += xs[k] * to_f32(as[k * r + j]);
+        __syncthreads();
     }
-    if (tid == 0) __hip_atomic_store(&cnt[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    red[tid] = (g < Gs) ? acc : 0.f;
+    __syncthreads();
+    if (tid < r_max) {
+        float v = 0.f;
+        if (tid < r)
+            for (int q = 0; q < Gs; ++q) v += red[q * r + tid];
+        ti[tid] = v;
+    }
 }
 
 // Expand.  One wave per (row, chunk of 64*VE output columns); lane l owns VE
@@ -194,45 +241,39 @@ __global__ __launch_bounds__(256) void k_bgmv_expand(PoolDev P, const float* __r
 }  // namespace
 
 BgmvShrinkPlan plan_bgmv_shrink(const PoolDev& P, int elem_bytes, int32_t n_rows) {
-    // Largest slice the LDS staging buffer holds at the pool's widest rank.
-    int ks_max = SHRINK_A_BYTES / (elem_bytes * P.r_max);
-    ks_max = std::min(ks_max, SHRINK_KS_MAX) / 8 * 8;
-    if (ks_max < 8) ks_max = 8;
-    // Aim for about 1024 workgroups in flight, but no slice under 128 rows.
-    int64_t want = std::max<int64_t>(1, ceil_div(1024, std::max(1, n_rows)));
-    int64_t most = std::max<int64_t>(1, ceil_div(P.d_in, 128));
-    int64_t s = std::min(want, most);
-    s = std::max<int64_t>(s, ceil_div(P.d_in, ks_max));
-    int ks = (int)align_up((size_t)ceil_div(P.d_in, s), 8);
-    if (ks > ks_max) ks = ks_max;
-    s = ceil_div(P.d_in, ks);
-    return BgmvShrinkPlan{(int32_t)s, ks};
+    (void)n_rows;
+    // The streaming kernel needs every rank in the pool to tile 16-byte
+    // vectors and whole k-rows per pass; uniform pools check one rank.
+    const int VE = 16 / elem_bytes;
+    BgmvShrinkPlan plan;
+    plan.slices = 1;
+    plan.ks = (P.vec_a && P.stream_ok) ? 1 : 0;
+    (void)VE;
+    return plan;
 }
 
-size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan& plan, int32_t n_rows) {
-    if (plan.slices <= 1 || n_rows <= 0) return 0;
-    size_t part = align_up((size_t)n_rows * plan.slices * SHRINK_PART_STRIDE * sizeof(float), 256);
-    size_t cnt = align_up((size_t)n_rows * sizeof(int32_t), 256);
-    return part + cnt;
-}
+size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan&, int32_t) { return 0; }
 
 hipError_t launch_bgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
-                              const int32_t* ids, int32_t n_rows, float* t, int64_t ldt, void* ws,
+                              const int32_t* ids, int32_t n_rows, float* t, int64_t ldt, void*,
                               const BgmvShrinkPlan& plan, hipStream_t stream) {
-    float* part = nullptr;
-    int32_t* cnt = nullptr;
-    if (plan.slices > 1) {
-        part = (float*)ws;
-        cnt = (int32_t*)((char*)ws + align_up((size_t)n_rows * plan.slices * SHRINK_PART_STRIDE *
-                                                  sizeof(float), 256));
+    dim3 grid((unsigned)n_rows);
+    const bool stream_path = plan.ks == 1;
+    if (dt == LORA_BF16) {
+        if (stream_path)
+            hipLaunchKernelGGL(k_bgmv_shrink_stream<bf16>, grid, dim3(SHRINK_THREADS), 0, stream, P,
+                               (const bf16*)x, ldx, ids, t, ldt);
+        else
+            hipLaunchKernelGGL(k_bgmv_shrink_lds<bf16>, grid, dim3(SHRINK_THREADS), 0, stream, P,
+                               (const bf16*)x, ldx, ids, t, ldt);
+    } else {
+        if (stream_path)
+            hipLaunchKernelGGL(k_bgmv_shrink_stream<float>, grid, dim3(SHRINK_THREADS), 0, stream, P,
+                               (const float*)x, ldx, ids, t, ldt);
+        else
+            hipLaunchKernelGGL(k_bgmv_shrink_lds<float>, grid, dim3(SHRINK_THREADS), 0, stream, P,
+                               (const float*)x, ldx, ids, t, ldt);
     }
-    dim3 grid((unsigned)((int64_t)n_rows * plan.slices));
-    if (dt == LORA_BF16)
-        hipLaunchKernelGGL(k_bgmv_shrink<bf16>, grid, dim3(SHRINK_THREADS), 0, stream, P,
-                           (const bf16*)x, ldx, ids, t, ldt, plan.slices, plan.ks, part, cnt);
-    else
-        hipLaunchKernelGGL(k_bgmv_shrink<float>, grid, dim3(SHRINK_THREADS), 0, stream, P,
-                           (const float*)x, ldx, ids, t, ldt, plan.slices, plan.ks, part, cnt);
     return hipGetLastError();
 }
 

@@ -33,8 +33,9 @@ struct PoolDev {
     int32_t d_in;
     int32_t d_out;
     int32_t r_max;
-    int32_t vec_a;       // every A block 16-byte aligned and rank*elem % 16 == 0
+    int32_t vec_a;       // every A block starts 16-byte aligned
     int32_t vec_b;       // every B block 16-byte aligned and d_out*elem % 16 == 0
+    int32_t stream_ok;   // every rank r: r*elem % 16 == 0 and (512*16/elem) % r == 0
 };
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -72,10 +73,10 @@ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 hipError_t launch_segments(const int32_t* ids, int32_t n_rows, int32_t n_adapters,
                            const lora_segments_t* seg, int32_t* status, hipStream_t stream);
 
-// BGMV shrink: split-K over d_in with a deterministic last-arriver sum.
+// BGMV shrink: one workgroup per row (no workspace).
 struct BgmvShrinkPlan {
-    int32_t slices;   // K slices per row
-    int32_t ks;       // k-rows per slice (multiple of 8)
+    int32_t slices;   // always 1
+    int32_t ks;       // 1: streaming kernel, 0: LDS-staged generic kernel
 };
 BgmvShrinkPlan plan_bgmv_shrink(const PoolDev& P, int elem_bytes, int32_t n_rows);
 size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan& plan, int32_t n_rows);

@@ -26,33 +26,51 @@
 namespace lora {
 namespace {
 
-template <typename T> struct MF;
-template <> struct MF<bf16> {
-    static constexpr int KSTEP = 32;
-    static constexpr int KPL = 8;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// MFMA shapes.  BLK x BLK output block, KSTEP reduction per instruction;
+// lane l supplies operand row/column l % BLK and k (l / BLK) * KPL .. + KPL.
+template <typename T, int BLK> struct MF;
+template <> struct MF<bf16, 16> {
+    static constexpr int KSTEP = 32, KPL = 8, NACC = 4;
     using frag = bf16x8_t;
+    using acc = f32x4_t;
     static __device__ __forceinline__ frag ld(const bf16* p) { return *(const bf16x8_t*)p; }
-    static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+    static __device__ __forceinline__ acc mma(frag a, frag b, acc c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
+    // output element q of lane l sits at (row, col) of the block
+    static __device__ __forceinline__ int row(int lane, int q) { return (lane >> 4) * 4 + q; }
 };
-template <> struct MF<float> {
-    static constexpr int KSTEP = 4;
-    static constexpr int KPL = 1;
+template <> struct MF<bf16, 32> {
+    static constexpr int KSTEP = 16, KPL = 8, NACC = 16;
+    using frag = bf16x8_t;
+    using acc = f32x16_t;
+    static __device__ __forceinline__ frag ld(const bf16* p) { return *(const bf16x8_t*)p; }
+    static __device__ __forceinline__ acc mma(frag a, frag b, acc c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int lane, int q) { return (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3); }
+};
+template <> struct MF<float, 16> {
+    static constexpr int KSTEP = 4, KPL = 1, NACC = 4;
     using frag = float;
+    using acc = f32x4_t;
     static __device__ __forceinline__ frag ld(const float* p) { return *p; }
-    static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+    static __device__ __forceinline__ acc mma(frag a, frag b, acc c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ int row(int lane, int q) { return (lane >> 4) * 4 + q; }
 };
 
-template <typename T_, int BM_, int BN_, int BK_, int WM_, int WN_>
+template <typename T_, int BM_, int BN_, int BK_, int WM_, int WN_, int BLK_ = 16>
 struct Cfg {
     using T = T_;
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    using M = MF<T_, BLK_>;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, BLK = BLK_;
     static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int FM = WTM / BLK, FN = WTN / BLK;
     static constexpr int VE = 16 / sizeof(T);
     static constexpr int LDK = BK + VE;
     static constexpr int A_ELEMS = BM * LDK;
@@ -61,20 +79,22 @@ struct Cfg {
     // ranks covered by one K-extension step of the LoRA epilogue: bf16 splits
     // the fp32 operand into hi + lo halves, fp32 takes it as is
     static constexpr int KH = (sizeof(T) == 2) ? BK / 2 : BK;
-    static_assert(FM >= 1 && FN >= 1, "wave tile smaller than 16x16");
-    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile not a multiple of 16");
-    static_assert(BK % MF<T>::KSTEP == 0, "BK not a multiple of the MFMA K");
+    static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA block");
+    static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile not a multiple of the MFMA block");
+    static_assert(BK % M::KSTEP == 0, "BK not a multiple of the MFMA K");
     static_assert(BK % VE == 0, "BK not a multiple of the vector width");
 };
 
 template <class C>
 struct Acc {
-    f32x4_t v[C::FM][C::FN];
+    typename C::M::acc v[C::FM][C::FN];
     __device__ __forceinline__ void zero() {
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) v[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int q = 0; q < C::M::NACC; ++q) v[i][j][q] = 0.f;
     }
 };
 
@@ -83,18 +103,18 @@ template <class C>
 __device__ __forceinline__ void mma_block(Acc<C>& acc, const typename C::T* sA,
                                           const typename C::T* sB, int wm, int wn, int lane) {
     using T = typename C::T;
-    using M = MF<T>;
-    const int lr = lane & 15;
-    const int kq = (lane >> 4) * M::KPL;
+    using M = typename C::M;
+    const int lr = lane % C::BLK;
+    const int kq = (lane / C::BLK) * M::KPL;
     const T* pa = sA + (wm * C::WTM + lr) * C::LDK + kq;
     const T* pb = sB + (wn * C::WTN + lr) * C::LDK + kq;
 #pragma unroll
     for (int kk = 0; kk < C::BK; kk += M::KSTEP) {
         typename M::frag a[C::FM], b[C::FN];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = M::ld(pa + i * 16 * C::LDK + kk);
+        for (int i = 0; i < C::FM; ++i) a[i] = M::ld(pa + i * C::BLK * C::LDK + kk);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = M::ld(pb + j * 16 * C::LDK + kk);
+        for (int j = 0; j < C::FN; ++j) b[j] = M::ld(pb + j * C::BLK * C::LDK + kk);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -383,19 +403,121 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     if (g.t) lora_kext<C>(acc, P, g.t, g.ldt, sRowA, sId, &sNext, smem, n0, tid, wm, wn, lane);
 
     TY* Y = (TY*)g.y;
-    const int lr = lane & 15;
-    const int lq = (lane >> 4) * 4;
+    const int lc = lane % C::BLK;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-            const int col = n0 + wn * C::WTN + j * 16 + lr;
+            const int col = n0 + wn * C::WTN + j * C::BLK + lc;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = m0 + wm * C::WTM + i * 16 + lq + q;
+            for (int q = 0; q < C::M::NACC; ++q) {
+                const int row = m0 + wm * C::WTM + i * C::BLK + C::M::row(lane, q);
                 if (row < g.n && col < N) Y[(int64_t)row * g.ldy + col] = from_f32<TY>(acc.v[i][j][q]);
             }
         }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny layer GEMM for decode batches (n_rows <= 64, W stored [d_out, d_in])
+// ---------------------------------------------------------------------------
+//
+// At decode sizes the base product is a stream of W with almost no reuse,
+// so the kernel is shaped for bytes in flight rather than for reuse: a
+// workgroup owns 16 output columns (16 rows of W^T) and all batch rows; its
+// NW waves split K, and every lane loads its MFMA operands straight from
+// global memory into registers, U K-steps at a time (U 16-byte loads of W
+// in flight per lane, with the matching x fragments, which stay in L2).
+// The per-wave partial tiles are added in LDS in wave order, then the scaled
+// expand s * t_m B_a[:, n] is added per row and y is rounded once.
+
+__device__ __forceinline__ bf16x8_t load8_bf16(const bf16* p, int valid) {
+    if (valid >= 8) return *(const bf16x8_t*)p;
+    union { bf16x8_t v; bf16 e[8]; } u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u.e[e] = (e < valid) ? p[e] : (bf16)0;
+    return u.v;
+}
+
+template <typename TY, int MB, int NW>
+__global__ __launch_bounds__(NW * 64) void k_gemm_skinny(PoolDev P, GemmDev g) {
+    // K-steps loaded per pass: bounded by the registers a lane has at NW waves
+    constexpr int U = (NW >= 16) ? ((MB >= 2) ? 4 : 8) : ((MB >= 4) ? 8 : 16);
+    constexpr int MT = MB * 16;
+    __shared__ float red[NW][MT][17];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int K = P.d_in;
+    const int N = P.d_out;
+    const int M = g.n;
+    const bf16* X = (const bf16*)g.x;
+    const bf16* Wt = (const bf16*)g.W;
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const bool n_ok = n0 + lr < N;
+    const bf16* wrow = Wt + (int64_t)(n_ok ? n0 + lr : 0) * g.ldw;
+
+    f32x4_t acc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = (K + 31) / 32;
+    const int spw = (nsteps + NW - 1) / NW;
+    const int s0 = wave * spw;
+    const int s1 = min(nsteps, s0 + spw);
+    for (int sb = s0; sb < s1; sb += U) {
+        bf16x8_t bw[U];
+        bf16x8_t ax[U][MB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (sb + u) * 32 + kq;
+            const int valid = (sb + u < s1) ? min(8, K - k) : 0;
+            bw[u] = (n_ok && valid > 0) ? load8_bf16(wrow + k, valid) : bf16x8_t{};
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int m = i * 16 + lr;
+                ax[u][i] = (m < M && valid > 0) ? load8_bf16(X + (int64_t)m * g.ldx + k, valid) : bf16x8_t{};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u][i], bw[u], acc[i], 0, 0, 0);
+    }
+
+    const int lq = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[wave][i * 16 + lq + q][lr] = acc[i][q];
+    __syncthreads();
+
+    TY* Y = (TY*)g.y;
+    for (int o = tid; o < MT * 16; o += NW * 64) {
+        const int m = o >> 4;
+        const int n = o & 15;
+        const int col = n0 + n;
+        if (m >= M || col >= N) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red[w][m][n];
+        const int a = g.ids[m];
+        if (id_ok(a, P.n_adapters)) {
+            if (g.t) {
+                const int r = P.ranks[a];
+                const bf16* Bu = (const bf16*)P.B + P.b_off[a] + col;
+                const float* tm = g.t + (int64_t)m * g.ldt;
+                float e = 0.f;
+                for (int j = 0; j < r; ++j) e += tm[j] * to_f32(Bu[(int64_t)j * N]);
+                v += P.scales[a] * e;
+            }
+        } else if (a != -1 && blockIdx.x == 0) {
+            flag_bad_id(P.err);
+        }
+        Y[(int64_t)m * g.ldy + col] = from_f32<TY>(v);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -472,16 +594,15 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
         mma_block<C>(acc, sA, sB, wm, wn, lane);
     }
 
-    const int lr = lane & 15;
-    const int lq = (lane >> 4) * 4;
+    const int lc = lane % C::BLK;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-            const int col = wn * C::WTN + j * 16 + lr;
+            const int col = wn * C::WTN + j * C::BLK + lc;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = wm * C::WTM + i * 16 + lq + q;
+            for (int q = 0; q < C::M::NACC; ++q) {
+                const int m = wm * C::WTM + i * C::BLK + C::M::row(lane, q);
                 if (m < cnt && col < r_max) t[(int64_t)sRow[m] * ldt + col] = acc.v[i][j][q];
             }
         }
@@ -543,16 +664,15 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_expand(PoolDev P, const float* _
     acc.zero();
     if (ok) lora_kext<C>(acc, P, t, ldt, sRow, sId, &sNext, smem, n0, tid, wm, wn, lane);
 
-    const int lr = lane & 15;
-    const int lq = (lane >> 4) * 4;
+    const int lc = lane % C::BLK;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-            const int col = n0 + wn * C::WTN + j * 16 + lr;
+            const int col = n0 + wn * C::WTN + j * C::BLK + lc;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = wm * C::WTM + i * 16 + lq + q;
+            for (int q = 0; q < C::M::NACC; ++q) {
+                const int m = wm * C::WTM + i * C::BLK + C::M::row(lane, q);
                 if (m < cnt && col < N) {
                     TY* p = y + (int64_t)sRow[m] * ldy + col;
                     float v = acc.v[i][j][q];
@@ -567,7 +687,7 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_expand(PoolDev P, const float* _
 // Tile configurations
 // ---------------------------------------------------------------------------
 
-using GemmBig = Cfg<bf16, 128, 128, 64, 2, 2>;
+using GemmBig = Cfg<bf16, 128, 128, 64, 2, 2, 32>;
 using GemmMid = Cfg<bf16, 64, 64, 64, 2, 2>;
 using GemmSmall = Cfg<bf16, 32, 64, 64, 2, 2>;
 using GemmF32 = Cfg<float, 64, 64, 32, 2, 2>;
@@ -599,13 +719,41 @@ hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename TY, int MB>
+hipError_t run_skinny(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
+    GemmDev g;
+    g.x = a.x;
+    g.ldx = a.ldx;
+    g.W = a.W;
+    g.ldw = a.ldw;
+    g.ids = a.ids;
+    g.n = a.n_rows;
+    g.t = a.t;
+    g.ldt = a.ldt;
+    g.y = a.y;
+    g.ldy = a.ldy;
+    g.tiles_m = 1;
+    g.tiles_n = (int32_t)ceil_div(P.d_out, 16);
+    dim3 grid((unsigned)g.tiles_n);
+    // fewer column tiles than CUs: more waves per tile to keep bytes in flight
+    if (g.tiles_n < 256)
+        hipLaunchKernelGGL((k_gemm_skinny<TY, MB, 16>), grid, dim3(16 * 64), 0, stream, P, g);
+    else
+        hipLaunchKernelGGL((k_gemm_skinny<TY, MB, 8>), grid, dim3(8 * 64), 0, stream, P, g);
+    return hipGetLastError();
+}
+
 template <typename TY>
 hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
+    if (a.w_out_in && a.n_rows <= 64) {
+        if (a.n_rows <= 16) return run_skinny<TY, 1>(P, a, stream);
+        if (a.n_rows <= 32) return run_skinny<TY, 2>(P, a, stream);
+        return run_skinny<TY, 4>(P, a, stream);
+    }
     // Largest tile that still gives about one workgroup per CU.
-    const int64_t n_big = ceil_div(a.n_rows, GemmBig::BM) * ceil_div(P.d_out, GemmBig::BN);
-    const int64_t n_mid = ceil_div(a.n_rows, GemmMid::BM) * ceil_div(P.d_out, GemmMid::BN);
-    if (n_big >= 256) return run_gemm<GemmBig, TY>(P, a, stream);
-    if (n_mid >= 256 || a.n_rows > 32) return run_gemm<GemmMid, TY>(P, a, stream);
+    auto tiles = [&](int bm, int bn) { return ceil_div(a.n_rows, bm) * ceil_div(P.d_out, bn); };
+    if (tiles(GemmBig::BM, GemmBig::BN) >= 200) return run_gemm<GemmBig, TY>(P, a, stream);
+    if (tiles(GemmMid::BM, GemmMid::BN) >= 128 || a.n_rows > 32) return run_gemm<GemmMid, TY>(P, a, stream);
     return run_gemm<GemmSmall, TY>(P, a, stream);
 }
 

@@ -285,12 +285,13 @@ def mixed_rank_ids(seed=4):
     return ids, ranks, block, pre_ids
 
 
-def decode_q_proj(device="cuda", dtype=torch.bfloat16, seed=1) -> Workload:
+def decode_q_proj(device="cuda", dtype=torch.bfloat16, seed=1, value_seed=None) -> Workload:
     """32 decode rows, 20 distinct adapters out of a uniform rank-16 pool of 250,
-    3 base-only rows (10%), one 4096->4096 projection."""
+    3 base-only rows (10%), one 4096->4096 projection.  ``value_seed`` draws
+    other values for the same batch (replicas of the layer)."""
     ids = decode_q_proj_ids(seed)
     n_rows, n_pool, n_distinct, n_base = len(ids), 250, 20, int((ids == -1).sum())
-    g = _gen(device, seed)
+    g = _gen(device, seed if value_seed is None else value_seed)
     d_in = d_out = 4096
     x = _randn(g, (n_rows, d_in), X_DIV, dtype, device)
     W = _randn(g, (d_in, d_out), W_DIV, dtype, device)
