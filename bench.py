@@ -3,9 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step is one pass of the layer over one synthetic batch: the shrink
-(x -> xA) for every row, then the base GEMM with the scaled expand fused into
-its epilogue.  The headline workload is the decode batch: one 4096->4096
+One step is one pass of the layer over one synthetic batch (lora_layer_apply's
+launch sequence): for the decode batch, a stream launch (split-K partial
+products of x W and the BGMV shrink partials x A[ids]) and a finish launch
+(sum of partials plus the scaled expand, y rounded once).  The headline workload is the decode batch: one 4096->4096
 q projection, rank 16, a uniform pool of 250 adapters, 32 single-token rows
 on 20 distinct adapters plus 3 base-only rows, bf16 inputs with fp32
 accumulation.  Successive steps rotate over 8 replicas of the layer
@@ -15,10 +16,10 @@ layers of a model would.  Steps are captured in HIP graphs and replayed.
 
 The JSON line carries:
   value        tokens/s of the whole step (wall clock around exactly K steps)
-  roofline     the dominant kernel (base GEMM + fused expand) against HBM
-               peak, from its average launch duration (HIP events)
-  adapter_term the shrink kernel's algorithmic bytes/s and the adapter
-               overhead fraction (layer time minus base-only time)
+  roofline     the dominant kernel (the stream launch) against HBM peak, from
+               its average launch duration (HIP events)
+  adapter_term the adapter overhead fraction (step time minus base-only step
+               time) and the standalone BGMV shrink's algorithmic bytes/s
   cpu_baseline the fp64 oracle on the host cores, on a bounded sample
   workloads    the other four workloads (skewed 8B decode, 70B prefill,
                mixed-rank 70B ragged and padded), measured the same way
@@ -123,33 +124,32 @@ def bench_decode(torch, args):
         p = w.projections[0]
         pool = make_pool(b, p.pool)
         Wt = p.W.t().contiguous()
-        del p.W
+        p.W = None
         n = w.n_rows
         ids = torch.as_tensor(w.ids, device=dev)
-        t = torch.zeros((n, p.pool.r_max), dtype=torch.float32, device=dev)
         y = torch.zeros((n, p.d_out), dtype=torch.bfloat16, device=dev)
         yb = torch.zeros_like(y)
-        ws = torch.zeros(max(b.lora_bgmv_shrink_workspace(pool, n), 16), dtype=torch.uint8, device=dev)
-        reps.append(dict(w=w, p=p, pool=pool, Wt=Wt, ids=ids, t=t, y=y, yb=yb, ws=ws))
+        ws = torch.zeros(b.lora_decode_workspace(pool, n, True), dtype=torch.uint8, device=dev)
+        wsb = torch.zeros(b.lora_decode_workspace(pool, n, False), dtype=torch.uint8, device=dev)
+        reps.append(dict(w=w, p=p, pool=pool, Wt=Wt, ids=ids, y=y, yb=yb, ws=ws, wsb=wsb))
     w0, p0 = reps[0]["w"], reps[0]["p"]
     n = w0.n_rows
 
-    def shrink(r):
-        b.lora_bgmv_shrink(r["pool"], r["p"].x, r["ids"], t=r["t"], ws=r["ws"])
+    def stream(r):
+        b.lora_decode_stream(r["pool"], r["p"].x, r["Wt"], r["ids"], r["ws"], True)
 
-    def gemm(r):
-        b.lora_base_gemm_expand(r["pool"], r["p"].x, r["Wt"], r["ids"], r["t"], w_layout=b.LORA_W_OUT_IN,
-                                y=r["y"])
+    def finish(r):
+        b.lora_decode_finish(r["pool"], r["ids"], r["ws"], r["y"], True)
 
-    def base_only(r):
-        b.lora_base_gemm_expand(r["pool"], r["p"].x, r["Wt"], r["ids"], None, w_layout=b.LORA_W_OUT_IN,
-                                y=r["yb"])
+    def base_step(r):
+        b.lora_decode_stream(r["pool"], r["p"].x, r["Wt"], r["ids"], r["wsb"], False)
+        b.lora_decode_finish(r["pool"], r["ids"], r["wsb"], r["yb"], False)
 
     def step(r):
-        shrink(r)
-        gemm(r)
+        stream(r)
+        finish(r)
 
-    # the step is lora_layer_apply's kernel sequence; check it gives the same bits
+    # the step is lora_layer_apply's launch sequence; check it gives the same bits
     r0 = reps[0]
     step(r0)
     y_ref = b.lora_layer_apply(r0["pool"], r0["p"].x, r0["Wt"], r0["ids"], w_layout=b.LORA_W_OUT_IN,
@@ -178,13 +178,19 @@ def bench_decode(torch, args):
 
     # ---- per-kernel launch durations (graphs of R back-to-back launches) ----
     kr = args.kernel_reps
-    g_gemm = capture(torch, lambda: [gemm(r) for r in reps])
-    g_shr = capture(torch, lambda: [shrink(r) for r in reps])
-    g_base = capture(torch, lambda: [base_only(r) for r in reps])
-    d_gemm = time_graph(torch, g_gemm, kr) / R
-    d_shr = time_graph(torch, g_shr, kr) / R
+    g_stream = capture(torch, lambda: [stream(r) for r in reps])
+    g_finish = capture(torch, lambda: [finish(r) for r in reps])
+    g_base = capture(torch, lambda: [base_step(r) for r in reps])
+    d_stream = time_graph(torch, g_stream, kr) / R
+    d_finish = time_graph(torch, g_finish, kr) / R
     d_base = time_graph(torch, g_base, kr) / R
     d_step = time_graph(torch, g_full, max(1, kr // 2)) / R
+
+    # the standalone BGMV shrink entry point on the same batch
+    for r in reps:
+        r["t"] = torch.zeros((n, r["p"].pool.r_max), dtype=torch.float32, device=dev)
+    g_shr = capture(torch, lambda: [b.lora_bgmv_shrink(r["pool"], r["p"].x, r["ids"], t=r["t"]) for r in reps])
+    d_shr = time_graph(torch, g_shr, kr) / R
 
     pool = p0.pool
     bA, U = distinct_bytes(pool, w0.ids, "A")
@@ -194,25 +200,28 @@ def bench_decode(torch, args):
     y_b = n * pool.d_out * eb
     t_b = n * pool.r_max * 4
     w_b = pool.d_in * pool.d_out * eb
-    gemm_bytes = w_b + bB + x_b + t_b + y_b + n * 4
+    stream_bytes = w_b + bA + x_b + n * 4
     shrink_bytes = bA + x_b + t_b + n * 4
-    achieved = gemm_bytes / d_gemm / 1e9
+    achieved = stream_bytes / d_stream / 1e9
     out = dict(
         sec_step=sec_step,
         tokens_per_s=n / sec_step,
         gpu_step_s=d_step,
-        kernels_us=dict(shrink=d_shr * 1e6, base_gemm_expand=d_gemm * 1e6, base_only_gemm=d_base * 1e6),
+        kernels_us=dict(decode_stream=round(d_stream * 1e6, 3), decode_finish=round(d_finish * 1e6, 3),
+                        base_only_step=round(d_base * 1e6, 3), bgmv_shrink_standalone=round(d_shr * 1e6, 3)),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                      kernel="k_layer_gemm (base GEMM + fused LoRA expand)",
-                      bytes_per_launch=gemm_bytes, avg_launch_us=round(d_gemm * 1e6, 3)),
+                      kernel="k_decode_stream (split-K base partials + BGMV shrink partials)",
+                      bytes_per_launch=stream_bytes, avg_launch_us=round(d_stream * 1e6, 3)),
         adapter_term=dict(
             distinct_adapters=U,
-            shrink_bytes=shrink_bytes, shrink_us=round(d_shr * 1e6, 3),
-            shrink_GBps=round(shrink_bytes / d_shr / 1e9, 1),
-            shrink_frac_hbm=round(shrink_bytes / d_shr / 1e9 / HBM_PEAK_GBS, 4),
             adapter_bytes=bA + bB,
+            step_us=round(d_step * 1e6, 3), base_only_step_us=round(d_base * 1e6, 3),
             overhead_fraction=round(max(0.0, (d_step - d_base) / d_step), 4),
+            layer_GBps=round((w_b + bA + bB + x_b + y_b) / d_step / 1e9, 1),
+            bgmv_shrink_bytes=shrink_bytes, bgmv_shrink_us=round(d_shr * 1e6, 3),
+            bgmv_shrink_GBps=round(shrink_bytes / d_shr / 1e9, 1),
+            bgmv_shrink_frac_hbm=round(shrink_bytes / d_shr / 1e9 / HBM_PEAK_GBS, 4),
         ),
     )
     return out, w0

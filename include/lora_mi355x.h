@@ -230,18 +230,46 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx,
                                void* y, lora_dtype_t y_dtype, int64_t ldy,
                                lora_mode_t mode, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* The second half of lora_layer_apply on its own, one launch:
+/* The second half of lora_layer_apply on its own:
  *   y = x W + s * t B[ids]   (t from lora_bgmv_shrink or lora_sgmv_shrink),
  *   y = x W                  when t is NULL (the base-only product).
  * Same argument rules as lora_layer_apply; t [n_rows, ldt] fp32 with
- * ldt >= r_max.  No workspace.  The base-only form measures what the
- * adapters add to a step ("Serving many LoRA adapters" (blog.ecitis.org),
- * section "What to measure": adapter overhead fraction). */
+ * ldt >= r_max.  The workspace (lora_base_gemm_expand_workspace) holds the
+ * scaled, split copy of t that the GEMM reads as extra K-blocks; with t NULL
+ * no workspace is needed.  The base-only form measures what the adapters add
+ * to a step ("Serving many LoRA adapters" (blog.ecitis.org), section "What
+ * to measure": adapter overhead fraction). */
+lora_status_t lora_base_gemm_expand_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes);
 lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx,
                                     const void* W, int64_t ldw, lora_w_layout_t w_layout,
                                     const int32_t* ids, const float* t, int64_t ldt,
                                     int32_t n_rows, void* y, lora_dtype_t y_dtype, int64_t ldy,
-                                    hipStream_t stream);
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Decode layer in two launches                                            */
+/* ---------------------------------------------------------------------- */
+
+/* For decode batches (bf16 pool, 1 <= n_rows <= 64, W stored LORA_W_OUT_IN)
+ * lora_layer_apply in BGMV mode runs as these two launches; they are
+ * exported so callers can place other work between them or time them.
+ *   lora_decode_stream: partial base products x W over K slices, and, when
+ *     with_lora != 0, the BGMV shrink of every row (each row gathers its own
+ *     adapter's A) over K slices, all into the workspace;
+ *   lora_decode_finish: y = sum of the base partials + s * (sum of the
+ *     shrink partials) B[ids], rounded once into y (with_lora = 0: y = x W).
+ * Both calls must see the same pool, ids, n_rows, with_lora and workspace;
+ * the workspace holds fp32 partial sums only (no zeroing needed).
+ * Sums run in a fixed order, so results are identical from run to run.
+ * ("Multi-LoRA batching and adapter paging", section "Walking through a
+ * batch": W is read once for all rows; the adapter term per row.) */
+lora_status_t lora_decode_workspace(lora_pool_t pool, int32_t n_rows, int with_lora, size_t* bytes);
+lora_status_t lora_decode_stream(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
+                                 int64_t ldw, const int32_t* ids, int32_t n_rows, int with_lora,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+lora_status_t lora_decode_finish(lora_pool_t pool, const int32_t* ids, int32_t n_rows, int with_lora,
+                                 void* y, lora_dtype_t y_dtype, int64_t ldy, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,9 @@ EXPORTS = [
     "lora_pool_destroy", "lora_pool_param_count", "lora_pool_last_error", "lora_workspace_clear",
     "lora_segments_workspace", "lora_segments_build", "lora_bgmv_shrink_workspace", "lora_bgmv_shrink",
     "lora_bgmv_expand", "lora_sgmv_shrink", "lora_sgmv_expand", "lora_layer_workspace",
-    "lora_layer_apply", "lora_base_gemm_expand",
+    "lora_layer_apply", "lora_base_gemm_expand_workspace", "lora_base_gemm_expand", "lora_decode_workspace",
+    "lora_decode_stream",
+    "lora_decode_finish",
 ]
 
 
@@ -73,7 +75,11 @@ def _load():
         "lora_sgmv_expand": (st, [p, p, i64, p, i32, p, st, i64, ctypes.c_int, p]),
         "lora_layer_workspace": (st, [p, i32, st, p]),
         "lora_layer_apply": (st, [p, p, i64, p, i64, st, p, p, i32, p, st, i64, st, p, sz, p]),
-        "lora_base_gemm_expand": (st, [p, p, i64, p, i64, st, p, p, i64, i32, p, st, i64, p]),
+        "lora_base_gemm_expand_workspace": (st, [p, i32, p]),
+        "lora_base_gemm_expand": (st, [p, p, i64, p, i64, st, p, p, i64, i32, p, st, i64, p, sz, p]),
+        "lora_decode_workspace": (st, [p, i32, ctypes.c_int, p]),
+        "lora_decode_stream": (st, [p, p, i64, p, i64, p, i32, ctypes.c_int, p, sz, p]),
+        "lora_decode_finish": (st, [p, p, i32, ctypes.c_int, p, st, i64, p, sz, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -344,12 +350,44 @@ def lora_layer_apply(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Te
     return y
 
 
+def lora_base_gemm_expand_workspace(pool: Pool, n_rows: int) -> int:
+    v = ctypes.c_size_t()
+    _check(_lib.lora_base_gemm_expand_workspace(pool.handle, n_rows, ctypes.byref(v)),
+           "lora_base_gemm_expand_workspace")
+    return v.value
+
+
 def lora_base_gemm_expand(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
                           t: Optional[torch.Tensor], w_layout: int = LORA_W_IN_OUT,
-                          y: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+                          y: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None,
+                          ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     n = ids.numel()
     y = _y_out(pool, n, y, y_dtype, x.device, False)
+    if t is not None and ws is None:
+        ws = _workspace(lora_base_gemm_expand_workspace(pool, n), x.device)
     _check(_lib.lora_base_gemm_expand(pool.handle, _ptr(x), _ld(x), _ptr(W), _ld(W), w_layout, _ptr(ids),
                                       _ptr(t), 0 if t is None else _ld(t), n, _ptr(y), _dt(y.dtype), _ld(y),
+                                      _ptr(ws), 0 if ws is None else ws.numel(),
                                       ctypes.c_void_p(_stream(x.device))), "lora_base_gemm_expand")
+    return y
+
+
+def lora_decode_workspace(pool: Pool, n_rows: int, with_lora: bool = True) -> int:
+    v = ctypes.c_size_t()
+    _check(_lib.lora_decode_workspace(pool.handle, n_rows, int(bool(with_lora)), ctypes.byref(v)),
+           "lora_decode_workspace")
+    return v.value
+
+
+def lora_decode_stream(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, ws: torch.Tensor,
+                       with_lora: bool = True):
+    _check(_lib.lora_decode_stream(pool.handle, _ptr(x), _ld(x), _ptr(W), _ld(W), _ptr(ids), ids.numel(),
+                                   int(bool(with_lora)), _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(x.device))),
+           "lora_decode_stream")
+
+
+def lora_decode_finish(pool: Pool, ids: torch.Tensor, ws: torch.Tensor, y: torch.Tensor, with_lora: bool = True):
+    _check(_lib.lora_decode_finish(pool.handle, _ptr(ids), ids.numel(), int(bool(with_lora)), _ptr(y), _dt(y.dtype),
+                                   _ld(y), _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(y.device))),
+           "lora_decode_finish")
     return y

@@ -33,6 +33,12 @@ lora_status_t dev_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA
 // Rank stride of the fp32 intermediate t inside layer workspaces.
 int64_t t_stride(int32_t r_max) { return (int64_t)align_up((size_t)r_max, 4); }
 
+// Bytes of the GEMM's K-extension operand for n_rows rows.
+size_t ext_bytes(const lora_pool_s* pool, int32_t n_rows) {
+    const int eb = pool->dtype == LORA_BF16 ? 2 : 4;
+    return align_up((size_t)n_rows * ext_cols(eb, pool->dev.r_max) * eb, 256);
+}
+
 __global__ void k_fill_zero(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
                             size_t n_tail) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -65,6 +71,12 @@ lora_status_t check_segments(const lora_segments_t* seg, int32_t n_rows, int32_t
 }
 
 lora_status_t check_pool(lora_pool_t p) { return p ? LORA_OK : LORA_E_INVALID; }
+
+constexpr int32_t kDecodeMaxRows = 64;
+
+bool decode_ok(const lora_pool_s* pool, int32_t n_rows) {
+    return pool->dtype == LORA_BF16 && n_rows >= 1 && n_rows <= kDecodeMaxRows;
+}
 
 lora_mode_t resolve_mode(lora_mode_t m, int32_t n_rows) {
     if (m != LORA_MODE_AUTO) return m;
@@ -333,10 +345,12 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
     if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
         return LORA_E_INVALID;
     const lora_mode_t m = resolve_mode(mode, n_rows);
-    size_t off = align_up((size_t)n_rows * t_stride(pool->dev.r_max) * 4, 256);
+    size_t off = align_up((size_t)n_rows * t_stride(pool->dev.r_max) * 4, 256) + ext_bytes(pool, n_rows);
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
         off += bgmv_shrink_ws_bytes(plan, n_rows);
+        if (decode_ok(pool, n_rows))
+            off = std::max(off, decode_ws_bytes(pool->dev, n_rows, plan_decode(pool->dev, n_rows, true)));
     } else {
         if (pool->dev.n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
         off = seg_layout(off, n_rows, pool->dev.n_adapters).end;
@@ -374,15 +388,34 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     if (st != LORA_OK) return st;
     if (!ws || ws_bytes < need || !al16(ws)) return LORA_E_WORKSPACE;
 
+    if (m == LORA_MODE_BGMV && w_layout == LORA_W_OUT_IN && decode_ok(pool, n_rows)) {
+        const DecodePlan D = plan_decode(P, n_rows, true);
+        DecodeArgs g;
+        g.x = x;
+        g.ldx = ldx;
+        g.W = W;
+        g.ldw = ldw;
+        g.ids = ids;
+        g.n = n_rows;
+        g.with_lora = 1;
+        g.y = y;
+        g.ldy = ldy;
+        decode_carve(P, n_rows, D, ws, g);
+        hipError_t e = launch_decode_stream(P, D, g, stream);
+        if (e == hipSuccess) e = launch_decode_finish(P, D, g, y_dtype, stream);
+        return dev_status(e);
+    }
     uint8_t* base = (uint8_t*)ws;
     float* t = (float*)base;
     const int64_t ldt = t_stride(P.r_max);
-    const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256);
+    void* t_ext = base + align_up((size_t)n_rows * ldt * 4, 256);
+    const int64_t lde = ext_cols(eb, P.r_max);
+    const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256) + ext_bytes(pool, n_rows);
     hipError_t e = hipSuccess;
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
         e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, base + after_t, plan,
-                               stream);
+                               stream, t_ext, lde);
     } else {
         lora_segments_t own;
         const lora_segments_t* sg = seg;
@@ -398,7 +431,7 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
         }
         if (e == hipSuccess)
             e = launch_sgmv_shrink(P, pool->dtype, x, ldx, sg, n_rows, P.n_adapters + 1, t, ldt, true,
-                                   stream);
+                                   stream, t_ext, lde);
     }
     if (e != hipSuccess) return LORA_E_DEVICE;
     GemmArgs g;
@@ -409,8 +442,10 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     g.w_out_in = (w_layout == LORA_W_OUT_IN) ? 1 : 0;
     g.ids = ids;
     g.n_rows = n_rows;
-    g.t = t;
-    g.ldt = ldt;
+    g.t = nullptr;
+    g.ldt = 0;
+    g.t_ext = t_ext;
+    g.lde = lde;
     g.y = y;
     g.ldy = ldy;
     g.vec_x = true;
@@ -418,10 +453,17 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
 }
 
+lora_status_t lora_base_gemm_expand_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes) {
+    if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
+    *bytes = ext_bytes(pool, n_rows);
+    return LORA_OK;
+}
+
 lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
                                     int64_t ldw, lora_w_layout_t w_layout, const int32_t* ids,
                                     const float* t, int64_t ldt, int32_t n_rows, void* y,
-                                    lora_dtype_t y_dtype, int64_t ldy, hipStream_t stream) {
+                                    lora_dtype_t y_dtype, int64_t ldy, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
     if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
     if (w_layout != LORA_W_IN_OUT && w_layout != LORA_W_OUT_IN) return LORA_E_INVALID;
     if (n_rows == 0) return LORA_OK;
@@ -443,13 +485,81 @@ lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx
     g.w_out_in = (w_layout == LORA_W_OUT_IN) ? 1 : 0;
     g.ids = ids;
     g.n_rows = n_rows;
-    g.t = t;
-    g.ldt = ldt;
+    g.t = nullptr;
+    g.ldt = 0;
+    g.t_ext = nullptr;
+    g.lde = 0;
     g.y = y;
     g.ldy = ldy;
     g.vec_x = true;
     g.vec_w = true;
+    const bool skinny = pool->dtype == LORA_BF16 && g.w_out_in && n_rows <= 64;
+    if (t && skinny) {
+        g.t = t;       // the skinny kernel adds s * t B in a VALU epilogue
+        g.ldt = ldt;
+    } else if (t) {
+        if (!ws || !al16(ws) || ws_bytes < ext_bytes(pool, n_rows)) return LORA_E_WORKSPACE;
+        g.t_ext = ws;
+        g.lde = ext_cols(eb, P.r_max);
+        hipError_t e = launch_make_t_ext(P, pool->dtype, t, ldt, ids, n_rows, ws, g.lde, stream);
+        if (e != hipSuccess) return LORA_E_DEVICE;
+    }
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
+}
+
+lora_status_t lora_decode_workspace(lora_pool_t pool, int32_t n_rows, int with_lora, size_t* bytes) {
+    if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
+    if (n_rows == 0) {
+        *bytes = 0;
+        return LORA_OK;
+    }
+    if (!decode_ok(pool, n_rows)) return LORA_E_UNSUPPORTED;
+    *bytes = decode_ws_bytes(pool->dev, n_rows, plan_decode(pool->dev, n_rows, with_lora != 0));
+    return LORA_OK;
+}
+
+lora_status_t lora_decode_stream(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
+                                 int64_t ldw, const int32_t* ids, int32_t n_rows, int with_lora,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    if (!decode_ok(pool, n_rows)) return LORA_E_UNSUPPORTED;
+    const PoolDev& P = pool->dev;
+    if (!x || !W || !ids || ldx < P.d_in || ldw < P.d_in) return LORA_E_INVALID;
+    if (!al16(x) || !al16(W) || !ld_ok(ldx, P.d_in, 2) || !ld_ok(ldw, P.d_in, 2)) return LORA_E_UNSUPPORTED;
+    const DecodePlan D = plan_decode(P, n_rows, with_lora != 0);
+    if (!ws || !al16(ws) || ws_bytes < decode_ws_bytes(P, n_rows, D)) return LORA_E_WORKSPACE;
+    DecodeArgs g{};
+    g.x = x;
+    g.ldx = ldx;
+    g.W = W;
+    g.ldw = ldw;
+    g.ids = ids;
+    g.n = n_rows;
+    g.with_lora = with_lora ? 1 : 0;
+    decode_carve(P, n_rows, D, ws, g);
+    return dev_status(launch_decode_stream(P, D, g, stream));
+}
+
+lora_status_t lora_decode_finish(lora_pool_t pool, const int32_t* ids, int32_t n_rows, int with_lora,
+                                 void* y, lora_dtype_t y_dtype, int64_t ldy, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    if (!decode_ok(pool, n_rows)) return LORA_E_UNSUPPORTED;
+    const PoolDev& P = pool->dev;
+    if (!ids || !y || ldy < P.d_out) return LORA_E_INVALID;
+    if (!al16(y) || !ld_ok(ldy, P.d_out, elem_bytes(y_dtype))) return LORA_E_UNSUPPORTED;
+    const DecodePlan D = plan_decode(P, n_rows, with_lora != 0);
+    if (!ws || !al16(ws) || ws_bytes < decode_ws_bytes(P, n_rows, D)) return LORA_E_WORKSPACE;
+    DecodeArgs g{};
+    g.ids = ids;
+    g.n = n_rows;
+    g.with_lora = with_lora ? 1 : 0;
+    g.y = y;
+    g.ldy = ldy;
+    decode_carve(P, n_rows, D, ws, g);
+    return dev_status(launch_decode_finish(P, D, g, y_dtype, stream));
 }
 
 }  // extern "C"

@@ -18,6 +18,17 @@ constexpr int SHRINK_LOADS = 16;        // 16-byte loads of A in flight per thre
 constexpr int SHRINK_X_FLOATS = 8192;   // x chunk staged in LDS (32 KiB)
 constexpr int SHRINK_A_ELEMS = 8192;    // generic path: A chunk staged in LDS
 
+// One row of the K-extension operand from the row's t (in LDS), after a
+// workgroup barrier.
+__device__ __forceinline__ void write_t_ext(bf16* out, float* sv, int r, float s, int cols) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) out[c] = ext_value_bf16(sv, r, s, c);
+}
+__device__ __forceinline__ void write_t_ext(float* out, float* sv, int r, float s, int cols) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) out[c] = ext_value_f32(sv, r, s, c);
+}
+
 // Streaming shrink, for ranks where 16-byte vectors tile every k-row
 // (r % VE == 0) and a pass of the workgroup covers whole k-rows
 // ((SHRINK_THREADS * VE) % r == 0): r in {8, 16, 32, 64} for bf16,
@@ -34,7 +45,8 @@ template <typename T>
 __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_stream(PoolDev P, const T* __restrict__ x,
                                                                       int64_t ldx,
                                                                       const int32_t* __restrict__ ids,
-                                                                      float* __restrict__ t, int64_t ldt) {
+                                                                      float* __restrict__ t, int64_t ldt,
+                                                                      T* __restrict__ t_ext, int64_t lde) {
     constexpr int VE = 16 / sizeof(T);
     __shared__ float xs[SHRINK_X_FLOATS];
     __shared__ float red[SHRINK_THREADS / 64][64];
@@ -95,12 +107,15 @@ __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_stream(PoolDev P
 #pragma unroll
         for (int e = 0; e < VE; ++e) red[wave][lane * VE + e] = acc[e];
     __syncthreads();
-    if (tid < r_max) {
+    __shared__ float sv[64];
+    if (tid < 64) {
         float v = 0.f;
         if (tid < r)
             for (int w = 0; w < SHRINK_THREADS / 64; ++w) v += red[w][tid];
-        ti[tid] = v;
+        if (tid < r_max) ti[tid] = v;
+        sv[tid] = v;
     }
+    if (t_ext) write_t_ext(t_ext + (int64_t)i * lde, sv, r, P.scales[a], ext_cols(sizeof(T), r_max));
 }
 
 // Generic shrink for any rank 1..64: k-chunks of A_a are staged in LDS and
@@ -110,7 +125,8 @@ template <typename T>
 __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_lds(PoolDev P, const T* __restrict__ x,
                                                                    int64_t ldx,
                                                                    const int32_t* __restrict__ ids,
-                                                                   float* __restrict__ t, int64_t ldt) {
+                                                                   float* __restrict__ t, int64_t ldt,
+                                                                   T* __restrict__ t_ext, int64_t lde) {
     __shared__ __attribute__((aligned(16))) T as[SHRINK_A_ELEMS];
     __shared__ float xs[SHRINK_A_ELEMS];
     __shared__ float red[SHRINK_THREADS];
@@ -154,12 +170,15 @@ __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_lds(PoolDev P, c
     }
     red[tid] = (g < Gs) ? acc : 0.f;
     __syncthreads();
-    if (tid < r_max) {
+    __shared__ float sv[64];
+    if (tid < 64) {
         float v = 0.f;
         if (tid < r)
             for (int q = 0; q < Gs; ++q) v += red[q * r + tid];
-        ti[tid] = v;
+        if (tid < r_max) ti[tid] = v;
+        sv[tid] = v;
     }
+    if (t_ext) write_t_ext(t_ext + (int64_t)i * lde, sv, r, P.scales[a], ext_cols(sizeof(T), r_max));
 }
 
 // Expand.  One wave per (row, chunk of 64*VE output columns); lane l owns VE
@@ -196,17 +215,29 @@ __global__ __launch_bounds__(256) void k_bgmv_expand(PoolDev P, const float* __r
         const float sc = P.scales[a];
         const T* Bu = (const T*)P.B + P.b_off[a] + c0;
         const float* ti = t + (int64_t)i * ldt;
-        for (int j = 0; j < r; ++j) {
-            const float tj = ti[j];
-            const T* bj = Bu + (int64_t)j * d_out;
-            if (full && P.vec_b) {
-                union { uint4 u; T e[VE]; } v;
-                v.u = *(const uint4*)bj;
+        constexpr int RC = 16;   // rank rows requested together
+        for (int j0 = 0; j0 < r; j0 += RC) {
+            uint4 bv[RC];
+            float tv[RC];
 #pragma unroll
-                for (int e = 0; e < VE; ++e) acc[e] += tj * to_f32(v.e[e]);
-            } else {
-                for (int e = 0; e < VE; ++e)
-                    if (c0 + e < d_out) acc[e] += tj * to_f32(bj[e]);
+            for (int q = 0; q < RC; ++q) {
+                const int j = j0 + q;
+                const T* bj = Bu + (int64_t)j * d_out;
+                tv[q] = (j < r) ? ti[j] : 0.f;
+                if (j < r && full && P.vec_b) {
+                    bv[q] = *(const uint4*)bj;
+                } else {
+                    union { uint4 u; T e[VE]; } w;
+                    for (int e = 0; e < VE; ++e) w.e[e] = (j < r && c0 + e < d_out) ? bj[e] : (T)0;
+                    bv[q] = w.u;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < RC; ++q) {
+                union { uint4 u; T e[VE]; } w;
+                w.u = bv[q];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc[e] += tv[q] * to_f32(w.e[e]);
             }
         }
 #pragma unroll
@@ -256,24 +287,50 @@ size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan&, int32_t) { return 0; }
 
 hipError_t launch_bgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
                               const int32_t* ids, int32_t n_rows, float* t, int64_t ldt, void*,
-                              const BgmvShrinkPlan& plan, hipStream_t stream) {
+                              const BgmvShrinkPlan& plan, hipStream_t stream, void* t_ext, int64_t lde) {
     dim3 grid((unsigned)n_rows);
     const bool stream_path = plan.ks == 1;
     if (dt == LORA_BF16) {
         if (stream_path)
             hipLaunchKernelGGL(k_bgmv_shrink_stream<bf16>, grid, dim3(SHRINK_THREADS), 0, stream, P,
-                               (const bf16*)x, ldx, ids, t, ldt);
+                               (const bf16*)x, ldx, ids, t, ldt, (bf16*)t_ext, lde);
         else
             hipLaunchKernelGGL(k_bgmv_shrink_lds<bf16>, grid, dim3(SHRINK_THREADS), 0, stream, P,
-                               (const bf16*)x, ldx, ids, t, ldt);
+                               (const bf16*)x, ldx, ids, t, ldt, (bf16*)t_ext, lde);
     } else {
         if (stream_path)
             hipLaunchKernelGGL(k_bgmv_shrink_stream<float>, grid, dim3(SHRINK_THREADS), 0, stream, P,
-                               (const float*)x, ldx, ids, t, ldt);
+                               (const float*)x, ldx, ids, t, ldt, (float*)t_ext, lde);
         else
             hipLaunchKernelGGL(k_bgmv_shrink_lds<float>, grid, dim3(SHRINK_THREADS), 0, stream, P,
-                               (const float*)x, ldx, ids, t, ldt);
+                               (const float*)x, ldx, ids, t, ldt, (float*)t_ext, lde);
     }
+    return hipGetLastError();
+}
+
+// t_ext from an existing t: one workgroup per row.
+template <typename T>
+__global__ __launch_bounds__(256) void k_make_t_ext(PoolDev P, const float* __restrict__ t, int64_t ldt,
+                                                    const int32_t* __restrict__ ids, T* __restrict__ t_ext,
+                                                    int64_t lde) {
+    __shared__ float sv[64];
+    const int i = blockIdx.x;
+    const int a = ids[i];
+    if (!id_ok(a, P.n_adapters)) return;
+    const int r = P.ranks[a];
+    if (threadIdx.x < 64) sv[threadIdx.x] = (threadIdx.x < r) ? t[(int64_t)i * ldt + threadIdx.x] : 0.f;
+    write_t_ext(t_ext + (int64_t)i * lde, sv, r, P.scales[a], ext_cols(sizeof(T), P.r_max));
+}
+
+hipError_t launch_make_t_ext(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
+                             const int32_t* ids, int32_t n_rows, void* t_ext, int64_t lde,
+                             hipStream_t stream) {
+    if (dt == LORA_BF16)
+        hipLaunchKernelGGL(k_make_t_ext<bf16>, dim3((unsigned)n_rows), dim3(256), 0, stream, P, t, ldt, ids,
+                           (bf16*)t_ext, lde);
+    else
+        hipLaunchKernelGGL(k_make_t_ext<float>, dim3((unsigned)n_rows), dim3(256), 0, stream, P, t, ldt, ids,
+                           (float*)t_ext, lde);
     return hipGetLastError();
 }
 

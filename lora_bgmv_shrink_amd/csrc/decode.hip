@@ -1,0 +1,417 @@
+// Decode layer in two launches (n_rows <= 64, bf16, W stored [d_out, d_in]).
+//
+// At decode sizes the layer is a stream of W (and of the adapters' A and B
+// blocks) with almost no reuse; the adapter term is bandwidth bound and its
+// cost is reading A and B ("Serving many LoRA adapters" (blog.ecitis.org),
+// section "Batching across different adapters").  A single pass over W per
+// CU is limited by how many misses a CU keeps in flight, so the work is cut
+// into many small independent pieces, and partial sums meet at the kernel
+// boundary (an in-kernel cross-XCD hand-off costs more than the whole pass):
+//
+//   stream: workgroups of two kinds in one launch
+//     base:   128 output columns x one K slice: x rows of the slice staged
+//             in LDS, each wave streams the W rows of 16 columns and writes
+//             its fp32 partial part_base[slice][m][n];
+//     shrink: one row x one K slice of its adapter: partial x_i A_a over
+//             the slice, written as part_t[slice][i][j] (BGMV: the row
+//             gathers its own adapter).
+//   finish: y[m][n] = sum_slices part_base + s_a * sum_j (sum_slices part_t)[j]
+//           * B_a[j][n], rounded once.
+//
+// Every sum runs in a fixed order, so results do not depend on timing.
+#include <climits>
+
+#include "lora_internal.hpp"
+
+namespace lora {
+namespace {
+
+constexpr int DS_THREADS = 512;     // 8 waves
+constexpr int DS_NB = 8;            // 16-column MFMA blocks per base workgroup, one per wave
+constexpr int DS_COLS = DS_NB * 16;
+constexpr int DS_USTEPS = 16;       // k-steps (of 32) per base slice at most
+constexpr int DS_SHRINK_LOADS = 8;  // 16-byte A loads in flight per thread (shrink)
+constexpr int FIN_THREADS = 256;    // finish workgroup: 4 waves, 4 columns per thread
+constexpr int FIN_COLS = FIN_THREADS * 4;
+constexpr int FIN_RCHUNK = 16;      // rank rows of B loaded together in the finish
+constexpr int FIN_SCHUNK = 8;       // partial slices loaded together in the finish
+
+__device__ __forceinline__ bf16x8_t ld8(const bf16* p, int valid, bool nt) {
+    if (valid >= 8) {
+        if (nt) {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+            return __builtin_bit_cast(bf16x8_t, v);
+        }
+        return *(const bf16x8_t*)p;
+    }
+    union { bf16x8_t v; bf16 e[8]; } u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u.e[e] = (e < valid) ? p[e] : (bf16)0;
+    return u.v;
+}
+
+// Base part: workgroup (tn, ks) owns columns [tn*128, +128) and k-rows of
+// slice ks.  x rows of the slice are staged once in LDS; wave w streams the
+// 16 rows of W^T for column block w (all of the slice's k-steps in flight,
+// nontemporal: W is read once) and keeps the whole 16-column partial.
+template <int MB>
+__device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b, uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tn = b % D.tiles_n;
+    const int ks = b / D.tiles_n;
+    const int K = P.d_in;
+    const int N = P.d_out;
+    const int M = g.n;
+    const int kbeg = ks * D.kslice;
+    const int kend = min(K, kbeg + D.kslice);
+    const int nsteps = (kend - kbeg + 31) / 32;
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int n = tn * DS_COLS + wave * 16 + lr;
+    const bf16* Wt = (const bf16*)g.W + (int64_t)(n < N ? n : 0) * g.ldw;
+
+    bf16x8_t bw[DS_USTEPS];
+#pragma unroll
+    for (int u = 0; u < DS_USTEPS; ++u) {
+        const int k = kbeg + u * 32 + kq;
+        const int valid = (u < nsteps) ? min(8, kend - k) : 0;
+        bw[u] = (valid > 0 && n < N) ? ld8(Wt + k, valid, true) : bf16x8_t{};
+    }
+
+    // x[0:16*MB][slice] -> LDS as [m][k] bf16, rows padded by 16 bytes
+    constexpr int XLD = DS_USTEPS * 32 + 8;
+    static_assert(MB * 16 * XLD * 2 <= DS_LDS_BYTES, "staged x does not fit the LDS block");
+    bf16* xs = (bf16*)lds;
+    const bf16* X = (const bf16*)g.x;
+    const int per_row = DS_USTEPS * 32 / 8;    // 16-byte pieces per staged row
+    for (int v = tid; v < MB * 16 * per_row; v += DS_THREADS) {
+        const int m = v / per_row;
+        const int c = (v - m * per_row) * 8;
+        const int k = kbeg + c;
+        const int valid = min(8, kend - k);
+        bf16x8_t val = bf16x8_t{};
+        if (m < M && valid > 0) val = ld8(X + (int64_t)m * g.ldx + k, valid, false);
+        *(bf16x8_t*)(xs + m * XLD + c) = val;
+    }
+    __syncthreads();
+
+    f32x4_t acc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < DS_USTEPS; ++u) {
+        if (u < nsteps) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const bf16x8_t a = *(const bf16x8_t*)(xs + (i * 16 + lr) * XLD + u * 32 + kq);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[u], acc[i], 0, 0, 0);
+            }
+        }
+    }
+
+    if (n < N) {
+        float* out = g.part_base + (int64_t)ks * M * N + n;
+        const int lq = (lane >> 4) * 4;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = i * 16 + lq + q;
+                if (m < M) out[(int64_t)m * N] = acc[i][q];
+            }
+    }
+}
+
+// Partial shrink of row i over k-rows [k0, k1): the streaming pattern of the
+// BGMV shrink (thread t owns columns (t % G) * 8 .. + 8 of every
+// (DS_THREADS / G)-th k-row), with x staged in LDS.
+__device__ void stream_shrink(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b, uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int i = b / D.t_slices;
+    const int s = b - i * D.t_slices;
+    const int a = g.ids[i];
+    float* outp = g.part_t + ((int64_t)s * g.n + i) * 64;
+    const bool ok = id_ok(a, P.n_adapters);
+    if (s == 0 && tid == 0) {
+        // row record for the finish pass: B block offset, rank (0: no term), scale
+        RowRec rec;
+        rec.b_off = ok ? P.b_off[a] : 0;
+        rec.rank = ok ? P.ranks[a] : 0;
+        rec.scale = ok ? P.scales[a] : 0.f;
+        g.rows[i] = rec;
+        if (!ok && a != -1) flag_bad_id(P.err);
+    }
+    if (!ok) return;   // the finish pass never reads t for such rows
+    const int r = P.ranks[a];
+    const int k0 = s * D.t_kslice;
+    const int k1 = min(P.d_in, k0 + D.t_kslice);
+    float* xs = (float*)lds;                                    // t_kslice floats
+    float (*red)[64] = (float (*)[64])(lds + D.t_kslice * 4);   // [8][64]
+    const bf16* xi = (const bf16*)g.x + (int64_t)i * g.ldx;
+    for (int k = k0 + tid; k < k1; k += DS_THREADS) xs[k - k0] = to_f32(xi[k]);
+
+    const bf16* Au = (const bf16*)P.A + P.a_off[a];
+    if (P.stream_ok) {
+        constexpr int VE = 8;
+        const int G = r / VE;
+        const int KPT = DS_THREADS / G;
+        const int jv = tid % G;
+        const int ksub = tid / G;
+        float acc[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+        uint4 av[DS_SHRINK_LOADS];
+        for (int kc = k0; kc < k1; kc += KPT * DS_SHRINK_LOADS) {
+#pragma unroll
+            for (int l = 0; l < DS_SHRINK_LOADS; ++l) {
+                const int k = kc + ksub + l * KPT;
+                av[l] = (k < k1) ? *(const uint4*)(Au + (int64_t)k * r + jv * VE) : uint4{0u, 0u, 0u, 0u};
+            }
+            __syncthreads();   // xs ready (first pass) / harmless afterwards
+#pragma unroll
+            for (int l = 0; l < DS_SHRINK_LOADS; ++l) {
+                const int k = kc + ksub + l * KPT;
+                const float xv = (k < k1) ? xs[k - k0] : 0.f;
+                union { uint4 u; bf16 e[VE]; } v;
+                v.u = av[l];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc[e] += xv * to_f32(v.e[e]);
+            }
+        }
+        for (int d = G; d < 64; d <<= 1)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], d, 64);
+        if (lane < G)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) red[wave][lane * VE + e] = acc[e];
+    } else {
+        // any rank: thread (j, g) sums column j over k-rows g, g + Gs, ...
+        __syncthreads();
+        const int Gs = DS_THREADS / r;
+        const int j = tid % r;
+        const int gq = tid / r;
+        float acc = 0.f;
+        if (gq < Gs)
+            for (int k = k0 + gq; k < k1; k += Gs) acc += xs[k - k0] * to_f32(Au[(int64_t)k * r + j]);
+        // fold the Gs groups into 8 wave slots in a fixed order
+        float* flat = &red[0][0];
+        __syncthreads();
+        if (tid < 8 * 64) flat[tid] = 0.f;
+        __syncthreads();
+        for (int q = 0; q < Gs; ++q) {
+            if (gq == q) flat[(q & 7) * 64 + j] += acc;
+            __syncthreads();
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        float v = 0.f;
+        if (tid < r)
+            for (int w = 0; w < 8; ++w) v += red[w][tid];
+        outp[tid] = v;
+    }
+}
+
+template <int MB>
+__global__ __launch_bounds__(DS_THREADS) void k_decode_stream(PoolDev P, DecodePlan D, DecodeArgs g) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_BYTES];
+    const int b = blockIdx.x;
+    // shrink workgroups first: they feed the finish pass's longest chain
+    if (b < D.shrink_wgs) stream_shrink(P, D, g, b, lds);
+    else stream_base<MB>(P, D, g, b - D.shrink_wgs, lds);
+}
+
+// Finish: workgroup (m, chunk) owns FIN_COLS columns of row m, 4 per thread.
+// The row's B rows are requested first (they depend only on the row
+// record), then the base partials; the t partials are summed into LDS in
+// slice order while those loads are in flight.
+template <typename TY>
+__global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, DecodePlan D, DecodeArgs g) {
+    __shared__ float st[64];
+    const int tid = threadIdx.x;
+    const int nch = (P.d_out + FIN_COLS - 1) / FIN_COLS;
+    const int m = blockIdx.x / nch;
+    const int c0 = (blockIdx.x - m * nch) * FIN_COLS + tid * 4;
+    const int N = P.d_out;
+    const int M = g.n;
+    int r = 0;
+    int64_t boff = 0;
+    float sc = 0.f;
+    if (g.with_lora) {
+        const RowRec rec = g.rows[m];
+        r = rec.rank;
+        boff = rec.b_off;
+        sc = rec.scale;
+    }
+    const bool in = c0 < N;
+    const bool full = c0 + 4 <= N;
+    const bf16* Bu = (const bf16*)P.B + boff + c0;
+    const bool vb = full && P.vec_b;
+
+    float e4[4] = {0.f, 0.f, 0.f, 0.f};
+    uint2 bv[FIN_RCHUNK];
+    int j0 = 0;
+    if (in && r > 0) {
+#pragma unroll
+        for (int q = 0; q < FIN_RCHUNK; ++q) {
+            const int j = q;
+            if (j < r && vb) {
+                bv[q] = *(const uint2*)(Bu + (int64_t)j * N);
+            } else {
+                union { uint2 u; bf16 e[4]; } w;
+                for (int e = 0; e < 4; ++e) w.e[e] = (j < r && c0 + e < N) ? Bu[(int64_t)j * N + e] : (bf16)0;
+                bv[q] = w.u;
+            }
+        }
+    }
+    // partial sums, FIN_SCHUNK slices requested together, added in slice order
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (in) {
+        const bool vp = full && (N % 4 == 0);
+        for (int s0 = 0; s0 < D.base_slices; s0 += FIN_SCHUNK) {
+            float4 u[FIN_SCHUNK];
+#pragma unroll
+            for (int q = 0; q < FIN_SCHUNK; ++q) {
+                const float* p = g.part_base + ((int64_t)(s0 + q) * M + m) * N + c0;
+                if (s0 + q >= D.base_slices) {
+                    u[q] = float4{0.f, 0.f, 0.f, 0.f};
+                } else if (vp) {
+                    u[q] = *(const float4*)p;
+                } else {
+                    u[q].x = p[0];
+                    u[q].y = (c0 + 1 < N) ? p[1] : 0.f;
+                    u[q].z = (c0 + 2 < N) ? p[2] : 0.f;
+                    u[q].w = (c0 + 3 < N) ? p[3] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < FIN_SCHUNK; ++q) {
+                if (s0 + q < D.base_slices) {
+                    v[0] += u[q].x; v[1] += u[q].y; v[2] += u[q].z; v[3] += u[q].w;
+                }
+            }
+        }
+    }
+    if (r > 0 && tid < r) {
+        float t = 0.f;
+        for (int s0 = 0; s0 < D.t_slices; s0 += FIN_SCHUNK) {
+            float u[FIN_SCHUNK];
+#pragma unroll
+            for (int q = 0; q < FIN_SCHUNK; ++q)
+                u[q] = (s0 + q < D.t_slices) ? g.part_t[((int64_t)(s0 + q) * M + m) * 64 + tid] : 0.f;
+#pragma unroll
+            for (int q = 0; q < FIN_SCHUNK; ++q)
+                if (s0 + q < D.t_slices) t += u[q];
+        }
+        st[tid] = t;
+    }
+    __syncthreads();
+    if (!in) return;
+    if (r > 0) {
+        for (;;) {
+#pragma unroll
+            for (int q = 0; q < FIN_RCHUNK; ++q) {
+                const float tj = (j0 + q < r) ? st[j0 + q] : 0.f;
+                union { uint2 u; bf16 e[4]; } w;
+                w.u = bv[q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) e4[e] += tj * to_f32(w.e[e]);
+            }
+            j0 += FIN_RCHUNK;
+            if (j0 >= r) break;
+#pragma unroll
+            for (int q = 0; q < FIN_RCHUNK; ++q) {
+                const int j = j0 + q;
+                if (j < r && vb) {
+                    bv[q] = *(const uint2*)(Bu + (int64_t)j * N);
+                } else {
+                    union { uint2 u; bf16 e[4]; } w;
+                    for (int e = 0; e < 4; ++e) w.e[e] = (j < r && c0 + e < N) ? Bu[(int64_t)j * N + e] : (bf16)0;
+                    bv[q] = w.u;
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += sc * e4[e];
+    }
+    TY* yr = (TY*)g.y + (int64_t)m * g.ldy;
+    for (int e = 0; e < 4 && c0 + e < N; ++e) yr[c0 + e] = from_f32<TY>(v[e]);
+}
+
+}  // namespace
+
+DecodePlan plan_decode(const PoolDev& P, int32_t n_rows, bool with_lora) {
+    DecodePlan D;
+    const int K = P.d_in;
+    D.tiles_n = (int32_t)ceil_div(P.d_out, DS_COLS);
+    const int ksteps = (int)ceil_div(K, 32);
+    // K slices: about 256 workgroups, at most DS_USTEPS k-steps each
+    const int want = (int)std::max<int64_t>(1, ceil_div(256, D.tiles_n));
+    int steps = (int)ceil_div(ksteps, want);
+    steps = std::max(1, std::min(steps, DS_USTEPS));
+    D.kslice = steps * 32;
+    D.base_slices = (int32_t)ceil_div(K, D.kslice);
+    D.base_wgs = D.tiles_n * D.base_slices;
+    // shrink slices: about 256 workgroups, slices of at least 512 k-rows,
+    // x slice within the LDS budget
+    if (with_lora && n_rows > 0) {
+        int ts = (int)std::max<int64_t>(1, ceil_div(256, n_rows));
+        ts = std::min<int>(ts, (int)std::max<int64_t>(1, ceil_div(K, 512)));
+        int tk = (int)align_up((size_t)ceil_div(K, ts), 64);
+        const int tk_max = (DS_LDS_BYTES - 8 * 64 * 4) / 4 / 64 * 64;
+        if (tk > tk_max) tk = tk_max;
+        D.t_kslice = tk;
+        D.t_slices = (int32_t)ceil_div(K, tk);
+    } else {
+        D.t_kslice = 0;
+        D.t_slices = 0;
+    }
+    D.shrink_wgs = with_lora ? n_rows * D.t_slices : 0;
+    return D;
+}
+
+size_t decode_ws_bytes(const PoolDev& P, int32_t n_rows, const DecodePlan& D) {
+    const size_t base = align_up((size_t)D.base_slices * n_rows * P.d_out * 4, 256);
+    const size_t t = align_up((size_t)D.t_slices * n_rows * 64 * 4, 256);
+    const size_t rows = D.t_slices ? align_up((size_t)n_rows * sizeof(RowRec), 256) : 0;
+    return base + t + rows;
+}
+
+void decode_carve(const PoolDev& P, int32_t n_rows, const DecodePlan& D, void* ws, DecodeArgs& g) {
+    uint8_t* w = (uint8_t*)ws;
+    const size_t base = align_up((size_t)D.base_slices * n_rows * P.d_out * 4, 256);
+    const size_t t = align_up((size_t)D.t_slices * n_rows * 64 * 4, 256);
+    g.part_base = (float*)w;
+    g.part_t = (float*)(w + base);
+    g.rows = (RowRec*)(w + base + t);
+}
+
+hipError_t launch_decode_stream(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
+                                hipStream_t stream) {
+    dim3 grid((unsigned)(D.base_wgs + D.shrink_wgs));
+    if (g.n <= 16)
+        hipLaunchKernelGGL((k_decode_stream<1>), grid, dim3(DS_THREADS), 0, stream, P, D, g);
+    else if (g.n <= 32)
+        hipLaunchKernelGGL((k_decode_stream<2>), grid, dim3(DS_THREADS), 0, stream, P, D, g);
+    else
+        hipLaunchKernelGGL((k_decode_stream<4>), grid, dim3(DS_THREADS), 0, stream, P, D, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_finish(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
+                                lora_dtype_t ydt, hipStream_t stream) {
+    const int nch = (int)ceil_div(P.d_out, FIN_COLS);
+    dim3 grid((unsigned)(g.n * nch));
+    if (ydt == LORA_BF16)
+        hipLaunchKernelGGL(k_decode_finish<bf16>, grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+    else
+        hipLaunchKernelGGL(k_decode_finish<float>, grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+    return hipGetLastError();
+}
+
+}  // namespace lora

@@ -61,6 +61,28 @@ __device__ __forceinline__ void flag_bad_id(int32_t* err) {
     __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// K-extension operand of the tiled layer GEMM ("t_ext"): per row, s * t
+// laid out in blocks of 32 ranks; a bf16 block is 64 columns [hi(32) | lo(32)]
+// (the fp32 value v = hi + lo to about 16 significant bits), an fp32 block is
+// the 32 values themselves.  Columns past the adapter's rank are 0.
+constexpr int EXT_RANKS = 32;
+__host__ __device__ constexpr int ext_block_cols(int elem_bytes) { return elem_bytes == 2 ? 64 : 32; }
+__host__ __device__ inline int ext_cols(int elem_bytes, int r_max) {
+    return ext_block_cols(elem_bytes) * ((r_max + EXT_RANKS - 1) / EXT_RANKS);
+}
+// column c of a row's t_ext, from the row's t (rank r, scale s)
+__device__ __forceinline__ bf16 ext_value_bf16(const float* t, int r, float s, int c) {
+    const int e = c >> 6;
+    const int kk = c & 63;
+    const int j = e * EXT_RANKS + (kk & 31);
+    const float v = (j < r) ? s * t[j] : 0.f;
+    const bf16 hi = f32_to_bf16(v);
+    return (kk < 32) ? hi : f32_to_bf16(v - to_f32(hi));
+}
+__device__ __forceinline__ float ext_value_f32(const float* t, int r, float s, int c) {
+    return (c < r) ? s * t[c] : 0.f;
+}
+
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -82,7 +104,8 @@ BgmvShrinkPlan plan_bgmv_shrink(const PoolDev& P, int elem_bytes, int32_t n_rows
 size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan& plan, int32_t n_rows);
 hipError_t launch_bgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
                               const int32_t* ids, int32_t n_rows, float* t, int64_t ldt,
-                              void* ws, const BgmvShrinkPlan& plan, hipStream_t stream);
+                              void* ws, const BgmvShrinkPlan& plan, hipStream_t stream,
+                              void* t_ext = nullptr, int64_t lde = 0);
 
 hipError_t launch_bgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                               const int32_t* ids, int32_t n_rows, void* y, lora_dtype_t ydt,
@@ -91,7 +114,12 @@ hipError_t launch_bgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t,
 // SGMV shrink / expand (MFMA over segment tiles).
 hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
                               const lora_segments_t* seg, int32_t n_rows, int32_t n_bins,
-                              float* t, int64_t ldt, bool vec_x, hipStream_t stream);
+                              float* t, int64_t ldt, bool vec_x, hipStream_t stream,
+                              void* t_ext = nullptr, int64_t lde = 0);
+// t_ext from an existing t (rows with invalid ids or -1 are left alone)
+hipError_t launch_make_t_ext(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
+                             const int32_t* ids, int32_t n_rows, void* t_ext, int64_t lde,
+                             hipStream_t stream);
 hipError_t launch_sgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                               const lora_segments_t* seg, int32_t n_rows, int32_t n_bins,
                               void* y, lora_dtype_t ydt, int64_t ldy, int accumulate,
@@ -106,8 +134,10 @@ struct GemmArgs {
     int w_out_in;
     const int32_t* ids;
     int32_t n_rows;
-    const float* t;   // nullptr: no LoRA term
+    const float* t;   // fp32 t for the skinny kernel's epilogue (nullptr: no LoRA term)
     int64_t ldt;
+    const void* t_ext;   // K-extension operand for the tiled kernel (nullptr: no LoRA term)
+    int64_t lde;
     void* y;
     int64_t ldy;
     bool vec_x;
@@ -117,5 +147,43 @@ hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt
                              const GemmArgs& g, hipStream_t stream);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+// Decode layer in two launches (bf16, n_rows <= 64, W stored [d_out, d_in]).
+constexpr int DS_LDS_BYTES = 72 * 1024;   // two workgroups per CU
+struct DecodePlan {
+    int32_t tiles_n;      // 64-column base tiles
+    int32_t kslice;       // k-rows per base slice (multiple of 32)
+    int32_t base_slices;  // partial base products per output
+    int32_t base_wgs;     // tiles_n * base_slices
+    int32_t t_kslice;     // k-rows per shrink slice
+    int32_t t_slices;     // partial shrink sums per row
+    int32_t shrink_wgs;   // n_rows * t_slices (0 without the LoRA term)
+};
+struct RowRec {
+    int64_t b_off;   // element offset of the row's B block
+    int32_t rank;    // 0: no adapter term (base-only or invalid id)
+    float scale;
+};
+struct DecodeArgs {
+    const void* x;
+    int64_t ldx;
+    const void* W;
+    int64_t ldw;
+    const int32_t* ids;
+    int32_t n;
+    int32_t with_lora;
+    float* part_base;   // [base_slices][n][d_out]
+    float* part_t;      // [t_slices][n][64]
+    RowRec* rows;       // [n], written by the shrink part
+    void* y;
+    int64_t ldy;
+};
+DecodePlan plan_decode(const PoolDev& P, int32_t n_rows, bool with_lora);
+size_t decode_ws_bytes(const PoolDev& P, int32_t n_rows, const DecodePlan& D);
+void decode_carve(const PoolDev& P, int32_t n_rows, const DecodePlan& D, void* ws, DecodeArgs& g);
+hipError_t launch_decode_stream(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
+                                hipStream_t stream);
+hipError_t launch_decode_finish(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
+                                lora_dtype_t ydt, hipStream_t stream);
 
 }  // namespace lora

@@ -151,6 +151,18 @@ struct RowLoader {
             }
         }
     }
+    // rows whose sId differs from u load zeros (the K-extension operand)
+    __device__ __forceinline__ void load_masked(const T* __restrict__ base, int64_t ld, const int* sRow,
+                                                const int* sId, int u, int k0, int tid) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int r = idx / VPR;
+            const int k = k0 + (idx - r * VPR) * C::VE;
+            reg[v] = (sId[r] == u) ? *(const uint4*)(base + (int64_t)sRow[r] * ld + k) : uint4{0u, 0u, 0u, 0u};
+        }
+    }
     __device__ __forceinline__ void store(T* s, int tid) const {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
@@ -159,6 +171,92 @@ struct RowLoader {
             const int r = idx / VPR;
             const int c = (idx - r * VPR) * C::VE;
             *(uint4*)(s + r * C::LDK + c) = reg[v];
+        }
+    }
+};
+
+// The B operand of one K-block, staged into LDS as [n][k]; one register set
+// serves two sources:
+//   rows:  K-contiguous rows n (W stored [d_out, d_in]),
+//   trans: row-major [K][N] rows k (W stored [d_in, d_out], or an adapter's
+//          B block [r, d_out] for the K-extension steps), transposed on the
+//          way into LDS.
+template <class C>
+struct BLoader {
+    using T = typename C::T;
+    static constexpr int VE = C::VE;
+    static constexpr int R_VPR = C::BK / VE;        // rows: vectors per row
+    static constexpr int T_VPR = C::BN / VE;        // trans: vectors per k-row
+    static constexpr int TOT = C::BN * C::BK / VE;  // same count for both
+    static constexpr int NV = (TOT + C::NT - 1) / C::NT;
+    uint4 reg[NV];
+    int kind;
+
+    __device__ __forceinline__ void load_rows(const T* __restrict__ base, int64_t ld, const int* sRow,
+                                              int k0, int K, int tid) {
+        kind = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int r = idx / R_VPR;
+            const int k = k0 + (idx - r * R_VPR) * VE;
+            const int gr = sRow[r];
+            if (gr >= 0 && k + VE <= K) {
+                reg[v] = *(const uint4*)(base + (int64_t)gr * ld + k);
+            } else {
+                union { uint4 u; T e[VE]; } tmp;
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    tmp.e[e] = (gr >= 0 && k + e < K) ? base[(int64_t)gr * ld + k + e] : (T)0;
+                reg[v] = tmp.u;
+            }
+        }
+    }
+    // k-row kr of the block reads source row j0 + (kr % kwrap), valid below kmax
+    __device__ __forceinline__ void load_trans(const T* __restrict__ base, int64_t ld, int j0, int kwrap,
+                                               int kmax, int n0, int N, bool vec, int tid) {
+        kind = 1;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int kr = idx / T_VPR;
+            const int k = j0 + kr % kwrap;
+            const int n = n0 + (idx - kr * T_VPR) * VE;
+            if (vec && k < kmax && n + VE <= N) {
+                reg[v] = *(const uint4*)(base + (int64_t)k * ld + n);
+            } else {
+                union { uint4 u; T e[VE]; } tmp;
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    tmp.e[e] = (k < kmax && n + e < N) ? base[(int64_t)k * ld + n + e] : (T)0;
+                reg[v] = tmp.u;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(T* s, int tid) const {
+        if (kind == 0) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int idx = tid + v * C::NT;
+                if (TOT % C::NT != 0 && idx >= TOT) break;
+                const int r = idx / R_VPR;
+                const int c = (idx - r * R_VPR) * VE;
+                *(uint4*)(s + r * C::LDK + c) = reg[v];
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int idx = tid + v * C::NT;
+                if (TOT % C::NT != 0 && idx >= TOT) break;
+                const int kr = idx / T_VPR;
+                const int c = (idx - kr * T_VPR) * VE;
+                union { uint4 u; T e[VE]; } tmp;
+                tmp.u = reg[v];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) s[(c + e) * C::LDK + kr] = tmp.e[e];
+            }
         }
     }
 };
@@ -240,12 +338,23 @@ __device__ void lora_kext(Acc<C>& acc, const PoolDev& P, const float* __restrict
         const float sc = P.scales[u];
         const T* Bu = (const T*)P.B + P.b_off[u];
         for (int j0 = 0; j0 < r; j0 += C::KH) {
-            for (int idx = tid; idx < C::BM * C::KH; idx += C::NT) {
+            // A side: s_u * t for rows of adapter u (all loads of the batch first)
+            constexpr int NA = (C::BM * C::KH + C::NT - 1) / C::NT;
+            float av[NA];
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const int idx = tid + q * C::NT;
+                const int m = idx / C::KH;
+                const int j = j0 + (idx - m * C::KH);
+                av[q] = (idx < C::BM * C::KH && sId[m] == u && j < r) ? t[(int64_t)sRow[m] * ldt + j] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                const int idx = tid + q * C::NT;
+                if (idx >= C::BM * C::KH) break;
                 const int m = idx / C::KH;
                 const int kk = idx - m * C::KH;
-                const int j = j0 + kk;
-                float v = 0.f;
-                if (sId[m] == u && j < r) v = sc * t[(int64_t)sRow[m] * ldt + j];
+                const float v = sc * av[q];
                 if constexpr (HL) {
                     const bf16 hi = f32_to_bf16(v);
                     const bf16 lo = f32_to_bf16(v - to_f32(hi));
@@ -255,15 +364,26 @@ __device__ void lora_kext(Acc<C>& acc, const PoolDev& P, const float* __restrict
                     sA[m * C::LDK + kk] = (T)v;
                 }
             }
-            for (int idx = tid; idx < C::KH * C::BN; idx += C::NT) {
+            // B side: B_u[j][n0 + n], transposed into [n][j]
+            constexpr int NB = (C::KH * C::BN + C::NT - 1) / C::NT;
+            T bv[NB];
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const int idx = tid + q * C::NT;
                 const int kk = idx / C::BN;
                 const int nn = idx - kk * C::BN;
                 const int j = j0 + kk;
                 const int col = n0 + nn;
-                T v = (T)0;
-                if (j < r && col < d_out) v = Bu[(int64_t)j * d_out + col];
-                sB[nn * C::LDK + kk] = v;
-                if constexpr (HL) sB[nn * C::LDK + C::KH + kk] = v;
+                bv[q] = (idx < C::KH * C::BN && j < r && col < d_out) ? Bu[(int64_t)j * d_out + col] : (T)0;
+            }
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const int idx = tid + q * C::NT;
+                if (idx >= C::KH * C::BN) break;
+                const int kk = idx / C::BN;
+                const int nn = idx - kk * C::BN;
+                sB[nn * C::LDK + kk] = bv[q];
+                if constexpr (HL) sB[nn * C::LDK + C::KH + kk] = bv[q];
             }
             __syncthreads();
             mma_block<C>(acc, sA, sB, wm, wn, lane);
@@ -316,22 +436,33 @@ struct GemmDev {
     int64_t ldw;
     const int32_t* ids;
     int32_t n;
-    const float* t;
+    const float* t;       // fp32 t (skinny kernel's epilogue)
     int64_t ldt;
+    const void* t_ext;    // K-extension operand (tiled kernel), or null
+    int64_t lde;
     void* y;
     int64_t ldy;
     int32_t tiles_m;
     int32_t tiles_n;
 };
 
+// The LoRA expand rides on the same K loop: after the d_in/BK blocks of
+// x W come, for every distinct adapter u among the tile's rows (ascending
+// id), ceil(r_u / KH) blocks whose A side is t_ext (s_u * t split into bf16
+// hi | lo halves, written by the shrink; rows of other adapters masked to 0)
+// and whose B side is B_u[j][n0:n0+BN] (each rank row twice for bf16, to
+// meet the hi and the lo half).  y is rounded once at the end.
 template <class C, typename TY, bool OUT_IN>
 __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     using T = typename C::T;
+    static_assert(C::BK == ext_block_cols(sizeof(T)) && C::KH == EXT_RANKS, "t_ext block layout");
     __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
     __shared__ int sRowA[C::BM];
     __shared__ int sRowB[OUT_IN ? C::BN : 1];
     __shared__ int sId[C::BM];
+    __shared__ int sExt[2 * C::BM];   // (u << 1) | block, in order
     __shared__ int sNext;
+    __shared__ int sNExt;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -371,36 +502,64 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     }
     if constexpr (OUT_IN)
         for (int r = tid; r < C::BN; r += C::NT) sRowB[r] = (n0 + r < N) ? n0 + r : -1;
+    if (tid == 0) sNExt = 0;
     __syncthreads();
+
+    // K-extension blocks: distinct adapters of the tile in ascending order
+    if (g.t_ext) {
+        int prev = -1;
+        for (;;) {
+            if (tid == 0) sNext = INT_MAX;
+            __syncthreads();
+            for (int m = tid; m < C::BM; m += C::NT) {
+                const int v = sId[m];
+                if (v > prev && v != INT_MAX) atomicMin(&sNext, v);
+            }
+            __syncthreads();
+            const int u = sNext;
+            if (u == INT_MAX) break;
+            if (tid == 0) {
+                const int nb = (P.ranks[u] + C::KH - 1) / C::KH;
+                for (int e = 0; e < nb; ++e) sExt[sNExt + e] = (u << 1) | e;
+                sNExt += nb;
+            }
+            prev = u;
+        }
+        __syncthreads();
+    }
+    const int nk = (K + C::BK - 1) / C::BK;
+    const int total = nk + sNExt;
 
     Acc<C> acc;
     acc.zero();
     const T* X = (const T*)g.x;
     const T* Wp = (const T*)g.W;
+    const T* TE = (const T*)g.t_ext;
     RowLoader<C, C::BM> la;
-    using LB = typename std::conditional<OUT_IN, RowLoader<C, C::BN>, TransLoader<C, C::BN>>::type;
-    LB lb;
-    auto load_b = [&](int k0) {
-        if constexpr (OUT_IN) lb.load(Wp, g.ldw, sRowB, k0, K, tid);
-        else lb.load(Wp, g.ldw, k0, K, n0, N, true, tid);
+    BLoader<C> lb;
+    auto load_step = [&](int s) {
+        if (s < nk) {
+            la.load(X, g.ldx, sRowA, s * C::BK, K, tid);
+            if constexpr (OUT_IN) lb.load_rows(Wp, g.ldw, sRowB, s * C::BK, K, tid);
+            else lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
+        } else {
+            const int code = sExt[s - nk];
+            const int u = code >> 1;
+            const int e = code & 1;
+            la.load_masked(TE, g.lde, sRowA, sId, u, e * C::BK, tid);
+            lb.load_trans((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
+        }
     };
-    const int nk = (K + C::BK - 1) / C::BK;
-    la.load(X, g.ldx, sRowA, 0, K, tid);
-    load_b(0);
-    for (int kb = 0; kb < nk; ++kb) {
+    load_step(0);
+    for (int kb = 0; kb < total; ++kb) {
         T* sA = smem + (kb & 1) * C::STAGE;
         T* sB = sA + C::A_ELEMS;
         la.store(sA, tid);
         lb.store(sB, tid);
         __syncthreads();
-        if (kb + 1 < nk) {
-            la.load(X, g.ldx, sRowA, (kb + 1) * C::BK, K, tid);
-            load_b((kb + 1) * C::BK);
-        }
+        if (kb + 1 < total) load_step(kb + 1);
         mma_block<C>(acc, sA, sB, wm, wn, lane);
     }
-    __syncthreads();
-    if (g.t) lora_kext<C>(acc, P, g.t, g.ldt, sRowA, sId, &sNext, smem, n0, tid, wm, wn, lane);
 
     TY* Y = (TY*)g.y;
     const int lc = lane % C::BLK;
@@ -530,7 +689,8 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
                                                        const int32_t* __restrict__ seg_ids,
                                                        const int32_t* __restrict__ seg_off,
                                                        const int32_t* __restrict__ n_seg_p,
-                                                       float* __restrict__ t, int64_t ldt) {
+                                                       float* __restrict__ t, int64_t ldt,
+                                                       typename C::T* __restrict__ t_ext, int64_t lde) {
     using T = typename C::T;
     static_assert(C::BN == 64, "shrink tile covers ranks up to 64");
     __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
@@ -570,6 +730,8 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
         return;
     }
     const int r = P.ranks[u];
+    const float sc = P.scales[u];
+    const int ext_rank_cols = EXT_RANKS * ((r_max + EXT_RANKS - 1) / EXT_RANKS);
     const T* Au = (const T*)P.A + P.a_off[u];
     const bool vec = P.vec_a && ((r * (int)sizeof(T)) % 16) == 0;
     const int K = P.d_in;
@@ -603,7 +765,23 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
 #pragma unroll
             for (int q = 0; q < C::M::NACC; ++q) {
                 const int m = wm * C::WTM + i * C::BLK + C::M::row(lane, q);
-                if (m < cnt && col < r_max) t[(int64_t)sRow[m] * ldt + col] = acc.v[i][j][q];
+                if (m >= cnt) continue;
+                const float v = acc.v[i][j][q];
+                if (col < r_max) t[(int64_t)sRow[m] * ldt + col] = v;
+                if (t_ext && col < ext_rank_cols) {
+                    // columns past rank r are exact zeros (B side of the shrink was zero there)
+                    T* er = t_ext + (int64_t)sRow[m] * lde;
+                    const float sv = sc * v;
+                    if constexpr (sizeof(T) == 2) {
+                        const int e = col / EXT_RANKS;
+                        const int jj = col - e * EXT_RANKS;
+                        const bf16 hi = f32_to_bf16(sv);
+                        er[e * 64 + jj] = (T)hi;
+                        er[e * 64 + 32 + jj] = (T)f32_to_bf16(sv - to_f32(hi));
+                    } else {
+                        er[col] = (T)sv;
+                    }
+                }
             }
         }
 }
@@ -687,6 +865,7 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_expand(PoolDev P, const float* _
 // Tile configurations
 // ---------------------------------------------------------------------------
 
+using GemmHuge = Cfg<bf16, 256, 256, 64, 2, 4, 32>;
 using GemmBig = Cfg<bf16, 128, 128, 64, 2, 2, 32>;
 using GemmMid = Cfg<bf16, 64, 64, 64, 2, 2>;
 using GemmSmall = Cfg<bf16, 32, 64, 64, 2, 2>;
@@ -705,8 +884,10 @@ hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     g.ldw = a.ldw;
     g.ids = a.ids;
     g.n = a.n_rows;
-    g.t = a.t;
-    g.ldt = a.ldt;
+    g.t = nullptr;
+    g.ldt = 0;
+    g.t_ext = a.t_ext;
+    g.lde = a.lde;
     g.y = a.y;
     g.ldy = a.ldy;
     g.tiles_m = (int32_t)ceil_div(a.n_rows, C::BM);
@@ -730,6 +911,8 @@ hipError_t run_skinny(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     g.n = a.n_rows;
     g.t = a.t;
     g.ldt = a.ldt;
+    g.t_ext = nullptr;
+    g.lde = 0;
     g.y = a.y;
     g.ldy = a.ldy;
     g.tiles_m = 1;
@@ -745,13 +928,14 @@ hipError_t run_skinny(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
 
 template <typename TY>
 hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
-    if (a.w_out_in && a.n_rows <= 64) {
+    if (a.w_out_in && a.n_rows <= 64 && !a.t_ext) {
         if (a.n_rows <= 16) return run_skinny<TY, 1>(P, a, stream);
         if (a.n_rows <= 32) return run_skinny<TY, 2>(P, a, stream);
         return run_skinny<TY, 4>(P, a, stream);
     }
     // Largest tile that still gives about one workgroup per CU.
     auto tiles = [&](int bm, int bn) { return ceil_div(a.n_rows, bm) * ceil_div(P.d_out, bn); };
+    if (tiles(GemmHuge::BM, GemmHuge::BN) >= 200) return run_gemm<GemmHuge, TY>(P, a, stream);
     if (tiles(GemmBig::BM, GemmBig::BN) >= 200) return run_gemm<GemmBig, TY>(P, a, stream);
     if (tiles(GemmMid::BM, GemmMid::BN) >= 128 || a.n_rows > 32) return run_gemm<GemmMid, TY>(P, a, stream);
     return run_gemm<GemmSmall, TY>(P, a, stream);
@@ -772,17 +956,17 @@ static int64_t seg_tiles(int32_t n_rows, int32_t n_bins, int bm) {
 
 hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
                               const lora_segments_t* seg, int32_t n_rows, int32_t n_bins, float* t,
-                              int64_t ldt, bool, hipStream_t stream) {
+                              int64_t ldt, bool, hipStream_t stream, void* t_ext, int64_t lde) {
     if (dt == LORA_BF16) {
         dim3 grid((unsigned)seg_tiles(n_rows, n_bins, ShrinkB::BM));
         hipLaunchKernelGGL(k_sgmv_shrink<ShrinkB>, grid, dim3(ShrinkB::NT), 0, stream, P,
                            (const bf16*)x, ldx, seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, t,
-                           ldt);
+                           ldt, (bf16*)t_ext, lde);
     } else {
         dim3 grid((unsigned)seg_tiles(n_rows, n_bins, ShrinkF::BM));
         hipLaunchKernelGGL(k_sgmv_shrink<ShrinkF>, grid, dim3(ShrinkF::NT), 0, stream, P,
                            (const float*)x, ldx, seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, t,
-                           ldt);
+                           ldt, (float*)t_ext, lde);
     }
     return hipGetLastError();
 }
