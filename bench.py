@@ -52,11 +52,34 @@ def parse():
     ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB read + 256 MiB write kernel (counter calibration)")
     return ap.parse_args()
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def profiled_traffic(kernel, sources, profile):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    for line in open(path).read().splitlines():
+        if ":" in line and line.split(":")[0] in ("traffic_kernel", "traffic_bytes_per_launch", "source_hash"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("traffic_kernel") != kernel or fields.get("source_hash") != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 # ---------------------------------------------------------------------------
@@ -210,7 +233,11 @@ def bench_decode(torch, args):
         kernels_us=dict(decode_stream=round(d_stream * 1e6, 3), decode_finish=round(d_finish * 1e6, 3),
                         base_only_step=round(d_base * 1e6, 3), bgmv_shrink_standalone=round(d_shr * 1e6, 3)),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                      frac=round(achieved / HBM_PEAK_GBS, 4),
+                      traffic=profiled_traffic("k_decode_stream",
+                                               ["lora_bgmv_shrink_amd/csrc/decode.hip",
+                                                "lora_bgmv_shrink_amd/csrc/lora_internal.hpp"],
+                                               "decode_q4096_r16_rows32_traffic.md"),
                       kernel="k_decode_stream (split-K base partials + BGMV shrink partials)",
                       bytes_per_launch=stream_bytes, avg_launch_us=round(d_stream * 1e6, 3)),
         adapter_term=dict(
@@ -363,6 +390,14 @@ def main():
 
     log("bench: decode q_proj (BGMV) ...")
     dec, w0 = bench_decode(torch, args)
+    if args.copy_probe:
+        # a plain elementwise kernel of known size: reads 256 MiB, writes 256 MiB
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     extra = {}
     for name in [s for s in args.workloads.split(",") if s]:
         log(f"bench: workload {name} ...")
