@@ -82,7 +82,8 @@ __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_stream(PoolDev P
 #pragma unroll
         for (int l = 0; l < SHRINK_LOADS; ++l) {
             const int k = kc0 + ksub + l * KPT;
-            av[l] = (k < d_in) ? *(const uint4*)(Au + (int64_t)k * r) : uint4{0u, 0u, 0u, 0u};
+            // past d_in: read row 0 again; it meets x = 0 below
+            av[l] = *(const uint4*)(Au + (int64_t)(k < d_in ? k : 0) * r);
         }
         const int kn = min(KC, d_in - kc0);
         for (int k = tid; k < kn; k += SHRINK_THREADS) xs[k] = to_f32(xi[kc0 + k]);

@@ -73,12 +73,24 @@ __device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeA
     const int n = tn * DS_COLS + wave * 16 + lr;
     const bf16* Wt = (const bf16*)g.W + (int64_t)(n < N ? n : 0) * g.ldw;
 
+    // a whole slice inside K (the usual case) loads without branches
+    const bool full = (kend - kbeg == DS_USTEPS * 32);
     bf16x8_t bw[DS_USTEPS];
+    if (full) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int u = 0; u < DS_USTEPS; ++u) {
-        const int k = kbeg + u * 32 + kq;
-        const int valid = (u < nsteps) ? min(8, kend - k) : 0;
-        bw[u] = (valid > 0 && n < N) ? ld8(Wt + k, valid, true) : bf16x8_t{};
+        for (int u = 0; u < DS_USTEPS; ++u) {
+            // a column past d_out reads row 0 (Wt is clamped); its output is never stored
+            const u32x4 v = __builtin_nontemporal_load((const u32x4*)(Wt + kbeg + u * 32 + kq));
+            bw[u] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < DS_USTEPS; ++u) {
+            const int k = kbeg + u * 32 + kq;
+            const int valid = (u < nsteps) ? min(8, kend - k) : 0;
+            bw[u] = (valid > 0 && n < N) ? ld8(Wt + k, valid, true) : bf16x8_t{};
+        }
     }
 
     // x[0:16*MB][slice] -> LDS as [m][k] bf16, rows padded by 16 bytes
@@ -91,9 +103,14 @@ __device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeA
         const int m = v / per_row;
         const int c = (v - m * per_row) * 8;
         const int k = kbeg + c;
-        const int valid = min(8, kend - k);
-        bf16x8_t val = bf16x8_t{};
-        if (m < M && valid > 0) val = ld8(X + (int64_t)m * g.ldx + k, valid, false);
+        bf16x8_t val;
+        if (full) {
+            // rows past the batch read row 0; they only feed rows that are never stored
+            val = *(const bf16x8_t*)(X + (int64_t)(m < M ? m : 0) * g.ldx + k);
+        } else {
+            const int valid = min(8, kend - k);
+            val = (m < M && valid > 0) ? ld8(X + (int64_t)m * g.ldx + k, valid, false) : bf16x8_t{};
+        }
         *(bf16x8_t*)(xs + m * XLD + c) = val;
     }
     __syncthreads();
@@ -170,7 +187,8 @@ __device__ void stream_shrink(const PoolDev& P, const DecodePlan& D, const Decod
 #pragma unroll
             for (int l = 0; l < DS_SHRINK_LOADS; ++l) {
                 const int k = kc + ksub + l * KPT;
-                av[l] = (k < k1) ? *(const uint4*)(Au + (int64_t)k * r + jv * VE) : uint4{0u, 0u, 0u, 0u};
+                // past the slice: read row k0 again; it meets x = 0 below
+                av[l] = *(const uint4*)(Au + (int64_t)(k < k1 ? k : k0) * r + jv * VE);
             }
             __syncthreads();   // xs ready (first pass) / harmless afterwards
 #pragma unroll

@@ -131,8 +131,25 @@ struct RowLoader {
     static constexpr int NV = (TOT + C::NT - 1) / C::NT;
     uint4 reg[NV];
 
+    // Inside K (k0 + BK <= K, decided once per block) every lane issues its
+    // vector load unconditionally; rows past the end read row 0 and are
+    // zeroed afterwards, so no branch splits the batch of loads.
     __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, const int* sRow,
                                          int k0, int K, int tid) {
+        if (k0 + C::BK <= K) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int idx = tid + v * C::NT;
+                if (TOT % C::NT != 0 && idx >= TOT) break;
+                const int r = idx / VPR;
+                const int k = k0 + (idx - r * VPR) * C::VE;
+                // a row past the end reads row 0; it only feeds output rows that are
+                // never stored
+                const int gr = sRow[r];
+                reg[v] = *(const uint4*)(base + (int64_t)(gr >= 0 ? gr : 0) * ld + k);
+            }
+            return;
+        }
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int idx = tid + v * C::NT;
@@ -140,15 +157,11 @@ struct RowLoader {
             const int r = idx / VPR;
             const int k = k0 + (idx - r * VPR) * C::VE;
             const int gr = sRow[r];
-            if (gr >= 0 && k + C::VE <= K) {
-                reg[v] = *(const uint4*)(base + (int64_t)gr * ld + k);
-            } else {
-                union { uint4 u; T e[C::VE]; } tmp;
+            union { uint4 u; T e[C::VE]; } tmp;
 #pragma unroll
-                for (int e = 0; e < C::VE; ++e)
-                    tmp.e[e] = (gr >= 0 && k + e < K) ? base[(int64_t)gr * ld + k + e] : (T)0;
-                reg[v] = tmp.u;
-            }
+            for (int e = 0; e < C::VE; ++e)
+                tmp.e[e] = (gr >= 0 && k + e < K) ? base[(int64_t)gr * ld + k + e] : (T)0;
+            reg[v] = tmp.u;
         }
     }
     // rows whose sId differs from u load zeros (the K-extension operand)
@@ -160,7 +173,9 @@ struct RowLoader {
             if (TOT % C::NT != 0 && idx >= TOT) break;
             const int r = idx / VPR;
             const int k = k0 + (idx - r * VPR) * C::VE;
-            reg[v] = (sId[r] == u) ? *(const uint4*)(base + (int64_t)sRow[r] * ld + k) : uint4{0u, 0u, 0u, 0u};
+            const bool ok = sId[r] == u;   // implies sRow[r] >= 0
+            const uint4 val = *(const uint4*)(base + (int64_t)(ok ? sRow[r] : 0) * ld + k);
+            reg[v] = ok ? val : uint4{0u, 0u, 0u, 0u};
         }
     }
     __device__ __forceinline__ void store(T* s, int tid) const {
@@ -195,6 +210,19 @@ struct BLoader {
     __device__ __forceinline__ void load_rows(const T* __restrict__ base, int64_t ld, const int* sRow,
                                               int k0, int K, int tid) {
         kind = 0;
+        if (k0 + C::BK <= K) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int idx = tid + v * C::NT;
+                if (TOT % C::NT != 0 && idx >= TOT) break;
+                const int r = idx / R_VPR;
+                const int k = k0 + (idx - r * R_VPR) * VE;
+                // a column past the end reads row 0; its outputs are never stored
+                const int gr = sRow[r];
+                reg[v] = *(const uint4*)(base + (int64_t)(gr >= 0 ? gr : 0) * ld + k);
+            }
+            return;
+        }
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int idx = tid + v * C::NT;
@@ -202,21 +230,32 @@ struct BLoader {
             const int r = idx / R_VPR;
             const int k = k0 + (idx - r * R_VPR) * VE;
             const int gr = sRow[r];
-            if (gr >= 0 && k + VE <= K) {
-                reg[v] = *(const uint4*)(base + (int64_t)gr * ld + k);
-            } else {
-                union { uint4 u; T e[VE]; } tmp;
+            union { uint4 u; T e[VE]; } tmp;
 #pragma unroll
-                for (int e = 0; e < VE; ++e)
-                    tmp.e[e] = (gr >= 0 && k + e < K) ? base[(int64_t)gr * ld + k + e] : (T)0;
-                reg[v] = tmp.u;
-            }
+            for (int e = 0; e < VE; ++e)
+                tmp.e[e] = (gr >= 0 && k + e < K) ? base[(int64_t)gr * ld + k + e] : (T)0;
+            reg[v] = tmp.u;
         }
     }
     // k-row kr of the block reads source row j0 + (kr % kwrap), valid below kmax
     __device__ __forceinline__ void load_trans(const T* __restrict__ base, int64_t ld, int j0, int kwrap,
                                                int kmax, int n0, int N, bool vec, int tid) {
         kind = 1;
+        if (vec && n0 + C::BN <= N) {
+            // all columns in range: a row at or past kmax reads row j0 (a valid row
+            // of the same matrix); the A side is exactly zero at those k (x past
+            // d_in, t_ext past the rank), so it adds nothing
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int idx = tid + v * C::NT;
+                if (TOT % C::NT != 0 && idx >= TOT) break;
+                const int kr = idx / T_VPR;
+                const int k = j0 + kr % kwrap;
+                const int n = n0 + (idx - kr * T_VPR) * VE;
+                reg[v] = *(const uint4*)(base + (int64_t)(k < kmax ? k : j0) * ld + n);
+            }
+            return;
+        }
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int idx = tid + v * C::NT;
