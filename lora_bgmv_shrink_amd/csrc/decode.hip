@@ -31,8 +31,12 @@ constexpr int DS_NB = 8;            // 16-column MFMA blocks per base workgroup,
 constexpr int DS_COLS = DS_NB * 16;
 constexpr int DS_USTEPS = 16;       // k-steps (of 32) per base slice at most
 constexpr int DS_SHRINK_LOADS = 8;  // 16-byte A loads in flight per thread (shrink)
-constexpr int FIN_THREADS = 256;    // finish workgroup: 4 waves, 4 columns per thread
+#ifndef LORA_FIN_THREADS
+#define LORA_FIN_THREADS 64
+#endif
+constexpr int FIN_THREADS = LORA_FIN_THREADS;   // finish workgroup, 4 columns per thread
 constexpr int FIN_COLS = FIN_THREADS * 4;
+static_assert(FIN_THREADS >= 64 && FIN_THREADS % 64 == 0, "the t partials need one thread per rank");
 constexpr int FIN_RCHUNK = 16;      // rank rows of B loaded together in the finish
 constexpr int FIN_SCHUNK = 8;       // partial slices loaded together in the finish
 
@@ -55,8 +59,9 @@ __device__ __forceinline__ bf16x8_t ld8(const bf16* p, int valid, bool nt) {
 // slice ks.  x rows of the slice are staged once in LDS; wave w streams the
 // 16 rows of W^T for column block w (all of the slice's k-steps in flight,
 // nontemporal: W is read once) and keeps the whole 16-column partial.
-template <int MB>
-__device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b, uint8_t* lds) {
+template <int MB, bool FULL>
+__device__ __forceinline__ void stream_base_body(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
+                                                 int b, uint8_t* lds) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -73,10 +78,34 @@ __device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeA
     const int n = tn * DS_COLS + wave * 16 + lr;
     const bf16* Wt = (const bf16*)g.W + (int64_t)(n < N ? n : 0) * g.ldw;
 
-    // a whole slice inside K (the usual case) loads without branches
-    const bool full = (kend - kbeg == DS_USTEPS * 32);
+
+    // x[0:16*MB][slice] -> LDS as [m][k] bf16, rows padded by 16 bytes.  The
+    // x pieces are requested before W: they come from L2 and return first, so
+    // they are staged while the W stream is still in flight.
+    constexpr int XLD = DS_USTEPS * 32 + 8;
+    static_assert(MB * 16 * XLD * 2 <= DS_LDS_BYTES, "staged x does not fit the LDS block");
+    constexpr int PER_ROW = DS_USTEPS * 32 / 8;    // 16-byte pieces per staged row
+    constexpr int XV = (MB * 16 * PER_ROW + DS_THREADS - 1) / DS_THREADS;
+    static_assert(MB * 16 * PER_ROW % DS_THREADS == 0, "x pieces do not split evenly");
+    bf16* xs = (bf16*)lds;
+    const bf16* X = (const bf16*)g.x;
+    bf16x8_t xv[XV];
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+        const int v = tid + q * DS_THREADS;
+        const int m = v / PER_ROW;
+        const int k = kbeg + (v - m * PER_ROW) * 8;
+        if constexpr (FULL) {
+            // rows past the batch read row 0; they only feed rows that are never stored
+            xv[q] = *(const bf16x8_t*)(X + (int64_t)(m < M ? m : 0) * g.ldx + k);
+        } else {
+            const int valid = min(8, kend - k);
+            xv[q] = (m < M && valid > 0) ? ld8(X + (int64_t)m * g.ldx + k, valid, false) : bf16x8_t{};
+        }
+    }
+
     bf16x8_t bw[DS_USTEPS];
-    if (full) {
+    if constexpr (FULL) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int u = 0; u < DS_USTEPS; ++u) {
@@ -93,25 +122,11 @@ __device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeA
         }
     }
 
-    // x[0:16*MB][slice] -> LDS as [m][k] bf16, rows padded by 16 bytes
-    constexpr int XLD = DS_USTEPS * 32 + 8;
-    static_assert(MB * 16 * XLD * 2 <= DS_LDS_BYTES, "staged x does not fit the LDS block");
-    bf16* xs = (bf16*)lds;
-    const bf16* X = (const bf16*)g.x;
-    const int per_row = DS_USTEPS * 32 / 8;    // 16-byte pieces per staged row
-    for (int v = tid; v < MB * 16 * per_row; v += DS_THREADS) {
-        const int m = v / per_row;
-        const int c = (v - m * per_row) * 8;
-        const int k = kbeg + c;
-        bf16x8_t val;
-        if (full) {
-            // rows past the batch read row 0; they only feed rows that are never stored
-            val = *(const bf16x8_t*)(X + (int64_t)(m < M ? m : 0) * g.ldx + k);
-        } else {
-            const int valid = min(8, kend - k);
-            val = (m < M && valid > 0) ? ld8(X + (int64_t)m * g.ldx + k, valid, false) : bf16x8_t{};
-        }
-        *(bf16x8_t*)(xs + m * XLD + c) = val;
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+        const int v = tid + q * DS_THREADS;
+        const int m = v / PER_ROW;
+        *(bf16x8_t*)(xs + m * XLD + (v - m * PER_ROW) * 8) = xv[q];
     }
     __syncthreads();
 
@@ -120,7 +135,7 @@ __device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeA
     for (int i = 0; i < MB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < DS_USTEPS; ++u) {
-        if (u < nsteps) {
+        if (FULL || u < nsteps) {
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 const bf16x8_t a = *(const bf16x8_t*)(xs + (i * 16 + lr) * XLD + u * 32 + kq);
@@ -140,6 +155,16 @@ __device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeA
                 if (m < M) out[(int64_t)m * N] = acc[i][q];
             }
     }
+}
+
+// A slice wholly inside K (the usual case) takes the branch-free form, whose
+// wait counts let x be staged while W is still arriving.
+template <int MB>
+__device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b, uint8_t* lds) {
+    const int ks = b / D.tiles_n;
+    const int kbeg = ks * D.kslice;
+    if (min(P.d_in, kbeg + D.kslice) - kbeg == DS_USTEPS * 32) stream_base_body<MB, true>(P, D, g, b, lds);
+    else stream_base_body<MB, false>(P, D, g, b, lds);
 }
 
 // Partial shrink of row i over k-rows [k0, k1): the streaming pattern of the
@@ -245,9 +270,10 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_stream(PoolDev P, DecodeP
 }
 
 // Finish: workgroup (m, chunk) owns FIN_COLS columns of row m, 4 per thread.
-// The row's B rows are requested first (they depend only on the row
-// record), then the base partials; the t partials are summed into LDS in
-// slice order while those loads are in flight.
+// Loads go out in the order their addresses are known: the base partials
+// first (they need nothing), then the row's t partials and B rows (after the
+// row record).  The t partials are summed into LDS in slice order while the
+// other loads are in flight.
 template <typename TY>
 __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, DecodePlan D, DecodeArgs g) {
     __shared__ float st[64];
@@ -257,6 +283,29 @@ __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, Decode
     const int c0 = (blockIdx.x - m * nch) * FIN_COLS + tid * 4;
     const int N = P.d_out;
     const int M = g.n;
+    const bool in = c0 < N;
+    const bool full = c0 + 4 <= N;
+    const bool vp = full && (N % 4 == 0);
+    const int cc = in ? c0 : 0;   // columns past d_out read column 0 and are not stored
+
+    // base partials, FIN_SCHUNK slices requested together, added in slice order
+    auto load_part = [&](int s0, float4* u) {
+#pragma unroll
+        for (int q = 0; q < FIN_SCHUNK; ++q) {
+            const float* p = g.part_base + ((int64_t)(s0 + q < D.base_slices ? s0 + q : 0) * M + m) * N + cc;
+            if (vp) {
+                u[q] = *(const float4*)p;
+            } else {
+                u[q].x = p[0];
+                u[q].y = (cc + 1 < N) ? p[1] : 0.f;
+                u[q].z = (cc + 2 < N) ? p[2] : 0.f;
+                u[q].w = (cc + 3 < N) ? p[3] : 0.f;
+            }
+        }
+    };
+    float4 u[FIN_SCHUNK];
+    load_part(0, u);
+
     int r = 0;
     int64_t boff = 0;
     float sc = 0.f;
@@ -266,72 +315,55 @@ __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, Decode
         boff = rec.b_off;
         sc = rec.scale;
     }
-    const bool in = c0 < N;
-    const bool full = c0 + 4 <= N;
-    const bf16* Bu = (const bf16*)P.B + boff + c0;
+    float tp[FIN_SCHUNK];
+    if (r > 0 && tid < r) {
+#pragma unroll
+        for (int q = 0; q < FIN_SCHUNK; ++q)
+            tp[q] = (q < D.t_slices) ? g.part_t[((int64_t)q * M + m) * 64 + tid] : 0.f;
+    }
+    const bf16* Bu = (const bf16*)P.B + boff + cc;
     const bool vb = full && P.vec_b;
-
-    float e4[4] = {0.f, 0.f, 0.f, 0.f};
     uint2 bv[FIN_RCHUNK];
-    int j0 = 0;
-    if (in && r > 0) {
+    auto load_b = [&](int j0) {
 #pragma unroll
         for (int q = 0; q < FIN_RCHUNK; ++q) {
-            const int j = q;
+            const int j = j0 + q;
             if (j < r && vb) {
                 bv[q] = *(const uint2*)(Bu + (int64_t)j * N);
             } else {
                 union { uint2 u; bf16 e[4]; } w;
-                for (int e = 0; e < 4; ++e) w.e[e] = (j < r && c0 + e < N) ? Bu[(int64_t)j * N + e] : (bf16)0;
+                for (int e = 0; e < 4; ++e) w.e[e] = (j < r && cc + e < N) ? Bu[(int64_t)j * N + e] : (bf16)0;
                 bv[q] = w.u;
             }
         }
-    }
-    // partial sums, FIN_SCHUNK slices requested together, added in slice order
+    };
+    if (r > 0) load_b(0);
+
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (in) {
-        const bool vp = full && (N % 4 == 0);
-        for (int s0 = 0; s0 < D.base_slices; s0 += FIN_SCHUNK) {
-            float4 u[FIN_SCHUNK];
+    for (int s0 = 0;;) {
 #pragma unroll
-            for (int q = 0; q < FIN_SCHUNK; ++q) {
-                const float* p = g.part_base + ((int64_t)(s0 + q) * M + m) * N + c0;
-                if (s0 + q >= D.base_slices) {
-                    u[q] = float4{0.f, 0.f, 0.f, 0.f};
-                } else if (vp) {
-                    u[q] = *(const float4*)p;
-                } else {
-                    u[q].x = p[0];
-                    u[q].y = (c0 + 1 < N) ? p[1] : 0.f;
-                    u[q].z = (c0 + 2 < N) ? p[2] : 0.f;
-                    u[q].w = (c0 + 3 < N) ? p[3] : 0.f;
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < FIN_SCHUNK; ++q) {
-                if (s0 + q < D.base_slices) {
-                    v[0] += u[q].x; v[1] += u[q].y; v[2] += u[q].z; v[3] += u[q].w;
-                }
+        for (int q = 0; q < FIN_SCHUNK; ++q) {
+            if (s0 + q < D.base_slices) {
+                v[0] += u[q].x; v[1] += u[q].y; v[2] += u[q].z; v[3] += u[q].w;
             }
         }
+        s0 += FIN_SCHUNK;
+        if (s0 >= D.base_slices) break;
+        load_part(s0, u);
     }
     if (r > 0 && tid < r) {
         float t = 0.f;
-        for (int s0 = 0; s0 < D.t_slices; s0 += FIN_SCHUNK) {
-            float u[FIN_SCHUNK];
 #pragma unroll
-            for (int q = 0; q < FIN_SCHUNK; ++q)
-                u[q] = (s0 + q < D.t_slices) ? g.part_t[((int64_t)(s0 + q) * M + m) * 64 + tid] : 0.f;
-#pragma unroll
-            for (int q = 0; q < FIN_SCHUNK; ++q)
-                if (s0 + q < D.t_slices) t += u[q];
-        }
+        for (int q = 0; q < FIN_SCHUNK; ++q)
+            if (q < D.t_slices) t += tp[q];
+        for (int s = FIN_SCHUNK; s < D.t_slices; ++s) t += g.part_t[((int64_t)s * M + m) * 64 + tid];
         st[tid] = t;
     }
     __syncthreads();
     if (!in) return;
     if (r > 0) {
-        for (;;) {
+        float e4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j0 = 0;;) {
 #pragma unroll
             for (int q = 0; q < FIN_RCHUNK; ++q) {
                 const float tj = (j0 + q < r) ? st[j0 + q] : 0.f;
@@ -342,17 +374,7 @@ __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, Decode
             }
             j0 += FIN_RCHUNK;
             if (j0 >= r) break;
-#pragma unroll
-            for (int q = 0; q < FIN_RCHUNK; ++q) {
-                const int j = j0 + q;
-                if (j < r && vb) {
-                    bv[q] = *(const uint2*)(Bu + (int64_t)j * N);
-                } else {
-                    union { uint2 u; bf16 e[4]; } w;
-                    for (int e = 0; e < 4; ++e) w.e[e] = (j < r && c0 + e < N) ? Bu[(int64_t)j * N + e] : (bf16)0;
-                    bv[q] = w.u;
-                }
-            }
+            load_b(j0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += sc * e4[e];

@@ -98,27 +98,48 @@ struct Acc {
     }
 };
 
-// acc += sA[wave rows][0:BK] x sB[wave cols][0:BK]^T
+// acc += sA[wave rows][0:BK] x sB[wave cols][0:BK]^T.  The fragments of
+// k-substep s+1 are requested from LDS before (or, for A with a large
+// accumulator, right after) the MFMAs of substep s that last read them, so
+// LDS latency overlaps the matrix-core work.  A wave whose accumulator takes
+// more than 96 registers keeps one set of A fragments, reloading each as soon
+// as its row of MFMAs has issued, so that the tile still fits 256 registers.
 template <class C>
 __device__ __forceinline__ void mma_block(Acc<C>& acc, const typename C::T* sA,
                                           const typename C::T* sB, int wm, int wn, int lane) {
     using T = typename C::T;
     using M = typename C::M;
+    constexpr int NSUB = C::BK / M::KSTEP;
+    constexpr bool ROLL_A = C::FM * C::FN * M::NACC > 96;
+    constexpr int NA = ROLL_A ? 1 : 2;
     const int lr = lane % C::BLK;
     const int kq = (lane / C::BLK) * M::KPL;
     const T* pa = sA + (wm * C::WTM + lr) * C::LDK + kq;
     const T* pb = sB + (wn * C::WTN + lr) * C::LDK + kq;
+    typename M::frag a[NA][C::FM], b[2][C::FN];
 #pragma unroll
-    for (int kk = 0; kk < C::BK; kk += M::KSTEP) {
-        typename M::frag a[C::FM], b[C::FN];
+    for (int i = 0; i < C::FM; ++i) a[0][i] = M::ld(pa + i * C::BLK * C::LDK);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = M::ld(pa + i * C::BLK * C::LDK + kk);
+    for (int j = 0; j < C::FN; ++j) b[0][j] = M::ld(pb + j * C::BLK * C::LDK);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = M::ld(pb + j * C::BLK * C::LDK + kk);
+    for (int s = 0; s < NSUB; ++s) {
+        const int cur = s & 1;
+        const int ca = ROLL_A ? 0 : cur;
+        const int kk = (s + 1) * M::KSTEP;
+        if (s + 1 < NSUB) {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+            for (int j = 0; j < C::FN; ++j) b[cur ^ 1][j] = M::ld(pb + j * C::BLK * C::LDK + kk);
+            if (!ROLL_A) {
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) acc.v[i][j] = M::mma(a[i], b[j], acc.v[i][j]);
+                for (int i = 0; i < C::FM; ++i) a[ca ^ 1][i] = M::ld(pa + i * C::BLK * C::LDK + kk);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) acc.v[i][j] = M::mma(a[ca][i], b[cur][j], acc.v[i][j]);
+            if (ROLL_A && s + 1 < NSUB) a[0][i] = M::ld(pa + i * C::BLK * C::LDK + kk);
+        }
     }
 }
 
@@ -205,11 +226,9 @@ struct BLoader {
     static constexpr int TOT = C::BN * C::BK / VE;  // same count for both
     static constexpr int NV = (TOT + C::NT - 1) / C::NT;
     uint4 reg[NV];
-    int kind;
 
     __device__ __forceinline__ void load_rows(const T* __restrict__ base, int64_t ld, const int* sRow,
                                               int k0, int K, int tid) {
-        kind = 0;
         if (k0 + C::BK <= K) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
@@ -240,7 +259,6 @@ struct BLoader {
     // k-row kr of the block reads source row j0 + (kr % kwrap), valid below kmax
     __device__ __forceinline__ void load_trans(const T* __restrict__ base, int64_t ld, int j0, int kwrap,
                                                int kmax, int n0, int N, bool vec, int tid) {
-        kind = 1;
         if (vec && n0 + C::BN <= N) {
             // all columns in range: a row at or past kmax reads row j0 (a valid row
             // of the same matrix); the A side is exactly zero at those k (x past
@@ -274,28 +292,27 @@ struct BLoader {
             }
         }
     }
-    __device__ __forceinline__ void store(T* s, int tid) const {
-        if (kind == 0) {
+    __device__ __forceinline__ void store_rows(T* s, int tid) const {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int idx = tid + v * C::NT;
-                if (TOT % C::NT != 0 && idx >= TOT) break;
-                const int r = idx / R_VPR;
-                const int c = (idx - r * R_VPR) * VE;
-                *(uint4*)(s + r * C::LDK + c) = reg[v];
-            }
-        } else {
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int r = idx / R_VPR;
+            const int c = (idx - r * R_VPR) * VE;
+            *(uint4*)(s + r * C::LDK + c) = reg[v];
+        }
+    }
+    __device__ __forceinline__ void store_trans(T* s, int tid) const {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int idx = tid + v * C::NT;
-                if (TOT % C::NT != 0 && idx >= TOT) break;
-                const int kr = idx / T_VPR;
-                const int c = (idx - kr * T_VPR) * VE;
-                union { uint4 u; T e[VE]; } tmp;
-                tmp.u = reg[v];
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int kr = idx / T_VPR;
+            const int c = (idx - kr * T_VPR) * VE;
+            union { uint4 u; T e[VE]; } tmp;
+            tmp.u = reg[v];
 #pragma unroll
-                for (int e = 0; e < VE; ++e) s[(c + e) * C::LDK + kr] = tmp.e[e];
-            }
+            for (int e = 0; e < VE; ++e) s[(c + e) * C::LDK + kr] = tmp.e[e];
         }
     }
 };
@@ -576,27 +593,41 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     const T* TE = (const T*)g.t_ext;
     RowLoader<C, C::BM> la;
     BLoader<C> lb;
-    auto load_step = [&](int s) {
-        if (s < nk) {
-            la.load(X, g.ldx, sRowA, s * C::BK, K, tid);
-            if constexpr (OUT_IN) lb.load_rows(Wp, g.ldw, sRowB, s * C::BK, K, tid);
-            else lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
-        } else {
-            const int code = sExt[s - nk];
-            const int u = code >> 1;
-            const int e = code & 1;
-            la.load_masked(TE, g.lde, sRowA, sId, u, e * C::BK, tid);
-            lb.load_trans((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
-        }
+    auto load_main = [&](int s) {
+        la.load(X, g.ldx, sRowA, s * C::BK, K, tid);
+        if constexpr (OUT_IN) lb.load_rows(Wp, g.ldw, sRowB, s * C::BK, K, tid);
+        else lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
     };
-    load_step(0);
-    for (int kb = 0; kb < total; ++kb) {
+    auto load_ext = [&](int s) {
+        const int code = sExt[s];
+        const int u = code >> 1;
+        const int e = code & 1;
+        la.load_masked(TE, g.lde, sRowA, sId, u, e * C::BK, tid);
+        lb.load_trans((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
+    };
+    const int n_ext = total - nk;
+    // x W over d_in, two LDS stages, next block prefetched into registers
+    load_main(0);
+    for (int kb = 0; kb < nk; ++kb) {
         T* sA = smem + (kb & 1) * C::STAGE;
         T* sB = sA + C::A_ELEMS;
         la.store(sA, tid);
-        lb.store(sB, tid);
+        if constexpr (OUT_IN) lb.store_rows(sB, tid);
+        else lb.store_trans(sB, tid);
         __syncthreads();
-        if (kb + 1 < total) load_step(kb + 1);
+        if (kb + 1 < nk) load_main(kb + 1);
+        else if (n_ext > 0) load_ext(0);
+        mma_block<C>(acc, sA, sB, wm, wn, lane);
+    }
+    // the LoRA K-extension blocks, same pipeline
+    for (int e = 0; e < n_ext; ++e) {
+        const int kb = nk + e;
+        T* sA = smem + (kb & 1) * C::STAGE;
+        T* sB = sA + C::A_ELEMS;
+        la.store(sA, tid);
+        lb.store_trans(sB, tid);
+        __syncthreads();
+        if (e + 1 < n_ext) load_ext(e + 1);
         mma_block<C>(acc, sA, sB, wm, wn, lane);
     }
 
