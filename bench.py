@@ -164,9 +164,15 @@ def bench_decode(torch, args):
     def finish(r):
         b.lora_decode_finish(r["pool"], r["ids"], r["ws"], r["y"], True)
 
-    def base_step(r):
+    def base_stream(r):
         b.lora_decode_stream(r["pool"], r["p"].x, r["Wt"], r["ids"], r["wsb"], False)
+
+    def base_finish(r):
         b.lora_decode_finish(r["pool"], r["ids"], r["wsb"], r["yb"], False)
+
+    def base_step(r):
+        base_stream(r)
+        base_finish(r)
 
     def step(r):
         stream(r)
@@ -207,6 +213,8 @@ def bench_decode(torch, args):
     d_stream = time_graph(torch, g_stream, kr) / R
     d_finish = time_graph(torch, g_finish, kr) / R
     d_base = time_graph(torch, g_base, kr) / R
+    d_bstream = time_graph(torch, capture(torch, lambda: [base_stream(r) for r in reps]), kr) / R
+    d_bfinish = time_graph(torch, capture(torch, lambda: [base_finish(r) for r in reps]), kr) / R
     d_step = time_graph(torch, g_full, max(1, kr // 2)) / R
 
     # the standalone BGMV shrink entry point on the same batch
@@ -231,7 +239,9 @@ def bench_decode(torch, args):
         tokens_per_s=n / sec_step,
         gpu_step_s=d_step,
         kernels_us=dict(decode_stream=round(d_stream * 1e6, 3), decode_finish=round(d_finish * 1e6, 3),
-                        base_only_step=round(d_base * 1e6, 3), bgmv_shrink_standalone=round(d_shr * 1e6, 3)),
+                        base_only_step=round(d_base * 1e6, 3), base_only_stream=round(d_bstream * 1e6, 3),
+                        base_only_finish=round(d_bfinish * 1e6, 3),
+                        bgmv_shrink_standalone=round(d_shr * 1e6, 3)),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4),
                       traffic=profiled_traffic("k_decode_stream",

@@ -8,13 +8,12 @@
 // into many small independent pieces, and partial sums meet at the kernel
 // boundary (an in-kernel cross-XCD hand-off costs more than the whole pass):
 //
-//   stream: workgroups of two kinds in one launch
-//     base:   128 output columns x one K slice: x rows of the slice staged
-//             in LDS, each wave streams the W rows of 16 columns and writes
-//             its fp32 partial part_base[slice][m][n];
-//     shrink: one row x one K slice of its adapter: partial x_i A_a over
-//             the slice, written as part_t[slice][i][j] (BGMV: the row
-//             gathers its own adapter).
+//   stream: workgroup (tn, ks) owns 128 output columns and K slice ks.  The
+//           x rows of the slice are staged once in LDS; each wave streams the
+//           W rows of 16 columns and the workgroup writes the fp32 partial
+//           part_base[ks][m][n].  Over the same staged x it also shrinks the
+//           rows i = tn, tn + tiles_n, ... : x_i A_a over the slice (BGMV: the
+//           row gathers its own adapter), written as part_t[ks][i][j].
 //   finish: y[m][n] = sum_slices part_base + s_a * sum_j (sum_slices part_t)[j]
 //           * B_a[j][n], rounded once.
 //
@@ -26,15 +25,13 @@
 namespace lora {
 namespace {
 
-constexpr int DS_THREADS = 512;     // 8 waves
+constexpr int DS_BASE_THREADS = 512;                // 8 base waves, 16 columns each
+constexpr int DS_THREADS = DS_BASE_THREADS + 64;    // + the shrink wave
 constexpr int DS_NB = 8;            // 16-column MFMA blocks per base workgroup, one per wave
 constexpr int DS_COLS = DS_NB * 16;
 constexpr int DS_USTEPS = 16;       // k-steps (of 32) per base slice at most
-constexpr int DS_SHRINK_LOADS = 8;  // 16-byte A loads in flight per thread (shrink)
-#ifndef LORA_FIN_THREADS
-#define LORA_FIN_THREADS 64
-#endif
-constexpr int FIN_THREADS = LORA_FIN_THREADS;   // finish workgroup, 4 columns per thread
+constexpr int DS_SHRINK_LOADS = 16; // 16-byte A pieces in flight per lane of the shrink wave
+constexpr int FIN_THREADS = 64;     // finish workgroup (one wave), 4 columns per thread
 constexpr int FIN_COLS = FIN_THREADS * 4;
 static_assert(FIN_THREADS >= 64 && FIN_THREADS % 64 == 0, "the t partials need one thread per rank");
 constexpr int FIN_RCHUNK = 16;      // rank rows of B loaded together in the finish
@@ -55,13 +52,90 @@ __device__ __forceinline__ bf16x8_t ld8(const bf16* p, int valid, bool nt) {
     return u.v;
 }
 
-// Base part: workgroup (tn, ks) owns columns [tn*128, +128) and k-rows of
-// slice ks.  x rows of the slice are staged once in LDS; wave w streams the
-// 16 rows of W^T for column block w (all of the slice's k-steps in flight,
-// nontemporal: W is read once) and keeps the whole 16-column partial.
+// Shrink wave of workgroup (tn, ks): rows i = tn, tn + tiles_n, ...; for
+// each, part_t[ks][i][0:r] = x_i[slice] A_a[slice] over the staged x row, and
+// (slice 0) the row record for the finish pass.  A wave of its own, with its
+// own load counter, so its A pieces stream while the base waves still wait
+// for W.  Ranks the pool holds that divide 4096 (G = r / 8 lanes per k-row, a
+// power of two) take 16-byte pieces: lane l owns columns (l % G) * 8 .. + 8 of
+// k-rows l / G + p * (64 / G).
+__device__ __forceinline__ void shrink_wave(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int tn,
+                                            int ks, int kbeg, int klen, const bf16* xs, int xld, int lane) {
+    const int M = g.n;
+    __syncthreads();   // x staged by the base waves
+    for (int i = tn; i < M; i += D.tiles_n) {
+        const int a = uload(g.ids, i);
+        const bool ok = id_ok(a, P.n_adapters);
+        const int r = ok ? uload(P.ranks, a) : 0;
+        if (ks == 0 && lane == 0) {
+            // row record for the finish pass: B block offset, rank (0: no term), scale
+            RowRec rec;
+            rec.b_off = ok ? uload(P.b_off, a) : 0;
+            rec.rank = r;
+            rec.scale = ok ? uload(P.scales, a) : 0.f;
+            g.rows[i] = rec;
+            if (!ok && a != -1) flag_bad_id(P.err);
+        }
+        if (r == 0) continue;   // the finish pass never reads t for such rows
+        const bf16* Au = (const bf16*)P.A + uload(P.a_off, a) + (int64_t)kbeg * r;
+        const bf16* xi = xs + i * xld;
+        float* outp = g.part_t + ((int64_t)ks * M + i) * 64;
+        if (P.stream_ok) {
+            const int G = r / 8;
+            const int RPP = 64 / G;   // k-rows per pass
+            const int passes = (klen + RPP - 1) / RPP;
+            const int jv = lane % G;
+            const int ksub = lane / G;
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+            for (int p0 = 0; p0 < passes; p0 += DS_SHRINK_LOADS) {
+                uint4 av[DS_SHRINK_LOADS];
+#pragma unroll
+                for (int q = 0; q < DS_SHRINK_LOADS; ++q) {
+                    const int kk = ksub + (p0 + q) * RPP;
+                    // past the slice: read its first k-row again; it meets x = 0 below
+                    av[q] = *(const uint4*)(Au + (int64_t)(kk < klen ? kk : 0) * r + jv * 8);
+                }
+#pragma unroll
+                for (int q = 0; q < DS_SHRINK_LOADS; ++q) {
+                    const int kk = ksub + (p0 + q) * RPP;
+                    const float xv = (kk < klen) ? to_f32(xi[kk]) : 0.f;
+                    union { uint4 u; bf16 e[8]; } v;
+                    v.u = av[q];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += xv * to_f32(v.e[e]);
+                }
+            }
+            for (int d = G; d < 64; d <<= 1)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], d, 64);
+            if (lane < G)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) outp[lane * 8 + e] = acc[e];
+        } else {
+            // any rank: lane (j, gq) sums column j over k-rows gq, gq + Gs, ...;
+            // the groups are then added in order gq = 0, 1, ...
+            const int Gs = 64 / r;
+            const int j = lane % r;
+            const int gq = lane / r;
+            float acc = 0.f;
+            if (gq < Gs)
+                for (int kk = gq; kk < klen; kk += Gs) acc += to_f32(xi[kk]) * to_f32(Au[(int64_t)kk * r + j]);
+            float v = acc;
+            for (int q = 1; q < Gs; ++q) v += __shfl(acc, j + q * r, 64);
+            if (lane < r) outp[lane] = v;
+        }
+    }
+}
+
+// Workgroup (tn, ks): base wave w < 8 streams the 16 rows of W^T for column
+// block w (all of the slice's k-steps in flight, nontemporal: W is read once)
+// and keeps the whole 16-column partial; x of the slice is staged in LDS and
+// serves the MFMAs and the shrink wave.
 template <int MB, bool FULL>
-__device__ __forceinline__ void stream_base_body(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
-                                                 int b, uint8_t* lds) {
+__device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b,
+                                            uint8_t* lds) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -72,12 +146,12 @@ __device__ __forceinline__ void stream_base_body(const PoolDev& P, const DecodeP
     const int M = g.n;
     const int kbeg = ks * D.kslice;
     const int kend = min(K, kbeg + D.kslice);
-    const int nsteps = (kend - kbeg + 31) / 32;
+    const int klen = kend - kbeg;
+    const int nsteps = (klen + 31) / 32;
     const int lr = lane & 15;
     const int kq = (lane >> 4) * 8;
     const int n = tn * DS_COLS + wave * 16 + lr;
     const bf16* Wt = (const bf16*)g.W + (int64_t)(n < N ? n : 0) * g.ldw;
-
 
     // x[0:16*MB][slice] -> LDS as [m][k] bf16, rows padded by 16 bytes.  The
     // x pieces are requested before W: they come from L2 and return first, so
@@ -85,14 +159,19 @@ __device__ __forceinline__ void stream_base_body(const PoolDev& P, const DecodeP
     constexpr int XLD = DS_USTEPS * 32 + 8;
     static_assert(MB * 16 * XLD * 2 <= DS_LDS_BYTES, "staged x does not fit the LDS block");
     constexpr int PER_ROW = DS_USTEPS * 32 / 8;    // 16-byte pieces per staged row
-    constexpr int XV = (MB * 16 * PER_ROW + DS_THREADS - 1) / DS_THREADS;
-    static_assert(MB * 16 * PER_ROW % DS_THREADS == 0, "x pieces do not split evenly");
+    constexpr int XV = MB * 16 * PER_ROW / DS_BASE_THREADS;
+    static_assert(MB * 16 * PER_ROW % DS_BASE_THREADS == 0, "x pieces do not split evenly");
     bf16* xs = (bf16*)lds;
+    if (wave == DS_NB) {
+        if (g.with_lora) shrink_wave(P, D, g, tn, ks, kbeg, klen, xs, XLD, lane);
+        else __syncthreads();
+        return;
+    }
     const bf16* X = (const bf16*)g.x;
     bf16x8_t xv[XV];
 #pragma unroll
     for (int q = 0; q < XV; ++q) {
-        const int v = tid + q * DS_THREADS;
+        const int v = tid + q * DS_BASE_THREADS;
         const int m = v / PER_ROW;
         const int k = kbeg + (v - m * PER_ROW) * 8;
         if constexpr (FULL) {
@@ -124,7 +203,7 @@ __device__ __forceinline__ void stream_base_body(const PoolDev& P, const DecodeP
 
 #pragma unroll
     for (int q = 0; q < XV; ++q) {
-        const int v = tid + q * DS_THREADS;
+        const int v = tid + q * DS_BASE_THREADS;
         const int m = v / PER_ROW;
         *(bf16x8_t*)(xs + m * XLD + (v - m * PER_ROW) * 8) = xv[q];
     }
@@ -157,124 +236,24 @@ __device__ __forceinline__ void stream_base_body(const PoolDev& P, const DecodeP
     }
 }
 
-// A slice wholly inside K (the usual case) takes the branch-free form, whose
-// wait counts let x be staged while W is still arriving.
-template <int MB>
-__device__ void stream_base(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b, uint8_t* lds) {
-    const int ks = b / D.tiles_n;
-    const int kbeg = ks * D.kslice;
-    if (min(P.d_in, kbeg + D.kslice) - kbeg == DS_USTEPS * 32) stream_base_body<MB, true>(P, D, g, b, lds);
-    else stream_base_body<MB, false>(P, D, g, b, lds);
-}
-
-// Partial shrink of row i over k-rows [k0, k1): the streaming pattern of the
-// BGMV shrink (thread t owns columns (t % G) * 8 .. + 8 of every
-// (DS_THREADS / G)-th k-row), with x staged in LDS.
-__device__ void stream_shrink(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b, uint8_t* lds) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int i = b / D.t_slices;
-    const int s = b - i * D.t_slices;
-    const int a = g.ids[i];
-    float* outp = g.part_t + ((int64_t)s * g.n + i) * 64;
-    const bool ok = id_ok(a, P.n_adapters);
-    if (s == 0 && tid == 0) {
-        // row record for the finish pass: B block offset, rank (0: no term), scale
-        RowRec rec;
-        rec.b_off = ok ? P.b_off[a] : 0;
-        rec.rank = ok ? P.ranks[a] : 0;
-        rec.scale = ok ? P.scales[a] : 0.f;
-        g.rows[i] = rec;
-        if (!ok && a != -1) flag_bad_id(P.err);
-    }
-    if (!ok) return;   // the finish pass never reads t for such rows
-    const int r = P.ranks[a];
-    const int k0 = s * D.t_kslice;
-    const int k1 = min(P.d_in, k0 + D.t_kslice);
-    float* xs = (float*)lds;                                    // t_kslice floats
-    float (*red)[64] = (float (*)[64])(lds + D.t_kslice * 4);   // [8][64]
-    const bf16* xi = (const bf16*)g.x + (int64_t)i * g.ldx;
-    for (int k = k0 + tid; k < k1; k += DS_THREADS) xs[k - k0] = to_f32(xi[k]);
-
-    const bf16* Au = (const bf16*)P.A + P.a_off[a];
-    if (P.stream_ok) {
-        constexpr int VE = 8;
-        const int G = r / VE;
-        const int KPT = DS_THREADS / G;
-        const int jv = tid % G;
-        const int ksub = tid / G;
-        float acc[VE];
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-        uint4 av[DS_SHRINK_LOADS];
-        for (int kc = k0; kc < k1; kc += KPT * DS_SHRINK_LOADS) {
-#pragma unroll
-            for (int l = 0; l < DS_SHRINK_LOADS; ++l) {
-                const int k = kc + ksub + l * KPT;
-                // past the slice: read row k0 again; it meets x = 0 below
-                av[l] = *(const uint4*)(Au + (int64_t)(k < k1 ? k : k0) * r + jv * VE);
-            }
-            __syncthreads();   // xs ready (first pass) / harmless afterwards
-#pragma unroll
-            for (int l = 0; l < DS_SHRINK_LOADS; ++l) {
-                const int k = kc + ksub + l * KPT;
-                const float xv = (k < k1) ? xs[k - k0] : 0.f;
-                union { uint4 u; bf16 e[VE]; } v;
-                v.u = av[l];
-#pragma unroll
-                for (int e = 0; e < VE; ++e) acc[e] += xv * to_f32(v.e[e]);
-            }
-        }
-        for (int d = G; d < 64; d <<= 1)
-#pragma unroll
-            for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], d, 64);
-        if (lane < G)
-#pragma unroll
-            for (int e = 0; e < VE; ++e) red[wave][lane * VE + e] = acc[e];
-    } else {
-        // any rank: thread (j, g) sums column j over k-rows g, g + Gs, ...
-        __syncthreads();
-        const int Gs = DS_THREADS / r;
-        const int j = tid % r;
-        const int gq = tid / r;
-        float acc = 0.f;
-        if (gq < Gs)
-            for (int k = k0 + gq; k < k1; k += Gs) acc += xs[k - k0] * to_f32(Au[(int64_t)k * r + j]);
-        // fold the Gs groups into 8 wave slots in a fixed order
-        float* flat = &red[0][0];
-        __syncthreads();
-        if (tid < 8 * 64) flat[tid] = 0.f;
-        __syncthreads();
-        for (int q = 0; q < Gs; ++q) {
-            if (gq == q) flat[(q & 7) * 64 + j] += acc;
-            __syncthreads();
-        }
-    }
-    __syncthreads();
-    if (tid < 64) {
-        float v = 0.f;
-        if (tid < r)
-            for (int w = 0; w < 8; ++w) v += red[w][tid];
-        outp[tid] = v;
-    }
-}
-
 template <int MB>
 __global__ __launch_bounds__(DS_THREADS) void k_decode_stream(PoolDev P, DecodePlan D, DecodeArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_BYTES];
+    // a slice wholly inside K (the usual case) takes the branch-free form,
+    // whose wait counts let x be staged while W is still arriving
     const int b = blockIdx.x;
-    // shrink workgroups first: they feed the finish pass's longest chain
-    if (b < D.shrink_wgs) stream_shrink(P, D, g, b, lds);
-    else stream_base<MB>(P, D, g, b - D.shrink_wgs, lds);
+    const int kbeg = (b / D.tiles_n) * D.kslice;
+    if (min(P.d_in, kbeg + D.kslice) - kbeg == DS_USTEPS * 32) stream_body<MB, true>(P, D, g, b, lds);
+    else stream_body<MB, false>(P, D, g, b, lds);
 }
 
 // Finish: workgroup (m, chunk) owns FIN_COLS columns of row m, 4 per thread.
 // Loads go out in the order their addresses are known: the base partials
-// first (they need nothing), then the row's t partials and B rows (after the
-// row record).  The t partials are summed into LDS in slice order while the
-// other loads are in flight.
-template <typename TY>
+// first (they need nothing), then, after the row record (a scalar load), the
+// row's t partials and B rows.  The t partials are summed into LDS in slice
+// order while the other loads are in flight.  VEC (d_out and every B block
+// 16-byte aligned) takes whole 4-column vectors without branches.
+template <typename TY, bool VEC>
 __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, DecodePlan D, DecodeArgs g) {
     __shared__ float st[64];
     const int tid = threadIdx.x;
@@ -284,52 +263,53 @@ __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, Decode
     const int N = P.d_out;
     const int M = g.n;
     const bool in = c0 < N;
-    const bool full = c0 + 4 <= N;
-    const bool vp = full && (N % 4 == 0);
     const int cc = in ? c0 : 0;   // columns past d_out read column 0 and are not stored
 
-    // base partials, FIN_SCHUNK slices requested together, added in slice order
-    auto load_part = [&](int s0, float4* u) {
-#pragma unroll
-        for (int q = 0; q < FIN_SCHUNK; ++q) {
-            const float* p = g.part_base + ((int64_t)(s0 + q < D.base_slices ? s0 + q : 0) * M + m) * N + cc;
-            if (vp) {
-                u[q] = *(const float4*)p;
-            } else {
-                u[q].x = p[0];
-                u[q].y = (cc + 1 < N) ? p[1] : 0.f;
-                u[q].z = (cc + 2 < N) ? p[2] : 0.f;
-                u[q].w = (cc + 3 < N) ? p[3] : 0.f;
-            }
+    auto load4 = [&](const float* p) {
+        float4 u;
+        if constexpr (VEC) {
+            u = *(const float4*)p;
+        } else {
+            u.x = p[0];
+            u.y = (cc + 1 < N) ? p[1] : 0.f;
+            u.z = (cc + 2 < N) ? p[2] : 0.f;
+            u.w = (cc + 3 < N) ? p[3] : 0.f;
         }
+        return u;
     };
+    // base partials, FIN_SCHUNK slices requested together, added in slice order
     float4 u[FIN_SCHUNK];
-    load_part(0, u);
+    auto load_part = [&](int s0) {
+#pragma unroll
+        for (int q = 0; q < FIN_SCHUNK; ++q)
+            u[q] = load4(g.part_base + ((int64_t)(s0 + q < D.base_slices ? s0 + q : 0) * M + m) * N + cc);
+    };
+    load_part(0);
 
     int r = 0;
     int64_t boff = 0;
     float sc = 0.f;
     if (g.with_lora) {
-        const RowRec rec = g.rows[m];
-        r = rec.rank;
-        boff = rec.b_off;
-        sc = rec.scale;
+        const RowRec* rec = g.rows + m;
+        r = uload(&rec->rank, 0);
+        boff = uload(&rec->b_off, 0);
+        sc = uload(&rec->scale, 0);
     }
     float tp[FIN_SCHUNK];
-    if (r > 0 && tid < r) {
+    if (tid < r) {
 #pragma unroll
         for (int q = 0; q < FIN_SCHUNK; ++q)
-            tp[q] = (q < D.t_slices) ? g.part_t[((int64_t)q * M + m) * 64 + tid] : 0.f;
+            tp[q] = g.part_t[((int64_t)(q < D.t_slices ? q : 0) * M + m) * 64 + tid];
     }
     const bf16* Bu = (const bf16*)P.B + boff + cc;
-    const bool vb = full && P.vec_b;
     uint2 bv[FIN_RCHUNK];
     auto load_b = [&](int j0) {
 #pragma unroll
         for (int q = 0; q < FIN_RCHUNK; ++q) {
             const int j = j0 + q;
-            if (j < r && vb) {
-                bv[q] = *(const uint2*)(Bu + (int64_t)j * N);
+            if constexpr (VEC) {
+                // rank rows past r read row 0 again; they meet t = 0
+                bv[q] = *(const uint2*)(Bu + (int64_t)(j < r ? j : 0) * N);
             } else {
                 union { uint2 u; bf16 e[4]; } w;
                 for (int e = 0; e < 4; ++e) w.e[e] = (j < r && cc + e < N) ? Bu[(int64_t)j * N + e] : (bf16)0;
@@ -349,9 +329,9 @@ __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, Decode
         }
         s0 += FIN_SCHUNK;
         if (s0 >= D.base_slices) break;
-        load_part(s0, u);
+        load_part(s0);
     }
-    if (r > 0 && tid < r) {
+    if (tid < r) {
         float t = 0.f;
 #pragma unroll
         for (int q = 0; q < FIN_SCHUNK; ++q)
@@ -397,21 +377,9 @@ DecodePlan plan_decode(const PoolDev& P, int32_t n_rows, bool with_lora) {
     D.kslice = steps * 32;
     D.base_slices = (int32_t)ceil_div(K, D.kslice);
     D.base_wgs = D.tiles_n * D.base_slices;
-    // shrink slices: about 256 workgroups, slices of at least 512 k-rows,
-    // x slice within the LDS budget
-    if (with_lora && n_rows > 0) {
-        int ts = (int)std::max<int64_t>(1, ceil_div(256, n_rows));
-        ts = std::min<int>(ts, (int)std::max<int64_t>(1, ceil_div(K, 512)));
-        int tk = (int)align_up((size_t)ceil_div(K, ts), 64);
-        const int tk_max = (DS_LDS_BYTES - 8 * 64 * 4) / 4 / 64 * 64;
-        if (tk > tk_max) tk = tk_max;
-        D.t_kslice = tk;
-        D.t_slices = (int32_t)ceil_div(K, tk);
-    } else {
-        D.t_kslice = 0;
-        D.t_slices = 0;
-    }
-    D.shrink_wgs = with_lora ? n_rows * D.t_slices : 0;
+    // the shrink partials follow the base slices (workgroup (tn, ks) shrinks
+    // rows tn, tn + tiles_n, ... over slice ks)
+    D.t_slices = (with_lora && n_rows > 0) ? D.base_slices : 0;
     return D;
 }
 
@@ -433,7 +401,7 @@ void decode_carve(const PoolDev& P, int32_t n_rows, const DecodePlan& D, void* w
 
 hipError_t launch_decode_stream(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
                                 hipStream_t stream) {
-    dim3 grid((unsigned)(D.base_wgs + D.shrink_wgs));
+    dim3 grid((unsigned)D.base_wgs);
     if (g.n <= 16)
         hipLaunchKernelGGL((k_decode_stream<1>), grid, dim3(DS_THREADS), 0, stream, P, D, g);
     else if (g.n <= 32)
@@ -447,10 +415,14 @@ hipError_t launch_decode_finish(const PoolDev& P, const DecodePlan& D, const Dec
                                 lora_dtype_t ydt, hipStream_t stream) {
     const int nch = (int)ceil_div(P.d_out, FIN_COLS);
     dim3 grid((unsigned)(g.n * nch));
-    if (ydt == LORA_BF16)
-        hipLaunchKernelGGL(k_decode_finish<bf16>, grid, dim3(FIN_THREADS), 0, stream, P, D, g);
-    else
-        hipLaunchKernelGGL(k_decode_finish<float>, grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+    const bool vec = P.vec_b != 0;   // d_out % 8 == 0 and 16-byte B blocks
+    if (ydt == LORA_BF16) {
+        if (vec) hipLaunchKernelGGL((k_decode_finish<bf16, true>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+        else hipLaunchKernelGGL((k_decode_finish<bf16, false>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+    } else {
+        if (vec) hipLaunchKernelGGL((k_decode_finish<float, true>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+        else hipLaunchKernelGGL((k_decode_finish<float, false>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+    }
     return hipGetLastError();
 }
 

@@ -57,6 +57,14 @@ __device__ __forceinline__ bool id_ok(int32_t a, int32_t n_adapters) {
     return a >= 0 && a < n_adapters;
 }
 
+// Read-only table entry at a workgroup-uniform index through the scalar
+// cache (a scalar load: it waits on its own counter, not behind the vector
+// loads in flight).  Only for data no kernel in flight writes.
+template <typename T>
+__device__ __forceinline__ T uload(const T* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 __device__ __forceinline__ void flag_bad_id(int32_t* err) {
     __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -151,13 +159,11 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 // Decode layer in two launches (bf16, n_rows <= 64, W stored [d_out, d_in]).
 constexpr int DS_LDS_BYTES = 72 * 1024;   // two workgroups per CU
 struct DecodePlan {
-    int32_t tiles_n;      // 64-column base tiles
-    int32_t kslice;       // k-rows per base slice (multiple of 32)
+    int32_t tiles_n;      // 128-column base tiles
+    int32_t kslice;       // k-rows per slice (multiple of 32, at most 512)
     int32_t base_slices;  // partial base products per output
     int32_t base_wgs;     // tiles_n * base_slices
-    int32_t t_kslice;     // k-rows per shrink slice
-    int32_t t_slices;     // partial shrink sums per row
-    int32_t shrink_wgs;   // n_rows * t_slices (0 without the LoRA term)
+    int32_t t_slices;     // partial shrink sums per row (base_slices, or 0 without the LoRA term)
 };
 struct RowRec {
     int64_t b_off;   // element offset of the row's B block

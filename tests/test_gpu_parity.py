@@ -490,6 +490,28 @@ def test_decode_two_launch(n_rows, layout):
     assert_close(yb, f64(p.x) @ f64(p.W), TOL[torch.bfloat16], "decode base-only")
 
 
+@pytest.mark.parametrize("n_rows", [1, 16, 33, 64])
+@pytest.mark.parametrize("ranks", ["pow2", "odd"])
+def test_decode_whole_slices(n_rows, ranks):
+    """d_in 4096 splits into whole 512-row slices (the branch-free stream form);
+    d_out 4000 leaves a ragged last tile; 33+ rows give a workgroup several
+    shrink rows; odd ranks take the any-rank shrink."""
+    say(f"decode two-launch path, whole K slices: {n_rows} rows, {ranks} ranks")
+    b = binding()
+    rk = [8, 16, 32, 64, 16, 8] if ranks == "pow2" else [3, 16, 40, 64, 12, 1]
+    w = wl.small_batch(seed=100 + n_rows, n_rows=n_rows, device=DEV, dtype=torch.bfloat16, d_in=4096,
+                       d_out=4000, n_adapters=6, layout=wl.RAGGED, ranks=rk, frac_base=0.1)
+    p = w.projections[0]
+    o = run_oracle(w)
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    Wt = w_stored(p.W, b.LORA_W_OUT_IN)
+    for ydt in (torch.float32, torch.bfloat16):
+        y = b.lora_layer_apply(pool, p.x, Wt, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV, y_dtype=ydt)
+        torch.cuda.synchronize()
+        assert_close(y, o["y"], TOL[torch.bfloat16], f"decode layer y={ydt}")
+
+
 def test_decode_invalid_ids_and_determinism():
     say("decode two-launch path: invalid ids flagged, run-to-run identical")
     b = binding()
