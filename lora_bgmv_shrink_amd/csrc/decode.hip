@@ -62,11 +62,15 @@ __device__ __forceinline__ bf16x8_t ld8(const bf16* p, int valid, bool nt) {
 __device__ __forceinline__ void shrink_wave(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int tn,
                                             int ks, int kbeg, int klen, const bf16* xs, int xld, int lane) {
     const int M = g.n;
+    // the first row's lookups (scalar loads) and row record go out before
+    // the x barrier; its A pieces after it
+    int i = tn;
+    int a = i < M ? uload(g.ids, i) : -1;
+    bool ok = id_ok(a, P.n_adapters);
+    int r = ok ? uload(P.ranks, a) : 0;
+    int64_t aoff = ok ? uload(P.a_off, a) : 0;
     __syncthreads();   // x staged by the base waves
-    for (int i = tn; i < M; i += D.tiles_n) {
-        const int a = uload(g.ids, i);
-        const bool ok = id_ok(a, P.n_adapters);
-        const int r = ok ? uload(P.ranks, a) : 0;
+    for (; i < M;) {
         if (ks == 0 && lane == 0) {
             // row record for the finish pass: B block offset, rank (0: no term), scale
             RowRec rec;
@@ -76,56 +80,63 @@ __device__ __forceinline__ void shrink_wave(const PoolDev& P, const DecodePlan& 
             g.rows[i] = rec;
             if (!ok && a != -1) flag_bad_id(P.err);
         }
-        if (r == 0) continue;   // the finish pass never reads t for such rows
-        const bf16* Au = (const bf16*)P.A + uload(P.a_off, a) + (int64_t)kbeg * r;
-        const bf16* xi = xs + i * xld;
-        float* outp = g.part_t + ((int64_t)ks * M + i) * 64;
-        if (P.stream_ok) {
-            const int G = r / 8;
-            const int RPP = 64 / G;   // k-rows per pass
-            const int passes = (klen + RPP - 1) / RPP;
-            const int jv = lane % G;
-            const int ksub = lane / G;
-            float acc[8];
+        if (r > 0) {   // the finish pass never reads t for rows without a term
+            const bf16* Au = (const bf16*)P.A + aoff + (int64_t)kbeg * r;
+            const bf16* xi = xs + i * xld;
+            float* outp = g.part_t + ((int64_t)ks * M + i) * 64;
+            if (P.stream_ok) {
+                const int G = r / 8;
+                const int RPP = 64 / G;   // k-rows per pass
+                const int passes = (klen + RPP - 1) / RPP;
+                const int jv = lane % G;
+                const int ksub = lane / G;
+                float acc[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-            for (int p0 = 0; p0 < passes; p0 += DS_SHRINK_LOADS) {
-                uint4 av[DS_SHRINK_LOADS];
+                for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+                for (int p0 = 0; p0 < passes; p0 += DS_SHRINK_LOADS) {
+                    uint4 av[DS_SHRINK_LOADS];
 #pragma unroll
-                for (int q = 0; q < DS_SHRINK_LOADS; ++q) {
-                    const int kk = ksub + (p0 + q) * RPP;
-                    // past the slice: read its first k-row again; it meets x = 0 below
-                    av[q] = *(const uint4*)(Au + (int64_t)(kk < klen ? kk : 0) * r + jv * 8);
+                    for (int q = 0; q < DS_SHRINK_LOADS; ++q) {
+                        const int kk = ksub + (p0 + q) * RPP;
+                        // past the slice: read its first k-row again; it meets x = 0 below
+                        av[q] = *(const uint4*)(Au + (int64_t)(kk < klen ? kk : 0) * r + jv * 8);
+                    }
+#pragma unroll
+                    for (int q = 0; q < DS_SHRINK_LOADS; ++q) {
+                        const int kk = ksub + (p0 + q) * RPP;
+                        const float xv = (kk < klen) ? to_f32(xi[kk]) : 0.f;
+                        union { uint4 u; bf16 e[8]; } v;
+                        v.u = av[q];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[e] += xv * to_f32(v.e[e]);
+                    }
                 }
+                for (int d = G; d < 64; d <<= 1)
 #pragma unroll
-                for (int q = 0; q < DS_SHRINK_LOADS; ++q) {
-                    const int kk = ksub + (p0 + q) * RPP;
-                    const float xv = (kk < klen) ? to_f32(xi[kk]) : 0.f;
-                    union { uint4 u; bf16 e[8]; } v;
-                    v.u = av[q];
+                    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], d, 64);
+                if (lane < G)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] += xv * to_f32(v.e[e]);
-                }
+                    for (int e = 0; e < 8; ++e) outp[lane * 8 + e] = acc[e];
+            } else {
+                // any rank: lane (j, gq) sums column j over k-rows gq, gq + Gs, ...;
+                // the groups are then added in order gq = 0, 1, ...
+                const int Gs = 64 / r;
+                const int j = lane % r;
+                const int gq = lane / r;
+                float acc = 0.f;
+                if (gq < Gs)
+                    for (int kk = gq; kk < klen; kk += Gs) acc += to_f32(xi[kk]) * to_f32(Au[(int64_t)kk * r + j]);
+                float v = acc;
+                for (int q = 1; q < Gs; ++q) v += __shfl(acc, j + q * r, 64);
+                if (lane < r) outp[lane] = v;
             }
-            for (int d = G; d < 64; d <<= 1)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], d, 64);
-            if (lane < G)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) outp[lane * 8 + e] = acc[e];
-        } else {
-            // any rank: lane (j, gq) sums column j over k-rows gq, gq + Gs, ...;
-            // the groups are then added in order gq = 0, 1, ...
-            const int Gs = 64 / r;
-            const int j = lane % r;
-            const int gq = lane / r;
-            float acc = 0.f;
-            if (gq < Gs)
-                for (int kk = gq; kk < klen; kk += Gs) acc += to_f32(xi[kk]) * to_f32(Au[(int64_t)kk * r + j]);
-            float v = acc;
-            for (int q = 1; q < Gs; ++q) v += __shfl(acc, j + q * r, 64);
-            if (lane < r) outp[lane] = v;
         }
+        i += D.tiles_n;
+        if (i >= M) break;
+        a = uload(g.ids, i);
+        ok = id_ok(a, P.n_adapters);
+        r = ok ? uload(P.ranks, a) : 0;
+        aoff = ok ? uload(P.a_off, a) : 0;
     }
 }
 

@@ -493,14 +493,14 @@ def test_decode_two_launch(n_rows, layout):
 @pytest.mark.parametrize("n_rows", [1, 16, 33, 64])
 @pytest.mark.parametrize("ranks", ["pow2", "odd"])
 def test_decode_whole_slices(n_rows, ranks):
-    """d_in 4096 splits into whole 512-row slices (the branch-free stream form);
-    d_out 4000 leaves a ragged last tile; 33+ rows give a workgroup several
-    shrink rows; odd ranks take the any-rank shrink."""
+    """d_in 4096 splits into whole 512-row quarters (the branch-free stream
+    form: 2 or 4 quarters per slice); d_out 4104 leaves a ragged last column
+    tile; odd ranks take the any-rank shrink."""
     say(f"decode two-launch path, whole K slices: {n_rows} rows, {ranks} ranks")
     b = binding()
     rk = [8, 16, 32, 64, 16, 8] if ranks == "pow2" else [3, 16, 40, 64, 12, 1]
     w = wl.small_batch(seed=100 + n_rows, n_rows=n_rows, device=DEV, dtype=torch.bfloat16, d_in=4096,
-                       d_out=4000, n_adapters=6, layout=wl.RAGGED, ranks=rk, frac_base=0.1)
+                       d_out=4104, n_adapters=6, layout=wl.RAGGED, ranks=rk, frac_base=0.1)
     p = w.projections[0]
     o = run_oracle(w)
     pool = pool_of(p.pool)
@@ -510,6 +510,25 @@ def test_decode_whole_slices(n_rows, ranks):
         y = b.lora_layer_apply(pool, p.x, Wt, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV, y_dtype=ydt)
         torch.cuda.synchronize()
         assert_close(y, o["y"], TOL[torch.bfloat16], f"decode layer y={ydt}")
+
+
+@pytest.mark.parametrize("n_rows,d_in,d_out", [(4, 256, 264), (20, 512, 1024), (9, 2056, 328)])
+def test_decode_small_shapes(n_rows, d_in, d_out):
+    """Shapes whose plan cuts the stream into one-quarter slices (8 column
+    blocks per workgroup) with ragged K and column tails."""
+    say(f"decode two-launch path, small shape: {n_rows} rows, {d_in} -> {d_out}")
+    b = binding()
+    w = wl.small_batch(seed=200 + n_rows, n_rows=n_rows, device=DEV, dtype=torch.bfloat16, d_in=d_in,
+                       d_out=d_out, n_adapters=5, ranks=[16, 8, 64, 32, 16], layout=wl.RAGGED, frac_base=0.2)
+    p = w.projections[0]
+    o = run_oracle(w)
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    Wt = w_stored(p.W, b.LORA_W_OUT_IN)
+    y = b.lora_layer_apply(pool, p.x, Wt, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV,
+                           y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(y, o["y"], TOL[torch.bfloat16], "decode layer")
 
 
 def test_decode_invalid_ids_and_determinism():
