@@ -144,7 +144,7 @@ __device__ __forceinline__ void shrink_wave(const PoolDev& P, const DecodePlan& 
 // block w (all of the slice's k-steps in flight, nontemporal: W is read once)
 // and keeps the whole 16-column partial; x of the slice is staged in LDS and
 // serves the MFMAs and the shrink wave.
-template <int MB, bool FULL>
+template <int MB, bool FULL, bool LORA>
 __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b,
                                             uint8_t* lds) {
     const int tid = threadIdx.x;
@@ -173,9 +173,8 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
     constexpr int XV = MB * 16 * PER_ROW / DS_BASE_THREADS;
     static_assert(MB * 16 * PER_ROW % DS_BASE_THREADS == 0, "x pieces do not split evenly");
     bf16* xs = (bf16*)lds;
-    if (wave == DS_NB) {
-        if (g.with_lora) shrink_wave(P, D, g, tn, ks, kbeg, klen, xs, XLD, lane);
-        else __syncthreads();
+    if (LORA && wave == DS_NB) {
+        shrink_wave(P, D, g, tn, ks, kbeg, klen, xs, XLD, lane);
         return;
     }
     const bf16* X = (const bf16*)g.x;
@@ -247,15 +246,20 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
     }
 }
 
-template <int MB>
-__global__ __launch_bounds__(DS_THREADS) void k_decode_stream(PoolDev P, DecodePlan D, DecodeArgs g) {
+// LORA: the workgroup has the shrink wave (the layer with its adapter term);
+// without it the stream is the base product alone.
+template <int MB, bool LORA>
+__global__ __launch_bounds__(LORA ? DS_THREADS : DS_BASE_THREADS) void k_decode_stream(PoolDev P, DecodePlan D,
+                                                                                    DecodeArgs g) {
+    // staged x; sized over half a CU's LDS so that each CU runs one
+    // workgroup and the grid (about one workgroup per CU) spreads over all
     __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_BYTES];
     // a slice wholly inside K (the usual case) takes the branch-free form,
     // whose wait counts let x be staged while W is still arriving
     const int b = blockIdx.x;
     const int kbeg = (b / D.tiles_n) * D.kslice;
-    if (min(P.d_in, kbeg + D.kslice) - kbeg == DS_USTEPS * 32) stream_body<MB, true>(P, D, g, b, lds);
-    else stream_body<MB, false>(P, D, g, b, lds);
+    if (min(P.d_in, kbeg + D.kslice) - kbeg == DS_USTEPS * 32) stream_body<MB, true, LORA>(P, D, g, b, lds);
+    else stream_body<MB, false, LORA>(P, D, g, b, lds);
 }
 
 // Finish: workgroup (m, chunk) owns FIN_COLS columns of row m, 4 per thread.
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_stream(PoolDev P, DecodeP
 // row's t partials and B rows.  The t partials are summed into LDS in slice
 // order while the other loads are in flight.  VEC (d_out and every B block
 // 16-byte aligned) takes whole 4-column vectors without branches.
-template <typename TY, bool VEC>
+template <typename TY, bool VEC, bool LORA>
 __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, DecodePlan D, DecodeArgs g) {
     __shared__ float st[64];
     const int tid = threadIdx.x;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(FIN_THREADS) void k_decode_finish(PoolDev P, Decode
     int r = 0;
     int64_t boff = 0;
     float sc = 0.f;
-    if (g.with_lora) {
+    if (LORA) {
         const RowRec* rec = g.rows + m;
         r = uload(&rec->rank, 0);
         boff = uload(&rec->b_off, 0);
@@ -413,12 +417,20 @@ void decode_carve(const PoolDev& P, int32_t n_rows, const DecodePlan& D, void* w
 hipError_t launch_decode_stream(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g,
                                 hipStream_t stream) {
     dim3 grid((unsigned)D.base_wgs);
-    if (g.n <= 16)
-        hipLaunchKernelGGL((k_decode_stream<1>), grid, dim3(DS_THREADS), 0, stream, P, D, g);
-    else if (g.n <= 32)
-        hipLaunchKernelGGL((k_decode_stream<2>), grid, dim3(DS_THREADS), 0, stream, P, D, g);
-    else
-        hipLaunchKernelGGL((k_decode_stream<4>), grid, dim3(DS_THREADS), 0, stream, P, D, g);
+    const int MB = g.n <= 16 ? 1 : (g.n <= 32 ? 2 : 4);
+#define LORA_DS(mb)                                                                                        \
+    if (g.with_lora)                                                                                       \
+        hipLaunchKernelGGL((k_decode_stream<mb, true>), grid, dim3(DS_THREADS), 0, stream, P, D, g);       \
+    else                                                                                                   \
+        hipLaunchKernelGGL((k_decode_stream<mb, false>), grid, dim3(DS_BASE_THREADS), 0, stream, P, D, g)
+    if (MB == 1) {
+        LORA_DS(1);
+    } else if (MB == 2) {
+        LORA_DS(2);
+    } else {
+        LORA_DS(4);
+    }
+#undef LORA_DS
     return hipGetLastError();
 }
 
@@ -427,13 +439,25 @@ hipError_t launch_decode_finish(const PoolDev& P, const DecodePlan& D, const Dec
     const int nch = (int)ceil_div(P.d_out, FIN_COLS);
     dim3 grid((unsigned)(g.n * nch));
     const bool vec = P.vec_b != 0;   // d_out % 8 == 0 and 16-byte B blocks
+#define LORA_FIN(ty, v, l) hipLaunchKernelGGL((k_decode_finish<ty, v, l>), grid, dim3(FIN_THREADS), 0, stream, P, D, g)
     if (ydt == LORA_BF16) {
-        if (vec) hipLaunchKernelGGL((k_decode_finish<bf16, true>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
-        else hipLaunchKernelGGL((k_decode_finish<bf16, false>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+        if (g.with_lora) {
+            if (vec) LORA_FIN(bf16, true, true);
+            else LORA_FIN(bf16, false, true);
+        } else {
+            if (vec) LORA_FIN(bf16, true, false);
+            else LORA_FIN(bf16, false, false);
+        }
     } else {
-        if (vec) hipLaunchKernelGGL((k_decode_finish<float, true>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
-        else hipLaunchKernelGGL((k_decode_finish<float, false>), grid, dim3(FIN_THREADS), 0, stream, P, D, g);
+        if (g.with_lora) {
+            if (vec) LORA_FIN(float, true, true);
+            else LORA_FIN(float, false, true);
+        } else {
+            if (vec) LORA_FIN(float, true, false);
+            else LORA_FIN(float, false, false);
+        }
     }
+#undef LORA_FIN
     return hipGetLastError();
 }
 

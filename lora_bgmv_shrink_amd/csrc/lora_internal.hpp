@@ -157,7 +157,7 @@ hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
 // Decode layer in two launches (bf16, n_rows <= 64, W stored [d_out, d_in]).
-constexpr int DS_LDS_BYTES = 72 * 1024;   // two workgroups per CU
+constexpr int DS_LDS_BYTES = 84 * 1024;   // > half a CU: one stream workgroup per CU
 struct DecodePlan {
     int32_t tiles_n;      // 128-column base tiles
     int32_t kslice;       // k-rows per slice (multiple of 32, at most 512)
