@@ -140,6 +140,17 @@ __device__ __forceinline__ void mma_block(Acc<C>& acc, const typename C::T* sA,
             for (int j = 0; j < C::FN; ++j) acc.v[i][j] = M::mma(a[ca][i], b[cur][j], acc.v[i][j]);
             if (ROLL_A && s + 1 < NSUB) a[0][i] = M::ld(pa + i * C::BLK * C::LDK + kk);
         }
+        if (ROLL_A && s + 1 < NSUB) {
+            // keep the order as written: B reads first, then per row its MFMAs
+            // and the reload of its A fragment (not sunk next to its next use)
+            __builtin_amdgcn_sched_group_barrier(0x100, C::FN, 0);
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, C::FN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 
@@ -182,6 +193,67 @@ struct RowLoader {
 #pragma unroll
             for (int e = 0; e < C::VE; ++e)
                 tmp.e[e] = (gr >= 0 && k + e < K) ? base[(int64_t)gr * ld + k + e] : (T)0;
+            reg[v] = tmp.u;
+        }
+    }
+    // A whole K-block (k0 + BK <= K) through a buffer resource whose base is
+    // the tile's first row and whose range ends after its last valid row:
+    // rows past it read as 0 (they only feed outputs never stored).  The
+    // row offset of each piece is a per-lane VGPR, the K position a scalar.
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int tid) {
+        static_assert(C::NT % VPR == 0, "pieces of a lane share one column");
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const int r0 = tid / VPR;
+        const int c = (tid - r0 * VPR) * C::VE;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            if (TOT % C::NT != 0 && tid + v * C::NT >= TOT) break;
+            const int voff = (int)(((int64_t)(r0 + v * (C::NT / VPR)) * ld + c) * (int64_t)sizeof(T));
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, k0 * (int)sizeof(T), 0);
+            reg[v] = __builtin_bit_cast(uint4, x);
+        }
+    }
+    // A whole K-block (k0 + BK <= K) of rows row0 .. row0 + ROWS - 1, those at
+    // or past nrows read as row 0 (they only feed outputs never stored):
+    // unconditional loads, no row table, no branch.
+    __device__ __forceinline__ void load_full(const T* __restrict__ base, int64_t ld, int row0, int nrows, int k0,
+                                              int tid) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int r = idx / VPR;
+            const int gr = row0 + r;
+            reg[v] = *(const uint4*)(base + (int64_t)(gr < nrows ? gr : 0) * ld + k0 + (idx - r * VPR) * C::VE);
+        }
+    }
+    // Rows row0 .. row0 + ROWS - 1 of the source, those at or past nrows read
+    // as row 0 (they only feed outputs that are never stored); no row table.
+    __device__ __forceinline__ void load_direct(const T* __restrict__ base, int64_t ld, int row0, int nrows,
+                                                int k0, int K, int tid) {
+        if (k0 + C::BK <= K) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int idx = tid + v * C::NT;
+                if (TOT % C::NT != 0 && idx >= TOT) break;
+                const int r = idx / VPR;
+                const int k = k0 + (idx - r * VPR) * C::VE;
+                const int gr = row0 + r;
+                reg[v] = *(const uint4*)(base + (int64_t)(gr < nrows ? gr : 0) * ld + k);
+            }
+            return;
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int r = idx / VPR;
+            const int k = k0 + (idx - r * VPR) * C::VE;
+            const int gr = row0 + r;
+            union { uint4 u; T e[C::VE]; } tmp;
+#pragma unroll
+            for (int e = 0; e < C::VE; ++e)
+                tmp.e[e] = (gr < nrows && k + e < K) ? base[(int64_t)gr * ld + k + e] : (T)0;
             reg[v] = tmp.u;
         }
     }
@@ -593,9 +665,10 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     const T* TE = (const T*)g.t_ext;
     RowLoader<C, C::BM> la;
     BLoader<C> lb;
+    RowLoader<C, C::BN> lw;   // W rows (OUT_IN) share the B register set's shape
     auto load_main = [&](int s) {
-        la.load(X, g.ldx, sRowA, s * C::BK, K, tid);
-        if constexpr (OUT_IN) lb.load_rows(Wp, g.ldw, sRowB, s * C::BK, K, tid);
+        la.load_direct(X, g.ldx, m0, g.n, s * C::BK, K, tid);
+        if constexpr (OUT_IN) lw.load_direct(Wp, g.ldw, n0, N, s * C::BK, K, tid);
         else lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
     };
     auto load_ext = [&](int s) {
@@ -607,19 +680,104 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     };
     const int n_ext = total - nk;
     // x W over d_in, two LDS stages, next block prefetched into registers
-    load_main(0);
-    for (int kb = 0; kb < nk; ++kb) {
-        T* sA = smem + (kb & 1) * C::STAGE;
-        T* sB = sA + C::A_ELEMS;
-        la.store(sA, tid);
-        if constexpr (OUT_IN) lb.store_rows(sB, tid);
-        else lb.store_trans(sB, tid);
-        __syncthreads();
-        if (kb + 1 < nk) load_main(kb + 1);
-        else if (n_ext > 0) load_ext(0);
-        mma_block<C>(acc, sA, sB, wm, wn, lane);
+    if constexpr (OUT_IN) {
+        // whole K-blocks in a branch-free loop (both operands K-contiguous);
+        // the last whole block and a ragged tail block after it
+        const int nkf = K / C::BK;
+        // buffer resources over the tile's rows (raw, 16-byte pieces); their
+        // fields are workgroup-uniform, said so with readfirstlane so that the
+        // loads take the descriptor from scalar registers directly
+        auto rsrc = [](const T* base, int rows, int64_t ld) {
+            const uint64_t a = (uint64_t)base;
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+            const int bytes = __builtin_amdgcn_readfirstlane((int)((int64_t)rows * ld * (int64_t)sizeof(T)));
+            return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, bytes,
+                                                     0x00020000);
+        };
+        const __amdgpu_buffer_rsrc_t rs_a = rsrc(X + (int64_t)m0 * g.ldx, max(0, min(C::BM, g.n - m0)), g.ldx);
+        const __amdgpu_buffer_rsrc_t rs_w = rsrc(Wp + (int64_t)n0 * g.ldw, max(0, min(C::BN, N - n0)), g.ldw);
+        auto load_full = [&](int s) {
+            la.load_buf(rs_a, g.ldx, s * C::BK, tid);
+            lw.load_buf(rs_w, g.ldw, s * C::BK, tid);
+        };
+        auto step = [&](int kb) {
+            T* sA = smem + (kb & 1) * C::STAGE;
+            T* sB = sA + C::A_ELEMS;
+            la.store(sA, tid);
+            lw.store(sB, tid);
+            __syncthreads();
+            return sA;
+        };
+        int kb = 0;
+        if constexpr (C::NT <= 256) {
+            // registers to spare (4 waves): two blocks in flight, in two
+            // register sets used alternately (the loop is unrolled by two)
+            RowLoader<C, C::BM> la2;
+            RowLoader<C, C::BN> lw2;
+            auto load_full2 = [&](int s) {
+                la2.load_buf(rs_a, g.ldx, s * C::BK, tid);
+                lw2.load_buf(rs_w, g.ldw, s * C::BK, tid);
+            };
+            auto step2 = [&](int k) {
+                T* sA = smem + (k & 1) * C::STAGE;
+                la2.store(sA, tid);
+                lw2.store(sA + C::A_ELEMS, tid);
+                __syncthreads();
+                return sA;
+            };
+            if (nkf >= 2) {
+                load_full(0);
+                load_full2(1);
+                for (; kb + 3 < nkf; kb += 2) {
+                    T* sA = step(kb);
+                    load_full(kb + 2);
+                    mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
+                    sA = step2(kb + 1);
+                    load_full2(kb + 3);
+                    mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
+                }
+                // two whole blocks left in the two register sets
+                T* sA = step(kb);
+                if (kb + 2 < nk) load_main(kb + 2);
+                mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
+                ++kb;
+                sA = step2(kb);
+                mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
+                ++kb;
+            } else {
+                if (nkf > 0) load_full(0);
+                else load_main(0);
+            }
+        } else {
+            if (nkf > 0) load_full(0);
+            else load_main(0);
+            for (; kb + 1 < nkf; ++kb) {
+                T* sA = step(kb);
+                load_full(kb + 1);
+                mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
+            }
+        }
+        for (; kb < nk; ++kb) {
+            T* sA = step(kb);
+            if (kb + 1 < nk) load_main(kb + 1);
+            mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
+        }
+    } else {
+        load_main(0);
+        for (int kb = 0; kb < nk; ++kb) {
+            T* sA = smem + (kb & 1) * C::STAGE;
+            T* sB = sA + C::A_ELEMS;
+            la.store(sA, tid);
+            lb.store_trans(sB, tid);
+            __syncthreads();
+            if (kb + 1 < nk) load_main(kb + 1);
+            mma_block<C>(acc, sA, sB, wm, wn, lane);
+        }
     }
-    // the LoRA K-extension blocks, same pipeline
+    // the LoRA K-extension blocks, same pipeline (their first block is fetched
+    // here; the stage it goes to was last read two blocks ago)
+    if (n_ext > 0) load_ext(0);
     for (int e = 0; e < n_ext; ++e) {
         const int kb = nk + e;
         T* sA = smem + (kb & 1) * C::STAGE;
