@@ -1098,7 +1098,8 @@ using GemmBig = Cfg<bf16, 128, 128, 64, 2, 2, 32>;
 using GemmMid = Cfg<bf16, 64, 64, 64, 2, 2>;
 using GemmSmall = Cfg<bf16, 32, 64, 64, 2, 2>;
 using GemmF32 = Cfg<float, 64, 64, 32, 2, 2>;
-using ShrinkB = Cfg<bf16, 64, 64, 64, 4, 1>;
+// K-blocks of 256: each workgroup keeps 64 KiB of x and A in flight
+using ShrinkB = Cfg<bf16, 64, 64, 256, 4, 1>;
 using ShrinkF = Cfg<float, 64, 64, 32, 4, 1>;
 using ExpandB = Cfg<bf16, 64, 64, 64, 2, 2>;
 using ExpandF = Cfg<float, 64, 64, 32, 2, 2>;
