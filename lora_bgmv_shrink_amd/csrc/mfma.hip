@@ -364,6 +364,56 @@ struct BLoader {
             }
         }
     }
+    // bf16 transposed pieces in pairs of k-rows: thread piece p = idx % (BK/2)
+    // owns k-rows 2p and 2p+1 of column vector idx / (BK/2), so the two rows'
+    // values of a column are written to LDS as one 32-bit word, and the lanes
+    // of a half-wave fill one LDS row with consecutive words (no bank
+    // conflicts).  reg[2v] holds row 2p, reg[2v+1] row 2p+1.
+    static constexpr int PAIRS = C::BK / 2;
+    static constexpr int P_TOT = PAIRS * T_VPR;
+    static constexpr int P_NV = (P_TOT + C::NT - 1) / C::NT;
+    static_assert(sizeof(T) != 2 || 2 * P_NV == NV, "pair pieces use the same registers");
+    __device__ __forceinline__ void load_trans_pairs(const T* __restrict__ base, int64_t ld, int j0, int kwrap,
+                                                     int kmax, int n0, int N, bool vec, int tid) {
+        const bool full = vec && n0 + C::BN <= N;
+#pragma unroll
+        for (int v = 0; v < P_NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (P_TOT % C::NT != 0 && idx >= P_TOT) break;
+            const int p = idx % PAIRS;
+            const int n = n0 + (idx / PAIRS) * VE;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kr = 2 * p + h;
+                const int k = j0 + kr % kwrap;
+                if (full) {
+                    // a row at or past kmax reads row j0; the A side is exactly zero there
+                    reg[2 * v + h] = *(const uint4*)(base + (int64_t)(k < kmax ? k : j0) * ld + n);
+                } else {
+                    union { uint4 u; T e[VE]; } tmp;
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        tmp.e[e] = (k < kmax && n + e < N) ? base[(int64_t)k * ld + n + e] : (T)0;
+                    reg[2 * v + h] = tmp.u;
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store_trans_pairs(T* s, int tid) const {
+#pragma unroll
+        for (int v = 0; v < P_NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (P_TOT % C::NT != 0 && idx >= P_TOT) break;
+            const int p = idx % PAIRS;
+            const int c = (idx / PAIRS) * VE;
+            union { uint4 u; unsigned short e[VE]; } r0, r1;
+            r0.u = reg[2 * v];
+            r1.u = reg[2 * v + 1];
+#pragma unroll
+            for (int e = 0; e < VE; ++e)
+                *(unsigned int*)(s + (c + e) * C::LDK + 2 * p) = (unsigned int)r0.e[e] | ((unsigned int)r1.e[e] << 16);
+        }
+    }
     __device__ __forceinline__ void store_rows(T* s, int tid) const {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
@@ -669,14 +719,23 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     auto load_main = [&](int s) {
         la.load_direct(X, g.ldx, m0, g.n, s * C::BK, K, tid);
         if constexpr (OUT_IN) lw.load_direct(Wp, g.ldw, n0, N, s * C::BK, K, tid);
+        else if constexpr (sizeof(T) == 2) lb.load_trans_pairs(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
         else lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
     };
+    constexpr bool PAIRS = sizeof(T) == 2;
     auto load_ext = [&](int s) {
         const int code = sExt[s];
         const int u = code >> 1;
         const int e = code & 1;
         la.load_masked(TE, g.lde, sRowA, sId, u, e * C::BK, tid);
-        lb.load_trans((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
+        if constexpr (PAIRS)
+            lb.load_trans_pairs((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
+        else
+            lb.load_trans((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
+    };
+    auto store_trans = [&](T* sB) {
+        if constexpr (PAIRS) lb.store_trans_pairs(sB, tid);
+        else lb.store_trans(sB, tid);
     };
     const int n_ext = total - nk;
     // x W over d_in, two LDS stages, next block prefetched into registers
@@ -769,7 +828,7 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             T* sA = smem + (kb & 1) * C::STAGE;
             T* sB = sA + C::A_ELEMS;
             la.store(sA, tid);
-            lb.store_trans(sB, tid);
+            store_trans(sB);
             __syncthreads();
             if (kb + 1 < nk) load_main(kb + 1);
             mma_block<C>(acc, sA, sB, wm, wn, lane);
@@ -783,7 +842,7 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
         T* sA = smem + (kb & 1) * C::STAGE;
         T* sB = sA + C::A_ELEMS;
         la.store(sA, tid);
-        lb.store_trans(sB, tid);
+        store_trans(sB);
         __syncthreads();
         if (e + 1 < n_ext) load_ext(e + 1);
         mma_block<C>(acc, sA, sB, wm, wn, lane);
