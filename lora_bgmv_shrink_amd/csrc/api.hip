@@ -354,6 +354,7 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
     } else {
         if (pool->dev.n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
         off = seg_layout(off, n_rows, pool->dev.n_adapters).end;
+        off += sgmv_shrink_part_bytes(pool->dev, n_rows);   // split-K partial sums of the shrink
     }
     *bytes = std::max<size_t>(off, 256);
     return LORA_OK;
@@ -419,8 +420,10 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     } else {
         lora_segments_t own;
         const lora_segments_t* sg = seg;
+        const SegLayout SL = seg_layout(after_t, n_rows, P.n_adapters);
+        float* part = sgmv_shrink_part_bytes(P, n_rows) ? (float*)(base + SL.end) : nullptr;
         if (!sg) {
-            SegLayout L = seg_layout(after_t, n_rows, P.n_adapters);
+            SegLayout L = SL;
             own.perm = (int32_t*)(base + L.perm);
             own.seg_ids = (int32_t*)(base + L.seg_ids);
             own.seg_off = (int32_t*)(base + L.seg_off);
@@ -431,7 +434,7 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
         }
         if (e == hipSuccess)
             e = launch_sgmv_shrink(P, pool->dtype, x, ldx, sg, n_rows, P.n_adapters + 1, t, ldt, true,
-                                   stream, t_ext, lde);
+                                   stream, t_ext, lde, ids, part);
     }
     if (e != hipSuccess) return LORA_E_DEVICE;
     GemmArgs g;

@@ -120,10 +120,15 @@ hipError_t launch_bgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t,
                               int64_t ldy, int accumulate, bool vec_y, hipStream_t stream);
 
 // SGMV shrink / expand (MFMA over segment tiles).
+// part (optional, sgmv_shrink_part_bytes of workspace): K is split into
+// slices whose partial sums a reduce pass adds in order (ids then required).
 hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
                               const lora_segments_t* seg, int32_t n_rows, int32_t n_bins,
                               float* t, int64_t ldt, bool vec_x, hipStream_t stream,
-                              void* t_ext = nullptr, int64_t lde = 0);
+                              void* t_ext = nullptr, int64_t lde = 0, const int32_t* ids = nullptr,
+                              float* part = nullptr);
+int32_t sgmv_shrink_slices(const PoolDev& P, int32_t n_rows);
+size_t sgmv_shrink_part_bytes(const PoolDev& P, int32_t n_rows);
 // t_ext from an existing t (rows with invalid ids or -1 are left alone)
 hipError_t launch_make_t_ext(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                              const int32_t* ids, int32_t n_rows, void* t_ext, int64_t lde,

@@ -439,47 +439,68 @@ struct BLoader {
     }
 };
 
-// Row-major [K][N] source -> LDS [n][k] (transposed on the way in).
+// Row-major [K][N] source -> LDS [n][k] (transposed on the way in).  bf16
+// pieces come in pairs of k-rows: piece p = idx % (BK/2) holds k-rows 2p and
+// 2p+1 of column vector idx / (BK/2), so each column's two values go to LDS
+// as one 32-bit word and a wave fills one LDS row with consecutive words (no
+// bank conflicts).  fp32 pieces are single k-rows.
 template <class C, int COLS>
 struct TransLoader {
     using T = typename C::T;
+    static constexpr bool PAIRS = sizeof(T) == 2;
     static constexpr int VPR = COLS / C::VE;
-    static constexpr int TOT = C::BK * VPR;
-    static constexpr int NV = (TOT + C::NT - 1) / C::NT;
+    static constexpr int KR = PAIRS ? C::BK / 2 : C::BK;   // pieces per column vector
+    static constexpr int TOT = KR * VPR;
+    static constexpr int NP = (TOT + C::NT - 1) / C::NT;
+    static constexpr int NV = PAIRS ? 2 * NP : NP;
     static_assert(COLS % C::VE == 0, "tile width not a multiple of the vector width");
     uint4 reg[NV];
 
+    __device__ __forceinline__ uint4 piece(const T* __restrict__ base, int64_t ld, int k, int K, int n, int N,
+                                           bool vec) const {
+        if (vec && k < K && n + C::VE <= N) return *(const uint4*)(base + (int64_t)k * ld + n);
+        union { uint4 u; T e[C::VE]; } tmp;
+#pragma unroll
+        for (int e = 0; e < C::VE; ++e) tmp.e[e] = (k < K && n + e < N) ? base[(int64_t)k * ld + n + e] : (T)0;
+        return tmp.u;
+    }
     __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int k0, int K,
                                          int n0, int N, bool vec, int tid) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
+        for (int v = 0; v < NP; ++v) {
             const int idx = tid + v * C::NT;
             if (TOT % C::NT != 0 && idx >= TOT) break;
-            const int kr = idx / VPR;
-            const int k = k0 + kr;
-            const int n = n0 + (idx - kr * VPR) * C::VE;
-            if (vec && k < K && n + C::VE <= N) {
-                reg[v] = *(const uint4*)(base + (int64_t)k * ld + n);
+            const int kp = idx % KR;
+            const int n = n0 + (idx / KR) * C::VE;
+            if constexpr (PAIRS) {
+                reg[2 * v] = piece(base, ld, k0 + 2 * kp, K, n, N, vec);
+                reg[2 * v + 1] = piece(base, ld, k0 + 2 * kp + 1, K, n, N, vec);
             } else {
-                union { uint4 u; T e[C::VE]; } tmp;
-#pragma unroll
-                for (int e = 0; e < C::VE; ++e)
-                    tmp.e[e] = (k < K && n + e < N) ? base[(int64_t)k * ld + n + e] : (T)0;
-                reg[v] = tmp.u;
+                reg[v] = piece(base, ld, k0 + kp, K, n, N, vec);
             }
         }
     }
     __device__ __forceinline__ void store(T* s, int tid) const {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
+        for (int v = 0; v < NP; ++v) {
             const int idx = tid + v * C::NT;
             if (TOT % C::NT != 0 && idx >= TOT) break;
-            const int kr = idx / VPR;
-            const int c = (idx - kr * VPR) * C::VE;
-            union { uint4 u; T e[C::VE]; } tmp;
-            tmp.u = reg[v];
+            const int kp = idx % KR;
+            const int c = (idx / KR) * C::VE;
+            if constexpr (PAIRS) {
+                union { uint4 u; unsigned short e[8]; } r0, r1;
+                r0.u = reg[2 * v];
+                r1.u = reg[2 * v + 1];
 #pragma unroll
-            for (int e = 0; e < C::VE; ++e) s[(c + e) * C::LDK + kr] = tmp.e[e];
+                for (int e = 0; e < 8; ++e)
+                    *(unsigned int*)(s + (c + e) * C::LDK + 2 * kp) =
+                        (unsigned int)r0.e[e] | ((unsigned int)r1.e[e] << 16);
+            } else {
+                union { uint4 u; T e[C::VE]; } tmp;
+                tmp.u = reg[v];
+#pragma unroll
+                for (int e = 0; e < C::VE; ++e) s[(c + e) * C::LDK + kp] = tmp.e[e];
+            }
         }
     }
 };
@@ -977,7 +998,12 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
                                                        const int32_t* __restrict__ seg_off,
                                                        const int32_t* __restrict__ n_seg_p,
                                                        float* __restrict__ t, int64_t ldt,
-                                                       typename C::T* __restrict__ t_ext, int64_t lde) {
+                                                       typename C::T* __restrict__ t_ext, int64_t lde,
+                                                       float* __restrict__ part, int32_t n_rows,
+                                                       int32_t ks_len) {
+    // part != nullptr: K is cut into slices of ks_len (a multiple of BK);
+    // workgroup (tile, blockIdx.y) writes the slice's partial
+    // part[slice][row][0:64] and the reduce pass forms t and t_ext.
     using T = typename C::T;
     static_assert(C::BN == 64, "shrink tile covers ranks up to 64");
     __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
@@ -1009,7 +1035,15 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
     __syncthreads();
 
     const int r_max = P.r_max;
+    const int slice = blockIdx.y;
     if (!id_ok(u, P.n_adapters)) {
+        if (part) {
+            for (int idx = tid; idx < cnt * 64; idx += C::NT) {
+                const int m = idx / 64;
+                part[((int64_t)slice * n_rows + sRow[m]) * 64 + (idx - m * 64)] = 0.f;
+            }
+            return;
+        }
         for (int idx = tid; idx < cnt * r_max; idx += C::NT) {
             const int m = idx / r_max;
             t[(int64_t)sRow[m] * ldt + (idx - m * r_max)] = 0.f;
@@ -1021,15 +1055,17 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
     const int ext_rank_cols = EXT_RANKS * ((r_max + EXT_RANKS - 1) / EXT_RANKS);
     const T* Au = (const T*)P.A + P.a_off[u];
     const bool vec = P.vec_a && ((r * (int)sizeof(T)) % 16) == 0;
-    const int K = P.d_in;
+    // this workgroup's K range; the loaders zero everything at or past kend
+    const int kbeg = part ? slice * ks_len : 0;
+    const int kend = part ? min(P.d_in, kbeg + ks_len) : P.d_in;
 
     Acc<C> acc;
     acc.zero();
     RowLoader<C, C::BM> la;
     TransLoader<C, C::BN> lb;
-    const int nk = (K + C::BK - 1) / C::BK;
-    la.load(x, ldx, sRow, 0, K, tid);
-    lb.load(Au, r, 0, K, 0, r, vec, tid);
+    const int nk = (kend - kbeg + C::BK - 1) / C::BK;
+    la.load(x, ldx, sRow, kbeg, kend, tid);
+    lb.load(Au, r, kbeg, kend, 0, r, vec, tid);
     for (int kb = 0; kb < nk; ++kb) {
         T* sA = smem + (kb & 1) * C::STAGE;
         T* sB = sA + C::A_ELEMS;
@@ -1037,8 +1073,8 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
         lb.store(sB, tid);
         __syncthreads();
         if (kb + 1 < nk) {
-            la.load(x, ldx, sRow, (kb + 1) * C::BK, K, tid);
-            lb.load(Au, r, (kb + 1) * C::BK, K, 0, r, vec, tid);
+            la.load(x, ldx, sRow, kbeg + (kb + 1) * C::BK, kend, tid);
+            lb.load(Au, r, kbeg + (kb + 1) * C::BK, kend, 0, r, vec, tid);
         }
         mma_block<C>(acc, sA, sB, wm, wn, lane);
     }
@@ -1054,6 +1090,11 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
                 const int m = wm * C::WTM + i * C::BLK + C::M::row(lane, q);
                 if (m >= cnt) continue;
                 const float v = acc.v[i][j][q];
+                if (part) {
+                    // columns past rank r are exact zeros (B side of the shrink was zero there)
+                    part[((int64_t)slice * n_rows + sRow[m]) * 64 + col] = v;
+                    continue;
+                }
                 if (col < r_max) t[(int64_t)sRow[m] * ldt + col] = v;
                 if (t_ext && col < ext_rank_cols) {
                     // columns past rank r are exact zeros (B side of the shrink was zero there)
@@ -1071,6 +1112,36 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
                 }
             }
         }
+}
+
+// t[row][j] = sum over slices (in order) of part[slice][row][j], and the
+// K-extension operand s * t (bf16 hi | lo blocks, or fp32) for the row.
+template <typename T>
+__global__ __launch_bounds__(256) void k_shrink_reduce(PoolDev P, const float* __restrict__ part, int32_t S,
+                                                       int32_t n_rows, const int32_t* __restrict__ ids,
+                                                       float* __restrict__ t, int64_t ldt,
+                                                       T* __restrict__ t_ext, int64_t lde) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int row = idx >> 6;
+    const int col = idx & 63;
+    if (row >= n_rows) return;
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[((int64_t)s * n_rows + row) * 64 + col];
+    if (col < P.r_max) t[(int64_t)row * ldt + col] = v;
+    const int ext_rank_cols = EXT_RANKS * ((P.r_max + EXT_RANKS - 1) / EXT_RANKS);
+    if (!t_ext || col >= ext_rank_cols) return;
+    const int a = ids[row];
+    const float sv = id_ok(a, P.n_adapters) ? P.scales[a] * v : 0.f;
+    T* er = t_ext + (int64_t)row * lde;
+    if constexpr (sizeof(T) == 2) {
+        const int e = col / EXT_RANKS;
+        const int jj = col - e * EXT_RANKS;
+        const bf16 hi = f32_to_bf16(sv);
+        er[e * 64 + jj] = (T)hi;
+        er[e * 64 + 32 + jj] = (T)f32_to_bf16(sv - to_f32(hi));
+    } else {
+        er[col] = (T)sv;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1242,21 +1313,47 @@ static int64_t seg_tiles(int32_t n_rows, int32_t n_bins, int bm) {
     return ceil_div(n_rows, bm) + std::min<int64_t>(n_rows, n_bins);
 }
 
-hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
-                              const lora_segments_t* seg, int32_t n_rows, int32_t n_bins, float* t,
-                              int64_t ldt, bool, hipStream_t stream, void* t_ext, int64_t lde) {
-    if (dt == LORA_BF16) {
-        dim3 grid((unsigned)seg_tiles(n_rows, n_bins, ShrinkB::BM));
-        hipLaunchKernelGGL(k_sgmv_shrink<ShrinkB>, grid, dim3(ShrinkB::NT), 0, stream, P,
-                           (const bf16*)x, ldx, seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, t,
-                           ldt, (bf16*)t_ext, lde);
-    } else {
-        dim3 grid((unsigned)seg_tiles(n_rows, n_bins, ShrinkF::BM));
-        hipLaunchKernelGGL(k_sgmv_shrink<ShrinkF>, grid, dim3(ShrinkF::NT), 0, stream, P,
-                           (const float*)x, ldx, seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, t,
-                           ldt, (float*)t_ext, lde);
+int32_t sgmv_shrink_slices(const PoolDev& P, int32_t n_rows) {
+    // about 512 workgroups over the row tiles, each slice at least 1024 k-rows
+    const int64_t tiles = std::max<int64_t>(1, ceil_div(n_rows, ShrinkB::BM));
+    const int64_t want = ceil_div(512, tiles);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(want, P.d_in / 1024));
+}
+
+size_t sgmv_shrink_part_bytes(const PoolDev& P, int32_t n_rows) {
+    const int32_t S = sgmv_shrink_slices(P, n_rows);
+    return S > 1 ? align_up((size_t)S * n_rows * 64 * 4, 256) : 0;
+}
+
+template <class C, typename T>
+static hipError_t run_shrink(const PoolDev& P, const void* x, int64_t ldx, const lora_segments_t* seg,
+                             int32_t n_rows, int32_t n_bins, float* t, int64_t ldt, void* t_ext, int64_t lde,
+                             const int32_t* ids, float* part, hipStream_t stream) {
+    int32_t S = part ? sgmv_shrink_slices(P, n_rows) : 1;
+    int32_t ks_len = P.d_in;
+    if (S > 1) {
+        ks_len = (int32_t)align_up((size_t)ceil_div(P.d_in, S), C::BK);
+        S = (int32_t)ceil_div(P.d_in, ks_len);
+    }
+    float* pt = S > 1 ? part : nullptr;
+    dim3 grid((unsigned)seg_tiles(n_rows, n_bins, C::BM), (unsigned)S);
+    hipLaunchKernelGGL(k_sgmv_shrink<C>, grid, dim3(C::NT), 0, stream, P, (const T*)x, ldx, seg->perm,
+                       seg->seg_ids, seg->seg_off, seg->n_seg, t, ldt, (T*)t_ext, lde, pt, n_rows, ks_len);
+    if (pt) {
+        dim3 rgrid((unsigned)ceil_div((int64_t)n_rows * 64, 256));
+        hipLaunchKernelGGL(k_shrink_reduce<T>, rgrid, dim3(256), 0, stream, P, (const float*)pt, S, n_rows, ids,
+                           t, ldt, (T*)t_ext, lde);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
+                              const lora_segments_t* seg, int32_t n_rows, int32_t n_bins, float* t,
+                              int64_t ldt, bool, hipStream_t stream, void* t_ext, int64_t lde,
+                              const int32_t* ids, float* part) {
+    if (dt == LORA_BF16)
+        return run_shrink<ShrinkB, bf16>(P, x, ldx, seg, n_rows, n_bins, t, ldt, t_ext, lde, ids, part, stream);
+    return run_shrink<ShrinkF, float>(P, x, ldx, seg, n_rows, n_bins, t, ldt, t_ext, lde, ids, part, stream);
 }
 
 template <class C, typename TY>

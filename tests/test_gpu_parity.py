@@ -531,6 +531,26 @@ def test_decode_small_shapes(n_rows, d_in, d_out):
     assert_close(y, o["y"], TOL[torch.bfloat16], "decode layer")
 
 
+@pytest.mark.parametrize("d_in", [2104, 3104])
+def test_sgmv_layer_split_k_shrink(d_in):
+    """SGMV layer with d_in >= 2048 and few row tiles: the shrink runs in K
+    slices (the last one ragged) whose partial sums a reduce pass adds."""
+    say(f"SGMV layer, split-K shrink: d_in {d_in}")
+    b = binding()
+    w = wl.small_batch(seed=d_in, device=DEV, dtype=torch.bfloat16, d_in=d_in, d_out=272, n_adapters=7,
+                       layout=wl.RAGGED, ranks=[3, 16, 64, 8, 40, 1, 32], frac_base=0.1,
+                       run_lengths=[1, 37, 64, 5, 1, 90, 2, 17])
+    p = w.projections[0]
+    o = run_oracle(w)
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    for lay in (b.LORA_W_OUT_IN, b.LORA_W_IN_OUT):
+        y = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=b.LORA_MODE_SGMV,
+                               y_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay}")
+
+
 def test_decode_invalid_ids_and_determinism():
     say("decode two-launch path: invalid ids flagged, run-to-run identical")
     b = binding()
