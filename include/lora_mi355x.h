@@ -217,13 +217,17 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
 
 /* y = x W + s * (x A[ids]) B[ids] for the whole batch: the shrink runs in
  * one launch (BGMV or SGMV), then one MFMA GEMM launch computes x W for all
- * rows and adds the scaled expand in its epilogue before the single
- * rounding of y ("Serving many LoRA adapters" (blog.ecitis.org), section
- * "Replay": segmented gather, grouped GEMM, scatter-add, fused output).
+ * rows and adds the scaled expand before the single rounding of y
+ * ("Serving many LoRA adapters" (blog.ecitis.org), section "Replay":
+ * segmented gather, grouped GEMM, scatter-add, fused output).  Each GEMM
+ * tile adds the expand either as extra K-blocks per distinct adapter (tiles
+ * of long runs of one id) or row by row after its K loop (tiles whose rows
+ * mostly carry different adapters).
  *   x [n_rows, ldx]; W per w_layout with leading dimension ldw; y [n_rows,
  *   ldy] of y_dtype.  `seg` may be NULL (SGMV builds segments in the
  *   workspace) or a descriptor already built for these ids.
- *   mode AUTO picks BGMV for short batches and SGMV otherwise. */
+ *   mode AUTO picks BGMV when n_rows <= 64 or n_rows <= 2 * n_adapters
+ *   (segments would mostly hold one or two rows) and SGMV otherwise. */
 lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx,
                                const void* W, int64_t ldw, lora_w_layout_t w_layout,
                                const int32_t* ids, const lora_segments_t* seg, int32_t n_rows,
@@ -235,8 +239,9 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx,
  *   y = x W                  when t is NULL (the base-only product).
  * Same argument rules as lora_layer_apply; t [n_rows, ldt] fp32 with
  * ldt >= r_max.  The workspace (lora_base_gemm_expand_workspace) holds the
- * scaled, split copy of t that the GEMM reads as extra K-blocks; with t NULL
- * no workspace is needed.  The base-only form measures what the adapters add
+ * scaled, split copy of t that the GEMM reads as extra K-blocks (tiles that
+ * add the expand row by row read t itself); with t NULL no workspace is
+ * needed.  The base-only form measures what the adapters add
  * to a step ("Serving many LoRA adapters" (blog.ecitis.org), section "What
  * to measure": adapter overhead fraction). */
 lora_status_t lora_base_gemm_expand_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes);

@@ -78,9 +78,12 @@ bool decode_ok(const lora_pool_s* pool, int32_t n_rows) {
     return pool->dtype == LORA_BF16 && n_rows >= 1 && n_rows <= kDecodeMaxRows;
 }
 
-lora_mode_t resolve_mode(lora_mode_t m, int32_t n_rows) {
+// AUTO: per-row gathers (BGMV) for decode-sized batches and for batches with
+// fewer than about two rows per pool adapter, where segments would mostly
+// hold one or two rows; grouping by adapter (SGMV) otherwise.
+lora_mode_t resolve_mode(lora_mode_t m, int32_t n_rows, int32_t n_adapters) {
     if (m != LORA_MODE_AUTO) return m;
-    return n_rows <= 64 ? LORA_MODE_BGMV : LORA_MODE_SGMV;
+    return (n_rows <= 64 || n_rows <= 2 * (int64_t)n_adapters) ? LORA_MODE_BGMV : LORA_MODE_SGMV;
 }
 
 }  // namespace
@@ -344,7 +347,7 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
     if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
     if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
         return LORA_E_INVALID;
-    const lora_mode_t m = resolve_mode(mode, n_rows);
+    const lora_mode_t m = resolve_mode(mode, n_rows, pool->dev.n_adapters);
     size_t off = align_up((size_t)n_rows * t_stride(pool->dev.r_max) * 4, 256) + ext_bytes(pool, n_rows);
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
@@ -379,7 +382,7 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     if (!al16(x) || !al16(W) || !al16(y) || !ld_ok(ldx, P.d_in, eb) || !ld_ok(ldw, w_min, eb) ||
         !ld_ok(ldy, P.d_out, ey))
         return LORA_E_UNSUPPORTED;
-    const lora_mode_t m = resolve_mode(mode, n_rows);
+    const lora_mode_t m = resolve_mode(mode, n_rows, pool->dev.n_adapters);
     if (m == LORA_MODE_SGMV && seg) {
         lora_status_t st = check_segments(seg, n_rows, P.n_adapters);
         if (st != LORA_OK) return st;
@@ -445,14 +448,15 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     g.w_out_in = (w_layout == LORA_W_OUT_IN) ? 1 : 0;
     g.ids = ids;
     g.n_rows = n_rows;
-    g.t = nullptr;
-    g.ldt = 0;
+    g.t = t;
+    g.ldt = ldt;
     g.t_ext = t_ext;
     g.lde = lde;
     g.y = y;
     g.ldy = ldy;
     g.vec_x = true;
     g.vec_w = true;
+    g.rows_distinct = (m == LORA_MODE_BGMV);
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
 }
 
@@ -501,7 +505,10 @@ lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx
         g.t = t;       // the skinny kernel adds s * t B in a VALU epilogue
         g.ldt = ldt;
     } else if (t) {
+        // tiles with few adapters fold t into the K loop, the others add it row by row
         if (!ws || !al16(ws) || ws_bytes < ext_bytes(pool, n_rows)) return LORA_E_WORKSPACE;
+        g.t = t;
+        g.ldt = ldt;
         g.t_ext = ws;
         g.lde = ext_cols(eb, P.r_max);
         hipError_t e = launch_make_t_ext(P, pool->dtype, t, ldt, ids, n_rows, ws, g.lde, stream);

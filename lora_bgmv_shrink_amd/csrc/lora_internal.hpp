@@ -147,14 +147,21 @@ struct GemmArgs {
     int w_out_in;
     const int32_t* ids;
     int32_t n_rows;
-    const float* t;   // fp32 t for the skinny kernel's epilogue (nullptr: no LoRA term)
+    // LoRA term: fp32 t (unscaled x A_a) for the skinny kernel's epilogue and
+    // the tiled kernel's row-wise epilogue; t_ext for the tiled kernel's
+    // K-extension.  Both nullptr: base product only.  The tiled kernel picks
+    // per tile among what is given.
+    const float* t;
     int64_t ldt;
-    const void* t_ext;   // K-extension operand for the tiled kernel (nullptr: no LoRA term)
+    const void* t_ext;
     int64_t lde;
     void* y;
     int64_t ldy;
     bool vec_x;
     bool vec_w;
+    // the caller expects most rows to carry different adapters (decode-style
+    // batches): a tile shape without the K-extension may be chosen
+    bool rows_distinct = false;
 };
 hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt,
                              const GemmArgs& g, hipStream_t stream);

@@ -645,6 +645,126 @@ struct GemmDev {
     int32_t tiles_n;
 };
 
+// VE consecutive outputs of one row, rounded once; 8-, 16- or 32-byte
+// pieces where the row is whole and aligned, else one element at a time.
+template <typename TY, int VE>
+__device__ __forceinline__ void store_row_piece(TY* p, const float* v, int valid, bool vec) {
+    if (vec && valid >= VE) {
+        union { TY e[VE]; uint2 h[VE * sizeof(TY) / 8]; } o;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) o.e[e] = from_f32<TY>(v[e]);
+        if constexpr (VE * sizeof(TY) == 8) {
+            *(uint2*)p = o.h[0];
+        } else {
+#pragma unroll
+            for (int h = 0; h < (int)(VE * sizeof(TY) / 16); ++h)
+                ((uint4*)p)[h] = make_uint4(o.h[2 * h].x, o.h[2 * h].y, o.h[2 * h + 1].x, o.h[2 * h + 1].y);
+        }
+    } else {
+        for (int e = 0; e < VE && e < valid; ++e) p[e] = from_f32<TY>(v[e]);
+    }
+}
+
+// Row-wise expand epilogue, for tiles whose rows carry many different
+// adapters (decode-style batches in arrival order), where the K-extension
+// would add one block of MFMA work per distinct adapter:
+//     y[m, n] = acc[m, n] + s_a * sum_j t[m, j] * B_a[j, n],   a = id of row m.
+// Each wave stages one block-row of its accumulators (BLK x WTN fp32) in
+// its own slice of LDS, then reads it back one output row piece per lane
+// (VE columns, a 16-byte piece of a B row) and streams the r rows of B_a
+// for that piece, RC rank rows at a time.  The tile's LDS stages must no
+// longer be in use when this starts.
+template <class C, typename TY>
+__device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev& g, Acc<C>& acc,
+                                                float* sw_all, const RowRec* sRec, int m0, int n0, int wm,
+                                                int wn, int wave, int lane) {
+    using T = typename C::T;
+    constexpr int VE = C::VE;
+    constexpr int LPR = C::WTN / VE;   // lanes per output row
+    constexpr int RPI = 64 / LPR;      // rows per pass of the wave (lanes past BLK rows idle)
+    constexpr int LDW = C::WTN + 4;    // fp32 pitch of a staged row
+    // rank rows requested together: all 16 of a rank-16 adapter where the
+    // tile's LDS already holds a CU to one 4-wave workgroup (registers to
+    // spare), else 8 so the epilogue does not raise the kernel's register count
+    constexpr int RC = (C::NT <= 256 && 2 * C::STAGE * (int)sizeof(T) > 80 * 1024) ? 16 : 8;
+    constexpr int PASSES = (C::BLK + RPI - 1) / RPI;
+    static_assert(C::WTN % VE == 0 && 64 % LPR == 0 && (C::BLK % RPI == 0 || RPI % C::BLK == 0),
+                  "epilogue lane map");
+    static_assert(C::WM * C::WN * C::BLK * LDW * 4 <= 2 * C::STAGE * (int)sizeof(T), "epilogue staging");
+    float* sw = sw_all + wave * C::BLK * LDW;
+    const int N = P.d_out;
+    const int lr = lane / LPR;
+    const int cc = (lane % LPR) * VE;
+    const int col = n0 + wn * C::WTN + cc;
+    const int valid_c = N - col;
+    const bool full = valid_c >= VE;
+    const bool vec_y = ((g.ldy * (int64_t)sizeof(TY)) & 15) == 0;
+    TY* Y = (TY*)g.y;
+    const int lc = lane % C::BLK;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < C::M::NACC; ++q) sw[C::M::row(lane, q) * LDW + j * C::BLK + lc] = acc.v[i][j][q];
+        __syncthreads();
+#pragma unroll 1
+        for (int it = 0; it < PASSES; ++it) {
+            const int rl = it * RPI + lr;
+            const int tr = wm * C::WTM + i * C::BLK + rl;   // row within the tile
+            const int row = m0 + tr;
+            if (rl >= C::BLK || row >= g.n || valid_c <= 0) continue;
+            float v[VE];
+#pragma unroll
+            for (int e = 0; e < VE; e += 4) {
+                const float4 b4 = *(const float4*)(sw + rl * LDW + cc + e);
+                v[e] = b4.x;
+                v[e + 1] = b4.y;
+                v[e + 2] = b4.z;
+                v[e + 3] = b4.w;
+            }
+            const RowRec rec = sRec[tr];
+            if (rec.rank > 0) {
+                const int r = rec.rank;
+                const T* Bu = (const T*)P.B + rec.b_off + col;
+                const float* trow = g.t + (int64_t)row * g.ldt;
+                float ex[VE];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) ex[e] = 0.f;
+                for (int j0 = 0; j0 < r; j0 += RC) {
+                    uint4 bv[RC];
+                    float tv[RC];
+#pragma unroll
+                    for (int q = 0; q < RC; ++q) {
+                        const int jj = j0 + q;
+                        const T* bj = Bu + (int64_t)jj * N;
+                        tv[q] = (jj < r) ? trow[jj] : 0.f;
+                        if (jj < r && full && P.vec_b) {
+                            bv[q] = *(const uint4*)bj;
+                        } else {
+                            union { uint4 u; T e[VE]; } w;
+#pragma unroll
+                            for (int e = 0; e < VE; ++e) w.e[e] = (jj < r && e < valid_c) ? bj[e] : (T)0;
+                            bv[q] = w.u;
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < RC; ++q) {
+                        union { uint4 u; T e[VE]; } w;
+                        w.u = bv[q];
+#pragma unroll
+                        for (int e = 0; e < VE; ++e) ex[e] += tv[q] * to_f32(w.e[e]);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < VE; ++e) v[e] += rec.scale * ex[e];
+            }
+            store_row_piece<TY, VE>(Y + (int64_t)row * g.ldy + col, v, valid_c, vec_y);
+        }
+        __syncthreads();
+    }
+}
+
 // The LoRA expand rides on the same K loop: after the d_in/BK blocks of
 // x W come, for every distinct adapter u among the tile's rows (ascending
 // id), ceil(r_u / KH) blocks whose A side is t_ext (s_u * t split into bf16
@@ -654,7 +774,9 @@ struct GemmDev {
 template <class C, typename TY, bool OUT_IN>
 __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     using T = typename C::T;
-    static_assert(C::BK == ext_block_cols(sizeof(T)) && C::KH == EXT_RANKS, "t_ext block layout");
+    // K-extension only where a K-block is one t_ext block; other tile shapes
+    // always take the row-wise epilogue
+    constexpr bool EXT = C::BK == ext_block_cols(sizeof(T)) && C::KH == EXT_RANKS;
     __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
     __shared__ int sRowA[C::BM];
     __shared__ int sRowB[OUT_IN ? C::BN : 1];
@@ -662,6 +784,10 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     __shared__ int sExt[2 * C::BM];   // (u << 1) | block, in order
     __shared__ int sNext;
     __shared__ int sNExt;
+    __shared__ int sRuns;
+    __shared__ int sValid;
+    __shared__ RowRec sRec[C::BM];   // per tile row: B offset, rank, scale (row-wise epilogue)
+    static_assert(C::BM <= C::NT, "one tile row per thread in the set-up");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -688,24 +814,62 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     const int K = P.d_in;
     const int N = P.d_out;
 
-    for (int r = tid; r < C::BM; r += C::NT) {
-        const int row = m0 + r;
+    if (tid < C::BM) {
+        const int row = m0 + tid;
         int id = INT_MAX;
         if (row < g.n) {
             const int a = g.ids[row];
             if (id_ok(a, P.n_adapters)) id = a;
             else if (a != -1 && tn == 0) flag_bad_id(P.err);
         }
-        sRowA[r] = row < g.n ? row : -1;
-        sId[r] = id;
+        sRowA[tid] = row < g.n ? row : -1;
+        sId[tid] = id;
+        if (g.t) {
+            RowRec rec{0, 0, 0.f};
+            if (id != INT_MAX) {
+                rec.b_off = P.b_off[id];
+                rec.rank = P.ranks[id];
+                rec.scale = P.scales[id];
+            }
+            sRec[tid] = rec;
+        }
     }
     if constexpr (OUT_IN)
         for (int r = tid; r < C::BN; r += C::NT) sRowB[r] = (n0 + r < N) ? n0 + r : -1;
-    if (tid == 0) sNExt = 0;
+    if (tid == 0) {
+        sNExt = 0;
+        sRuns = 0;
+        sValid = 0;
+    }
     __syncthreads();
 
+    // Runs of one adapter id down the tile's rows (looking past a few
+    // base-only rows) estimate its distinct adapters.  The K-extension costs
+    // a block of MFMA work per adapter but reads each adapter's B once; the
+    // row-wise epilogue reads B once per row.  Tiles whose runs average at
+    // most two rows (decode-style rows in arrival order) take the epilogue.
+    bool gather = false;
+    if (g.t) {
+        if (tid < C::BM) {
+            const int v = sId[tid];
+            if (v != INT_MAX) {
+                int prev = INT_MAX;
+                for (int k = tid - 1; k >= 0 && k >= tid - 8; --k)
+                    if (sId[k] != INT_MAX) {
+                        prev = sId[k];
+                        break;
+                    }
+                atomicAdd(&sValid, 1);
+                if (prev != v) atomicAdd(&sRuns, 1);
+            }
+        }
+        __syncthreads();
+        const int per_adapter = (P.r_max + EXT_RANKS - 1) / EXT_RANKS;
+        gather = !EXT || !g.t_ext || (sRuns * per_adapter > 2 && 2 * sRuns >= sValid);
+    }
+
     // K-extension blocks: distinct adapters of the tile in ascending order
-    if (g.t_ext) {
+    if (EXT && g.t_ext && !gather) {
         int prev = -1;
         for (;;) {
             if (tid == 0) sNext = INT_MAX;
@@ -857,16 +1021,24 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     }
     // the LoRA K-extension blocks, same pipeline (their first block is fetched
     // here; the stage it goes to was last read two blocks ago)
-    if (n_ext > 0) load_ext(0);
-    for (int e = 0; e < n_ext; ++e) {
-        const int kb = nk + e;
-        T* sA = smem + (kb & 1) * C::STAGE;
-        T* sB = sA + C::A_ELEMS;
-        la.store(sA, tid);
-        store_trans(sB);
-        __syncthreads();
-        if (e + 1 < n_ext) load_ext(e + 1);
-        mma_block<C>(acc, sA, sB, wm, wn, lane);
+    if constexpr (EXT) {
+        if (n_ext > 0) load_ext(0);
+        for (int e = 0; e < n_ext; ++e) {
+            const int kb = nk + e;
+            T* sA = smem + (kb & 1) * C::STAGE;
+            T* sB = sA + C::A_ELEMS;
+            la.store(sA, tid);
+            store_trans(sB);
+            __syncthreads();
+            if (e + 1 < n_ext) load_ext(e + 1);
+            mma_block<C>(acc, sA, sB, wm, wn, lane);
+        }
+    }
+
+    if (gather) {
+        __syncthreads();   // every wave is done with the LDS stages
+        gather_epilogue<C, TY>(P, g, acc, (float*)smem, sRec, m0, n0, wm, wn, wave, lane);
+        return;
     }
 
     TY* Y = (TY*)g.y;
@@ -1226,6 +1398,11 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_expand(PoolDev P, const float* _
 using GemmHuge = Cfg<bf16, 256, 256, 64, 2, 4, 32>;
 using GemmBig = Cfg<bf16, 128, 128, 64, 2, 2, 32>;
 using GemmMid = Cfg<bf16, 64, 64, 64, 2, 2>;
+// base products and decode-style batches of a few hundred rows: the tiles
+// are small to reach every CU, so each K-block is made 256 deep to keep
+// 64 KiB per workgroup in flight (too deep for the K-extension: the LoRA
+// term is added row by row after the K loop)
+using GemmMed = Cfg<bf16, 64, 64, 256, 2, 2>;
 using GemmSmall = Cfg<bf16, 32, 64, 64, 2, 2>;
 using GemmF32 = Cfg<float, 64, 64, 32, 2, 2>;
 // K-blocks of 256: each workgroup keeps 64 KiB of x and A in flight
@@ -1243,8 +1420,8 @@ hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     g.ldw = a.ldw;
     g.ids = a.ids;
     g.n = a.n_rows;
-    g.t = nullptr;
-    g.ldt = 0;
+    g.t = a.t;
+    g.ldt = a.ldt;
     g.t_ext = a.t_ext;
     g.lde = a.lde;
     g.y = a.y;
@@ -1296,6 +1473,7 @@ hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream
     auto tiles = [&](int bm, int bn) { return ceil_div(a.n_rows, bm) * ceil_div(P.d_out, bn); };
     if (tiles(GemmHuge::BM, GemmHuge::BN) >= 200) return run_gemm<GemmHuge, TY>(P, a, stream);
     if (tiles(GemmBig::BM, GemmBig::BN) >= 200) return run_gemm<GemmBig, TY>(P, a, stream);
+    if (a.w_out_in && (!a.t_ext || (a.t && a.rows_distinct))) return run_gemm<GemmMed, TY>(P, a, stream);
     if (tiles(GemmMid::BM, GemmMid::BN) >= 128 || a.n_rows > 32) return run_gemm<GemmMid, TY>(P, a, stream);
     return run_gemm<GemmSmall, TY>(P, a, stream);
 }

@@ -551,6 +551,33 @@ def test_sgmv_layer_split_k_shrink(d_in):
         assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay}")
 
 
+@pytest.mark.parametrize("d_in,d_out,layout,runs", [
+    (136, 200, wl.RAGGED, None),        # K shorter than one 256-deep block
+    (776, 1032, wl.RAGGED, None),       # whole blocks plus a ragged K tail
+    (1000, 776, wl.UNIFORM, [1, 2, 1, 40, 3, 1, 1, 90, 1, 2, 5, 1, 60, 1, 1, 91]),
+])
+def test_layer_many_adapters_per_tile(d_in, d_out, layout, runs):
+    """Row tiles that hold many different adapters add the LoRA term row by
+    row after the K loop; tiles of one or two long runs in the same launch
+    keep the K-extension.  Both W layouts, both modes, fp32 and bf16 y."""
+    say(f"layer, many adapters per tile: d_in {d_in} d_out {d_out} runs {runs is not None}")
+    b = binding()
+    ranks = (RAGGED_RANKS * 4)[:40] if layout == wl.RAGGED else 16
+    w = wl.small_batch(seed=d_in + d_out, n_rows=257, device=DEV, dtype=torch.bfloat16, d_in=d_in,
+                       d_out=d_out, n_adapters=40, layout=layout, ranks=ranks, frac_base=0.1,
+                       run_lengths=runs, scale=np.linspace(-2.0, 2.0, 40).astype(np.float32))
+    p = w.projections[0]
+    o = run_oracle(w)
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    for lay in (b.LORA_W_OUT_IN, b.LORA_W_IN_OUT):
+        for m in (b.LORA_MODE_BGMV, b.LORA_MODE_SGMV, b.LORA_MODE_AUTO):
+            for ydt in (torch.float32, torch.bfloat16):
+                y = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=m, y_dtype=ydt)
+                torch.cuda.synchronize()
+                assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay} mode {m} {ydt}")
+
+
 def test_decode_invalid_ids_and_determinism():
     say("decode two-launch path: invalid ids flagged, run-to-run identical")
     b = binding()
