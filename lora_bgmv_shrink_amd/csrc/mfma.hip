@@ -684,9 +684,11 @@ __device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev&
     constexpr int RPI = 64 / LPR;      // rows per pass of the wave (lanes past BLK rows idle)
     constexpr int LDW = C::WTN + 4;    // fp32 pitch of a staged row
     // rank rows requested together: all 16 of a rank-16 adapter where the
-    // tile's LDS already holds a CU to one 4-wave workgroup (registers to
-    // spare), else 8 so the epilogue does not raise the kernel's register count
-    constexpr int RC = (C::NT <= 256 && 2 * C::STAGE * (int)sizeof(T) > 80 * 1024) ? 16 : 8;
+    // tile's LDS already limits a CU to two workgroups and the accumulator is
+    // small (registers to spare), else 8 so that the epilogue does not raise
+    // the kernel's register count
+    constexpr int RC =
+        (2 * C::STAGE * (int)sizeof(T) > 64 * 1024 && C::FM * C::FN * C::M::NACC <= 64) ? 16 : 8;
     constexpr int PASSES = (C::BLK + RPI - 1) / RPI;
     static_assert(C::WTN % VE == 0 && 64 % LPR == 0 && (C::BLK % RPI == 0 || RPI % C::BLK == 0),
                   "epilogue lane map");
@@ -1396,7 +1398,7 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_expand(PoolDev P, const float* _
 // ---------------------------------------------------------------------------
 
 using GemmHuge = Cfg<bf16, 256, 256, 64, 2, 4, 32>;
-using GemmBig = Cfg<bf16, 128, 128, 64, 2, 2, 32>;
+using GemmBig = Cfg<bf16, 128, 128, 64, 2, 4, 32>;
 using GemmMid = Cfg<bf16, 64, 64, 64, 2, 2>;
 // base products and decode-style batches of a few hundred rows: the tiles
 // are small to reach every CU, so each K-block is made 256 deep to keep
