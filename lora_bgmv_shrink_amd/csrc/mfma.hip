@@ -1464,8 +1464,22 @@ hipError_t run_skinny(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Rows [r0, n) of a GEMM call as a call of their own (the row tiles of the
+// two calls are disjoint; every pointer moves by r0 rows).
 template <typename TY>
-hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
+GemmArgs rows_from(const GemmArgs& a, int32_t r0) {
+    GemmArgs b = a;
+    b.x = (const bf16*)a.x + (int64_t)r0 * a.ldx;
+    b.ids = a.ids + r0;
+    b.n_rows = a.n_rows - r0;
+    if (a.t) b.t = a.t + (int64_t)r0 * a.ldt;
+    if (a.t_ext) b.t_ext = (const bf16*)a.t_ext + (int64_t)r0 * a.lde;
+    b.y = (TY*)a.y + (int64_t)r0 * a.ldy;
+    return b;
+}
+
+template <typename TY>
+hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream, bool tail = false) {
     if (a.w_out_in && a.n_rows <= 64 && !a.t_ext) {
         if (a.n_rows <= 16) return run_skinny<TY, 1>(P, a, stream);
         if (a.n_rows <= 32) return run_skinny<TY, 2>(P, a, stream);
@@ -1473,8 +1487,31 @@ hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream
     }
     // Largest tile that still gives about one workgroup per CU.
     auto tiles = [&](int bm, int bn) { return ceil_div(a.n_rows, bm) * ceil_div(P.d_out, bn); };
-    if (tiles(GemmHuge::BM, GemmHuge::BN) >= 200) return run_gemm<GemmHuge, TY>(P, a, stream);
-    if (tiles(GemmBig::BM, GemmBig::BN) >= 200) return run_gemm<GemmBig, TY>(P, a, stream);
+    const int64_t th = tiles(GemmHuge::BM, GemmHuge::BN);
+    if (th >= 200) {
+        // The 256x256 tiles run one per CU, in rounds of 256.  When the last
+        // round would be mostly idle, the row tiles that fill whole rounds
+        // take the 256x256 launch and the remaining rows a launch of 128x128
+        // tiles (a quarter of the work each).
+        const int64_t tn = ceil_div(P.d_out, GemmHuge::BN);
+        const int64_t tm_h = (th / 256) * 256 / tn;
+        const int32_t r0 = (int32_t)(tm_h * GemmHuge::BM);
+        if (tm_h > 0 && r0 < a.n_rows) {
+            const double rounds = (double)ceil_div(th, 256);
+            const double rounds_h = (double)ceil_div(tm_h * tn, 256);
+            const double tail_rounds =
+                0.35 * (double)ceil_div(ceil_div(a.n_rows - r0, GemmBig::BM) * ceil_div(P.d_out, GemmBig::BN), 256);
+            if (rounds_h + tail_rounds < rounds - 0.25) {
+                GemmArgs h = a;
+                h.n_rows = r0;
+                const hipError_t e = run_gemm<GemmHuge, TY>(P, h, stream);
+                if (e != hipSuccess) return e;
+                return run_gemm_bf16<TY>(P, rows_from<TY>(a, r0), stream, true);
+            }
+        }
+        return run_gemm<GemmHuge, TY>(P, a, stream);
+    }
+    if (tiles(GemmBig::BM, GemmBig::BN) >= (tail ? 64 : 200)) return run_gemm<GemmBig, TY>(P, a, stream);
     if (a.w_out_in && (!a.t_ext || (a.t && a.rows_distinct))) return run_gemm<GemmMed, TY>(P, a, stream);
     if (tiles(GemmMid::BM, GemmMid::BN) >= 128 || a.n_rows > 32) return run_gemm<GemmMid, TY>(P, a, stream);
     return run_gemm<GemmSmall, TY>(P, a, stream);

@@ -578,6 +578,30 @@ def test_layer_many_adapters_per_tile(d_in, d_out, layout, runs):
                 assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay} mode {m} {ydt}")
 
 
+def test_layer_tail_rows_split_launch():
+    """520 rows x 22,016 columns: 258 tiles of 256x256 would leave a last
+    round of two; rows [0, 512) take the 256x256 launch and rows [512, 520)
+    a launch of 128x128 tiles.  Every row checked, both W layouts and modes."""
+    say("layer, 256x256 launch plus a tail launch: 520 x 136 -> 22016")
+    b = binding()
+    w = wl.small_batch(seed=520, n_rows=520, device=DEV, dtype=torch.bfloat16, d_in=136, d_out=22016,
+                       n_adapters=12, layout=wl.RAGGED, ranks=RAGGED_RANKS, frac_base=0.1,
+                       run_lengths=[1, 3, 200, 5, 1, 290, 2, 7, 1, 10])
+    p = w.projections[0]
+    o = run_oracle(w)
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    for lay in (b.LORA_W_OUT_IN, b.LORA_W_IN_OUT):
+        for m in (b.LORA_MODE_BGMV, b.LORA_MODE_SGMV):
+            y = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=m, y_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay} mode {m}")
+    yb = b.lora_base_gemm_expand(pool, p.x, w_stored(p.W, b.LORA_W_OUT_IN), ids, None, w_layout=b.LORA_W_OUT_IN,
+                                 y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(yb, o["y"] - o["lora"], TOL[torch.bfloat16], "base-only y")
+
+
 def test_decode_invalid_ids_and_determinism():
     say("decode two-launch path: invalid ids flagged, run-to-run identical")
     b = binding()
