@@ -416,6 +416,7 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     const int64_t lde = ext_cols(eb, P.r_max);
     const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256) + ext_bytes(pool, n_rows);
     hipError_t e = hipSuccess;
+    const int32_t* gemm_perm = nullptr;   // SGMV: the GEMM visits rows grouped by adapter
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
         e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, base + after_t, plan,
@@ -438,6 +439,7 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
         if (e == hipSuccess)
             e = launch_sgmv_shrink(P, pool->dtype, x, ldx, sg, n_rows, P.n_adapters + 1, t, ldt, true,
                                    stream, t_ext, lde, ids, part);
+        if ((int64_t)n_rows * ldx * eb < ((int64_t)1 << 31)) gemm_perm = sg->perm;
     }
     if (e != hipSuccess) return LORA_E_DEVICE;
     GemmArgs g;
@@ -457,6 +459,8 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     g.vec_x = true;
     g.vec_w = true;
     g.rows_distinct = (m == LORA_MODE_BGMV);
+    g.perm = gemm_perm;
+    g.x_rows = n_rows;
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
 }
 

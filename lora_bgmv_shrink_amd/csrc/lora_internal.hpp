@@ -162,6 +162,11 @@ struct GemmArgs {
     // the caller expects most rows to carry different adapters (decode-style
     // batches): a tile shape without the K-extension may be chosen
     bool rows_distinct = false;
+    // tiled kernel: visit the rows in this order (tile row m is row perm[m];
+    // null: in order), e.g. grouped by adapter so that a tile holds few
+    // adapters.  x_rows: rows x holds (0: n_rows).  Needs x under 2 GiB.
+    const int32_t* perm = nullptr;
+    int32_t x_rows = 0;
 };
 hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt,
                              const GemmArgs& g, hipStream_t stream);

@@ -213,6 +213,32 @@ struct RowLoader {
             reg[v] = __builtin_bit_cast(uint4, x);
         }
     }
+    // Byte offsets of this lane's pieces within a buffer resource: row
+    // sRow[r] - base_row of the source, or `none` (past the resource's range,
+    // so the piece reads as 0) for a row of -1.  Computed once per tile.
+    __device__ __forceinline__ void row_offsets(const int* sRow, int base_row, int64_t ld, int none, int tid,
+                                                int (&voff)[NV]) const {
+        static_assert(C::NT % VPR == 0, "pieces of a lane share one column");
+        const int r0 = tid / VPR;
+        const int c = (tid - r0 * VPR) * C::VE;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int gr = (TOT % C::NT != 0 && tid + v * C::NT >= TOT) ? -1 : sRow[r0 + v * (C::NT / VPR)];
+            voff[v] = gr >= 0 ? (int)(((int64_t)(gr - base_row) * ld + c) * (int64_t)sizeof(T)) : none;
+        }
+    }
+    // A whole K-block (k0 + BK <= K) through a buffer resource, each piece at
+    // its precomputed row offset (a VGPR) plus the K position (a scalar).
+    __device__ __forceinline__ void load_buf_off(__amdgpu_buffer_rsrc_t rs, const int (&voff)[NV], int k0,
+                                                 int tid) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            if (TOT % C::NT != 0 && tid + v * C::NT >= TOT) break;
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[v], k0 * (int)sizeof(T), 0);
+            reg[v] = __builtin_bit_cast(uint4, x);
+        }
+    }
     // A whole K-block (k0 + BK <= K) of rows row0 .. row0 + ROWS - 1, those at
     // or past nrows read as row 0 (they only feed outputs never stored):
     // unconditional loads, no row table, no branch.
@@ -643,6 +669,10 @@ struct GemmDev {
     int64_t ldy;
     int32_t tiles_m;
     int32_t tiles_n;
+    // tiled kernel: tile row m is row perm[m] of x, ids, t, t_ext and y
+    // (null: row m); x holds x_rows addressable rows
+    const int32_t* perm;
+    int32_t x_rows;
 };
 
 // VE consecutive outputs of one row, rounded once; 8-, 16- or 32-byte
@@ -676,8 +706,8 @@ __device__ __forceinline__ void store_row_piece(TY* p, const float* v, int valid
 // longer be in use when this starts.
 template <class C, typename TY>
 __device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev& g, Acc<C>& acc,
-                                                float* sw_all, const RowRec* sRec, int m0, int n0, int wm,
-                                                int wn, int wave, int lane) {
+                                                float* sw_all, const RowRec* sRec, const int* sRow, int n0,
+                                                int wm, int wn, int wave, int lane) {
     using T = typename C::T;
     constexpr int VE = C::VE;
     constexpr int LPR = C::WTN / VE;   // lanes per output row
@@ -714,8 +744,8 @@ __device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev&
         for (int it = 0; it < PASSES; ++it) {
             const int rl = it * RPI + lr;
             const int tr = wm * C::WTM + i * C::BLK + rl;   // row within the tile
-            const int row = m0 + tr;
-            if (rl >= C::BLK || row >= g.n || valid_c <= 0) continue;
+            const int row = (rl < C::BLK) ? sRow[tr] : -1;    // its row of t and y
+            if (row < 0 || valid_c <= 0) continue;
             float v[VE];
 #pragma unroll
             for (int e = 0; e < VE; e += 4) {
@@ -818,13 +848,16 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
 
     if (tid < C::BM) {
         const int row = m0 + tid;
+        // a perm entry outside x's rows (a malformed descriptor) skips the row
+        const int pr = row < g.n ? (g.perm ? g.perm[row] : row) : -1;
+        const int src = (pr >= 0 && pr < g.x_rows) ? pr : -1;
         int id = INT_MAX;
-        if (row < g.n) {
-            const int a = g.ids[row];
+        if (src >= 0) {
+            const int a = g.ids[src];
             if (id_ok(a, P.n_adapters)) id = a;
             else if (a != -1 && tn == 0) flag_bad_id(P.err);
         }
-        sRowA[tid] = row < g.n ? row : -1;
+        sRowA[tid] = src;
         sId[tid] = id;
         if (g.t) {
             RowRec rec{0, 0, 0.f};
@@ -904,7 +937,8 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     BLoader<C> lb;
     RowLoader<C, C::BN> lw;   // W rows (OUT_IN) share the B register set's shape
     auto load_main = [&](int s) {
-        la.load_direct(X, g.ldx, m0, g.n, s * C::BK, K, tid);
+        if (g.perm) la.load(X, g.ldx, sRowA, s * C::BK, K, tid);
+        else la.load_direct(X, g.ldx, m0, g.n, s * C::BK, K, tid);
         if constexpr (OUT_IN) lw.load_direct(Wp, g.ldw, n0, N, s * C::BK, K, tid);
         else if constexpr (sizeof(T) == 2) lb.load_trans_pairs(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
         else lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
@@ -941,10 +975,16 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, bytes,
                                                      0x00020000);
         };
-        const __amdgpu_buffer_rsrc_t rs_a = rsrc(X + (int64_t)m0 * g.ldx, max(0, min(C::BM, g.n - m0)), g.ldx);
+        // x rows: relative to the tile's first row, or (rows gathered through
+        // perm) to row 0 of x; a row of -1 reads past the range
+        const int a_base = g.perm ? 0 : m0;
+        const int a_rows = g.perm ? g.x_rows : max(0, min(C::BM, g.n - m0));
+        const __amdgpu_buffer_rsrc_t rs_a = rsrc(X + (int64_t)a_base * g.ldx, a_rows, g.ldx);
         const __amdgpu_buffer_rsrc_t rs_w = rsrc(Wp + (int64_t)n0 * g.ldw, max(0, min(C::BN, N - n0)), g.ldw);
+        int a_off[RowLoader<C, C::BM>::NV];
+        la.row_offsets(sRowA, a_base, g.ldx, (int)((int64_t)a_rows * g.ldx * (int64_t)sizeof(T)), tid, a_off);
         auto load_full = [&](int s) {
-            la.load_buf(rs_a, g.ldx, s * C::BK, tid);
+            la.load_buf_off(rs_a, a_off, s * C::BK, tid);
             lw.load_buf(rs_w, g.ldw, s * C::BK, tid);
         };
         auto step = [&](int kb) {
@@ -962,7 +1002,7 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             RowLoader<C, C::BM> la2;
             RowLoader<C, C::BN> lw2;
             auto load_full2 = [&](int s) {
-                la2.load_buf(rs_a, g.ldx, s * C::BK, tid);
+                la2.load_buf_off(rs_a, a_off, s * C::BK, tid);
                 lw2.load_buf(rs_w, g.ldw, s * C::BK, tid);
             };
             auto step2 = [&](int k) {
@@ -1039,7 +1079,7 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
 
     if (gather) {
         __syncthreads();   // every wave is done with the LDS stages
-        gather_epilogue<C, TY>(P, g, acc, (float*)smem, sRec, m0, n0, wm, wn, wave, lane);
+        gather_epilogue<C, TY>(P, g, acc, (float*)smem, sRec, sRowA, n0, wm, wn, wave, lane);
         return;
     }
 
@@ -1052,8 +1092,8 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             const int col = n0 + wn * C::WTN + j * C::BLK + lc;
 #pragma unroll
             for (int q = 0; q < C::M::NACC; ++q) {
-                const int row = m0 + wm * C::WTM + i * C::BLK + C::M::row(lane, q);
-                if (row < g.n && col < N) Y[(int64_t)row * g.ldy + col] = from_f32<TY>(acc.v[i][j][q]);
+                const int row = sRowA[wm * C::WTM + i * C::BLK + C::M::row(lane, q)];
+                if (row >= 0 && col < N) Y[(int64_t)row * g.ldy + col] = from_f32<TY>(acc.v[i][j][q]);
             }
         }
 }
@@ -1430,6 +1470,8 @@ hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     g.ldy = a.ldy;
     g.tiles_m = (int32_t)ceil_div(a.n_rows, C::BM);
     g.tiles_n = (int32_t)ceil_div(P.d_out, C::BN);
+    g.perm = a.perm;
+    g.x_rows = a.x_rows > 0 ? a.x_rows : a.n_rows;
     dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n));
     if (a.w_out_in)
         hipLaunchKernelGGL((k_layer_gemm<C, TY, true>), grid, dim3(C::NT), 0, stream, P, g);
@@ -1453,6 +1495,8 @@ hipError_t run_skinny(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     g.lde = 0;
     g.y = a.y;
     g.ldy = a.ldy;
+    g.perm = nullptr;
+    g.x_rows = a.n_rows;
     g.tiles_m = 1;
     g.tiles_n = (int32_t)ceil_div(P.d_out, 16);
     dim3 grid((unsigned)g.tiles_n);
@@ -1464,14 +1508,21 @@ hipError_t run_skinny(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Rows [r0, n) of a GEMM call as a call of their own (the row tiles of the
-// two calls are disjoint; every pointer moves by r0 rows).
+// Tile rows [r0, n) of a GEMM call as a call of their own (the row tiles of
+// the two calls are disjoint).  With perm only perm moves; otherwise every
+// row pointer moves by r0 rows.
 template <typename TY>
 GemmArgs rows_from(const GemmArgs& a, int32_t r0) {
     GemmArgs b = a;
-    b.x = (const bf16*)a.x + (int64_t)r0 * a.ldx;
-    b.ids = a.ids + r0;
     b.n_rows = a.n_rows - r0;
+    if (a.perm) {
+        b.perm = a.perm + r0;
+        b.x_rows = a.x_rows > 0 ? a.x_rows : a.n_rows;
+        return b;
+    }
+    b.x = (const bf16*)a.x + (int64_t)r0 * a.ldx;
+    b.x_rows = 0;
+    b.ids = a.ids + r0;
     if (a.t) b.t = a.t + (int64_t)r0 * a.ldt;
     if (a.t_ext) b.t_ext = (const bf16*)a.t_ext + (int64_t)r0 * a.lde;
     b.y = (TY*)a.y + (int64_t)r0 * a.ldy;
@@ -1480,7 +1531,7 @@ GemmArgs rows_from(const GemmArgs& a, int32_t r0) {
 
 template <typename TY>
 hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream, bool tail = false) {
-    if (a.w_out_in && a.n_rows <= 64 && !a.t_ext) {
+    if (a.w_out_in && a.n_rows <= 64 && !a.t_ext && !a.perm) {
         if (a.n_rows <= 16) return run_skinny<TY, 1>(P, a, stream);
         if (a.n_rows <= 32) return run_skinny<TY, 2>(P, a, stream);
         return run_skinny<TY, 4>(P, a, stream);
