@@ -295,10 +295,15 @@ def bench_multi(torch, args, name):
     for label, plist in pools:
         hs = [make_pool(b, pl) for pl in plist]
         wss = [torch.zeros(b.lora_layer_workspace(h, n), dtype=torch.uint8, device=dev) for h in hs]
+        # one batch, one group-by: the segments are built once per step and
+        # handed to every projection (a layer that picks BGMV ignores them)
+        seg = b.segments_alloc(n, plist[0].n_adapters, dev)
 
         def step():
+            b.lora_segments_build(ids, plist[0].n_adapters, seg=seg)
             for pr, h, ws in zip(projs, hs, wss):
-                b.lora_layer_apply(h, pr["p"].x, pr["Wt"], ids, w_layout=b.LORA_W_OUT_IN, y=pr["y"], ws=ws)
+                b.lora_layer_apply(h, pr["p"].x, pr["Wt"], ids, w_layout=b.LORA_W_OUT_IN, seg=seg, y=pr["y"],
+                                   ws=ws)
 
         def base_step():
             for pr, h in zip(projs, hs):
