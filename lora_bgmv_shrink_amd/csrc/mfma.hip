@@ -798,8 +798,8 @@ __device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev&
 }
 
 // The LoRA expand rides on the same K loop: after the d_in/BK blocks of
-// x W come, for every distinct adapter u among the tile's rows (ascending
-// id), ceil(r_u / KH) blocks whose A side is t_ext (s_u * t split into bf16
+// x W come, for every distinct adapter u among the tile's rows (in the
+// order they first appear down the rows), ceil(r_u / KH) blocks whose A side is t_ext (s_u * t split into bf16
 // hi | lo halves, written by the shrink; rows of other adapters masked to 0)
 // and whose B side is B_u[j][n0:n0+BN] (each rank row twice for bf16, to
 // meet the hi and the lo half).  y is rounded once at the end.
@@ -812,9 +812,9 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
     __shared__ int sRowA[C::BM];
     __shared__ int sRowB[OUT_IN ? C::BN : 1];
-    __shared__ int sId[C::BM];
+    __shared__ __attribute__((aligned(16))) int sId[C::BM];
     __shared__ int sExt[2 * C::BM];   // (u << 1) | block, in order
-    __shared__ int sNext;
+    __shared__ int sWaveSum[(C::BM + 63) / 64];
     __shared__ int sNExt;
     __shared__ int sRuns;
     __shared__ int sValid;
@@ -859,7 +859,7 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
         }
         sRowA[tid] = src;
         sId[tid] = id;
-        if (g.t) {
+        if (g.t || g.t_ext) {
             RowRec rec{0, 0, 0.f};
             if (id != INT_MAX) {
                 rec.b_off = P.b_off[id];
@@ -903,26 +903,36 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
         gather = !EXT || !g.t_ext || (sRuns * per_adapter > 2 && 2 * sRuns >= sValid);
     }
 
-    // K-extension blocks: distinct adapters of the tile in ascending order
+    // K-extension blocks: one set per distinct adapter of the tile, in the
+    // order in which the adapters first appear down its rows.  The first row
+    // of each run of one id looks back for an earlier run of that id; a run
+    // that finds none brings its adapter's blocks, placed by a prefix sum
+    // over the rows.
     if (EXT && g.t_ext && !gather) {
-        int prev = -1;
-        for (;;) {
-            if (tid == 0) sNext = INT_MAX;
-            __syncthreads();
-            for (int m = tid; m < C::BM; m += C::NT) {
-                const int v = sId[m];
-                if (v > prev && v != INT_MAX) atomicMin(&sNext, v);
+        const int v = tid < C::BM ? sId[tid] : INT_MAX;
+        int nb = 0;
+        if (v != INT_MAX && (tid == 0 || sId[tid - 1] != v)) {
+            bool seen = false;
+            for (int k = 0; k < tid; k += 4) {
+                const int4 q = *(const int4*)(sId + k);
+                seen |= (q.x == v) | (k + 1 < tid && q.y == v) | (k + 2 < tid && q.z == v) |
+                        (k + 3 < tid && q.w == v);
             }
-            __syncthreads();
-            const int u = sNext;
-            if (u == INT_MAX) break;
-            if (tid == 0) {
-                const int nb = (P.ranks[u] + C::KH - 1) / C::KH;
-                for (int e = 0; e < nb; ++e) sExt[sNExt + e] = (u << 1) | e;
-                sNExt += nb;
-            }
-            prev = u;
+            if (!seen) nb = (sRec[tid].rank + C::KH - 1) / C::KH;
         }
+        // exclusive prefix sum of nb over the tile's rows
+        int incl = nb;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += o;
+        }
+        if (lane == 63 && wave < (C::BM + 63) / 64) sWaveSum[wave] = incl;
+        __syncthreads();
+        int before = incl - nb;
+        for (int w = 0; w < wave && w < (C::BM + 63) / 64; ++w) before += sWaveSum[w];
+        for (int e = 0; e < nb; ++e) sExt[before + e] = (v << 1) | e;
+        if (tid == C::BM - 1) sNExt = before + nb;
         __syncthreads();
     }
     const int nk = (K + C::BK - 1) / C::BK;
