@@ -268,6 +268,27 @@ def test_permutation_and_determinism():
     assert_close(ys[b.LORA_MODE_BGMV], ys[b.LORA_MODE_SGMV].cpu().double().numpy(), TOL[w.dtype], "BGMV vs SGMV")
 
 
+def test_layer_with_prebuilt_segments():
+    """A segments descriptor built once for the batch and handed to the layer
+    gives the same bits as the layer building its own."""
+    say("layer with a prebuilt segments descriptor")
+    b = binding()
+    for name in ("bf16_ragged", "bf16_r64_prefill", "f32_uniform"):
+        w, o = _oracle(name)
+        p = w.projections[0]
+        pool = pool_of(p.pool)
+        ids = ids_dev(w)
+        seg = b.lora_segments_build(ids, p.pool.n_adapters)
+        for lay in (b.LORA_W_OUT_IN, b.LORA_W_IN_OUT):
+            Ws = w_stored(p.W, lay)
+            y0 = b.lora_layer_apply(pool, p.x, Ws, ids, w_layout=lay, mode=b.LORA_MODE_SGMV, y_dtype=torch.float32)
+            y1 = b.lora_layer_apply(pool, p.x, Ws, ids, w_layout=lay, seg=seg, mode=b.LORA_MODE_SGMV,
+                                    y_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(y0, y1), f"{name} layout {lay}: prebuilt segments change the result"
+            assert_close(y1, o["y"], TOL[w.dtype], f"{name} layout {lay}")
+
+
 def test_base_only_rows_and_all_base():
     say("properties: base-only rows equal the all-base product")
     b = binding()
