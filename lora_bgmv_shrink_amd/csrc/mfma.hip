@@ -723,7 +723,6 @@ __device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev&
     static_assert(C::WTN % VE == 0 && 64 % LPR == 0 && (C::BLK % RPI == 0 || RPI % C::BLK == 0),
                   "epilogue lane map");
     static_assert(C::WM * C::WN * C::BLK * LDW * 4 <= 2 * C::STAGE * (int)sizeof(T), "epilogue staging");
-    float* sw = sw_all + wave * C::BLK * LDW;
     const int N = P.d_out;
     const int lr = lane / LPR;
     const int cc = (lane % LPR) * VE;
@@ -733,74 +732,167 @@ __device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev&
     const bool vec_y = ((g.ldy * (int64_t)sizeof(TY)) & 15) == 0;
     TY* Y = (TY*)g.y;
     const int lc = lane % C::BLK;
+
+    if constexpr (PASSES == 1 && RC == 16) {
+        // rank rows [j0, j0 + RC) of one row piece: B pieces and t values requested
+        auto request = [&](uint4 (&bv)[RC], float (&tv)[RC], const T* Bu, const float* trow, int r, int j0)
+            __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
+            for (int q = 0; q < RC; ++q) {
+                const int jj = j0 + q;
+                const T* bj = Bu + (int64_t)jj * N;
+                tv[q] = (jj < r) ? trow[jj] : 0.f;
+                if (jj < r && full && P.vec_b) {
+                    bv[q] = *(const uint4*)bj;
+                } else {
+                    union { uint4 u; T e[VE]; } w;
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+                    for (int e = 0; e < VE; ++e) w.e[e] = (jj < r && e < valid_c) ? bj[e] : (T)0;
+                    bv[q] = w.u;
+                }
+            }
+        };
+        auto accumulate = [&](float (&ex)[VE], const uint4 (&bv)[RC], const float (&tv)[RC])
+            __attribute__((always_inline)) {
 #pragma unroll
-            for (int q = 0; q < C::M::NACC; ++q) sw[C::M::row(lane, q) * LDW + j * C::BLK + lc] = acc.v[i][j][q];
-        __syncthreads();
-#pragma unroll 1
-        for (int it = 0; it < PASSES; ++it) {
-            const int rl = it * RPI + lr;
-            const int tr = wm * C::WTM + i * C::BLK + rl;   // row within the tile
-            const int row = (rl < C::BLK) ? sRow[tr] : -1;    // its row of t and y
-            if (row < 0 || valid_c <= 0) continue;
-            float v[VE];
+            for (int q = 0; q < RC; ++q) {
+                union { uint4 u; T e[VE]; } w;
+                w.u = bv[q];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) ex[e] += tv[q] * to_f32(w.e[e]);
+            }
+        };
+        auto load_staged = [&](float (&v)[VE], const float* src) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < VE; e += 4) {
-                const float4 b4 = *(const float4*)(sw + rl * LDW + cc + e);
+                const float4 b4 = *(const float4*)(src + e);
                 v[e] = b4.x;
                 v[e + 1] = b4.y;
                 v[e + 2] = b4.z;
                 v[e + 3] = b4.w;
             }
-            const RowRec rec = sRec[tr];
-            if (rec.rank > 0) {
-                const int r = rec.rank;
-                const T* Bu = (const T*)P.B + rec.b_off + col;
-                const float* trow = g.t + (int64_t)row * g.ldt;
-                float ex[VE];
+        };
+
+        {
+            // Each lane's FM row pieces are known before the accumulators are
+            // staged, so the first RC rank rows of all of them are requested in
+            // one round, then the whole wave tile is staged.
+            static_assert(C::WM * C::WN * C::WTM * LDW * 4 <= 2 * C::STAGE * (int)sizeof(T), "wave tile staging");
+            float* sw = sw_all + wave * C::WTM * LDW;
+            int rowp[C::FM];
+            RowRec recp[C::FM];
+            uint4 bv[C::FM][RC];
+            float tv[C::FM][RC];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) {
+                const int tr = wm * C::WTM + i * C::BLK + lr;
+                rowp[i] = (lr < C::BLK && valid_c > 0) ? sRow[tr] : -1;
+                recp[i] = rowp[i] >= 0 ? sRec[tr] : RowRec{0, 0, 0.f};
+                request(bv[i], tv[i], (const T*)P.B + recp[i].b_off + col,
+                        g.t + (int64_t)(rowp[i] >= 0 ? rowp[i] : 0) * g.ldt, recp[i].rank, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < C::M::NACC; ++q)
+                        sw[(i * C::BLK + C::M::row(lane, q)) * LDW + j * C::BLK + lc] = acc.v[i][j][q];
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) {
+                if (rowp[i] < 0) continue;
+                float v[VE], ex[VE];
+                load_staged(v, sw + (i * C::BLK + lr) * LDW + cc);
 #pragma unroll
                 for (int e = 0; e < VE; ++e) ex[e] = 0.f;
-                for (int j0 = 0; j0 < r; j0 += RC) {
-                    uint4 bv[RC];
-                    float tv[RC];
+                accumulate(ex, bv[i], tv[i]);
+                const int r = recp[i].rank;
+                const T* Bu = (const T*)P.B + recp[i].b_off + col;
+                const float* trow = g.t + (int64_t)rowp[i] * g.ldt;
+                for (int j0 = RC; j0 < r; j0 += RC) {
+                    uint4 bw[RC];
+                    float tw[RC];
+                    request(bw, tw, Bu, trow, r, j0);
+                    accumulate(ex, bw, tw);
+                }
 #pragma unroll
-                    for (int q = 0; q < RC; ++q) {
-                        const int jj = j0 + q;
-                        const T* bj = Bu + (int64_t)jj * N;
-                        tv[q] = (jj < r) ? trow[jj] : 0.f;
-                        if (jj < r && full && P.vec_b) {
-                            bv[q] = *(const uint4*)bj;
-                        } else {
+                for (int e = 0; e < VE; ++e) v[e] += recp[i].scale * ex[e];
+                store_row_piece<TY, VE>(Y + (int64_t)rowp[i] * g.ldy + col, v, valid_c, vec_y);
+            }
+        }
+    } else {
+        float* sw = sw_all + wave * C::BLK * LDW;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int q = 0; q < C::M::NACC; ++q) sw[C::M::row(lane, q) * LDW + j * C::BLK + lc] = acc.v[i][j][q];
+            __syncthreads();
+#pragma unroll 1
+            for (int it = 0; it < PASSES; ++it) {
+                const int rl = it * RPI + lr;
+                const int tr = wm * C::WTM + i * C::BLK + rl;   // row within the tile
+                const int row = (rl < C::BLK) ? sRow[tr] : -1;    // its row of t and y
+                if (row < 0 || valid_c <= 0) continue;
+                float v[VE];
+#pragma unroll
+                for (int e = 0; e < VE; e += 4) {
+                    const float4 b4 = *(const float4*)(sw + rl * LDW + cc + e);
+                    v[e] = b4.x;
+                    v[e + 1] = b4.y;
+                    v[e + 2] = b4.z;
+                    v[e + 3] = b4.w;
+                }
+                const RowRec rec = sRec[tr];
+                if (rec.rank > 0) {
+                    const int r = rec.rank;
+                    const T* Bu = (const T*)P.B + rec.b_off + col;
+                    const float* trow = g.t + (int64_t)row * g.ldt;
+                    float ex[VE];
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) ex[e] = 0.f;
+                    for (int j0 = 0; j0 < r; j0 += RC) {
+                        uint4 bv[RC];
+                        float tv[RC];
+#pragma unroll
+                        for (int q = 0; q < RC; ++q) {
+                            const int jj = j0 + q;
+                            const T* bj = Bu + (int64_t)jj * N;
+                            tv[q] = (jj < r) ? trow[jj] : 0.f;
+                            if (jj < r && full && P.vec_b) {
+                                bv[q] = *(const uint4*)bj;
+                            } else {
+                                union { uint4 u; T e[VE]; } w;
+#pragma unroll
+                                for (int e = 0; e < VE; ++e) w.e[e] = (jj < r && e < valid_c) ? bj[e] : (T)0;
+                                bv[q] = w.u;
+                            }
+                        }
+#pragma unroll
+                        for (int q = 0; q < RC; ++q) {
                             union { uint4 u; T e[VE]; } w;
+                            w.u = bv[q];
 #pragma unroll
-                            for (int e = 0; e < VE; ++e) w.e[e] = (jj < r && e < valid_c) ? bj[e] : (T)0;
-                            bv[q] = w.u;
+                            for (int e = 0; e < VE; ++e) ex[e] += tv[q] * to_f32(w.e[e]);
                         }
                     }
 #pragma unroll
-                    for (int q = 0; q < RC; ++q) {
-                        union { uint4 u; T e[VE]; } w;
-                        w.u = bv[q];
-#pragma unroll
-                        for (int e = 0; e < VE; ++e) ex[e] += tv[q] * to_f32(w.e[e]);
-                    }
+                    for (int e = 0; e < VE; ++e) v[e] += rec.scale * ex[e];
                 }
-#pragma unroll
-                for (int e = 0; e < VE; ++e) v[e] += rec.scale * ex[e];
+                store_row_piece<TY, VE>(Y + (int64_t)row * g.ldy + col, v, valid_c, vec_y);
             }
-            store_row_piece<TY, VE>(Y + (int64_t)row * g.ldy + col, v, valid_c, vec_y);
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
 // The LoRA expand rides on the same K loop: after the d_in/BK blocks of
 // x W come, for every distinct adapter u among the tile's rows (in the
-// order they first appear down the rows), ceil(r_u / KH) blocks whose A side is t_ext (s_u * t split into bf16
-// hi | lo halves, written by the shrink; rows of other adapters masked to 0)
+// order they first appear down the rows), ceil(r_u / KH) blocks whose A
+// side is t_ext (s_u * t split into bf16 hi | lo halves, written by the
+// shrink; rows of other adapters masked to 0)
 // and whose B side is B_u[j][n0:n0+BN] (each rank row twice for bf16, to
 // meet the hi and the lo half).  y is rounded once at the end.
 template <class C, typename TY, bool OUT_IN>
