@@ -48,6 +48,8 @@ def _bind(lib):
     lib.oracle_count_bad_ids.restype = i64
     lib.oracle_count_bad_ids.argtypes = [p, i64, i32]
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_merge.restype = ctypes.c_int
+    lib.oracle_merge.argtypes = [i64, i64, p, i32, i32, p, p, p, p, p, p, ctypes.c_double, ctypes.c_int]
     return lib
 
 
@@ -145,6 +147,22 @@ def layer(x, W, ids, pool: OraclePool, rows: Optional[Sequence[int]] = None,
     if y is not None:
         out["y"] = y
     out["bad"] = int(bad)
+    return out
+
+
+def merge(W, pool: OraclePool, adapter: int, sign: float = 1.0, threads: int = 0, lib=None) -> np.ndarray:
+    """``W + sign * s_a * A_a B_a`` in fp64 for ``W`` [d_in, d_out] (a new
+    array; ``W`` is not modified).  Raises for an adapter outside the pool."""
+    lib = lib or load()
+    out = np.array(_c(W, np.float64), dtype=np.float64, copy=True)
+    assert out.shape == (pool.d_in, pool.d_out)
+    rc = lib.oracle_merge(pool.d_in, pool.d_out, _ptr(out), int(adapter), pool.n_adapters,
+                          _ptr(_c(pool.ranks, np.int32)), _ptr(_c(pool.a_off, np.int64)),
+                          _ptr(_c(pool.b_off, np.int64)), _ptr(_c(pool.A, np.float64)),
+                          _ptr(_c(pool.B, np.float64)), _ptr(_c(pool.scales, np.float64)),
+                          float(sign), int(threads))
+    if rc != 0:
+        raise ValueError(f"adapter {adapter} outside [0, {pool.n_adapters})")
     return out
 
 

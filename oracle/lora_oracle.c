@@ -176,6 +176,44 @@ int64_t oracle_layer(int64_t n_rows, int64_t d_in, int64_t d_out,
     return bad;
 }
 
+/*
+ * Merged weights of one adapter ("Serving many LoRA adapters",
+ * blog.ecitis.org, section "Merge or keep separate": the adapter folded into
+ * the base weight, in this file's row-vector convention):
+ *
+ *   W[k][c] += sign * s_a * sum_j A_a[k][j] * B_a[j][c]      W [d_in, d_out]
+ *
+ * sign = +1 merges the adapter, -1 takes it back out.  W is updated in
+ * place; each element's sum runs over j = 0 .. r_a-1 in order and is scaled
+ * and added once.  Returns 1 (W untouched) for an adapter outside
+ * [0, n_adapters), else 0.  ``n_threads`` <= 0 keeps the OpenMP default.
+ */
+int oracle_merge(int64_t d_in, int64_t d_out, double* W, int32_t adapter, int32_t n_adapters,
+                 const int32_t* ranks, const int64_t* a_off, const int64_t* b_off,
+                 const double* A, const double* B, const double* scales, double sign, int n_threads)
+{
+    if (!id_valid(adapter, n_adapters)) return 1;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    const int32_t r = ranks[adapter];
+    const double* Aa = A + a_off[adapter];
+    const double* Ba = B + b_off[adapter];
+    const double s = sign * scales[adapter];
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < d_in; ++k) {
+        const double* Ak = Aa + k * (int64_t)r;   /* row k of A_a */
+        for (int64_t c = 0; c < d_out; ++c) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < r; ++j) acc += Ak[j] * Ba[c + (int64_t)j * d_out];
+            W[k * d_out + c] += s * acc;
+        }
+    }
+    return 0;
+}
+
 /* Threads an OpenMP parallel region would use (1 without OpenMP). */
 int oracle_max_threads(void)
 {

@@ -37,6 +37,13 @@ MUTATIONS = [
     ("segments_invalid_dropped", "int32_t key = id_valid(ids[i], n_adapters) ? ids[i] : -1;",
      "int32_t key = ids[i];"),
     ("shrink_uses_scale", "ti[j] = acc;\n", "ti[j] = scales[a] * acc;\n"),
+    ("merge_drop_scale", "W[k * d_out + c] += s * acc;", "W[k * d_out + c] += acc;"),
+    ("merge_overwrites", "W[k * d_out + c] += s * acc;", "W[k * d_out + c] = s * acc;"),
+    ("merge_sign_ignored", "const double s = sign * scales[adapter];", "const double s = scales[adapter];"),
+    ("merge_A_transposed", "acc += Ak[j] *", "acc += Aa[(int64_t)j * d_in + k] *"),
+    ("merge_B_transposed", "Ba[c + (int64_t)j * d_out]", "Ba[c * r + j]"),
+    ("merge_rank_off_by_one", "for (int32_t j = 0; j < r; ++j) acc += Ak[j]",
+     "for (int32_t j = 0; j + 1 < r; ++j) acc += Ak[j]"),
 ]
 
 

@@ -297,6 +297,55 @@ def pin_invalid_ids(lib):
         assert np.all(o["t"][i] == 0)
 
 
+def _merge_case(layout):
+    ranks = 12 if layout == wl.UNIFORM else [3, 16, 8, 1, 24, 5]
+    w = wl.small_batch(seed=11, n_rows=24, d_in=40, d_out=36, n_adapters=6, ranks=ranks, layout=layout,
+                       dtype=torch.float64, frac_base=0.0, scale=[2.0, 0.5, -1.0, 3.0, 1.0, 0.25])
+    p = w.projections[0]
+    op, _ = oracle_pool(p.pool)
+    return w, p, op
+
+
+def pin_merge_serves_the_adapter(lib):
+    """[P4 Merge or keep separate] the merged weight serves the adapter's
+    requests as a plain product: x (W + s A_a B_a) equals the layer with
+    every row on adapter a."""
+    for layout in (wl.UNIFORM, wl.RAGGED):
+        w, p, op = _merge_case(layout)
+        x, W = f64(p.x), f64(p.W)
+        for a in range(op.n_adapters):
+            Wm = oracle.merge(W, op, a, lib=lib)
+            ids = np.full(x.shape[0], a, np.int32)
+            o = oracle.layer(x, W, ids, op, want=("y",), lib=lib)
+            _close(x @ Wm, o["y"], 1e-12, f"merged adapter {a} ({layout})")
+
+
+def pin_merge_then_unmerge(lib):
+    """[P4 Merge or keep separate] taking the adapter back out (sign -1)
+    restores the base weight; merging twice adds the term twice."""
+    w, p, op = _merge_case(wl.RAGGED)
+    W = f64(p.W)
+    for a in (0, 3, 5):
+        Wm = oracle.merge(W, op, a, 1.0, lib=lib)
+        _close(oracle.merge(Wm, op, a, -1.0, lib=lib), W, 1e-12, f"unmerge adapter {a}")
+        _close(oracle.merge(Wm, op, a, 1.0, lib=lib) - W, 2.0 * (Wm - W), 1e-12, f"merge twice {a}")
+    with pytest.raises(ValueError):
+        oracle.merge(W, op, op.n_adapters, lib=lib)
+
+
+def pin_merge_rank_one_outer_product(lib):
+    """Closed form: a rank-1 adapter adds s * outer(A[:, 0], B[0, :])."""
+    rng = np.random.default_rng(7)
+    d_in, d_out = 9, 7
+    A = rng.standard_normal((2, d_in, 1))
+    B = rng.standard_normal((2, 1, d_out))
+    op = oracle.OraclePool.uniform(A, B, [1.5, -0.75])
+    W = rng.standard_normal((d_in, d_out))
+    for a, s in ((0, 1.5), (1, -0.75)):
+        _close(oracle.merge(W, op, a, lib=lib), W + s * np.outer(A[a, :, 0], B[a, 0, :]), 1e-14,
+               f"rank-1 merge {a}")
+
+
 def pin_empty_batch(lib):
     """Zero rows: nothing computed, no error."""
     _, p, op = _tiny()
@@ -310,7 +359,8 @@ PINS = [pin_tiny_segments_golden, pin_walkthrough_segments_golden, pin_segments_
         pin_page_script_agreement, pin_merged_weights, pin_additivity_base_only,
         pin_einsum_gather_formulation, pin_permutation_equivariance, pin_walkthrough_shared_adapter,
         pin_special_cases_plain_gemm, pin_linearity_in_scale, pin_ragged_equals_padded,
-        pin_invalid_ids, pin_empty_batch]
+        pin_invalid_ids, pin_empty_batch, pin_merge_serves_the_adapter, pin_merge_then_unmerge,
+        pin_merge_rank_one_outer_product]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
