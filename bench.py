@@ -394,6 +394,39 @@ def cpu_baseline(w, seconds):
                        f"x{n_done} passes, {el:.1f} s, fp64")
 
 
+def bench_merge(torch, args):
+    """lora_merge_adapter (W += s A_a B_a in place) on 8B and 70B q_proj
+    shapes: merges then unmerges over 4 weight replicas (more than the
+    Infinity Cache holds), captured in a graph; HBM GB/s of the algorithmic
+    bytes (W read and written once, A_a and B_a read once)."""
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for label, d, r in (("q_proj_8b_r16", 4096, 16), ("q_proj_70b_r64", 8192, 64)):
+        g = wl._gen(dev, 7000 + d + r)
+        pool_w = wl.make_uniform_pool(g, dev, torch.bfloat16, 8, d, d, r)
+        h = make_pool(b, pool_w)
+        Ws = [wl._randn(g, (d, d), wl.W_DIV, torch.bfloat16, dev) for _ in range(4)]
+
+        def step():
+            for Wt in Ws:
+                b.lora_merge_adapter(h, Wt, 3, w_layout=b.LORA_W_OUT_IN, sign=1.0)
+            for Wt in Ws:
+                b.lora_merge_adapter(h, Wt, 3, w_layout=b.LORA_W_OUT_IN, sign=-1.0)
+
+        gr = capture(torch, step)
+        sec = time_graph(torch, gr, max(2, args.extra_steps)) / (2 * len(Ws))
+        nbytes = 2 * d * d * 2 + r * (d + d) * 2
+        out[label] = dict(d_in=d, d_out=d, rank=r, us_per_merge=round(sec * 1e6, 2),
+                          GBps=round(nbytes / sec / 1e9, 1), frac_hbm=round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                          bytes_per_merge=nbytes)
+        del Ws, gr
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -418,6 +451,8 @@ def main():
         log(f"bench: workload {name} ...")
         extra[name] = bench_multi(torch, args, name)
         torch.cuda.empty_cache()
+    log("bench: merge kernel ...")
+    merge = bench_merge(torch, args)
     cpu = None
     if not args.no_cpu:
         log("bench: cpu baseline (oracle) ...")
@@ -448,6 +483,7 @@ def main():
         "adapter_term": dec["adapter_term"],
         "gpu_step_us": round(dec["gpu_step_s"] * 1e6, 3),
         "workloads": extra,
+        "merge": merge,
     }
     if cpu:
         line["gpu_over_cpu"] = round(line["value"] / cpu["value"], 1)

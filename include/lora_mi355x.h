@@ -252,6 +252,27 @@ lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx
                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Merged weights                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Fold adapter `adapter` into a base weight, in place:
+ *   W += sign * s_a * A_a B_a
+ * ("Serving many LoRA adapters" (blog.ecitis.org), section "Merge or keep
+ * separate": a replica with the adapter merged serves its requests as plain
+ * base-model GEMMs; sign = -1 takes the adapter back out, other values scale
+ * the term.)
+ *   W: device, the pool's dtype, caller-owned; layout per w_layout
+ *      ([d_in, d_out] or [d_out, d_in]) with leading dimension ldw.
+ *   Each element is read once, updated in fp32 and rounded once, so for a
+ *   bf16 W a merge followed by an unmerge restores W only to within bf16
+ *   rounding of each step.
+ *   Errors: LORA_E_ID_RANGE for an adapter outside [0, n_adapters);
+ *   LORA_E_INVALID for a null W, a non-finite sign or ldw below the row
+ *   length; LORA_E_UNSUPPORTED for a W or ldw that is not 16-byte aligned. */
+lora_status_t lora_merge_adapter(lora_pool_t pool, int32_t adapter, void* W, int64_t ldw,
+                                 lora_w_layout_t w_layout, float sign, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Decode layer in two launches                                            */
 /* ---------------------------------------------------------------------- */
 

@@ -36,7 +36,7 @@ EXPORTS = [
     "lora_bgmv_expand", "lora_sgmv_shrink", "lora_sgmv_expand", "lora_layer_workspace",
     "lora_layer_apply", "lora_base_gemm_expand_workspace", "lora_base_gemm_expand", "lora_decode_workspace",
     "lora_decode_stream",
-    "lora_decode_finish",
+    "lora_decode_finish", "lora_merge_adapter",
 ]
 
 
@@ -80,6 +80,7 @@ def _load():
         "lora_decode_workspace": (st, [p, i32, ctypes.c_int, p]),
         "lora_decode_stream": (st, [p, p, i64, p, i64, p, i32, ctypes.c_int, p, sz, p]),
         "lora_decode_finish": (st, [p, p, i32, ctypes.c_int, p, st, i64, p, sz, p]),
+        "lora_merge_adapter": (st, [p, i32, p, i64, st, ctypes.c_float, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -391,3 +392,13 @@ def lora_decode_finish(pool: Pool, ids: torch.Tensor, ws: torch.Tensor, y: torch
                                    _ld(y), _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(y.device))),
            "lora_decode_finish")
     return y
+
+
+def lora_merge_adapter(pool: Pool, W: torch.Tensor, adapter: int, w_layout: int = LORA_W_IN_OUT,
+                       sign: float = 1.0) -> torch.Tensor:
+    """W += sign * s_a * A_a B_a in place (W of the pool's dtype, stored per
+    ``w_layout``); returns W."""
+    assert W.is_cuda and W.dim() == 2 and W.stride(1) == 1
+    _check(_lib.lora_merge_adapter(pool.handle, int(adapter), _ptr(W), _ld(W), int(w_layout), float(sign),
+                                   ctypes.c_void_p(_stream(W.device))), "lora_merge_adapter")
+    return W

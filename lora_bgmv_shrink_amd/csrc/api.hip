@@ -2,6 +2,7 @@
 // dispatch.  The semantics of every entry point are documented in
 // include/lora_mi355x.h.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -519,6 +520,18 @@ lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx
         if (e != hipSuccess) return LORA_E_DEVICE;
     }
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
+}
+
+lora_status_t lora_merge_adapter(lora_pool_t pool, int32_t adapter, void* W, int64_t ldw,
+                                 lora_w_layout_t w_layout, float sign, hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || !W || !std::isfinite(sign)) return LORA_E_INVALID;
+    if (w_layout != LORA_W_IN_OUT && w_layout != LORA_W_OUT_IN) return LORA_E_INVALID;
+    const PoolDev& P = pool->dev;
+    if (adapter < 0 || adapter >= P.n_adapters) return LORA_E_ID_RANGE;
+    const int64_t w_min = (w_layout == LORA_W_IN_OUT) ? P.d_out : P.d_in;
+    if (ldw < w_min) return LORA_E_INVALID;
+    if (!al16(W) || !ld_ok(ldw, w_min, elem_bytes(pool->dtype))) return LORA_E_UNSUPPORTED;
+    return dev_status(launch_merge(P, pool->dtype, adapter, sign, W, ldw, w_layout == LORA_W_OUT_IN, stream));
 }
 
 lora_status_t lora_decode_workspace(lora_pool_t pool, int32_t n_rows, int with_lora, size_t* bytes) {

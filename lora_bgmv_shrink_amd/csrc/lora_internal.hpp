@@ -173,6 +173,10 @@ hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
+// W += sign * s_a * A_a B_a in place (W stored [d_out, d_in] when out_in).
+hipError_t launch_merge(const PoolDev& P, lora_dtype_t dt, int32_t adapter, float sign, void* W, int64_t ldw,
+                        bool out_in, hipStream_t stream);
+
 // Decode layer in two launches (bf16, n_rows <= 64, W stored [d_out, d_in]).
 constexpr int DS_LDS_BYTES = 84 * 1024;   // > half a CU: one stream workgroup per CU
 struct DecodePlan {

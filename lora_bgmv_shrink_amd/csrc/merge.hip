@@ -1,0 +1,264 @@
+// Folding one adapter into a base weight, in place:
+//
+//     W += sign * s_a * A_a B_a
+//
+// ("Serving many LoRA adapters" (blog.ecitis.org), section "Merge or keep
+// separate": a merged replica serves its adapter as plain base-model
+// inference; taking the adapter back out is the same update with the
+// opposite sign.)  W is the caller's weight in either storage layout:
+//   IN_OUT  W [d_in, d_out]:  element (k, c) at W[k * ldw + c]
+//   OUT_IN  W [d_out, d_in]:  element (k, c) at W[c * ldw + k]
+// Every element is read once, updated in fp32 and rounded once.
+//
+// The update streams W twice (read + write) and is HBM-bound, except that a
+// rank-64 update of a bf16 weight asks 32 flop per byte, more than the fp32
+// vector units deliver at HBM speed: the bf16 kernel forms A_a B_a on the
+// matrix cores (16x16x32 MFMA over the rank), the fp32 kernel (8 bytes per
+// element, 16 flop per byte at rank 64) on the vector units.
+#include <hip/hip_runtime.h>
+
+#include "lora_internal.hpp"
+
+namespace lora {
+namespace {
+
+// bf16 tile: 64 rows x 128 columns of W as stored, four waves of 32 x 64.
+constexpr int MG_ROWS = 64;
+constexpr int MG_COLS = 128;
+constexpr int MG_THREADS = 256;
+constexpr int MG_RPAD = 64 + 8;               // bf16 pitch of the staged B^T rows
+constexpr int MG_LDT = MG_COLS + 4;           // fp32 pitch of the staged product
+constexpr int MG_PIECES = MG_ROWS * MG_COLS / 8 / MG_THREADS;   // 16-byte W pieces per thread
+
+// One 16-byte W piece of the tile: stored row `row`, columns col .. col + 7.
+struct Piece {
+    int row, col;
+};
+__device__ __forceinline__ Piece piece_of(int tid, int p) {
+    const int idx = tid + p * MG_THREADS;
+    return Piece{idx / (MG_COLS / 8), (idx % (MG_COLS / 8)) * 8};
+}
+
+// Rows and columns below are those of W as stored.  The product term of
+// stored element (row, col) is sum_j L[row][j] * R[j][col] with
+//   IN_OUT: L = A_a (row = k), R = B_a (col = c)
+//   OUT_IN: L = B_a^T (row = c), R = A_a^T (col = k)
+// A_a rows are j-contiguous, so its MFMA operand comes straight from global
+// memory; B_a is staged into LDS as [c][j].
+//
+// A workgroup walks tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...; the
+// next tile's W pieces are requested before the current tile is worked on,
+// so W reads stay in flight across tiles.
+template <bool OUT_IN>
+__global__ __launch_bounds__(MG_THREADS) void k_merge_bf16(PoolDev P, int32_t adapter, float sign,
+                                                            bf16* __restrict__ W, int64_t ldw, int32_t tiles_c,
+                                                            int32_t n_tiles) {
+    constexpr int NC = OUT_IN ? MG_ROWS : MG_COLS;   // c values per tile
+    __shared__ __attribute__((aligned(16))) bf16 sBt[NC * MG_RPAD];
+    __shared__ __attribute__((aligned(16))) float sAcc[MG_ROWS * MG_LDT];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave >> 1;   // 32-row half of the tile
+    const int wc = wave & 1;    // 64-column half of the tile
+    const int n_rows = OUT_IN ? P.d_out : P.d_in;   // stored rows
+    const int n_cols = OUT_IN ? P.d_in : P.d_out;   // stored columns
+    const int r = uload(P.ranks, adapter);
+    const float s = sign * uload(P.scales, adapter);
+    const bf16* Aa = (const bf16*)P.A + uload(P.a_off, adapter);
+    const bf16* Ba = (const bf16*)P.B + uload(P.b_off, adapter);
+    const int d_in = P.d_in;
+    const int d_out = P.d_out;
+    const int steps = (r + 31) / 32;   // 32 ranks per MFMA step
+
+    auto load_w = [&](uint4 (&wv)[MG_PIECES], int t) __attribute__((always_inline)) {
+        const int row0 = (t / tiles_c) * MG_ROWS;
+        const int col0 = (t % tiles_c) * MG_COLS;
+#pragma unroll
+        for (int p = 0; p < MG_PIECES; ++p) {
+            const Piece q = piece_of(tid, p);
+            const int row = row0 + q.row, col = col0 + q.col;
+            const bf16* src = W + (int64_t)(row < n_rows ? row : 0) * ldw + col;
+            if (row < n_rows && col + 8 <= n_cols) {
+                wv[p] = *(const uint4*)src;
+            } else {
+                union { uint4 u; bf16 e[8]; } v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v.e[e] = (row < n_rows && col + e < n_cols) ? src[e] : (bf16)0;
+                wv[p] = v.u;
+            }
+        }
+    };
+
+    // L and R operands of 16x16x32 steps over j; lane l takes row/column
+    // l % 16 and ranks (l / 16) * 8 .. + 8
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const bool vec_a = P.vec_a && (r % 8) == 0;
+    auto a_frag = [&](int k, int j0) __attribute__((always_inline)) {
+        const int j = j0 + kq;
+        if (vec_a && k < d_in && j < r) return *(const bf16x8_t*)(Aa + (int64_t)k * r + j);
+        union { bf16x8_t v; bf16 e[8]; } t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t.e[e] = (k < d_in && j + e < r) ? Aa[(int64_t)k * r + j + e] : (bf16)0;
+        return t.v;
+    };
+    auto bt_frag = [&](int c_local, int j0) __attribute__((always_inline)) {
+        return *(const bf16x8_t*)(sBt + c_local * MG_RPAD + j0 + kq);
+    };
+
+    uint4 wv[MG_PIECES], wn[MG_PIECES];
+    int t = blockIdx.x;
+    if (t < n_tiles) load_w(wv, t);
+    for (; t < n_tiles; t += gridDim.x) {
+        const int row0 = (t / tiles_c) * MG_ROWS;
+        const int col0 = (t % tiles_c) * MG_COLS;
+        if (t + (int)gridDim.x < n_tiles) load_w(wn, t + gridDim.x);
+
+        // this tile's A_a operands (two rank steps at most)
+        bf16x8_t Ag[2][OUT_IN ? 4 : 2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if (st >= steps) break;
+#pragma unroll
+            for (int f = 0; f < (OUT_IN ? 4 : 2); ++f) {
+                const int k = OUT_IN ? col0 + wc * 64 + f * 16 + lr : row0 + wr * 32 + f * 16 + lr;
+                Ag[st][f] = a_frag(k, st * 32);
+            }
+        }
+        // B_a[j][c] for the tile's c range -> sBt[c - c0][j] (16-byte pieces
+        // of B rows, transposed on the way in); ranks past r are 0
+        const int c0 = OUT_IN ? row0 : col0;
+        constexpr int BPR = NC / 8;   // pieces per B row
+        for (int idx = tid; idx < 64 * BPR; idx += MG_THREADS) {
+            const int j = idx / BPR;
+            const int c = (idx - j * BPR) * 8;
+            union { uint4 u; bf16 e[8]; } v;
+            const bf16* src = Ba + (int64_t)j * d_out + c0 + c;
+            if (j < r && c0 + c + 8 <= d_out && P.vec_b) {
+                v.u = *(const uint4*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v.e[e] = (j < r && c0 + c + e < d_out) ? src[e] : (bf16)0;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sBt[(c + e) * MG_RPAD + j] = v.e[e];
+        }
+        __syncthreads();
+
+        f32x4_t acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) acc[i][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if (st >= steps) break;
+            const int j0 = st * 32;
+            bf16x8_t L[2], R[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) L[i] = OUT_IN ? bt_frag(wr * 32 + i * 16 + lr, j0) : Ag[st][i];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) R[jb] = OUT_IN ? Ag[st][jb] : bt_frag(wc * 64 + jb * 16 + lr, j0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+                    acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(L[i], R[jb], acc[i][jb], 0, 0, 0);
+        }
+
+        // the product into LDS in W's layout, then W + s * product per piece
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sAcc[(wr * 32 + i * 16 + (lane >> 4) * 4 + q) * MG_LDT + wc * 64 + jb * 16 + lr] = acc[i][jb][q];
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < MG_PIECES; ++p) {
+            const Piece q = piece_of(tid, p);
+            const int row = row0 + q.row, col = col0 + q.col;
+            if (row >= n_rows || col >= n_cols) continue;
+            const float* pr = sAcc + q.row * MG_LDT + q.col;
+            union { uint4 u; bf16 e[8]; } v;
+            v.u = wv[p];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v.e[e] = f32_to_bf16(to_f32(v.e[e]) + s * pr[e]);
+            bf16* dst = W + (int64_t)row * ldw + col;
+            if (col + 8 <= n_cols) {
+                *(uint4*)dst = v.u;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < n_cols) dst[e] = v.e[e];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < MG_PIECES; ++p) wv[p] = wn[p];
+        __syncthreads();   // sBt and sAcc are rewritten for the next tile
+    }
+}
+
+// fp32: each thread updates four consecutive stored elements, summing over
+// the rank in order.
+template <bool OUT_IN>
+__global__ __launch_bounds__(256) void k_merge_f32(PoolDev P, int32_t adapter, float sign, float* __restrict__ W,
+                                                   int64_t ldw) {
+    const int n_rows = OUT_IN ? P.d_out : P.d_in;
+    const int n_cols = OUT_IN ? P.d_in : P.d_out;
+    const int per_row = (n_cols + 3) / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n_rows * per_row) return;
+    const int row = (int)(idx / per_row);
+    const int col = (int)(idx - (int64_t)row * per_row) * 4;
+    const int r = uload(P.ranks, adapter);
+    const float s = sign * uload(P.scales, adapter);
+    const float* Aa = (const float*)P.A + uload(P.a_off, adapter);
+    const float* Ba = (const float*)P.B + uload(P.b_off, adapter);
+    const int d_out = P.d_out;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < r; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (col + e >= n_cols) break;
+            // IN_OUT: element (k = row, c = col + e); OUT_IN: (k = col + e, c = row)
+            const int k = OUT_IN ? col + e : row;
+            const int c = OUT_IN ? row : col + e;
+            acc[e] += Aa[(int64_t)k * r + j] * Ba[(int64_t)j * d_out + c];
+        }
+    }
+    float* w = W + (int64_t)row * ldw + col;
+    for (int e = 0; e < 4 && col + e < n_cols; ++e) w[e] += s * acc[e];
+}
+
+}  // namespace
+
+hipError_t launch_merge(const PoolDev& P, lora_dtype_t dt, int32_t adapter, float sign, void* W, int64_t ldw,
+                        bool out_in, hipStream_t stream) {
+    const int n_rows = out_in ? P.d_out : P.d_in;
+    const int n_cols = out_in ? P.d_in : P.d_out;
+    if (dt == LORA_BF16) {
+        // about three workgroups per CU (the LDS of one is ~52 KiB), each
+        // walking its share of the tiles
+        const int tiles_c = (int)ceil_div(n_cols, MG_COLS);
+        const int64_t n_tiles = ceil_div(n_rows, MG_ROWS) * tiles_c;
+        dim3 grid((unsigned)std::min<int64_t>(n_tiles, 768));
+        if (out_in)
+            hipLaunchKernelGGL(k_merge_bf16<true>, grid, dim3(MG_THREADS), 0, stream, P, adapter, sign, (bf16*)W,
+                               ldw, tiles_c, (int32_t)n_tiles);
+        else
+            hipLaunchKernelGGL(k_merge_bf16<false>, grid, dim3(MG_THREADS), 0, stream, P, adapter, sign, (bf16*)W,
+                               ldw, tiles_c, (int32_t)n_tiles);
+    } else {
+        dim3 grid((unsigned)ceil_div((int64_t)n_rows * ceil_div(n_cols, 4), 256));
+        if (out_in)
+            hipLaunchKernelGGL(k_merge_f32<true>, grid, dim3(256), 0, stream, P, adapter, sign, (float*)W, ldw);
+        else
+            hipLaunchKernelGGL(k_merge_f32<false>, grid, dim3(256), 0, stream, P, adapter, sign, (float*)W, ldw);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lora
