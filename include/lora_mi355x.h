@@ -56,7 +56,8 @@ typedef enum {
     LORA_E_UNSUPPORTED = 2, /* valid but not handled: alignment, rank > 64, ... */
     LORA_E_WORKSPACE = 3,   /* workspace missing or too small */
     LORA_E_ID_RANGE = 4,    /* reported by lora_pool_last_error only */
-    LORA_E_DEVICE = 5       /* a HIP runtime call failed */
+    LORA_E_DEVICE = 5,      /* a HIP runtime call failed */
+    LORA_E_NOT_RESIDENT = 6 /* lora_cache_map: an adapter is not resident yet */
 } lora_status_t;
 
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype_t;
@@ -296,6 +297,147 @@ lora_status_t lora_decode_stream(lora_pool_t pool, const void* x, int64_t ldx, c
 lora_status_t lora_decode_finish(lora_pool_t pool, const int32_t* ids, int32_t n_rows, int with_lora,
                                  void* y, lora_dtype_t y_dtype, int64_t ldy, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Adapter slot cache (paging)                                             */
+/* ---------------------------------------------------------------------- */
+
+/* GPU adapter slots treated as a cache over adapters kept in host memory
+ * ("Multi-LoRA batching and adapter paging", section "Adapter paging": a
+ * resident adapter is scheduled at once; a missing one evicts a cold
+ * adapter and is copied in; concurrent loads are capped; pinned adapters
+ * are never evicted.  "Serving many LoRA adapters" (blog.ecitis.org),
+ * section "Paging adapters": a fetch never blocks the step, a miss delays
+ * only that request's admission while the load runs, eviction is LRU over
+ * adapter ids, and an adapter with queued requests is not evicted.
+ * "Serving Many LoRA Adapters" (praveentn.live), section "S-LoRA": adapters
+ * outside the batch live in host DRAM and are prefetched over PCIe while
+ * the GPU computes.)
+ *
+ * An adapter is a set of n_parts projections (e.g. every projection of
+ * every layer), part p being A_p [d_in[p], r] and B_p [r, d_out[p]] with
+ * one rank r and one scale s for the whole adapter.  A slot holds a whole
+ * adapter; each part is exposed as a RAGGED lora_pool_t over the slot
+ * arena (lora_cache_pool) whose "adapter ids" are slot numbers, so the hot
+ * calls run unchanged on ids translated by lora_cache_map.  A slot has room
+ * for rank r_max; an adapter of rank r is computed at rank r.
+ *
+ * Host blob.  Each registered adapter is one contiguous host buffer in the
+ * compact layout of lora_cache_blob_layout (part p's A at a_off[p], its B
+ * at b_off[p], row-major, element offsets).  A load is one host-to-device
+ * copy of that blob plus one small table-update kernel, both on the cache's
+ * own copy stream (default priority).  The blob should be pinned
+ * (hipHostMalloc); it must stay valid and unchanged while registered.
+ *
+ * Not thread-safe: one thread drives a cache.  Destroying the cache waits
+ * for the device and frees the arena, the pools and the copy stream. */
+typedef struct lora_cache_s* lora_cache_t;
+
+typedef enum {
+    LORA_CACHE_RESIDENT = 0, /* loaded: lora_cache_map accepts it */
+    LORA_CACHE_LOADING = 1,  /* a copy is in flight (started now or earlier) */
+    LORA_CACHE_DEFERRED = 2  /* not resident and no load started: the load cap
+                                is reached or every slot is pinned, held or in use */
+} lora_cache_state_t;
+
+/* flags for lora_cache_create */
+#define LORA_CACHE_HOST_ONLY 1 /* policy only: no device memory and no HIP call;
+                                  loads complete only at lora_cache_poll or
+                                  lora_cache_wait (so a run of the policy depends
+                                  on the call sequence alone); no pools; blobs
+                                  may be NULL */
+#define LORA_CACHE_ANY_RANK 2  /* accept every rank 1..r_max (otherwise ranks must
+                                  be multiples of 16 bytes of elements that divide
+                                  512*16/elem, the ranks the streaming shrink takes) */
+
+typedef struct {
+    int64_t requests;          /* lora_cache_request calls */
+    int64_t hits;              /* ... that found the adapter resident */
+    int64_t pending;           /* ... that found its load still in flight */
+    int64_t loads_started;     /* ... that started a load (the misses served) */
+    int64_t deferred_load_cap; /* ... deferred: loads_in_flight == max */
+    int64_t deferred_no_slot;  /* ... deferred: no evictable slot */
+    int64_t loads_completed;
+    int64_t evictions;         /* loads that replaced a resident adapter */
+    int64_t bytes_loaded;      /* host-to-device bytes of started loads */
+    int64_t bytes_resident;    /* blob bytes of the adapters in slots */
+    int32_t n_slots;
+    int32_t slots_resident;    /* loaded */
+    int32_t slots_loading;     /* = loads in flight */
+    int32_t slots_bound;       /* mapped by a batch not yet released */
+} lora_cache_stats_t;
+
+/* Element offsets of each part inside an adapter's compact blob for rank r
+ * (host only).  a_off/b_off are [n_parts] (host out); every block starts on
+ * a 256-byte boundary.  *blob_elems is the blob length in elements. */
+lora_status_t lora_cache_blob_layout(lora_cache_t cache, int32_t rank, int64_t* a_off,
+                                     int64_t* b_off, int64_t* blob_elems);
+
+/* Create a cache of n_slots slots over adapters 0..n_adapters-1.
+ *   d_in/d_out (host, n_parts each) are the part shapes; 1 <= r_max <= 64;
+ *   1 <= max_loads_in_flight.  Allocates the slot arena (n_slots blobs of
+ *   rank r_max), the per-part pool tables and the copy stream (all freed by
+ *   lora_cache_destroy) unless flags has LORA_CACHE_HOST_ONLY. */
+lora_status_t lora_cache_create(lora_cache_t* out, lora_dtype_t dtype, int32_t n_parts,
+                                const int32_t* d_in, const int32_t* d_out, int32_t r_max,
+                                int32_t n_adapters, int32_t n_slots,
+                                int32_t max_loads_in_flight, int32_t flags);
+lora_status_t lora_cache_destroy(lora_cache_t cache);
+
+/* Register adapter `adapter` (host tier): rank, scale s = alpha/r, and the
+ * host blob.  Re-registering a resident, loading or bound adapter is
+ * LORA_E_INVALID.  Ranks outside [1, r_max] (or not taken, see
+ * LORA_CACHE_ANY_RANK) are LORA_E_UNSUPPORTED. */
+lora_status_t lora_cache_register(lora_cache_t cache, int32_t adapter, int32_t rank, float scale,
+                                  const void* blob);
+
+/* Pin (pinned != 0) or unpin an adapter: a pinned adapter is never evicted
+ * while resident.  Pinning does not load it. */
+lora_status_t lora_cache_pin(lora_cache_t cache, int32_t adapter, int32_t pinned);
+
+/* Add delta to the adapter's count of queued requests; an adapter with a
+ * positive count is not evicted.  A count below zero is LORA_E_INVALID. */
+lora_status_t lora_cache_hold(lora_cache_t cache, int32_t adapter, int32_t delta);
+
+/* Ask for an adapter (never blocks).  Resident: marks it recently used and
+ * returns RESIDENT.  Loading: LOADING.  Otherwise a load starts when fewer
+ * than max_loads_in_flight are in flight and a slot is free or evictable
+ * (the least recently used slot whose adapter is not pinned, held or bound;
+ * empty slots first, ties to the lowest slot): LOADING; else DEFERRED.
+ * Completed loads are noticed first (see lora_cache_poll). */
+lora_status_t lora_cache_request(lora_cache_t cache, int32_t adapter, lora_cache_state_t* state);
+
+/* Notice completed loads without waiting (HOST_ONLY: complete them all).
+ * lora_cache_request and lora_cache_map notice completed loads too, except
+ * in a HOST_ONLY cache.
+ * *n_completed (may be NULL) gets the number noticed by this call. */
+lora_status_t lora_cache_poll(lora_cache_t cache, int32_t* n_completed);
+
+/* Block until every load in flight has completed (a warm-up job's
+ * prefetch), then poll. */
+lora_status_t lora_cache_wait(lora_cache_t cache);
+
+/* Bind a batch: adapters[n] (host, -1 = base-only row) -> slots[n] (host out,
+ * -1 stays -1).  Every id >= 0 must be registered (else LORA_E_INVALID) and
+ * resident (else LORA_E_NOT_RESIDENT); on error nothing is bound.  Bound
+ * adapters are marked recently used and are not evicted until
+ * lora_cache_release; `stream` is made to wait for their loads.  Several
+ * maps may precede one release (e.g. one per part). */
+lora_status_t lora_cache_map(lora_cache_t cache, const int32_t* adapters, int32_t n,
+                             int32_t* slots, hipStream_t stream);
+
+/* End of the batch's use of its bound slots: records on `stream` (after the
+ * batch's launches) the point a later eviction of those slots waits for. */
+lora_status_t lora_cache_release(lora_cache_t cache, hipStream_t stream);
+
+/* The pool of part p (owned by the cache; lora_pool_destroy refuses it).
+ * NULL for a HOST_ONLY cache or p out of range. */
+lora_pool_t lora_cache_pool(lora_cache_t cache, int32_t part);
+
+/* Slot of an adapter, or -1 when it is neither resident nor loading. */
+int32_t lora_cache_slot_of(lora_cache_t cache, int32_t adapter);
+
+lora_status_t lora_cache_stats(lora_cache_t cache, lora_cache_stats_t* out);
 
 #ifdef __cplusplus
 }

@@ -22,11 +22,14 @@ import torch  # loads the HIP runtime the library binds to
 
 from .build import LIB_PATH
 
-LORA_OK, LORA_E_INVALID, LORA_E_UNSUPPORTED, LORA_E_WORKSPACE, LORA_E_ID_RANGE, LORA_E_DEVICE = range(6)
+(LORA_OK, LORA_E_INVALID, LORA_E_UNSUPPORTED, LORA_E_WORKSPACE, LORA_E_ID_RANGE, LORA_E_DEVICE,
+ LORA_E_NOT_RESIDENT) = range(7)
 LORA_F32, LORA_BF16 = 0, 1
 LORA_LAYOUT_UNIFORM, LORA_LAYOUT_RAGGED = 0, 1
 LORA_MODE_AUTO, LORA_MODE_BGMV, LORA_MODE_SGMV = 0, 1, 2
 LORA_W_IN_OUT, LORA_W_OUT_IN = 0, 1
+LORA_CACHE_RESIDENT, LORA_CACHE_LOADING, LORA_CACHE_DEFERRED = 0, 1, 2
+LORA_CACHE_HOST_ONLY, LORA_CACHE_ANY_RANK = 1, 2
 
 # Every symbol the C header declares.
 EXPORTS = [
@@ -37,6 +40,9 @@ EXPORTS = [
     "lora_layer_apply", "lora_base_gemm_expand_workspace", "lora_base_gemm_expand", "lora_decode_workspace",
     "lora_decode_stream",
     "lora_decode_finish", "lora_merge_adapter",
+    "lora_cache_blob_layout", "lora_cache_create", "lora_cache_destroy", "lora_cache_register",
+    "lora_cache_pin", "lora_cache_hold", "lora_cache_request", "lora_cache_poll", "lora_cache_wait",
+    "lora_cache_map", "lora_cache_release", "lora_cache_pool", "lora_cache_slot_of", "lora_cache_stats",
 ]
 
 
@@ -44,6 +50,13 @@ class LoraError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {_lib.lora_status_string(status).decode()}")
+
+
+class CacheStatsT(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int64) for k in (
+        "requests", "hits", "pending", "loads_started", "deferred_load_cap", "deferred_no_slot",
+        "loads_completed", "evictions", "bytes_loaded", "bytes_resident")] + \
+        [(k, ctypes.c_int32) for k in ("n_slots", "slots_resident", "slots_loading", "slots_bound")]
 
 
 class SegmentsT(ctypes.Structure):
@@ -81,6 +94,20 @@ def _load():
         "lora_decode_stream": (st, [p, p, i64, p, i64, p, i32, ctypes.c_int, p, sz, p]),
         "lora_decode_finish": (st, [p, p, i32, ctypes.c_int, p, st, i64, p, sz, p]),
         "lora_merge_adapter": (st, [p, i32, p, i64, st, ctypes.c_float, p]),
+        "lora_cache_blob_layout": (st, [p, i32, p, p, p]),
+        "lora_cache_create": (st, [p, st, i32, p, p, i32, i32, i32, i32, i32]),
+        "lora_cache_destroy": (st, [p]),
+        "lora_cache_register": (st, [p, i32, i32, ctypes.c_float, p]),
+        "lora_cache_pin": (st, [p, i32, i32]),
+        "lora_cache_hold": (st, [p, i32, i32]),
+        "lora_cache_request": (st, [p, i32, p]),
+        "lora_cache_poll": (st, [p, p]),
+        "lora_cache_wait": (st, [p]),
+        "lora_cache_map": (st, [p, p, i32, p, p]),
+        "lora_cache_release": (st, [p, p]),
+        "lora_cache_pool": (p, [p, i32]),
+        "lora_cache_slot_of": (i32, [p, i32]),
+        "lora_cache_stats": (st, [p, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -137,9 +164,10 @@ class Pool:
     r_max: int
     A: torch.Tensor
     B: torch.Tensor
+    owned: bool = True   # False for the pools of an adapter cache (the cache frees them)
 
     def destroy(self):
-        if self.handle:
+        if self.handle and self.owned:
             _check(_lib.lora_pool_destroy(self.handle), "lora_pool_destroy")
             self.handle = None
 
@@ -402,3 +430,129 @@ def lora_merge_adapter(pool: Pool, W: torch.Tensor, adapter: int, w_layout: int 
     _check(_lib.lora_merge_adapter(pool.handle, int(adapter), _ptr(W), _ld(W), int(w_layout), float(sign),
                                    ctypes.c_void_p(_stream(W.device))), "lora_merge_adapter")
     return W
+
+
+# --------------------------------------------------------------------------
+# Adapter slot cache
+# --------------------------------------------------------------------------
+
+class Cache:
+    """An adapter slot cache (lora_cache_*).  ``parts`` lists the (d_in,
+    d_out) of every projection an adapter carries.  ``register`` packs an
+    adapter's per-part A/B tensors into one pinned host blob in the layout
+    lora_cache_blob_layout gives and keeps it alive while the cache lives.
+    With ``host_only`` no device memory is used (policy only)."""
+
+    def __init__(self, dtype: torch.dtype, parts, r_max: int, n_adapters: int, n_slots: int,
+                 max_loads_in_flight: int, host_only: bool = False, any_rank: bool = False,
+                 device=None):
+        self.dtype = dtype
+        self.parts = [(int(a), int(b)) for a, b in parts]
+        self.r_max, self.n_adapters, self.n_slots = r_max, n_adapters, n_slots
+        self.host_only = host_only
+        self.device = torch.device(device) if device is not None else None
+        d_in = np.ascontiguousarray([a for a, _ in self.parts], np.int32)
+        d_out = np.ascontiguousarray([b for _, b in self.parts], np.int32)
+        flags = (LORA_CACHE_HOST_ONLY if host_only else 0) | (LORA_CACHE_ANY_RANK if any_rank else 0)
+        h = ctypes.c_void_p()
+        if host_only:
+            st = _lib.lora_cache_create(ctypes.byref(h), _dt(dtype), len(self.parts), d_in.ctypes.data,
+                                        d_out.ctypes.data, r_max, n_adapters, n_slots, max_loads_in_flight, flags)
+        else:
+            with torch.cuda.device(self.device):
+                st = _lib.lora_cache_create(ctypes.byref(h), _dt(dtype), len(self.parts), d_in.ctypes.data,
+                                            d_out.ctypes.data, r_max, n_adapters, n_slots, max_loads_in_flight,
+                                            flags)
+        _check(st, "lora_cache_create")
+        self.handle = h
+        self.blobs = {}
+        self._pools = {}
+
+    def blob_layout(self, rank: int):
+        n = len(self.parts)
+        a_off = np.zeros(n, np.int64)
+        b_off = np.zeros(n, np.int64)
+        total = ctypes.c_int64()
+        _check(_lib.lora_cache_blob_layout(self.handle, rank, a_off.ctypes.data, b_off.ctypes.data,
+                                           ctypes.byref(total)), "lora_cache_blob_layout")
+        return a_off, b_off, total.value
+
+    def register(self, adapter: int, rank: int, scale: float, A_parts=None, B_parts=None):
+        """A_parts[p]: [d_in_p, rank], B_parts[p]: [rank, d_out_p] (any device)."""
+        blob_ptr = None
+        if not self.host_only:
+            a_off, b_off, total = self.blob_layout(rank)
+            blob = torch.zeros(total, dtype=self.dtype, pin_memory=True)
+            for p, (di, do) in enumerate(self.parts):
+                Ap, Bp = A_parts[p], B_parts[p]
+                assert tuple(Ap.shape) == (di, rank) and tuple(Bp.shape) == (rank, do)
+                blob[a_off[p]:a_off[p] + di * rank].copy_(Ap.reshape(-1))
+                blob[b_off[p]:b_off[p] + rank * do].copy_(Bp.reshape(-1))
+            self.blobs[adapter] = blob
+            blob_ptr = _ptr(blob)
+        _check(_lib.lora_cache_register(self.handle, adapter, rank, float(scale), blob_ptr),
+               "lora_cache_register")
+
+    def pin(self, adapter: int, pinned: bool = True):
+        _check(_lib.lora_cache_pin(self.handle, adapter, int(bool(pinned))), "lora_cache_pin")
+
+    def hold(self, adapter: int, delta: int):
+        _check(_lib.lora_cache_hold(self.handle, adapter, int(delta)), "lora_cache_hold")
+
+    def request(self, adapter: int) -> int:
+        v = ctypes.c_int()
+        _check(_lib.lora_cache_request(self.handle, adapter, ctypes.byref(v)), "lora_cache_request")
+        return int(v.value)
+
+    def poll(self) -> int:
+        v = ctypes.c_int32()
+        _check(_lib.lora_cache_poll(self.handle, ctypes.byref(v)), "lora_cache_poll")
+        return int(v.value)
+
+    def wait(self):
+        _check(_lib.lora_cache_wait(self.handle), "lora_cache_wait")
+
+    def _stream(self):
+        return None if self.host_only else ctypes.c_void_p(_stream(self.device))
+
+    def map(self, adapters) -> np.ndarray:
+        """Host adapter ids -> host slot ids (raises LoraError with status
+        LORA_E_NOT_RESIDENT when one is not resident)."""
+        a = np.ascontiguousarray(adapters, np.int32)
+        out = np.zeros(max(a.size, 1), np.int32)
+        _check(_lib.lora_cache_map(self.handle, a.ctypes.data, a.size, out.ctypes.data, self._stream()),
+               "lora_cache_map")
+        return out[:a.size]
+
+    def release(self):
+        _check(_lib.lora_cache_release(self.handle, self._stream()), "lora_cache_release")
+
+    def pool(self, part: int) -> Pool:
+        if part not in self._pools:
+            h = _lib.lora_cache_pool(self.handle, part)
+            if not h:
+                raise LoraError(LORA_E_INVALID, "lora_cache_pool")
+            z = torch.empty(0, dtype=self.dtype, device=self.device)
+            di, do = self.parts[part]
+            self._pools[part] = Pool(ctypes.c_void_p(h), self.dtype, self.n_slots, di, do, self.r_max, z, z,
+                                     owned=False)
+        return self._pools[part]
+
+    def slot_of(self, adapter: int) -> int:
+        return int(_lib.lora_cache_slot_of(self.handle, adapter))
+
+    def stats(self) -> dict:
+        s = CacheStatsT()
+        _check(_lib.lora_cache_stats(self.handle, ctypes.byref(s)), "lora_cache_stats")
+        return {k: int(getattr(s, k)) for k, _ in CacheStatsT._fields_}
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            _check(_lib.lora_cache_destroy(self.handle), "lora_cache_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

@@ -7,16 +7,10 @@
 #include <vector>
 
 #include "lora_internal.hpp"
+#include "pool.hpp"
 
 using namespace lora;
 
-struct lora_pool_s {
-    PoolDev dev;
-    lora_layout_t layout;
-    lora_dtype_t dtype;
-    std::vector<int32_t> ranks;
-    void* tables;   // one device allocation: ranks, a_off, b_off, scales, err
-};
 
 namespace {
 
@@ -111,6 +105,7 @@ const char* lora_status_string(lora_status_t s) {
         case LORA_E_WORKSPACE: return "LORA_E_WORKSPACE: workspace missing or too small";
         case LORA_E_ID_RANGE: return "LORA_E_ID_RANGE: an adapter id was outside [-1, n_adapters)";
         case LORA_E_DEVICE: return "LORA_E_DEVICE: a HIP runtime call failed";
+        case LORA_E_NOT_RESIDENT: return "LORA_E_NOT_RESIDENT: an adapter of the batch is not resident";
     }
     return "unknown lora_status_t";
 }
@@ -207,6 +202,7 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
         return LORA_E_DEVICE;
     }
     lora_pool_s* p = new lora_pool_s;
+    p->owned_by_cache = false;
     p->layout = layout;
     p->dtype = dtype;
     p->ranks = rk;
@@ -232,6 +228,7 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
 
 lora_status_t lora_pool_destroy(lora_pool_t pool) {
     if (!pool) return LORA_OK;
+    if (pool->owned_by_cache) return LORA_E_INVALID;
     hipError_t e = hipDeviceSynchronize();
     hipError_t f = hipFree(pool->tables);
     delete pool;

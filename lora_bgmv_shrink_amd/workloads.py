@@ -29,7 +29,7 @@ made on ``cpu`` but is equally seeded.  Tests always hand the oracle the exact t
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 import torch
@@ -401,3 +401,41 @@ CONFIG_BUILDERS = {
     3: prefill_70b,
     4: mixed_rank_70b,
 }
+
+
+# --------------------------------------------------------------------------
+# Adapter sets for the slot cache (host tier)
+# --------------------------------------------------------------------------
+
+@dataclass
+class AdapterSet:
+    """Adapters of several projections each, kept on the host: adapter u has
+    rank ranks[u], scale scales[u] and, for part p, A[u][p] [d_in_p, r_u]
+    and B[u][p] [r_u, d_out_p]."""
+    parts: List[Tuple[int, int]]
+    ranks: np.ndarray
+    scales: np.ndarray
+    A: List[List[torch.Tensor]]
+    B: List[List[torch.Tensor]]
+
+
+def adapter_set(parts, ranks, scales, dtype=torch.bfloat16, seed=0, a_div=64.0, b_div=16.0) -> AdapterSet:
+    """Host (CPU) adapters with this module's value distributions: A ~
+    N(0,1)/a_div, B ~ N(0,1)/b_div, drawn per adapter from a generator
+    seeded ``1000*seed + u``."""
+    ranks = np.asarray(ranks, np.int32)
+    scales = np.asarray(scales, np.float32)
+    As, Bs = [], []
+    for u, r in enumerate(ranks):
+        g = _gen("cpu", 1000 * seed + u)
+        As.append([_randn(g, (di, int(r)), a_div, dtype, "cpu") for di, _ in parts])
+        Bs.append([_randn(g, (int(r), do), b_div, dtype, "cpu") for _, do in parts])
+    return AdapterSet([(int(a), int(b)) for a, b in parts], ranks, scales, As, Bs)
+
+
+def eight_b_parts(layers: int = 32):
+    """(d_in, d_out) of every projection of an 8B-shaped model, layer by
+    layer: q, k, v, o, gate, up, down."""
+    one = [(4096, 4096), (4096, 1024), (4096, 1024), (4096, 4096), (4096, 14336), (4096, 14336),
+           (14336, 4096)]
+    return one * layers

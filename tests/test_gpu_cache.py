@@ -1,0 +1,181 @@
+"""The adapter slot cache on the GPU, through the C ABI.
+
+Adapters live on the host; batches ask for them, the cache copies them into
+slots on its own stream, and the layer runs on the cache's per-part pools
+with slot ids.  The result must equal the fp64 oracle run with the original
+adapter ids on the adapters themselves, within |gpu - oracle| <= 2e-2 *
+max(1, |oracle|) (bf16 inputs, fp32 accumulation), through evictions and
+reloads, with every adapter's own rank and scale ("Serving many LoRA
+adapters" (blog.ecitis.org), section "Correctness across tenants": the
+scale travels with the adapter).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import TOL, assert_close, binding, requires_gpu, say
+from _marshal import f64
+from lora_bgmv_shrink_amd import workloads as wl
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+DEV = "cuda"
+
+
+def _oracle_pool(aset: wl.AdapterSet, part: int) -> oracle.OraclePool:
+    d_in, d_out = aset.parts[part]
+    n = len(aset.ranks)
+    a_off, b_off, As, Bs = [], [], [], []
+    pa = pb = 0
+    for u in range(n):
+        A = f64(aset.A[u][part]).reshape(-1)
+        B = f64(aset.B[u][part]).reshape(-1)
+        a_off.append(pa)
+        b_off.append(pb)
+        pa += A.size
+        pb += B.size
+        As.append(A)
+        Bs.append(B)
+    return oracle.OraclePool(n, d_in, d_out, int(aset.ranks.max()), aset.ranks.astype(np.int32),
+                             np.array(a_off, np.int64), np.array(b_off, np.int64), np.concatenate(As),
+                             np.concatenate(Bs), aset.scales.astype(np.float64))
+
+
+def _cache_for(aset: wl.AdapterSet, n_slots: int, max_loads: int):
+    b = binding()
+    c = b.Cache(torch.bfloat16, aset.parts, int(aset.ranks.max()), len(aset.ranks), n_slots, max_loads,
+                device=DEV)
+    for u in range(len(aset.ranks)):
+        c.register(u, int(aset.ranks[u]), float(aset.scales[u]), aset.A[u], aset.B[u])
+    return c
+
+
+def _make_resident(c, adapters):
+    b = binding()
+    for a in adapters:
+        for _ in range(50):
+            st = c.request(int(a))
+            if st == b.LORA_CACHE_RESIDENT:
+                break
+            c.wait()
+        else:
+            raise AssertionError(f"adapter {a} never became resident")
+
+
+def _batch(rng, n_adapters, n_rows, n_distinct, frac_base=0.1):
+    use = rng.choice(n_adapters, size=n_distinct, replace=False)
+    ids = use[rng.integers(0, n_distinct, size=n_rows)].astype(np.int32)
+    ids[rng.random(n_rows) < frac_base] = -1
+    return ids, sorted(set(int(a) for a in use))
+
+
+PARTS = [(512, 384), (384, 512)]
+
+
+@pytest.mark.parametrize("mode_name,n_rows", [("bgmv", 48), ("sgmv", 160)])
+def test_layer_through_cache_matches_oracle(mode_name, n_rows):
+    b = binding()
+    mode = b.LORA_MODE_BGMV if mode_name == "bgmv" else b.LORA_MODE_SGMV
+    n_adapters = 12
+    ranks = [8, 16, 32, 64] * 3
+    scales = np.linspace(0.5, 3.0, n_adapters).astype(np.float32)
+    aset = wl.adapter_set(PARTS, ranks, scales, seed=5)
+    c = _cache_for(aset, n_slots=5, max_loads=2)
+    ops = [_oracle_pool(aset, p) for p in range(len(PARTS))]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(11)
+    Ws = [(torch.randn(di, do, generator=g) / 16).to(torch.bfloat16) for di, do in PARTS]
+    W_dev = [W.t().contiguous().to(DEV) for W in Ws]   # stored [d_out, d_in]
+    rng = np.random.default_rng(3)
+    for step in range(6):
+        ids, used = _batch(rng, n_adapters, n_rows, 4)
+        say(f"cache step {step}: {mode_name}, {n_rows} rows, adapters {used}")
+        _make_resident(c, used)
+        slots = c.map(ids)
+        assert all((s == -1) == (a == -1) for s, a in zip(slots, ids))
+        ids_d = torch.as_tensor(slots, dtype=torch.int32, device=DEV)
+        ys, xs = [], []
+        for p, (di, do) in enumerate(PARTS):
+            x = (torch.randn(n_rows, di, generator=g)).to(torch.bfloat16)
+            xs.append(x)
+            ys.append(b.lora_layer_apply(c.pool(p), x.to(DEV), W_dev[p], ids_d, w_layout=b.LORA_W_OUT_IN,
+                                         mode=mode))
+        c.release()
+        torch.cuda.synchronize()
+        for p in range(len(PARTS)):
+            ref = oracle.layer(f64(xs[p]), f64(Ws[p]), ids, ops[p], want=("y",))["y"]
+            assert_close(ys[p], ref, TOL[torch.bfloat16], f"step {step} part {p}")
+    s = c.stats()
+    say(f"  cache stats: {s}")
+    assert s["evictions"] > 0 and s["hits"] > 0
+    assert s["loads_completed"] == s["loads_started"]
+    assert s["slots_resident"] <= 5 and s["slots_bound"] == 0
+    c.destroy()
+
+
+def test_eviction_copy_waits_for_the_batch_that_read_the_slot():
+    """Slots read by a batch are evicted right after its release while the
+    batch is still queued behind several milliseconds of other work: the
+    copies must not land before the batch has read the old adapters."""
+    b = binding()
+    parts = [(2048, 2048)]
+    aset = wl.adapter_set(parts, [64] * 4, [2.0, 1.5, -1.0, 0.75], seed=9)
+    c = _cache_for(aset, n_slots=2, max_loads=2)
+    op = _oracle_pool(aset, 0)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(12)
+    W = (torch.randn(2048, 2048, generator=g) / 64).to(torch.bfloat16)
+    Wd = W.t().contiguous().to(DEV)
+    x = torch.randn(1024, 2048, generator=g).to(torch.bfloat16)
+    ids = np.array([0, 1] * 512, np.int32)
+    _make_resident(c, [0, 1])
+    slots = c.map(ids)
+    busy = torch.randn(4096, 4096, device=DEV)
+    for _ in range(12):                      # keep the compute stream busy
+        busy = busy @ busy
+        busy = busy / busy.abs().max()
+    y = b.lora_layer_apply(c.pool(0), x.to(DEV), Wd, torch.as_tensor(slots, device=DEV), w_layout=b.LORA_W_OUT_IN,
+                           mode=b.LORA_MODE_SGMV)
+    c.release()
+    # both slots evicted at once: adapters 2 and 3 replace 0 and 1
+    assert c.request(2) == b.LORA_CACHE_LOADING
+    assert c.request(3) == b.LORA_CACHE_LOADING
+    assert c.slot_of(0) == -1 and c.slot_of(1) == -1
+    torch.cuda.synchronize()
+    ref = oracle.layer(f64(x), f64(W), ids, op, want=("y",))["y"]
+    assert_close(y, ref, TOL[torch.bfloat16], "batch read before its slots were overwritten")
+    c.wait()
+    ids2 = np.array([2, 3, -1, 3] * 64, np.int32)
+    slots2 = c.map(ids2)
+    x2 = torch.randn(256, 2048, generator=g).to(torch.bfloat16)
+    y2 = b.lora_layer_apply(c.pool(0), x2.to(DEV), Wd, torch.as_tensor(slots2, device=DEV),
+                            w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_SGMV)
+    c.release()
+    torch.cuda.synchronize()
+    ref2 = oracle.layer(f64(x2), f64(W), ids2, op, want=("y",))["y"]
+    assert_close(y2, ref2, TOL[torch.bfloat16], "reloaded slots")
+    c.destroy()
+
+
+def test_cache_pools_belong_to_the_cache():
+    b = binding()
+    aset = wl.adapter_set([(256, 128)], [16, 16], [1.0, 1.0], seed=1)
+    c = _cache_for(aset, n_slots=1, max_loads=1)
+    p = c.pool(0)
+    assert b.library().lora_pool_destroy(p.handle) == b.LORA_E_INVALID
+    _make_resident(c, [0])
+    assert b.lora_pool_param_count(p, c.slot_of(0)) == 16 * (256 + 128)
+    # the only slot is bound: the other adapter is deferred, not loaded
+    c.map([0])
+    assert c.request(1) == b.LORA_CACHE_DEFERRED
+    with pytest.raises(b.LoraError) as e:
+        c.map([1])
+    assert e.value.status == b.LORA_E_NOT_RESIDENT
+    c.release()
+    assert c.request(1) == b.LORA_CACHE_LOADING
+    c.wait()
+    assert c.stats()["bytes_loaded"] == 2 * c.blob_layout(16)[2] * 2
+    c.destroy()
