@@ -23,6 +23,9 @@ The JSON line carries:
   cpu_baseline the fp64 oracle on the host cores, on a bounded sample
   workloads    the other four workloads (skewed 8B decode, 70B prefill,
                mixed-rank 70B ragged and padded), measured the same way
+  merge        the merge kernel's HBM GB/s (W += s A B in place)
+  paging       the adapter slot cache: cold-load latency and H2D GB/s of
+               whole 8B-shaped adapters, decode step time with loads in flight
 """
 from __future__ import annotations
 
@@ -52,6 +55,7 @@ def parse():
     ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-paging", action="store_true", help="skip the adapter-paging measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write kernel (counter calibration)")
     return ap.parse_args()
@@ -216,6 +220,7 @@ def bench_decode(torch, args):
     d_bstream = time_graph(torch, capture(torch, lambda: [base_stream(r) for r in reps]), kr) / R
     d_bfinish = time_graph(torch, capture(torch, lambda: [base_finish(r) for r in reps]), kr) / R
     d_step = time_graph(torch, g_full, max(1, kr // 2)) / R
+    decode_graph = g_full
 
     # the standalone BGMV shrink entry point on the same batch
     for r in reps:
@@ -260,6 +265,9 @@ def bench_decode(torch, args):
             bgmv_shrink_GBps=round(shrink_bytes / d_shr / 1e9, 1),
             bgmv_shrink_frac_hbm=round(shrink_bytes / d_shr / 1e9 / HBM_PEAK_GBS, 4),
         ),
+        # the graph replays launches over reps' tensors and pools: whoever
+        # replays it must hold reps too
+        _decode_graph=(decode_graph, reps),
     )
     return out, w0
 
@@ -394,6 +402,91 @@ def cpu_baseline(w, seconds):
                        f"x{n_done} passes, {el:.1f} s, fp64")
 
 
+def bench_paging(torch, args, decode, R):
+    """Adapter slot cache: cold-load latency and host-to-device GB/s of whole
+    8B-shaped adapters (32 layers x 7 projections; rank 8 is about the 40 MB
+    hot adapter of the paging page, rank 16 twice that), and the decode step
+    time while loads are in flight on the cache's stream versus idle (a
+    fetch must not stall the decode loop).  Blobs are pinned host memory."""
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    decode_graph, decode_reps = decode   # the replica tensors stay referenced while the graph replays
+    assert len(decode_reps) == R
+    dev = torch.device("cuda:0")
+    parts = wl.eight_b_parts(32)
+    n_ad, n_slots = 8, 4
+    c = b.Cache(torch.bfloat16, parts, 16, n_ad, n_slots, 4, device=dev)
+    ranks = [8, 16] * (n_ad // 2)
+    blob_bytes = {}
+    g = wl._gen(dev, 9100)
+    for a, r in enumerate(ranks):
+        n_el = c.blob_layout(r)[2]
+        blob = torch.empty(n_el, dtype=torch.bfloat16, pin_memory=True)
+        blob.copy_((torch.randn(n_el, generator=g, device=dev) / 64).to(torch.bfloat16))
+        c.register_blob(a, r, 2.0, blob)
+        blob_bytes[r] = n_el * 2
+    torch.cuda.synchronize()
+
+    # cold loads one at a time: request (miss) then wait
+    lat = {8: [], 16: []}
+    for _ in range(3):
+        for a in range(n_ad):
+            if c.slot_of(a) >= 0:
+                continue
+            t0 = time.perf_counter()
+            st = c.request(a)
+            assert st == b.LORA_CACHE_LOADING, st
+            c.wait()
+            lat[ranks[a]].append(time.perf_counter() - t0)
+    # back-to-back loads (cap 4 in flight) of 4 adapters not resident
+    miss = [a for a in range(n_ad) if c.slot_of(a) < 0][:4]
+    t0 = time.perf_counter()
+    for a in miss:
+        assert c.request(a) == b.LORA_CACHE_LOADING
+    c.wait()
+    burst_s = time.perf_counter() - t0
+    burst_bytes = sum(blob_bytes[ranks[a]] for a in miss)
+
+    # decode steps with and without loads in flight
+    reps = 50
+    for _ in range(5):
+        decode_graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        decode_graph.replay()
+    torch.cuda.synchronize()
+    idle_s = (time.perf_counter() - t0) / (reps * R)
+    miss = [a for a in range(n_ad) if c.slot_of(a) < 0][:4]
+    t0 = time.perf_counter()
+    for a in miss:
+        assert c.request(a) == b.LORA_CACHE_LOADING
+    for _ in range(reps):
+        decode_graph.replay()
+    torch.cuda.synchronize()
+    busy_s = (time.perf_counter() - t0) / (reps * R)
+    n_done = c.poll()
+    c.wait()
+    st = c.stats()
+    c.destroy()
+    pct = lambda v, q: float(sorted(v)[min(len(v) - 1, int(round(q * (len(v) - 1))))])
+    out = dict(adapter="8B-shaped, 32 layers x 7 projections, bf16", slots=n_slots,
+               blob_MB={str(r): round(v / 1e6, 2) for r, v in blob_bytes.items()})
+    for r in (8, 16):
+        v = lat[r]
+        out[f"rank{r}"] = dict(loads=len(v), cold_load_ms_p50=round(pct(v, 0.5) * 1e3, 3),
+                               cold_load_ms_p95=round(pct(v, 0.95) * 1e3, 3),
+                               h2d_GBps_p50=round(blob_bytes[r] / pct(v, 0.5) / 1e9, 1))
+    out["burst"] = dict(loads=len(miss), MB=round(burst_bytes / 1e6, 1), ms=round(burst_s * 1e3, 3),
+                        h2d_GBps=round(burst_bytes / burst_s / 1e9, 1))
+    out["decode_step_us_idle"] = round(idle_s * 1e6, 3)
+    out["decode_step_us_while_loading"] = round(busy_s * 1e6, 3)
+    out["loads_completed_during_decode"] = n_done
+    out["evictions"] = st["evictions"]
+    return out
+
+
 def bench_merge(torch, args):
     """lora_merge_adapter (W += s A_a B_a in place) on 8B and 70B q_proj
     shapes: merges then unmerges over 4 weight replicas (more than the
@@ -453,6 +546,12 @@ def main():
         torch.cuda.empty_cache()
     log("bench: merge kernel ...")
     merge = bench_merge(torch, args)
+    decode = dec.pop("_decode_graph")
+    paging = None
+    if not args.no_paging:
+        log("bench: adapter paging ...")
+        paging = bench_paging(torch, args, decode, args.replicas)
+    del decode
     cpu = None
     if not args.no_cpu:
         log("bench: cpu baseline (oracle) ...")
@@ -484,6 +583,7 @@ def main():
         "gpu_step_us": round(dec["gpu_step_s"] * 1e6, 3),
         "workloads": extra,
         "merge": merge,
+        "paging": paging,
     }
     if cpu:
         line["gpu_over_cpu"] = round(line["value"] / cpu["value"], 1)

@@ -493,6 +493,15 @@ class Cache:
         _check(_lib.lora_cache_register(self.handle, adapter, rank, float(scale), blob_ptr),
                "lora_cache_register")
 
+    def register_blob(self, adapter: int, rank: int, scale: float, blob: torch.Tensor):
+        """Register an adapter whose host blob is already packed (a pinned
+        1-D tensor of the cache dtype, ``blob_layout(rank)[2]`` elements)."""
+        assert blob.dim() == 1 and blob.dtype == self.dtype and not blob.is_cuda
+        assert blob.numel() == self.blob_layout(rank)[2]
+        self.blobs[adapter] = blob
+        _check(_lib.lora_cache_register(self.handle, adapter, rank, float(scale), _ptr(blob)),
+               "lora_cache_register")
+
     def pin(self, adapter: int, pinned: bool = True):
         _check(_lib.lora_cache_pin(self.handle, adapter, int(bool(pinned))), "lora_cache_pin")
 

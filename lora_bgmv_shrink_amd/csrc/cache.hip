@@ -54,24 +54,54 @@ __host__ __device__ inline int64_t block_elems(int64_t rows, int64_t cols) {
 }
 
 // After a load into `slot`: the slot's rank and scale (one entry shared by
-// every part's pool) and every part's block offsets.  One thread: the loop
-// is a prefix sum over at most a few hundred parts.
-__global__ void k_cache_slot_tables(int32_t* __restrict__ ranks, float* __restrict__ scales,
-                                    int64_t* __restrict__ a_off, int64_t* __restrict__ b_off,
-                                    const int32_t* __restrict__ d_in,
-                                    const int32_t* __restrict__ d_out, int32_t n_parts,
-                                    int32_t n_slots, int32_t slot, int32_t rank, float scale,
-                                    int64_t slot_base) {
-    if (blockIdx.x != 0 || threadIdx.x != 0) return;
-    int64_t o = slot_base;
-    for (int32_t p = 0; p < n_parts; ++p) {
-        a_off[(int64_t)p * n_slots + slot] = o;
-        o += block_elems(d_in[p], rank);
-        b_off[(int64_t)p * n_slots + slot] = o;
-        o += block_elems(rank, d_out[p]);
+// every part's pool) and every part's block offsets.  One workgroup of 256
+// threads walks the parts 256 at a time: thread t sizes part p0 + t, an
+// exclusive prefix sum (wave shuffles, then the four wave totals) places it,
+// and the chunk total carries into the next chunk.
+constexpr int kTableThreads = 256;
+
+__global__ void __launch_bounds__(kTableThreads)
+k_cache_slot_tables(int32_t* __restrict__ ranks, float* __restrict__ scales,
+                    int64_t* __restrict__ a_off, int64_t* __restrict__ b_off,
+                    const int32_t* __restrict__ d_in, const int32_t* __restrict__ d_out,
+                    int32_t n_parts, int32_t n_slots, int32_t slot, int32_t rank, float scale,
+                    int64_t slot_base) {
+    __shared__ int64_t wave_sum[kTableThreads / 64];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = t >> 6;
+    int64_t carry = slot_base;
+    for (int32_t p0 = 0; p0 < n_parts; p0 += kTableThreads) {
+        const int32_t p = p0 + t;
+        int64_t ea = 0, eb = 0;
+        if (p < n_parts) {
+            ea = block_elems(d_in[p], rank);
+            eb = block_elems(rank, d_out[p]);
+        }
+        int64_t v = ea + eb;   // inclusive scan within the wave
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t u = __shfl_up(v, o, 64);
+            if (lane >= o) v += u;
+        }
+        if (lane == 63) wave_sum[w] = v;
+        __syncthreads();
+        int64_t before = 0, total = 0;
+        for (int k = 0; k < kTableThreads / 64; ++k) {
+            before += k < w ? wave_sum[k] : 0;
+            total += wave_sum[k];
+        }
+        if (p < n_parts) {
+            const int64_t o = carry + before + v - (ea + eb);
+            a_off[(int64_t)p * n_slots + slot] = o;
+            b_off[(int64_t)p * n_slots + slot] = o + ea;
+        }
+        carry += total;
+        __syncthreads();   // wave_sum is rewritten by the next chunk
     }
-    ranks[slot] = rank;
-    scales[slot] = scale;
+    if (t == 0) {
+        ranks[slot] = rank;
+        scales[slot] = scale;
+    }
 }
 
 }  // namespace
@@ -187,7 +217,7 @@ lora_status_t start_load(lora_cache_s* c, int32_t v, int32_t adapter) {
         char* dst = (char*)c->arena + (size_t)v * (size_t)c->cap_elems * c->eb;
         if (hipMemcpyAsync(dst, e.blob, (size_t)bytes, hipMemcpyHostToDevice, c->copy) != hipSuccess)
             return LORA_E_DEVICE;
-        hipLaunchKernelGGL(k_cache_slot_tables, dim3(1), dim3(64), 0, c->copy, c->t_ranks,
+        hipLaunchKernelGGL(k_cache_slot_tables, dim3(1), dim3(kTableThreads), 0, c->copy, c->t_ranks,
                            c->t_scales, c->t_aoff, c->t_boff, c->t_din, c->t_dout, c->n_parts,
                            c->n_slots, v, e.rank, e.scale, (int64_t)v * c->cap_elems);
         if (hipGetLastError() != hipSuccess) return LORA_E_DEVICE;

@@ -179,3 +179,34 @@ def test_cache_pools_belong_to_the_cache():
     c.wait()
     assert c.stats()["bytes_loaded"] == 2 * c.blob_layout(16)[2] * 2
     c.destroy()
+
+
+def test_many_parts_offsets():
+    """300 parts of mixed shapes: the slot tables place every part's blocks
+    (parts past the first 256 exercise the carry between chunks of the
+    table-update kernel)."""
+    b = binding()
+    parts = [(64 + 32 * (p % 3), 32 + 16 * (p % 4)) for p in range(300)]
+    aset = wl.adapter_set(parts, [8, 16, 16], [2.0, -0.5, 1.25], seed=4)
+    c = _cache_for(aset, n_slots=2, max_loads=1)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(13)
+    rng = np.random.default_rng(2)
+    check = [0, 1, 255, 256, 257, 299]
+    Ws = {p: (torch.randn(*parts[p], generator=g) / 16).to(torch.bfloat16) for p in check}
+    for used in ([0, 1], [2, 0], [1, 2]):
+        _make_resident(c, used)
+        ids = np.array(used, np.int32)[rng.integers(0, 2, size=24)]
+        ids[::7] = -1
+        slots = c.map(ids)
+        ids_d = torch.as_tensor(slots, device=DEV)
+        outs = {}
+        for p in check:
+            x = torch.randn(24, parts[p][0], generator=g).to(torch.bfloat16)
+            outs[p] = (x, b.lora_layer_apply(c.pool(p), x.to(DEV), Ws[p].to(DEV), ids_d, mode=b.LORA_MODE_BGMV))
+        c.release()
+        torch.cuda.synchronize()
+        for p in check:
+            ref = oracle.layer(f64(outs[p][0]), f64(Ws[p]), ids, _oracle_pool(aset, p), want=("y",))["y"]
+            assert_close(outs[p][1], ref, TOL[torch.bfloat16], f"adapters {used} part {p}")
+    c.destroy()
