@@ -26,6 +26,9 @@ The JSON line carries:
   merge        the merge kernel's HBM GB/s (W += s A B in place)
   paging       the adapter slot cache: cold-load latency and H2D GB/s of
                whole 8B-shaped adapters, decode step time with loads in flight
+  serving      a Zipf decode serving loop through the admission scheduler and
+               the slot cache: distinct adapters per step, adapter overhead
+               fraction, hit rate and queue waits, locality weight vs FIFO
 """
 from __future__ import annotations
 
@@ -34,6 +37,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -487,6 +492,105 @@ def bench_paging(torch, args, decode, R):
     return out
 
 
+def bench_serving(torch, args):
+    """A decode serving loop on one q projection (4096 -> 4096, rank 16):
+    single-token requests with adapter ids ~ Zipf(1.1) over 1000 adapters
+    kept on the host, a standing backlog of 256 requests plus Poisson(32)
+    arrivals per step (the queue is saturated, so admission has a choice);
+    each step the admission scheduler forms a batch of at most 32 rows, the
+    slot cache (250 slots) maps it to slots, and lora_layer_apply runs it.
+    Reported per policy (the page's locality weight 0.35; 0 = first come
+    first served; a strong weight of 8; 0.35 with a cap of 8 adapters per
+    batch): distinct
+    adapters per step (the cost driver), cache hit rate, queue waits in
+    steps (overall and for the less popular half of the adapters), and the
+    GPU time of the last 64 batches the loop formed, graph-replayed, against
+    the base-only decode of the same rows and W (adapter overhead
+    fraction)."""
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    d, r, n_ad, n_slots, rows_max = 4096, 16, 1000, 250, 32
+    g = wl._gen(dev, 9200)
+    W = wl._randn(g, (d, d), wl.W_DIV, torch.bfloat16, dev)          # stored [d_out, d_in]
+    x = wl._randn(g, (rows_max, d), 1.0, torch.bfloat16, dev)
+    out = {}
+    for label, w_local, cap in (("locality_0.35", 0.35, rows_max), ("fifo", 0.0, rows_max),
+                                ("locality_8", 8.0, rows_max), ("locality_0.35_cap8", 0.35, 8)):
+        c = b.Cache(torch.bfloat16, [(d, d)], r, n_ad, n_slots, 8, device=dev)
+        n_el = c.blob_layout(r)[2]
+        blobs = torch.empty(n_ad * n_el, dtype=torch.bfloat16, pin_memory=True)
+        blobs.copy_((torch.randn(n_ad * n_el, generator=g, device=dev) / 32).to(torch.bfloat16))
+        for a in range(n_ad):
+            c.register_blob(a, r, 2.0, blobs[a * n_el:(a + 1) * n_el])
+        sch = b.Scheduler(n_ad, 1.0, w_local, max_adapters=cap, max_rows=rows_max, cache=c)
+        rng = np.random.default_rng(77)
+        p = wl.zipf_probs(n_ad, 1.1)
+        steps, warm = 1500, 300
+        distinct, waits_all, waits_tail, last, n_rows = [], [], [], [], []
+        rid = 0
+        stats0 = None
+        for step in range(steps):
+            k = int(rng.poisson(32)) + (256 if step == 0 else 0)
+            ids = rng.choice(n_ad, size=k, p=p)
+            for j, a in enumerate(ids):
+                sch.submit(rid, int(a), 1, step + (j + 0.5) / max(k, 1))
+                rid += 1
+            (req, ad, rw, wt), info = sch.step(float(step + 1), rows_max)
+            if step == warm:
+                stats0 = c.stats()
+            n = len(ad)
+            if n == 0:
+                continue
+            slots = c.map(ad)
+            b.lora_layer_apply(c.pool(0), x[:n], W, torch.as_tensor(slots, device=dev), w_layout=b.LORA_W_OUT_IN,
+                               mode=b.LORA_MODE_BGMV)
+            c.release()
+            if step >= warm:
+                n_rows.append(n)
+                distinct.append(info["distinct_adapters"])
+                waits_all.extend(wt.tolist())
+                waits_tail.extend(wt[ad >= n_ad // 2].tolist())
+            if step >= steps - 64:
+                last.append(slots.copy())
+        torch.cuda.synchronize()
+        c.wait()                      # no copy in flight while the batches are timed
+        st = c.stats()
+        # GPU time of the last batches (their slots are still those adapters'
+        # or others of the same rank; the time does not depend on the values)
+        pool = c.pool(0)
+        ids_l = [torch.as_tensor(sl, device=dev) for sl in last]
+        ys = [torch.empty((len(sl), d), dtype=torch.bfloat16, device=dev) for sl in last]
+        ws = torch.zeros(b.lora_layer_workspace(pool, rows_max, b.LORA_MODE_BGMV), dtype=torch.uint8, device=dev)
+        wsb = torch.zeros(b.lora_decode_workspace(pool, rows_max, False), dtype=torch.uint8, device=dev)
+        g_lora = capture(torch, lambda: [b.lora_layer_apply(pool, x[:len(sl)], W, ii, w_layout=b.LORA_W_OUT_IN,
+                                                            mode=b.LORA_MODE_BGMV, y=yy, ws=ws)
+                                         for sl, ii, yy in zip(last, ids_l, ys)])
+        g_base = capture(torch, lambda: [(b.lora_decode_stream(pool, x[:len(sl)], W, ii, wsb, False),
+                                          b.lora_decode_finish(pool, ii, wsb, yy, False))
+                                         for sl, ii, yy in zip(last, ids_l, ys)])
+        lora_us = time_graph(torch, g_lora, 20) / len(last) * 1e6
+        base_us = time_graph(torch, g_base, 20) / len(last) * 1e6
+        hits = st["hits"] - stats0["hits"]
+        loads = st["loads_started"] - stats0["loads_started"]
+        q = lambda v, f: round(float(np.quantile(np.asarray(v, np.float64), f)), 3) if len(v) else None
+        out[label] = dict(
+            w_local=w_local, max_adapters=cap, steps=len(distinct), rows_per_step=round(float(np.mean(n_rows)), 2),
+            distinct_adapters_per_step=dict(p10=q(distinct, .1), p50=q(distinct, .5), p90=q(distinct, .9),
+                                            max=int(max(distinct))),
+            gpu_step_us=round(lora_us, 3), base_only_step_us=round(base_us, 3),
+            adapter_overhead_fraction=round(max(0.0, (lora_us - base_us) / lora_us), 4),
+            cache_hit_rate=round(hits / max(1, hits + loads), 4), loads=loads,
+            wait_steps=dict(p50=q(waits_all, .5), p99=q(waits_all, .99)),
+            wait_steps_less_popular_half=dict(p50=q(waits_tail, .5), p99=q(waits_tail, .99), n=len(waits_tail)))
+        del g_lora, g_base
+        sch.destroy()
+        c.destroy()
+        del blobs
+    return out
+
+
 def bench_merge(torch, args):
     """lora_merge_adapter (W += s A_a B_a in place) on 8B and 70B q_proj
     shapes: merges then unmerges over 4 weight replicas (more than the
@@ -547,10 +651,12 @@ def main():
     log("bench: merge kernel ...")
     merge = bench_merge(torch, args)
     decode = dec.pop("_decode_graph")
-    paging = None
+    paging = serving = None
     if not args.no_paging:
         log("bench: adapter paging ...")
         paging = bench_paging(torch, args, decode, args.replicas)
+        log("bench: serving loop (admission + cache + layer) ...")
+        serving = bench_serving(torch, args)
     del decode
     cpu = None
     if not args.no_cpu:
@@ -584,6 +690,7 @@ def main():
         "workloads": extra,
         "merge": merge,
         "paging": paging,
+        "serving": serving,
     }
     if cpu:
         line["gpu_over_cpu"] = round(line["value"] / cpu["value"], 1)

@@ -439,6 +439,79 @@ int32_t lora_cache_slot_of(lora_cache_t cache, int32_t adapter);
 
 lora_status_t lora_cache_stats(lora_cache_t cache, lora_cache_stats_t* out);
 
+/* ---------------------------------------------------------------------- */
+/* Adapter-aware admission                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* Forms each step's batch from a queue of requests (host only, no device
+ * work).  Every queued request scores
+ *     w_fair * (now - arrival) + w_local * locality * rows,
+ * locality being 1 when the request's adapter is active (used by the
+ * previous step's batch or already admitted to this one) and 0 otherwise
+ * ("Serving many LoRA adapters" (blog.ecitis.org), section "Adapter-aware
+ * scheduling": cost grows with distinct adapters per step; the wait term
+ * grows without bound, so no tenant starves).  The batch fills in score
+ * order (ties: earlier arrival, then earlier submission) under:
+ *   - max_rows rows (tokens) per batch;
+ *   - max_adapters distinct adapters per batch ("Serving multiple LoRAs...",
+ *     section "Scheduling the adapters": requests beyond the cap wait for a
+ *     later batch); base-only requests (adapter -1) never count;
+ *   - rank_groups != 0: one rank class per batch, classes being ranks
+ *     1, 2, 3-4, 5-8, 9-16, 17-32, 33-64 (same section, exercise 2: batch
+ *     by rank group);
+ *   - with a cache: the adapter must be resident.  A request whose adapter
+ *     is not is skipped for this step, and asking the cache for it starts
+ *     its load ("Serving many LoRA adapters", section "Paging adapters":
+ *     defer that request, prefetch while it queues).  Queued requests hold
+ *     their adapter in the cache (lora_cache_hold) so it is not evicted.
+ * A request that does not fit stays queued.  Not thread-safe. */
+typedef struct lora_sched_s* lora_sched_t;
+
+typedef struct {
+    double w_fair;        /* weight of the wait, per unit of the caller's clock (>= 0) */
+    double w_local;       /* weight of locality x rows (>= 0) */
+    int32_t max_adapters; /* distinct adapters per batch, >= 1 */
+    int32_t max_rows;     /* rows per batch, >= 1 */
+    int32_t rank_groups;  /* != 0: one rank class per batch */
+} lora_sched_config_t;
+
+typedef struct {
+    int32_t admitted;            /* requests in the batch */
+    int32_t rows;                /* their rows */
+    int32_t distinct_adapters;   /* distinct ids >= 0 in the batch */
+    int32_t skipped_rows;        /* skipped: would exceed max_rows (or capacity) */
+    int32_t skipped_cap;         /* skipped: new adapter with the batch at max_adapters */
+    int32_t skipped_rank_group;  /* skipped: other rank class */
+    int32_t deferred_not_resident; /* skipped: adapter not resident in the cache */
+    int32_t queued;              /* requests left in the queue */
+    double max_wait_admitted;    /* longest wait among admitted requests */
+    double max_wait_queued;      /* longest wait among those left */
+} lora_sched_step_t;
+
+/* ranks (host, n_adapters) may be NULL unless cfg->rank_groups != 0;
+ * cache may be NULL (every adapter counts as resident).  The cache must
+ * outlive the scheduler and cover the same adapter ids. */
+lora_status_t lora_sched_create(lora_sched_t* out, const lora_sched_config_t* cfg,
+                                int32_t n_adapters, const int32_t* ranks, lora_cache_t cache);
+/* Drops the queue (and the cache holds of its requests). */
+lora_status_t lora_sched_destroy(lora_sched_t sched);
+
+/* Queue a request of `rows` rows (>= 1) for adapter `adapter` (-1: base
+ * only) that arrived at time `arrival` (finite). */
+lora_status_t lora_sched_submit(lora_sched_t sched, int64_t request, int32_t adapter, int32_t rows,
+                                double arrival);
+
+/* Form one batch at time `now` of at most `capacity` requests.  Writes,
+ * in admission order, requests/adapters/rows/waits[0 .. info->admitted)
+ * (host out arrays of `capacity` entries each; waits may be NULL) and the
+ * step's counts into *info. */
+lora_status_t lora_sched_step(lora_sched_t sched, double now, int32_t capacity, int64_t* requests,
+                              int32_t* adapters, int32_t* rows, double* waits,
+                              lora_sched_step_t* info);
+
+/* Requests waiting in the queue. */
+int32_t lora_sched_queued(lora_sched_t sched);
+
 #ifdef __cplusplus
 }
 #endif

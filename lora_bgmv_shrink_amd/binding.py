@@ -43,6 +43,7 @@ EXPORTS = [
     "lora_cache_blob_layout", "lora_cache_create", "lora_cache_destroy", "lora_cache_register",
     "lora_cache_pin", "lora_cache_hold", "lora_cache_request", "lora_cache_poll", "lora_cache_wait",
     "lora_cache_map", "lora_cache_release", "lora_cache_pool", "lora_cache_slot_of", "lora_cache_stats",
+    "lora_sched_create", "lora_sched_destroy", "lora_sched_submit", "lora_sched_step", "lora_sched_queued",
 ]
 
 
@@ -57,6 +58,18 @@ class CacheStatsT(ctypes.Structure):
         "requests", "hits", "pending", "loads_started", "deferred_load_cap", "deferred_no_slot",
         "loads_completed", "evictions", "bytes_loaded", "bytes_resident")] + \
         [(k, ctypes.c_int32) for k in ("n_slots", "slots_resident", "slots_loading", "slots_bound")]
+
+
+class SchedConfigT(ctypes.Structure):
+    _fields_ = [("w_fair", ctypes.c_double), ("w_local", ctypes.c_double), ("max_adapters", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32), ("rank_groups", ctypes.c_int32)]
+
+
+class SchedStepT(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in (
+        "admitted", "rows", "distinct_adapters", "skipped_rows", "skipped_cap", "skipped_rank_group",
+        "deferred_not_resident", "queued")] + [("max_wait_admitted", ctypes.c_double),
+                                               ("max_wait_queued", ctypes.c_double)]
 
 
 class SegmentsT(ctypes.Structure):
@@ -108,6 +121,11 @@ def _load():
         "lora_cache_pool": (p, [p, i32]),
         "lora_cache_slot_of": (i32, [p, i32]),
         "lora_cache_stats": (st, [p, p]),
+        "lora_sched_create": (st, [p, p, i32, p, p]),
+        "lora_sched_destroy": (st, [p]),
+        "lora_sched_submit": (st, [p, i64, i32, i32, ctypes.c_double]),
+        "lora_sched_step": (st, [p, ctypes.c_double, i32, p, p, p, p, p]),
+        "lora_sched_queued": (i32, [p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -467,6 +485,7 @@ class Cache:
         self.handle = h
         self.blobs = {}
         self._pools = {}
+        self._scheds = []
 
     def blob_layout(self, rank: int):
         n = len(self.parts)
@@ -556,8 +575,64 @@ class Cache:
         return {k: int(getattr(s, k)) for k, _ in CacheStatsT._fields_}
 
     def destroy(self):
+        for sc in getattr(self, "_scheds", []):
+            sc.destroy()
         if getattr(self, "handle", None):
             _check(_lib.lora_cache_destroy(self.handle), "lora_cache_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+# --------------------------------------------------------------------------
+# Adapter-aware admission
+# --------------------------------------------------------------------------
+
+class Scheduler:
+    """lora_sched_*: forms each step's batch from a request queue.  ``cache``
+    (a ``Cache`` or None) gates admission on residency."""
+
+    def __init__(self, n_adapters: int, w_fair: float = 1.0, w_local: float = 0.35, max_adapters: int = 32,
+                 max_rows: int = 256, rank_groups: bool = False, ranks=None, cache: Optional[Cache] = None):
+        cfg = SchedConfigT(float(w_fair), float(w_local), int(max_adapters), int(max_rows), int(bool(rank_groups)))
+        rk = None if ranks is None else np.ascontiguousarray(ranks, np.int32)
+        h = ctypes.c_void_p()
+        _check(_lib.lora_sched_create(ctypes.byref(h), ctypes.byref(cfg), n_adapters,
+                                      None if rk is None else rk.ctypes.data,
+                                      None if cache is None else cache.handle), "lora_sched_create")
+        self.handle = h
+        self.cache = cache   # kept alive: the scheduler holds adapters in it
+        if cache is not None:
+            cache._scheds.append(self)   # the cache destroys its schedulers first
+
+    def submit(self, request: int, adapter: int, rows: int, arrival: float):
+        _check(_lib.lora_sched_submit(self.handle, int(request), int(adapter), int(rows), float(arrival)),
+               "lora_sched_submit")
+
+    def step(self, now: float, capacity: int):
+        """-> (requests, adapters, rows, waits) numpy arrays, info dict."""
+        cap = max(int(capacity), 1)
+        req = np.zeros(cap, np.int64)
+        ad = np.zeros(cap, np.int32)
+        rw = np.zeros(cap, np.int32)
+        wt = np.zeros(cap, np.float64)
+        info = SchedStepT()
+        _check(_lib.lora_sched_step(self.handle, float(now), int(capacity), req.ctypes.data, ad.ctypes.data,
+                                    rw.ctypes.data, wt.ctypes.data, ctypes.byref(info)), "lora_sched_step")
+        k = info.admitted
+        d = {f: getattr(info, f) for f, _ in SchedStepT._fields_}
+        return (req[:k], ad[:k], rw[:k], wt[:k]), d
+
+    def queued(self) -> int:
+        return int(_lib.lora_sched_queued(self.handle))
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            _check(_lib.lora_sched_destroy(self.handle), "lora_sched_destroy")
             self.handle = None
 
     def __del__(self):
