@@ -50,6 +50,8 @@ def _bind(lib):
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_merge.restype = ctypes.c_int
     lib.oracle_merge.argtypes = [i64, i64, p, i32, i32, p, p, p, p, p, p, ctypes.c_double, ctypes.c_int]
+    lib.oracle_dequant_q4.restype = None
+    lib.oracle_dequant_q4.argtypes = [i64, i64, p, i64, p, i64, i64, p]
     return lib
 
 
@@ -164,6 +166,20 @@ def merge(W, pool: OraclePool, adapter: int, sign: float = 1.0, threads: int = 0
     if rc != 0:
         raise ValueError(f"adapter {adapter} outside [0, {pool.n_adapters})")
     return out
+
+
+def dequant_q4(q, scale, d_in: int, group: int = 128, lib=None) -> np.ndarray:
+    """4-bit base weight -> fp64 W [d_in, d_out].  ``q`` [d_out, ldq] uint8
+    (two signed nibbles per byte, low nibble first), ``scale`` [d_out, lds]
+    (widened to fp64 exactly)."""
+    lib = lib or load()
+    q = _c(q, np.uint8)
+    sc = _c(scale, np.float64)
+    d_out = q.shape[0]
+    assert q.shape[1] * 2 >= d_in and sc.shape[0] == d_out and sc.shape[1] * group >= d_in
+    W = np.empty((d_in, d_out), np.float64)
+    lib.oracle_dequant_q4(d_in, d_out, _ptr(q), q.shape[1], _ptr(sc), sc.shape[1], group, _ptr(W))
+    return W
 
 
 def max_threads(lib=None) -> int:

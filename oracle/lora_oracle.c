@@ -223,3 +223,27 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * A 4-bit base weight, widened.  The pages leave the 4-bit format open
+ * ("Serving Many LoRA Adapters" (praveentn.live), section "When It Falls
+ * Down": a 4-bit base with FP16/BF16 adapters); the one read here:
+ *   q[n * ldq + k / 2] holds the weight of output column n and input k as a
+ *   signed 4-bit two's-complement value, k even in the low nibble, k odd in
+ *   the high nibble; scale[n * lds + k / group] is the scale of that weight's
+ *   group of `group` consecutive inputs.  The weight is q * scale.
+ * Writes W[k][n] ([d_in, d_out], the layer's orientation).  Each value is an
+ * integer in [-8, 7] times a scale, exact in fp64.
+ */
+void oracle_dequant_q4(int64_t d_in, int64_t d_out, const uint8_t* q, int64_t ldq, const double* scale,
+                       int64_t lds, int64_t group, double* W)
+{
+    for (int64_t n = 0; n < d_out; ++n) {
+        for (int64_t k = 0; k < d_in; ++k) {
+            const uint8_t byte = q[n * ldq + k / 2];
+            const int nib = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            const int v = nib >= 8 ? nib - 16 : nib;
+            W[k * d_out + n] = (double)v * scale[n * lds + k / group];
+        }
+    }
+}

@@ -355,7 +355,39 @@ def pin_empty_batch(lib):
     assert perm.size == 0 and seg_ids.size == 0 and seg_off.tolist() == [0]
 
 
-PINS = [pin_tiny_segments_golden, pin_walkthrough_segments_golden, pin_segments_vs_numpy_stable_sort,
+def pin_dequant_q4_golden(lib):
+    """The oracle's 4-bit base weight against entries worked out by hand
+    (tests/golden/q4_dequant.json): nibble order, sign, group index and
+    orientation."""
+    g = json.load(open(os.path.join(GOLDEN, "q4_dequant.json")))
+    q = np.array(g["q_rows"], np.uint8)
+    W = oracle.dequant_q4(q, np.array(g["scales"]), g["d_in"], group=g["group"], lib=lib)
+    assert W.shape == (g["d_in"], g["d_out"])
+    want = np.zeros_like(W)
+    for k, n, v in g["nonzero"]:
+        want[k, n] = v
+    assert np.array_equal(W, want)
+
+
+def pin_q4_values_are_scaled_integers(lib):
+    """With power-of-two scales every 4-bit weight is exact in bf16 (so a
+    bf16 layer can serve as a cross-check of a 4-bit one), and every weight
+    is an integer in [-8, 7] times its group's scale, both ends reached."""
+    import torch
+    rng = np.random.default_rng(3)
+    d_in, d_out = 256, 64
+    q = rng.integers(0, 256, size=(d_out, d_in // 2), dtype=np.uint8)
+    sc = 2.0 ** rng.integers(-8, -4, size=(d_out, d_in // 128))
+    W = oracle.dequant_q4(q, sc, d_in, lib=lib)
+    Wb = torch.from_numpy(W).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(W, Wb)
+    # the nibbles decode to integers in [-8, 7] times the group's scale
+    ratio = W.T / np.repeat(sc, 128, axis=1)
+    assert np.array_equal(ratio, np.round(ratio)) and ratio.min() >= -8 and ratio.max() <= 7
+    assert ratio.min() == -8 and ratio.max() == 7
+
+
+PINS = [pin_dequant_q4_golden, pin_q4_values_are_scaled_integers, pin_tiny_segments_golden, pin_walkthrough_segments_golden, pin_segments_vs_numpy_stable_sort,
         pin_page_script_agreement, pin_merged_weights, pin_additivity_base_only,
         pin_einsum_gather_formulation, pin_permutation_equivariance, pin_walkthrough_shared_adapter,
         pin_special_cases_plain_gemm, pin_linearity_in_scale, pin_ragged_equals_padded,
@@ -385,3 +417,4 @@ def test_sampled_rows_match_full_batch():
     part = run_oracle(w, rows=rows)
     for k in ("t", "lora", "y"):
         assert np.array_equal(part[k], full[k][rows]), k
+
