@@ -45,7 +45,8 @@ MUTATIONS = [
     ("q4_nibbles_swapped", "const int nib = (k % 2 == 0) ? (byte & 15) : (byte >> 4);",
      "const int nib = (k % 2 == 0) ? (byte >> 4) : (byte & 15);"),
     ("q4_unsigned", "const int v = nib >= 8 ? nib - 16 : nib;", "const int v = nib;"),
-    ("q4_group_from_byte_index", "scale[n * lds + k / group]", "scale[n * lds + (k / 2) / group]"),
+    ("q4_group_from_byte_index", "(double)v * scale[n * lds + k / group]",
+     "(double)v * scale[n * lds + (k / 2) / group]"),
     ("q4_transposed_out", "W[k * d_out + n] = (double)v", "W[n * d_in + k] = (double)v"),
     ("merge_rank_off_by_one", "for (int32_t j = 0; j < r; ++j) acc += Ak[j]",
      "for (int32_t j = 0; j + 1 < r; ++j) acc += Ak[j]"),
