@@ -24,6 +24,7 @@ The JSON line carries:
   workloads    the other four workloads (skewed 8B decode, 70B prefill,
                mixed-rank 70B ragged and padded), measured the same way
   merge        the merge kernel's HBM GB/s (W += s A B in place)
+  q4_decode    the headline decode batch over a 4-bit base weight
   paging       the adapter slot cache: cold-load latency and H2D GB/s of
                whole 8B-shaped adapters, decode step time with loads in flight
   serving      a Zipf decode serving loop through the admission scheduler and
@@ -594,6 +595,63 @@ def bench_serving(torch, args):
     return out
 
 
+def bench_q4_decode(torch, args):
+    """The headline decode batch (q 4096 -> 4096, rank 16, 32 rows on 20
+    adapters of a pool of 250) over a 4-bit base weight with bf16 adapters:
+    lora_decode_stream_q4 + lora_decode_finish, graph-replayed over 24
+    replicas (each its own weight, pool and x; the step's working set times
+    24 exceeds the Infinity Cache).  The stream launch's algorithmic bytes:
+    the 4-bit weight, its scales, the distinct adapters' A blocks, x and the
+    ids."""
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    R = 24
+    reps = []
+    for r in range(R):
+        w = wl.decode_q_proj(device=dev, value_seed=None if r == 0 else 7 + 1000 * r)
+        p = w.projections[0]
+        p.W = None
+        pool = make_pool(b, p.pool)
+        Wq, sc = wl.q4_weight(100 + r, 4096, 4096, dev)
+        n = w.n_rows
+        ids = torch.as_tensor(w.ids, device=dev)
+        reps.append(dict(w=w, p=p, pool=pool, Wq=Wq, sc=sc, ids=ids,
+                         y=torch.zeros((n, 4096), dtype=torch.bfloat16, device=dev),
+                         ws=torch.zeros(b.lora_decode_workspace(pool, n, True), dtype=torch.uint8, device=dev),
+                         wsb=torch.zeros(b.lora_decode_workspace(pool, n, False), dtype=torch.uint8, device=dev)))
+    n = reps[0]["w"].n_rows
+
+    def stream(r, lora=True):
+        b.lora_decode_stream_q4(r["pool"], r["p"].x, r["Wq"], r["sc"], r["ids"], r["ws" if lora else "wsb"], lora)
+
+    def finish(r, lora=True):
+        b.lora_decode_finish(r["pool"], r["ids"], r["ws" if lora else "wsb"], r["y"], lora)
+
+    g_step = capture(torch, lambda: [(stream(r), finish(r)) for r in reps])
+    g_stream = capture(torch, lambda: [stream(r) for r in reps])
+    g_base = capture(torch, lambda: [(stream(r, False), finish(r, False)) for r in reps])
+    kr = max(4, args.kernel_reps // 2)
+    d_step = time_graph(torch, g_step, kr) / R
+    d_stream = time_graph(torch, g_stream, kr) / R
+    d_base = time_graph(torch, g_base, kr) / R
+    pool = reps[0]["p"].pool
+    bA, U = distinct_bytes(pool, reps[0]["w"].ids, "A")
+    wbytes = 4096 * 4096 // 2 + 4096 * (4096 // 128) * 4
+    stream_bytes = wbytes + bA + n * 4096 * 2 + n * 4
+    out = dict(workload="decode_q4base_q4096_r16_pool250_rows32", replicas=R, distinct_adapters=U,
+               step_us=round(d_step * 1e6, 3), tokens_per_s=round(n / d_step, 1),
+               base_only_step_us=round(d_base * 1e6, 3),
+               overhead_fraction=round(max(0.0, (d_step - d_base) / d_step), 4),
+               stream_us=round(d_stream * 1e6, 3), stream_bytes=stream_bytes,
+               stream_GBps=round(stream_bytes / d_stream / 1e9, 1),
+               stream_frac_hbm=round(stream_bytes / d_stream / 1e9 / HBM_PEAK_GBS, 4))
+    del g_step, g_stream, g_base, reps
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_merge(torch, args):
     """lora_merge_adapter (W += s A_a B_a in place) on 8B and 70B q_proj
     shapes: merges then unmerges over 4 weight replicas (more than the
@@ -653,6 +711,8 @@ def main():
         torch.cuda.empty_cache()
     log("bench: merge kernel ...")
     merge = bench_merge(torch, args)
+    log("bench: 4-bit base decode ...")
+    q4 = bench_q4_decode(torch, args)
     decode = dec.pop("_decode_graph")
     paging = serving = None
     if not args.no_paging:
@@ -692,6 +752,7 @@ def main():
         "gpu_step_us": round(dec["gpu_step_s"] * 1e6, 3),
         "workloads": extra,
         "merge": merge,
+        "q4_decode": q4,
         "paging": paging,
         "serving": serving,
     }

@@ -294,6 +294,28 @@ lora_status_t lora_decode_workspace(lora_pool_t pool, int32_t n_rows, int with_l
 lora_status_t lora_decode_stream(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
                                  int64_t ldw, const int32_t* ids, int32_t n_rows, int with_lora,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+/* The stream launch over a 4-bit base weight, with bf16 x and bf16 adapters
+ * ("Serving Many LoRA Adapters" (praveentn.live), section "When It Falls
+ * Down": a 4-bit base with FP16/BF16 adapters needs a mixed-precision path).
+ * The pages leave the format open; the one taken:
+ *   Wq [d_out, ldq] bytes (device): the weight of output n and input k is a
+ *     signed 4-bit two's-complement value in byte Wq[n * ldq + k / 2], k
+ *     even in the low nibble;
+ *   w_scale [d_out, lds] fp32 (device): the scale of inputs k = 128 g ..
+ *     128 g + 127 of output n is w_scale[n * lds + g];
+ *   the weight is q * scale (the layer's W[k][n]).
+ * Products of x with the 4-bit values accumulate in fp32 per group of 128
+ * inputs, and each group's sum is scaled once.  Follow with
+ * lora_decode_finish (same pool, ids, n_rows, with_lora, workspace), which
+ * adds the adapter term and rounds y once; lora_decode_workspace sizes the
+ * workspace.  Requires d_in % 128 == 0, ldq >= d_in / 2 with ldq % 16 == 0, a
+ * 16-byte aligned Wq, a 4-byte aligned w_scale and lds >= d_in / 128
+ * (otherwise LORA_E_UNSUPPORTED / LORA_E_INVALID); the other rules are
+ * lora_decode_stream's. */
+lora_status_t lora_decode_stream_q4(lora_pool_t pool, const void* x, int64_t ldx, const uint8_t* Wq,
+                                    int64_t ldq, const float* w_scale, int64_t lds, const int32_t* ids,
+                                    int32_t n_rows, int with_lora, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
 lora_status_t lora_decode_finish(lora_pool_t pool, const int32_t* ids, int32_t n_rows, int with_lora,
                                  void* y, lora_dtype_t y_dtype, int64_t ldy, void* ws,
                                  size_t ws_bytes, hipStream_t stream);

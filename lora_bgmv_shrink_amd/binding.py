@@ -43,6 +43,7 @@ EXPORTS = [
     "lora_cache_blob_layout", "lora_cache_create", "lora_cache_destroy", "lora_cache_register",
     "lora_cache_pin", "lora_cache_hold", "lora_cache_request", "lora_cache_poll", "lora_cache_wait",
     "lora_cache_map", "lora_cache_release", "lora_cache_pool", "lora_cache_slot_of", "lora_cache_stats",
+    "lora_decode_stream_q4",
     "lora_sched_create", "lora_sched_destroy", "lora_sched_submit", "lora_sched_step", "lora_sched_queued",
 ]
 
@@ -121,6 +122,7 @@ def _load():
         "lora_cache_pool": (p, [p, i32]),
         "lora_cache_slot_of": (i32, [p, i32]),
         "lora_cache_stats": (st, [p, p]),
+        "lora_decode_stream_q4": (st, [p, p, i64, p, i64, p, i64, p, i32, ctypes.c_int, p, sz, p]),
         "lora_sched_create": (st, [p, p, i32, p, p]),
         "lora_sched_destroy": (st, [p]),
         "lora_sched_submit": (st, [p, i64, i32, i32, ctypes.c_double]),
@@ -431,6 +433,16 @@ def lora_decode_stream(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.
     _check(_lib.lora_decode_stream(pool.handle, _ptr(x), _ld(x), _ptr(W), _ld(W), _ptr(ids), ids.numel(),
                                    int(bool(with_lora)), _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(x.device))),
            "lora_decode_stream")
+
+
+def lora_decode_stream_q4(pool: Pool, x: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, ids: torch.Tensor,
+                          ws: torch.Tensor, with_lora: bool = True):
+    """Stream launch over a 4-bit base: Wq [d_out, ldq] uint8, w_scale
+    [d_out, lds] fp32 (see the header for the format)."""
+    assert Wq.dtype == torch.uint8 and w_scale.dtype == torch.float32
+    _check(_lib.lora_decode_stream_q4(pool.handle, _ptr(x), _ld(x), _ptr(Wq), _ld(Wq), _ptr(w_scale), _ld(w_scale),
+                                      _ptr(ids), ids.numel(), int(bool(with_lora)), _ptr(ws), ws.numel(),
+                                      ctypes.c_void_p(_stream(x.device))), "lora_decode_stream_q4")
 
 
 def lora_decode_finish(pool: Pool, ids: torch.Tensor, ws: torch.Tensor, y: torch.Tensor, with_lora: bool = True):

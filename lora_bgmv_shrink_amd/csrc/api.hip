@@ -392,7 +392,7 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
 
     if (m == LORA_MODE_BGMV && w_layout == LORA_W_OUT_IN && decode_ok(pool, n_rows)) {
         const DecodePlan D = plan_decode(P, n_rows, true);
-        DecodeArgs g;
+        DecodeArgs g{};
         g.x = x;
         g.ldx = ldx;
         g.W = W;
@@ -558,6 +558,36 @@ lora_status_t lora_decode_stream(lora_pool_t pool, const void* x, int64_t ldx, c
     g.ldx = ldx;
     g.W = W;
     g.ldw = ldw;
+    g.ids = ids;
+    g.n = n_rows;
+    g.with_lora = with_lora ? 1 : 0;
+    decode_carve(P, n_rows, D, ws, g);
+    return dev_status(launch_decode_stream(P, D, g, stream));
+}
+
+lora_status_t lora_decode_stream_q4(lora_pool_t pool, const void* x, int64_t ldx, const uint8_t* Wq,
+                                    int64_t ldq, const float* w_scale, int64_t lds, const int32_t* ids,
+                                    int32_t n_rows, int with_lora, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    if (!decode_ok(pool, n_rows)) return LORA_E_UNSUPPORTED;
+    const PoolDev& P = pool->dev;
+    if (!x || !Wq || !w_scale || !ids || ldx < P.d_in || ldq < P.d_in / 2 || lds < P.d_in / 128)
+        return LORA_E_INVALID;
+    if (P.d_in % 128 != 0) return LORA_E_UNSUPPORTED;
+    if (!al16(x) || !al16(Wq) || !ld_ok(ldx, P.d_in, 2) || ldq % 16 != 0 || ((uintptr_t)w_scale & 3u) != 0)
+        return LORA_E_UNSUPPORTED;
+    const DecodePlan D = plan_decode(P, n_rows, with_lora != 0);
+    if (!ws || !al16(ws) || ws_bytes < decode_ws_bytes(P, n_rows, D)) return LORA_E_WORKSPACE;
+    DecodeArgs g{};
+    g.x = x;
+    g.ldx = ldx;
+    g.W = Wq;
+    g.ldw = ldq;
+    g.w_q4 = 1;
+    g.wscale = w_scale;
+    g.lds = lds;
     g.ids = ids;
     g.n = n_rows;
     g.with_lora = with_lora ? 1 : 0;

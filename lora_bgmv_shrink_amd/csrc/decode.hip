@@ -52,6 +52,19 @@ __device__ __forceinline__ bf16x8_t ld8(const bf16* p, int valid, bool nt) {
     return u.v;
 }
 
+// Eight signed 4-bit weights (two's complement, element e in bits 4e..4e+3)
+// as bf16.  Integers in [-8, 7] are exact in fp32 and in bf16, so the high
+// half of the fp32 pattern is the bf16 value.
+__device__ __forceinline__ bf16x8_t dequant8_q4(uint32_t w) {
+    union { bf16x8_t v; bf16 e[8]; } u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int q = ((int)(w << (28 - 4 * e))) >> 28;
+        u.e[e] = (bf16)(__float_as_uint((float)q) >> 16);
+    }
+    return u.v;
+}
+
 // Shrink wave of workgroup (tn, ks): rows i = tn, tn + tiles_n, ...; for
 // each, part_t[ks][i][0:r] = x_i[slice] A_a[slice] over the staged x row, and
 // (slice 0) the row record for the finish pass.  A wave of its own, with its
@@ -144,7 +157,15 @@ __device__ __forceinline__ void shrink_wave(const PoolDev& P, const DecodePlan& 
 // block w (all of the slice's k-steps in flight, nontemporal: W is read once)
 // and keeps the whole 16-column partial; x of the slice is staged in LDS and
 // serves the MFMAs and the shrink wave.
-template <int MB, bool FULL, bool LORA>
+//
+// Q4: W holds signed 4-bit weights, row n of bytes at W + n * ldw (input k
+// in the low nibble when even), with scale wscale[n * lds + k / 128].  The
+// k order of a dot product is free, so lane group g = lane / 16 loads 16
+// bytes (32 inputs) per 128-input group j of the slice: inputs
+// j * 128 + g * 32 .. + 32, taken 8 at a time in four MFMA steps, with x read
+// from LDS at the same inputs.  The four steps of group j thus cover exactly
+// that group in every lane; its sums are scaled once and added.
+template <int MB, bool FULL, bool LORA, bool Q4>
 __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& D, const DecodeArgs& g, int b,
                                             uint8_t* lds) {
     const int tid = threadIdx.x;
@@ -162,7 +183,7 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
     const int lr = lane & 15;
     const int kq = (lane >> 4) * 8;
     const int n = tn * DS_COLS + wave * 16 + lr;
-    const bf16* Wt = (const bf16*)g.W + (int64_t)(n < N ? n : 0) * g.ldw;
+    const int nc = n < N ? n : 0;   // a column past d_out reads row 0; its output is never stored
 
     // x[0:16*MB][slice] -> LDS as [m][k] bf16, rows padded by 16 bytes.  The
     // x pieces are requested before W: they come from L2 and return first, so
@@ -193,16 +214,36 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
         }
     }
 
-    bf16x8_t bw[DS_USTEPS];
-    if constexpr (FULL) {
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NW = Q4 ? 1 : DS_USTEPS;
+    constexpr int NQ = Q4 ? DS_USTEPS / 4 : 1;
+    bf16x8_t bw[NW];
+    u32x4 wq[NQ];
+    float wsc[NQ];
+    // 4-bit: 128-input groups in the slice (klen is a multiple of 128)
+    const int ngrp = FULL ? DS_USTEPS / 4 : klen / 128;
+    if constexpr (Q4) {
+        const uint8_t* Wq = (const uint8_t*)g.W + (int64_t)nc * g.ldw + kbeg / 2 + (lane >> 4) * 16;
+        const float* Sc = g.wscale + (int64_t)nc * g.lds + kbeg / 128;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            if (FULL || j < ngrp) {
+                wq[j] = __builtin_nontemporal_load((const u32x4*)(Wq + j * 64));
+                wsc[j] = Sc[j];
+            } else {
+                wq[j] = u32x4{0u, 0u, 0u, 0u};
+                wsc[j] = 0.f;
+            }
+        }
+    } else if constexpr (FULL) {
+        const bf16* Wt = (const bf16*)g.W + (int64_t)nc * g.ldw;
 #pragma unroll
         for (int u = 0; u < DS_USTEPS; ++u) {
-            // a column past d_out reads row 0 (Wt is clamped); its output is never stored
             const u32x4 v = __builtin_nontemporal_load((const u32x4*)(Wt + kbeg + u * 32 + kq));
             bw[u] = __builtin_bit_cast(bf16x8_t, v);
         }
     } else {
+        const bf16* Wt = (const bf16*)g.W + (int64_t)nc * g.ldw;
 #pragma unroll
         for (int u = 0; u < DS_USTEPS; ++u) {
             const int k = kbeg + u * 32 + kq;
@@ -222,13 +263,36 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
     f32x4_t acc[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (Q4) {
 #pragma unroll
-    for (int u = 0; u < DS_USTEPS; ++u) {
-        if (FULL || u < nsteps) {
+        for (int j = 0; j < NQ; ++j) {
+            if (FULL || j < ngrp) {
+                f32x4_t ag[MB];
 #pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                const bf16x8_t a = *(const bf16x8_t*)(xs + (i * 16 + lr) * XLD + u * 32 + kq);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[u], acc[i], 0, 0, 0);
+                for (int i = 0; i < MB; ++i) ag[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                const int k0 = j * 128 + (lane >> 4) * 32;   // this lane's 32 inputs of group j
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const bf16x8_t b = dequant8_q4(wq[j][st]);
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) {
+                        const bf16x8_t a = *(const bf16x8_t*)(xs + (i * 16 + lr) * XLD + k0 + st * 8);
+                        ag[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, ag[i], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i) acc[i] += wsc[j] * ag[i];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < DS_USTEPS; ++u) {
+            if (FULL || u < nsteps) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const bf16x8_t a = *(const bf16x8_t*)(xs + (i * 16 + lr) * XLD + u * 32 + kq);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[u], acc[i], 0, 0, 0);
+                }
             }
         }
     }
@@ -248,7 +312,7 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
 
 // LORA: the workgroup has the shrink wave (the layer with its adapter term);
 // without it the stream is the base product alone.
-template <int MB, bool LORA>
+template <int MB, bool LORA, bool Q4 = false>
 __global__ __launch_bounds__(LORA ? DS_THREADS : DS_BASE_THREADS) void k_decode_stream(PoolDev P, DecodePlan D,
                                                                                     DecodeArgs g) {
     // staged x; sized over half a CU's LDS so that each CU runs one
@@ -258,8 +322,8 @@ __global__ __launch_bounds__(LORA ? DS_THREADS : DS_BASE_THREADS) void k_decode_
     // whose wait counts let x be staged while W is still arriving
     const int b = blockIdx.x;
     const int kbeg = (b / D.tiles_n) * D.kslice;
-    if (min(P.d_in, kbeg + D.kslice) - kbeg == DS_USTEPS * 32) stream_body<MB, true, LORA>(P, D, g, b, lds);
-    else stream_body<MB, false, LORA>(P, D, g, b, lds);
+    if (min(P.d_in, kbeg + D.kslice) - kbeg == DS_USTEPS * 32) stream_body<MB, true, LORA, Q4>(P, D, g, b, lds);
+    else stream_body<MB, false, LORA, Q4>(P, D, g, b, lds);
 }
 
 // Finish: workgroup (m, chunk) owns FIN_COLS columns of row m, 4 per thread.
@@ -389,6 +453,7 @@ DecodePlan plan_decode(const PoolDev& P, int32_t n_rows, bool with_lora) {
     const int want = (int)std::max<int64_t>(1, ceil_div(256, D.tiles_n));
     int steps = (int)ceil_div(ksteps, want);
     steps = std::max(1, std::min(steps, DS_USTEPS));
+    steps = (int)ceil_div(steps, 4) * 4;   // whole groups of 128 k-rows (the 4-bit scale groups)
     D.kslice = steps * 32;
     D.base_slices = (int32_t)ceil_div(K, D.kslice);
     D.base_wgs = D.tiles_n * D.base_slices;
@@ -419,7 +484,14 @@ hipError_t launch_decode_stream(const PoolDev& P, const DecodePlan& D, const Dec
     dim3 grid((unsigned)D.base_wgs);
     const int MB = g.n <= 16 ? 1 : (g.n <= 32 ? 2 : 4);
 #define LORA_DS(mb)                                                                                        \
-    if (g.with_lora)                                                                                       \
+    if (g.w_q4) {                                                                                          \
+        if (g.with_lora)                                                                                   \
+            hipLaunchKernelGGL((k_decode_stream<mb, true, true>), grid, dim3(DS_THREADS), 0, stream, P, D, \
+                               g);                                                                         \
+        else                                                                                               \
+            hipLaunchKernelGGL((k_decode_stream<mb, false, true>), grid, dim3(DS_BASE_THREADS), 0, stream, \
+                               P, D, g);                                                                   \
+    } else if (g.with_lora)                                                                                \
         hipLaunchKernelGGL((k_decode_stream<mb, true>), grid, dim3(DS_THREADS), 0, stream, P, D, g);       \
     else                                                                                                   \
         hipLaunchKernelGGL((k_decode_stream<mb, false>), grid, dim3(DS_BASE_THREADS), 0, stream, P, D, g)

@@ -181,7 +181,7 @@ hipError_t launch_merge(const PoolDev& P, lora_dtype_t dt, int32_t adapter, floa
 constexpr int DS_LDS_BYTES = 84 * 1024;   // > half a CU: one stream workgroup per CU
 struct DecodePlan {
     int32_t tiles_n;      // 128-column base tiles
-    int32_t kslice;       // k-rows per slice (multiple of 32, at most 512)
+    int32_t kslice;       // k-rows per slice (multiple of 128, at most 512)
     int32_t base_slices;  // partial base products per output
     int32_t base_wgs;     // tiles_n * base_slices
     int32_t t_slices;     // partial shrink sums per row (base_slices, or 0 without the LoRA term)
@@ -194,8 +194,11 @@ struct RowRec {
 struct DecodeArgs {
     const void* x;
     int64_t ldx;
-    const void* W;
-    int64_t ldw;
+    const void* W;      // bf16 [d_out, ldw], or (w_q4) 4-bit bytes [d_out, ldw]
+    int64_t ldw;        // elements, or bytes for a 4-bit W
+    int32_t w_q4;       // W holds signed 4-bit weights with per-128-input scales
+    const float* wscale;   // w_q4: [d_out, lds] fp32
+    int64_t lds;
     const int32_t* ids;
     int32_t n;
     int32_t with_lora;

@@ -439,3 +439,21 @@ def eight_b_parts(layers: int = 32):
     one = [(4096, 4096), (4096, 1024), (4096, 1024), (4096, 4096), (4096, 14336), (4096, 14336),
            (14336, 4096)]
     return one * layers
+
+
+def q4_weight(seed: int, d_in: int, d_out: int, device="cuda", pow2_scales: bool = False):
+    """A 4-bit base weight in the layout lora_decode_stream_q4 reads: bytes
+    Wq [d_out, d_in / 2] with uniformly drawn nibbles (signed values -8..7)
+    and fp32 scales [d_out, d_in / 128] drawn so that q * scale has about the
+    spread of the bf16 weights here (std ~ 1/64).  With ``pow2_scales`` every
+    scale is a power of two (each weight is then exact in bf16)."""
+    g = _gen(device, 5000 + seed)
+    Wq = torch.randint(0, 256, (d_out, d_in // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    n_g = d_in // 128
+    if pow2_scales:
+        e = torch.randint(-10, -7, (d_out, n_g), generator=g, device=device, dtype=torch.int32)
+        sc = torch.pow(2.0, e.to(torch.float32))
+    else:
+        u = torch.rand((d_out, n_g), generator=g, device=device, dtype=torch.float32)
+        sc = (0.5 + u) / (64.0 * 4.6)
+    return Wq.contiguous(), sc.contiguous()

@@ -1,0 +1,127 @@
+"""Decode over a 4-bit base weight (lora_decode_stream_q4 + lora_decode_finish)
+against the fp64 oracle on the widened weight, through the C ABI.
+
+The weight format is the reading stated in include/lora_mi355x.h (signed
+nibbles, one fp32 scale per output and 128 inputs); the oracle widens it with
+its own plain loop (pinned in test_oracle_pins.py).  x and the adapters are
+bf16 with fp32 accumulation: |gpu - oracle| <= 2e-2 * max(1, |oracle|).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import TOL, assert_close, binding, pool_of, requires_gpu, say
+from _marshal import f64, oracle_pool
+from lora_bgmv_shrink_amd import workloads as wl
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+DEV = "cuda"
+
+
+def _run_q4(b, pool, x, Wq, sc, ids, with_lora):
+    n = ids.numel()
+    ws = torch.zeros(b.lora_decode_workspace(pool, n, with_lora), dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, pool.d_out), dtype=torch.bfloat16, device=DEV)
+    b.lora_decode_stream_q4(pool, x, Wq, sc, ids, ws, with_lora)
+    b.lora_decode_finish(pool, ids, ws, y, with_lora)
+    torch.cuda.synchronize()
+    return y
+
+
+def _oracle_y(x, Wq, sc, ids_np, op, d_in, with_lora):
+    W = oracle.dequant_q4(Wq.cpu().numpy(), sc.cpu().double().numpy(), d_in)
+    ids_o = ids_np if with_lora else np.full_like(ids_np, -1)
+    return oracle.layer(f64(x), W, ids_o, op, want=("y",))["y"]
+
+
+@pytest.mark.parametrize("d_in,d_out", [(1024, 776), (4096, 1024), (1536, 2048)])
+@pytest.mark.parametrize("n_rows", [1, 7, 32, 64])
+@pytest.mark.parametrize("with_lora", [True, False])
+def test_q4_decode_matches_oracle(d_in, d_out, n_rows, with_lora):
+    say(f"q4 decode: {d_in}->{d_out}, {n_rows} rows, lora {with_lora}")
+    b = binding()
+    w = wl.small_batch(seed=11, n_rows=n_rows, d_in=d_in, d_out=d_out, n_adapters=6, ranks=16,
+                       dtype=torch.bfloat16, device=DEV, frac_base=0.15)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    op, _ = oracle_pool(p.pool)
+    Wq, sc = wl.q4_weight(1, d_in, d_out, DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y = _run_q4(b, pool, p.x, Wq, sc, ids, with_lora)
+    ref = _oracle_y(p.x, Wq, sc, w.ids, op, d_in, with_lora)
+    assert_close(y, ref, TOL[torch.bfloat16], "q4 decode")
+
+
+def test_q4_agrees_with_bf16_decode_on_exact_weights():
+    """Power-of-two scales make every 4-bit weight exact in bf16: the 4-bit
+    path and the bf16 decode path then compute the same layer."""
+    b = binding()
+    d_in, d_out, n = 2048, 1024, 24
+    w = wl.small_batch(seed=12, n_rows=n, d_in=d_in, d_out=d_out, n_adapters=5, ranks=32,
+                       dtype=torch.bfloat16, device=DEV, frac_base=0.1)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    Wq, sc = wl.q4_weight(2, d_in, d_out, DEV, pow2_scales=True)
+    Wd = oracle.dequant_q4(Wq.cpu().numpy(), sc.cpu().double().numpy(), d_in)     # [d_in, d_out]
+    Wb = torch.from_numpy(Wd.T.copy()).to(torch.bfloat16).to(DEV)                  # stored [d_out, d_in]
+    assert np.array_equal(Wb.double().cpu().numpy().T, Wd)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y4 = _run_q4(b, pool, p.x, Wq, sc, ids, True)
+    yb = b.lora_layer_apply(pool, p.x, Wb, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV)
+    torch.cuda.synchronize()
+    op, _ = oracle_pool(p.pool)
+    ref = oracle.layer(f64(p.x), Wd, w.ids, op, want=("y",))["y"]
+    assert_close(y4, ref, TOL[torch.bfloat16], "q4 vs oracle")
+    assert_close(yb, ref, TOL[torch.bfloat16], "bf16 vs oracle")
+    d = (y4.float() - yb.float()).abs().max().item()
+    say(f"  max |q4 - bf16| = {d:.3e}")
+    assert d <= 2e-2 * max(1.0, yb.float().abs().max().item())
+
+
+def test_q4_decode_q_proj_full_size():
+    """The 8B q projection decode batch (4096 -> 4096, 32 rows, 20 adapters,
+    pool of 250) on a 4-bit base: every output against the oracle, and the
+    run is bit-identical when repeated."""
+    b = binding()
+    w = wl.decode_q_proj(device=DEV)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    Wq, sc = wl.q4_weight(3, 4096, 4096, DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y = _run_q4(b, pool, p.x, Wq, sc, ids, True)
+    y2 = _run_q4(b, pool, p.x, Wq, sc, ids, True)
+    assert torch.equal(y, y2)
+    used = sorted(set(int(a) for a in w.ids if a >= 0))
+    op, mp = oracle_pool(p.pool, used=used)
+    from _marshal import remap_ids
+    ref = _oracle_y(p.x, Wq, sc, remap_ids(w.ids, mp, p.pool.n_adapters), op, 4096, True)
+    assert_close(y, ref, TOL[torch.bfloat16], "q4 q_proj")
+
+
+def test_q4_argument_checks():
+    b = binding()
+    w = wl.small_batch(seed=1, n_rows=4, d_in=1024, d_out=256, n_adapters=2, ranks=16, dtype=torch.bfloat16,
+                       device=DEV)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    Wq, sc = wl.q4_weight(4, 1024, 256, DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    ws = torch.zeros(b.lora_decode_workspace(pool, 4, True), dtype=torch.uint8, device=DEV)
+    with pytest.raises(b.LoraError) as e:           # scales for fewer groups than d_in needs
+        b.lora_decode_stream_q4(pool, p.x, Wq, sc[:, :4].contiguous(), ids, ws, True)
+    assert e.value.status == b.LORA_E_INVALID
+    with pytest.raises(b.LoraError) as e:           # rows shorter than d_in / 2 bytes
+        b.lora_decode_stream_q4(pool, p.x, Wq[:, :511].contiguous(), sc, ids, ws, True)
+    assert e.value.status == b.LORA_E_INVALID
+    w2 = wl.small_batch(seed=1, n_rows=4, d_in=1000, d_out=256, n_adapters=2, ranks=16, dtype=torch.bfloat16,
+                        device=DEV)
+    pool2 = pool_of(w2.projections[0].pool)
+    Wq2 = torch.zeros((256, 512), dtype=torch.uint8, device=DEV)
+    sc2 = torch.ones((256, 8), dtype=torch.float32, device=DEV)
+    with pytest.raises(b.LoraError) as e:           # d_in not a multiple of 128
+        b.lora_decode_stream_q4(pool2, w2.projections[0].x, Wq2, sc2, ids, ws, True)
+    assert e.value.status == b.LORA_E_UNSUPPORTED
