@@ -210,3 +210,69 @@ def test_many_parts_offsets():
             ref = oracle.layer(f64(outs[p][0]), f64(Ws[p]), ids, _oracle_pool(aset, p), want=("y",))["y"]
             assert_close(outs[p][1], ref, TOL[torch.bfloat16], f"adapters {used} part {p}")
     c.destroy()
+
+
+def test_serving_loop_outputs_match_oracle():
+    """Admission, paging and the layer together: Zipf requests over 40
+    adapters, 8 slots, at most 2 loads in flight, batches of up to 24 rows.
+    Every admitted batch is mapped to slots and run; its outputs must equal
+    the oracle run with the original adapter ids (deferred requests wait for
+    their adapter, nothing blocks)."""
+    b = binding()
+    parts = [(512, 384)]
+    n_ad = 40
+    ranks = [8, 16, 32, 64] * (n_ad // 4)
+    scales = np.linspace(0.25, 3.0, n_ad).astype(np.float32)
+    aset = wl.adapter_set(parts, ranks, scales, seed=21)
+    c = _cache_for(aset, n_slots=8, max_loads=2)
+    sch = b.Scheduler(n_ad, 1.0, 0.35, max_adapters=6, max_rows=24, cache=c)
+    op = _oracle_pool(aset, 0)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(31)
+    W = (torch.randn(512, 384, generator=g) / 16).to(torch.bfloat16)
+    Wd = W.t().contiguous().to(DEV)
+    rng = np.random.default_rng(8)
+    p = 1.0 / np.arange(1, n_ad + 1) ** 1.1
+    p /= p.sum()
+    rid, checked, deferred = 0, 0, 0
+    for step in range(60):
+        for _ in range(int(rng.poisson(20))):
+            a = -1 if rng.random() < 0.1 else int(rng.choice(n_ad, p=p))
+            sch.submit(rid, a, 1, step + rng.random())
+            rid += 1
+        (req, ad, rw, wt), info = sch.step(float(step + 1), 24)
+        deferred += info["deferred_not_resident"]
+        if len(ad) == 0:
+            c.wait()
+            continue
+        slots = c.map(ad)
+        x = torch.randn(len(ad), 512, generator=g).to(torch.bfloat16)
+        y = b.lora_layer_apply(c.pool(0), x.to(DEV), Wd, torch.as_tensor(slots, device=DEV),
+                               w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV)
+        c.release()
+        torch.cuda.synchronize()
+        ref = oracle.layer(f64(x), f64(W), ad.astype(np.int32), op, want=("y",))["y"]
+        assert_close(y, ref, TOL[torch.bfloat16], f"serving step {step}")
+        checked += len(ad)
+        if step % 3 == 0:
+            c.wait()        # let loads finish now and then, as steps would
+    s = c.stats()
+    say(f"  serving: {checked} rows checked, {deferred} deferrals, cache {s}")
+    assert checked > 600 and deferred > 0 and s["evictions"] > 0
+    sch.destroy()
+    c.destroy()
+
+
+def test_destroy_with_loads_in_flight():
+    """Destroying a cache while copies are still queued waits for them
+    (no use of freed memory), and a new cache works afterwards."""
+    b = binding()
+    aset = wl.adapter_set([(1024, 1024)], [64] * 6, [1.0] * 6, seed=2)
+    c = _cache_for(aset, n_slots=6, max_loads=6)
+    for a in range(6):
+        assert c.request(a) == b.LORA_CACHE_LOADING
+    c.destroy()
+    c2 = _cache_for(aset, n_slots=2, max_loads=1)
+    _make_resident(c2, [3])
+    assert c2.slot_of(3) >= 0
+    c2.destroy()
