@@ -25,6 +25,8 @@ The JSON line carries:
                mixed-rank 70B ragged and padded), measured the same way
   merge        the merge kernel's HBM GB/s (W += s A B in place)
   q4_decode    the headline decode batch over a 4-bit base weight
+  adapter_term_prefill  the SGMV shrink and expand of the 70B prefill batch
+               on their own: algorithmic HBM GB/s against the 8 TB/s peak
   paging       the adapter slot cache: cold-load latency and H2D GB/s of
                whole 8B-shaped adapters, decode step time with loads in flight
   serving      a Zipf decode serving loop through the admission scheduler and
@@ -652,6 +654,53 @@ def bench_q4_decode(torch, args):
     return out
 
 
+def bench_sgmv_adapter_term(torch, args):
+    """The adapter term of the 70B prefill batch on its own (13,894 rows in
+    arrival order, 8 rank-64 adapters, q and o projections 8192 -> 8192):
+    lora_sgmv_shrink (t = x A per segment, K split over its workspace) and
+    lora_sgmv_expand accumulating
+    s t B into y, each graph-replayed alternately over the two projections
+    (x and y of one are 228 MB, so the pair exceeds the Infinity Cache).
+    Algorithmic bytes: shrink = x + the distinct A blocks + t; expand = t +
+    the distinct B blocks + y read and written."""
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.prefill_70b(device=dev, projections=["q", "o"])
+    n = w.n_rows
+    ids = torch.as_tensor(w.ids, device=dev)
+    pr = []
+    for pp in w.projections:
+        pp.W = None
+        h = make_pool(b, pp.pool)
+        pr.append(dict(p=pp, h=h, t=torch.zeros((n, pp.pool.r_max), dtype=torch.float32, device=dev),
+                       y=torch.zeros((n, pp.d_out), dtype=torch.bfloat16, device=dev)))
+    seg = b.lora_segments_build(ids, pr[0]["p"].pool.n_adapters)
+    for r in pr:   # K-split partial sums of the shrink (no zeroing needed)
+        r["ws"] = torch.empty(max(1, b.lora_sgmv_shrink_workspace(r["h"], n)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    g_shr = capture(torch, lambda: [b.lora_sgmv_shrink(r["h"], r["p"].x, seg, t=r["t"], ws=r["ws"]) for r in pr])
+    g_exp = capture(torch, lambda: [b.lora_sgmv_expand(r["h"], r["t"], seg, y=r["y"], accumulate=True) for r in pr])
+    reps = max(4, args.extra_steps)
+    d_shr = time_graph(torch, g_shr, reps) / len(pr)
+    d_exp = time_graph(torch, g_exp, reps) / len(pr)
+    pool = pr[0]["p"].pool
+    bA, U = distinct_bytes(pool, w.ids, "A")
+    bB, _ = distinct_bytes(pool, w.ids, "B")
+    d_in, d_out, r = pool.d_in, pool.d_out, pool.r_max
+    shr_bytes = n * d_in * 2 + bA + n * r * 4
+    exp_bytes = n * r * 4 + bB + 2 * n * d_out * 2
+    out = dict(workload="prefill_sgmv_70b_q_o_r64_rows%d" % n, rows=n, distinct_adapters=U,
+               sgmv_shrink=dict(us=round(d_shr * 1e6, 2), bytes=shr_bytes, GBps=round(shr_bytes / d_shr / 1e9, 1),
+                                frac_hbm=round(shr_bytes / d_shr / 1e9 / HBM_PEAK_GBS, 4)),
+               sgmv_expand=dict(us=round(d_exp * 1e6, 2), bytes=exp_bytes, GBps=round(exp_bytes / d_exp / 1e9, 1),
+                                frac_hbm=round(exp_bytes / d_exp / 1e9 / HBM_PEAK_GBS, 4)))
+    del g_shr, g_exp, pr
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_merge(torch, args):
     """lora_merge_adapter (W += s A_a B_a in place) on 8B and 70B q_proj
     shapes: merges then unmerges over 4 weight replicas (more than the
@@ -713,6 +762,8 @@ def main():
     merge = bench_merge(torch, args)
     log("bench: 4-bit base decode ...")
     q4 = bench_q4_decode(torch, args)
+    log("bench: SGMV adapter term (prefill) ...")
+    sgmv = bench_sgmv_adapter_term(torch, args)
     decode = dec.pop("_decode_graph")
     paging = serving = None
     if not args.no_paging:
@@ -753,6 +804,7 @@ def main():
         "workloads": extra,
         "merge": merge,
         "q4_decode": q4,
+        "adapter_term_prefill": sgmv,
         "paging": paging,
         "serving": serving,
     }

@@ -193,14 +193,24 @@ lora_status_t lora_bgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
 /* SGMV: rows grouped by adapter, one small product per segment (prefill) */
 /* ---------------------------------------------------------------------- */
 
+/* Workspace bytes with which lora_sgmv_shrink splits K for this batch size
+ * (0: it does not split).  No zero-filling is needed. */
+lora_status_t lora_sgmv_shrink_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes);
+
 /* Shrink over segments from lora_segments_build (same t layout and values
  * as lora_bgmv_shrink: original row order).  Rows of the base-only run get
  * t = 0.  Id-range errors are reported by lora_segments_build's `status`.
  * The grid is sized from n_rows and the pool size, so the segment count
- * never has to come back to the host. */
+ * never has to come back to the host.  With a workspace of
+ * lora_sgmv_shrink_workspace bytes, K is cut into slices whose fp32 partial
+ * sums a second launch adds in slice order (results do not depend on
+ * timing, but differ from the unsplit form in rounding); with ws = NULL
+ * every workgroup walks all of K.  A non-NULL ws that is too small or not
+ * 16-byte aligned is LORA_E_WORKSPACE. */
 lora_status_t lora_sgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
                                const lora_segments_t* seg, int32_t n_rows,
-                               float* t, int64_t ldt, hipStream_t stream);
+                               float* t, int64_t ldt, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
 
 /* Expand over segments (same semantics as lora_bgmv_expand). */
 lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,

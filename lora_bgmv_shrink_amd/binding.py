@@ -36,7 +36,7 @@ EXPORTS = [
     "lora_status_string", "lora_adapter_param_count", "lora_pool_ragged_offsets", "lora_pool_create",
     "lora_pool_destroy", "lora_pool_param_count", "lora_pool_last_error", "lora_workspace_clear",
     "lora_segments_workspace", "lora_segments_build", "lora_bgmv_shrink_workspace", "lora_bgmv_shrink",
-    "lora_bgmv_expand", "lora_sgmv_shrink", "lora_sgmv_expand", "lora_layer_workspace",
+    "lora_bgmv_expand", "lora_sgmv_shrink_workspace", "lora_sgmv_shrink", "lora_sgmv_expand", "lora_layer_workspace",
     "lora_layer_apply", "lora_base_gemm_expand_workspace", "lora_base_gemm_expand", "lora_decode_workspace",
     "lora_decode_stream",
     "lora_decode_finish", "lora_merge_adapter",
@@ -98,7 +98,8 @@ def _load():
         "lora_bgmv_shrink_workspace": (st, [p, i32, p]),
         "lora_bgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p, sz, p]),
         "lora_bgmv_expand": (st, [p, p, i64, p, i32, p, st, i64, ctypes.c_int, p]),
-        "lora_sgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p]),
+        "lora_sgmv_shrink_workspace": (st, [p, i32, p]),
+        "lora_sgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p, sz, p]),
         "lora_sgmv_expand": (st, [p, p, i64, p, i32, p, st, i64, ctypes.c_int, p]),
         "lora_layer_workspace": (st, [p, i32, st, p]),
         "lora_layer_apply": (st, [p, p, i64, p, i64, st, p, p, i32, p, st, i64, st, p, sz, p]),
@@ -352,12 +353,24 @@ def lora_bgmv_expand(pool: Pool, t: torch.Tensor, ids: torch.Tensor, y: Optional
     return y
 
 
-def lora_sgmv_shrink(pool: Pool, x: torch.Tensor, seg: Segments, t: Optional[torch.Tensor] = None) -> torch.Tensor:
+def lora_sgmv_shrink_workspace(pool: Pool, n_rows: int) -> int:
+    v = ctypes.c_size_t()
+    _check(_lib.lora_sgmv_shrink_workspace(pool.handle, n_rows, ctypes.byref(v)), "lora_sgmv_shrink_workspace")
+    return v.value
+
+
+def lora_sgmv_shrink(pool: Pool, x: torch.Tensor, seg: Segments, t: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
+    """With ``split`` (and no ``ws`` given) a workspace of the size the
+    library asks for is allocated, so K is split when it pays."""
     n = x.shape[0]
     t = _t_out(pool, n, t, x.device)
+    if ws is None and split:
+        ws = _workspace(lora_sgmv_shrink_workspace(pool, n), x.device)
     cs = seg.c_struct()
-    _check(_lib.lora_sgmv_shrink(pool.handle, _ptr(x), _ld(x), ctypes.byref(cs), n, _ptr(t), _ld(t),
-                                 ctypes.c_void_p(_stream(x.device))), "lora_sgmv_shrink")
+    _check(_lib.lora_sgmv_shrink(pool.handle, _ptr(x), _ld(x), ctypes.byref(cs), n, _ptr(t), _ld(t), _ptr(ws),
+                                 0 if ws is None else ws.numel(), ctypes.c_void_p(_stream(x.device))),
+           "lora_sgmv_shrink")
     return t
 
 

@@ -310,9 +310,15 @@ lora_status_t lora_bgmv_expand(lora_pool_t pool, const float* t, int64_t ldt, co
                                          accumulate ? 1 : 0, true, stream));
 }
 
+lora_status_t lora_sgmv_shrink_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes) {
+    if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
+    *bytes = sgmv_shrink_part_bytes(pool->dev, n_rows);
+    return LORA_OK;
+}
+
 lora_status_t lora_sgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
                                const lora_segments_t* seg, int32_t n_rows, float* t, int64_t ldt,
-                               hipStream_t stream) {
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
     if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
     if (n_rows == 0) return LORA_OK;
     const int eb = elem_bytes(pool->dtype);
@@ -320,8 +326,15 @@ lora_status_t lora_sgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
     lora_status_t st = check_segments(seg, n_rows, pool->dev.n_adapters);
     if (st != LORA_OK) return st;
     if (!al16(x) || !ld_ok(ldx, pool->dev.d_in, eb)) return LORA_E_UNSUPPORTED;
+    const size_t need = sgmv_shrink_part_bytes(pool->dev, n_rows);
+    float* part = nullptr;
+    if (ws) {
+        if (!al16(ws) || ws_bytes < need) return LORA_E_WORKSPACE;
+        if (need > 0) part = (float*)ws;
+    }
     return dev_status(launch_sgmv_shrink(pool->dev, pool->dtype, x, ldx, seg, n_rows,
-                                         pool->dev.n_adapters + 1, t, ldt, true, stream));
+                                         pool->dev.n_adapters + 1, t, ldt, true, stream, nullptr, 0,
+                                         nullptr, part));
 }
 
 lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,

@@ -105,7 +105,7 @@ def test_validation_before_any_device_work():
     # hot calls with a null pool
     assert lib.lora_bgmv_shrink(None, fake, 64, fake, 4, fake, 16, None, 0, None) == b.LORA_E_INVALID
     assert lib.lora_bgmv_expand(None, fake, 16, fake, 4, fake, 1, 64, 0, None) == b.LORA_E_INVALID
-    assert lib.lora_sgmv_shrink(None, fake, 64, None, 4, fake, 16, None) == b.LORA_E_INVALID
+    assert lib.lora_sgmv_shrink(None, fake, 64, None, 4, fake, 16, None, 0, None) == b.LORA_E_INVALID
     assert lib.lora_sgmv_expand(None, fake, 16, None, 4, fake, 1, 64, 0, None) == b.LORA_E_INVALID
     assert lib.lora_layer_apply(None, fake, 64, fake, 64, 0, fake, None, 4, fake, 1, 64, 0, None, 0, None) == b.LORA_E_INVALID
     # segments: bad sizes, missing descriptor, too-small capacity, too many adapters

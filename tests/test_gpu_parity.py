@@ -150,6 +150,37 @@ def test_shrink(name, mode):
     assert np.all(t.cpu().numpy()[base] == 0)
 
 
+@pytest.mark.parametrize("ranks", [16, [8, 16, 32, 64, 24, 8]])
+@pytest.mark.parametrize("split", [True, False])
+def test_sgmv_shrink_split_and_unsplit(ranks, split):
+    """The standalone SGMV shrink with its K-split workspace and without
+    (ws = NULL), on a shape where the split gives 4 slices: both match the
+    oracle, columns past each rank and base-only rows are exactly 0, and a
+    repeated call is bit-identical."""
+    say(f"sgmv shrink split={split} ranks={ranks}")
+    b = binding()
+    layout = wl.UNIFORM if isinstance(ranks, int) else wl.RAGGED
+    w = wl.small_batch(seed=21, n_rows=300, d_in=4096, d_out=256, n_adapters=6, ranks=ranks, layout=layout,
+                       dtype=torch.bfloat16, device="cuda", run_lengths=[40, 3, 77, 1, 120, 59])
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    if split:
+        assert b.lora_sgmv_shrink_workspace(pool, w.n_rows) > 0
+    seg = b.lora_segments_build(ids, p.pool.n_adapters)
+    t = b.lora_sgmv_shrink(pool, p.x, seg, split=split)
+    t2 = b.lora_sgmv_shrink(pool, p.x, seg, split=split)
+    torch.cuda.synchronize()
+    assert torch.equal(t, t2)
+    o = run_oracle(w, want=("t",))
+    assert_close(t, o["t"], TOL[torch.bfloat16], f"t split={split}")
+    tn = t.cpu().numpy()
+    assert np.all(tn[w.ids == -1] == 0)
+    for i, a in enumerate(w.ids.tolist()):
+        if a >= 0:
+            assert np.all(tn[i, int(p.pool.ranks[a]):] == 0)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("mode", ["bgmv", "sgmv"])
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
