@@ -1377,22 +1377,46 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
 
     Acc<C> acc;
     acc.zero();
-    RowLoader<C, C::BM> la;
-    TransLoader<C, C::BN> lb;
+    // Two K-blocks in flight: even blocks go through register set 0 and LDS
+    // stage 0, odd blocks through set 1 and stage 1; block kb + 2 is
+    // requested as soon as block kb is in LDS, so each wave waits on memory
+    // once per two blocks' worth of loads.  One barrier per block: a wave
+    // that writes a stage has passed the barrier after which every wave is
+    // done with the block that stage held before.
+    RowLoader<C, C::BM> la0, la1;
+    TransLoader<C, C::BN> lb0, lb1;
     const int nk = (kend - kbeg + C::BK - 1) / C::BK;
-    la.load(x, ldx, sRow, kbeg, kend, tid);
-    lb.load(Au, r, kbeg, kend, 0, r, vec, tid);
-    for (int kb = 0; kb < nk; ++kb) {
-        T* sA = smem + (kb & 1) * C::STAGE;
-        T* sB = sA + C::A_ELEMS;
-        la.store(sA, tid);
-        lb.store(sB, tid);
-        __syncthreads();
-        if (kb + 1 < nk) {
-            la.load(x, ldx, sRow, kbeg + (kb + 1) * C::BK, kend, tid);
-            lb.load(Au, r, kbeg + (kb + 1) * C::BK, kend, 0, r, vec, tid);
+    la0.load(x, ldx, sRow, kbeg, kend, tid);
+    lb0.load(Au, r, kbeg, kend, 0, r, vec, tid);
+    if (nk > 1) {
+        la1.load(x, ldx, sRow, kbeg + C::BK, kend, tid);
+        lb1.load(Au, r, kbeg + C::BK, kend, 0, r, vec, tid);
+    }
+    for (int kb = 0; kb < nk; kb += 2) {
+        {
+            T* sA = smem;
+            T* sB = sA + C::A_ELEMS;
+            la0.store(sA, tid);
+            lb0.store(sB, tid);
+            __syncthreads();
+            if (kb + 2 < nk) {
+                la0.load(x, ldx, sRow, kbeg + (kb + 2) * C::BK, kend, tid);
+                lb0.load(Au, r, kbeg + (kb + 2) * C::BK, kend, 0, r, vec, tid);
+            }
+            mma_block<C>(acc, sA, sB, wm, wn, lane);
         }
-        mma_block<C>(acc, sA, sB, wm, wn, lane);
+        if (kb + 1 < nk) {
+            T* sA = smem + C::STAGE;
+            T* sB = sA + C::A_ELEMS;
+            la1.store(sA, tid);
+            lb1.store(sB, tid);
+            __syncthreads();
+            if (kb + 3 < nk) {
+                la1.load(x, ldx, sRow, kbeg + (kb + 3) * C::BK, kend, tid);
+                lb1.load(Au, r, kbeg + (kb + 3) * C::BK, kend, 0, r, vec, tid);
+            }
+            mma_block<C>(acc, sA, sB, wm, wn, lane);
+        }
     }
 
     const int lc = lane % C::BLK;
