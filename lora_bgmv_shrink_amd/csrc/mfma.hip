@@ -531,92 +531,6 @@ struct TransLoader {
     }
 };
 
-// LoRA expand as extra K-steps on the accumulator.  For every distinct
-// adapter u among the tile's rows (ascending id), the tile is extended by
-//   A-side: s_u * t[row][j] for rows with id u, 0 elsewhere   (BM x r_u)
-//   B-side: B_u[j][n0 + n]                                   (r_u x BN)
-// bf16 operands carry the fp32 s*t as hi + lo bf16 halves against B_u
-// twice, so the intermediate keeps ~16 significant bits.  sId[m] holds the
-// row's adapter id or INT_MAX (base-only, invalid or past the end); sRow[m]
-// is the row's index into t.
-template <class C>
-__device__ void lora_kext(Acc<C>& acc, const PoolDev& P, const float* __restrict__ t, int64_t ldt,
-                          const int* sRow, const int* sId, int* sNext, typename C::T* smem, int n0,
-                          int tid, int wm, int wn, int lane) {
-    using T = typename C::T;
-    constexpr bool HL = sizeof(T) == 2;
-    T* sA = smem;
-    T* sB = smem + C::A_ELEMS;
-    const int d_out = P.d_out;
-    int prev = -1;
-    for (;;) {
-        if (tid == 0) *sNext = INT_MAX;
-        __syncthreads();
-        for (int m = tid; m < C::BM; m += C::NT) {
-            const int v = sId[m];
-            if (v > prev && v != INT_MAX) atomicMin(sNext, v);
-        }
-        __syncthreads();
-        const int u = *sNext;
-        if (u == INT_MAX) break;
-        const int r = P.ranks[u];
-        const float sc = P.scales[u];
-        const T* Bu = (const T*)P.B + P.b_off[u];
-        for (int j0 = 0; j0 < r; j0 += C::KH) {
-            // A side: s_u * t for rows of adapter u (all loads of the batch first)
-            constexpr int NA = (C::BM * C::KH + C::NT - 1) / C::NT;
-            float av[NA];
-#pragma unroll
-            for (int q = 0; q < NA; ++q) {
-                const int idx = tid + q * C::NT;
-                const int m = idx / C::KH;
-                const int j = j0 + (idx - m * C::KH);
-                av[q] = (idx < C::BM * C::KH && sId[m] == u && j < r) ? t[(int64_t)sRow[m] * ldt + j] : 0.f;
-            }
-#pragma unroll
-            for (int q = 0; q < NA; ++q) {
-                const int idx = tid + q * C::NT;
-                if (idx >= C::BM * C::KH) break;
-                const int m = idx / C::KH;
-                const int kk = idx - m * C::KH;
-                const float v = sc * av[q];
-                if constexpr (HL) {
-                    const bf16 hi = f32_to_bf16(v);
-                    const bf16 lo = f32_to_bf16(v - to_f32(hi));
-                    sA[m * C::LDK + kk] = (T)hi;
-                    sA[m * C::LDK + C::KH + kk] = (T)lo;
-                } else {
-                    sA[m * C::LDK + kk] = (T)v;
-                }
-            }
-            // B side: B_u[j][n0 + n], transposed into [n][j]
-            constexpr int NB = (C::KH * C::BN + C::NT - 1) / C::NT;
-            T bv[NB];
-#pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const int idx = tid + q * C::NT;
-                const int kk = idx / C::BN;
-                const int nn = idx - kk * C::BN;
-                const int j = j0 + kk;
-                const int col = n0 + nn;
-                bv[q] = (idx < C::KH * C::BN && j < r && col < d_out) ? Bu[(int64_t)j * d_out + col] : (T)0;
-            }
-#pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const int idx = tid + q * C::NT;
-                if (idx >= C::KH * C::BN) break;
-                const int kk = idx / C::BN;
-                const int nn = idx - kk * C::BN;
-                sB[nn * C::LDK + kk] = bv[q];
-                if constexpr (HL) sB[nn * C::LDK + C::KH + kk] = bv[q];
-            }
-            __syncthreads();
-            mma_block<C>(acc, sA, sB, wm, wn, lane);
-            __syncthreads();
-        }
-        prev = u;
-    }
-}
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -1485,37 +1399,62 @@ __global__ __launch_bounds__(256) void k_shrink_reduce(PoolDev P, const float* _
 }
 
 // ---------------------------------------------------------------------------
-// SGMV expand: y[rows of segment, n-tile] (+)= s_u * t[rows] B_u
+// SGMV expand: y[rows of segment tile] (+)= s_u * t[rows] B_u
 // ---------------------------------------------------------------------------
+//
+// Per output element the expand does r <= 64 multiply-adds and moves y once
+// (read and written when accumulating): a stream of y whose product belongs
+// on the matrix cores (at rank 64 it would take the fp32 vector units longer
+// than the stream).  Workgroup (tile, chunk) owns up to 64 rows of one
+// segment and EXP_SPAN output columns, taken 128 at a time:
+//   - the A side is s_u * t of the tile's rows as bf16 pairs (hi, lo) with
+//     hi + lo = s_u * t to about 16 significant bits, in blocks of 32 ranks
+//     laid [hi(32) | lo(32)] along K; the B side holds each rank row of B_u
+//     twice (against hi and against lo), staged transposed as [column][K];
+//   - 4 waves, each 64 rows x 32 columns of 16x16x32 bf16 MFMAs;
+//   - the fp32 tile then goes through LDS so that y moves in 16-byte pieces,
+//     read and written once, rounded once.
+// Each workgroup sums its ranks in a fixed order: results do not depend on
+// timing.  Only the bf16 pool dtype takes this kernel (fp32 pools take
+// k_sgmv_expand_f32 below).
+constexpr int EXP_ROWS = 64;
+constexpr int EXP_COLS = 128;
+constexpr int EXP_THREADS = 256;
+constexpr int EXP_KMAX = 128;                  // 2 x 64 ranks
+constexpr int EXP_KLD = EXP_KMAX + 8;          // bf16 pitch of the staged rows (16-byte pad)
+constexpr int EXP_CLD = EXP_COLS + 4;          // fp32 pitch of the staged output tile
+constexpr int EXP_SPAN = 1024;                 // columns per workgroup, in pieces of EXP_COLS
 
-template <class C, typename TY>
-__global__ __launch_bounds__(C::NT) void k_sgmv_expand(PoolDev P, const float* __restrict__ t,
-                                                       int64_t ldt, const int32_t* __restrict__ perm,
-                                                       const int32_t* __restrict__ seg_ids,
-                                                       const int32_t* __restrict__ seg_off,
-                                                       const int32_t* __restrict__ n_seg_p,
-                                                       TY* __restrict__ y, int64_t ldy,
-                                                       int accumulate, int tiles_n) {
-    using T = typename C::T;
-    __shared__ __attribute__((aligned(16))) T smem[C::STAGE];
-    __shared__ int sRow[C::BM];
-    __shared__ int sId[C::BM];
+__device__ __forceinline__ int exp_kcols(int r) { return 64 * ((r + 31) / 32); }
+
+template <typename TY>
+__global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const float* __restrict__ t,
+                                                             int64_t ldt, const int32_t* __restrict__ perm,
+                                                             const int32_t* __restrict__ seg_ids,
+                                                             const int32_t* __restrict__ seg_off,
+                                                             const int32_t* __restrict__ n_seg_p,
+                                                             TY* __restrict__ y, int64_t ldy, int accumulate,
+                                                             int vec_y) {
+    // A [64 rows][KLD] bf16 stays for the workgroup's whole span; the second
+    // region holds B^T [128 columns][KLD] bf16 of one 128-column piece, then
+    // that piece's fp32 output tile [64][CLD]
+    constexpr int A_BYTES = EXP_ROWS * EXP_KLD * 2;
+    constexpr int B_BYTES = EXP_COLS * EXP_KLD * 2;
+    constexpr int C_BYTES = EXP_ROWS * EXP_CLD * 4;
+    constexpr int R2_BYTES = B_BYTES > C_BYTES ? B_BYTES : C_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[A_BYTES + R2_BYTES];
+    __shared__ int sRow[EXP_ROWS];
     __shared__ int sInfo[3];
-    __shared__ int sNext;
+    bf16* sA = (bf16*)lds;
+    bf16* sB = (bf16*)(lds + A_BYTES);
+    float* sC = (float*)(lds + A_BYTES);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave / C::WN;
-    const int wn = wave - wm * C::WN;
-    const int tb = blockIdx.x / tiles_n;
-    const int tn = blockIdx.x - tb * tiles_n;
-    const int n0 = tn * C::BN;
-    const int N = P.d_out;
-
     if (wave == 0) {
         int s = 0, c = 0;
-        const bool found = find_seg_tile(seg_off, *n_seg_p, C::BM, tb, lane, s, c);
+        const bool found = find_seg_tile(seg_off, *n_seg_p, EXP_ROWS, blockIdx.x, lane, s, c);
         if (lane == 0) {
             sInfo[0] = found ? 1 : 0;
             sInfo[1] = s;
@@ -1525,38 +1464,217 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_expand(PoolDev P, const float* _
     __syncthreads();
     if (!sInfo[0]) return;
     const int s = sInfo[1];
-    const int row0 = seg_off[s] + sInfo[2] * C::BM;
-    const int cnt = min(C::BM, seg_off[s + 1] - row0);
+    const int row0 = seg_off[s] + sInfo[2] * EXP_ROWS;
+    const int cnt = min(EXP_ROWS, seg_off[s + 1] - row0);
     const int u = seg_ids[s];
     const bool ok = id_ok(u, P.n_adapters);
-    for (int r = tid; r < C::BM; r += C::NT) {
-        sRow[r] = r < cnt ? perm[row0 + r] : -1;
-        sId[r] = (r < cnt && ok) ? u : INT_MAX;
-    }
+    if (!ok && accumulate) return;   // base-only rows keep their y
+    if (tid < EXP_ROWS) sRow[tid] = tid < cnt ? perm[row0 + tid] : -1;
     __syncthreads();
-    if (!ok && accumulate) return;
 
-    Acc<C> acc;
-    acc.zero();
-    if (ok) lora_kext<C>(acc, P, t, ldt, sRow, sId, &sNext, smem, n0, tid, wm, wn, lane);
-
-    const int lc = lane % C::BLK;
+    const int N = P.d_out;
+    const int rk = ok ? P.ranks[u] : 0;
+    const int K = exp_kcols(rk);   // 0 for a base-only tile
+    const bf16* Bu = (const bf16*)P.B + (ok ? P.b_off[u] : 0);
+    const bool vb = P.vec_b != 0;
+    if (ok) {
+        const float sc = P.scales[u];
+        // A: row m, K column 64 e + h * 32 + jj holds the hi (h = 0) or lo
+        // (h = 1) part of s * t[m][32 e + jj] (0 past the rank and past cnt)
+        for (int idx = tid; idx < EXP_ROWS * (K / 2); idx += EXP_THREADS) {
+            const int m = idx / (K / 2);
+            const int j = idx - m * (K / 2);
+            const float v = (m < cnt && j < rk) ? sc * t[(int64_t)sRow[m] * ldt + j] : 0.f;
+            const bf16 hi = f32_to_bf16(v);
+            const bf16 lo = f32_to_bf16(v - to_f32(hi));
+            const int e = j >> 5;
+            const int jj = j & 31;
+            sA[m * EXP_KLD + e * 64 + jj] = hi;
+            sA[m * EXP_KLD + e * 64 + 32 + jj] = lo;
+        }
+    }
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int lq = (lane >> 4) * 4;
+    const int span0 = blockIdx.y * EXP_SPAN;
+    for (int piece = 0; piece < EXP_SPAN / EXP_COLS; ++piece) {
+        const int n0 = span0 + piece * EXP_COLS;
+        if (n0 >= N) break;   // uniform over the workgroup
+        if (ok) {
+            // B^T: column n, K column 64 e + h * 32 + jj holds B_u[32 e + jj][n]
+            // (both h).  Consecutive lanes take consecutive ranks of one
+            // 8-column group, so their LDS writes are consecutive halves.
+            for (int idx = tid; idx < (K / 2) * (EXP_COLS / 8); idx += EXP_THREADS) {
+                const int j = idx % (K / 2);
+                const int c8 = (idx / (K / 2)) * 8;
+                const int nc = n0 + c8;
+                union { uint4 u4; bf16 e[8]; } v;
+                if (j < rk && vb && nc + 8 <= N) {
+                    v.u4 = *(const uint4*)(Bu + (int64_t)j * N + nc);
+                } else {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+                    for (int e = 0; e < 8; ++e)
+                        v.e[e] = (j < rk && nc + e < N) ? Bu[(int64_t)j * N + nc + e] : (bf16)0;
+                }
+                const int kc = (j >> 5) * 64 + (j & 31);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            const int col = n0 + wn * C::WTN + j * C::BLK + lc;
-#pragma unroll
-            for (int q = 0; q < C::M::NACC; ++q) {
-                const int m = wm * C::WTM + i * C::BLK + C::M::row(lane, q);
-                if (m < cnt && col < N) {
-                    TY* p = y + (int64_t)sRow[m] * ldy + col;
-                    float v = acc.v[i][j][q];
-                    if (accumulate) v += to_f32(*p);
-                    *p = from_f32<TY>(v);
+                for (int e = 0; e < 8; ++e) {
+                    sB[(c8 + e) * EXP_KLD + kc] = v.e[e];
+                    sB[(c8 + e) * EXP_KLD + kc + 32] = v.e[e];
                 }
             }
         }
+        __syncthreads();   // A (first piece) and B^T staged
+        f32x4_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            bf16x8_t a[4], bb[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(sA + (i * 16 + lr) * EXP_KLD + k0 + kq);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bb[j] = *(const bf16x8_t*)(sB + (wave * 32 + j * 16 + lr) * EXP_KLD + k0 + kq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();   // every wave is done with B^T before sC overwrites it
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sC[(i * 16 + lq + q) * EXP_CLD + wave * 32 + j * 16 + lr] = acc[i][j][q];
+        __syncthreads();
+        // thread: row tid / 4, columns (tid % 4) * 32 .. + 32 in four 8-column pieces
+        const int m = tid >> 2;
+        if (m < cnt) {
+            TY* yr = y + (int64_t)sRow[m] * ldy;
+            const float* cr = sC + m * EXP_CLD;
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc) {
+                const int cl = (tid & 3) * 32 + pc * 8;
+                const int nc = n0 + cl;
+                if (nc < N) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = cr[cl + e];
+                    if (vec_y && nc + 8 <= N) {
+                        if constexpr (sizeof(TY) == 2) {
+                            union { uint4 u4; bf16 e[8]; } o;
+                            if (accumulate) {
+                                o.u4 = *(const uint4*)(yr + nc);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) v[e] += to_f32(o.e[e]);
+                            }
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) o.e[e] = f32_to_bf16(v[e]);
+                            *(uint4*)(yr + nc) = o.u4;
+                        } else {
+                            if (accumulate) {
+                                const float4 p0 = *(const float4*)(yr + nc);
+                                const float4 p1 = *(const float4*)(yr + nc + 4);
+                                v[0] += p0.x; v[1] += p0.y; v[2] += p0.z; v[3] += p0.w;
+                                v[4] += p1.x; v[5] += p1.y; v[6] += p1.z; v[7] += p1.w;
+                            }
+                            *(float4*)(yr + nc) = float4{v[0], v[1], v[2], v[3]};
+                            *(float4*)(yr + nc + 4) = float4{v[4], v[5], v[6], v[7]};
+                        }
+                    } else {
+                        for (int e = 0; e < 8 && nc + e < N; ++e) {
+                            float w = v[e];
+                            if (accumulate) w += to_f32(yr[nc + e]);
+                            yr[nc + e] = from_f32<TY>(w);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();   // sC read before the next piece's B^T overwrites it
+    }
+}
+
+// fp32 pools: the same tiling on the vector units (fp32 products, no split).
+constexpr int EXPF_ROWS = 64;
+constexpr int EXPF_COLS = 256;
+constexpr int EXPF_THREADS = 256;
+
+template <typename TY>
+__global__ __launch_bounds__(EXPF_THREADS) void k_sgmv_expand_f32(PoolDev P, const float* __restrict__ t,
+                                                                  int64_t ldt, const int32_t* __restrict__ perm,
+                                                                  const int32_t* __restrict__ seg_ids,
+                                                                  const int32_t* __restrict__ seg_off,
+                                                                  const int32_t* __restrict__ n_seg_p,
+                                                                  TY* __restrict__ y, int64_t ldy,
+                                                                  int accumulate) {
+    __shared__ __attribute__((aligned(16))) float sT[64][EXPF_ROWS];   // s_u * t: [rank][row]
+    __shared__ int sRow[EXPF_ROWS];
+    __shared__ int sInfo[3];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    if (wave == 0) {
+        int s = 0, c = 0;
+        const bool found = find_seg_tile(seg_off, *n_seg_p, EXPF_ROWS, blockIdx.x, lane, s, c);
+        if (lane == 0) {
+            sInfo[0] = found ? 1 : 0;
+            sInfo[1] = s;
+            sInfo[2] = c;
+        }
+    }
+    __syncthreads();
+    if (!sInfo[0]) return;
+    const int s = sInfo[1];
+    const int row0 = seg_off[s] + sInfo[2] * EXPF_ROWS;
+    const int cnt = min(EXPF_ROWS, seg_off[s + 1] - row0);
+    const int u = seg_ids[s];
+    const bool ok = id_ok(u, P.n_adapters);
+    if (!ok && accumulate) return;
+    if (tid < EXPF_ROWS) sRow[tid] = tid < cnt ? perm[row0 + tid] : -1;
+    __syncthreads();
+    const int N = P.d_out;
+    const int col = blockIdx.y * EXPF_COLS + tid;
+    const int rk = ok ? P.ranks[u] : 0;
+    if (ok) {
+        const float sc = P.scales[u];
+        for (int idx = tid; idx < 64 * EXPF_ROWS; idx += EXPF_THREADS) {
+            const int j = idx / EXPF_ROWS;
+            const int m = idx - j * EXPF_ROWS;
+            sT[j][m] = (m < cnt && j < rk) ? sc * t[(int64_t)sRow[m] * ldt + j] : 0.f;
+        }
+    }
+    __syncthreads();
+    if (col >= N) return;
+    float acc[EXPF_ROWS];
+#pragma unroll
+    for (int m = 0; m < EXPF_ROWS; ++m) acc[m] = 0.f;
+    const float* Bc = (const float*)P.B + (ok ? P.b_off[u] : 0) + col;
+    for (int j = 0; j < rk; ++j) {
+        const float b = Bc[(int64_t)j * N];
+#pragma unroll
+        for (int m = 0; m < EXPF_ROWS; m += 4) {
+            const float4 tv = *(const float4*)&sT[j][m];
+            acc[m] += tv.x * b;
+            acc[m + 1] += tv.y * b;
+            acc[m + 2] += tv.z * b;
+            acc[m + 3] += tv.w * b;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < EXPF_ROWS; ++m) {
+        if (m < cnt) {
+            TY* p = y + (int64_t)sRow[m] * ldy + col;
+            float v = acc[m];
+            if (accumulate) v += to_f32(*p);
+            *p = from_f32<TY>(v);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1576,8 +1694,6 @@ using GemmF32 = Cfg<float, 64, 64, 32, 2, 2>;
 // K-blocks of 128 (32 KiB of x and A per block): two workgroups fit a CU
 using ShrinkB = Cfg<bf16, 64, 64, 128, 4, 1>;
 using ShrinkF = Cfg<float, 64, 64, 32, 4, 1>;
-using ExpandB = Cfg<bf16, 64, 64, 64, 2, 2>;
-using ExpandF = Cfg<float, 64, 64, 32, 2, 2>;
 
 template <class C, typename TY>
 hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
@@ -1751,27 +1867,31 @@ hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, 
     return run_shrink<ShrinkF, float>(P, x, ldx, seg, n_rows, n_bins, t, ldt, t_ext, lde, ids, part, stream);
 }
 
-template <class C, typename TY>
-static hipError_t run_expand(const PoolDev& P, const float* t, int64_t ldt, const lora_segments_t* seg,
-                             int32_t n_rows, int32_t n_bins, void* y, int64_t ldy, int accumulate,
-                             hipStream_t stream) {
-    const int tiles_n = (int)ceil_div(P.d_out, C::BN);
-    dim3 grid((unsigned)(seg_tiles(n_rows, n_bins, C::BM) * tiles_n));
-    hipLaunchKernelGGL((k_sgmv_expand<C, TY>), grid, dim3(C::NT), 0, stream, P, t, ldt, seg->perm,
-                       seg->seg_ids, seg->seg_off, seg->n_seg, (TY*)y, ldy, accumulate, tiles_n);
-    return hipGetLastError();
-}
-
 hipError_t launch_sgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                               const lora_segments_t* seg, int32_t n_rows, int32_t n_bins, void* y,
                               lora_dtype_t ydt, int64_t ldy, int accumulate, hipStream_t stream) {
-    if (dt == LORA_BF16)
-        return ydt == LORA_BF16
-                   ? run_expand<ExpandB, bf16>(P, t, ldt, seg, n_rows, n_bins, y, ldy, accumulate, stream)
-                   : run_expand<ExpandB, float>(P, t, ldt, seg, n_rows, n_bins, y, ldy, accumulate, stream);
-    return ydt == LORA_BF16
-               ? run_expand<ExpandF, bf16>(P, t, ldt, seg, n_rows, n_bins, y, ldy, accumulate, stream)
-               : run_expand<ExpandF, float>(P, t, ldt, seg, n_rows, n_bins, y, ldy, accumulate, stream);
+    const unsigned row_tiles = (unsigned)seg_tiles(n_rows, n_bins, EXP_ROWS);
+    if (dt == LORA_BF16) {
+        const dim3 grid(row_tiles, (unsigned)ceil_div(P.d_out, EXP_SPAN));
+        // 16-byte y pieces when y and its rows are 16-byte aligned
+        const size_t yb = ydt == LORA_BF16 ? 2 : 4;
+        const int vec_y = (((uintptr_t)y & 15u) == 0 && (ldy * (int64_t)yb) % 16 == 0) ? 1 : 0;
+        if (ydt == LORA_BF16)
+            hipLaunchKernelGGL(k_sgmv_expand<bf16>, grid, dim3(EXP_THREADS), 0, stream, P, t, ldt, seg->perm,
+                               seg->seg_ids, seg->seg_off, seg->n_seg, (bf16*)y, ldy, accumulate, vec_y);
+        else
+            hipLaunchKernelGGL(k_sgmv_expand<float>, grid, dim3(EXP_THREADS), 0, stream, P, t, ldt, seg->perm,
+                               seg->seg_ids, seg->seg_off, seg->n_seg, (float*)y, ldy, accumulate, vec_y);
+    } else {
+        const dim3 grid(row_tiles, (unsigned)ceil_div(P.d_out, EXPF_COLS));
+        if (ydt == LORA_BF16)
+            hipLaunchKernelGGL(k_sgmv_expand_f32<bf16>, grid, dim3(EXPF_THREADS), 0, stream, P, t, ldt,
+                               seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, (bf16*)y, ldy, accumulate);
+        else
+            hipLaunchKernelGGL(k_sgmv_expand_f32<float>, grid, dim3(EXPF_THREADS), 0, stream, P, t, ldt,
+                               seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, (float*)y, ldy, accumulate);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace lora
