@@ -1552,14 +1552,15 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
                 for (int q = 0; q < 4; ++q)
                     sC[(i * 16 + lq + q) * EXP_CLD + wave * 32 + j * 16 + lr] = acc[i][j][q];
         __syncthreads();
-        // thread: row tid / 4, columns (tid % 4) * 32 .. + 32 in four 8-column pieces
-        const int m = tid >> 2;
-        if (m < cnt) {
-            TY* yr = y + (int64_t)sRow[m] * ldy;
-            const float* cr = sC + m * EXP_CLD;
+        // 16 threads per row, 8 columns each: a wave moves 4 rows of 128
+        // contiguous columns per pass; 16 rows per pass of the workgroup
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const int cl = (tid & 3) * 32 + pc * 8;
+        for (int pass = 0; pass < EXP_ROWS / 16; ++pass) {
+            const int m = pass * 16 + (tid >> 4);
+            if (m < cnt) {
+                TY* yr = y + (int64_t)sRow[m] * ldy;
+                const float* cr = sC + m * EXP_CLD;
+                const int cl = (tid & 15) * 8;
                 const int nc = n0 + cl;
                 if (nc < N) {
                     float v[8];
