@@ -1692,8 +1692,10 @@ using GemmMid = Cfg<bf16, 64, 64, 64, 2, 2>;
 using GemmMed = Cfg<bf16, 64, 64, 256, 2, 2>;
 using GemmSmall = Cfg<bf16, 32, 64, 64, 2, 2>;
 using GemmF32 = Cfg<float, 64, 64, 32, 2, 2>;
-// K-blocks of 128 (32 KiB of x and A per block): two workgroups fit a CU
-using ShrinkB = Cfg<bf16, 64, 64, 128, 4, 1>;
+// K-blocks of 64 (16 KiB of x and A per block, two in flight): four
+// workgroups fit a CU (64: 102.7 us on the 70B prefill q/o shrink, against
+// 112.5 at 128 and 144.7 at 32)
+using ShrinkB = Cfg<bf16, 64, 64, 64, 4, 1>;
 using ShrinkF = Cfg<float, 64, 64, 32, 4, 1>;
 
 template <class C, typename TY>
@@ -1825,8 +1827,8 @@ static int64_t seg_tiles(int32_t n_rows, int32_t n_bins, int bm) {
 }
 
 int32_t sgmv_shrink_slices(const PoolDev& P, int32_t n_rows) {
-    // about 1024 workgroups (two per CU) over the row tiles, each slice at
-    // least 1024 k-rows
+    // about 1024 workgroups over the row tiles (one round at four per CU;
+    // 2048 measured slower), each slice at least 1024 k-rows
     const int64_t tiles = std::max<int64_t>(1, ceil_div(n_rows, ShrinkB::BM));
     const int64_t want = ceil_div(1024, tiles);
     return (int32_t)std::max<int64_t>(1, std::min<int64_t>(want, P.d_in / 1024));
