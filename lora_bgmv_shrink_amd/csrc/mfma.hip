@@ -1423,7 +1423,7 @@ constexpr int EXP_THREADS = 256;
 constexpr int EXP_KMAX = 128;                  // 2 x 64 ranks
 constexpr int EXP_KLD = EXP_KMAX + 8;          // bf16 pitch of the staged rows (16-byte pad)
 constexpr int EXP_CLD = EXP_COLS + 4;          // fp32 pitch of the staged output tile
-constexpr int EXP_SPAN = 1024;                 // columns per workgroup, in pieces of EXP_COLS
+constexpr int EXP_SPAN = 512;                 // columns per workgroup, in pieces of EXP_COLS (256: slower; 1024: slower)
 
 __device__ __forceinline__ int exp_kcols(int r) { return 64 * ((r + 31) / 32); }
 
