@@ -536,7 +536,9 @@ lora_status_t lora_sched_submit(lora_sched_t sched, int64_t request, int32_t ada
 /* Form one batch at time `now` of at most `capacity` requests.  Writes,
  * in admission order, requests/adapters/rows/waits[0 .. info->admitted)
  * (host out arrays of `capacity` entries each; waits may be NULL) and the
- * step's counts into *info. */
+ * step's counts into *info.  If asking the cache fails, the fill stops
+ * there: the requests admitted so far form the batch (and leave the queue)
+ * and the cache's error is returned. */
 lora_status_t lora_sched_step(lora_sched_t sched, double now, int32_t capacity, int64_t* requests,
                               int32_t* adapters, int32_t* rows, double* waits,
                               lora_sched_step_t* info);

@@ -129,6 +129,7 @@ lora_status_t lora_sched_step(lora_sched_t s, double now, int32_t capacity, int6
     s->done.assign(n, 0);
     int32_t distinct = 0, batch_rows = 0, admitted = 0, batch_class = -1;
     std::vector<int32_t> batch_adapters;
+    lora_status_t err = LORA_OK;   // a cache error ends the fill; the step is still closed consistently
     for (;;) {
         if (admitted >= capacity || batch_rows >= c.max_rows) break;
         // best pending request by score, then arrival, then submission
@@ -155,7 +156,11 @@ lora_status_t lora_sched_step(lora_sched_t s, double now, int32_t capacity, int6
             if (s->resident[a] < 0) {
                 lora_cache_state_t st;
                 const lora_status_t e = lora_cache_request(s->cache, a, &st);
-                if (e != LORA_OK) return e;
+                if (e != LORA_OK) {
+                    err = e;
+                    s->done[best] = 0;   // not decided: it stays queued
+                    break;
+                }
                 s->resident[a] = st == LORA_CACHE_RESIDENT ? 1 : 0;
                 s->touched.push_back(a);
             }
@@ -220,7 +225,7 @@ lora_status_t lora_sched_step(lora_sched_t s, double now, int32_t capacity, int6
     info->rows = batch_rows;
     info->distinct_adapters = distinct;
     info->queued = (int32_t)k;
-    return LORA_OK;
+    return err;
 }
 
 }  // extern "C"
