@@ -276,3 +276,35 @@ def test_destroy_with_loads_in_flight():
     _make_resident(c2, [3])
     assert c2.slot_of(3) >= 0
     c2.destroy()
+
+
+def test_fp32_cache_layer_matches_oracle():
+    """An fp32 adapter cache (4-byte blobs and pools) through the fp32 layer,
+    |gpu - oracle| <= 1e-4 * max(1, |oracle|)."""
+    b = binding()
+    parts = [(256, 192), (192, 320)]
+    ranks = [4, 8, 16, 32, 8, 16]
+    aset = wl.adapter_set(parts, ranks, np.linspace(0.5, 2.0, 6).astype(np.float32), dtype=torch.float32,
+                          seed=17)
+    c = b.Cache(torch.float32, parts, 32, 6, 3, 2, device=DEV)
+    for u in range(6):
+        c.register(u, ranks[u], float(aset.scales[u]), aset.A[u], aset.B[u])
+    g = torch.Generator(device="cpu")
+    g.manual_seed(19)
+    Ws = [torch.randn(di, do, generator=g) / 16 for di, do in parts]
+    rng = np.random.default_rng(4)
+    for step in range(4):
+        used = sorted(rng.choice(6, size=3, replace=False).tolist())
+        ids = np.array(used, np.int32)[rng.integers(0, 3, size=70)]
+        ids[::9] = -1
+        _make_resident(c, used)
+        slots = c.map(ids)
+        ids_d = torch.as_tensor(slots, device=DEV)
+        for p, (di, do) in enumerate(parts):
+            x = torch.randn(70, di, generator=g)
+            y = b.lora_layer_apply(c.pool(p), x.to(DEV), Ws[p].to(DEV), ids_d)
+            torch.cuda.synchronize()
+            ref = oracle.layer(f64(x), f64(Ws[p]), ids, _oracle_pool(aset, p), want=("y",))["y"]
+            assert_close(y, ref, TOL[torch.float32], f"fp32 cache step {step} part {p}")
+        c.release()
+    c.destroy()

@@ -125,3 +125,23 @@ def test_q4_argument_checks():
     with pytest.raises(b.LoraError) as e:           # d_in not a multiple of 128
         b.lora_decode_stream_q4(pool2, w2.projections[0].x, Wq2, sc2, ids, ws, True)
     assert e.value.status == b.LORA_E_UNSUPPORTED
+
+
+def test_q4_decode_ragged_pool_fp32_y():
+    """A ragged pool of ranks 8/16/32/64 and an fp32 y on the 4-bit base."""
+    b = binding()
+    d_in, d_out, n = 2048, 768, 40
+    w = wl.small_batch(seed=13, n_rows=n, d_in=d_in, d_out=d_out, n_adapters=8, ranks=[8, 16, 32, 64] * 2,
+                       layout=wl.RAGGED, dtype=torch.bfloat16, device=DEV, frac_base=0.1)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    op, _ = oracle_pool(p.pool)
+    Wq, sc = wl.q4_weight(6, d_in, d_out, DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    ws = torch.zeros(b.lora_decode_workspace(pool, n, True), dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, d_out), dtype=torch.float32, device=DEV)
+    b.lora_decode_stream_q4(pool, p.x, Wq, sc, ids, ws, True)
+    b.lora_decode_finish(pool, ids, ws, y, True)
+    torch.cuda.synchronize()
+    ref = _oracle_y(p.x, Wq, sc, w.ids, op, d_in, True)
+    assert_close(y, ref, TOL[torch.bfloat16], "q4 ragged, fp32 y")
