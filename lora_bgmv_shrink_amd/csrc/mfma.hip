@@ -1012,9 +1012,10 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             return sA;
         };
         int kb = 0;
-        if constexpr (C::NT <= 256) {
-            // registers to spare (4 waves): two blocks in flight, in two
-            // register sets used alternately (the loop is unrolled by two)
+        if constexpr (C::NT <= 256 || (C::BM + C::BN) * C::BK * (int)sizeof(T) <= 64 * C::NT) {
+            // registers to spare (4 waves, or at most 64 staged bytes a
+            // thread): two blocks in flight, in two register sets used
+            // alternately (the loop is unrolled by two)
             RowLoader<C, C::BM> la2;
             RowLoader<C, C::BN> lw2;
             auto load_full2 = [&](int s) {
