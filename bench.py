@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-paging", action="store_true", help="skip the adapter-paging measurements")
+    ap.add_argument("--comparators", action="store_true",
+                    help="also time the vendor GEMM on the decode base product and a device copy of the "
+                         "decode stream's bytes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write kernel (counter calibration)")
     return ap.parse_args()
@@ -250,6 +253,33 @@ def bench_decode(torch, args):
     stream_bytes = w_b + bA + x_b + n * 4
     shrink_bytes = bA + x_b + t_b + n * 4
     achieved = stream_bytes / d_stream / 1e9
+    comparators = None
+    if args.comparators:
+        # context, not part of the layer: the vendor GEMM on the bare base
+        # product of the same batch, and a plain device copy that moves the
+        # stream launch's algorithmic bytes (half read, half written)
+        half = (stream_bytes // 4) * 2
+        pool_dout = p0.pool.d_out
+        for r in reps:
+            r["y_mm"] = torch.empty((n, pool_dout), dtype=torch.bfloat16, device=dev)
+            r["cp_src"] = torch.ones(half // 2, dtype=torch.bfloat16, device=dev)
+            r["cp_dst"] = torch.empty_like(r["cp_src"])
+        g_mm = capture(torch, lambda: [torch.mm(r["p"].x, r["Wt"].t(), out=r["y_mm"]) for r in reps])
+        g_cp = capture(torch, lambda: [r["cp_dst"].copy_(r["cp_src"]) for r in reps])
+        d_mm = time_graph(torch, g_mm, kr) / R
+        d_cp = time_graph(torch, g_cp, kr) / R
+        mm_bytes = p0.pool.d_in * pool_dout * 2 + n * p0.pool.d_in * 2 + n * pool_dout * 2
+        comparators = dict(
+            vendor_base_product=dict(call="torch.mm (hipBLASLt): x[32,4096] times W^T, W stored [d_out, d_in], bf16",
+                                     us=round(d_mm * 1e6, 3), GBps=round(mm_bytes / d_mm / 1e9, 1)),
+            device_copy_same_bytes=dict(bytes=2 * half, us=round(d_cp * 1e6, 3),
+                                        GBps=round(2 * half / d_cp / 1e9, 1)),
+            decode_stream_rate_over_copy_rate=round(d_cp / d_stream, 3),
+            layer_step_over_vendor_base_product=round(d_step / d_mm, 3),
+        )
+        del g_mm, g_cp
+        for r in reps:
+            del r["y_mm"], r["cp_src"], r["cp_dst"]
     out = dict(
         sec_step=sec_step,
         tokens_per_s=n / sec_step,
@@ -276,6 +306,7 @@ def bench_decode(torch, args):
             bgmv_shrink_GBps=round(shrink_bytes / d_shr / 1e9, 1),
             bgmv_shrink_frac_hbm=round(shrink_bytes / d_shr / 1e9 / HBM_PEAK_GBS, 4),
         ),
+        comparators=comparators,
         # the graph replays launches over reps' tensors and pools: whoever
         # replays it must hold reps too
         _decode_graph=(decode_graph, reps),
@@ -800,6 +831,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": dec["kernels_us"],
         "adapter_term": dec["adapter_term"],
+        "comparators": dec["comparators"],
         "gpu_step_us": round(dec["gpu_step_s"] * 1e6, 3),
         "workloads": extra,
         "merge": merge,
