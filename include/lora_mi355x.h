@@ -73,7 +73,10 @@ typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora
 /* Storage of the base weight.  LORA_W_IN_OUT: W as [d_in, d_out] (the
  * page-3 convention y = xW).  LORA_W_OUT_IN: W stored transposed, [d_out,
  * d_in] (the x W^T convention of "Serving Many LoRA Adapters"
- * (praveentn.live), section "Why Naive Batching Breaks"). */
+ * (praveentn.live), section "Why Naive Batching Breaks").  Both give the
+ * same bits.  LORA_W_OUT_IN is the fast one: the decode path needs it, and
+ * on batches of thousands of rows the GEMM over LORA_W_IN_OUT, whose tiles
+ * are transposed on their way into LDS, takes about twice as long. */
 typedef enum { LORA_W_IN_OUT = 0, LORA_W_OUT_IN = 1 } lora_w_layout_t;
 
 typedef struct lora_pool_s* lora_pool_t;

@@ -390,15 +390,26 @@ struct BLoader {
             }
         }
     }
-    // bf16 transposed pieces in pairs of k-rows: thread piece p = idx % (BK/2)
-    // owns k-rows 2p and 2p+1 of column vector idx / (BK/2), so the two rows'
-    // values of a column are written to LDS as one 32-bit word, and the lanes
-    // of a half-wave fill one LDS row with consecutive words (no bank
-    // conflicts).  reg[2v] holds row 2p, reg[2v+1] row 2p+1.
+    // bf16 transposed pieces in pairs of k-rows: piece idx owns k-rows 2p and
+    // 2p+1 of one column vector (pair_piece gives p and the vector), so the
+    // two rows' values of a column are written to LDS as one 32-bit word.
+    // reg[2v] holds row 2p, reg[2v+1] row 2p+1.
     static constexpr int PAIRS = C::BK / 2;
     static constexpr int P_TOT = PAIRS * T_VPR;
     static constexpr int P_NV = (P_TOT + C::NT - 1) / C::NT;
     static_assert(sizeof(T) != 2 || 2 * P_NV == NV, "pair pieces use the same registers");
+    // Lanes in groups of PF take consecutive pairs of one column vector and
+    // the groups step along the columns, so that a wave's loads cover whole
+    // 128-byte row pieces (8 column vectors of a row) instead of 16 bytes
+    // of 32 rows; the LDS stores then meet 4-way bank conflicts.  PF = 8 was
+    // measured against 16 and 32 (the pairs of one vector in a half-wave).
+    static constexpr int PF = 8 < PAIRS ? 8 : PAIRS;
+    static_assert(PAIRS % PF == 0, "pairs per lane group");
+    __device__ __forceinline__ static void pair_piece(int idx, int& p, int& cv) {
+        const int lo = idx % PF, rest = idx / PF;
+        cv = rest % T_VPR;
+        p = lo + PF * (rest / T_VPR);
+    }
     __device__ __forceinline__ void load_trans_pairs(const T* __restrict__ base, int64_t ld, int j0, int kwrap,
                                                      int kmax, int n0, int N, bool vec, int tid) {
         const bool full = vec && n0 + C::BN <= N;
@@ -406,8 +417,9 @@ struct BLoader {
         for (int v = 0; v < P_NV; ++v) {
             const int idx = tid + v * C::NT;
             if (P_TOT % C::NT != 0 && idx >= P_TOT) break;
-            const int p = idx % PAIRS;
-            const int n = n0 + (idx / PAIRS) * VE;
+            int p, cv;
+            pair_piece(idx, p, cv);
+            const int n = n0 + cv * VE;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int kr = 2 * p + h;
@@ -430,8 +442,9 @@ struct BLoader {
         for (int v = 0; v < P_NV; ++v) {
             const int idx = tid + v * C::NT;
             if (P_TOT % C::NT != 0 && idx >= P_TOT) break;
-            const int p = idx % PAIRS;
-            const int c = (idx / PAIRS) * VE;
+            int p, cv;
+            pair_piece(idx, p, cv);
+            const int c = cv * VE;
             union { uint4 u; unsigned short e[VE]; } r0, r1;
             r0.u = reg[2 * v];
             r1.u = reg[2 * v + 1];
