@@ -459,7 +459,7 @@ def test_skewed_decode_8b(proj):
 
 @pytest.mark.parametrize("proj", ["q", "k", "down"])
 def test_prefill_70b(proj):
-    say(f"prefill 70B {proj} r64: sampled rows x columns")
+    say(f"prefill 70B {proj} r64: sampled rows x columns, both W layouts")
     b = binding()
     w = wl.prefill_70b(device=DEV, projections=[proj])
     p = w.projections[0]
@@ -474,6 +474,12 @@ def test_prefill_70b(proj):
     torch.cuda.synchronize()
     ys = y[rows][:, cols]
     assert_close(ys, o["y"], TOL[w.dtype], "y sampled")
+    # W stored [d_in, d_out]: other loaders, the same products in the same
+    # order, so the same bits on every row and column
+    yi = b.lora_layer_apply(pool, p.x, w_stored(p.W, b.LORA_W_IN_OUT), ids, w_layout=b.LORA_W_IN_OUT,
+                            mode=b.LORA_MODE_SGMV)
+    torch.cuda.synchronize()
+    assert torch.equal(yi, y), "W layouts differ"
     seg = b.lora_segments_build(ids, p.pool.n_adapters)
     t = b.lora_sgmv_shrink(pool, p.x, seg)
     torch.cuda.synchronize()
