@@ -392,8 +392,15 @@ def bench_multi(torch, args, name):
             adapter_bytes=abytes,
             overhead_fraction=round(max(0.0, (sec - d_base) / sec), 4),
         )
+        res[label]["base_only_ms"] = round(d_base * 1e3, 4)
         for h in hs:
             h.destroy()
+    if args.comparators:
+        # context: the vendor GEMM (hipBLASLt through torch.mm) on the same
+        # seven base products, W stored [d_out, d_in], no adapter term
+        g_mm = capture(torch, lambda: [torch.mm(pr["p"].x, pr["Wt"].t(), out=pr["y"]) for pr in projs])
+        res["vendor_base_product_ms"] = round(time_graph(torch, g_mm, 3) * 1e3, 4)
+        del g_mm
     return res
 
 
