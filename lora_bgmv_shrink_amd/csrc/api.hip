@@ -76,6 +76,16 @@ bool decode_ok(const lora_pool_s* pool, int32_t n_rows) {
 // AUTO: per-row gathers (BGMV) for decode-sized batches and for batches with
 // fewer than about two rows per pool adapter, where segments would mostly
 // hold one or two rows; grouping by adapter (SGMV) otherwise.
+// BGMV batches of a few hundred rows (bf16 pool): the base product goes to
+// fp32 partials and the BGMV expand adds them to the adapter term and rounds
+// y once.  With many adapters per tile the GEMM's row-wise epilogue costs
+// more than this separate pass (its B reads wait on each row's adapter).
+bool bgmv_split_ok(const lora_pool_s* pool, int32_t n_rows) {
+    return pool->dtype == LORA_BF16 && n_rows > 64 && n_rows <= 512;
+}
+
+int64_t split_ld(const PoolDev& P) { return (int64_t)align_up((size_t)P.d_out, 4); }
+
 lora_mode_t resolve_mode(lora_mode_t m, int32_t n_rows, int32_t n_adapters) {
     if (m != LORA_MODE_AUTO) return m;
     return (n_rows <= 64 || n_rows <= 2 * (int64_t)n_adapters) ? LORA_MODE_BGMV : LORA_MODE_SGMV;
@@ -363,6 +373,8 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
         off += bgmv_shrink_ws_bytes(plan, n_rows);
+        if (bgmv_split_ok(pool, n_rows))
+            off = align_up(off, 256) + (size_t)n_rows * split_ld(pool->dev) * 4;
         if (decode_ok(pool, n_rows))
             off = std::max(off, decode_ws_bytes(pool->dev, n_rows, plan_decode(pool->dev, n_rows, true)));
     } else {
@@ -428,10 +440,13 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256) + ext_bytes(pool, n_rows);
     hipError_t e = hipSuccess;
     const int32_t* gemm_perm = nullptr;   // SGMV: the GEMM visits rows grouped by adapter
+    const bool split = m == LORA_MODE_BGMV && y_dtype == LORA_BF16 && bgmv_split_ok(pool, n_rows);
+    size_t split_at = 0;
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
+        split_at = align_up(after_t + bgmv_shrink_ws_bytes(plan, n_rows), 256);
         e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, base + after_t, plan,
-                               stream, t_ext, lde);
+                               stream, split ? nullptr : t_ext, lde);
     } else {
         lora_segments_t own;
         const lora_segments_t* sg = seg;
@@ -472,6 +487,22 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     g.rows_distinct = (m == LORA_MODE_BGMV);
     g.perm = gemm_perm;
     g.x_rows = n_rows;
+    if (split) {
+        // base product into fp32 partials, then y = partials + s t B, rounded once
+        float* part = (float*)(base + split_at);
+        const int64_t ldp = split_ld(P);
+        g.t = nullptr;
+        g.ldt = 0;
+        g.t_ext = nullptr;
+        g.lde = 0;
+        g.y = part;
+        g.ldy = ldp;
+        e = launch_layer_gemm(P, pool->dtype, LORA_F32, g, stream);
+        if (e == hipSuccess)
+            e = launch_bgmv_expand(P, pool->dtype, t, ldt, ids, n_rows, y, y_dtype, ldy, 0, true, stream, part,
+                                   ldp);
+        return dev_status(e);
+    }
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
 }
 

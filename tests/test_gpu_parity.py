@@ -335,6 +335,14 @@ def test_base_only_rows_and_all_base():
     assert_close(y0, base_ref, TOL[w.dtype], "all base-only = x W")
     mask = torch.as_tensor(w.ids == -1, device=DEV)
     assert torch.equal(y[mask], y0[mask]), "base-only rows depend on other rows' adapters"
+    # bf16 y in BGMV mode (200 rows: base product in fp32 partials, then the
+    # expand adds the term and rounds once; base-only rows take the partials)
+    yb = b.lora_layer_apply(pool, p.x, p.W, ids, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
+    yb0 = b.lora_layer_apply(pool, p.x, p.W, allbase, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_close(yb0, base_ref, TOL[torch.bfloat16], "all base-only = x W (bf16 y)")
+    assert torch.equal(yb[mask], yb0[mask]), "base-only rows depend on other rows' adapters (bf16 y)"
+    assert_close(yb, o["y"], TOL[torch.bfloat16], "y bf16, BGMV")
     t = b.lora_bgmv_shrink(pool, p.x, allbase)
     torch.cuda.synchronize()
     assert torch.count_nonzero(t).item() == 0
@@ -356,6 +364,11 @@ def test_out_of_range_ids_flag_and_base_only():
         assert b.lora_pool_last_error(pool) == 0
         base_ref = f64(p.x[[3, 50, 100]]) @ f64(p.W)
         assert_close(y[[3, 50, 100]], base_ref, TOL[w.dtype], f"invalid rows base-only mode {m}")
+    # bf16 y in BGMV mode: the expand that adds the fp32 base partials flags too
+    y = b.lora_layer_apply(pool, p.x, p.W, ids, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
+    assert b.lora_pool_last_error(pool) & 1 == 1
+    assert b.lora_pool_last_error(pool) == 0
+    assert_close(y[[3, 50, 100]], f64(p.x[[3, 50, 100]]) @ f64(p.W), TOL[torch.bfloat16], "invalid rows, bf16 y")
 
 
 def test_empty_and_single_row():
