@@ -225,7 +225,7 @@ lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
 /* The fused layer                                                         */
 /* ---------------------------------------------------------------------- */
 
-/* Workspace bytes for lora_layer_apply (for BGMV batches of 65..512 rows of
+/* Workspace bytes for lora_layer_apply (for BGMV batches of 65..2048 rows of
  * a bf16 pool this holds n_rows * d_out fp32 base partials). */
 lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t mode,
                                    size_t* bytes);
@@ -237,7 +237,7 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
  * segmented gather, grouped GEMM, scatter-add, fused output).  Each GEMM
  * tile adds the expand either as extra K-blocks per distinct adapter (tiles
  * of long runs of one id) or row by row after its K loop (tiles whose rows
- * mostly carry different adapters).  BGMV batches of 65..512 rows with a
+ * mostly carry different adapters).  BGMV batches of 65..2048 rows with a
  * bf16 pool and bf16 y take a third form: the GEMM writes the base product
  * in fp32 into the workspace, and one BGMV expand launch adds it to the
  * scaled expand and rounds y once (rows without a term get the base alone).

@@ -76,12 +76,13 @@ bool decode_ok(const lora_pool_s* pool, int32_t n_rows) {
 // AUTO: per-row gathers (BGMV) for decode-sized batches and for batches with
 // fewer than about two rows per pool adapter, where segments would mostly
 // hold one or two rows; grouping by adapter (SGMV) otherwise.
-// BGMV batches of a few hundred rows (bf16 pool): the base product goes to
-// fp32 partials and the BGMV expand adds them to the adapter term and rounds
-// y once.  With many adapters per tile the GEMM's row-wise epilogue costs
-// more than this separate pass (its B reads wait on each row's adapter).
+// BGMV batches of 65..2048 rows (bf16 pool): the base product goes to fp32
+// partials and the BGMV expand adds them to the adapter term and rounds y
+// once.  With many adapters per tile the GEMM's row-wise epilogue costs more
+// than this separate pass (its B reads wait on each row's adapter); 2048 is
+// the largest batch measured.
 bool bgmv_split_ok(const lora_pool_s* pool, int32_t n_rows) {
-    return pool->dtype == LORA_BF16 && n_rows > 64 && n_rows <= 512;
+    return pool->dtype == LORA_BF16 && n_rows > 64 && n_rows <= 2048;
 }
 
 int64_t split_ld(const PoolDev& P) { return (int64_t)align_up((size_t)P.d_out, 4); }

@@ -667,6 +667,11 @@ def test_layer_tail_rows_split_launch():
             y = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=m, y_dtype=torch.float32)
             torch.cuda.synchronize()
             assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay} mode {m}")
+        # bf16 y in BGMV mode: base product in fp32 partials, added by the expand
+        y = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=b.LORA_MODE_BGMV,
+                               y_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert_close(y, o["y"], TOL[torch.bfloat16], f"y bf16 layout {lay} BGMV")
     yb = b.lora_base_gemm_expand(pool, p.x, w_stored(p.W, b.LORA_W_OUT_IN), ids, None, w_layout=b.LORA_W_OUT_IN,
                                  y_dtype=torch.float32)
     torch.cuda.synchronize()
