@@ -1821,7 +1821,9 @@ hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream
         }
         return run_gemm<GemmHuge, TY>(P, a, stream);
     }
-    if (tiles(GemmBig::BM, GemmBig::BN) >= (tail ? 64 : 200)) return run_gemm<GemmBig, TY>(P, a, stream);
+    // 128x128 tiles from 96 of them: fewer workgroups than CUs, but a
+    // 128x128 tile moves half the x and W bytes per flop of a 64x64 tile
+    if (tiles(GemmBig::BM, GemmBig::BN) >= (tail ? 64 : 96)) return run_gemm<GemmBig, TY>(P, a, stream);
     if (a.w_out_in && (!a.t_ext || (a.t && a.rows_distinct))) return run_gemm<GemmMed, TY>(P, a, stream);
     if (tiles(GemmMid::BM, GemmMid::BN) >= 128 || a.n_rows > 32) return run_gemm<GemmMid, TY>(P, a, stream);
     return run_gemm<GemmSmall, TY>(P, a, stream);
