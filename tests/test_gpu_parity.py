@@ -649,6 +649,31 @@ def test_layer_many_adapters_per_tile(d_in, d_out, layout, runs):
                 assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay} mode {m} {ydt}")
 
 
+def test_bgmv_split_form_medium_batch():
+    """600 rows x 512 -> 2560 in BGMV mode: 100 tiles of 128x128.  bf16 y
+    takes the split form (base product in fp32 partials, added by the
+    expand, one rounding); fp32 y the fused GEMM.  Both W layouts, every
+    row against the oracle, and the two forms within one bf16 rounding."""
+    say("layer, BGMV split form: 600 x 512 -> 2560, both W layouts")
+    b = binding()
+    w = wl.small_batch(seed=600, n_rows=600, device=DEV, dtype=torch.bfloat16, d_in=512, d_out=2560,
+                       n_adapters=40, layout=wl.RAGGED, ranks=(RAGGED_RANKS * 4)[:40], frac_base=0.1,
+                       scale=np.linspace(-2.0, 2.0, 40).astype(np.float32))
+    p = w.projections[0]
+    o = run_oracle(w)
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    for lay in (b.LORA_W_OUT_IN, b.LORA_W_IN_OUT):
+        yb = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=b.LORA_MODE_BGMV,
+                                y_dtype=torch.bfloat16)
+        yf = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=b.LORA_MODE_BGMV,
+                                y_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert_close(yb, o["y"], TOL[torch.bfloat16], f"y bf16 (split form), layout {lay}")
+        assert_close(yf, o["y"], TOL[torch.bfloat16], f"y fp32 (fused), layout {lay}")
+        assert_close(yb, f64(yf), TOL[torch.bfloat16], f"split vs fused, layout {lay}")
+
+
 def test_layer_tail_rows_split_launch():
     """520 rows x 22,016 columns: 258 tiles of 256x256 would leave a last
     round of two; rows [0, 512) take the 256x256 launch and rows [512, 520)
