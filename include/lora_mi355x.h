@@ -57,7 +57,9 @@ typedef enum {
     LORA_E_WORKSPACE = 3,   /* workspace missing or too small */
     LORA_E_ID_RANGE = 4,    /* reported by lora_pool_last_error only */
     LORA_E_DEVICE = 5,      /* a HIP runtime call failed */
-    LORA_E_NOT_RESIDENT = 6 /* lora_cache_map: an adapter is not resident yet */
+    LORA_E_NOT_RESIDENT = 6, /* lora_cache_map: an adapter is not resident yet */
+    LORA_E_SCRATCH = 7      /* lora_layer_apply_noalloc: the call needs more than
+                               LORA_NOALLOC_SCRATCH_BYTES of scratch */
 } lora_status_t;
 
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype_t;
@@ -251,6 +253,26 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx,
                                const int32_t* ids, const lora_segments_t* seg, int32_t n_rows,
                                void* y, lora_dtype_t y_dtype, int64_t ldy,
                                lora_mode_t mode, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* lora_layer_apply for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation and kernels as lora_layer_apply (same arguments, same bits),
+ * but with no workspace argument: the scratch it needs lives in one
+ * file-scope device array of LORA_NOALLOC_SCRATCH_BYTES per GPU, which the
+ * library holds from the first call on that GPU until the process ends.
+ * The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  The scratch needed is what lora_layer_workspace
+ * reports for (pool, n_rows, mode); beyond the maximum the call returns
+ * LORA_E_SCRATCH before any launch (use lora_layer_apply with a workspace
+ * then).  Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (two streams, or two threads) race and give
+ * wrong results: serialize them.  The device is the stream's. */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lora_status_t lora_layer_apply_noalloc(lora_pool_t pool, const void* x, int64_t ldx,
+                                       const void* W, int64_t ldw, lora_w_layout_t w_layout,
+                                       const int32_t* ids, const lora_segments_t* seg,
+                                       int32_t n_rows, void* y, lora_dtype_t y_dtype, int64_t ldy,
+                                       lora_mode_t mode, hipStream_t stream);
 
 /* The second half of lora_layer_apply on its own:
  *   y = x W + s * t B[ids]   (t from lora_bgmv_shrink or lora_sgmv_shrink),

@@ -23,7 +23,8 @@ import torch  # loads the HIP runtime the library binds to
 from .build import LIB_PATH
 
 (LORA_OK, LORA_E_INVALID, LORA_E_UNSUPPORTED, LORA_E_WORKSPACE, LORA_E_ID_RANGE, LORA_E_DEVICE,
- LORA_E_NOT_RESIDENT) = range(7)
+ LORA_E_NOT_RESIDENT, LORA_E_SCRATCH) = range(8)
+LORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 LORA_F32, LORA_BF16 = 0, 1
 LORA_LAYOUT_UNIFORM, LORA_LAYOUT_RAGGED = 0, 1
 LORA_MODE_AUTO, LORA_MODE_BGMV, LORA_MODE_SGMV = 0, 1, 2
@@ -45,6 +46,7 @@ EXPORTS = [
     "lora_cache_map", "lora_cache_release", "lora_cache_pool", "lora_cache_slot_of", "lora_cache_stats",
     "lora_decode_stream_q4",
     "lora_sched_create", "lora_sched_destroy", "lora_sched_submit", "lora_sched_step", "lora_sched_queued",
+    "lora_layer_apply_noalloc",
 ]
 
 
@@ -129,6 +131,7 @@ def _load():
         "lora_sched_submit": (st, [p, i64, i32, i32, ctypes.c_double]),
         "lora_sched_step": (st, [p, ctypes.c_double, i32, p, p, p, p, p]),
         "lora_sched_queued": (i32, [p]),
+        "lora_layer_apply_noalloc": (st, [p, p, i64, p, i64, st, p, p, i32, p, st, i64, st, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -409,6 +412,20 @@ def lora_layer_apply(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Te
                                  None if cs is None else ctypes.byref(cs), n, _ptr(y), _dt(y.dtype), _ld(y),
                                  mode, _ptr(ws), 0 if ws is None else ws.numel(),
                                  ctypes.c_void_p(_stream(x.device))), "lora_layer_apply")
+    return y
+
+
+def lora_layer_apply_noalloc(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
+                             w_layout: int, y: torch.Tensor, seg: Optional[Segments] = None,
+                             mode: int = LORA_MODE_AUTO) -> torch.Tensor:
+    """lora_layer_apply with the library's static scratch instead of a
+    workspace; y must be given (nothing is allocated here either)."""
+    n = ids.numel()
+    cs = None if seg is None else seg.c_struct()
+    _check(_lib.lora_layer_apply_noalloc(pool.handle, _ptr(x), _ld(x), _ptr(W), _ld(W), w_layout, _ptr(ids),
+                                         None if cs is None else ctypes.byref(cs), n, _ptr(y), _dt(y.dtype),
+                                         _ld(y), mode, ctypes.c_void_p(_stream(x.device))),
+           "lora_layer_apply_noalloc")
     return y
 
 

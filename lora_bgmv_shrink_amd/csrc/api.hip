@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "lora_internal.hpp"
@@ -106,6 +107,46 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
 }
 }  // namespace lora
 
+// Scratch of lora_layer_apply_noalloc: one copy of this array per device,
+// held by the device from the library's first use there until the process
+// ends.  In host code `scratch` is only a stand-in for the symbol: its device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the stream's device (fetched with that
+// device current on first use, then kept).
+lora_status_t scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return LORA_E_DEVICE;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return LORA_E_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return LORA_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return LORA_E_DEVICE;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return LORA_E_DEVICE;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return LORA_E_DEVICE;
+        if (e != hipSuccess || !p) return LORA_E_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LORA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* lora_status_string(lora_status_t s) {
@@ -117,6 +158,9 @@ const char* lora_status_string(lora_status_t s) {
         case LORA_E_ID_RANGE: return "LORA_E_ID_RANGE: an adapter id was outside [-1, n_adapters)";
         case LORA_E_DEVICE: return "LORA_E_DEVICE: a HIP runtime call failed";
         case LORA_E_NOT_RESIDENT: return "LORA_E_NOT_RESIDENT: an adapter of the batch is not resident";
+        case LORA_E_SCRATCH:
+            return "LORA_E_SCRATCH: the call needs more scratch than the static array holds "
+                   "(LORA_NOALLOC_SCRATCH_BYTES); use lora_layer_apply with a workspace";
     }
     return "unknown lora_status_t";
 }
@@ -505,6 +549,28 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
         return dev_status(e);
     }
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
+}
+
+lora_status_t lora_layer_apply_noalloc(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
+                                       int64_t ldw, lora_w_layout_t w_layout, const int32_t* ids,
+                                       const lora_segments_t* seg, int32_t n_rows, void* y,
+                                       lora_dtype_t y_dtype, int64_t ldy, lora_mode_t mode,
+                                       hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
+    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
+        return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    size_t need = 0;
+    lora_status_t st = lora_layer_workspace(pool, n_rows, mode, &need);
+    if (st != LORA_OK) return st;
+    if (need > LORA_NOALLOC_SCRATCH_BYTES) return LORA_E_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_address(stream, &ws);
+    if (st != LORA_OK) return st;
+    // the layer's workspace needs no zero fill: every value a kernel reads
+    // from it was written earlier in the same call
+    return lora_layer_apply(pool, x, ldx, W, ldw, w_layout, ids, seg, n_rows, y, y_dtype, ldy, mode, ws,
+                            LORA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 lora_status_t lora_base_gemm_expand_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes) {

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     from lora_bgmv_shrink_amd import binding as b
     lib = b.library()
-    for s in range(7):
+    for s in range(8):
         assert lib.lora_status_string(s).decode().startswith("LORA_")
     assert b"unknown" in lib.lora_status_string(99)
 
