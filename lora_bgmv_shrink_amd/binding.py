@@ -6,7 +6,9 @@ current stream.  Output tensors and zero-filled workspaces are allocated
 here with torch when the caller does not pass them.
 
 The functions carry the C names (see include/lora_mi355x.h for the
-semantics, layouts and error behaviour of each).  A non-OK status raises
+semantics, layouts and error behaviour of each).  Calls that take a base
+weight have no default for its storage (``w_layout``): LORA_W_OUT_IN
+([d_out, d_in]) is the fast one, and the caller says which it holds.  A non-OK status raises
 ``LoraError``.  Importing this module without the built library raises
 ``ImportError``; there is no fallback.
 """
@@ -399,7 +401,7 @@ def lora_layer_workspace(pool: Pool, n_rows: int, mode: int = LORA_MODE_AUTO) ->
 
 
 def lora_layer_apply(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
-                     w_layout: int = LORA_W_IN_OUT, seg: Optional[Segments] = None,
+                     w_layout: int, seg: Optional[Segments] = None,
                      y: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None,
                      mode: int = LORA_MODE_AUTO, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     n = ids.numel()
@@ -437,7 +439,7 @@ def lora_base_gemm_expand_workspace(pool: Pool, n_rows: int) -> int:
 
 
 def lora_base_gemm_expand(pool: Pool, x: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
-                          t: Optional[torch.Tensor], w_layout: int = LORA_W_IN_OUT,
+                          t: Optional[torch.Tensor], w_layout: int,
                           y: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None,
                           ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     n = ids.numel()
@@ -482,7 +484,7 @@ def lora_decode_finish(pool: Pool, ids: torch.Tensor, ws: torch.Tensor, y: torch
     return y
 
 
-def lora_merge_adapter(pool: Pool, W: torch.Tensor, adapter: int, w_layout: int = LORA_W_IN_OUT,
+def lora_merge_adapter(pool: Pool, W: torch.Tensor, adapter: int, w_layout: int,
                        sign: float = 1.0) -> torch.Tensor:
     """W += sign * s_a * A_a B_a in place (W of the pool's dtype, stored per
     ``w_layout``); returns W."""

@@ -1,13 +1,14 @@
 // BGMV: every row gathers its own adapter by index (decode batches).
 //
-// "Serving multiple LoRAs: segmented matrix multiplies and adapter
-// scheduling", section "Not merging the weights, computing in batches": each
-// token gathers its adapter's A and B by index and does a small
-// matrix-vector product; the shrink (x -> xA, rank r) runs first, then the
-// expand ((xA) -> (xA)B).  The adapter term is bound by reading A and B
-// ("Serving many LoRA adapters" (blog.ecitis.org), section "Batching across
-// different adapters"), so both kernels are built around wide, coalesced
-// streaming of the adapter blocks; their arithmetic is VALU.
+// The per-row form of the batched adapter term ("Serving multiple LoRAs:
+// segmented matrix multiplies and adapter scheduling", section "Not merging
+// the weights, computing in batches"): row i looks up A and B of adapter a_i
+// through the pool tables, forms t_i = x_i A (the rank-r shrink) and later
+// adds s * t_i B (the expand).  Neither step has enough arithmetic per byte
+// to need the matrix cores; both are limited by how fast the adapter blocks
+// stream in ("Serving many LoRA adapters" (blog.ecitis.org), section
+// "Batching across different adapters"), so the kernels are organised around
+// wide, coalesced loads of A and B and do their sums on the vector units.
 #include "lora_internal.hpp"
 
 namespace lora {

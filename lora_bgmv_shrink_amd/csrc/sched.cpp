@@ -29,13 +29,15 @@ int rank_class(int32_t r) {
     return c;
 }
 
-// The score, with no fused multiply-add, so that it is the same double as
-// the plain expression evaluated left to right.
+// Priority of a queued request: a fairness part that grows linearly with
+// how long it has waited, plus a bonus for locality when its adapter is
+// already active, in proportion to the rows it would add to that adapter's
+// work.  No fused multiply-add, so the policy model computes the same double.
 #pragma clang fp contract(off)
-double score(double w_fair, double w_local, double wait, bool local, int32_t rows) {
-    const double a = w_fair * wait;
-    const double b = w_local * (local ? 1.0 : 0.0);
-    return a + b * (double)rows;
+double priority(double w_fair, double w_local, double wait, bool adapter_active, int32_t rows) {
+    const double fairness = w_fair * wait;
+    const double locality_bonus = adapter_active ? w_local * (double)rows : 0.0;
+    return fairness + locality_bonus;
 }
 
 }  // namespace
@@ -139,7 +141,7 @@ lora_status_t lora_sched_step(lora_sched_t s, double now, int32_t capacity, int6
             if (s->done[i]) continue;
             const Req& r = s->queue[i];
             const bool local = r.adapter >= 0 && (s->active_prev[r.adapter] || s->in_batch[r.adapter]);
-            const double sc = score(c.w_fair, c.w_local, now - r.arrival, local, r.rows);
+            const double sc = priority(c.w_fair, c.w_local, now - r.arrival, local, r.rows);
             if (best < 0 || sc > best_score ||
                 (sc == best_score && (r.arrival < s->queue[best].arrival ||
                                       (r.arrival == s->queue[best].arrival &&

@@ -7,10 +7,10 @@ with the library.
 
 What it follows:
   * "Serving many LoRA adapters" (blog.ecitis.org), section "Adapter-aware
-    scheduling": a queued request scores its wait time (weight w_fair) plus,
-    when its adapter is already active, its token estimate (weight
-    w_local); the wait term grows without bound, so every request is
-    eventually admitted.
+    scheduling": a queued request's priority is a fairness part linear in
+    its wait (weight w_fair) plus a locality bonus, when its adapter is
+    already active, proportional to the work it brings (weight w_local per
+    row); since the fairness part keeps growing, no request waits forever.
   * "Serving multiple LoRAs: segmented matrix multiplies and adapter
     scheduling", section "Scheduling the adapters": a cap on the adapters a
     batch may hold (requests beyond it wait for a later batch); exercise 2:
@@ -69,8 +69,12 @@ class AdmissionModel:
         self.queue.append((request, adapter, rows, arrival, self.seq))
         self.seq += 1
 
-    def _score(self, wait, local, rows):
-        return self.w_fair * wait + (self.w_local * (1.0 if local else 0.0)) * rows
+    def _priority(self, wait, adapter_active, rows):
+        # fairness grows linearly with the wait; a request whose adapter is
+        # already active gets a locality bonus in proportion to its rows
+        fairness = self.w_fair * wait
+        locality_bonus = self.w_local * rows if adapter_active else 0.0
+        return fairness + locality_bonus
 
     def step(self, now, capacity):
         batch, in_batch, taken = [], [], []
@@ -85,7 +89,7 @@ class AdmissionModel:
                 if i in decided:
                     continue
                 local = a >= 0 and (a in self.prev_active or a in in_batch)
-                key = (self._score(now - arr, local, rw), -arr, -sq)
+                key = (self._priority(now - arr, local, rw), -arr, -sq)
                 if best is None or key > best[0]:
                     best = (key, i)
             if best is None:

@@ -68,7 +68,7 @@ def test_library_matches_hand_scenarios(sc):
 
 # Plausible mistakes in the model; each must break at least one scenario.
 class _NoLocality(am.AdmissionModel):
-    def _score(self, wait, local, rows):
+    def _priority(self, wait, adapter_active, rows):
         return self.w_fair * wait
 
 
@@ -102,8 +102,8 @@ class _NoRankGroups(am.AdmissionModel):
 
 
 class _LocalityNotScaledByRows(am.AdmissionModel):
-    def _score(self, wait, local, rows):
-        return self.w_fair * wait + self.w_local * (1.0 if local else 0.0)
+    def _priority(self, wait, adapter_active, rows):
+        return self.w_fair * wait + (self.w_local if adapter_active else 0.0)
 
 
 @pytest.mark.parametrize("cls", [_NoLocality, _NoCarryOver, _BaseCountsToCap, _NoCap, _LaterSubmissionWins,

@@ -203,7 +203,8 @@ def test_many_parts_offsets():
         outs = {}
         for p in check:
             x = torch.randn(24, parts[p][0], generator=g).to(torch.bfloat16)
-            outs[p] = (x, b.lora_layer_apply(c.pool(p), x.to(DEV), Ws[p].to(DEV), ids_d, mode=b.LORA_MODE_BGMV))
+            outs[p] = (x, b.lora_layer_apply(c.pool(p), x.to(DEV), Ws[p].to(DEV), ids_d, w_layout=b.LORA_W_IN_OUT,
+                                                 mode=b.LORA_MODE_BGMV))
         c.release()
         torch.cuda.synchronize()
         for p in check:
@@ -302,7 +303,7 @@ def test_fp32_cache_layer_matches_oracle():
         ids_d = torch.as_tensor(slots, device=DEV)
         for p, (di, do) in enumerate(parts):
             x = torch.randn(70, di, generator=g)
-            y = b.lora_layer_apply(c.pool(p), x.to(DEV), Ws[p].to(DEV), ids_d)
+            y = b.lora_layer_apply(c.pool(p), x.to(DEV), Ws[p].to(DEV), ids_d, w_layout=b.LORA_W_IN_OUT)
             torch.cuda.synchronize()
             ref = oracle.layer(f64(x), f64(Ws[p]), ids, _oracle_pool(aset, p), want=("y",))["y"]
             assert_close(y, ref, TOL[torch.float32], f"fp32 cache step {step} part {p}")

@@ -70,8 +70,8 @@ def test_merge_then_unmerge(name):
     pool = pool_of(p.pool)
     for a in (2, 9):
         Ws = p.W.clone()
-        b.lora_merge_adapter(pool, Ws, a, sign=1.0)
-        b.lora_merge_adapter(pool, Ws, a, sign=-1.0)
+        b.lora_merge_adapter(pool, Ws, a, b.LORA_W_IN_OUT, sign=1.0)
+        b.lora_merge_adapter(pool, Ws, a, b.LORA_W_IN_OUT, sign=-1.0)
         torch.cuda.synchronize()
         assert_close(Ws, f64(p.W), TOL[w.dtype], f"unmerged adapter {a}")
 
@@ -132,10 +132,10 @@ def test_merge_argument_errors():
     Ws = p.W.clone()
     for bad in (-1, p.pool.n_adapters):
         with pytest.raises(b.LoraError) as e:
-            b.lora_merge_adapter(pool, Ws, bad)
+            b.lora_merge_adapter(pool, Ws, bad, b.LORA_W_IN_OUT)
         assert e.value.status == b.LORA_E_ID_RANGE
     with pytest.raises(b.LoraError) as e:
-        b.lora_merge_adapter(pool, Ws, 0, sign=float("nan"))
+        b.lora_merge_adapter(pool, Ws, 0, b.LORA_W_IN_OUT, sign=float("nan"))
     assert e.value.status == b.LORA_E_INVALID
     torch.cuda.synchronize()
     assert torch.equal(Ws, p.W), "a rejected call changed W"
