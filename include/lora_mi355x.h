@@ -227,8 +227,10 @@ lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
 /* The fused layer                                                         */
 /* ---------------------------------------------------------------------- */
 
-/* Workspace bytes for lora_layer_apply (for BGMV batches of 65..2048 rows of
- * a bf16 pool this holds n_rows * d_out fp32 base partials). */
+/* Workspace bytes for lora_layer_apply.  The W layout is not an argument,
+ * so for BGMV batches of 65..1024 rows of a bf16 pool the size covers the
+ * few-hundred-row form (W stored [d_out, d_in]): segments, fp32 base
+ * partials (S * n_rows * d_out * 4 bytes, S <= 8 K slices) and t partials. */
 lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t mode,
                                    size_t* bytes);
 
@@ -239,10 +241,17 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
  * segmented gather, grouped GEMM, scatter-add, fused output).  Each GEMM
  * tile adds the expand either as extra K-blocks per distinct adapter (tiles
  * of long runs of one id) or row by row after its K loop (tiles whose rows
- * mostly carry different adapters).  BGMV batches of 65..2048 rows with a
- * bf16 pool and bf16 y take a third form: the GEMM writes the base product
- * in fp32 into the workspace, and one BGMV expand launch adds it to the
- * scaled expand and rounds y once (rows without a term get the base alone).
+ * mostly carry different adapters).  Two forms differ:
+ *  - decode (BGMV, 1..64 rows, bf16 pool, W stored [d_out, d_in]): the two
+ *    launches of lora_decode_stream / lora_decode_finish;
+ *  - few hundred rows (BGMV, 65..1024 rows, bf16 pool, W stored [d_out,
+ *    d_in]): the shrink per segment tile (rows grouped by adapter, so each
+ *    distinct adapter's A is read once per tile), the base product in fp32
+ *    K-slice partials, and a finish per segment tile that adds the partials
+ *    and the scaled expand (each adapter's B read once per tile) and rounds
+ *    y once ("Serving many LoRA adapters", section "Batching across
+ *    different adapters": the cost is reading each distinct adapter).
+ *    Segments are built in the workspace unless `seg` is given.
  *   x [n_rows, ldx]; W per w_layout with leading dimension ldw; y [n_rows,
  *   ldy] of y_dtype.  `seg` may be NULL (SGMV builds segments in the
  *   workspace) or a descriptor already built for these ids.

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "liblora_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "segments.hip", "bgmv.hip", "mfma.hip", "decode.hip", "merge.hip", "cache.hip", "sched.cpp"]
+SOURCES = ["api.hip", "segments.hip", "bgmv.hip", "mfma.hip", "decode.hip", "merge.hip", "cache.hip", "rows.hip", "sched.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

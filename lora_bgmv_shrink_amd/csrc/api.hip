@@ -74,19 +74,53 @@ bool decode_ok(const lora_pool_s* pool, int32_t n_rows) {
     return pool->dtype == LORA_BF16 && n_rows >= 1 && n_rows <= kDecodeMaxRows;
 }
 
-// AUTO: per-row gathers (BGMV) for decode-sized batches and for batches with
-// fewer than about two rows per pool adapter, where segments would mostly
-// hold one or two rows; grouping by adapter (SGMV) otherwise.
-// BGMV batches of 65..2048 rows (bf16 pool): the base product goes to fp32
-// partials and the BGMV expand adds them to the adapter term and rounds y
-// once.  With many adapters per tile the GEMM's row-wise epilogue costs more
-// than this separate pass (its B reads wait on each row's adapter); 2048 is
-// the largest batch measured.
-bool bgmv_split_ok(const lora_pool_s* pool, int32_t n_rows) {
-    return pool->dtype == LORA_BF16 && n_rows > 64 && n_rows <= 2048;
+// BGMV batches of 65..kRowsMaxRows rows of a bf16 pool with W stored
+// [d_out, d_in] take the few-hundred-row path (rows.hip): segments, the
+// shrink per segment tile, the base product in split-K partial sums, and a
+// finish that adds the partials and the scaled expand per segment tile.
+constexpr int32_t kRowsMaxRows = 1024;
+
+bool rows_ok(const lora_pool_s* pool, int32_t n_rows) {
+    return pool->dtype == LORA_BF16 && n_rows > kDecodeMaxRows && n_rows <= kRowsMaxRows &&
+           pool->dev.n_adapters <= kMaxAdaptersSegments;
 }
 
-int64_t split_ld(const PoolDev& P) { return (int64_t)align_up((size_t)P.d_out, 4); }
+// workspace of the few-hundred-row path: segments, then the plan's partials
+size_t rows_ws_bytes(const lora_pool_s* pool, int32_t n_rows) {
+    const RowsPlan R = plan_rows(pool->dev, n_rows);
+    return align_up(seg_layout(0, n_rows, pool->dev.n_adapters).end, 256) + R.bytes;
+}
+
+// The few-hundred-row path.  seg: caller's segments of these ids, or NULL
+// (built at the start of the workspace).
+hipError_t run_rows(const lora_pool_s* pool, const void* x, int64_t ldx, const void* W, int64_t ldw,
+                    const int32_t* ids, const lora_segments_t* seg, int32_t n_rows, void* y,
+                    lora_dtype_t y_dtype, int64_t ldy, void* ws, hipStream_t stream) {
+    const PoolDev& P = pool->dev;
+    uint8_t* base = (uint8_t*)ws;
+    const SegLayout L = seg_layout(0, n_rows, P.n_adapters);
+    lora_segments_t own;
+    hipError_t e = hipSuccess;
+    if (!seg) {
+        own.perm = (int32_t*)(base + L.perm);
+        own.seg_ids = (int32_t*)(base + L.seg_ids);
+        own.seg_off = (int32_t*)(base + L.seg_off);
+        own.n_seg = (int32_t*)(base + L.n_seg);
+        own.cap = L.cap;
+        e = launch_segments(ids, n_rows, P.n_adapters, &own, P.err, stream);
+        seg = &own;
+    }
+    const RowsPlan R = plan_rows(P, n_rows);
+    uint8_t* rb = base + align_up(L.end, 256);
+    float* part = (float*)(rb + R.part_off);
+    float* tpart = (float*)(rb + R.tpart_off);
+    if (e == hipSuccess)
+        e = launch_rows_adapter(P, R, x, ldx, ids, seg, n_rows, part, tpart, y, y_dtype, ldy, stream, true, false);
+    if (e == hipSuccess) e = launch_rows_gemm(P, R, x, ldx, W, ldw, nullptr, 0, false, n_rows, part, stream);
+    if (e == hipSuccess)
+        e = launch_rows_adapter(P, R, x, ldx, ids, seg, n_rows, part, tpart, y, y_dtype, ldy, stream, false, true);
+    return e;
+}
 
 lora_mode_t resolve_mode(lora_mode_t m, int32_t n_rows, int32_t n_adapters) {
     if (m != LORA_MODE_AUTO) return m;
@@ -418,8 +452,9 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
         off += bgmv_shrink_ws_bytes(plan, n_rows);
-        if (bgmv_split_ok(pool, n_rows))
-            off = align_up(off, 256) + (size_t)n_rows * split_ld(pool->dev) * 4;
+        // the W layout is not known here: room for the few-hundred-row path
+        // (W stored [d_out, d_in]) and for the fused GEMM (either layout)
+        if (rows_ok(pool, n_rows)) off = std::max(off, rows_ws_bytes(pool, n_rows));
         if (decode_ok(pool, n_rows))
             off = std::max(off, decode_ws_bytes(pool->dev, n_rows, plan_decode(pool->dev, n_rows, true)));
     } else {
@@ -477,6 +512,13 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
         if (e == hipSuccess) e = launch_decode_finish(P, D, g, y_dtype, stream);
         return dev_status(e);
     }
+    if (m == LORA_MODE_BGMV && w_layout == LORA_W_OUT_IN && rows_ok(pool, n_rows)) {
+        if (seg) {
+            lora_status_t sst = check_segments(seg, n_rows, P.n_adapters);
+            if (sst != LORA_OK) return sst;
+        }
+        return dev_status(run_rows(pool, x, ldx, W, ldw, ids, seg, n_rows, y, y_dtype, ldy, ws, stream));
+    }
     uint8_t* base = (uint8_t*)ws;
     float* t = (float*)base;
     const int64_t ldt = t_stride(P.r_max);
@@ -485,13 +527,10 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256) + ext_bytes(pool, n_rows);
     hipError_t e = hipSuccess;
     const int32_t* gemm_perm = nullptr;   // SGMV: the GEMM visits rows grouped by adapter
-    const bool split = m == LORA_MODE_BGMV && y_dtype == LORA_BF16 && bgmv_split_ok(pool, n_rows);
-    size_t split_at = 0;
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
-        split_at = align_up(after_t + bgmv_shrink_ws_bytes(plan, n_rows), 256);
         e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, base + after_t, plan,
-                               stream, split ? nullptr : t_ext, lde);
+                               stream, t_ext, lde);
     } else {
         lora_segments_t own;
         const lora_segments_t* sg = seg;
@@ -532,22 +571,6 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     g.rows_distinct = (m == LORA_MODE_BGMV);
     g.perm = gemm_perm;
     g.x_rows = n_rows;
-    if (split) {
-        // base product into fp32 partials, then y = partials + s t B, rounded once
-        float* part = (float*)(base + split_at);
-        const int64_t ldp = split_ld(P);
-        g.t = nullptr;
-        g.ldt = 0;
-        g.t_ext = nullptr;
-        g.lde = 0;
-        g.y = part;
-        g.ldy = ldp;
-        e = launch_layer_gemm(P, pool->dtype, LORA_F32, g, stream);
-        if (e == hipSuccess)
-            e = launch_bgmv_expand(P, pool->dtype, t, ldt, ids, n_rows, y, y_dtype, ldy, 0, true, stream, part,
-                                   ldp);
-        return dev_status(e);
-    }
     return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
 }
 

@@ -91,6 +91,39 @@ __device__ __forceinline__ float ext_value_f32(const float* t, int r, float s, i
     return (c < r) ? s * t[c] : 0.f;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Map workgroup b to (segment s, chunk c) over the segment tiles of height
+// BM.  Run by one whole wave; returns false past the last tile.
+__device__ inline bool find_seg_tile(const int32_t* __restrict__ seg_off, int n_seg, int BM, int b,
+                              int lane, int& s_out, int& c_out) {
+    int base = 0;
+    for (int s0 = 0; s0 < n_seg; s0 += 64) {
+        const int s = s0 + lane;
+        int cnt = 0;
+        if (s < n_seg) cnt = (seg_off[s + 1] - seg_off[s] + BM - 1) / BM;
+        const int incl = wave_incl_scan(cnt, lane);
+        const int excl = base + incl - cnt;
+        const uint64_t hit = __ballot(s < n_seg && b >= excl && b < base + incl);
+        if (hit) {
+            const int L = __ffsll((unsigned long long)hit) - 1;
+            s_out = s0 + L;
+            c_out = b - __shfl(excl, L, 64);
+            return true;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    return false;
+}
+
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -173,6 +206,32 @@ struct GemmArgs {
 };
 hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt,
                              const GemmArgs& g, hipStream_t stream);
+
+// Batches of a few hundred rows (bf16, W stored [d_out, d_in]): the base
+// product in split-K partial sums over 128 x 64 tiles, and the adapter term
+// over the segments of lora_segments_build (rows.hip).
+struct RowsPlan {
+    int32_t wide;               // 256 x 128 tiles (else 128 x 64)
+    int32_t tiles_m, tiles_n;
+    int32_t S, kslice;          // K slices of the base product
+    int32_t St, ks_len;         // K slices of the shrink
+    int64_t ldp;                // fp32 pitch of a base partial row
+    int64_t rtp;                // fp32 pitch of a t partial row
+    size_t part_off, tpart_off, tiles_off, bytes;   // workspace layout
+};
+RowsPlan plan_rows(const PoolDev& P, int32_t n_rows);
+// base partials part[S][n_rows][ldp] = x W over each K slice; q4: W holds
+// 4-bit weights (bytes [d_out][ldw]) with fp32 scales [d_out][lds] per 128
+// inputs (d_in % 128 == 0)
+hipError_t launch_rows_gemm(const PoolDev& P, const RowsPlan& R, const void* x, int64_t ldx, const void* W,
+                            int64_t ldw, const float* wscale, int64_t lds, bool q4, int32_t n_rows, float* part,
+                            hipStream_t stream);
+// shrink: tpart[St][n_rows][rtp] = x_rows A_u over each K slice, per segment
+// tile; finish: y = sum of part + s_u (sum of tpart) B_u, rounded once
+hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* x, int64_t ldx,
+                               const int32_t* ids, const lora_segments_t* seg, int32_t n_rows,
+                               const float* part, float* tpart, void* y, lora_dtype_t ydt, int64_t ldy,
+                               hipStream_t stream, bool shrink, bool finish);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 

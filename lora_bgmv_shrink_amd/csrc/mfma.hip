@@ -545,38 +545,6 @@ struct TransLoader {
 };
 
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
-    return v;
-}
-
-// Map workgroup b to (segment s, chunk c) over the segment tiles of height
-// BM.  Run by one whole wave; returns false past the last tile.
-__device__ bool find_seg_tile(const int32_t* __restrict__ seg_off, int n_seg, int BM, int b,
-                              int lane, int& s_out, int& c_out) {
-    int base = 0;
-    for (int s0 = 0; s0 < n_seg; s0 += 64) {
-        const int s = s0 + lane;
-        int cnt = 0;
-        if (s < n_seg) cnt = (seg_off[s + 1] - seg_off[s] + BM - 1) / BM;
-        const int incl = wave_incl_scan(cnt, lane);
-        const int excl = base + incl - cnt;
-        const uint64_t hit = __ballot(s < n_seg && b >= excl && b < base + incl);
-        if (hit) {
-            const int L = __ffsll((unsigned long long)hit) - 1;
-            s_out = s0 + L;
-            c_out = b - __shfl(excl, L, 64);
-            return true;
-        }
-        base += __shfl(incl, 63, 64);
-    }
-    return false;
-}
-
 // ---------------------------------------------------------------------------
 // Fused layer GEMM
 // ---------------------------------------------------------------------------

@@ -1,0 +1,751 @@
+// Batches of a few hundred rows (65 .. 2048): the base product x W, and the
+// adapter term grouped by adapter, in three launches.
+//
+// At a few hundred rows x W does about as many flops per byte of W as the
+// matrix cores deliver per byte of HBM bandwidth (256 rows: 256 flop/byte
+// against a ridge near 310), so the product has to keep the matrix cores and
+// the memory pipeline of every CU busy at once.  A CU's vector-memory path
+// (about 64 bytes a clock) is then the tightest limit, so the tile is chosen
+// for the bytes it moves per MFMA, and the launch is cut into enough
+// independent tiles (row tiles, column tiles, K slices) to cover every CU:
+//
+//   k_rows_gemm   tile = 128 rows x 64 columns x one K slice, 4 waves; wave w
+//                 owns rows 32w .. 32w + 31 and all 64 columns.  Its x
+//                 fragments come straight from memory (x is small and stays
+//                 in L2); the W block (64 columns x 128 k) is shared by the
+//                 four waves, so it goes through LDS, and the next four W
+//                 blocks are always in flight in registers (W comes from HBM
+//                 and is read once per row tile).  Writes fp32 partial sums
+//                 part[slice][row][col].
+//                 A 4-bit W (signed nibbles, one fp32 scale per output and
+//                 128 inputs) is widened exactly to bf16 on its way into LDS;
+//                 a 128-deep block is one scale group, so each block's sums
+//                 are scaled once and added ("Serving Many LoRA Adapters"
+//                 (praveentn.live), section "When It Falls Down": a 4-bit base
+//                 with BF16 adapters).
+//
+// The adapter term costs the reads of each distinct adapter's A and B
+// ("Serving many LoRA adapters" (blog.ecitis.org), section "Batching across
+// different adapters").  With skewed ids a row-by-row gather reads a popular
+// adapter once per row, so the shrink and the expand run over the segments
+// of lora_segments_build (rows grouped by adapter id, "Serving multiple
+// LoRAs: segmented matrix multiplies and adapter scheduling", section "Not
+// merging the weights, computing in batches"), and each segment tile reads
+// its adapter's slice once:
+//
+//   k_seg_shrink  (segment tile of 16 rows, K slice): t partials = x_rows A_u
+//                 on the matrix cores, A_u's slice transposed into LDS.
+//   k_seg_finish  (segment tile of 8 rows, 512 columns): y = sum of the base
+//                 partials in slice order + s_u * (t summed in slice order)
+//                 B_u, rounded once; base-only rows get the base alone.
+//
+// Every sum runs in a fixed order, so results do not depend on timing.
+#include "lora_internal.hpp"
+
+namespace lora {
+namespace {
+
+constexpr int RG_KB = 128;            // k per block (one 4-bit scale group)
+constexpr int RG_LDK = RG_KB + 8;     // bf16 pitch of a staged W column
+
+struct RowsGemmArgs {
+    const bf16* x;
+    int64_t ldx;
+    const void* W;        // bf16 [N][ldw] elements, or 4-bit bytes [N][ldw]
+    int64_t ldw;
+    const float* wscale;  // 4-bit: [N][lds]
+    int64_t lds;
+    float* part;          // [S][M][ldp]
+    int64_t ldp;
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n, S, kslice;
+};
+
+// Workgroup b -> logical tile.  Consecutive workgroups are dispatched to
+// different XCDs (b % 8), so each XCD is given a contiguous run of logical
+// tiles: the row tiles of one column tile (which read the same W block) and
+// neighbouring column tiles (which read the same x slice) share its L2.
+__device__ __forceinline__ int xcd_tile(int b, int G) {
+    const int q = G >> 3, rem = G & 7;
+    const int xc = b & 7, local = b >> 3;
+    return xc * q + min(xc, rem) + local;
+}
+
+__device__ __forceinline__ bf16x8_t ld8_guard(const bf16* p, int valid) {
+    union { bf16x8_t v; bf16 e[8]; } u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u.e[e] = (e < valid) ? p[e] : (bf16)0;
+    return u.v;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Eight signed 4-bit values (element e in bits 4e .. 4e+3) as exact bf16.
+__device__ __forceinline__ u32x4 widen8_q4(uint32_t w) {
+    union { u32x4 v; bf16 e[8]; } u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int q = ((int)(w << (28 - 4 * e))) >> 28;
+        u.e[e] = (bf16)(__float_as_uint((float)q) >> 16);
+    }
+    return u.v;
+}
+
+// NW waves, each owning 32 rows and all BN columns of the tile (BM = 32 NW
+// rows); RING W and x blocks in flight per thread.
+template <bool Q4, int NW, int BN, int RING>
+__global__ __launch_bounds__(NW * 64) void k_rows_gemm(RowsGemmArgs a) {
+    constexpr int RG_BM = 32 * NW;
+    constexpr int RG_BN = BN;
+    constexpr int RG_NT = NW * 64;
+    constexpr int NB = BN / 16;                                   // 16-column MFMA blocks
+    constexpr int RG_WPT_B = RG_BN * RG_KB * 2 / 16 / RG_NT;      // 16-byte W pieces per thread (bf16)
+    constexpr int CPP = RG_NT / 16;                               // columns per pass of the W loader
+    static_assert(RG_WPT_B * RG_NT * 16 == RG_BN * RG_KB * 2, "W block does not split evenly");
+    static_assert(!Q4 || RG_BN * 4 == RG_NT, "4-bit loader: one 16-byte piece per thread");
+    __shared__ __attribute__((aligned(16))) bf16 sW[2][RG_BN * RG_LDK];
+    __shared__ float sSc[2][RG_BN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int G = a.tiles_m * a.tiles_n * a.S;
+    const int L = xcd_tile(blockIdx.x, G);
+    const int tm = L % a.tiles_m;
+    const int rest = L / a.tiles_m;
+    const int tn = rest % a.tiles_n;
+    const int ks = rest / a.tiles_n;
+    const int m0 = tm * RG_BM;
+    const int n0 = tn * RG_BN;
+    const int kbeg = ks * a.kslice;
+    const int klen = min(a.K, kbeg + a.kslice) - kbeg;
+
+    // x rows of this wave (rows past M read row M-1; never stored)
+    const bf16* xr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wave * 32 + i * 16 + lr;
+        xr[i] = a.x + (int64_t)min(m, a.M - 1) * a.ldx + kbeg + kq;
+    }
+    // W pieces of this thread.  bf16: piece v = tid + 256 p covers column
+    // v / 16 and k-piece v % 16 (8 k) of the block; 4-bit: column tid / 4 and
+    // k 32 (tid % 4) .. + 32 (16 bytes).
+    constexpr int WPT = Q4 ? 1 : RG_WPT_B;
+    const bf16* wb[WPT];
+    const uint8_t* wq = nullptr;
+    const float* wsp = nullptr;
+    if constexpr (Q4) {
+        const int c = tid >> 2;
+        const int n = min(n0 + c, a.N - 1);
+        wq = (const uint8_t*)a.W + (int64_t)n * a.ldw + kbeg / 2 + (tid & 3) * 16;
+        wsp = a.wscale + (int64_t)n * a.lds + kbeg / RG_KB;
+    } else {
+#pragma unroll
+        for (int p = 0; p < WPT; ++p) {
+            const int c = (tid >> 4) + CPP * p;
+            const int n = min(n0 + c, a.N - 1);
+            wb[p] = (const bf16*)a.W + (int64_t)n * a.ldw + kbeg + (tid & 15) * 8;
+        }
+    }
+
+    // the register ring: four W blocks and two x blocks, as separate named
+    // arrays so that every index is static
+    u32x4 w0[WPT], w1[WPT], w2[WPT], w3[WPT];
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    bf16x8_t x0[2][4], x1[2][4], x2[2][4], x3[2][4];
+    f32x4_t acc[2][NB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // whole blocks: plain 16-byte loads, no branch (the main loop stays
+    // branch-free so that each wait covers only the loads it needs)
+    auto load_w = [&](u32x4 (&dst)[WPT], float& sc, int kb) __attribute__((always_inline)) {
+        const int k0 = kb * RG_KB;
+        if constexpr (Q4) {
+            dst[0] = *(const u32x4*)(wq + k0 / 2);
+            sc = wsp[kb];
+        } else {
+#pragma unroll
+            for (int p = 0; p < WPT; ++p) dst[p] = *(const u32x4*)(wb[p] + k0);
+        }
+    };
+    auto load_x = [&](bf16x8_t (&dst)[2][4], int kb) __attribute__((always_inline)) {
+        const int k0 = kb * RG_KB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dst[i][s] = *(const bf16x8_t*)(xr[i] + k0 + s * 32);
+    };
+    auto store_w = [&](const u32x4 (&src)[WPT], float sc, int stage) __attribute__((always_inline)) {
+        bf16* s = sW[stage];
+        if constexpr (Q4) {
+            const int c = tid >> 2;
+            const int k = (tid & 3) * 32;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) *(u32x4*)(s + c * RG_LDK + k + h * 8) = widen8_q4(src[0][h]);
+            if ((tid & 3) == 0) sSc[stage][c] = sc;
+        } else {
+#pragma unroll
+            for (int p = 0; p < WPT; ++p) {
+                const int c = (tid >> 4) + CPP * p;
+                *(u32x4*)(s + c * RG_LDK + (tid & 15) * 8) = src[p];
+            }
+        }
+    };
+    auto mma = [&](const bf16x8_t (&xa)[2][4], int stage) __attribute__((always_inline)) {
+        const bf16* s = sW[stage];
+        f32x4_t g[2][NB];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) g[i][j] = Q4 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            bf16x8_t b[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) b[j] = *(const bf16x8_t*)(s + (j * 16 + lr) * RG_LDK + st * 32 + kq);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    g[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i][st], b[j], g[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if constexpr (Q4) {
+                const float sc = sSc[stage][j * 16 + lr];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][j] += sc * g[i][j];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][j] = g[i][j];
+            }
+        }
+    };
+    // One block: its W goes from registers to LDS stage kb & 1 (last read by
+    // block kb - 2, whose MFMAs every wave finished before the barrier of
+    // block kb - 1), then the MFMAs, then block kb + RING (W and x) is
+    // requested into the registers this block used.  Loads complete in
+    // order, so x is requested as far ahead as W: a wait for x never waits
+    // on a W block that is still young.  Requests past the last whole block
+    // fetch that block again (from cache, never used), so the loop has no
+    // branch around its loads.
+#define RG_STEP(W_, S_, X_, KB_)                               \
+    {                                                          \
+        const int kb_ = (KB_);                                 \
+        store_w(W_, S_, kb_ & 1);                              \
+        __syncthreads();                                       \
+        load_w(W_, S_, min(kb_ + RING, last));                 \
+        mma(X_, kb_ & 1);                                      \
+        load_x(X_, min(kb_ + RING, last));                     \
+    }
+
+    static_assert(RING == 3 || RING == 4, "register ring of 3 or 4 blocks");
+    const int nfull = klen / RG_KB;   // whole blocks (a 4-bit W has no partial block)
+    if (nfull > 0) {
+        const int last = nfull - 1;
+        load_w(w0, s0, 0);
+        load_x(x0, 0);
+        load_w(w1, s1, min(1, last));
+        load_x(x1, min(1, last));
+        load_w(w2, s2, min(2, last));
+        load_x(x2, min(2, last));
+        if constexpr (RING == 4) {
+            load_w(w3, s3, min(3, last));
+            load_x(x3, min(3, last));
+        }
+        int kb = 0;
+        for (; kb + RING <= nfull; kb += RING) {
+            RG_STEP(w0, s0, x0, kb);
+            RG_STEP(w1, s1, x1, kb + 1);
+            RG_STEP(w2, s2, x2, kb + 2);
+            if constexpr (RING == 4) RG_STEP(w3, s3, x3, kb + 3);
+        }
+        if (kb < nfull) RG_STEP(w0, s0, x0, kb);
+        if (kb + 1 < nfull) RG_STEP(w1, s1, x1, kb + 1);
+        if constexpr (RING == 4)
+            if (kb + 2 < nfull) RG_STEP(w2, s2, x2, kb + 2);
+    }
+#undef RG_STEP
+    if constexpr (!Q4) {
+        if (klen > nfull * RG_KB) {
+            // ragged last block: element-wise loads, zero past the slice
+            const int k0 = nfull * RG_KB;
+            u32x4 tw[WPT];
+#pragma unroll
+            for (int p = 0; p < WPT; ++p) {
+                const int valid = min(8, max(0, klen - k0 - (tid & 15) * 8));
+                tw[p] = __builtin_bit_cast(u32x4, ld8_guard(wb[p] + k0, valid));
+            }
+            bf16x8_t tx[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int valid = min(8, max(0, klen - (k0 + s * 32 + kq)));
+                    tx[i][s] = ld8_guard(xr[i] + k0 + s * 32, valid);
+                }
+            float dummy = 0.f;
+            store_w(tw, dummy, nfull & 1);
+            __syncthreads();
+            mma(tx, nfull & 1);
+        }
+    }
+
+    // partial sums: lane l holds rows (l / 16) * 4 + q of column l % 16 of
+    // each 16 x 16 block
+    float* out = a.part + (int64_t)ks * a.M * a.ldp;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int n = n0 + j * 16 + lr;
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = m0 + wave * 32 + i * 16 + (lane >> 4) * 4 + q;
+                if (m < a.M) out[(int64_t)m * a.ldp + n] = acc[i][j][q];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Shrink over segment tiles
+// ---------------------------------------------------------------------------
+
+constexpr int SS_ROWS = 16;    // rows per segment tile (one MFMA block)
+constexpr int SS_NT = 256;
+constexpr int SS_MAX_LDS = 72 * 1024;   // x + transposed A staging
+
+// Per segment tile of SS_ROWS rows, written by the shrink (slice 0) for the
+// finish: where its rows are in perm, and its adapter's rank (0: base-only
+// rows), scale and B offset.  valid = 0 past the last tile.
+struct TileRec {
+    int64_t b_off;
+    int32_t valid, row0, cnt, rank;
+    float scale;
+    int32_t pad;
+};
+
+struct SegShrinkArgs {
+    TileRec* tiles;
+    const bf16* x;
+    int64_t ldx;
+    const int32_t* perm;
+    const int32_t* seg_ids;
+    const int32_t* seg_off;
+    const int32_t* n_seg;
+    float* tpart;      // [St][M][rtp]
+    int64_t rtp;
+    int32_t M;
+    int32_t ks_len;    // k per slice (multiple of 128)
+    int32_t kp;        // LDS pitch (bf16) of a staged row: ks_len + 8
+};
+
+__global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int sRow[SS_ROWS];
+    __shared__ int sInfo[3];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    if (wave == 0) {
+        int s = 0, c = 0;
+        const bool found = find_seg_tile(a.seg_off, *a.n_seg, SS_ROWS, blockIdx.x, lane, s, c);
+        if (lane == 0) {
+            sInfo[0] = found ? 1 : 0;
+            sInfo[1] = s;
+            sInfo[2] = c;
+        }
+    }
+    __syncthreads();
+    const int ks = blockIdx.y;
+    if (!sInfo[0]) {
+        if (ks == 0 && tid == 0) a.tiles[blockIdx.x].valid = 0;
+        return;
+    }
+    const int s = sInfo[1];
+    const int u = a.seg_ids[s];
+    const bool ok = id_ok(u, P.n_adapters);
+    const int row0 = a.seg_off[s] + sInfo[2] * SS_ROWS;
+    const int cnt = min(SS_ROWS, a.seg_off[s + 1] - row0);
+    if (ks == 0 && tid == 0) {
+        TileRec rec;
+        rec.b_off = ok ? P.b_off[u] : 0;
+        rec.valid = 1;
+        rec.row0 = row0;
+        rec.cnt = cnt;
+        rec.rank = ok ? P.ranks[u] : 0;
+        rec.scale = ok ? P.scales[u] : 0.f;
+        rec.pad = 0;
+        a.tiles[blockIdx.x] = rec;
+    }
+    if (!ok) return;   // base-only rows (and invalid ids): no t
+    if (tid < SS_ROWS) sRow[tid] = tid < cnt ? a.perm[row0 + tid] : -1;
+    const int r = P.ranks[u];
+    const int RB = (r + 15) / 16;   // 16-rank blocks
+    const int kbeg = ks * a.ks_len;
+    const int klen = min(P.d_in, kbeg + a.ks_len) - kbeg;
+    const int KP = a.kp;
+    bf16* sX = (bf16*)smem;                  // [16][KP]
+    bf16* sA = sX + SS_ROWS * KP;            // [RB * 16][KP], A_u transposed
+    const bf16* Au = (const bf16*)P.A + P.a_off[u] + (int64_t)kbeg * r;
+    __syncthreads();
+
+    // x rows of the tile, 16-byte pieces; k past the slice and rows past the
+    // tile are 0
+    const int pieces = a.ks_len / 8;
+    for (int v = tid; v < SS_ROWS * pieces; v += SS_NT) {
+        const int m = v / pieces;
+        const int k = (v - m * pieces) * 8;
+        bf16x8_t val{};
+        const int row = sRow[m];
+        if (row >= 0 && k < klen) {
+            const bf16* src = a.x + (int64_t)row * a.ldx + kbeg + k;
+            val = (k + 8 <= klen) ? *(const bf16x8_t*)src : ld8_guard(src, klen - k);
+        }
+        *(bf16x8_t*)(sX + m * KP + k) = val;
+    }
+    // A_u[k][j] -> sA[j][k]; ranks past r and k past the slice are 0
+    if (P.vec_a && r % 8 == 0) {
+        const int G = r / 8;
+        for (int v = tid; v < a.ks_len * G; v += SS_NT) {
+            const int k = v / G;
+            const int j0 = (v - k * G) * 8;
+            union { uint4 q; bf16 e[8]; } w;
+            w.q = k < klen ? *(const uint4*)(Au + (int64_t)k * r + j0) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sA[(j0 + e) * KP + k] = w.e[e];
+        }
+        for (int v = tid; v < (RB * 16 - r) * a.ks_len; v += SS_NT) {
+            const int j = r + v / a.ks_len;
+            sA[j * KP + v % a.ks_len] = 0;
+        }
+    } else {
+        for (int v = tid; v < RB * 16 * a.ks_len; v += SS_NT) {
+            const int k = v / (RB * 16);
+            const int j = v - k * (RB * 16);
+            sA[j * KP + k] = (j < r && k < klen) ? Au[(int64_t)k * r + j] : (bf16)0;
+        }
+    }
+    __syncthreads();
+
+    // wave w takes k-steps w, w + 4, ...; acc[jb] = x rows x ranks 16 jb ..
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nsteps = a.ks_len / 32;
+    for (int st = wave; st < nsteps; st += 4) {
+        const bf16x8_t xa = *(const bf16x8_t*)(sX + lr * KP + st * 32 + kq);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            if (jb < RB) {
+                const bf16x8_t bb = *(const bf16x8_t*)(sA + (jb * 16 + lr) * KP + st * 32 + kq);
+                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bb, acc[jb], 0, 0, 0);
+            }
+    }
+    __syncthreads();   // staging no longer read: reuse it for the wave sums
+    float* red = (float*)smem;   // [4][16][64]
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+        if (jb < RB)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                red[(wave * SS_ROWS + (lane >> 4) * 4 + q) * 64 + jb * 16 + lr] = acc[jb][q];
+    __syncthreads();
+    for (int v = tid; v < SS_ROWS * 64; v += SS_NT) {
+        const int m = v >> 6;
+        const int j = v & 63;
+        if (m >= cnt || j >= r) continue;
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) t += red[(w * SS_ROWS + m) * 64 + j];
+        a.tpart[((int64_t)ks * a.M + sRow[m]) * a.rtp + j] = t;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Finish over segment tiles: partial sums + scaled expand, y rounded once
+// ---------------------------------------------------------------------------
+
+constexpr int FS_NT = 256;             // 4 waves
+constexpr int FS_VE = 8;               // columns per lane (16-byte B pieces)
+constexpr int FS_COLS = 64 * FS_VE;    // columns per workgroup
+constexpr int FS_RC = 16;              // rank rows of B requested together
+
+struct SegFinishArgs {
+    const TileRec* tiles;
+    const int32_t* ids;
+    const int32_t* perm;
+    const float* part;    // [S][M][ldp]
+    int64_t ldp;
+    int32_t S;
+    const float* tpart;   // [St][M][rtp]
+    int64_t rtp;
+    int32_t St;
+    int32_t M;
+    int32_t n_chunks;     // column chunks of FS_COLS
+    void* y;
+    int64_t ldy;
+};
+
+// Workgroup (segment tile, 512-column chunk).  The tile's record comes from
+// the shrink (scalar loads); its t (rows x rank, summed over the shrink
+// slices in order) is formed in LDS.  Wave w then produces rows w, w + 4, ...
+// of the tile, one 8-column piece per lane: the base partials of every K
+// slice (SB >= S requested together, indices past S clamped and masked, so
+// the loads carry no branch) added in slice order, plus s_u * t B_u with the
+// r rows of B_u's piece (the tile's rows share the adapter, so after the
+// first wave they come from L1), y rounded once.
+template <typename TY, int SB>
+__global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a) {
+    __shared__ float sT[SS_ROWS][64];
+    __shared__ int sRow[SS_ROWS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tile = blockIdx.x / a.n_chunks;
+    const int ch = blockIdx.x - tile * a.n_chunks;
+    const TileRec* rp = a.tiles + tile;
+    if (!uload(&rp->valid, 0)) return;
+    const int row0 = uload(&rp->row0, 0);
+    const int cnt = uload(&rp->cnt, 0);
+    const int r = uload(&rp->rank, 0);
+    const float sc = uload(&rp->scale, 0);
+    const int64_t boff = uload(&rp->b_off, 0);
+    if (tid < SS_ROWS) sRow[tid] = a.perm[row0 + min(tid, cnt - 1)];
+    __syncthreads();
+    if (r > 0) {
+        // t[m][j] = sum over the shrink slices in order, four requested at once
+        const int64_t sl = (int64_t)a.M * a.rtp;
+        for (int v = tid; v < SS_ROWS * 64; v += FS_NT) {
+            const int m = v >> 6;
+            const int j = v & 63;
+            if (m >= cnt || j >= r) continue;
+            const float* __restrict__ tp = a.tpart + (int64_t)sRow[m] * a.rtp + j;
+            float t = 0.f;
+            for (int k0 = 0; k0 < a.St; k0 += 4) {
+                float q[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[e] = tp[(int64_t)min(k0 + e, a.St - 1) * sl];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t += (k0 + e < a.St) ? q[e] : 0.f;
+            }
+            sT[m][j] = t;
+        }
+    } else if (ch == 0 && tid < cnt) {
+        if (a.ids[sRow[tid]] != -1) flag_bad_id(P.err);   // invalid ids run as base-only rows
+    }
+    __syncthreads();
+
+    const int N = P.d_out;
+    const int col = ch * FS_COLS + lane * FS_VE;
+    if (col >= N) return;
+    const bool fast = col + FS_VE <= N && P.vec_b && ((a.ldy * (int64_t)sizeof(TY)) & 15) == 0;
+    const int valid = min(FS_VE, N - col);
+    const int64_t slice = (int64_t)a.M * a.ldp;
+    const float* __restrict__ part = a.part;
+    TY* __restrict__ Y = (TY*)a.y;
+    const bf16* __restrict__ Bu = (const bf16*)P.B + boff + col;
+    for (int m = wave; m < cnt; m += FS_NT / 64) {
+        const int row = sRow[m];
+        if (!fast) {
+            // ragged or unaligned piece: one element at a time
+            for (int e = 0; e < valid; ++e) {
+                float v = 0.f;
+                for (int k = 0; k < a.S; ++k) v += part[k * slice + (int64_t)row * a.ldp + col + e];
+                float ex = 0.f;
+                for (int j = 0; j < r; ++j) ex += sT[m][j] * to_f32(Bu[(int64_t)j * N + e]);
+                Y[(int64_t)row * a.ldy + col + e] = from_f32<TY>(v + sc * ex);
+            }
+            continue;
+        }
+        float4 pv[SB][2];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const float* q = part + (int64_t)min(k, a.S - 1) * slice + (int64_t)row * a.ldp + col;
+            pv[k][0] = *(const float4*)q;
+            pv[k][1] = *(const float4*)(q + 4);
+        }
+        float ex[FS_VE];
+#pragma unroll
+        for (int e = 0; e < FS_VE; ++e) ex[e] = 0.f;
+        for (int j0 = 0; j0 < r; j0 += FS_RC) {
+            uint4 bv[FS_RC];
+#pragma unroll
+            for (int q = 0; q < FS_RC; ++q)   // rows past r meet t = 0
+                bv[q] = *(const uint4*)(Bu + (int64_t)min(j0 + q, r - 1) * N);
+#pragma unroll
+            for (int q = 0; q < FS_RC; ++q) {
+                const float tj = (j0 + q < r) ? sT[m][j0 + q] : 0.f;
+                union { uint4 v; bf16 e[8]; } w;
+                w.v = bv[q];
+#pragma unroll
+                for (int e = 0; e < FS_VE; ++e) ex[e] += tj * to_f32(w.e[e]);
+            }
+        }
+        float v[FS_VE];
+#pragma unroll
+        for (int e = 0; e < FS_VE; ++e) v[e] = 0.f;
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            if (k >= a.S) break;
+            v[0] += pv[k][0].x; v[1] += pv[k][0].y; v[2] += pv[k][0].z; v[3] += pv[k][0].w;
+            v[4] += pv[k][1].x; v[5] += pv[k][1].y; v[6] += pv[k][1].z; v[7] += pv[k][1].w;
+        }
+#pragma unroll
+        for (int e = 0; e < FS_VE; ++e) v[e] += sc * ex[e];
+        TY* yr = Y + (int64_t)row * a.ldy + col;
+        if constexpr (sizeof(TY) == 2) {
+            union { uint4 q; bf16 e[8]; } o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o.e[e] = f32_to_bf16(v[e]);
+            *(uint4*)yr = o.q;
+        } else {
+            *(float4*)yr = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(yr + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    }
+}
+
+// segment tiles of SS_ROWS rows: at most one partial tile per segment on top
+// of the full ones (the grid is sized without reading the segment count)
+int64_t rows_tiles(int32_t n_rows, int32_t n_bins) {
+    return ceil_div(n_rows, SS_ROWS) + std::min<int64_t>(n_rows, n_bins);
+}
+
+}  // namespace
+
+RowsPlan plan_rows(const PoolDev& P, int32_t n_rows) {
+    RowsPlan R;
+    const int K = P.d_in, N = P.d_out;
+    // long or wide projections: 256 x 128 tiles (x re-read once per 128
+    // columns, W once per 256 rows; split K covers the CUs); the others
+    // 128 x 64 tiles, for more workgroups.  Measured on the skewed 256-row
+    // 8B batch: gate 4096x14336 87 -> 55 us, down 14336x4096 75 -> 54 us; q
+    // 4096x4096 is no faster wide (its fp32 partials grow with the split).
+    R.wide = (N >= 8192 || K >= 8192) ? 1 : 0;
+    const int bm = R.wide ? 256 : 128, bn = R.wide ? 128 : 64;
+    R.tiles_m = (int32_t)ceil_div(n_rows, bm);
+    R.tiles_n = (int32_t)ceil_div(N, bn);
+    // split K (into at most 8 slices) until the launch covers the CUs
+    const int kblocks = (int)ceil_div(K, RG_KB);
+    int S = 1;
+    while ((int64_t)R.tiles_m * R.tiles_n * S < 200 && kblocks / (2 * S) >= 4 && S < 8) S *= 2;
+    R.kslice = (int32_t)(ceil_div(kblocks, S) * RG_KB);
+    R.S = (int32_t)ceil_div(K, R.kslice);
+    R.ldp = (int64_t)align_up((size_t)N, 4);
+    // shrink: K slices sized so that x and the transposed A fit the LDS budget
+    const int rb = (int)ceil_div(P.r_max, 16) * 16;
+    // (long K: 512-deep slices, twice the workgroups; 14336-deep down
+    // projection 47 -> 35 us)
+    int ks_len = K >= 8192 ? 512 : 1024;
+    while (ks_len > 128 && (SS_ROWS + rb) * (ks_len + 8) * 2 > SS_MAX_LDS) ks_len /= 2;
+    R.ks_len = ks_len;
+    R.St = (int32_t)ceil_div(K, ks_len);
+    R.rtp = (int64_t)align_up((size_t)P.r_max, 4);
+    const size_t part = align_up((size_t)R.S * n_rows * R.ldp * 4, 256);
+    const size_t tpart = align_up((size_t)R.St * n_rows * R.rtp * 4, 256);
+    const size_t tiles = align_up((size_t)rows_tiles(n_rows, P.n_adapters + 1) * sizeof(TileRec), 256);
+    R.part_off = 0;
+    R.tpart_off = part;
+    R.tiles_off = part + tpart;
+    R.bytes = part + tpart + tiles;
+    return R;
+}
+
+hipError_t launch_rows_gemm(const PoolDev& P, const RowsPlan& R, const void* x, int64_t ldx, const void* W,
+                            int64_t ldw, const float* wscale, int64_t lds, bool q4, int32_t n_rows, float* part,
+                            hipStream_t stream) {
+    RowsGemmArgs a;
+    a.x = (const bf16*)x;
+    a.ldx = ldx;
+    a.W = W;
+    a.ldw = ldw;
+    a.wscale = wscale;
+    a.lds = lds;
+    a.part = part;
+    a.ldp = R.ldp;
+    a.M = n_rows;
+    a.N = P.d_out;
+    a.K = P.d_in;
+    a.tiles_m = R.tiles_m;
+    a.tiles_n = R.tiles_n;
+    a.S = R.S;
+    a.kslice = R.kslice;
+    dim3 grid((unsigned)(R.tiles_m * R.tiles_n * R.S));
+    if (q4) hipLaunchKernelGGL((k_rows_gemm<true, 4, 64, 4>), grid, dim3(256), 0, stream, a);
+    else if (R.wide) hipLaunchKernelGGL((k_rows_gemm<false, 8, 128, 3>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((k_rows_gemm<false, 4, 64, 4>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* x, int64_t ldx,
+                               const int32_t* ids, const lora_segments_t* seg, int32_t n_rows,
+                               const float* part, float* tpart, void* y, lora_dtype_t ydt, int64_t ldy,
+                               hipStream_t stream, bool shrink, bool finish) {
+    const int n_bins = P.n_adapters + 1;
+    // the tile records follow the t partials (RowsPlan::tiles_off)
+    TileRec* tiles = (TileRec*)((uint8_t*)tpart + (R.tiles_off - R.tpart_off));
+    if (shrink) {
+        SegShrinkArgs s;
+        s.tiles = tiles;
+        s.x = (const bf16*)x;
+        s.ldx = ldx;
+        s.perm = seg->perm;
+        s.seg_ids = seg->seg_ids;
+        s.seg_off = seg->seg_off;
+        s.n_seg = seg->n_seg;
+        s.tpart = tpart;
+        s.rtp = R.rtp;
+        s.M = n_rows;
+        s.ks_len = R.ks_len;
+        s.kp = R.ks_len + 8;
+        const int rb = (int)ceil_div(P.r_max, 16) * 16;
+        const size_t lds = std::max<size_t>((size_t)(SS_ROWS + rb) * s.kp * 2, 4 * SS_ROWS * 64 * 4);
+        dim3 grid((unsigned)rows_tiles(n_rows, n_bins), (unsigned)R.St);
+        hipLaunchKernelGGL(k_seg_shrink, grid, dim3(SS_NT), lds, stream, P, s);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (finish) {
+        SegFinishArgs f;
+        f.tiles = tiles;
+        f.ids = ids;
+        f.perm = seg->perm;
+        f.part = part;
+        f.ldp = R.ldp;
+        f.S = R.S;
+        f.tpart = tpart;
+        f.rtp = R.rtp;
+        f.St = R.St;
+        f.M = n_rows;
+        f.n_chunks = (int32_t)ceil_div(P.d_out, FS_COLS);
+        f.y = y;
+        f.ldy = ldy;
+        dim3 grid((unsigned)(rows_tiles(n_rows, n_bins) * f.n_chunks));
+#define LORA_FIN(TY_, SB_) hipLaunchKernelGGL((k_seg_finish<TY_, SB_>), grid, dim3(FS_NT), 0, stream, P, f)
+        if (ydt == LORA_BF16) {
+            if (R.S <= 1) LORA_FIN(bf16, 1);
+            else if (R.S <= 2) LORA_FIN(bf16, 2);
+            else if (R.S <= 4) LORA_FIN(bf16, 4);
+            else LORA_FIN(bf16, 8);
+        } else {
+            if (R.S <= 1) LORA_FIN(float, 1);
+            else if (R.S <= 2) LORA_FIN(float, 2);
+            else if (R.S <= 4) LORA_FIN(float, 4);
+            else LORA_FIN(float, 8);
+        }
+#undef LORA_FIN
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace lora

@@ -22,15 +22,6 @@ constexpr int SEG_WAVES = SEG_THREADS / 64;
 constexpr int SEG_HIST_INTS = 16384;   // per-wave histograms, 64 KiB
 constexpr int SEG_MAX_BINS = 16384;    // n_adapters + 1
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
-    return v;
-}
-
 __global__ __launch_bounds__(SEG_THREADS) void k_segments(const int32_t* __restrict__ ids, int32_t n,
                                                           int32_t n_ad, int32_t* __restrict__ perm,
                                                           int32_t* __restrict__ seg_ids,

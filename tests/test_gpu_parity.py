@@ -265,7 +265,7 @@ def test_walkthrough_shared_adapter():
     p = w.projections[0]
     pool = pool_of(p.pool)
     for m in (b.LORA_MODE_BGMV, b.LORA_MODE_SGMV):
-        y = b.lora_layer_apply(pool, p.x, p.W, ids_dev(w), mode=m)
+        y = b.lora_layer_apply(pool, p.x, p.W, ids_dev(w), w_layout=b.LORA_W_IN_OUT, mode=m)
         torch.cuda.synchronize()
         assert_close(y, o["y"], 1e-4, f"walk-through mode {m}")
         assert torch.equal(y[0], y[2]), "rows sharing T1 with equal inputs differ"
@@ -327,9 +327,9 @@ def test_base_only_rows_and_all_base():
     p = w.projections[0]
     pool = pool_of(p.pool)
     ids = ids_dev(w)
-    y = b.lora_layer_apply(pool, p.x, p.W, ids, y_dtype=torch.float32)
+    y = b.lora_layer_apply(pool, p.x, p.W, ids, w_layout=b.LORA_W_IN_OUT, y_dtype=torch.float32)
     allbase = torch.full_like(ids, -1)
-    y0 = b.lora_layer_apply(pool, p.x, p.W, allbase, y_dtype=torch.float32)
+    y0 = b.lora_layer_apply(pool, p.x, p.W, allbase, w_layout=b.LORA_W_IN_OUT, y_dtype=torch.float32)
     torch.cuda.synchronize()
     base_ref = f64(p.x) @ f64(p.W)
     assert_close(y0, base_ref, TOL[w.dtype], "all base-only = x W")
@@ -337,8 +337,8 @@ def test_base_only_rows_and_all_base():
     assert torch.equal(y[mask], y0[mask]), "base-only rows depend on other rows' adapters"
     # bf16 y in BGMV mode (200 rows: base product in fp32 partials, then the
     # expand adds the term and rounds once; base-only rows take the partials)
-    yb = b.lora_layer_apply(pool, p.x, p.W, ids, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
-    yb0 = b.lora_layer_apply(pool, p.x, p.W, allbase, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
+    yb = b.lora_layer_apply(pool, p.x, p.W, ids, w_layout=b.LORA_W_IN_OUT, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
+    yb0 = b.lora_layer_apply(pool, p.x, p.W, allbase, w_layout=b.LORA_W_IN_OUT, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert_close(yb0, base_ref, TOL[torch.bfloat16], "all base-only = x W (bf16 y)")
     assert torch.equal(yb[mask], yb0[mask]), "base-only rows depend on other rows' adapters (bf16 y)"
@@ -359,13 +359,13 @@ def test_out_of_range_ids_flag_and_base_only():
     ids = torch.as_tensor(bad, device=DEV)
     assert b.lora_pool_last_error(pool) == 0
     for m in (b.LORA_MODE_BGMV, b.LORA_MODE_SGMV):
-        y = b.lora_layer_apply(pool, p.x, p.W, ids, mode=m, y_dtype=torch.float32)
+        y = b.lora_layer_apply(pool, p.x, p.W, ids, w_layout=b.LORA_W_IN_OUT, mode=m, y_dtype=torch.float32)
         assert b.lora_pool_last_error(pool) & 1 == 1
         assert b.lora_pool_last_error(pool) == 0
         base_ref = f64(p.x[[3, 50, 100]]) @ f64(p.W)
         assert_close(y[[3, 50, 100]], base_ref, TOL[w.dtype], f"invalid rows base-only mode {m}")
     # bf16 y in BGMV mode: the expand that adds the fp32 base partials flags too
-    y = b.lora_layer_apply(pool, p.x, p.W, ids, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
+    y = b.lora_layer_apply(pool, p.x, p.W, ids, w_layout=b.LORA_W_IN_OUT, mode=b.LORA_MODE_BGMV, y_dtype=torch.bfloat16)
     assert b.lora_pool_last_error(pool) & 1 == 1
     assert b.lora_pool_last_error(pool) == 0
     assert_close(y[[3, 50, 100]], f64(p.x[[3, 50, 100]]) @ f64(p.W), TOL[torch.bfloat16], "invalid rows, bf16 y")
@@ -378,18 +378,18 @@ def test_empty_and_single_row():
     p = w.projections[0]
     pool = pool_of(p.pool)
     ids0 = torch.zeros(0, dtype=torch.int32, device=DEV)
-    y0 = b.lora_layer_apply(pool, p.x[:0], p.W, ids0)
+    y0 = b.lora_layer_apply(pool, p.x[:0], p.W, ids0, w_layout=b.LORA_W_IN_OUT)
     seg0 = b.lora_segments_build(ids0, p.pool.n_adapters)
     torch.cuda.synchronize()
     assert y0.shape[0] == 0 and int(seg0.n_seg.item()) == 0
     for r in (0, 7):
-        y1 = b.lora_layer_apply(pool, p.x[r:r + 1], p.W, ids_dev(w)[r:r + 1], y_dtype=torch.float32)
+        y1 = b.lora_layer_apply(pool, p.x[r:r + 1], p.W, ids_dev(w)[r:r + 1], w_layout=b.LORA_W_IN_OUT, y_dtype=torch.float32)
         torch.cuda.synchronize()
         assert_close(y1, o["y"][r:r + 1], TOL[w.dtype], f"single row {r}")
     one = torch.full_like(ids_dev(w), 4)
     ref = run_oracle(wl.Workload("one", w.dtype, np.full(w.n_rows, 4, np.int32), w.projections))
     for m in (b.LORA_MODE_BGMV, b.LORA_MODE_SGMV):
-        y = b.lora_layer_apply(pool, p.x, p.W, one, mode=m, y_dtype=torch.float32)
+        y = b.lora_layer_apply(pool, p.x, p.W, one, w_layout=b.LORA_W_IN_OUT, mode=m, y_dtype=torch.float32)
         torch.cuda.synchronize()
         assert_close(y, ref["y"], TOL[w.dtype], f"single adapter mode {m}")
 
@@ -404,7 +404,7 @@ def test_workspace_reuse_and_clear():
     n = b.lora_layer_workspace(pool, w.n_rows, b.LORA_MODE_BGMV)
     ws = torch.empty(n, dtype=torch.uint8, device=DEV)
     b.lora_workspace_clear(ws)
-    outs = [b.lora_layer_apply(pool, p.x, p.W, ids, mode=b.LORA_MODE_BGMV, ws=ws, y_dtype=torch.float32)
+    outs = [b.lora_layer_apply(pool, p.x, p.W, ids, w_layout=b.LORA_W_IN_OUT, mode=b.LORA_MODE_BGMV, ws=ws, y_dtype=torch.float32)
             for _ in range(3)]
     torch.cuda.synchronize()
     for y in outs[1:]:
@@ -448,26 +448,117 @@ def _sample_rows(w, k, rng):
 
 @pytest.mark.parametrize("proj", [p[0] for p in wl.PROJ_8B])
 def test_skewed_decode_8b(proj):
-    say(f"skewed decode 8B {proj}: t on all rows, y on sampled rows")
+    """All 256 rows of the skewed batch (110 adapters) against the oracle on
+    sampled columns (rows and columns are independent, so the sampled values
+    are exact), in BGMV mode (the few-hundred-row path: shrink and finish per
+    segment tile, split-K base product) and SGMV mode; t on every row."""
+    say(f"skewed decode 8B {proj}: y on all rows x sampled columns, t on all rows")
     b = binding()
     w = wl.skewed_decode_8b(device=DEV, projections=[proj])
     p = w.projections[0]
     pool = pool_of(p.pool)
     ids = ids_dev(w)
     ot = run_oracle(w, want=("t",))
-    rows = _sample_rows(w, 24, np.random.default_rng(2))
-    oy = run_oracle(w, rows=rows, want=("y",))
+    rng = np.random.default_rng(2)
+    cols = sorted(set(rng.choice(p.d_out, 256, replace=False).tolist()) | {0, p.d_out - 1})
+    oy = run_oracle(w, cols=cols, want=("y",), threads=0)
     Ws = w_stored(p.W, b.LORA_W_OUT_IN)
+    ys = {}
     for m in (b.LORA_MODE_BGMV, b.LORA_MODE_SGMV):
         y = b.lora_layer_apply(pool, p.x, Ws, ids, w_layout=b.LORA_W_OUT_IN, mode=m)
         torch.cuda.synchronize()
-        assert_close(y[rows], oy["y"], TOL[w.dtype], f"y mode {m}")
+        assert_close(y[:, cols], oy["y"], TOL[w.dtype], f"y mode {m}, all rows")
+        ys[m] = y
+    seg = b.lora_segments_build(ids, p.pool.n_adapters)
+    y2 = b.lora_layer_apply(pool, p.x, Ws, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV, seg=seg)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, ys[b.LORA_MODE_BGMV]), "caller's segments give other bits"
     t = b.lora_bgmv_shrink(pool, p.x, ids)
     torch.cuda.synchronize()
     assert_close(t, ot["t"], TOL[w.dtype], "t bgmv")
-    t = b.lora_sgmv_shrink(pool, p.x, b.lora_segments_build(ids, p.pool.n_adapters))
+    t = b.lora_sgmv_shrink(pool, p.x, seg)
     torch.cuda.synchronize()
     assert_close(t, ot["t"], TOL[w.dtype], "t sgmv")
+
+
+# Batches of a few hundred rows in BGMV mode (W stored [d_out, d_in], bf16
+# pool): segment-tile shrink and finish around a split-K base product.
+ROWS_CASES = [
+    # n_rows, d_in, d_out, layout, ranks, n_adapters, id pattern
+    (65, 512, 384, wl.UNIFORM, 16, 40, "zipf"),
+    (128, 1000, 776, wl.RAGGED, RAGGED_RANKS, 12, "uniform"),
+    (257, 2056, 328, wl.UNIFORM, 64, 9, "runs"),
+    (300, 1024, 8200, wl.RAGGED, RAGGED_RANKS, 12, "zipf"),       # 256 x 128 tiles, 2 row tiles
+    (1024, 8264, 264, wl.UNIFORM, 8, 600, "zipf"),                # long, ragged K: 256 x 128 tiles, split K
+    (200, 768, 520, wl.UNIFORM, 16, 150, "allbase"),
+    (200, 768, 520, wl.UNIFORM, 16, 150, "one"),
+    (200, 768, 520, wl.UNIFORM, 16, 150, "distinct"),
+]
+
+
+def _rows_ids(pattern, n, n_ad, rng):
+    if pattern == "zipf":
+        k = np.arange(1, n_ad + 1)
+        p = k ** -1.1
+        ids = rng.choice(n_ad, n, p=p / p.sum())
+    elif pattern == "runs":
+        ids = np.repeat(rng.integers(0, n_ad, 20), -(-n // 20))[:n]
+    elif pattern == "allbase":
+        ids = np.full(n, -1)
+    elif pattern == "one":
+        ids = np.full(n, n_ad // 2)
+    elif pattern == "distinct":
+        ids = rng.permutation(n_ad)[:n] if n <= n_ad else rng.integers(0, n_ad, n)
+    else:
+        ids = rng.integers(0, n_ad, n)
+    if pattern not in ("allbase", "one"):
+        ids = np.where(rng.random(n) < 0.08, -1, ids)
+    return ids.astype(np.int32)
+
+
+@pytest.mark.parametrize("case", ROWS_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[6]}" for c in ROWS_CASES])
+def test_rows_path(case):
+    n, d_in, d_out, layout, ranks, n_ad, pattern = case
+    say(f"few-hundred-row path: {n} x {d_in} -> {d_out}, {pattern}")
+    b = binding()
+    rng = np.random.default_rng(n + d_out)
+    w = wl.small_batch(seed=n, n_rows=n, device=DEV, dtype=torch.bfloat16, d_in=d_in, d_out=d_out,
+                       n_adapters=n_ad, layout=layout, ranks=ranks, frac_base=0.0,
+                       scale=np.linspace(-2.0, 2.0, n_ad).astype(np.float32))
+    w = wl.Workload(w.name, w.dtype, _rows_ids(pattern, n, n_ad, rng), w.projections)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    cols = None if d_out <= 1024 else sorted(set(rng.choice(d_out, 300, replace=False).tolist()) | {0, d_out - 1})
+    o = run_oracle(w, cols=cols, threads=0)
+    Ws = w_stored(p.W, b.LORA_W_OUT_IN)
+    for ydt in (torch.bfloat16, torch.float32):
+        y = b.lora_layer_apply(pool, p.x, Ws, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV, y_dtype=ydt)
+        torch.cuda.synchronize()
+        ys = y if cols is None else y[:, cols]
+        assert_close(ys, o["y"], TOL[torch.bfloat16], f"y {ydt}")
+    y2 = b.lora_layer_apply(pool, p.x, Ws, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV,
+                            y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "run-to-run bits"
+
+
+def test_rows_path_invalid_ids():
+    say("few-hundred-row path: invalid ids flagged and run as base-only rows")
+    b = binding()
+    w = wl.small_batch(seed=11, n_rows=150, device=DEV, dtype=torch.bfloat16, d_in=512, d_out=640,
+                       n_adapters=70, ranks=16, frac_base=0.1)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    bad = w.ids.copy()
+    bad[[3, 77, 149]] = [70, -2, 1000]
+    ids = torch.as_tensor(bad, device=DEV)
+    y = b.lora_layer_apply(pool, p.x, w_stored(p.W, b.LORA_W_OUT_IN), ids, w_layout=b.LORA_W_OUT_IN,
+                           mode=b.LORA_MODE_BGMV)
+    assert b.lora_pool_last_error(pool) & 1 == 1
+    o = run_oracle(wl.Workload("bad", w.dtype, bad, w.projections))
+    assert o["bad"] == 3
+    assert_close(y, o["y"], TOL[torch.bfloat16], "y with invalid ids")
 
 
 @pytest.mark.parametrize("proj", ["q", "k", "down"])
@@ -650,11 +741,12 @@ def test_layer_many_adapters_per_tile(d_in, d_out, layout, runs):
 
 
 def test_bgmv_split_form_medium_batch():
-    """600 rows x 512 -> 2560 in BGMV mode: 100 tiles of 128x128.  bf16 y
-    takes the split form (base product in fp32 partials, added by the
-    expand, one rounding); fp32 y the fused GEMM.  Both W layouts, every
-    row against the oracle, and the two forms within one bf16 rounding."""
-    say("layer, BGMV split form: 600 x 512 -> 2560, both W layouts")
+    """600 rows x 512 -> 2560 in BGMV mode.  W stored [d_out, d_in] takes the
+    few-hundred-row path (base product in fp32 partials, added with the
+    expand by the finish, one rounding); W stored [d_in, d_out] the fused
+    GEMM.  Both y dtypes, every row against the oracle, and bf16 y within
+    one bf16 rounding of fp32 y."""
+    say("layer, BGMV 600 x 512 -> 2560: few-hundred-row path and fused GEMM, both W layouts")
     b = binding()
     w = wl.small_batch(seed=600, n_rows=600, device=DEV, dtype=torch.bfloat16, d_in=512, d_out=2560,
                        n_adapters=40, layout=wl.RAGGED, ranks=(RAGGED_RANKS * 4)[:40], frac_base=0.1,
@@ -669,9 +761,9 @@ def test_bgmv_split_form_medium_batch():
         yf = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=b.LORA_MODE_BGMV,
                                 y_dtype=torch.float32)
         torch.cuda.synchronize()
-        assert_close(yb, o["y"], TOL[torch.bfloat16], f"y bf16 (split form), layout {lay}")
-        assert_close(yf, o["y"], TOL[torch.bfloat16], f"y fp32 (fused), layout {lay}")
-        assert_close(yb, f64(yf), TOL[torch.bfloat16], f"split vs fused, layout {lay}")
+        assert_close(yb, o["y"], TOL[torch.bfloat16], f"y bf16, layout {lay}")
+        assert_close(yf, o["y"], TOL[torch.bfloat16], f"y fp32, layout {lay}")
+        assert_close(yb, f64(yf), TOL[torch.bfloat16], f"bf16 vs fp32 y, layout {lay}")
 
 
 def test_layer_tail_rows_split_launch():
@@ -692,7 +784,7 @@ def test_layer_tail_rows_split_launch():
             y = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=m, y_dtype=torch.float32)
             torch.cuda.synchronize()
             assert_close(y, o["y"], TOL[torch.bfloat16], f"y layout {lay} mode {m}")
-        # bf16 y in BGMV mode: base product in fp32 partials, added by the expand
+        # bf16 y in BGMV mode (W [d_out, d_in]: the few-hundred-row path)
         y = b.lora_layer_apply(pool, p.x, w_stored(p.W, lay), ids, w_layout=lay, mode=b.LORA_MODE_BGMV,
                                y_dtype=torch.bfloat16)
         torch.cuda.synchronize()
