@@ -368,6 +368,31 @@ lora_status_t lora_decode_finish(lora_pool_t pool, const int32_t* ids, int32_t n
                                  void* y, lora_dtype_t y_dtype, int64_t ldy, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* The layer over a 4-bit base weight, any batch size, with bf16 x and bf16
+ * adapters ("Serving Many LoRA Adapters" (praveentn.live), section "When It
+ * Falls Down": a 4-bit quantized base with BF16 adapters needs the batched
+ * adapter kernels to run on a mixed-precision path).  The weight format is
+ * lora_decode_stream_q4's (signed nibbles, one fp32 scale per output and 128
+ * inputs); the adapter term is the bf16 one, unchanged.
+ *   1..64 rows: lora_decode_stream_q4 + lora_decode_finish;
+ *   more rows: segments (built in the workspace unless `seg` is given), the
+ *     shrink per segment tile (past 1024 rows the SGMV shrink), the base
+ *     product over 128 x 64 tiles whose 4-bit W blocks are widened exactly
+ *     to bf16 in LDS (each 128-deep block is one scale group: its sums are
+ *     scaled once and added), and the finish per segment tile (base partials
+ *     + s * t B_a, y rounded once).
+ * The workspace (lora_layer_q4_workspace) holds fp32 base partials of
+ * n_rows * d_out * 4 bytes or more.  Requires a bf16 pool, d_in % 128 == 0,
+ * ldq >= d_in / 2 with ldq % 16 == 0, a 16-byte aligned Wq, a 4-byte aligned
+ * w_scale and lds >= d_in / 128; otherwise LORA_E_UNSUPPORTED /
+ * LORA_E_INVALID.  The other rules are lora_layer_apply's. */
+lora_status_t lora_layer_q4_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes);
+lora_status_t lora_layer_apply_q4(lora_pool_t pool, const void* x, int64_t ldx, const uint8_t* Wq,
+                                  int64_t ldq, const float* w_scale, int64_t lds, const int32_t* ids,
+                                  const lora_segments_t* seg, int32_t n_rows, void* y,
+                                  lora_dtype_t y_dtype, int64_t ldy, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* Adapter slot cache (paging)                                             */
 /* ---------------------------------------------------------------------- */

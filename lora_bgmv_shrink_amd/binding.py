@@ -48,7 +48,7 @@ EXPORTS = [
     "lora_cache_map", "lora_cache_release", "lora_cache_pool", "lora_cache_slot_of", "lora_cache_stats",
     "lora_decode_stream_q4",
     "lora_sched_create", "lora_sched_destroy", "lora_sched_submit", "lora_sched_step", "lora_sched_queued",
-    "lora_layer_apply_noalloc",
+    "lora_layer_apply_noalloc", "lora_layer_q4_workspace", "lora_layer_apply_q4",
 ]
 
 
@@ -134,6 +134,8 @@ def _load():
         "lora_sched_step": (st, [p, ctypes.c_double, i32, p, p, p, p, p]),
         "lora_sched_queued": (i32, [p]),
         "lora_layer_apply_noalloc": (st, [p, p, i64, p, i64, st, p, p, i32, p, st, i64, st, p]),
+        "lora_layer_q4_workspace": (st, [p, i32, p]),
+        "lora_layer_apply_q4": (st, [p, p, i64, p, i64, p, i64, p, p, i32, p, st, i64, p, sz, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -481,6 +483,30 @@ def lora_decode_finish(pool: Pool, ids: torch.Tensor, ws: torch.Tensor, y: torch
     _check(_lib.lora_decode_finish(pool.handle, _ptr(ids), ids.numel(), int(bool(with_lora)), _ptr(y), _dt(y.dtype),
                                    _ld(y), _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(y.device))),
            "lora_decode_finish")
+    return y
+
+
+def lora_layer_q4_workspace(pool: Pool, n_rows: int) -> int:
+    v = ctypes.c_size_t()
+    _check(_lib.lora_layer_q4_workspace(pool.handle, n_rows, ctypes.byref(v)), "lora_layer_q4_workspace")
+    return v.value
+
+
+def lora_layer_apply_q4(pool: Pool, x: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, ids: torch.Tensor,
+                        seg: Optional[Segments] = None, y: Optional[torch.Tensor] = None,
+                        y_dtype: Optional[torch.dtype] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer over a 4-bit base: Wq [d_out, ldq] uint8, w_scale [d_out,
+    lds] fp32 (format in the header)."""
+    assert Wq.dtype == torch.uint8 and w_scale.dtype == torch.float32
+    n = ids.numel()
+    y = _y_out(pool, n, y, y_dtype, x.device, False)
+    if ws is None:
+        ws = _workspace(lora_layer_q4_workspace(pool, n), x.device)
+    cs = None if seg is None else seg.c_struct()
+    _check(_lib.lora_layer_apply_q4(pool.handle, _ptr(x), _ld(x), _ptr(Wq), _ld(Wq), _ptr(w_scale), _ld(w_scale),
+                                    _ptr(ids), None if cs is None else ctypes.byref(cs), n, _ptr(y), _dt(y.dtype),
+                                    _ld(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    ctypes.c_void_p(_stream(x.device))), "lora_layer_apply_q4")
     return y
 
 

@@ -85,17 +85,22 @@ bool rows_ok(const lora_pool_s* pool, int32_t n_rows) {
            pool->dev.n_adapters <= kMaxAdaptersSegments;
 }
 
-// workspace of the few-hundred-row path: segments, then the plan's partials
-size_t rows_ws_bytes(const lora_pool_s* pool, int32_t n_rows) {
-    const RowsPlan R = plan_rows(pool->dev, n_rows);
-    return align_up(seg_layout(0, n_rows, pool->dev.n_adapters).end, 256) + R.bytes;
+// workspace of the few-hundred-row path: segments, the plan's partials and
+// tile records, and (batches past the segment-tile shrink) the SGMV shrink's
+// K-split partials
+size_t rows_ws_bytes(const lora_pool_s* pool, int32_t n_rows, bool q4 = false) {
+    const RowsPlan R = plan_rows(pool->dev, n_rows, q4);
+    size_t b = align_up(seg_layout(0, n_rows, pool->dev.n_adapters).end, 256) + R.bytes;
+    if (!R.tile_shrink) b = align_up(b, 256) + sgmv_shrink_part_bytes(pool->dev, n_rows);
+    return b;
 }
 
-// The few-hundred-row path.  seg: caller's segments of these ids, or NULL
-// (built at the start of the workspace).
+// The few-hundred-row path (also the 4-bit base above decode sizes).  seg:
+// caller's segments of these ids, or NULL (built at the start of the
+// workspace).  q4: W is 4-bit bytes with fp32 scales wscale [d_out][lds].
 hipError_t run_rows(const lora_pool_s* pool, const void* x, int64_t ldx, const void* W, int64_t ldw,
-                    const int32_t* ids, const lora_segments_t* seg, int32_t n_rows, void* y,
-                    lora_dtype_t y_dtype, int64_t ldy, void* ws, hipStream_t stream) {
+                    const float* wscale, int64_t lds, bool q4, const int32_t* ids, const lora_segments_t* seg,
+                    int32_t n_rows, void* y, lora_dtype_t y_dtype, int64_t ldy, void* ws, hipStream_t stream) {
     const PoolDev& P = pool->dev;
     uint8_t* base = (uint8_t*)ws;
     const SegLayout L = seg_layout(0, n_rows, P.n_adapters);
@@ -110,13 +115,19 @@ hipError_t run_rows(const lora_pool_s* pool, const void* x, int64_t ldx, const v
         e = launch_segments(ids, n_rows, P.n_adapters, &own, P.err, stream);
         seg = &own;
     }
-    const RowsPlan R = plan_rows(P, n_rows);
+    const RowsPlan R = plan_rows(P, n_rows, q4);
     uint8_t* rb = base + align_up(L.end, 256);
     float* part = (float*)(rb + R.part_off);
     float* tpart = (float*)(rb + R.tpart_off);
+    if (e == hipSuccess && !R.tile_shrink) {
+        // long batches: t from the SGMV shrink (K split into its own partials)
+        float* sp = sgmv_shrink_part_bytes(P, n_rows) ? (float*)(rb + align_up(R.bytes, 256)) : nullptr;
+        e = launch_sgmv_shrink(P, pool->dtype, x, ldx, seg, n_rows, P.n_adapters + 1, tpart, R.rtp, true, stream,
+                               nullptr, 0, ids, sp);
+    }
     if (e == hipSuccess)
         e = launch_rows_adapter(P, R, x, ldx, ids, seg, n_rows, part, tpart, y, y_dtype, ldy, stream, true, false);
-    if (e == hipSuccess) e = launch_rows_gemm(P, R, x, ldx, W, ldw, nullptr, 0, false, n_rows, part, stream);
+    if (e == hipSuccess) e = launch_rows_gemm(P, R, x, ldx, W, ldw, wscale, lds, q4, n_rows, part, stream);
     if (e == hipSuccess)
         e = launch_rows_adapter(P, R, x, ldx, ids, seg, n_rows, part, tpart, y, y_dtype, ldy, stream, false, true);
     return e;
@@ -517,7 +528,8 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
             lora_status_t sst = check_segments(seg, n_rows, P.n_adapters);
             if (sst != LORA_OK) return sst;
         }
-        return dev_status(run_rows(pool, x, ldx, W, ldw, ids, seg, n_rows, y, y_dtype, ldy, ws, stream));
+        return dev_status(
+            run_rows(pool, x, ldx, W, ldw, nullptr, 0, false, ids, seg, n_rows, y, y_dtype, ldy, ws, stream));
     }
     uint8_t* base = (uint8_t*)ws;
     float* t = (float*)base;
@@ -748,6 +760,70 @@ lora_status_t lora_decode_finish(lora_pool_t pool, const int32_t* ids, int32_t n
     g.ldy = ldy;
     decode_carve(P, n_rows, D, ws, g);
     return dev_status(launch_decode_finish(P, D, g, y_dtype, stream));
+}
+
+lora_status_t lora_layer_q4_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes) {
+    if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
+    if (n_rows == 0) {
+        *bytes = 0;
+        return LORA_OK;
+    }
+    if (pool->dtype != LORA_BF16) return LORA_E_UNSUPPORTED;
+    if (decode_ok(pool, n_rows)) {
+        *bytes = decode_ws_bytes(pool->dev, n_rows, plan_decode(pool->dev, n_rows, true));
+        return LORA_OK;
+    }
+    if (pool->dev.n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
+    *bytes = rows_ws_bytes(pool, n_rows, true);
+    return LORA_OK;
+}
+
+lora_status_t lora_layer_apply_q4(lora_pool_t pool, const void* x, int64_t ldx, const uint8_t* Wq, int64_t ldq,
+                                  const float* w_scale, int64_t lds, const int32_t* ids,
+                                  const lora_segments_t* seg, int32_t n_rows, void* y, lora_dtype_t y_dtype,
+                                  int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
+    if (n_rows == 0) return LORA_OK;
+    const PoolDev& P = pool->dev;
+    if (pool->dtype != LORA_BF16) return LORA_E_UNSUPPORTED;
+    if (!x || !Wq || !w_scale || !ids || !y || ldx < P.d_in || ldq < P.d_in / 2 || lds < P.d_in / 128 ||
+        ldy < P.d_out)
+        return LORA_E_INVALID;
+    if (P.d_in % 128 != 0) return LORA_E_UNSUPPORTED;
+    const int ey = elem_bytes(y_dtype);
+    if (!al16(x) || !al16(Wq) || !al16(y) || !ld_ok(ldx, P.d_in, 2) || ldq % 16 != 0 ||
+        ((uintptr_t)w_scale & 3u) != 0 || !ld_ok(ldy, P.d_out, ey))
+        return LORA_E_UNSUPPORTED;
+    if (seg) {
+        lora_status_t sst = check_segments(seg, n_rows, P.n_adapters);
+        if (sst != LORA_OK) return sst;
+    }
+    size_t need = 0;
+    lora_status_t st = lora_layer_q4_workspace(pool, n_rows, &need);
+    if (st != LORA_OK) return st;
+    if (!ws || ws_bytes < need || !al16(ws)) return LORA_E_WORKSPACE;
+    if (decode_ok(pool, n_rows)) {
+        const DecodePlan D = plan_decode(P, n_rows, true);
+        DecodeArgs g{};
+        g.x = x;
+        g.ldx = ldx;
+        g.W = Wq;
+        g.ldw = ldq;
+        g.w_q4 = 1;
+        g.wscale = w_scale;
+        g.lds = lds;
+        g.ids = ids;
+        g.n = n_rows;
+        g.with_lora = 1;
+        g.y = y;
+        g.ldy = ldy;
+        decode_carve(P, n_rows, D, ws, g);
+        hipError_t e = launch_decode_stream(P, D, g, stream);
+        if (e == hipSuccess) e = launch_decode_finish(P, D, g, y_dtype, stream);
+        return dev_status(e);
+    }
+    return dev_status(run_rows(pool, x, ldx, Wq, ldq, w_scale, lds, true, ids, seg, n_rows, y, y_dtype, ldy, ws,
+                               stream));
 }
 
 }  // extern "C"

@@ -212,6 +212,7 @@ hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt
 // over the segments of lora_segments_build (rows.hip).
 struct RowsPlan {
     int32_t wide;               // 256 x 128 tiles (else 128 x 64)
+    int32_t tile_shrink;        // shrink per segment tile (else the SGMV shrink writes t)
     int32_t tiles_m, tiles_n;
     int32_t S, kslice;          // K slices of the base product
     int32_t St, ks_len;         // K slices of the shrink
@@ -219,7 +220,7 @@ struct RowsPlan {
     int64_t rtp;                // fp32 pitch of a t partial row
     size_t part_off, tpart_off, tiles_off, bytes;   // workspace layout
 };
-RowsPlan plan_rows(const PoolDev& P, int32_t n_rows);
+RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4 = false);
 // base partials part[S][n_rows][ldp] = x W over each K slice; q4: W holds
 // 4-bit weights (bytes [d_out][ldw]) with fp32 scales [d_out][lds] per 128
 // inputs (d_in % 128 == 0)
@@ -227,7 +228,9 @@ hipError_t launch_rows_gemm(const PoolDev& P, const RowsPlan& R, const void* x, 
                             int64_t ldw, const float* wscale, int64_t lds, bool q4, int32_t n_rows, float* part,
                             hipStream_t stream);
 // shrink: tpart[St][n_rows][rtp] = x_rows A_u over each K slice, per segment
-// tile; finish: y = sum of part + s_u (sum of tpart) B_u, rounded once
+// tile, and the tile records (or, without the segment-tile shrink, only the
+// records: tpart is then t from the SGMV shrink, one slice of pitch rtp);
+// finish: y = sum of part + s_u (sum of tpart) B_u, rounded once
 hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* x, int64_t ldx,
                                const int32_t* ids, const lora_segments_t* seg, int32_t n_rows,
                                const float* part, float* tpart, void* y, lora_dtype_t ydt, int64_t ldy,

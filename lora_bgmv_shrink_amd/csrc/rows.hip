@@ -46,6 +46,7 @@ namespace lora {
 namespace {
 
 constexpr int RG_KB = 128;            // k per block (one 4-bit scale group)
+constexpr int kRowsTileShrinkMax = 1024;   // rows the segment-tile shrink serves
 constexpr int RG_LDK = RG_KB + 8;     // bf16 pitch of a staged W column
 
 struct RowsGemmArgs {
@@ -614,6 +615,35 @@ __global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a
     }
 }
 
+// Tile records without the segment-tile shrink (when the SGMV shrink forms
+// t): one wave per tile finds its segment and writes the record.
+__global__ __launch_bounds__(64) void k_tile_recs(PoolDev P, const int32_t* __restrict__ seg_ids,
+                                                  const int32_t* __restrict__ seg_off,
+                                                  const int32_t* __restrict__ n_seg, TileRec* __restrict__ tiles) {
+    const int lane = threadIdx.x;
+    int s = 0, c = 0;
+    const bool found = find_seg_tile(seg_off, *n_seg, SS_ROWS, blockIdx.x, lane, s, c);
+    if (lane != 0) return;
+    TileRec rec;
+    rec.pad = 0;
+    if (!found) {
+        rec.valid = 0;
+        rec.b_off = 0;
+        rec.row0 = rec.cnt = rec.rank = 0;
+        rec.scale = 0.f;
+    } else {
+        const int u = seg_ids[s];
+        const bool ok = id_ok(u, P.n_adapters);
+        rec.valid = 1;
+        rec.row0 = seg_off[s] + c * SS_ROWS;
+        rec.cnt = min(SS_ROWS, seg_off[s + 1] - rec.row0);
+        rec.b_off = ok ? P.b_off[u] : 0;
+        rec.rank = ok ? P.ranks[u] : 0;
+        rec.scale = ok ? P.scales[u] : 0.f;
+    }
+    tiles[blockIdx.x] = rec;
+}
+
 // segment tiles of SS_ROWS rows: at most one partial tile per segment on top
 // of the full ones (the grid is sized without reading the segment count)
 int64_t rows_tiles(int32_t n_rows, int32_t n_bins) {
@@ -622,7 +652,7 @@ int64_t rows_tiles(int32_t n_rows, int32_t n_bins) {
 
 }  // namespace
 
-RowsPlan plan_rows(const PoolDev& P, int32_t n_rows) {
+RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4) {
     RowsPlan R;
     const int K = P.d_in, N = P.d_out;
     // long or wide projections: 256 x 128 tiles (x re-read once per 128
@@ -630,7 +660,7 @@ RowsPlan plan_rows(const PoolDev& P, int32_t n_rows) {
     // 128 x 64 tiles, for more workgroups.  Measured on the skewed 256-row
     // 8B batch: gate 4096x14336 87 -> 55 us, down 14336x4096 75 -> 54 us; q
     // 4096x4096 is no faster wide (its fp32 partials grow with the split).
-    R.wide = (N >= 8192 || K >= 8192) ? 1 : 0;
+    R.wide = (!q4 && (N >= 8192 || K >= 8192)) ? 1 : 0;   // 4-bit W: 128 x 64 tiles
     const int bm = R.wide ? 256 : 128, bn = R.wide ? 128 : 64;
     R.tiles_m = (int32_t)ceil_div(n_rows, bm);
     R.tiles_n = (int32_t)ceil_div(N, bn);
@@ -650,6 +680,10 @@ RowsPlan plan_rows(const PoolDev& P, int32_t n_rows) {
     R.ks_len = ks_len;
     R.St = (int32_t)ceil_div(K, ks_len);
     R.rtp = (int64_t)align_up((size_t)P.r_max, 4);
+    // batches past the segment-tile shrink's range take the SGMV shrink,
+    // which writes t itself (one slice)
+    R.tile_shrink = n_rows <= kRowsTileShrinkMax ? 1 : 0;
+    if (!R.tile_shrink) R.St = 1;
     const size_t part = align_up((size_t)R.S * n_rows * R.ldp * 4, 256);
     const size_t tpart = align_up((size_t)R.St * n_rows * R.rtp * 4, 256);
     const size_t tiles = align_up((size_t)rows_tiles(n_rows, P.n_adapters + 1) * sizeof(TileRec), 256);
@@ -693,7 +727,13 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
     const int n_bins = P.n_adapters + 1;
     // the tile records follow the t partials (RowsPlan::tiles_off)
     TileRec* tiles = (TileRec*)((uint8_t*)tpart + (R.tiles_off - R.tpart_off));
-    if (shrink) {
+    if (shrink && !R.tile_shrink) {
+        // t comes from the SGMV shrink (tpart is t, one slice); only the records
+        hipLaunchKernelGGL(k_tile_recs, dim3((unsigned)rows_tiles(n_rows, n_bins)), dim3(64), 0, stream, P,
+                           seg->seg_ids, seg->seg_off, seg->n_seg, tiles);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else if (shrink) {
         SegShrinkArgs s;
         s.tiles = tiles;
         s.x = (const bf16*)x;

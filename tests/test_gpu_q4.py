@@ -145,3 +145,101 @@ def test_q4_decode_ragged_pool_fp32_y():
     torch.cuda.synchronize()
     ref = _oracle_y(p.x, Wq, sc, w.ids, op, d_in, True)
     assert_close(y, ref, TOL[torch.bfloat16], "q4 ragged, fp32 y")
+
+
+# ---------------------------------------------------------------------------
+# The layer over a 4-bit base at any batch size (lora_layer_apply_q4)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_rows,d_in,d_out,layout,ranks,n_ad,runs", [
+    (40, 1024, 776, wl.UNIFORM, 16, 6, None),                     # decode launches
+    (65, 1024, 776, wl.UNIFORM, 16, 30, None),                    # segment-tile path
+    (300, 2048, 1032, wl.RAGGED, [8, 16, 32, 64, 1, 3, 24, 40], 8, None),
+    (700, 1536, 520, wl.UNIFORM, 64, 5, [300, 7, 200, 1, 64, 65, 63]),
+    (1100, 1024, 640, wl.RAGGED, [8, 16, 32, 64] * 3, 12, [500, 1, 300, 299]),   # SGMV shrink form
+])
+@pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float32])
+def test_q4_layer_matches_oracle(n_rows, d_in, d_out, layout, ranks, n_ad, runs, ydt):
+    say(f"q4 layer: {n_rows} rows, {d_in}->{d_out}, y {ydt}")
+    b = binding()
+    w = wl.small_batch(seed=n_rows, n_rows=n_rows, d_in=d_in, d_out=d_out, n_adapters=n_ad, ranks=ranks,
+                       layout=layout, dtype=torch.bfloat16, device=DEV, frac_base=0.1, run_lengths=runs,
+                       scale=np.linspace(-2.0, 2.0, n_ad).astype(np.float32))
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    op, _ = oracle_pool(p.pool)
+    Wq, sc = wl.q4_weight(20 + n_rows, d_in, d_out, DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y = b.lora_layer_apply_q4(pool, p.x, Wq, sc, ids, y_dtype=ydt)
+    y2 = b.lora_layer_apply_q4(pool, p.x, Wq, sc, ids, y_dtype=ydt,
+                               seg=b.lora_segments_build(ids, p.pool.n_adapters))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "caller's segments give other bits"
+    ref = _oracle_y(p.x, Wq, sc, w.ids, op, d_in, True)
+    assert_close(y, ref, TOL[torch.bfloat16], "q4 layer")
+
+
+def test_q4_layer_agrees_with_bf16_layer_on_exact_weights():
+    """Power-of-two scales: the 4-bit layer and the bf16 layer (W stored
+    [d_out, d_in]) compute the same function at 300 rows."""
+    b = binding()
+    d_in, d_out, n = 2048, 1024, 300
+    w = wl.small_batch(seed=14, n_rows=n, d_in=d_in, d_out=d_out, n_adapters=50, ranks=16,
+                       dtype=torch.bfloat16, device=DEV, frac_base=0.1)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    Wq, sc = wl.q4_weight(7, d_in, d_out, DEV, pow2_scales=True)
+    Wd = oracle.dequant_q4(Wq.cpu().numpy(), sc.cpu().double().numpy(), d_in)
+    Wb = torch.from_numpy(Wd.T.copy()).to(torch.bfloat16).to(DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y4 = b.lora_layer_apply_q4(pool, p.x, Wq, sc, ids, y_dtype=torch.float32)
+    yb = b.lora_layer_apply(pool, p.x, Wb, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_BGMV,
+                            y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(y4, f64(yb), 1e-4, "q4 vs bf16 layer (fp32 y)")
+
+
+def test_q4_layer_small_batch_is_the_decode_pair():
+    b = binding()
+    w = wl.small_batch(seed=15, n_rows=33, d_in=1024, d_out=512, n_adapters=7, ranks=16,
+                       dtype=torch.bfloat16, device=DEV, frac_base=0.1)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    Wq, sc = wl.q4_weight(8, 1024, 512, DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y = b.lora_layer_apply_q4(pool, p.x, Wq, sc, ids)
+    y2 = _run_q4(b, pool, p.x, Wq, sc, ids, True)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("proj", ["q", "k", "down"])
+def test_q4_layer_prefill_70b(proj):
+    """The 70B prefill batch (16 requests, 8 rank-64 adapters, rows in
+    arrival order) over a 4-bit base weight: sampled rows (every request
+    boundary) x sampled columns against the oracle on the widened weight of
+    those columns."""
+    from _marshal import oracle_pool as opool, remap_ids
+    say(f"q4 layer, 70B prefill {proj}: sampled rows x columns")
+    b = binding()
+    w = wl.prefill_70b(device=DEV, projections=[proj])
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    Wq, sc = wl.q4_weight(30, p.d_in, p.d_out, DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y = b.lora_layer_apply_q4(pool, p.x, Wq, sc, ids)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    n = w.n_rows
+    rows = set(rng.choice(n, 40, replace=False).tolist()) | {0, n - 1}
+    off = np.cumsum([0] + list(w.lengths))
+    for o in off[1:-1]:
+        rows |= {int(o) - 1, int(o)}
+    rows = sorted(rows)
+    cols = sorted(set(rng.choice(p.d_out, 160, replace=False).tolist()) | {0, p.d_out - 1})
+    ci = torch.as_tensor(cols, device=DEV)
+    Wd = oracle.dequant_q4(Wq[ci].cpu().numpy(), sc[ci].cpu().double().numpy(), p.d_in)   # [d_in, len(cols)]
+    ids_r = w.ids[rows]
+    op, mp = opool(p.pool, used=ids_r.tolist(), cols=cols)
+    ref = oracle.layer(f64(p.x[torch.as_tensor(rows, device=DEV)]), Wd, remap_ids(ids_r, mp, p.pool.n_adapters),
+                       op, want=("y",), threads=0)["y"]
+    assert_close(y[rows][:, cols], ref, TOL[torch.bfloat16], "q4 prefill sampled")
