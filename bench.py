@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-paging", action="store_true", help="skip the adapter-paging measurements")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the merge, 4-bit and standalone SGMV legs (profiling runs of the workloads)")
     ap.add_argument("--comparators", action="store_true",
                     help="also time the vendor GEMM on the decode base product and a device copy of the "
                          "decode stream's bytes")
@@ -151,6 +153,8 @@ def distinct_bytes(p, ids, which):
 # ---------------------------------------------------------------------------
 
 def bench_decode(torch, args):
+    import numpy as np
+
     from lora_bgmv_shrink_amd import binding as b
     from lora_bgmv_shrink_amd import workloads as wl
 
@@ -242,6 +246,24 @@ def bench_decode(torch, args):
                                     for r in reps])
     d_shr = time_graph(torch, g_shr, kr) / R
 
+    # diversity sweep: 32 rows on 1, 2, 4, ... 32 distinct adapters (each used
+    # round-robin), same replicas and launches as the headline step
+    sweep = []
+    for U_s in (1, 2, 4, 8, 16, 32):
+        ids_s = torch.as_tensor(((np.arange(n) % U_s) * 7) % 250, dtype=torch.int32, device=dev)
+        for r in reps:
+            r["ids_s"] = ids_s
+
+        def step_s(r):
+            b.lora_decode_stream(r["pool"], r["p"].x, r["Wt"], r["ids_s"], r["ws"], True)
+            b.lora_decode_finish(r["pool"], r["ids_s"], r["ws"], r["y"], True)
+
+        d_s = time_graph(torch, capture(torch, lambda: [step_s(r) for r in reps]), kr) / R
+        sweep.append(dict(distinct_adapters=U_s, step_us=round(d_s * 1e6, 3),
+                          adapter_bytes=U_s * 16 * (4096 + 4096) * 2))
+    for r in reps:
+        del r["ids_s"]
+
     pool = p0.pool
     bA, U = distinct_bytes(pool, w0.ids, "A")
     bB, _ = distinct_bytes(pool, w0.ids, "B")
@@ -295,6 +317,8 @@ def bench_decode(torch, args):
                                                 "lora_bgmv_shrink_amd/csrc/lora_internal.hpp"],
                                                "decode_q4096_r16_rows32_traffic.md"),
                       kernel="k_decode_stream (split-K base partials + BGMV shrink partials)",
+                      what="the stream launch: the base weight W (92% of its bytes) and the distinct "
+                           "adapters' A blocks; the adapter term alone is adapter_term.bgmv_shrink_frac_hbm",
                       bytes_per_launch=stream_bytes, avg_launch_us=round(d_stream * 1e6, 3)),
         adapter_term=dict(
             distinct_adapters=U,
@@ -307,6 +331,7 @@ def bench_decode(torch, args):
             bgmv_shrink_frac_hbm=round(shrink_bytes / d_shr / 1e9 / HBM_PEAK_GBS, 4),
         ),
         comparators=comparators,
+        diversity_sweep=sweep,
         # the graph replays launches over reps' tensors and pools: whoever
         # replays it must hold reps too
         _decode_graph=(decode_graph, reps),
@@ -355,9 +380,15 @@ def bench_multi(torch, args, name):
                 b.lora_layer_apply(h, pr["p"].x, pr["Wt"], ids, w_layout=b.LORA_W_OUT_IN, seg=seg, y=pr["y"],
                                    ws=ws)
 
+        # base-only: the same calls with every row base-only (the adapter term
+        # drops out; the kernels are the same)
+        ids_base = torch.full_like(ids, -1)
+        seg_base = b.lora_segments_build(ids_base, plist[0].n_adapters)
+
         def base_step():
-            for pr, h in zip(projs, hs):
-                b.lora_base_gemm_expand(h, pr["p"].x, pr["Wt"], ids, None, w_layout=b.LORA_W_OUT_IN, y=pr["y"])
+            for pr, h, ws in zip(projs, hs, wss):
+                b.lora_layer_apply(h, pr["p"].x, pr["Wt"], ids_base, w_layout=b.LORA_W_OUT_IN, seg=seg_base,
+                                   y=pr["y"], ws=ws)
 
         g = capture(torch, step)
         gb = capture(torch, base_step)
@@ -389,6 +420,7 @@ def bench_multi(torch, args, name):
             ms_per_step=round(sec * 1e3, 4),
             tflops=round(flops / sec / 1e12, 1), mfma_frac=round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
             weight_plus_adapter_GBps=round((wbytes + abytes) / sec / 1e9, 1),
+            weight_plus_adapter_frac_hbm=round((wbytes + abytes) / sec / 1e9 / HBM_PEAK_GBS, 4),
             adapter_bytes=abytes,
             overhead_fraction=round(max(0.0, (sec - d_base) / sec), 4),
         )
@@ -408,9 +440,25 @@ def bench_multi(torch, args, name):
 # CPU baseline: the oracle as it stands
 # ---------------------------------------------------------------------------
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, seconds):
+    """The fp64 oracle on the host cores: the full decode batch (base + LoRA)
+    at all cores and at one thread, and the LoRA term alone (x A then
+    s t B, no base product).  The oracle is rebuilt here for this host
+    (-O3 -march=native, OpenMP, no fast-math) into a temporary file; the
+    in-tree build stays portable."""
+    import tempfile
+
     import numpy as np
-    import torch
 
     import oracle
 
@@ -437,18 +485,42 @@ def cpu_baseline(w, seconds):
                            pool.scales[used].astype(np.float64))
     x = p.x.float().cpu().double().numpy()
     Wm = p.W.float().cpu().double().numpy()
-    threads = oracle.max_threads()
-    n_done = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.layer(x, Wm, ids, op, threads=threads)
-        n_done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return dict(value=round(n_done * w.n_rows / el, 2), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"full decode batch ({w.n_rows} rows, q 4096->4096, r16, 20 adapters, base + LoRA) "
-                       f"x{n_done} passes, {el:.1f} s, fp64")
+    lib = None
+    native = False
+    try:
+        tmp = os.path.join(tempfile.gettempdir(), f"liboracle_native_{os.getpid()}.so")
+        oracle.build(out=tmp, extra=("-march=native",))
+        lib = oracle.load(tmp)
+        native = True
+    except Exception as e:   # no compiler: the in-tree build
+        log(f"cpu baseline: native oracle build failed ({e}); using the in-tree build")
+        lib = oracle.load()
+    threads = oracle.max_threads(lib)
+
+    def rate(fn, budget, min_passes=1):
+        n_done = 0
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            n_done += 1
+            el = time.perf_counter() - t0
+            if el >= budget and n_done >= min_passes:
+                return n_done, el
+
+    n_all, el_all = rate(lambda: oracle.layer(x, Wm, ids, op, threads=threads, lib=lib), 0.5 * seconds)
+    n_one, el_one = rate(lambda: oracle.layer(x, Wm, ids, op, threads=1, lib=lib), 0.35 * seconds)
+    n_lo, el_lo = rate(lambda: oracle.layer(x, None, ids, op, want=("lora",), threads=1, lib=lib),
+                       0.15 * seconds)
+    rows = w.n_rows
+    return dict(value=round(n_all * rows / el_all, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"full decode batch ({rows} rows, q 4096->4096, r16, 20 adapters, base + LoRA) "
+                       f"x{n_all} passes, {el_all:.1f} s, fp64, {threads} threads",
+                one_thread=dict(value=round(n_one * rows / el_one, 2), unit="tokens/s", cores=1,
+                                sample=f"same batch x{n_one} passes, {el_one:.1f} s"),
+                lora_term_one_thread=dict(value=round(n_lo * rows / el_lo, 2), unit="tokens/s", cores=1,
+                                          sample=f"LoRA term alone (x A, s t B; no x W) x{n_lo} passes, "
+                                                 f"{el_lo:.1f} s"),
+                cpu_model=_cpu_model(), build="gcc -O3 -march=native -fopenmp" if native else "gcc -O3 -fopenmp")
 
 
 def bench_paging(torch, args, decode, R):
@@ -692,6 +764,47 @@ def bench_q4_decode(torch, args):
     return out
 
 
+def bench_q4_prefill(torch, args):
+    """The 70B prefill batch (13,894 rows in arrival order, 8 rank-64
+    adapters, seven projections) over 4-bit base weights with bf16 adapters:
+    lora_layer_apply_q4 per projection, segments built once per step,
+    graph-replayed.  MFMA fraction against the bf16 peak (the 4-bit weights
+    are widened to bf16 for the matrix cores)."""
+    from lora_bgmv_shrink_amd import binding as b
+    from lora_bgmv_shrink_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.prefill_70b(device=dev)
+    n = w.n_rows
+    ids = torch.as_tensor(w.ids, device=dev)
+    projs, flops, wbytes = [], 0, 0
+    for i, pp in enumerate(w.projections):
+        pp.W = None
+        Wq, sc = wl.q4_weight(200 + i, pp.d_in, pp.d_out, dev)
+        h = make_pool(b, pp.pool)
+        projs.append(dict(p=pp, Wq=Wq, sc=sc, h=h, y=torch.empty((n, pp.d_out), dtype=torch.bfloat16, device=dev)))
+        flops += 2 * n * pp.d_in * pp.d_out + 2 * n * 64 * (pp.d_in + pp.d_out)
+        wbytes += pp.d_in * pp.d_out // 2 + pp.d_out * (pp.d_in // 128) * 4
+    ws = torch.zeros(max(b.lora_layer_q4_workspace(pr["h"], n) for pr in projs), dtype=torch.uint8, device=dev)
+    seg = b.segments_alloc(n, 64, dev)
+
+    def step():
+        b.lora_segments_build(ids, 64, seg=seg)
+        for pr in projs:
+            b.lora_layer_apply_q4(pr["h"], pr["p"].x, pr["Wq"], pr["sc"], ids, seg=seg, y=pr["y"], ws=ws)
+
+    g = capture(torch, step)
+    d = time_graph(torch, g, max(2, args.extra_steps // 2))
+    out = dict(workload="prefill_q4base_70b_r64_pool64", rows=n, ms_per_step=round(d * 1e3, 4),
+               tokens_per_s_seven_projections=round(n / d, 1), tflops=round(flops / d / 1e12, 1),
+               mfma_frac=round(flops / d / 1e12 / BF16_PEAK_TFLOPS, 4), weight_bytes=wbytes)
+    for pr in projs:
+        pr["h"].destroy()
+    del g, projs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_sgmv_adapter_term(torch, args):
     """The adapter term of the 70B prefill batch on its own (13,894 rows in
     arrival order, 8 rank-64 adapters, q and o projections 8192 -> 8192):
@@ -796,12 +909,17 @@ def main():
         log(f"bench: workload {name} ...")
         extra[name] = bench_multi(torch, args, name)
         torch.cuda.empty_cache()
-    log("bench: merge kernel ...")
-    merge = bench_merge(torch, args)
-    log("bench: 4-bit base decode ...")
-    q4 = bench_q4_decode(torch, args)
-    log("bench: SGMV adapter term (prefill) ...")
-    sgmv = bench_sgmv_adapter_term(torch, args)
+    merge = q4 = sgmv = q4p = None
+    if not args.no_extras:
+        log("bench: merge kernel ...")
+        merge = bench_merge(torch, args)
+        log("bench: 4-bit base decode ...")
+        q4 = bench_q4_decode(torch, args)
+        log("bench: SGMV adapter term (prefill) ...")
+        sgmv = bench_sgmv_adapter_term(torch, args)
+        if "prefill" in args.workloads.split(","):
+            log("bench: 4-bit base prefill ...")
+            q4p = bench_q4_prefill(torch, args)
     decode = dec.pop("_decode_graph")
     paging = serving = None
     if not args.no_paging:
@@ -839,10 +957,12 @@ def main():
         "kernels_us": dec["kernels_us"],
         "adapter_term": dec["adapter_term"],
         "comparators": dec["comparators"],
+        "diversity_sweep_rows32": dec["diversity_sweep"],
         "gpu_step_us": round(dec["gpu_step_s"] * 1e6, 3),
         "workloads": extra,
         "merge": merge,
         "q4_decode": q4,
+        "q4_prefill": q4p,
         "adapter_term_prefill": sgmv,
         "paging": paging,
         "serving": serving,

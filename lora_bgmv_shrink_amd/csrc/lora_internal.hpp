@@ -124,6 +124,55 @@ __device__ inline bool find_seg_tile(const int32_t* __restrict__ seg_off, int n_
     return false;
 }
 
+// find_seg_tile for callers that know the descriptor's capacity (cap >=
+// n_seg): the first 256 run boundaries are requested together with the run
+// count (the entries past n_seg are read but never used), so a batch of up
+// to 256 runs finds its tile in one round of loads.  Also returns the run's
+// first and one-past-last position in perm.
+__device__ inline bool find_seg_tile_cap(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_seg_p,
+                                         int cap, int BM, int b, int lane, int& s_out, int& c_out, int& lo_out,
+                                         int& hi_out) {
+    constexpr int PRE = 4;   // chunks of 64 runs requested up front
+    int lo[PRE], hi[PRE];
+#pragma unroll
+    for (int q = 0; q < PRE; ++q) {
+        const int s = q * 64 + lane;
+        lo[q] = s < cap ? seg_off[s] : 0;
+        hi[q] = s < cap ? seg_off[s + 1] : 0;
+    }
+    const int n_seg = *n_seg_p;
+    int base = 0;
+    for (int s0 = 0; s0 < n_seg; s0 += 64) {
+        const int s = s0 + lane;
+        int l = 0, h = 0;
+        if (s0 < PRE * 64) {
+#pragma unroll
+            for (int q = 0; q < PRE; ++q)
+                if (s0 == q * 64) {
+                    l = lo[q];
+                    h = hi[q];
+                }
+        } else if (s < n_seg) {
+            l = seg_off[s];
+            h = seg_off[s + 1];
+        }
+        const int cnt = s < n_seg ? (h - l + BM - 1) / BM : 0;
+        const int incl = wave_incl_scan(cnt, lane);
+        const int excl = base + incl - cnt;
+        const uint64_t hit = __ballot(s < n_seg && b >= excl && b < base + incl);
+        if (hit) {
+            const int L = __ffsll((unsigned long long)hit) - 1;
+            s_out = s0 + L;
+            c_out = b - __shfl(excl, L, 64);
+            lo_out = __shfl(l, L, 64);
+            hi_out = __shfl(h, L, 64);
+            return true;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    return false;
+}
+
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

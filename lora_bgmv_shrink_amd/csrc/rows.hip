@@ -340,6 +340,7 @@ struct SegShrinkArgs {
     const int32_t* seg_ids;
     const int32_t* seg_off;
     const int32_t* n_seg;
+    int32_t cap;       // capacity of the descriptor (>= its run count)
     float* tpart;      // [St][M][rtp]
     int64_t rtp;
     int32_t M;
@@ -350,17 +351,18 @@ struct SegShrinkArgs {
 __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int sRow[SS_ROWS];
-    __shared__ int sInfo[3];
+    __shared__ int sInfo[4];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     if (wave == 0) {
-        int s = 0, c = 0;
-        const bool found = find_seg_tile(a.seg_off, *a.n_seg, SS_ROWS, blockIdx.x, lane, s, c);
+        int s = 0, c = 0, lo = 0, hi = 0;
+        const bool found = find_seg_tile_cap(a.seg_off, a.n_seg, a.cap, SS_ROWS, blockIdx.x, lane, s, c, lo, hi);
         if (lane == 0) {
             sInfo[0] = found ? 1 : 0;
             sInfo[1] = s;
-            sInfo[2] = c;
+            sInfo[2] = lo + c * SS_ROWS;
+            sInfo[3] = hi;
         }
     }
     __syncthreads();
@@ -372,8 +374,8 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
     const int s = sInfo[1];
     const int u = a.seg_ids[s];
     const bool ok = id_ok(u, P.n_adapters);
-    const int row0 = a.seg_off[s] + sInfo[2] * SS_ROWS;
-    const int cnt = min(SS_ROWS, a.seg_off[s + 1] - row0);
+    const int row0 = sInfo[2];
+    const int cnt = min(SS_ROWS, sInfo[3] - row0);
     if (ks == 0 && tid == 0) {
         TileRec rec;
         rec.b_off = ok ? P.b_off[u] : 0;
@@ -521,6 +523,10 @@ __global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a
     const float sc = uload(&rp->scale, 0);
     const int64_t boff = uload(&rp->b_off, 0);
     if (tid < SS_ROWS) sRow[tid] = a.perm[row0 + min(tid, cnt - 1)];
+    const int N = P.d_out;
+    const int col = ch * FS_COLS + lane * FS_VE;
+    const bool fast = col + FS_VE <= N && P.vec_b && ((a.ldy * (int64_t)sizeof(TY)) & 15) == 0;
+    const bf16* __restrict__ Bu = (const bf16*)P.B + boff + (col < N ? col : 0);
     __syncthreads();
     if (r > 0) {
         // t[m][j] = sum over the shrink slices in order, four requested at once
@@ -545,15 +551,11 @@ __global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a
     }
     __syncthreads();
 
-    const int N = P.d_out;
-    const int col = ch * FS_COLS + lane * FS_VE;
     if (col >= N) return;
-    const bool fast = col + FS_VE <= N && P.vec_b && ((a.ldy * (int64_t)sizeof(TY)) & 15) == 0;
     const int valid = min(FS_VE, N - col);
     const int64_t slice = (int64_t)a.M * a.ldp;
     const float* __restrict__ part = a.part;
     TY* __restrict__ Y = (TY*)a.y;
-    const bf16* __restrict__ Bu = (const bf16*)P.B + boff + col;
     for (int m = wave; m < cnt; m += FS_NT / 64) {
         const int row = sRow[m];
         if (!fast) {
@@ -742,6 +744,7 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
         s.seg_ids = seg->seg_ids;
         s.seg_off = seg->seg_off;
         s.n_seg = seg->n_seg;
+        s.cap = std::min<int32_t>(seg->cap, std::max<int32_t>(1, std::min<int32_t>(n_rows, n_bins)));
         s.tpart = tpart;
         s.rtp = R.rtp;
         s.M = n_rows;
