@@ -561,7 +561,7 @@ def test_rows_path_invalid_ids():
     assert_close(y, o["y"], TOL[torch.bfloat16], "y with invalid ids")
 
 
-@pytest.mark.parametrize("proj", ["q", "k", "down"])
+@pytest.mark.parametrize("proj", [p[0] for p in wl.PROJ_70B])
 def test_prefill_70b(proj):
     say(f"prefill 70B {proj} r64: sampled rows x columns, both W layouts")
     b = binding()
@@ -590,7 +590,7 @@ def test_prefill_70b(proj):
     assert_close(t[rows], o["t"], TOL[w.dtype], "t sampled")
 
 
-@pytest.mark.parametrize("proj", ["q", "v", "up"])
+@pytest.mark.parametrize("proj", [p[0] for p in wl.PROJ_70B])
 def test_mixed_rank_70b(proj):
     say(f"mixed-rank 70B {proj}: ragged vs padded, sampled vs oracle")
     b = binding()
