@@ -615,6 +615,9 @@ def bench_serving(torch, args):
     arrivals per step (the queue is saturated, so admission has a choice);
     each step the admission scheduler forms a batch of at most 32 rows, the
     slot cache (250 slots) maps it to slots, and lora_layer_apply runs it.
+    A load started in a step completes before the next step (the cache
+    completes loads only where the loop waits), so the run depends on the
+    seed alone.
     Reported per policy (the page's locality weight 0.35; 0 = first come
     first served; a strong weight of 8; 0.35 with a cap of 8 adapters per
     batch): distinct
@@ -634,7 +637,9 @@ def bench_serving(torch, args):
     out = {}
     for label, w_local, cap in (("locality_0.35", 0.35, rows_max), ("fifo", 0.0, rows_max),
                                 ("locality_8", 8.0, rows_max), ("locality_0.35_cap8", 0.35, 8)):
-        c = b.Cache(torch.bfloat16, [(d, d)], r, n_ad, n_slots, 8, device=dev)
+        # loads complete only where the loop waits for them (after each
+        # step's batch), so one seed always forms the same batches
+        c = b.Cache(torch.bfloat16, [(d, d)], r, n_ad, n_slots, 8, device=dev, explicit_poll=True)
         n_el = c.blob_layout(r)[2]
         blobs = torch.empty(n_ad * n_el, dtype=torch.bfloat16, pin_memory=True)
         blobs.copy_((torch.randn(n_ad * n_el, generator=g, device=dev) / 32).to(torch.bfloat16))
@@ -658,11 +663,13 @@ def bench_serving(torch, args):
                 stats0 = c.stats()
             n = len(ad)
             if n == 0:
+                c.wait()
                 continue
             slots = c.map(ad)
             b.lora_layer_apply(c.pool(0), x[:n], W, torch.as_tensor(slots, device=dev), w_layout=b.LORA_W_OUT_IN,
                                mode=b.LORA_MODE_BGMV)
             c.release()
+            c.wait()   # the loads this step started are resident from the next step on
             if step >= warm:
                 n_rows.append(n)
                 distinct.append(info["distinct_adapters"])

@@ -444,6 +444,11 @@ typedef enum {
 #define LORA_CACHE_ANY_RANK 2  /* accept every rank 1..r_max (otherwise ranks must
                                   be multiples of 16 bytes of elements that divide
                                   512*16/elem, the ranks the streaming shrink takes) */
+#define LORA_CACHE_EXPLICIT_POLL 4 /* a device cache whose loads complete only at
+                                  lora_cache_poll or lora_cache_wait, never inside
+                                  lora_cache_request or lora_cache_map: admission
+                                  then depends on the call sequence and the points
+                                  where the caller polls, not on copy timing */
 
 typedef struct {
     int64_t requests;          /* lora_cache_request calls */

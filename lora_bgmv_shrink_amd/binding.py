@@ -32,7 +32,7 @@ LORA_LAYOUT_UNIFORM, LORA_LAYOUT_RAGGED = 0, 1
 LORA_MODE_AUTO, LORA_MODE_BGMV, LORA_MODE_SGMV = 0, 1, 2
 LORA_W_IN_OUT, LORA_W_OUT_IN = 0, 1
 LORA_CACHE_RESIDENT, LORA_CACHE_LOADING, LORA_CACHE_DEFERRED = 0, 1, 2
-LORA_CACHE_HOST_ONLY, LORA_CACHE_ANY_RANK = 1, 2
+LORA_CACHE_HOST_ONLY, LORA_CACHE_ANY_RANK, LORA_CACHE_EXPLICIT_POLL = 1, 2, 4
 
 # Every symbol the C header declares.
 EXPORTS = [
@@ -533,7 +533,7 @@ class Cache:
 
     def __init__(self, dtype: torch.dtype, parts, r_max: int, n_adapters: int, n_slots: int,
                  max_loads_in_flight: int, host_only: bool = False, any_rank: bool = False,
-                 device=None):
+                 device=None, explicit_poll: bool = False):
         self.dtype = dtype
         self.parts = [(int(a), int(b)) for a, b in parts]
         self.r_max, self.n_adapters, self.n_slots = r_max, n_adapters, n_slots
@@ -541,7 +541,8 @@ class Cache:
         self.device = torch.device(device) if device is not None else None
         d_in = np.ascontiguousarray([a for a, _ in self.parts], np.int32)
         d_out = np.ascontiguousarray([b for _, b in self.parts], np.int32)
-        flags = (LORA_CACHE_HOST_ONLY if host_only else 0) | (LORA_CACHE_ANY_RANK if any_rank else 0)
+        flags = ((LORA_CACHE_HOST_ONLY if host_only else 0) | (LORA_CACHE_ANY_RANK if any_rank else 0) |
+                 (LORA_CACHE_EXPLICIT_POLL if explicit_poll else 0))
         h = ctypes.c_void_p()
         if host_only:
             st = _lib.lora_cache_create(ctypes.byref(h), _dt(dtype), len(self.parts), d_in.ctypes.data,

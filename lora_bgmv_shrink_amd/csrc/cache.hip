@@ -154,10 +154,11 @@ bool rank_taken(const lora_cache_s* c, int32_t rank) {
 
 // Notice completed loads.  A host-only cache has no copies: its loads
 // complete when the caller polls or waits (explicit), never inside request
-// or map, so a policy run is a pure function of the call sequence.
+// or map, so a policy run is a pure function of the call sequence.  A device
+// cache created with LORA_CACHE_EXPLICIT_POLL behaves the same way.
 lora_status_t poll_loads(lora_cache_s* c, int32_t* n_done, bool explicit_poll) {
     int32_t done = 0;
-    if (c->host_only && !explicit_poll) {
+    if ((c->host_only || (c->flags & LORA_CACHE_EXPLICIT_POLL)) && !explicit_poll) {
         if (n_done) *n_done = 0;
         return LORA_OK;
     }
@@ -269,7 +270,7 @@ lora_status_t lora_cache_create(lora_cache_t* out, lora_dtype_t dtype, int32_t n
     *out = nullptr;
     if ((dtype != LORA_F32 && dtype != LORA_BF16) || n_parts < 1 || !d_in || !d_out ||
         r_max < 1 || n_adapters < 1 || n_slots < 1 || max_loads_in_flight < 1 ||
-        (flags & ~(LORA_CACHE_HOST_ONLY | LORA_CACHE_ANY_RANK)) != 0)
+        (flags & ~(LORA_CACHE_HOST_ONLY | LORA_CACHE_ANY_RANK | LORA_CACHE_EXPLICIT_POLL)) != 0)
         return LORA_E_INVALID;
     if (r_max > kMaxRank) return LORA_E_UNSUPPORTED;
     for (int32_t p = 0; p < n_parts; ++p)

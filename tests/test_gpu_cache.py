@@ -309,3 +309,26 @@ def test_fp32_cache_layer_matches_oracle():
             assert_close(y, ref, TOL[torch.float32], f"fp32 cache step {step} part {p}")
         c.release()
     c.destroy()
+
+
+def test_explicit_poll_cache_completes_loads_only_when_asked():
+    """LORA_CACHE_EXPLICIT_POLL: a finished copy is not noticed by request or
+    map; the adapter becomes resident at the caller's poll."""
+    b = binding()
+    d, r = 256, 16
+    c = b.Cache(torch.bfloat16, [(d, d)], r, 4, 2, 2, device=DEV, explicit_poll=True)
+    n_el = c.blob_layout(r)[2]
+    blob = torch.zeros(n_el, dtype=torch.bfloat16, pin_memory=True)
+    for a in range(4):
+        c.register_blob(a, r, 2.0, blob)
+    assert c.request(1) == b.LORA_CACHE_LOADING
+    torch.cuda.synchronize()
+    import time
+    time.sleep(0.05)                                # the copy is long done
+    assert c.request(1) == b.LORA_CACHE_LOADING     # but not noticed
+    with pytest.raises(b.LoraError) as e:
+        c.map([1])
+    assert e.value.status == b.LORA_E_NOT_RESIDENT
+    assert c.poll() == 1
+    assert c.request(1) == b.LORA_CACHE_RESIDENT
+    c.destroy()
