@@ -20,7 +20,22 @@ constexpr int kMaxAdaptersSegments = 16383;
 constexpr int64_t kRaggedAlignElems = 128;   // 256 B in bf16, 512 B in fp32
 
 int elem_bytes(lora_dtype_t d) { return d == LORA_BF16 ? 2 : 4; }
-bool dtype_ok(lora_dtype_t d) { return d == LORA_F32 || d == LORA_BF16; }
+// Enum arguments come from C callers and may hold any int: validate their
+// bits as an int (a value past the enumerators is not a valid enum value in
+// C++, so it must not be read as one), then use the enum.
+// (taken by reference: even copying an invalid value is a load of it)
+template <typename E>
+int raw(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+    int v = 0;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+bool dtype_ok(const lora_dtype_t& d) { return raw(d) == LORA_F32 || raw(d) == LORA_BF16; }
+bool mode_ok(const lora_mode_t& m) {
+    return raw(m) == LORA_MODE_AUTO || raw(m) == LORA_MODE_BGMV || raw(m) == LORA_MODE_SGMV;
+}
+bool w_layout_ok(const lora_w_layout_t& w) { return raw(w) == LORA_W_IN_OUT || raw(w) == LORA_W_OUT_IN; }
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool ld_ok(int64_t ld, int64_t minv, int eb) { return ld >= minv && (ld * eb) % 16 == 0; }
 
@@ -194,7 +209,11 @@ lora_status_t scratch_address(hipStream_t stream, void** out) {
 
 extern "C" {
 
-const char* lora_status_string(lora_status_t s) {
+const char* lora_status_string(lora_status_t status) {
+    // a caller may pass any int: read the bits as an int, not as the enum
+    // (values past the enumerators are not valid enum values in C++)
+    int s = 0;
+    std::memcpy(&s, &status, sizeof s);
     switch (s) {
         case LORA_OK: return "LORA_OK";
         case LORA_E_INVALID: return "LORA_E_INVALID: invalid argument";
@@ -240,7 +259,7 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
                                const void* A, const void* B, const float* scales) {
     if (!out) return LORA_E_INVALID;
     *out = nullptr;
-    if (!dtype_ok(dtype) || (layout != LORA_LAYOUT_UNIFORM && layout != LORA_LAYOUT_RAGGED))
+    if (!dtype_ok(dtype) || (raw(layout) != LORA_LAYOUT_UNIFORM && raw(layout) != LORA_LAYOUT_RAGGED))
         return LORA_E_INVALID;
     if (n_adapters <= 0 || d_in <= 0 || d_out <= 0 || r_max <= 0 || !A || !B || !scales)
         return LORA_E_INVALID;
@@ -456,8 +475,7 @@ lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
 lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t mode,
                                    size_t* bytes) {
     if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
-    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
-        return LORA_E_INVALID;
+    if (!mode_ok(mode)) return LORA_E_INVALID;
     const lora_mode_t m = resolve_mode(mode, n_rows, pool->dev.n_adapters);
     size_t off = align_up((size_t)n_rows * t_stride(pool->dev.r_max) * 4, 256) + ext_bytes(pool, n_rows);
     if (m == LORA_MODE_BGMV) {
@@ -483,9 +501,8 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
                                lora_dtype_t y_dtype, int64_t ldy, lora_mode_t mode, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
     if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
-    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
-        return LORA_E_INVALID;
-    if (w_layout != LORA_W_IN_OUT && w_layout != LORA_W_OUT_IN) return LORA_E_INVALID;
+    if (!mode_ok(mode)) return LORA_E_INVALID;
+    if (!w_layout_ok(w_layout)) return LORA_E_INVALID;
     if (n_rows == 0) return LORA_OK;
     const PoolDev& P = pool->dev;
     const int eb = elem_bytes(pool->dtype);
@@ -592,8 +609,7 @@ lora_status_t lora_layer_apply_noalloc(lora_pool_t pool, const void* x, int64_t 
                                        lora_dtype_t y_dtype, int64_t ldy, lora_mode_t mode,
                                        hipStream_t stream) {
     if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
-    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
-        return LORA_E_INVALID;
+    if (!mode_ok(mode)) return LORA_E_INVALID;
     if (n_rows == 0) return LORA_OK;
     size_t need = 0;
     lora_status_t st = lora_layer_workspace(pool, n_rows, mode, &need);
@@ -620,7 +636,7 @@ lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx
                                     lora_dtype_t y_dtype, int64_t ldy, void* ws, size_t ws_bytes,
                                     hipStream_t stream) {
     if (check_pool(pool) != LORA_OK || n_rows < 0 || !dtype_ok(y_dtype)) return LORA_E_INVALID;
-    if (w_layout != LORA_W_IN_OUT && w_layout != LORA_W_OUT_IN) return LORA_E_INVALID;
+    if (!w_layout_ok(w_layout)) return LORA_E_INVALID;
     if (n_rows == 0) return LORA_OK;
     const PoolDev& P = pool->dev;
     const int eb = elem_bytes(pool->dtype);
@@ -668,7 +684,7 @@ lora_status_t lora_base_gemm_expand(lora_pool_t pool, const void* x, int64_t ldx
 lora_status_t lora_merge_adapter(lora_pool_t pool, int32_t adapter, void* W, int64_t ldw,
                                  lora_w_layout_t w_layout, float sign, hipStream_t stream) {
     if (check_pool(pool) != LORA_OK || !W || !std::isfinite(sign)) return LORA_E_INVALID;
-    if (w_layout != LORA_W_IN_OUT && w_layout != LORA_W_OUT_IN) return LORA_E_INVALID;
+    if (!w_layout_ok(w_layout)) return LORA_E_INVALID;
     const PoolDev& P = pool->dev;
     if (adapter < 0 || adapter >= P.n_adapters) return LORA_E_ID_RANGE;
     const int64_t w_min = (w_layout == LORA_W_IN_OUT) ? P.d_out : P.d_in;

@@ -268,7 +268,9 @@ lora_status_t lora_cache_create(lora_cache_t* out, lora_dtype_t dtype, int32_t n
                                 int32_t flags) {
     if (!out) return LORA_E_INVALID;
     *out = nullptr;
-    if ((dtype != LORA_F32 && dtype != LORA_BF16) || n_parts < 1 || !d_in || !d_out ||
+    int dt = 0;   // validated as an int: a C caller may pass any value
+    std::memcpy(&dt, &dtype, sizeof dt);
+    if ((dt != LORA_F32 && dt != LORA_BF16) || n_parts < 1 || !d_in || !d_out ||
         r_max < 1 || n_adapters < 1 || n_slots < 1 || max_loads_in_flight < 1 ||
         (flags & ~(LORA_CACHE_HOST_ONLY | LORA_CACHE_ANY_RANK | LORA_CACHE_EXPLICIT_POLL)) != 0)
         return LORA_E_INVALID;

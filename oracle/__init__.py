@@ -57,11 +57,15 @@ def _bind(lib):
 
 
 def load(path: Optional[str] = None):
-    """Load (building when absent or stale) and return the ctypes library."""
+    """Load (building when absent or stale) and return the ctypes library.
+    LORA_ORACLE_LIB names a prebuilt copy to load instead (the sanitizer
+    run's instrumented build)."""
     global _lib
     if path is not None:
         return _bind(ctypes.CDLL(path))
     with _lock:
+        if _lib is None and os.environ.get("LORA_ORACLE_LIB"):
+            _lib = _bind(ctypes.CDLL(os.environ["LORA_ORACLE_LIB"]))
         if _lib is None:
             if (not os.path.exists(LIB)) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
                 build()
