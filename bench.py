@@ -240,10 +240,7 @@ def bench_decode(torch, args):
     # the standalone BGMV shrink entry point on the same batch
     for r in reps:
         r["t"] = torch.zeros((n, r["p"].pool.r_max), dtype=torch.float32, device=dev)
-        nb = b.lora_bgmv_shrink_workspace(r["pool"], n)   # K-slice partial sums (no zeroing needed)
-        r["ws_shr"] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-    g_shr = capture(torch, lambda: [b.lora_bgmv_shrink(r["pool"], r["p"].x, r["ids"], t=r["t"], ws=r["ws_shr"])
-                                    for r in reps])
+    g_shr = capture(torch, lambda: [b.lora_bgmv_shrink(r["pool"], r["p"].x, r["ids"], t=r["t"]) for r in reps])
     d_shr = time_graph(torch, g_shr, kr) / R
 
     # diversity sweep: 32 rows on 1, 2, 4, ... 32 distinct adapters (each used

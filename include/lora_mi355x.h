@@ -159,7 +159,9 @@ lora_status_t lora_workspace_clear(void* ws, size_t bytes, hipStream_t stream);
 /* Segments                                                                */
 /* ---------------------------------------------------------------------- */
 
-/* Workspace bytes for lora_segments_build (0 when none is needed). */
+/* Workspace bytes for lora_segments_build: always 0 with the present
+ * one-workgroup counting sort (the argument is kept so that a build for
+ * larger pools can take scratch without an interface change); ws may be NULL. */
 lora_status_t lora_segments_workspace(int32_t n_rows, int32_t n_adapters, size_t* bytes);
 
 /* Stable group-by of ids[n_rows] (device) into *seg (one launch, integer
@@ -173,19 +175,23 @@ lora_status_t lora_segments_build(const int32_t* ids, int32_t n_rows, int32_t n_
 /* BGMV: per-row gather of the row's adapter (decode)                     */
 /* ---------------------------------------------------------------------- */
 
-/* Workspace bytes for lora_bgmv_shrink at this batch size. */
-lora_status_t lora_bgmv_shrink_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes);
-
 /* Shrink: t[i, 0:r_max] = x_i A[a_i] (fp32, unscaled), one launch for the
- * whole batch.  Columns [r_{a_i}, r_max) and base-only rows are written 0.
+ * whole batch: every row gathers its own adapter's A by id ("Serving
+ * multiple LoRAs: segmented matrix multiplies and adapter scheduling",
+ * section "Not merging the weights, computing in batches"; "Serving Many
+ * LoRA Adapters" (praveentn.live), section "Punica: The Segmented
+ * Gather-Scatter Kernel": one launch over a heterogeneous batch).  Columns
+ * [r_{a_i}, r_max) and base-only rows are written 0.
  *   x [n_rows, ldx] (pool dtype), ids [n_rows], t [n_rows, ldt] fp32,
- *   ldt >= r_max. */
+ *   ldt >= r_max.  No workspace. */
 lora_status_t lora_bgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
                                const int32_t* ids, int32_t n_rows,
-                               float* t, int64_t ldt,
-                               void* ws, size_t ws_bytes, hipStream_t stream);
+                               float* t, int64_t ldt, hipStream_t stream);
 
-/* Expand: y_i (+)= s_{a_i} * t_i B[a_i], one launch for the whole batch.
+/* Expand: y_i (+)= s_{a_i} * t_i B[a_i], one launch for the whole batch,
+ * each row gathering its own adapter's B (same passages as the shrink; the
+ * scale travels with the adapter: "Serving many LoRA adapters"
+ * (blog.ecitis.org), section "Correctness across tenants").
  * accumulate = 0: y_i is overwritten with the LoRA term (0 on base-only
  * rows).  accumulate = 1: the term is added to y_i; base-only rows are not
  * touched.  y [n_rows, ldy] of y_dtype. */
@@ -202,8 +208,10 @@ lora_status_t lora_bgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
  * (0: it does not split).  No zero-filling is needed. */
 lora_status_t lora_sgmv_shrink_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes);
 
-/* Shrink over segments from lora_segments_build (same t layout and values
- * as lora_bgmv_shrink: original row order).  Rows of the base-only run get
+/* Shrink over segments from lora_segments_build, one small product per
+ * segment ("Serving multiple LoRAs...", section "Not merging the weights,
+ * computing in batches": sort rows by adapter, then one contraction per run)
+ * (same t layout and values as lora_bgmv_shrink: original row order).  Rows of the base-only run get
  * t = 0.  Id-range errors are reported by lora_segments_build's `status`.
  * The grid is sized from n_rows and the pool size, so the segment count
  * never has to come back to the host.  With a workspace of
@@ -217,7 +225,9 @@ lora_status_t lora_sgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx,
                                float* t, int64_t ldt, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
-/* Expand over segments (same semantics as lora_bgmv_expand). */
+/* Expand over segments (same semantics as lora_bgmv_expand; the results go
+ * back to each row's original position: "Serving many LoRA adapters"
+ * (blog.ecitis.org), section "Replay": grouped product, then scatter-add). */
 lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
                                const lora_segments_t* seg, int32_t n_rows,
                                void* y, lora_dtype_t y_dtype, int64_t ldy, int accumulate,

@@ -38,7 +38,7 @@ LORA_CACHE_HOST_ONLY, LORA_CACHE_ANY_RANK, LORA_CACHE_EXPLICIT_POLL = 1, 2, 4
 EXPORTS = [
     "lora_status_string", "lora_adapter_param_count", "lora_pool_ragged_offsets", "lora_pool_create",
     "lora_pool_destroy", "lora_pool_param_count", "lora_pool_last_error", "lora_workspace_clear",
-    "lora_segments_workspace", "lora_segments_build", "lora_bgmv_shrink_workspace", "lora_bgmv_shrink",
+    "lora_segments_workspace", "lora_segments_build", "lora_bgmv_shrink",
     "lora_bgmv_expand", "lora_sgmv_shrink_workspace", "lora_sgmv_shrink", "lora_sgmv_expand", "lora_layer_workspace",
     "lora_layer_apply", "lora_base_gemm_expand_workspace", "lora_base_gemm_expand", "lora_decode_workspace",
     "lora_decode_stream",
@@ -99,8 +99,7 @@ def _load():
         "lora_workspace_clear": (st, [p, sz, p]),
         "lora_segments_workspace": (st, [i32, i32, p]),
         "lora_segments_build": (st, [p, i32, i32, p, p, p, sz, p]),
-        "lora_bgmv_shrink_workspace": (st, [p, i32, p]),
-        "lora_bgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p, sz, p]),
+        "lora_bgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p]),
         "lora_bgmv_expand": (st, [p, p, i64, p, i32, p, st, i64, ctypes.c_int, p]),
         "lora_sgmv_shrink_workspace": (st, [p, i32, p]),
         "lora_sgmv_shrink": (st, [p, p, i64, p, i32, p, i64, p, sz, p]),
@@ -324,22 +323,11 @@ def _t_out(pool: Pool, n: int, t: Optional[torch.Tensor], device) -> torch.Tenso
     return t
 
 
-def lora_bgmv_shrink_workspace(pool: Pool, n_rows: int) -> int:
-    b = ctypes.c_size_t()
-    _check(_lib.lora_bgmv_shrink_workspace(pool.handle, n_rows, ctypes.byref(b)), "lora_bgmv_shrink_workspace")
-    return b.value
-
-
-def lora_bgmv_shrink(pool: Pool, x: torch.Tensor, ids: torch.Tensor, t: Optional[torch.Tensor] = None,
-                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+def lora_bgmv_shrink(pool: Pool, x: torch.Tensor, ids: torch.Tensor, t: Optional[torch.Tensor] = None) -> torch.Tensor:
     n = ids.numel()
     t = _t_out(pool, n, t, x.device)
-    need = lora_bgmv_shrink_workspace(pool, n)
-    if ws is None:
-        ws = _workspace(need, x.device)
-    _check(_lib.lora_bgmv_shrink(pool.handle, _ptr(x), _ld(x), _ptr(ids), n, _ptr(t), _ld(t), _ptr(ws),
-                                 0 if ws is None else ws.numel(), ctypes.c_void_p(_stream(x.device))),
-           "lora_bgmv_shrink")
+    _check(_lib.lora_bgmv_shrink(pool.handle, _ptr(x), _ld(x), _ptr(ids), n, _ptr(t), _ld(t),
+                                 ctypes.c_void_p(_stream(x.device))), "lora_bgmv_shrink")
     return t
 
 

@@ -394,16 +394,8 @@ lora_status_t lora_segments_build(const int32_t* ids, int32_t n_rows, int32_t n_
     return dev_status(launch_segments(ids, n_rows, n_adapters, seg, status, stream));
 }
 
-lora_status_t lora_bgmv_shrink_workspace(lora_pool_t pool, int32_t n_rows, size_t* bytes) {
-    if (!pool || !bytes || n_rows < 0) return LORA_E_INVALID;
-    BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
-    *bytes = bgmv_shrink_ws_bytes(plan, n_rows);
-    return LORA_OK;
-}
-
 lora_status_t lora_bgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx, const int32_t* ids,
-                               int32_t n_rows, float* t, int64_t ldt, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
+                               int32_t n_rows, float* t, int64_t ldt, hipStream_t stream) {
     if (check_pool(pool) != LORA_OK || n_rows < 0) return LORA_E_INVALID;
     if (n_rows == 0) return LORA_OK;
     const int eb = elem_bytes(pool->dtype);
@@ -411,10 +403,7 @@ lora_status_t lora_bgmv_shrink(lora_pool_t pool, const void* x, int64_t ldx, con
     if (ldx < pool->dev.d_in || ldt < pool->dev.r_max) return LORA_E_INVALID;
     if (!al16(x) || !ld_ok(ldx, pool->dev.d_in, eb)) return LORA_E_UNSUPPORTED;
     BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, eb, n_rows);
-    const size_t need = bgmv_shrink_ws_bytes(plan, n_rows);
-    if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return LORA_E_WORKSPACE;
-    return dev_status(launch_bgmv_shrink(pool->dev, pool->dtype, x, ldx, ids, n_rows, t, ldt, ws,
-                                         plan, stream));
+    return dev_status(launch_bgmv_shrink(pool->dev, pool->dtype, x, ldx, ids, n_rows, t, ldt, plan, stream));
 }
 
 lora_status_t lora_bgmv_expand(lora_pool_t pool, const float* t, int64_t ldt, const int32_t* ids,
@@ -479,8 +468,6 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
     const lora_mode_t m = resolve_mode(mode, n_rows, pool->dev.n_adapters);
     size_t off = align_up((size_t)n_rows * t_stride(pool->dev.r_max) * 4, 256) + ext_bytes(pool, n_rows);
     if (m == LORA_MODE_BGMV) {
-        BgmvShrinkPlan plan = plan_bgmv_shrink(pool->dev, elem_bytes(pool->dtype), n_rows);
-        off += bgmv_shrink_ws_bytes(plan, n_rows);
         // the W layout is not known here: room for the few-hundred-row path
         // (W stored [d_out, d_in]) and for the fused GEMM (either layout)
         if (rows_ok(pool, n_rows)) off = std::max(off, rows_ws_bytes(pool, n_rows));
@@ -558,8 +545,7 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
     const int32_t* gemm_perm = nullptr;   // SGMV: the GEMM visits rows grouped by adapter
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
-        e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, base + after_t, plan,
-                               stream, t_ext, lde);
+        e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, plan, stream, t_ext, lde);
     } else {
         lora_segments_t own;
         const lora_segments_t* sg = seg;

@@ -185,15 +185,12 @@ __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_lds(PoolDev P, c
 
 // Expand.  One wave per (row, chunk of 64*VE output columns); lane l owns VE
 // consecutive columns and streams the matching 16-byte pieces of the r rows
-// of B_a:  y_i[c] (+)= s_a * sum_j t_i[j] * B_a[j][c].  With an fp32 addend
-// (the base product of the same rows), y_i[c] = addend_i[c] + that term,
-// rounded once; rows without a term get the addend alone.
+// of B_a:  y_i[c] (+)= s_a * sum_j t_i[j] * B_a[j][c].
 template <typename T, typename TY>
 __global__ __launch_bounds__(256) void k_bgmv_expand(PoolDev P, const float* __restrict__ t,
                                                      int64_t ldt, const int32_t* __restrict__ ids,
                                                      int n, TY* __restrict__ y, int64_t ldy,
-                                                     int accumulate, int vec_y, int n_chunks,
-                                                     const float* __restrict__ addend, int64_t lda) {
+                                                     int accumulate, int vec_y, int n_chunks) {
     constexpr int VE = 16 / sizeof(T);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -214,7 +211,7 @@ __global__ __launch_bounds__(256) void k_bgmv_expand(PoolDev P, const float* __r
 
     if (!id_ok(a, P.n_adapters)) {
         if (lane == 0 && ch == 0 && a != -1) flag_bad_id(P.err);
-        if (accumulate && !addend) return;
+        if (accumulate) return;
     } else {
         const int r = P.ranks[a];
         const float sc = P.scales[a];
@@ -248,25 +245,6 @@ __global__ __launch_bounds__(256) void k_bgmv_expand(PoolDev P, const float* __r
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[e] *= sc;
     }
-    if (addend) {
-        // the base product of this row: 16-byte pieces when whole (lda is a
-        // multiple of 4 floats and the rows start 16-byte aligned)
-        const float* ai = addend + (int64_t)i * lda + c0;
-        if (full) {
-#pragma unroll
-            for (int e = 0; e < VE; e += 4) {
-                const float4 b4 = *(const float4*)(ai + e);
-                acc[e] += b4.x;
-                acc[e + 1] += b4.y;
-                acc[e + 2] += b4.z;
-                acc[e + 3] += b4.w;
-            }
-        } else {
-            for (int e = 0; e < VE; ++e)
-                if (c0 + e < d_out) acc[e] += ai[e];
-        }
-    }
-
     if (full && vec_y && (int)(16 / sizeof(TY)) <= VE) {
         // VE * sizeof(TY) bytes per lane: one or two 16-byte stores
         constexpr int YV = 16 / sizeof(TY);
@@ -294,22 +272,16 @@ __global__ __launch_bounds__(256) void k_bgmv_expand(PoolDev P, const float* __r
 
 }  // namespace
 
-BgmvShrinkPlan plan_bgmv_shrink(const PoolDev& P, int elem_bytes, int32_t n_rows) {
-    (void)n_rows;
+BgmvShrinkPlan plan_bgmv_shrink(const PoolDev& P, int, int32_t) {
     // The streaming kernel needs every rank in the pool to tile 16-byte
     // vectors and whole k-rows per pass; uniform pools check one rank.
-    const int VE = 16 / elem_bytes;
     BgmvShrinkPlan plan;
-    plan.slices = 1;
     plan.ks = (P.vec_a && P.stream_ok) ? 1 : 0;
-    (void)VE;
     return plan;
 }
 
-size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan&, int32_t) { return 0; }
-
 hipError_t launch_bgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
-                              const int32_t* ids, int32_t n_rows, float* t, int64_t ldt, void*,
+                              const int32_t* ids, int32_t n_rows, float* t, int64_t ldt,
                               const BgmvShrinkPlan& plan, hipStream_t stream, void* t_ext, int64_t lde) {
     dim3 grid((unsigned)n_rows);
     const bool stream_path = plan.ks == 1;
@@ -359,9 +331,7 @@ hipError_t launch_make_t_ext(const PoolDev& P, lora_dtype_t dt, const float* t, 
 
 hipError_t launch_bgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                               const int32_t* ids, int32_t n_rows, void* y, lora_dtype_t ydt,
-                              int64_t ldy, int accumulate, bool vec_y, hipStream_t stream,
-                              const float* addend, int64_t lda) {
-    if (addend && (accumulate || (lda & 3) || ((uintptr_t)addend & 15))) return hipErrorInvalidValue;
+                              int64_t ldy, int accumulate, bool vec_y, hipStream_t stream) {
     const int VE = (dt == LORA_BF16) ? 8 : 4;
     const int n_chunks = (int)ceil_div(P.d_out, 64 * VE);
     dim3 grid((unsigned)(ceil_div(n_rows, 4) * n_chunks));
@@ -369,17 +339,17 @@ hipError_t launch_bgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t,
     if (dt == LORA_BF16) {
         if (ydt == LORA_BF16)
             hipLaunchKernelGGL((k_bgmv_expand<bf16, bf16>), grid, dim3(256), 0, stream, P, t, ldt, ids,
-                               n_rows, (bf16*)y, ldy, accumulate, vy, n_chunks, addend, lda);
+                               n_rows, (bf16*)y, ldy, accumulate, vy, n_chunks);
         else
             hipLaunchKernelGGL((k_bgmv_expand<bf16, float>), grid, dim3(256), 0, stream, P, t, ldt,
-                               ids, n_rows, (float*)y, ldy, accumulate, vy, n_chunks, addend, lda);
+                               ids, n_rows, (float*)y, ldy, accumulate, vy, n_chunks);
     } else {
         if (ydt == LORA_BF16)
             hipLaunchKernelGGL((k_bgmv_expand<float, bf16>), grid, dim3(256), 0, stream, P, t, ldt,
-                               ids, n_rows, (bf16*)y, ldy, accumulate, vy, n_chunks, addend, lda);
+                               ids, n_rows, (bf16*)y, ldy, accumulate, vy, n_chunks);
         else
             hipLaunchKernelGGL((k_bgmv_expand<float, float>), grid, dim3(256), 0, stream, P, t, ldt,
-                               ids, n_rows, (float*)y, ldy, accumulate, vy, n_chunks, addend, lda);
+                               ids, n_rows, (float*)y, ldy, accumulate, vy, n_chunks);
     }
     return hipGetLastError();
 }

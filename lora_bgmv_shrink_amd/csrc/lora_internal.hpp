@@ -187,22 +187,17 @@ hipError_t launch_segments(const int32_t* ids, int32_t n_rows, int32_t n_adapter
 
 // BGMV shrink: one workgroup per row (no workspace).
 struct BgmvShrinkPlan {
-    int32_t slices;   // always 1
     int32_t ks;       // 1: streaming kernel, 0: LDS-staged generic kernel
 };
 BgmvShrinkPlan plan_bgmv_shrink(const PoolDev& P, int elem_bytes, int32_t n_rows);
-size_t bgmv_shrink_ws_bytes(const BgmvShrinkPlan& plan, int32_t n_rows);
 hipError_t launch_bgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, int64_t ldx,
                               const int32_t* ids, int32_t n_rows, float* t, int64_t ldt,
-                              void* ws, const BgmvShrinkPlan& plan, hipStream_t stream,
+                              const BgmvShrinkPlan& plan, hipStream_t stream,
                               void* t_ext = nullptr, int64_t lde = 0);
 
-// addend (optional, fp32, rows of lda floats, lda % 4 == 0, 16-byte aligned;
-// not with accumulate): y = addend + the term, rounded once.
 hipError_t launch_bgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                               const int32_t* ids, int32_t n_rows, void* y, lora_dtype_t ydt,
-                              int64_t ldy, int accumulate, bool vec_y, hipStream_t stream,
-                              const float* addend = nullptr, int64_t lda = 0);
+                              int64_t ldy, int accumulate, bool vec_y, hipStream_t stream);
 
 // SGMV shrink / expand (MFMA over segment tiles).
 // part (optional, sgmv_shrink_part_bytes of workspace): K is split into

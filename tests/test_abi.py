@@ -103,7 +103,7 @@ def test_validation_before_any_device_work():
     odd = np.array([0, 64 * 8 + 3], np.int64)
     assert lib.lora_pool_create(ctypes.byref(h), 1, 1, 2, 64, 64, 8, rk.ctypes.data, odd.ctypes.data, bo.ctypes.data, fake, fake, sc2.ctypes.data) == b.LORA_E_UNSUPPORTED
     # hot calls with a null pool
-    assert lib.lora_bgmv_shrink(None, fake, 64, fake, 4, fake, 16, None, 0, None) == b.LORA_E_INVALID
+    assert lib.lora_bgmv_shrink(None, fake, 64, fake, 4, fake, 16, None) == b.LORA_E_INVALID
     assert lib.lora_bgmv_expand(None, fake, 16, fake, 4, fake, 1, 64, 0, None) == b.LORA_E_INVALID
     assert lib.lora_sgmv_shrink(None, fake, 64, None, 4, fake, 16, None, 0, None) == b.LORA_E_INVALID
     assert lib.lora_sgmv_expand(None, fake, 16, None, 4, fake, 1, 64, 0, None) == b.LORA_E_INVALID
