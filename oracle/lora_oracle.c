@@ -15,8 +15,9 @@
  *   tokens is several rows with one adapter id; rows of a matrix product are
  *   independent, so the loop below runs per row.
  *
- *   Base-only rows (adapter id -1, "Serving many LoRA adapters",
- *   blog.ecitis.org, section "Replay": "req C -> base only") get y = x W.
+ *   Base-only rows (adapter id -1; "Serving many LoRA adapters",
+ *   blog.ecitis.org, section "Replay", has a request with no adapter served
+ *   by the base model alone) get y = x W.
  *   Ids outside [-1, n_adapters) are counted as errors and treated as
  *   base-only.
  *
