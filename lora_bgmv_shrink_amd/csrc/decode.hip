@@ -37,15 +37,18 @@ static_assert(FIN_THREADS >= 64 && FIN_THREADS % 64 == 0, "the t partials need o
 constexpr int FIN_RCHUNK = 16;      // rank rows of B loaded together in the finish
 constexpr int FIN_SCHUNK = 8;       // partial slices loaded together in the finish
 
-__device__ __forceinline__ bf16x8_t ld8(const bf16* p, int valid, bool nt) {
-    if (valid >= 8) {
-        if (nt) {
-            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-            u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-            return __builtin_bit_cast(bf16x8_t, v);
-        }
-        return *(const bf16x8_t*)p;
-    }
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes, nontemporal or ordinary
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+    if constexpr (NT) return __builtin_nontemporal_load((const u32x4_t*)p);
+    else return *(const u32x4_t*)p;
+}
+
+template <bool NT = false>
+__device__ __forceinline__ bf16x8_t ld8(const bf16* p, int valid) {
+    if (valid >= 8) return __builtin_bit_cast(bf16x8_t, ld16<NT>(p));
     union { bf16x8_t v; bf16 e[8]; } u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) u.e[e] = (e < valid) ? p[e] : (bf16)0;
@@ -154,9 +157,15 @@ __device__ __forceinline__ void shrink_wave(const PoolDev& P, const DecodePlan& 
 }
 
 // Workgroup (tn, ks): base wave w < 8 streams the 16 rows of W^T for column
-// block w (all of the slice's k-steps in flight, nontemporal: W is read once)
-// and keeps the whole 16-column partial; x of the slice is staged in LDS and
-// serves the MFMAs and the shrink wave.
+// block w (all of the slice's k-steps in flight) and keeps the whole 16-column
+// partial; x of the slice is staged in LDS and serves the MFMAs and the shrink
+// wave.  W is read once.  With the shrink wave, W goes through nontemporal
+// loads, which leave the caches to the adapter blocks that rows of one adapter
+// share; without it, ordinary loads measured 5-7% faster (a wave's load takes
+// 64 bytes of each of 16 rows, the two halves of a 128-byte line coming from
+// two loads, and an ordinary load keeps the line for the second).  The shrink
+// wave's A pieces go out after the x barrier: requested beside x they slowed
+// the staging of x, which every MFMA waits for, by more than they gained.
 //
 // Q4: W holds signed 4-bit weights, row n of bytes at W + n * ldw (input k
 // in the low nibble when even), with scale wscale[n * lds + k / 128].  The
@@ -210,7 +219,7 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
             xv[q] = *(const bf16x8_t*)(X + (int64_t)(m < M ? m : 0) * g.ldx + k);
         } else {
             const int valid = min(8, kend - k);
-            xv[q] = (m < M && valid > 0) ? ld8(X + (int64_t)m * g.ldx + k, valid, false) : bf16x8_t{};
+            xv[q] = (m < M && valid > 0) ? ld8(X + (int64_t)m * g.ldx + k, valid) : bf16x8_t{};
         }
     }
 
@@ -228,7 +237,7 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             if (FULL || j < ngrp) {
-                wq[j] = __builtin_nontemporal_load((const u32x4*)(Wq + j * 64));
+                wq[j] = ld16<LORA>(Wq + j * 64);
                 wsc[j] = Sc[j];
             } else {
                 wq[j] = u32x4{0u, 0u, 0u, 0u};
@@ -239,8 +248,7 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
         const bf16* Wt = (const bf16*)g.W + (int64_t)nc * g.ldw;
 #pragma unroll
         for (int u = 0; u < DS_USTEPS; ++u) {
-            const u32x4 v = __builtin_nontemporal_load((const u32x4*)(Wt + kbeg + u * 32 + kq));
-            bw[u] = __builtin_bit_cast(bf16x8_t, v);
+            bw[u] = __builtin_bit_cast(bf16x8_t, ld16<LORA>(Wt + kbeg + u * 32 + kq));
         }
     } else {
         const bf16* Wt = (const bf16*)g.W + (int64_t)nc * g.ldw;
@@ -248,7 +256,7 @@ __device__ __forceinline__ void stream_body(const PoolDev& P, const DecodePlan& 
         for (int u = 0; u < DS_USTEPS; ++u) {
             const int k = kbeg + u * 32 + kq;
             const int valid = (u < nsteps) ? min(8, kend - k) : 0;
-            bw[u] = (valid > 0 && n < N) ? ld8(Wt + k, valid, true) : bf16x8_t{};
+            bw[u] = (valid > 0 && n < N) ? ld8<LORA>(Wt + k, valid) : bf16x8_t{};
         }
     }
 
