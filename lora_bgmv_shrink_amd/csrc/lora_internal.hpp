@@ -125,36 +125,39 @@ __device__ inline bool find_seg_tile(const int32_t* __restrict__ seg_off, int n_
 }
 
 // find_seg_tile for callers that know the descriptor's capacity (cap >=
-// n_seg): the first 256 run boundaries are requested together with the run
-// count (the entries past n_seg are read but never used), so a batch of up
-// to 256 runs finds its tile in one round of loads.  Also returns the run's
-// first and one-past-last position in perm.
-__device__ inline bool find_seg_tile_cap(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_seg_p,
-                                         int cap, int BM, int b, int lane, int& s_out, int& c_out, int& lo_out,
-                                         int& hi_out) {
+// n_seg): the first 256 run boundaries and run ids are requested together
+// with the run count (the entries past n_seg are read but never used), so a
+// batch of up to 256 runs finds its tile in one round of loads.  Also
+// returns the run's id and its first and one-past-last position in perm.
+__device__ inline bool find_seg_tile_cap(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_ids,
+                                         const int32_t* __restrict__ n_seg_p, int cap, int BM, int b, int lane,
+                                         int& s_out, int& c_out, int& lo_out, int& hi_out, int& id_out) {
     constexpr int PRE = 4;   // chunks of 64 runs requested up front
-    int lo[PRE], hi[PRE];
+    int lo[PRE], hi[PRE], id[PRE];
 #pragma unroll
     for (int q = 0; q < PRE; ++q) {
         const int s = q * 64 + lane;
         lo[q] = s < cap ? seg_off[s] : 0;
         hi[q] = s < cap ? seg_off[s + 1] : 0;
+        id[q] = s < cap ? seg_ids[s] : -1;
     }
     const int n_seg = *n_seg_p;
     int base = 0;
     for (int s0 = 0; s0 < n_seg; s0 += 64) {
         const int s = s0 + lane;
-        int l = 0, h = 0;
+        int l = 0, h = 0, u = -1;
         if (s0 < PRE * 64) {
 #pragma unroll
             for (int q = 0; q < PRE; ++q)
                 if (s0 == q * 64) {
                     l = lo[q];
                     h = hi[q];
+                    u = id[q];
                 }
         } else if (s < n_seg) {
             l = seg_off[s];
             h = seg_off[s + 1];
+            u = seg_ids[s];
         }
         const int cnt = s < n_seg ? (h - l + BM - 1) / BM : 0;
         const int incl = wave_incl_scan(cnt, lane);
@@ -166,6 +169,7 @@ __device__ inline bool find_seg_tile_cap(const int32_t* __restrict__ seg_off, co
             c_out = b - __shfl(excl, L, 64);
             lo_out = __shfl(l, L, 64);
             hi_out = __shfl(h, L, 64);
+            id_out = __shfl(u, L, 64);
             return true;
         }
         base += __shfl(incl, 63, 64);
@@ -262,7 +266,7 @@ struct RowsPlan {
     int32_t St, ks_len;         // K slices of the shrink
     int64_t ldp;                // fp32 pitch of a base partial row
     int64_t rtp;                // fp32 pitch of a t partial row
-    size_t part_off, tpart_off, tiles_off, bytes;   // workspace layout
+    size_t part_off, tpart_off, recs_off, bytes;   // workspace layout
 };
 RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4 = false);
 // base partials part[S][n_rows][ldp] = x W over each K slice; q4: W holds
@@ -299,6 +303,14 @@ struct RowRec {
     int64_t b_off;   // element offset of the row's B block
     int32_t rank;    // 0: no adapter term (base-only or invalid id)
     float scale;
+};
+// RowRec of the row at one position of perm (rows grouped by adapter)
+struct SegRowRec {
+    int64_t b_off;
+    int32_t row;     // the row, in the caller's order
+    int32_t rank;
+    float scale;
+    int32_t pad[3];
 };
 struct DecodeArgs {
     const void* x;

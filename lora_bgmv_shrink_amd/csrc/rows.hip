@@ -1,5 +1,5 @@
-// Batches of a few hundred rows (65 .. 2048): the base product x W, and the
-// adapter term grouped by adapter, in three launches.
+// Batches of a few hundred rows: the base product x W, and the adapter term
+// grouped by adapter, in three launches.
 //
 // At a few hundred rows x W does about as many flops per byte of W as the
 // matrix cores deliver per byte of HBM bandwidth (256 rows: 256 flop/byte
@@ -34,10 +34,15 @@
 // its adapter's slice once:
 //
 //   k_seg_shrink  (segment tile of 16 rows, K slice): t partials = x_rows A_u
-//                 on the matrix cores, A_u's slice transposed into LDS.
-//   k_seg_finish  (segment tile of 8 rows, 512 columns): y = sum of the base
+//                 on the matrix cores, A_u's slice transposed into LDS; slice
+//                 0 also writes each row's record (B offset, rank, scale).
+//   k_seg_finish  (one wave per row and 256 columns): y = sum of the base
 //                 partials in slice order + s_u * (t summed in slice order)
-//                 B_u, rounded once; base-only rows get the base alone.
+//                 B_u, rounded once; base-only rows get the base alone.  The
+//                 partials need only the row, so they are requested at once;
+//                 B follows the row's record.  A column chunk always runs on
+//                 one XCD, so the rows of a popular adapter read its B piece
+//                 from that XCD's L2.
 //
 // Every sum runs in a fixed order, so results do not depend on timing.
 #include "lora_internal.hpp"
@@ -321,19 +326,11 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm(RowsGemmArgs a) {
 constexpr int SS_ROWS = 16;    // rows per segment tile (one MFMA block)
 constexpr int SS_NT = 256;
 constexpr int SS_MAX_LDS = 72 * 1024;   // x + transposed A staging
-
-// Per segment tile of SS_ROWS rows, written by the shrink (slice 0) for the
-// finish: where its rows are in perm, and its adapter's rank (0: base-only
-// rows), scale and B offset.  valid = 0 past the last tile.
-struct TileRec {
-    int64_t b_off;
-    int32_t valid, row0, cnt, rank;
-    float scale;
-    int32_t pad;
-};
+constexpr int SS_LB = 8;       // 16-byte pieces of x and of A per thread per staging batch
 
 struct SegShrinkArgs {
-    TileRec* tiles;
+    SegRowRec* recs;   // [M] by position in perm, the finish's records (slice 0 writes them)
+    const int32_t* ids;
     const bf16* x;
     int64_t ldx;
     const int32_t* perm;
@@ -356,74 +353,105 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
     const int lane = tid & 63;
     const int wave = tid >> 6;
     if (wave == 0) {
-        int s = 0, c = 0, lo = 0, hi = 0;
-        const bool found = find_seg_tile_cap(a.seg_off, a.n_seg, a.cap, SS_ROWS, blockIdx.x, lane, s, c, lo, hi);
+        int s = 0, c = 0, lo = 0, hi = 0, u = -1;
+        const bool found =
+            find_seg_tile_cap(a.seg_off, a.seg_ids, a.n_seg, a.cap, SS_ROWS, blockIdx.x, lane, s, c, lo, hi, u);
         if (lane == 0) {
             sInfo[0] = found ? 1 : 0;
-            sInfo[1] = s;
+            sInfo[1] = u;
             sInfo[2] = lo + c * SS_ROWS;
             sInfo[3] = hi;
         }
     }
     __syncthreads();
     const int ks = blockIdx.y;
-    if (!sInfo[0]) {
-        if (ks == 0 && tid == 0) a.tiles[blockIdx.x].valid = 0;
-        return;
-    }
-    const int s = sInfo[1];
-    const int u = a.seg_ids[s];
+    if (!sInfo[0]) return;   // past the last tile
+    // tile-uniform values, read from LDS by every lane: made visibly uniform
+    // so that the pool tables come through scalar loads
+    const int u = __builtin_amdgcn_readfirstlane(sInfo[1]);
     const bool ok = id_ok(u, P.n_adapters);
-    const int row0 = sInfo[2];
-    const int cnt = min(SS_ROWS, sInfo[3] - row0);
-    if (ks == 0 && tid == 0) {
-        TileRec rec;
+    const int row0 = __builtin_amdgcn_readfirstlane(sInfo[2]);
+    const int cnt = min(SS_ROWS, __builtin_amdgcn_readfirstlane(sInfo[3]) - row0);
+    const int r = ok ? uload(P.ranks, u) : 0;
+    const int64_t aoff = ok ? uload(P.a_off, u) : 0;
+    if (tid < SS_ROWS) sRow[tid] = tid < cnt ? a.perm[row0 + tid] : -1;
+    __syncthreads();
+    if (ks == 0 && tid < cnt) {
+        // the finish's record of the row at position row0 + tid of perm
+        const int row = sRow[tid];
+        SegRowRec rec;
         rec.b_off = ok ? P.b_off[u] : 0;
-        rec.valid = 1;
-        rec.row0 = row0;
-        rec.cnt = cnt;
-        rec.rank = ok ? P.ranks[u] : 0;
+        rec.row = row;
+        rec.rank = r;
         rec.scale = ok ? P.scales[u] : 0.f;
-        rec.pad = 0;
-        a.tiles[blockIdx.x] = rec;
+        rec.pad[0] = rec.pad[1] = rec.pad[2] = 0;
+        a.recs[row0 + tid] = rec;
+        if (!ok && a.ids[row] != -1) flag_bad_id(P.err);   // invalid ids run as base-only rows
     }
     if (!ok) return;   // base-only rows (and invalid ids): no t
-    if (tid < SS_ROWS) sRow[tid] = tid < cnt ? a.perm[row0 + tid] : -1;
-    const int r = P.ranks[u];
     const int RB = (r + 15) / 16;   // 16-rank blocks
     const int kbeg = ks * a.ks_len;
     const int klen = min(P.d_in, kbeg + a.ks_len) - kbeg;
     const int KP = a.kp;
     bf16* sX = (bf16*)smem;                  // [16][KP]
     bf16* sA = sX + SS_ROWS * KP;            // [RB * 16][KP], A_u transposed
-    const bf16* Au = (const bf16*)P.A + P.a_off[u] + (int64_t)kbeg * r;
-    __syncthreads();
+    const bf16* Au = (const bf16*)P.A + aoff + (int64_t)kbeg * r;
 
-    // x rows of the tile, 16-byte pieces; k past the slice and rows past the
-    // tile are 0
+    // Stage the tile's x rows ([16][slice]) and A_u transposed ([rank][slice])
+    // in LDS.  Each thread requests SS_LB 16-byte pieces of each before it
+    // stores any, so a batch costs one memory round trip (one slice of rank
+    // 16 is a single batch); k past the slice, rows past the tile and ranks
+    // past r are 0.
     const int pieces = a.ks_len / 8;
-    for (int v = tid; v < SS_ROWS * pieces; v += SS_NT) {
-        const int m = v / pieces;
-        const int k = (v - m * pieces) * 8;
-        bf16x8_t val{};
-        const int row = sRow[m];
-        if (row >= 0 && k < klen) {
-            const bf16* src = a.x + (int64_t)row * a.ldx + kbeg + k;
-            val = (k + 8 <= klen) ? *(const bf16x8_t*)src : ld8_guard(src, klen - k);
-        }
-        *(bf16x8_t*)(sX + m * KP + k) = val;
-    }
-    // A_u[k][j] -> sA[j][k]; ranks past r and k past the slice are 0
-    if (P.vec_a && r % 8 == 0) {
-        const int G = r / 8;
-        for (int v = tid; v < a.ks_len * G; v += SS_NT) {
-            const int k = v / G;
-            const int j0 = (v - k * G) * 8;
-            union { uint4 q; bf16 e[8]; } w;
-            w.q = k < klen ? *(const uint4*)(Au + (int64_t)k * r + j0) : uint4{0u, 0u, 0u, 0u};
+    const int nx = SS_ROWS * pieces;
+    const bool va = P.vec_a && r % 8 == 0;
+    const int G = va ? r / 8 : 1;
+    const int na = va ? a.ks_len * G : 0;
+    const int nmax = max(nx, na);
+    // the loads carry no branch (an out-of-range piece reads a valid address
+    // and is masked), so the compiler keeps them all in flight; a piece cut
+    // by the end of the slice (d_in not a multiple of 8) is filled afterwards
+    for (int b0 = 0; b0 < nmax; b0 += SS_NT * SS_LB) {
+        u32x4 xv[SS_LB];
+        u32x4 av[SS_LB];
+        bool xok[SS_LB], aok[SS_LB];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sA[(j0 + e) * KP + k] = w.e[e];
+        for (int q = 0; q < SS_LB; ++q) {
+            const int v = b0 + q * SS_NT + tid;
+            const int m = min(v / pieces, SS_ROWS - 1);
+            const int k = (v - m * pieces) * 8;
+            const int row = sRow[m];
+            xok[q] = v < nx && row >= 0 && k + 8 <= klen;
+            xv[q] = *(const u32x4*)(xok[q] ? a.x + (int64_t)row * a.ldx + kbeg + k : a.x);
+            const int ka = v / G;
+            aok[q] = v < na && ka < klen;
+            av[q] = *(const u32x4*)(aok[q] ? Au + (int64_t)ka * r + (v - ka * G) * 8 : Au);
         }
+#pragma unroll
+        for (int q = 0; q < SS_LB; ++q) {
+            const int v = b0 + q * SS_NT + tid;
+            if (v < nx) {
+                const int m = v / pieces;
+                *(u32x4*)(sX + m * KP + (v - m * pieces) * 8) = xok[q] ? xv[q] : u32x4{0u, 0u, 0u, 0u};
+            }
+            if (v < na) {
+                const int k = v / G;
+                const int j0 = (v - k * G) * 8;
+                union { u32x4 q4; bf16 e[8]; } w;
+                w.q4 = aok[q] ? av[q] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sA[(j0 + e) * KP + k] = w.e[e];
+            }
+        }
+    }
+    if (klen % 8) {   // the piece cut by the end of the slice, per row
+        const int k = klen / 8 * 8;
+        for (int m = tid; m < SS_ROWS; m += SS_NT) {
+            const int row = sRow[m];
+            if (row >= 0) *(bf16x8_t*)(sX + m * KP + k) = ld8_guard(a.x + (int64_t)row * a.ldx + kbeg + k, klen - k);
+        }
+    }
+    if (va) {
         for (int v = tid; v < (RB * 16 - r) * a.ks_len; v += SS_NT) {
             const int j = r + v / a.ks_len;
             sA[j * KP + v % a.ks_len] = 0;
@@ -477,16 +505,15 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
 // Finish over segment tiles: partial sums + scaled expand, y rounded once
 // ---------------------------------------------------------------------------
 
-constexpr int FS_NT = 256;             // 4 waves
-constexpr int FS_VE = 8;               // columns per lane (16-byte B pieces)
-constexpr int FS_COLS = 64 * FS_VE;    // columns per workgroup
+constexpr int FS_NT = 256;             // 4 waves, one row each
+constexpr int FS_VE = 4;               // columns per lane
+constexpr int FS_COLS = 64 * FS_VE;    // columns per wave
 constexpr int FS_RC = 16;              // rank rows of B requested together
+constexpr int FS_TB = 16;              // shrink slices of t requested together
 
 struct SegFinishArgs {
-    const TileRec* tiles;
-    const int32_t* ids;
-    const int32_t* perm;
-    const float* part;    // [S][M][ldp]
+    const SegRowRec* recs;   // [M], by position in perm
+    const float* part;    // [S][M][ldp], ldp a multiple of 4
     int64_t ldp;
     int32_t S;
     const float* tpart;   // [St][M][rtp]
@@ -498,152 +525,149 @@ struct SegFinishArgs {
     int64_t ldy;
 };
 
-// Workgroup (segment tile, 512-column chunk).  The tile's record comes from
-// the shrink (scalar loads); its t (rows x rank, summed over the shrink
-// slices in order) is formed in LDS.  Wave w then produces rows w, w + 4, ...
-// of the tile, one 8-column piece per lane: the base partials of every K
-// slice (SB >= S requested together, indices past S clamped and masked, so
-// the loads carry no branch) added in slice order, plus s_u * t B_u with the
-// r rows of B_u's piece (the tile's rows share the adapter, so after the
-// first wave they come from L1), y rounded once.
-template <typename TY, int SB>
+// Wave (position p of perm, FS_COLS columns), lane l: columns c .. c + 3
+// (c = chunk * FS_COLS + 4 l) and, for the expand, rank column j = l of t.
+// The record at p (scalar loads) gives the row i, its adapter's B offset,
+// rank and scale; then i's base partials (all SB >= S slices; slices past S
+// are clamped and masked), t's first FS_TB shrink slices and B's r rows go
+// out together, with no branch between them.  Consecutive positions hold
+// the rows of one adapter, so a workgroup's waves and its neighbours (same
+// chunk, same XCD) read one B piece.  t_j is summed in slice order in lane
+// j and read by every lane with readlane.  VEC: d_out % 8 == 0 and 16-byte
+// B blocks (y and ldy are 16-byte aligned at the API), so every lane's four
+// columns are whole; otherwise each element is read on its own.
+template <typename TY, int SB, bool VEC>
 __global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a) {
-    __shared__ float sT[SS_ROWS][64];
-    __shared__ int sRow[SS_ROWS];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int tile = blockIdx.x / a.n_chunks;
-    const int ch = blockIdx.x - tile * a.n_chunks;
-    const TileRec* rp = a.tiles + tile;
-    if (!uload(&rp->valid, 0)) return;
-    const int row0 = uload(&rp->row0, 0);
-    const int cnt = uload(&rp->cnt, 0);
-    const int r = uload(&rp->rank, 0);
-    const float sc = uload(&rp->scale, 0);
-    const int64_t boff = uload(&rp->b_off, 0);
-    if (tid < SS_ROWS) sRow[tid] = a.perm[row0 + min(tid, cnt - 1)];
+    const int lane = threadIdx.x & 63;
+    const int rg = blockIdx.x / a.n_chunks;
+    const int ch = blockIdx.x - rg * a.n_chunks;
+    // the wave's position, made visibly uniform so that its record comes
+    // through scalar loads
+    const int p = __builtin_amdgcn_readfirstlane(rg * (FS_NT / 64) + (int)(threadIdx.x >> 6));
+    if (p >= a.M) return;   // whole waves
     const int N = P.d_out;
     const int col = ch * FS_COLS + lane * FS_VE;
-    const bool fast = col + FS_VE <= N && P.vec_b && ((a.ldy * (int64_t)sizeof(TY)) & 15) == 0;
-    const bf16* __restrict__ Bu = (const bf16*)P.B + boff + (col < N ? col : 0);
-    __syncthreads();
-    if (r > 0) {
-        // t[m][j] = sum over the shrink slices in order, four requested at once
-        const int64_t sl = (int64_t)a.M * a.rtp;
-        for (int v = tid; v < SS_ROWS * 64; v += FS_NT) {
-            const int m = v >> 6;
-            const int j = v & 63;
-            if (m >= cnt || j >= r) continue;
-            const float* __restrict__ tp = a.tpart + (int64_t)sRow[m] * a.rtp + j;
-            float t = 0.f;
-            for (int k0 = 0; k0 < a.St; k0 += 4) {
-                float q[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) q[e] = tp[(int64_t)min(k0 + e, a.St - 1) * sl];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t += (k0 + e < a.St) ? q[e] : 0.f;
-            }
-            sT[m][j] = t;
-        }
-    } else if (ch == 0 && tid < cnt) {
-        if (a.ids[sRow[tid]] != -1) flag_bad_id(P.err);   // invalid ids run as base-only rows
-    }
-    __syncthreads();
+    const int cc = col < N ? col : 0;   // lanes past d_out read column 0; nothing is stored
+    const SegRowRec* rp = a.recs + p;
+    const int i = uload(&rp->row, 0);
+    const int r = uload(&rp->rank, 0);
+    const int64_t boff = uload(&rp->b_off, 0);
+    const float sc = uload(&rp->scale, 0);
 
-    if (col >= N) return;
-    const int valid = min(FS_VE, N - col);
     const int64_t slice = (int64_t)a.M * a.ldp;
-    const float* __restrict__ part = a.part;
-    TY* __restrict__ Y = (TY*)a.y;
-    for (int m = wave; m < cnt; m += FS_NT / 64) {
-        const int row = sRow[m];
-        if (!fast) {
-            // ragged or unaligned piece: one element at a time
-            for (int e = 0; e < valid; ++e) {
-                float v = 0.f;
-                for (int k = 0; k < a.S; ++k) v += part[k * slice + (int64_t)row * a.ldp + col + e];
-                float ex = 0.f;
-                for (int j = 0; j < r; ++j) ex += sT[m][j] * to_f32(Bu[(int64_t)j * N + e]);
-                Y[(int64_t)row * a.ldy + col + e] = from_f32<TY>(v + sc * ex);
-            }
-            continue;
-        }
-        float4 pv[SB][2];
+    const float* __restrict__ prow = a.part + (int64_t)i * a.ldp + cc;
+    float pv[SB][FS_VE];
 #pragma unroll
-        for (int k = 0; k < SB; ++k) {
-            const float* q = part + (int64_t)min(k, a.S - 1) * slice + (int64_t)row * a.ldp + col;
-            pv[k][0] = *(const float4*)q;
-            pv[k][1] = *(const float4*)(q + 4);
-        }
-        float ex[FS_VE];
-#pragma unroll
-        for (int e = 0; e < FS_VE; ++e) ex[e] = 0.f;
-        for (int j0 = 0; j0 < r; j0 += FS_RC) {
-            uint4 bv[FS_RC];
-#pragma unroll
-            for (int q = 0; q < FS_RC; ++q)   // rows past r meet t = 0
-                bv[q] = *(const uint4*)(Bu + (int64_t)min(j0 + q, r - 1) * N);
-#pragma unroll
-            for (int q = 0; q < FS_RC; ++q) {
-                const float tj = (j0 + q < r) ? sT[m][j0 + q] : 0.f;
-                union { uint4 v; bf16 e[8]; } w;
-                w.v = bv[q];
-#pragma unroll
-                for (int e = 0; e < FS_VE; ++e) ex[e] += tj * to_f32(w.e[e]);
-            }
-        }
-        float v[FS_VE];
-#pragma unroll
-        for (int e = 0; e < FS_VE; ++e) v[e] = 0.f;
-#pragma unroll
-        for (int k = 0; k < SB; ++k) {
-            if (k >= a.S) break;
-            v[0] += pv[k][0].x; v[1] += pv[k][0].y; v[2] += pv[k][0].z; v[3] += pv[k][0].w;
-            v[4] += pv[k][1].x; v[5] += pv[k][1].y; v[6] += pv[k][1].z; v[7] += pv[k][1].w;
-        }
-#pragma unroll
-        for (int e = 0; e < FS_VE; ++e) v[e] += sc * ex[e];
-        TY* yr = Y + (int64_t)row * a.ldy + col;
-        if constexpr (sizeof(TY) == 2) {
-            union { uint4 q; bf16 e[8]; } o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o.e[e] = f32_to_bf16(v[e]);
-            *(uint4*)yr = o.q;
+    for (int k = 0; k < SB; ++k) {
+        const float* q = prow + (int64_t)min(k, a.S - 1) * slice;
+        if constexpr (VEC) {
+            const float4 f = *(const float4*)q;
+            pv[k][0] = f.x; pv[k][1] = f.y; pv[k][2] = f.z; pv[k][3] = f.w;
         } else {
-            *(float4*)yr = make_float4(v[0], v[1], v[2], v[3]);
-            *(float4*)(yr + 4) = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+            for (int e = 0; e < FS_VE; ++e) pv[k][e] = q[cc + e < N ? e : 0];
         }
+    }
+    const int64_t tsl = (int64_t)a.M * a.rtp;
+    const float* __restrict__ trow = a.tpart + (int64_t)i * a.rtp + min(lane, (int)a.rtp - 1);
+    float tq[FS_TB];
+#pragma unroll
+    for (int q = 0; q < FS_TB; ++q) tq[q] = trow[(int64_t)min(q, a.St - 1) * tsl];
+
+    // B rows j0 .. j0 + FS_RC - 1 of the lane's columns (rows past r read
+    // row r - 1 again; they meet t = 0); rows without a term skip B
+    const int rr = max(r, 1);
+    const bf16* __restrict__ Bu = (const bf16*)P.B + boff + cc;
+    uint2 bv[FS_RC];
+    auto load_b = [&](int j0) {
+#pragma unroll
+        for (int q = 0; q < FS_RC; ++q) {
+            const bf16* src = Bu + (int64_t)min(j0 + q, rr - 1) * N;
+            if constexpr (VEC) {
+                bv[q] = *(const uint2*)src;
+            } else {
+                union { uint2 u; bf16 e[4]; } w;
+#pragma unroll
+                for (int e = 0; e < FS_VE; ++e) w.e[e] = src[cc + e < N ? e : 0];
+                bv[q] = w.u;
+            }
+        }
+    };
+    if (r > 0) load_b(0);
+
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < FS_TB; ++q) t += (q < a.St) ? tq[q] : 0.f;
+    for (int k0 = FS_TB; k0 < a.St; k0 += FS_TB) {
+#pragma unroll
+        for (int q = 0; q < FS_TB; ++q) tq[q] = trow[(int64_t)min(k0 + q, a.St - 1) * tsl];
+#pragma unroll
+        for (int q = 0; q < FS_TB; ++q) t += (k0 + q < a.St) ? tq[q] : 0.f;
+    }
+
+    float v[FS_VE];
+#pragma unroll
+    for (int e = 0; e < FS_VE; ++e) v[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+        if (k < a.S)
+#pragma unroll
+            for (int e = 0; e < FS_VE; ++e) v[e] += pv[k][e];
+
+    float ex[FS_VE];
+#pragma unroll
+    for (int e = 0; e < FS_VE; ++e) ex[e] = 0.f;
+    for (int j0 = 0; r > 0;) {
+#pragma unroll
+        for (int q = 0; q < FS_RC; ++q) {
+            const int j = j0 + q;
+            const float tj = (j < r) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), j)) : 0.f;
+            union { uint2 u; bf16 e[4]; } w;
+            w.u = bv[q];
+#pragma unroll
+            for (int e = 0; e < FS_VE; ++e) ex[e] += tj * to_f32(w.e[e]);
+        }
+        j0 += FS_RC;
+        if (j0 >= r) break;
+        load_b(j0);
+    }
+    if (col >= N) return;
+    TY* yr = (TY*)a.y + (int64_t)i * a.ldy + col;
+    float o[FS_VE];
+#pragma unroll
+    for (int e = 0; e < FS_VE; ++e) o[e] = v[e] + sc * ex[e];
+    if constexpr (VEC) {
+        if constexpr (sizeof(TY) == 2) {
+            union { uint2 u; bf16 e[4]; } w;
+#pragma unroll
+            for (int e = 0; e < FS_VE; ++e) w.e[e] = f32_to_bf16(o[e]);
+            *(uint2*)yr = w.u;
+        } else {
+            *(float4*)yr = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    } else {
+        for (int e = 0; e < FS_VE && col + e < N; ++e) yr[e] = from_f32<TY>(o[e]);
     }
 }
 
-// Tile records without the segment-tile shrink (when the SGMV shrink forms
-// t): one wave per tile finds its segment and writes the record.
-__global__ __launch_bounds__(64) void k_tile_recs(PoolDev P, const int32_t* __restrict__ seg_ids,
-                                                  const int32_t* __restrict__ seg_off,
-                                                  const int32_t* __restrict__ n_seg, TileRec* __restrict__ tiles) {
-    const int lane = threadIdx.x;
-    int s = 0, c = 0;
-    const bool found = find_seg_tile(seg_off, *n_seg, SS_ROWS, blockIdx.x, lane, s, c);
-    if (lane != 0) return;
-    TileRec rec;
-    rec.pad = 0;
-    if (!found) {
-        rec.valid = 0;
-        rec.b_off = 0;
-        rec.row0 = rec.cnt = rec.rank = 0;
-        rec.scale = 0.f;
-    } else {
-        const int u = seg_ids[s];
-        const bool ok = id_ok(u, P.n_adapters);
-        rec.valid = 1;
-        rec.row0 = seg_off[s] + c * SS_ROWS;
-        rec.cnt = min(SS_ROWS, seg_off[s + 1] - rec.row0);
-        rec.b_off = ok ? P.b_off[u] : 0;
-        rec.rank = ok ? P.ranks[u] : 0;
-        rec.scale = ok ? P.scales[u] : 0.f;
-    }
-    tiles[blockIdx.x] = rec;
+// Row records without the segment-tile shrink (when the SGMV shrink forms
+// t): one thread per position of perm.
+__global__ __launch_bounds__(256) void k_row_recs(PoolDev P, const int32_t* __restrict__ ids,
+                                                  const int32_t* __restrict__ perm, int32_t n,
+                                                  SegRowRec* __restrict__ recs) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= n) return;
+    const int i = perm[p];
+    const int u = ids[i];
+    const bool ok = id_ok(u, P.n_adapters);
+    SegRowRec rec;
+    rec.b_off = ok ? P.b_off[u] : 0;
+    rec.row = i;
+    rec.rank = ok ? P.ranks[u] : 0;
+    rec.scale = ok ? P.scales[u] : 0.f;
+    rec.pad[0] = rec.pad[1] = rec.pad[2] = 0;
+    recs[p] = rec;
+    if (!ok && u != -1) flag_bad_id(P.err);   // invalid ids run as base-only rows
 }
 
 // segment tiles of SS_ROWS rows: at most one partial tile per segment on top
@@ -688,11 +712,11 @@ RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4) {
     if (!R.tile_shrink) R.St = 1;
     const size_t part = align_up((size_t)R.S * n_rows * R.ldp * 4, 256);
     const size_t tpart = align_up((size_t)R.St * n_rows * R.rtp * 4, 256);
-    const size_t tiles = align_up((size_t)rows_tiles(n_rows, P.n_adapters + 1) * sizeof(TileRec), 256);
+    const size_t recs = align_up((size_t)n_rows * sizeof(SegRowRec), 256);
     R.part_off = 0;
     R.tpart_off = part;
-    R.tiles_off = part + tpart;
-    R.bytes = part + tpart + tiles;
+    R.recs_off = part + tpart;
+    R.bytes = part + tpart + recs;
     return R;
 }
 
@@ -727,17 +751,18 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
                                const float* part, float* tpart, void* y, lora_dtype_t ydt, int64_t ldy,
                                hipStream_t stream, bool shrink, bool finish) {
     const int n_bins = P.n_adapters + 1;
-    // the tile records follow the t partials (RowsPlan::tiles_off)
-    TileRec* tiles = (TileRec*)((uint8_t*)tpart + (R.tiles_off - R.tpart_off));
+    // the row records follow the t partials (RowsPlan::recs_off)
+    SegRowRec* recs = (SegRowRec*)((uint8_t*)tpart + (R.recs_off - R.tpart_off));
     if (shrink && !R.tile_shrink) {
         // t comes from the SGMV shrink (tpart is t, one slice); only the records
-        hipLaunchKernelGGL(k_tile_recs, dim3((unsigned)rows_tiles(n_rows, n_bins)), dim3(64), 0, stream, P,
-                           seg->seg_ids, seg->seg_off, seg->n_seg, tiles);
+        hipLaunchKernelGGL(k_row_recs, dim3((unsigned)ceil_div(n_rows, 256)), dim3(256), 0, stream, P, ids,
+                           seg->perm, n_rows, recs);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else if (shrink) {
         SegShrinkArgs s;
-        s.tiles = tiles;
+        s.recs = recs;
+        s.ids = ids;
         s.x = (const bf16*)x;
         s.ldx = ldx;
         s.perm = seg->perm;
@@ -759,9 +784,7 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
     }
     if (finish) {
         SegFinishArgs f;
-        f.tiles = tiles;
-        f.ids = ids;
-        f.perm = seg->perm;
+        f.recs = recs;
         f.part = part;
         f.ldp = R.ldp;
         f.S = R.S;
@@ -772,8 +795,15 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
         f.n_chunks = (int32_t)ceil_div(P.d_out, FS_COLS);
         f.y = y;
         f.ldy = ldy;
-        dim3 grid((unsigned)(rows_tiles(n_rows, n_bins) * f.n_chunks));
-#define LORA_FIN(TY_, SB_) hipLaunchKernelGGL((k_seg_finish<TY_, SB_>), grid, dim3(FS_NT), 0, stream, P, f)
+        // chunk-minor: with a multiple of 8 chunks a chunk stays on one XCD,
+        // and neighbouring workgroups hold neighbouring positions of perm
+        dim3 grid((unsigned)(ceil_div(n_rows, FS_NT / 64) * f.n_chunks));
+        const bool vec = P.vec_b != 0;
+#define LORA_FIN(TY_, SB_)                                                                           \
+    do {                                                                                             \
+        if (vec) hipLaunchKernelGGL((k_seg_finish<TY_, SB_, true>), grid, dim3(FS_NT), 0, stream, P, f);  \
+        else hipLaunchKernelGGL((k_seg_finish<TY_, SB_, false>), grid, dim3(FS_NT), 0, stream, P, f);     \
+    } while (0)
         if (ydt == LORA_BF16) {
             if (R.S <= 1) LORA_FIN(bf16, 1);
             else if (R.S <= 2) LORA_FIN(bf16, 2);
