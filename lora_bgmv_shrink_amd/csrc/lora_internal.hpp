@@ -125,39 +125,44 @@ __device__ inline bool find_seg_tile(const int32_t* __restrict__ seg_off, int n_
 }
 
 // find_seg_tile for callers that know the descriptor's capacity (cap >=
-// n_seg): the first 256 run boundaries and run ids are requested together
-// with the run count (the entries past n_seg are read but never used), so a
-// batch of up to 256 runs finds its tile in one round of loads.  Also
-// returns the run's id and its first and one-past-last position in perm.
-__device__ inline bool find_seg_tile_cap(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_ids,
-                                         const int32_t* __restrict__ n_seg_p, int cap, int BM, int b, int lane,
-                                         int& s_out, int& c_out, int& lo_out, int& hi_out, int& id_out) {
-    constexpr int PRE = 4;   // chunks of 64 runs requested up front
-    int lo[PRE], hi[PRE], id[PRE];
-#pragma unroll
-    for (int q = 0; q < PRE; ++q) {
-        const int s = q * 64 + lane;
-        lo[q] = s < cap ? seg_off[s] : 0;
-        hi[q] = s < cap ? seg_off[s + 1] : 0;
-        id[q] = s < cap ? seg_ids[s] : -1;
+// n_seg) and search many times: seg_tile_cache_load copies the first
+// SEG_CACHE run boundaries and run ids to LDS (entries past n_seg are read
+// but never used) and returns the run count, once per workgroup (all its
+// threads, then a barrier); seg_tile_find then maps tile b to (run s, chunk
+// c) from LDS, loading from memory only past SEG_CACHE runs.  Also returns
+// the run's id and its first and one-past-last position in perm.  The find
+// is run by one whole wave.
+constexpr int SEG_CACHE = 256;
+struct SegTileCache {
+    int lo[SEG_CACHE], hi[SEG_CACHE], id[SEG_CACHE];
+};
+__device__ inline int seg_tile_cache_load(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_ids,
+                                          const int32_t* __restrict__ n_seg_p, int cap, int tid, int nthreads,
+                                          SegTileCache& C) {
+    for (int s = tid; s < SEG_CACHE; s += nthreads) {
+        C.lo[s] = s < cap ? seg_off[s] : 0;
+        C.hi[s] = s < cap ? seg_off[s + 1] : 0;
+        C.id[s] = s < cap ? seg_ids[s] : -1;
     }
-    const int n_seg = *n_seg_p;
+    return *n_seg_p;
+}
+__device__ inline bool seg_tile_find(const SegTileCache& C, int n_seg, const int32_t* __restrict__ seg_off,
+                                     const int32_t* __restrict__ seg_ids, int BM, int b, int lane, int& s_out,
+                                     int& c_out, int& lo_out, int& hi_out, int& id_out) {
     int base = 0;
     for (int s0 = 0; s0 < n_seg; s0 += 64) {
         const int s = s0 + lane;
         int l = 0, h = 0, u = -1;
-        if (s0 < PRE * 64) {
-#pragma unroll
-            for (int q = 0; q < PRE; ++q)
-                if (s0 == q * 64) {
-                    l = lo[q];
-                    h = hi[q];
-                    u = id[q];
-                }
-        } else if (s < n_seg) {
-            l = seg_off[s];
-            h = seg_off[s + 1];
-            u = seg_ids[s];
+        if (s < n_seg) {
+            if (s < SEG_CACHE) {
+                l = C.lo[s];
+                h = C.hi[s];
+                u = C.id[s];
+            } else {
+                l = seg_off[s];
+                h = seg_off[s + 1];
+                u = seg_ids[s];
+            }
         }
         const int cnt = s < n_seg ? (h - l + BM - 1) / BM : 0;
         const int incl = wave_incl_scan(cnt, lane);
@@ -303,14 +308,6 @@ struct RowRec {
     int64_t b_off;   // element offset of the row's B block
     int32_t rank;    // 0: no adapter term (base-only or invalid id)
     float scale;
-};
-// RowRec of the row at one position of perm (rows grouped by adapter)
-struct SegRowRec {
-    int64_t b_off;
-    int32_t row;     // the row, in the caller's order
-    int32_t rank;
-    float scale;
-    int32_t pad[3];
 };
 struct DecodeArgs {
     const void* x;

@@ -325,11 +325,13 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm(RowsGemmArgs a) {
 
 constexpr int SS_ROWS = 16;    // rows per segment tile (one MFMA block)
 constexpr int SS_NT = 256;
-constexpr int SS_MAX_LDS = 72 * 1024;   // x + transposed A staging
+constexpr int SS_MAX_LDS = 40 * 1024;   // transposed A staging (four workgroups per CU)
 constexpr int SS_LB = 8;       // 16-byte pieces of x and of A per thread per staging batch
+constexpr int SS_MU = 4;       // k-steps per wave whose LDS fragments are read together
+constexpr int SS_XS = 8;       // x fragments per lane: a slice of at most 32 k-steps over 4 waves
 
 struct SegShrinkArgs {
-    SegRowRec* recs;   // [M] by position in perm, the finish's records (slice 0 writes them)
+    RowRec* recs;      // [M], the finish's record of each row (slice 0 writes it)
     const int32_t* ids;
     const bf16* x;
     int64_t ldx;
@@ -343,29 +345,61 @@ struct SegShrinkArgs {
     int32_t M;
     int32_t ks_len;    // k per slice (multiple of 128)
     int32_t kp;        // LDS pitch (bf16) of a staged row: ks_len + 8
+    int32_t St;        // K slices
 };
 
-__global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ int sRow[SS_ROWS];
-    __shared__ int sInfo[4];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    if (wave == 0) {
-        int s = 0, c = 0, lo = 0, hi = 0, u = -1;
-        const bool found =
-            find_seg_tile_cap(a.seg_off, a.seg_ids, a.n_seg, a.cap, SS_ROWS, blockIdx.x, lane, s, c, lo, hi, u);
-        if (lane == 0) {
-            sInfo[0] = found ? 1 : 0;
-            sInfo[1] = u;
-            sInfo[2] = lo + c * SS_ROWS;
-            sInfo[3] = hi;
+// Stores one batch of A pieces (16 bytes: 8 ranks of one k-row) transposed,
+// sA[j][k]; pieces past the slice are 0.
+__device__ __forceinline__ void stage_a(const u32x4 (&av)[SS_LB], const bool (&aok)[SS_LB], int b0, int tid, int G,
+                                        int na, int KP, bf16* sA) {
+#pragma unroll
+    for (int q = 0; q < SS_LB; ++q) {
+        const int v = b0 + q * SS_NT + tid;
+        if (v < na) {
+            const int k = v / G;
+            const int j0 = (v - k * G) * 8;
+            union { u32x4 q4; bf16 e[8]; } w;
+            w.q4 = aok[q] ? av[q] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sA[(j0 + e) * KP + k] = w.e[e];
         }
     }
-    __syncthreads();
-    const int ks = blockIdx.y;
-    if (!sInfo[0]) return;   // past the last tile
+}
+
+// The shrink's matrix-core phase: wave w takes k-steps w, w + 4, ... of the
+// slice (nsteps a multiple of 4, at most 4 SS_XS); its x fragments are in
+// registers, and the A fragments of SS_MU steps are read from LDS before
+// their MFMAs, so a round costs one LDS round trip (one step at a time, the
+// eight steps of a 1024-deep slice took 1.6 us).  acc[jb] = x rows x ranks
+// 16 jb .. 16 jb + 15.
+template <int RB>
+__device__ __forceinline__ void shrink_mma(const u32x4 (&xf)[SS_XS], const bool (&xok)[SS_XS], const bf16* sA,
+                                           int KP, int nsteps, int wave, int lane, f32x4_t (&acc)[4]) {
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+#pragma unroll
+    for (int q0 = 0; q0 < SS_XS; q0 += SS_MU) {
+        if (wave + 4 * q0 >= nsteps) break;
+        bf16x8_t xa[SS_MU], bb[SS_MU][RB];
+#pragma unroll
+        for (int q = 0; q < SS_MU; ++q) {
+            const int st = wave + 4 * (q0 + q);
+            const int sr = st < nsteps ? st : wave;   // past the slice: read a valid step (x is 0 there)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb) bb[q][jb] = *(const bf16x8_t*)(sA + (jb * 16 + lr) * KP + sr * 32 + kq);
+            xa[q] = __builtin_bit_cast(bf16x8_t, xok[q0 + q] ? xf[q0 + q] : u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int q = 0; q < SS_MU; ++q)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb)
+                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q], bb[q][jb], acc[jb], 0, 0, 0);
+    }
+}
+
+// The shrink of one segment tile (from sInfo) over K slice ks.
+__device__ __forceinline__ void shrink_task(const PoolDev& P, const SegShrinkArgs& a, int ks, const int* sInfo,
+                                            int* sRow, uint8_t* smem, int tid, int lane, int wave) {
     // tile-uniform values, read from LDS by every lane: made visibly uniform
     // so that the pool tables come through scalar loads
     const int u = __builtin_amdgcn_readfirstlane(sInfo[1]);
@@ -374,18 +408,14 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
     const int cnt = min(SS_ROWS, __builtin_amdgcn_readfirstlane(sInfo[3]) - row0);
     const int r = ok ? uload(P.ranks, u) : 0;
     const int64_t aoff = ok ? uload(P.a_off, u) : 0;
-    if (tid < SS_ROWS) sRow[tid] = tid < cnt ? a.perm[row0 + tid] : -1;
-    __syncthreads();
     if (ks == 0 && tid < cnt) {
-        // the finish's record of the row at position row0 + tid of perm
-        const int row = sRow[tid];
-        SegRowRec rec;
+        // the finish's record of the row: B offset, rank (0: no term), scale
+        const int row = a.perm[row0 + tid];
+        RowRec rec;
         rec.b_off = ok ? P.b_off[u] : 0;
-        rec.row = row;
         rec.rank = r;
         rec.scale = ok ? P.scales[u] : 0.f;
-        rec.pad[0] = rec.pad[1] = rec.pad[2] = 0;
-        a.recs[row0 + tid] = rec;
+        a.recs[row] = rec;
         if (!ok && a.ids[row] != -1) flag_bad_id(P.err);   // invalid ids run as base-only rows
     }
     if (!ok) return;   // base-only rows (and invalid ids): no t
@@ -393,65 +423,63 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
     const int kbeg = ks * a.ks_len;
     const int klen = min(P.d_in, kbeg + a.ks_len) - kbeg;
     const int KP = a.kp;
-    bf16* sX = (bf16*)smem;                  // [16][KP]
-    bf16* sA = sX + SS_ROWS * KP;            // [RB * 16][KP], A_u transposed
+    bf16* sA = (bf16*)smem;   // [RB * 16][KP], A_u's slice transposed
     const bf16* Au = (const bf16*)P.A + aoff + (int64_t)kbeg * r;
-
-    // Stage the tile's x rows ([16][slice]) and A_u transposed ([rank][slice])
-    // in LDS.  Each thread requests SS_LB 16-byte pieces of each before it
-    // stores any, so a batch costs one memory round trip (one slice of rank
-    // 16 is a single batch); k past the slice, rows past the tile and ranks
-    // past r are 0.
-    const int pieces = a.ks_len / 8;
-    const int nx = SS_ROWS * pieces;
     const bool va = P.vec_a && r % 8 == 0;
     const int G = va ? r / 8 : 1;
     const int na = va ? a.ks_len * G : 0;
-    const int nmax = max(nx, na);
-    // the loads carry no branch (an out-of-range piece reads a valid address
-    // and is masked), so the compiler keeps them all in flight; a piece cut
-    // by the end of the slice (d_in not a multiple of 8) is filled afterwards
-    for (int b0 = 0; b0 < nmax; b0 += SS_NT * SS_LB) {
-        u32x4 xv[SS_LB];
-        u32x4 av[SS_LB];
-        bool xok[SS_LB], aok[SS_LB];
+
+    // Requests in dependency order, none waiting on a later one: the tile
+    // row of this lane's x fragments (perm), the first SS_LB 16-byte A
+    // pieces per thread (all of a rank-16 slice), then, once perm is in, the
+    // x fragments of this wave's k-steps.  The loads carry no branch (out-of-
+    // range pieces read a valid address and are masked), so all stay in
+    // flight.  x is not staged: lane l of wave w holds row l % 16 of the tile
+    // at k-group (l / 16) * 8 of steps w, w + 4, ... in registers, which is
+    // the matrix cores' operand layout, and LDS holds A alone (four
+    // workgroups per CU).
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int xrow = lr < cnt ? a.perm[row0 + lr] : -1;
+    u32x4 av[SS_LB];
+    bool aok[SS_LB];
+#pragma unroll
+    for (int q = 0; q < SS_LB; ++q) {
+        const int v = q * SS_NT + tid;
+        const int ka = v / G;
+        aok[q] = v < na && ka < klen;
+        av[q] = *(const u32x4*)(aok[q] ? Au + (int64_t)ka * r + (v - ka * G) * 8 : Au);
+    }
+    const int nsteps = a.ks_len / 32;
+    u32x4 xf[SS_XS];
+    bool xok[SS_XS];
+#pragma unroll
+    for (int q = 0; q < SS_XS; ++q) {
+        const int k = (wave + 4 * q) * 32 + kq;
+        xok[q] = xrow >= 0 && k + 8 <= klen;   // also false past the slice's steps
+        xf[q] = *(const u32x4*)(xok[q] ? a.x + (int64_t)xrow * a.ldx + kbeg + k : a.x);
+    }
+    if (klen % 8) {   // the piece cut by the end of the slice (d_in not a multiple of 8)
+        const int k = klen / 8 * 8;
+#pragma unroll
+        for (int q = 0; q < SS_XS; ++q)
+            if (xrow >= 0 && (wave + 4 * q) * 32 + kq == k) {
+                xf[q] = __builtin_bit_cast(u32x4, ld8_guard(a.x + (int64_t)xrow * a.ldx + kbeg + k, klen - k));
+                xok[q] = true;
+            }
+    }
+    stage_a(av, aok, 0, tid, G, na, KP, sA);
+    for (int b0 = SS_NT * SS_LB; b0 < na; b0 += SS_NT * SS_LB) {   // ranks above 16
 #pragma unroll
         for (int q = 0; q < SS_LB; ++q) {
             const int v = b0 + q * SS_NT + tid;
-            const int m = min(v / pieces, SS_ROWS - 1);
-            const int k = (v - m * pieces) * 8;
-            const int row = sRow[m];
-            xok[q] = v < nx && row >= 0 && k + 8 <= klen;
-            xv[q] = *(const u32x4*)(xok[q] ? a.x + (int64_t)row * a.ldx + kbeg + k : a.x);
             const int ka = v / G;
             aok[q] = v < na && ka < klen;
             av[q] = *(const u32x4*)(aok[q] ? Au + (int64_t)ka * r + (v - ka * G) * 8 : Au);
         }
-#pragma unroll
-        for (int q = 0; q < SS_LB; ++q) {
-            const int v = b0 + q * SS_NT + tid;
-            if (v < nx) {
-                const int m = v / pieces;
-                *(u32x4*)(sX + m * KP + (v - m * pieces) * 8) = xok[q] ? xv[q] : u32x4{0u, 0u, 0u, 0u};
-            }
-            if (v < na) {
-                const int k = v / G;
-                const int j0 = (v - k * G) * 8;
-                union { u32x4 q4; bf16 e[8]; } w;
-                w.q4 = aok[q] ? av[q] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sA[(j0 + e) * KP + k] = w.e[e];
-            }
-        }
+        stage_a(av, aok, b0, tid, G, na, KP, sA);
     }
-    if (klen % 8) {   // the piece cut by the end of the slice, per row
-        const int k = klen / 8 * 8;
-        for (int m = tid; m < SS_ROWS; m += SS_NT) {
-            const int row = sRow[m];
-            if (row >= 0) *(bf16x8_t*)(sX + m * KP + k) = ld8_guard(a.x + (int64_t)row * a.ldx + kbeg + k, klen - k);
-        }
-    }
-    if (va) {
+    if (va) {   // ranks r .. 16 RB - 1 are 0
         for (int v = tid; v < (RB * 16 - r) * a.ks_len; v += SS_NT) {
             const int j = r + v / a.ks_len;
             sA[j * KP + v % a.ks_len] = 0;
@@ -463,23 +491,17 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
             sA[j * KP + k] = (j < r && k < klen) ? Au[(int64_t)k * r + j] : (bf16)0;
         }
     }
+    if (tid < SS_ROWS) sRow[tid] = tid < cnt ? a.perm[row0 + tid] : -1;
     __syncthreads();
 
-    // wave w takes k-steps w, w + 4, ...; acc[jb] = x rows x ranks 16 jb ..
-    const int lr = lane & 15;
-    const int kq = (lane >> 4) * 8;
     f32x4_t acc[4];
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int nsteps = a.ks_len / 32;
-    for (int st = wave; st < nsteps; st += 4) {
-        const bf16x8_t xa = *(const bf16x8_t*)(sX + lr * KP + st * 32 + kq);
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            if (jb < RB) {
-                const bf16x8_t bb = *(const bf16x8_t*)(sA + (jb * 16 + lr) * KP + st * 32 + kq);
-                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bb, acc[jb], 0, 0, 0);
-            }
+    switch (RB) {
+        case 1: shrink_mma<1>(xf, xok, sA, KP, nsteps, wave, lane, acc); break;
+        case 2: shrink_mma<2>(xf, xok, sA, KP, nsteps, wave, lane, acc); break;
+        case 3: shrink_mma<3>(xf, xok, sA, KP, nsteps, wave, lane, acc); break;
+        default: shrink_mma<4>(xf, xok, sA, KP, nsteps, wave, lane, acc); break;
     }
     __syncthreads();   // staging no longer read: reuse it for the wave sums
     float* red = (float*)smem;   // [4][16][64]
@@ -488,7 +510,7 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
         if (jb < RB)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                red[(wave * SS_ROWS + (lane >> 4) * 4 + q) * 64 + jb * 16 + lr] = acc[jb][q];
+                red[(wave * SS_ROWS + (lane >> 4) * 4 + q) * 64 + jb * 16 + (lane & 15)] = acc[jb][q];
     __syncthreads();
     for (int v = tid; v < SS_ROWS * 64; v += SS_NT) {
         const int m = v >> 6;
@@ -499,6 +521,37 @@ __global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a
         for (int w = 0; w < 4; ++w) t += red[(w * SS_ROWS + m) * 64 + j];
         a.tpart[((int64_t)ks * a.M + sRow[m]) * a.rtp + j] = t;
     }
+}
+
+
+// Workgroup b: tile b / St, K slice b % St (tile-major, so that every real
+// tile is dispatched before the empty ones: the grid is sized without the
+// run count, and in slice-major order the empty tiles held LDS slots that
+// real ones waited for).
+__global__ __launch_bounds__(SS_NT) void k_seg_shrink(PoolDev P, SegShrinkArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int sRow[SS_ROWS];
+    __shared__ int sInfo[4];
+    __shared__ SegTileCache C;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n_seg = seg_tile_cache_load(a.seg_off, a.seg_ids, a.n_seg, a.cap, tid, SS_NT, C);
+    __syncthreads();
+    if (wave == 0) {
+        int s = 0, c = 0, lo = 0, hi = 0, u = -1;
+        const bool found = seg_tile_find(C, n_seg, a.seg_off, a.seg_ids, SS_ROWS, blockIdx.x / a.St, lane, s, c, lo,
+                                         hi, u);
+        if (lane == 0) {
+            sInfo[0] = found ? 1 : 0;
+            sInfo[1] = u;
+            sInfo[2] = lo + c * SS_ROWS;
+            sInfo[3] = hi;
+        }
+    }
+    __syncthreads();
+    if (!sInfo[0]) return;   // past the last tile
+    shrink_task(P, a, blockIdx.x % a.St, sInfo, sRow, smem, tid, lane, wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -512,7 +565,7 @@ constexpr int FS_RC = 16;              // rank rows of B requested together
 constexpr int FS_TB = 16;              // shrink slices of t requested together
 
 struct SegFinishArgs {
-    const SegRowRec* recs;   // [M], by position in perm
+    const RowRec* recs;   // [M]
     const float* part;    // [S][M][ldp], ldp a multiple of 4
     int64_t ldp;
     int32_t S;
@@ -525,14 +578,14 @@ struct SegFinishArgs {
     int64_t ldy;
 };
 
-// Wave (position p of perm, FS_COLS columns), lane l: columns c .. c + 3
-// (c = chunk * FS_COLS + 4 l) and, for the expand, rank column j = l of t.
-// The record at p (scalar loads) gives the row i, its adapter's B offset,
-// rank and scale; then i's base partials (all SB >= S slices; slices past S
-// are clamped and masked), t's first FS_TB shrink slices and B's r rows go
-// out together, with no branch between them.  Consecutive positions hold
-// the rows of one adapter, so a workgroup's waves and its neighbours (same
-// chunk, same XCD) read one B piece.  t_j is summed in slice order in lane
+// Wave (row i, FS_COLS columns), lane l: columns c .. c + 3 (c = chunk *
+// FS_COLS + 4 l) and, for the expand, rank column j = l of t.  Everything but
+// B is addressed by the row alone, so the row's record (scalar loads), its
+// base partials (all SB >= S slices; slices past S are clamped and masked),
+// and t's first FS_TB shrink slices go out together, with no branch between
+// them; B's r rows follow the record.  Rows run in the caller's order (rows
+// in adapter order, so that neighbouring waves share B, measured 10-20%
+// slower on the 14336-column projections).  t_j is summed in slice order in lane
 // j and read by every lane with readlane.  VEC: d_out % 8 == 0 and 16-byte
 // B blocks (y and ldy are 16-byte aligned at the API), so every lane's four
 // columns are whole; otherwise each element is read on its own.
@@ -541,15 +594,14 @@ __global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a
     const int lane = threadIdx.x & 63;
     const int rg = blockIdx.x / a.n_chunks;
     const int ch = blockIdx.x - rg * a.n_chunks;
-    // the wave's position, made visibly uniform so that its record comes
-    // through scalar loads
-    const int p = __builtin_amdgcn_readfirstlane(rg * (FS_NT / 64) + (int)(threadIdx.x >> 6));
-    if (p >= a.M) return;   // whole waves
+    // the wave's row, made visibly uniform so that its record comes through
+    // scalar loads
+    const int i = __builtin_amdgcn_readfirstlane(rg * (FS_NT / 64) + (int)(threadIdx.x >> 6));
+    if (i >= a.M) return;   // whole waves
     const int N = P.d_out;
     const int col = ch * FS_COLS + lane * FS_VE;
     const int cc = col < N ? col : 0;   // lanes past d_out read column 0; nothing is stored
-    const SegRowRec* rp = a.recs + p;
-    const int i = uload(&rp->row, 0);
+    const RowRec* rp = a.recs + i;
     const int r = uload(&rp->rank, 0);
     const int64_t boff = uload(&rp->b_off, 0);
     const float sc = uload(&rp->scale, 0);
@@ -651,22 +703,18 @@ __global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a
 }
 
 // Row records without the segment-tile shrink (when the SGMV shrink forms
-// t): one thread per position of perm.
-__global__ __launch_bounds__(256) void k_row_recs(PoolDev P, const int32_t* __restrict__ ids,
-                                                  const int32_t* __restrict__ perm, int32_t n,
-                                                  SegRowRec* __restrict__ recs) {
-    const int p = blockIdx.x * 256 + threadIdx.x;
-    if (p >= n) return;
-    const int i = perm[p];
+// t): one thread per row.
+__global__ __launch_bounds__(256) void k_row_recs(PoolDev P, const int32_t* __restrict__ ids, int32_t n,
+                                                  RowRec* __restrict__ recs) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
     const int u = ids[i];
     const bool ok = id_ok(u, P.n_adapters);
-    SegRowRec rec;
+    RowRec rec;
     rec.b_off = ok ? P.b_off[u] : 0;
-    rec.row = i;
     rec.rank = ok ? P.ranks[u] : 0;
     rec.scale = ok ? P.scales[u] : 0.f;
-    rec.pad[0] = rec.pad[1] = rec.pad[2] = 0;
-    recs[p] = rec;
+    recs[i] = rec;
     if (!ok && u != -1) flag_bad_id(P.err);   // invalid ids run as base-only rows
 }
 
@@ -697,12 +745,12 @@ RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4) {
     R.kslice = (int32_t)(ceil_div(kblocks, S) * RG_KB);
     R.S = (int32_t)ceil_div(K, R.kslice);
     R.ldp = (int64_t)align_up((size_t)N, 4);
-    // shrink: K slices sized so that x and the transposed A fit the LDS budget
+    // shrink: K slices sized so that the transposed A fits the LDS budget
     const int rb = (int)ceil_div(P.r_max, 16) * 16;
-    // (long K: 512-deep slices, twice the workgroups; 14336-deep down
-    // projection 47 -> 35 us)
-    int ks_len = K >= 8192 ? 512 : 1024;
-    while (ks_len > 128 && (SS_ROWS + rb) * (ks_len + 8) * 2 > SS_MAX_LDS) ks_len /= 2;
+    // (1024-deep slices also for long K: the launch rate of workgroups,
+    // about 190 per us, bounds a grid of thousands)
+    int ks_len = 1024;
+    while (ks_len > 128 && rb * (ks_len + 8) * 2 > SS_MAX_LDS) ks_len /= 2;
     R.ks_len = ks_len;
     R.St = (int32_t)ceil_div(K, ks_len);
     R.rtp = (int64_t)align_up((size_t)P.r_max, 4);
@@ -712,7 +760,7 @@ RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4) {
     if (!R.tile_shrink) R.St = 1;
     const size_t part = align_up((size_t)R.S * n_rows * R.ldp * 4, 256);
     const size_t tpart = align_up((size_t)R.St * n_rows * R.rtp * 4, 256);
-    const size_t recs = align_up((size_t)n_rows * sizeof(SegRowRec), 256);
+    const size_t recs = align_up((size_t)n_rows * sizeof(RowRec), 256);
     R.part_off = 0;
     R.tpart_off = part;
     R.recs_off = part + tpart;
@@ -752,11 +800,11 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
                                hipStream_t stream, bool shrink, bool finish) {
     const int n_bins = P.n_adapters + 1;
     // the row records follow the t partials (RowsPlan::recs_off)
-    SegRowRec* recs = (SegRowRec*)((uint8_t*)tpart + (R.recs_off - R.tpart_off));
+    RowRec* recs = (RowRec*)((uint8_t*)tpart + (R.recs_off - R.tpart_off));
     if (shrink && !R.tile_shrink) {
         // t comes from the SGMV shrink (tpart is t, one slice); only the records
-        hipLaunchKernelGGL(k_row_recs, dim3((unsigned)ceil_div(n_rows, 256)), dim3(256), 0, stream, P, ids,
-                           seg->perm, n_rows, recs);
+        hipLaunchKernelGGL(k_row_recs, dim3((unsigned)ceil_div(n_rows, 256)), dim3(256), 0, stream, P, ids, n_rows,
+                           recs);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else if (shrink) {
@@ -776,8 +824,9 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
         s.ks_len = R.ks_len;
         s.kp = R.ks_len + 8;
         const int rb = (int)ceil_div(P.r_max, 16) * 16;
-        const size_t lds = std::max<size_t>((size_t)(SS_ROWS + rb) * s.kp * 2, 4 * SS_ROWS * 64 * 4);
-        dim3 grid((unsigned)rows_tiles(n_rows, n_bins), (unsigned)R.St);
+        const size_t lds = std::max<size_t>((size_t)rb * s.kp * 2, 4 * SS_ROWS * 64 * 4);
+        s.St = R.St;
+        dim3 grid((unsigned)(rows_tiles(n_rows, n_bins) * R.St));
         hipLaunchKernelGGL(k_seg_shrink, grid, dim3(SS_NT), lds, stream, P, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -795,8 +844,7 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
         f.n_chunks = (int32_t)ceil_div(P.d_out, FS_COLS);
         f.y = y;
         f.ldy = ldy;
-        // chunk-minor: with a multiple of 8 chunks a chunk stays on one XCD,
-        // and neighbouring workgroups hold neighbouring positions of perm
+        // chunk-minor: with a multiple of 8 chunks a chunk stays on one XCD
         dim3 grid((unsigned)(ceil_div(n_rows, FS_NT / 64) * f.n_chunks));
         const bool vec = P.vec_b != 0;
 #define LORA_FIN(TY_, SB_)                                                                           \
