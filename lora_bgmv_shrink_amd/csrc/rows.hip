@@ -319,6 +319,176 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm(RowsGemmArgs a) {
         }
 }
 
+// bf16 W: the same tile, with x staged through LDS as well.  A wave's
+// MFMA operand holds 16 rows x 8 k per load, so x fragments loaded straight
+// from memory touch 16 rows (half a 128-byte line each) per instruction; on
+// L2-resident data that pattern measured 2.8x slower than whole-line loads,
+// and x is most of what a few-hundred-row tile reads (it is re-read once per
+// column tile).  Here x and W blocks (XB = 64 k) are loaded in whole lines
+// (a wave's load: 8 rows or columns x 128 bytes) into a RING_X-deep register
+// ring, stored to double-buffered LDS (pitch XB + 8: the fragment reads of 16
+// rows hit distinct banks), and the MFMAs read both from LDS.
+constexpr int XB = 64;
+constexpr int XLDK = XB + 8;
+constexpr int RING_X = 4;
+
+template <int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
+    constexpr int BM = 32 * NW;
+    constexpr int NT = NW * 64;
+    constexpr int NB = BN / 16;
+    constexpr int PPR = XB / 8;                 // 16-byte pieces per row of a block
+    constexpr int XPT = BM * PPR / NT;          // x pieces per thread per block
+    constexpr int WPT = BN * PPR / NT;          // W pieces per thread per block
+    static_assert(XPT * NT == BM * PPR && WPT * NT == BN * PPR, "blocks do not split evenly");
+    __shared__ __attribute__((aligned(16))) bf16 sX[2][BM * XLDK];
+    __shared__ __attribute__((aligned(16))) bf16 sW[2][BN * XLDK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int G = a.tiles_m * a.tiles_n * a.S;
+    const int L = xcd_tile(blockIdx.x, G);
+    const int tm = L % a.tiles_m;
+    const int rest = L / a.tiles_m;
+    const int tn = rest % a.tiles_n;
+    const int ks = rest / a.tiles_n;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int kbeg = ks * a.kslice;
+    const int klen = min(a.K, kbeg + a.kslice) - kbeg;
+
+    // piece v = tid + NT p: row (column) v / PPR, k-piece v % PPR; rows past
+    // M and columns past N read the last one (never stored)
+    const bf16* xp[XPT];
+    const bf16* wp[WPT];
+#pragma unroll
+    for (int p = 0; p < XPT; ++p) {
+        const int v = tid + NT * p;
+        xp[p] = a.x + (int64_t)min(m0 + v / PPR, a.M - 1) * a.ldx + kbeg + (v % PPR) * 8;
+    }
+#pragma unroll
+    for (int p = 0; p < WPT; ++p) {
+        const int v = tid + NT * p;
+        wp[p] = (const bf16*)a.W + (int64_t)min(n0 + v / PPR, a.N - 1) * a.ldw + kbeg + (v % PPR) * 8;
+    }
+
+    // the register ring, as separate named arrays so that every index is static
+    u32x4 x0[XPT], x1[XPT], x2[XPT], x3[XPT];
+    u32x4 w0[WPT], w1[WPT], w2[WPT], w3[WPT];
+    f32x4_t acc[2][NB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto load = [&](u32x4 (&dx)[XPT], u32x4 (&dw)[WPT], int kb) __attribute__((always_inline)) {
+        const int k0 = kb * XB;
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) dx[p] = *(const u32x4*)(xp[p] + k0);
+#pragma unroll
+        for (int p = 0; p < WPT; ++p) dw[p] = *(const u32x4*)(wp[p] + k0);
+    };
+    auto store = [&](const u32x4 (&dx)[XPT], const u32x4 (&dw)[WPT], int stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            const int v = tid + NT * p;
+            *(u32x4*)(sX[stage] + (v / PPR) * XLDK + (v % PPR) * 8) = dx[p];
+        }
+#pragma unroll
+        for (int p = 0; p < WPT; ++p) {
+            const int v = tid + NT * p;
+            *(u32x4*)(sW[stage] + (v / PPR) * XLDK + (v % PPR) * 8) = dw[p];
+        }
+    };
+    auto mma = [&](int stage) __attribute__((always_inline)) {
+        const bf16* sx = sX[stage] + (wave * 32 + lr) * XLDK + kq;
+        const bf16* sw = sW[stage] + lr * XLDK + kq;
+#pragma unroll
+        for (int st = 0; st < XB / 32; ++st) {
+            bf16x8_t xa[2], b[NB];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xa[i] = *(const bf16x8_t*)(sx + i * 16 * XLDK + st * 32);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) b[j] = *(const bf16x8_t*)(sw + j * 16 * XLDK + st * 32);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // One block: registers -> LDS stage kb & 1 (last read by block kb - 2,
+    // whose MFMAs every wave finished before the barrier of block kb - 1),
+    // then block kb + RING_X is requested into the freed registers, then the
+    // MFMAs.  Requests past the last whole block fetch that block again (from
+    // cache, never used), so the loop has no branch around its loads.
+#define RX_STEP(X_, W_, KB_)                             \
+    {                                                    \
+        const int kb_ = (KB_);                           \
+        store(X_, W_, kb_ & 1);                          \
+        __syncthreads();                                 \
+        load(X_, W_, min(kb_ + RING_X, last));           \
+        mma(kb_ & 1);                                    \
+    }
+    const int nfull = klen / XB;
+    if (nfull > 0) {
+        const int last = nfull - 1;
+        load(x0, w0, 0);
+        load(x1, w1, min(1, last));
+        load(x2, w2, min(2, last));
+        load(x3, w3, min(3, last));
+        int kb = 0;
+        for (; kb + RING_X <= nfull; kb += RING_X) {
+            RX_STEP(x0, w0, kb);
+            RX_STEP(x1, w1, kb + 1);
+            RX_STEP(x2, w2, kb + 2);
+            RX_STEP(x3, w3, kb + 3);
+        }
+        if (kb < nfull) RX_STEP(x0, w0, kb);
+        if (kb + 1 < nfull) RX_STEP(x1, w1, kb + 1);
+        if (kb + 2 < nfull) RX_STEP(x2, w2, kb + 2);
+    }
+#undef RX_STEP
+    if (klen > nfull * XB) {
+        // ragged last block: element-wise loads, zero past the slice
+        const int k0 = nfull * XB;
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            const int v = tid + NT * p;
+            const int valid = min(8, max(0, klen - k0 - (v % PPR) * 8));
+            x0[p] = __builtin_bit_cast(u32x4, ld8_guard(xp[p] + k0, valid));
+        }
+#pragma unroll
+        for (int p = 0; p < WPT; ++p) {
+            const int v = tid + NT * p;
+            const int valid = min(8, max(0, klen - k0 - (v % PPR) * 8));
+            w0[p] = __builtin_bit_cast(u32x4, ld8_guard(wp[p] + k0, valid));
+        }
+        store(x0, w0, nfull & 1);
+        __syncthreads();
+        mma(nfull & 1);
+    }
+
+    // partial sums: lane l holds rows (l / 16) * 4 + q of column l % 16 of
+    // each 16 x 16 block
+    float* out = a.part + (int64_t)ks * a.M * a.ldp;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int n = n0 + j * 16 + lr;
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = m0 + wave * 32 + i * 16 + (lane >> 4) * 4 + q;
+                if (m < a.M) out[(int64_t)m * a.ldp + n] = acc[i][j][q];
+            }
+        }
+}
+
 // ---------------------------------------------------------------------------
 // Shrink over segment tiles
 // ---------------------------------------------------------------------------
@@ -789,8 +959,8 @@ hipError_t launch_rows_gemm(const PoolDev& P, const RowsPlan& R, const void* x, 
     a.kslice = R.kslice;
     dim3 grid((unsigned)(R.tiles_m * R.tiles_n * R.S));
     if (q4) hipLaunchKernelGGL((k_rows_gemm<true, 4, 64, 4>), grid, dim3(256), 0, stream, a);
-    else if (R.wide) hipLaunchKernelGGL((k_rows_gemm<false, 8, 128, 3>), grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL((k_rows_gemm<false, 4, 64, 4>), grid, dim3(256), 0, stream, a);
+    else if (R.wide) hipLaunchKernelGGL((k_rows_gemm_x<8, 128>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((k_rows_gemm_x<4, 64>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
