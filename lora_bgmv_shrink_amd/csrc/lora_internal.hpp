@@ -264,7 +264,7 @@ hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt
 // product in split-K partial sums over 128 x 64 tiles, and the adapter term
 // over the segments of lora_segments_build (rows.hip).
 struct RowsPlan {
-    int32_t wide;               // 256 x 128 tiles (else 128 x 64)
+    int32_t shape;              // tile: 0 128 x 64, 1 256 x 128
     int32_t tile_shrink;        // shrink per segment tile (else the SGMV shrink writes t)
     int32_t tiles_m, tiles_n;
     int32_t S, kslice;          // K slices of the base product

@@ -384,6 +384,7 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    const int nfull = klen / XB;
     auto load = [&](u32x4 (&dx)[XPT], u32x4 (&dw)[WPT], int kb) __attribute__((always_inline)) {
         const int k0 = kb * XB;
 #pragma unroll
@@ -433,7 +434,6 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
         load(X_, W_, min(kb_ + RING_X, last));           \
         mma(kb_ & 1);                                    \
     }
-    const int nfull = klen / XB;
     if (nfull > 0) {
         const int last = nfull - 1;
         load(x0, w0, 0);
@@ -901,11 +901,12 @@ RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4) {
     const int K = P.d_in, N = P.d_out;
     // long or wide projections: 256 x 128 tiles (x re-read once per 128
     // columns, W once per 256 rows; split K covers the CUs); the others
-    // 128 x 64 tiles, for more workgroups.  Measured on the skewed 256-row
-    // 8B batch: gate 4096x14336 87 -> 55 us, down 14336x4096 75 -> 54 us; q
-    // 4096x4096 is no faster wide (its fp32 partials grow with the split).
-    R.wide = (!q4 && (N >= 8192 || K >= 8192)) ? 1 : 0;   // 4-bit W: 128 x 64 tiles
-    const int bm = R.wide ? 256 : 128, bn = R.wide ? 128 : 64;
+    // 128 x 64 tiles, for more workgroups.  On the skewed 256-row 8B batch
+    // the 4096 x 4096 projections were slower with 256 x 128 or 256 x 64
+    // tiles (their fp32 partials grow with the split) and with eight waves
+    // and a deeper register ring on 128 x 64.
+    R.shape = (!q4 && (N >= 8192 || K >= 8192)) ? 1 : 0;   // 4-bit W: 128 x 64 tiles
+    const int bm = R.shape ? 256 : 128, bn = R.shape ? 128 : 64;
     R.tiles_m = (int32_t)ceil_div(n_rows, bm);
     R.tiles_n = (int32_t)ceil_div(N, bn);
     // split K (into at most 8 slices) until the launch covers the CUs
@@ -959,7 +960,7 @@ hipError_t launch_rows_gemm(const PoolDev& P, const RowsPlan& R, const void* x, 
     a.kslice = R.kslice;
     dim3 grid((unsigned)(R.tiles_m * R.tiles_n * R.S));
     if (q4) hipLaunchKernelGGL((k_rows_gemm<true, 4, 64, 4>), grid, dim3(256), 0, stream, a);
-    else if (R.wide) hipLaunchKernelGGL((k_rows_gemm_x<8, 128>), grid, dim3(512), 0, stream, a);
+    else if (R.shape == 1) hipLaunchKernelGGL((k_rows_gemm_x<8, 128>), grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL((k_rows_gemm_x<4, 64>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
