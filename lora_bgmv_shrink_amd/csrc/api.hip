@@ -341,6 +341,7 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
     p->dev.vec_a = vec_a ? 1 : 0;
     p->dev.vec_b = vec_b ? 1 : 0;
     p->dev.stream_ok = stream_ok ? 1 : 0;
+    p->dev.uniform = layout == LORA_LAYOUT_UNIFORM ? 1 : 0;
     *out = p;
     return LORA_OK;
 }

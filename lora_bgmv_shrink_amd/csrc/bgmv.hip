@@ -18,6 +18,7 @@ constexpr int SHRINK_THREADS = 512;     // one workgroup (8 waves) per row
 constexpr int SHRINK_LOADS = 16;        // 16-byte loads of A in flight per thread
 constexpr int SHRINK_X_FLOATS = 8192;   // x chunk staged in LDS (32 KiB)
 constexpr int SHRINK_A_ELEMS = 8192;    // generic path: A chunk staged in LDS
+constexpr int SHRINK_XV = 4;            // 16-byte x pieces per thread requested together
 
 // One row of the K-extension operand from the row's t (in LDS), after a
 // workgroup barrier.
@@ -28,6 +29,35 @@ __device__ __forceinline__ void write_t_ext(bf16* out, float* sv, int r, float s
 __device__ __forceinline__ void write_t_ext(float* out, float* sv, int r, float s, int cols) {
     __syncthreads();
     for (int c = threadIdx.x; c < cols; c += blockDim.x) out[c] = ext_value_f32(sv, r, s, c);
+}
+
+// x[0:kn] -> xs as fp32 (row start 16-byte aligned): 16-byte pieces, each
+// thread's SHRINK_XV pieces requested before any is stored (a loop of
+// element loads and stores waited for one round trip per iteration), then
+// the elements past the last whole piece.
+template <typename T>
+__device__ __forceinline__ void stage_x(const T* __restrict__ x, int kn, float* xs, int tid) {
+    constexpr int VE = 16 / sizeof(T);
+    const int npc = kn / VE;
+    for (int p0 = tid; p0 < npc; p0 += SHRINK_THREADS * SHRINK_XV) {
+        uint4 v[SHRINK_XV];
+#pragma unroll
+        for (int q = 0; q < SHRINK_XV; ++q) {
+            const int p = p0 + q * SHRINK_THREADS;
+            v[q] = *(const uint4*)(x + (int64_t)(p < npc ? p : 0) * VE);
+        }
+#pragma unroll
+        for (int q = 0; q < SHRINK_XV; ++q) {
+            const int p = p0 + q * SHRINK_THREADS;
+            if (p < npc) {
+                union { uint4 u; T e[VE]; } w;
+                w.u = v[q];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) xs[p * VE + e] = to_f32(w.e[e]);
+            }
+        }
+    }
+    for (int k = npc * VE + tid; k < kn; k += SHRINK_THREADS) xs[k] = to_f32(x[k]);
 }
 
 // Streaming shrink, for ranks where 16-byte vectors tile every k-row
@@ -64,14 +94,14 @@ __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_stream(PoolDev P
         if (tid < r_max) ti[tid] = 0.f;
         return;
     }
-    const int r = P.ranks[a];
+    const int r = pool_rank(P, a);
     const int G = r / VE;
     const int KPT = SHRINK_THREADS / G;
     const int KC = KPT * SHRINK_LOADS;   // k-rows per chunk (<= SHRINK_X_FLOATS)
     const int jv = tid % G;
     const int ksub = tid / G;
     const int d_in = P.d_in;
-    const T* Au = (const T*)P.A + P.a_off[a] + jv * VE;
+    const T* Au = (const T*)P.A + pool_a_off(P, a) + jv * VE;
     const T* xi = x + (int64_t)i * ldx;
 
     float acc[VE];
@@ -87,7 +117,7 @@ __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_stream(PoolDev P
             av[l] = *(const uint4*)(Au + (int64_t)(k < d_in ? k : 0) * r);
         }
         const int kn = min(KC, d_in - kc0);
-        for (int k = tid; k < kn; k += SHRINK_THREADS) xs[k] = to_f32(xi[kc0 + k]);
+        stage_x(xi + kc0, kn, xs, tid);
         __syncthreads();
 #pragma unroll
         for (int l = 0; l < SHRINK_LOADS; ++l) {
@@ -160,11 +190,24 @@ __global__ __launch_bounds__(SHRINK_THREADS) void k_bgmv_shrink_lds(PoolDev P, c
         int done = 0;
         if (P.vec_a) {   // block start 16-byte aligned and k0 * r * elem a multiple of 16
             const int nv = F / VE;
-            for (int v = tid; v < nv; v += SHRINK_THREADS) *(uint4*)(as + v * VE) = *(const uint4*)(src + v * VE);
+            // SHRINK_XV pieces per thread requested before any is stored
+            for (int v0 = tid; v0 < nv; v0 += SHRINK_THREADS * SHRINK_XV) {
+                uint4 w[SHRINK_XV];
+#pragma unroll
+                for (int q = 0; q < SHRINK_XV; ++q) {
+                    const int v = v0 + q * SHRINK_THREADS;
+                    w[q] = *(const uint4*)(src + (int64_t)(v < nv ? v : 0) * VE);
+                }
+#pragma unroll
+                for (int q = 0; q < SHRINK_XV; ++q) {
+                    const int v = v0 + q * SHRINK_THREADS;
+                    if (v < nv) *(uint4*)(as + v * VE) = w[q];
+                }
+            }
             done = nv * VE;
         }
         for (int e = done + tid; e < F; e += SHRINK_THREADS) as[e] = src[e];
-        for (int k = tid; k < nk; k += SHRINK_THREADS) xs[k] = to_f32(xi[k0 + k]);
+        stage_x(xi + k0, nk, xs, tid);
         __syncthreads();
         if (g < Gs)
             for (int k = g; k < nk; k += Gs) acc += xs[k] * to_f32(as[k * r + j]);

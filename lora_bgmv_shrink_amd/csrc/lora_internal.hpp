@@ -36,7 +36,15 @@ struct PoolDev {
     int32_t vec_a;       // every A block starts 16-byte aligned
     int32_t vec_b;       // every B block 16-byte aligned and d_out*elem % 16 == 0
     int32_t stream_ok;   // every rank r: r*elem % 16 == 0 and (512*16/elem) % r == 0
+    // the uniform layout: every rank is r_max and adapter u's blocks start at
+    // u * d_in * r_max (A) and u * r_max * d_out (B), so kernels whose path
+    // waits on them form the rank and A offset without a table load
+    int32_t uniform = 0;
 };
+__device__ __forceinline__ int pool_rank(const PoolDev& P, int u) { return P.uniform ? P.r_max : P.ranks[u]; }
+__device__ __forceinline__ int64_t pool_a_off(const PoolDev& P, int u) {
+    return P.uniform ? (int64_t)u * P.d_in * P.r_max : P.a_off[u];
+}
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 h) { return __uint_as_float((uint32_t)h << 16); }

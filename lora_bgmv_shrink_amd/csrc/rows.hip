@@ -576,8 +576,8 @@ __device__ __forceinline__ void shrink_task(const PoolDev& P, const SegShrinkArg
     const bool ok = id_ok(u, P.n_adapters);
     const int row0 = __builtin_amdgcn_readfirstlane(sInfo[2]);
     const int cnt = min(SS_ROWS, __builtin_amdgcn_readfirstlane(sInfo[3]) - row0);
-    const int r = ok ? uload(P.ranks, u) : 0;
-    const int64_t aoff = ok ? uload(P.a_off, u) : 0;
+    const int r = ok ? (P.uniform ? P.r_max : uload(P.ranks, u)) : 0;
+    const int64_t aoff = ok ? (P.uniform ? (int64_t)u * P.d_in * P.r_max : uload(P.a_off, u)) : 0;
     if (ks == 0 && tid < cnt) {
         // the finish's record of the row: B offset, rank (0: no term), scale
         const int row = a.perm[row0 + tid];
