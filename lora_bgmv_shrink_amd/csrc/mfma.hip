@@ -1463,16 +1463,34 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
         const float sc = P.scales[u];
         // A: row m, K column 64 e + h * 32 + jj holds the hi (h = 0) or lo
         // (h = 1) part of s * t[m][32 e + jj] (0 past the rank and past cnt)
-        for (int idx = tid; idx < EXP_ROWS * (K / 2); idx += EXP_THREADS) {
+        // (every load of a thread requested before any is stored: at most
+        // EXP_ROWS * 64 / EXP_THREADS = 16 per thread)
+        constexpr int TPT = EXP_ROWS * (EXP_KMAX / 2) / EXP_THREADS;
+        const int nA = EXP_ROWS * (K / 2);
+        float tv[TPT];
+#pragma unroll
+        for (int q = 0; q < TPT; ++q) {
+            const int idx = tid + q * EXP_THREADS;
             const int m = idx / (K / 2);
             const int j = idx - m * (K / 2);
-            const float v = (m < cnt && j < rk) ? sc * t[(int64_t)sRow[m] * ldt + j] : 0.f;
-            const bf16 hi = f32_to_bf16(v);
-            const bf16 lo = f32_to_bf16(v - to_f32(hi));
-            const int e = j >> 5;
-            const int jj = j & 31;
-            sA[m * EXP_KLD + e * 64 + jj] = hi;
-            sA[m * EXP_KLD + e * 64 + 32 + jj] = lo;
+            const bool in = idx < nA && m < cnt && j < rk;
+            tv[q] = t[in ? (int64_t)sRow[m] * ldt + j : 0];
+            tv[q] = in ? tv[q] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < TPT; ++q) {
+            const int idx = tid + q * EXP_THREADS;
+            if (idx < nA) {
+                const int m = idx / (K / 2);
+                const int j = idx - m * (K / 2);
+                const float v = sc * tv[q];
+                const bf16 hi = f32_to_bf16(v);
+                const bf16 lo = f32_to_bf16(v - to_f32(hi));
+                const int e = j >> 5;
+                const int jj = j & 31;
+                sA[m * EXP_KLD + e * 64 + jj] = hi;
+                sA[m * EXP_KLD + e * 64 + 32 + jj] = lo;
+            }
         }
     }
     const int lr = lane & 15;
@@ -1486,13 +1504,30 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
             // B^T: column n, K column 64 e + h * 32 + jj holds B_u[32 e + jj][n]
             // (both h).  Consecutive lanes take consecutive ranks of one
             // 8-column group, so their LDS writes are consecutive halves.
-            for (int idx = tid; idx < (K / 2) * (EXP_COLS / 8); idx += EXP_THREADS) {
+            // (whole 16-byte pieces: every load of a thread requested, without
+            // a branch, before any is stored; ragged or unaligned pieces after)
+            constexpr int BPT = (EXP_KMAX / 2) * (EXP_COLS / 8) / EXP_THREADS;
+            const int nB = (K / 2) * (EXP_COLS / 8);
+            uint4 bv[BPT];
+            bool bw[BPT];
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                const int j = idx % (K / 2);
+                const int nc = n0 + (idx / (K / 2)) * 8;
+                bw[q] = idx < nB && j < rk && vb && nc + 8 <= N;
+                bv[q] = *(const uint4*)(bw[q] ? Bu + (int64_t)j * N + nc : Bu);
+            }
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                if (idx >= nB) continue;
                 const int j = idx % (K / 2);
                 const int c8 = (idx / (K / 2)) * 8;
                 const int nc = n0 + c8;
                 union { uint4 u4; bf16 e[8]; } v;
-                if (j < rk && vb && nc + 8 <= N) {
-                    v.u4 = *(const uint4*)(Bu + (int64_t)j * N + nc);
+                if (bw[q]) {
+                    v.u4 = bv[q];
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -1535,47 +1570,57 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
                     sC[(i * 16 + lq + q) * EXP_CLD + wave * 32 + j * 16 + lr] = acc[i][j][q];
         __syncthreads();
         // 16 threads per row, 8 columns each: a wave moves 4 rows of 128
-        // contiguous columns per pass; 16 rows per pass of the workgroup
+        // contiguous columns per pass; 16 rows per pass of the workgroup.
+        // Whole 16-byte pieces of y (the usual case) are requested, for all
+        // passes, before any is used (one round trip, not one per pass);
+        // ragged or unaligned pieces go element by element.
+        constexpr int NPASS = EXP_ROWS / 16;
+        constexpr int YV = 8 * (int)sizeof(TY) / 16;   // 16-byte pieces per 8 columns
+        const int cl = (tid & 15) * 8;
+        const int nc = n0 + cl;
+        uint4 yv[NPASS][YV];
+        bool whole[NPASS];
 #pragma unroll
-        for (int pass = 0; pass < EXP_ROWS / 16; ++pass) {
+        for (int pass = 0; pass < NPASS; ++pass) whole[pass] = pass * 16 + (tid >> 4) < cnt && vec_y && nc + 8 <= N;
+        if (accumulate && vec_y && N >= 8) {
+            // no branch around the loads: a lane without a whole piece reads
+            // one that is in bounds (the tile's first row, the last whole
+            // piece of columns) and ignores it
+            const int c = min(nc, N - 8);
+#pragma unroll
+            for (int pass = 0; pass < NPASS; ++pass) {
+                const int m = pass * 16 + (tid >> 4);
+                const TY* src = y + (int64_t)sRow[m < cnt ? m : 0] * ldy + c;
+#pragma unroll
+                for (int h = 0; h < YV; ++h) yv[pass][h] = *(const uint4*)(src + h * (16 / sizeof(TY)));
+            }
+        }
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
             const int m = pass * 16 + (tid >> 4);
-            if (m < cnt) {
-                TY* yr = y + (int64_t)sRow[m] * ldy;
-                const float* cr = sC + m * EXP_CLD;
-                const int cl = (tid & 15) * 8;
-                const int nc = n0 + cl;
-                if (nc < N) {
-                    float v[8];
+            if (m >= cnt || nc >= N) continue;
+            TY* yr = y + (int64_t)sRow[m] * ldy;
+            const float* cr = sC + m * EXP_CLD;
+            float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = cr[cl + e];
-                    if (vec_y && nc + 8 <= N) {
-                        if constexpr (sizeof(TY) == 2) {
-                            union { uint4 u4; bf16 e[8]; } o;
-                            if (accumulate) {
-                                o.u4 = *(const uint4*)(yr + nc);
+            for (int e = 0; e < 8; ++e) v[e] = cr[cl + e];
+            if (whole[pass]) {
+                union { uint4 u4[YV]; TY e[8]; } o;
+                if (accumulate) {
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) v[e] += to_f32(o.e[e]);
-                            }
+                    for (int h = 0; h < YV; ++h) o.u4[h] = yv[pass][h];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) o.e[e] = f32_to_bf16(v[e]);
-                            *(uint4*)(yr + nc) = o.u4;
-                        } else {
-                            if (accumulate) {
-                                const float4 p0 = *(const float4*)(yr + nc);
-                                const float4 p1 = *(const float4*)(yr + nc + 4);
-                                v[0] += p0.x; v[1] += p0.y; v[2] += p0.z; v[3] += p0.w;
-                                v[4] += p1.x; v[5] += p1.y; v[6] += p1.z; v[7] += p1.w;
-                            }
-                            *(float4*)(yr + nc) = float4{v[0], v[1], v[2], v[3]};
-                            *(float4*)(yr + nc + 4) = float4{v[4], v[5], v[6], v[7]};
-                        }
-                    } else {
-                        for (int e = 0; e < 8 && nc + e < N; ++e) {
-                            float w = v[e];
-                            if (accumulate) w += to_f32(yr[nc + e]);
-                            yr[nc + e] = from_f32<TY>(w);
-                        }
-                    }
+                    for (int e = 0; e < 8; ++e) v[e] += to_f32(o.e[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o.e[e] = from_f32<TY>(v[e]);
+#pragma unroll
+                for (int h = 0; h < YV; ++h) *(uint4*)(yr + nc + h * (16 / sizeof(TY))) = o.u4[h];
+            } else {
+                for (int e = 0; e < 8 && nc + e < N; ++e) {
+                    float w = v[e];
+                    if (accumulate) w += to_f32(yr[nc + e]);
+                    yr[nc + e] = from_f32<TY>(w);
                 }
             }
         }
