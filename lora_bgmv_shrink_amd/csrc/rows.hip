@@ -9,13 +9,12 @@
 // for the bytes it moves per MFMA, and the launch is cut into enough
 // independent tiles (row tiles, column tiles, K slices) to cover every CU:
 //
-//   k_rows_gemm   tile = 128 rows x 64 columns x one K slice, 4 waves; wave w
-//                 owns rows 32w .. 32w + 31 and all 64 columns.  Its x
-//                 fragments come straight from memory (x is small and stays
-//                 in L2); the W block (64 columns x 128 k) is shared by the
-//                 four waves, so it goes through LDS, and the next four W
-//                 blocks are always in flight in registers (W comes from HBM
-//                 and is read once per row tile).  Writes fp32 partial sums
+//   k_rows_gemm_x tile = 128 rows x 64 columns (4 waves) or 256 x 128 (8
+//                 waves) x one K slice; wave w owns rows 32w .. 32w + 31 and
+//                 all the tile's columns.  x and W blocks are loaded in whole
+//                 lines, four blocks ahead in registers, and go through LDS
+//                 to the matrix cores; W comes from HBM and is read once per
+//                 row tile, x stays in L2.  Writes fp32 partial sums
 //                 part[slice][row][col].
 //                 A 4-bit W (signed nibbles, one fp32 scale per output and
 //                 128 inputs) is widened exactly to bf16 on its way into LDS;
@@ -50,9 +49,8 @@
 namespace lora {
 namespace {
 
-constexpr int RG_KB = 128;            // k per block (one 4-bit scale group)
+constexpr int RG_KB = 128;            // K slices are whole 128-deep groups (the 4-bit scale group)
 constexpr int kRowsTileShrinkMax = 1024;   // rows the segment-tile shrink serves
-constexpr int RG_LDK = RG_KB + 8;     // bf16 pitch of a staged W column
 
 struct RowsGemmArgs {
     const bf16* x;
@@ -97,252 +95,35 @@ __device__ __forceinline__ u32x4 widen8_q4(uint32_t w) {
     return u.v;
 }
 
-// NW waves, each owning 32 rows and all BN columns of the tile (BM = 32 NW
-// rows); RING W and x blocks in flight per thread.
-template <bool Q4, int NW, int BN, int RING>
-__global__ __launch_bounds__(NW * 64) void k_rows_gemm(RowsGemmArgs a) {
-    constexpr int RG_BM = 32 * NW;
-    constexpr int RG_BN = BN;
-    constexpr int RG_NT = NW * 64;
-    constexpr int NB = BN / 16;                                   // 16-column MFMA blocks
-    constexpr int RG_WPT_B = RG_BN * RG_KB * 2 / 16 / RG_NT;      // 16-byte W pieces per thread (bf16)
-    constexpr int CPP = RG_NT / 16;                               // columns per pass of the W loader
-    static_assert(RG_WPT_B * RG_NT * 16 == RG_BN * RG_KB * 2, "W block does not split evenly");
-    static_assert(!Q4 || RG_BN * 4 == RG_NT, "4-bit loader: one 16-byte piece per thread");
-    __shared__ __attribute__((aligned(16))) bf16 sW[2][RG_BN * RG_LDK];
-    __shared__ float sSc[2][RG_BN];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int lr = lane & 15;
-    const int kq = (lane >> 4) * 8;
-    const int G = a.tiles_m * a.tiles_n * a.S;
-    const int L = xcd_tile(blockIdx.x, G);
-    const int tm = L % a.tiles_m;
-    const int rest = L / a.tiles_m;
-    const int tn = rest % a.tiles_n;
-    const int ks = rest / a.tiles_n;
-    const int m0 = tm * RG_BM;
-    const int n0 = tn * RG_BN;
-    const int kbeg = ks * a.kslice;
-    const int klen = min(a.K, kbeg + a.kslice) - kbeg;
-
-    // x rows of this wave (rows past M read row M-1; never stored)
-    const bf16* xr[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = m0 + wave * 32 + i * 16 + lr;
-        xr[i] = a.x + (int64_t)min(m, a.M - 1) * a.ldx + kbeg + kq;
-    }
-    // W pieces of this thread.  bf16: piece v = tid + 256 p covers column
-    // v / 16 and k-piece v % 16 (8 k) of the block; 4-bit: column tid / 4 and
-    // k 32 (tid % 4) .. + 32 (16 bytes).
-    constexpr int WPT = Q4 ? 1 : RG_WPT_B;
-    const bf16* wb[WPT];
-    const uint8_t* wq = nullptr;
-    const float* wsp = nullptr;
-    if constexpr (Q4) {
-        const int c = tid >> 2;
-        const int n = min(n0 + c, a.N - 1);
-        wq = (const uint8_t*)a.W + (int64_t)n * a.ldw + kbeg / 2 + (tid & 3) * 16;
-        wsp = a.wscale + (int64_t)n * a.lds + kbeg / RG_KB;
-    } else {
-#pragma unroll
-        for (int p = 0; p < WPT; ++p) {
-            const int c = (tid >> 4) + CPP * p;
-            const int n = min(n0 + c, a.N - 1);
-            wb[p] = (const bf16*)a.W + (int64_t)n * a.ldw + kbeg + (tid & 15) * 8;
-        }
-    }
-
-    // the register ring: four W blocks and two x blocks, as separate named
-    // arrays so that every index is static
-    u32x4 w0[WPT], w1[WPT], w2[WPT], w3[WPT];
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    bf16x8_t x0[2][4], x1[2][4], x2[2][4], x3[2][4];
-    f32x4_t acc[2][NB];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // whole blocks: plain 16-byte loads, no branch (the main loop stays
-    // branch-free so that each wait covers only the loads it needs)
-    auto load_w = [&](u32x4 (&dst)[WPT], float& sc, int kb) __attribute__((always_inline)) {
-        const int k0 = kb * RG_KB;
-        if constexpr (Q4) {
-            dst[0] = *(const u32x4*)(wq + k0 / 2);
-            sc = wsp[kb];
-        } else {
-#pragma unroll
-            for (int p = 0; p < WPT; ++p) dst[p] = *(const u32x4*)(wb[p] + k0);
-        }
-    };
-    auto load_x = [&](bf16x8_t (&dst)[2][4], int kb) __attribute__((always_inline)) {
-        const int k0 = kb * RG_KB;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) dst[i][s] = *(const bf16x8_t*)(xr[i] + k0 + s * 32);
-    };
-    auto store_w = [&](const u32x4 (&src)[WPT], float sc, int stage) __attribute__((always_inline)) {
-        bf16* s = sW[stage];
-        if constexpr (Q4) {
-            const int c = tid >> 2;
-            const int k = (tid & 3) * 32;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) *(u32x4*)(s + c * RG_LDK + k + h * 8) = widen8_q4(src[0][h]);
-            if ((tid & 3) == 0) sSc[stage][c] = sc;
-        } else {
-#pragma unroll
-            for (int p = 0; p < WPT; ++p) {
-                const int c = (tid >> 4) + CPP * p;
-                *(u32x4*)(s + c * RG_LDK + (tid & 15) * 8) = src[p];
-            }
-        }
-    };
-    auto mma = [&](const bf16x8_t (&xa)[2][4], int stage) __attribute__((always_inline)) {
-        const bf16* s = sW[stage];
-        f32x4_t g[2][NB];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) g[i][j] = Q4 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            bf16x8_t b[NB];
-#pragma unroll
-            for (int j = 0; j < NB; ++j) b[j] = *(const bf16x8_t*)(s + (j * 16 + lr) * RG_LDK + st * 32 + kq);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    g[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i][st], b[j], g[i][j], 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            if constexpr (Q4) {
-                const float sc = sSc[stage][j * 16 + lr];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) acc[i][j] += sc * g[i][j];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) acc[i][j] = g[i][j];
-            }
-        }
-    };
-    // One block: its W goes from registers to LDS stage kb & 1 (last read by
-    // block kb - 2, whose MFMAs every wave finished before the barrier of
-    // block kb - 1), then the MFMAs, then block kb + RING (W and x) is
-    // requested into the registers this block used.  Loads complete in
-    // order, so x is requested as far ahead as W: a wait for x never waits
-    // on a W block that is still young.  Requests past the last whole block
-    // fetch that block again (from cache, never used), so the loop has no
-    // branch around its loads.
-#define RG_STEP(W_, S_, X_, KB_)                               \
-    {                                                          \
-        const int kb_ = (KB_);                                 \
-        store_w(W_, S_, kb_ & 1);                              \
-        __syncthreads();                                       \
-        load_w(W_, S_, min(kb_ + RING, last));                 \
-        mma(X_, kb_ & 1);                                      \
-        load_x(X_, min(kb_ + RING, last));                     \
-    }
-
-    static_assert(RING == 3 || RING == 4, "register ring of 3 or 4 blocks");
-    const int nfull = klen / RG_KB;   // whole blocks (a 4-bit W has no partial block)
-    if (nfull > 0) {
-        const int last = nfull - 1;
-        load_w(w0, s0, 0);
-        load_x(x0, 0);
-        load_w(w1, s1, min(1, last));
-        load_x(x1, min(1, last));
-        load_w(w2, s2, min(2, last));
-        load_x(x2, min(2, last));
-        if constexpr (RING == 4) {
-            load_w(w3, s3, min(3, last));
-            load_x(x3, min(3, last));
-        }
-        int kb = 0;
-        for (; kb + RING <= nfull; kb += RING) {
-            RG_STEP(w0, s0, x0, kb);
-            RG_STEP(w1, s1, x1, kb + 1);
-            RG_STEP(w2, s2, x2, kb + 2);
-            if constexpr (RING == 4) RG_STEP(w3, s3, x3, kb + 3);
-        }
-        if (kb < nfull) RG_STEP(w0, s0, x0, kb);
-        if (kb + 1 < nfull) RG_STEP(w1, s1, x1, kb + 1);
-        if constexpr (RING == 4)
-            if (kb + 2 < nfull) RG_STEP(w2, s2, x2, kb + 2);
-    }
-#undef RG_STEP
-    if constexpr (!Q4) {
-        if (klen > nfull * RG_KB) {
-            // ragged last block: element-wise loads, zero past the slice
-            const int k0 = nfull * RG_KB;
-            u32x4 tw[WPT];
-#pragma unroll
-            for (int p = 0; p < WPT; ++p) {
-                const int valid = min(8, max(0, klen - k0 - (tid & 15) * 8));
-                tw[p] = __builtin_bit_cast(u32x4, ld8_guard(wb[p] + k0, valid));
-            }
-            bf16x8_t tx[2][4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int valid = min(8, max(0, klen - (k0 + s * 32 + kq)));
-                    tx[i][s] = ld8_guard(xr[i] + k0 + s * 32, valid);
-                }
-            float dummy = 0.f;
-            store_w(tw, dummy, nfull & 1);
-            __syncthreads();
-            mma(tx, nfull & 1);
-        }
-    }
-
-    // partial sums: lane l holds rows (l / 16) * 4 + q of column l % 16 of
-    // each 16 x 16 block
-    float* out = a.part + (int64_t)ks * a.M * a.ldp;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int n = n0 + j * 16 + lr;
-            if (n >= a.N) continue;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = m0 + wave * 32 + i * 16 + (lane >> 4) * 4 + q;
-                if (m < a.M) out[(int64_t)m * a.ldp + n] = acc[i][j][q];
-            }
-        }
-}
-
-// bf16 W: the same tile, with x staged through LDS as well.  A wave's
-// MFMA operand holds 16 rows x 8 k per load, so x fragments loaded straight
-// from memory touch 16 rows (half a 128-byte line each) per instruction; on
-// L2-resident data that pattern measured 2.8x slower than whole-line loads,
-// and x is most of what a few-hundred-row tile reads (it is re-read once per
-// column tile).  Here x and W blocks (XB = 64 k) are loaded in whole lines
-// (a wave's load: 8 rows or columns x 128 bytes) into a RING_X-deep register
-// ring, stored to double-buffered LDS (pitch XB + 8: the fragment reads of 16
-// rows hit distinct banks), and the MFMAs read both from LDS.
-constexpr int XB = 64;
-constexpr int XLDK = XB + 8;
+// The same tile with x staged through LDS as well.  A wave's MFMA operand
+// holds 16 rows x 8 k per load, so x fragments loaded straight from memory
+// touch 16 rows (half a 128-byte line each) per instruction; on L2-resident
+// data that pattern measured 2.8x slower than whole-line loads, and x is
+// most of what a few-hundred-row tile reads (it is re-read once per column
+// tile).  Here x and W blocks (KB k) are loaded in whole lines (a wave's
+// load: rows or columns x 128 bytes) into a RING_X-deep register ring,
+// stored to double-buffered LDS (pitch KB + 8: the fragment reads of 16 rows
+// hit distinct banks), and the MFMAs read both from LDS.  Q4: a block is one
+// 128-input scale group; its 4-bit W (16 bytes = 32 inputs of one column a
+// piece) is widened exactly to bf16 on its way into LDS, and the block's
+// sums are scaled once per column and added.
 constexpr int RING_X = 4;
 
-template <int NW, int BN>
+template <bool Q4, int NW, int BN, int KB>
 __global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
     constexpr int BM = 32 * NW;
     constexpr int NT = NW * 64;
     constexpr int NB = BN / 16;
-    constexpr int PPR = XB / 8;                 // 16-byte pieces per row of a block
-    constexpr int XPT = BM * PPR / NT;          // x pieces per thread per block
-    constexpr int WPT = BN * PPR / NT;          // W pieces per thread per block
-    static_assert(XPT * NT == BM * PPR && WPT * NT == BN * PPR, "blocks do not split evenly");
-    __shared__ __attribute__((aligned(16))) bf16 sX[2][BM * XLDK];
-    __shared__ __attribute__((aligned(16))) bf16 sW[2][BN * XLDK];
+    constexpr int LDK = KB + 8;
+    constexpr int PPR = KB / 8;                              // 16-byte bf16 pieces per row of a block
+    constexpr int XPT = BM * PPR / NT;                       // x pieces per thread per block
+    constexpr int WPR = Q4 ? KB / 32 : PPR;                  // 16-byte W pieces per column of a block
+    constexpr int WPT = BN * WPR / NT;                       // W pieces per thread per block
+    static_assert(XPT * NT == BM * PPR && WPT * NT == BN * WPR && WPT >= 1, "blocks do not split evenly");
+    static_assert(!Q4 || (KB == 128 && WPT == 1), "4-bit blocks: one scale group, one piece per thread");
+    __shared__ __attribute__((aligned(16))) bf16 sX[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) bf16 sW[2][BN * LDK];
+    __shared__ float sSc[2][Q4 ? BN : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -360,10 +141,12 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
     const int kbeg = ks * a.kslice;
     const int klen = min(a.K, kbeg + a.kslice) - kbeg;
 
-    // piece v = tid + NT p: row (column) v / PPR, k-piece v % PPR; rows past
-    // M and columns past N read the last one (never stored)
+    // piece v = tid + NT p: row (column) v / PPR (v / WPR), piece v % PPR
+    // (v % WPR); rows past M and columns past N read the last one (never
+    // stored)
     const bf16* xp[XPT];
-    const bf16* wp[WPT];
+    const uint8_t* wp[WPT];
+    const float* scp = nullptr;
 #pragma unroll
     for (int p = 0; p < XPT; ++p) {
         const int v = tid + NT * p;
@@ -372,53 +155,81 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
 #pragma unroll
     for (int p = 0; p < WPT; ++p) {
         const int v = tid + NT * p;
-        wp[p] = (const bf16*)a.W + (int64_t)min(n0 + v / PPR, a.N - 1) * a.ldw + kbeg + (v % PPR) * 8;
+        const int n = min(n0 + v / WPR, a.N - 1);
+        if constexpr (Q4) wp[p] = (const uint8_t*)a.W + (int64_t)n * a.ldw + kbeg / 2 + (v % WPR) * 16;
+        else wp[p] = (const uint8_t*)((const bf16*)a.W + (int64_t)n * a.ldw + kbeg + (v % WPR) * 8);
     }
+    if constexpr (Q4) scp = a.wscale + (int64_t)min(n0 + tid / WPR, a.N - 1) * a.lds + kbeg / KB;
 
+    const int nfull = klen / KB;
     // the register ring, as separate named arrays so that every index is static
     u32x4 x0[XPT], x1[XPT], x2[XPT], x3[XPT];
     u32x4 w0[WPT], w1[WPT], w2[WPT], w3[WPT];
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
     f32x4_t acc[2][NB];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nfull = klen / XB;
-    auto load = [&](u32x4 (&dx)[XPT], u32x4 (&dw)[WPT], int kb) __attribute__((always_inline)) {
-        const int k0 = kb * XB;
+    auto load = [&](u32x4 (&dx)[XPT], u32x4 (&dw)[WPT], float& sc, int kb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int p = 0; p < XPT; ++p) dx[p] = *(const u32x4*)(xp[p] + k0);
+        for (int p = 0; p < XPT; ++p) dx[p] = *(const u32x4*)(xp[p] + kb * KB);
 #pragma unroll
-        for (int p = 0; p < WPT; ++p) dw[p] = *(const u32x4*)(wp[p] + k0);
+        for (int p = 0; p < WPT; ++p) dw[p] = *(const u32x4*)(wp[p] + (Q4 ? kb * KB / 2 : kb * KB * 2));
+        if constexpr (Q4) sc = scp[kb];
     };
-    auto store = [&](const u32x4 (&dx)[XPT], const u32x4 (&dw)[WPT], int stage) __attribute__((always_inline)) {
+    auto store = [&](const u32x4 (&dx)[XPT], const u32x4 (&dw)[WPT], float sc, int stage)
+                     __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
             const int v = tid + NT * p;
-            *(u32x4*)(sX[stage] + (v / PPR) * XLDK + (v % PPR) * 8) = dx[p];
+            *(u32x4*)(sX[stage] + (v / PPR) * LDK + (v % PPR) * 8) = dx[p];
         }
 #pragma unroll
         for (int p = 0; p < WPT; ++p) {
             const int v = tid + NT * p;
-            *(u32x4*)(sW[stage] + (v / PPR) * XLDK + (v % PPR) * 8) = dw[p];
+            if constexpr (Q4) {
+                bf16* d = sW[stage] + (v / WPR) * LDK + (v % WPR) * 32;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) *(u32x4*)(d + h * 8) = widen8_q4(dw[p][h]);
+                if (v % WPR == 0) sSc[stage][v / WPR] = sc;
+            } else {
+                *(u32x4*)(sW[stage] + (v / WPR) * LDK + (v % WPR) * 8) = dw[p];
+            }
         }
     };
     auto mma = [&](int stage) __attribute__((always_inline)) {
-        const bf16* sx = sX[stage] + (wave * 32 + lr) * XLDK + kq;
-        const bf16* sw = sW[stage] + lr * XLDK + kq;
+        const bf16* sx = sX[stage] + (wave * 32 + lr) * LDK + kq;
+        const bf16* sw = sW[stage] + lr * LDK + kq;
+        f32x4_t g[2][NB];
 #pragma unroll
-        for (int st = 0; st < XB / 32; ++st) {
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) g[i][j] = Q4 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j];
+#pragma unroll
+        for (int st = 0; st < KB / 32; ++st) {
             bf16x8_t xa[2], b[NB];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) xa[i] = *(const bf16x8_t*)(sx + i * 16 * XLDK + st * 32);
+            for (int i = 0; i < 2; ++i) xa[i] = *(const bf16x8_t*)(sx + i * 16 * LDK + st * 32);
 #pragma unroll
-            for (int j = 0; j < NB; ++j) b[j] = *(const bf16x8_t*)(sw + j * 16 * XLDK + st * 32);
+            for (int j = 0; j < NB; ++j) b[j] = *(const bf16x8_t*)(sw + j * 16 * LDK + st * 32);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], b[j], acc[i][j], 0, 0, 0);
+                    g[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], b[j], g[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if constexpr (Q4) {
+                const float sc = sSc[stage][j * 16 + lr];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][j] += sc * g[i][j];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][j] = g[i][j];
+            }
         }
     };
     // One block: registers -> LDS stage kb & 1 (last read by block kb - 2,
@@ -426,35 +237,36 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
     // then block kb + RING_X is requested into the freed registers, then the
     // MFMAs.  Requests past the last whole block fetch that block again (from
     // cache, never used), so the loop has no branch around its loads.
-#define RX_STEP(X_, W_, KB_)                             \
+#define RX_STEP(X_, W_, C_, KB_)                         \
     {                                                    \
         const int kb_ = (KB_);                           \
-        store(X_, W_, kb_ & 1);                          \
+        store(X_, W_, C_, kb_ & 1);                      \
         __syncthreads();                                 \
-        load(X_, W_, min(kb_ + RING_X, last));           \
+        load(X_, W_, C_, min(kb_ + RING_X, last));       \
         mma(kb_ & 1);                                    \
     }
     if (nfull > 0) {
         const int last = nfull - 1;
-        load(x0, w0, 0);
-        load(x1, w1, min(1, last));
-        load(x2, w2, min(2, last));
-        load(x3, w3, min(3, last));
+        load(x0, w0, c0, 0);
+        load(x1, w1, c1, min(1, last));
+        load(x2, w2, c2, min(2, last));
+        load(x3, w3, c3, min(3, last));
         int kb = 0;
         for (; kb + RING_X <= nfull; kb += RING_X) {
-            RX_STEP(x0, w0, kb);
-            RX_STEP(x1, w1, kb + 1);
-            RX_STEP(x2, w2, kb + 2);
-            RX_STEP(x3, w3, kb + 3);
+            RX_STEP(x0, w0, c0, kb);
+            RX_STEP(x1, w1, c1, kb + 1);
+            RX_STEP(x2, w2, c2, kb + 2);
+            RX_STEP(x3, w3, c3, kb + 3);
         }
-        if (kb < nfull) RX_STEP(x0, w0, kb);
-        if (kb + 1 < nfull) RX_STEP(x1, w1, kb + 1);
-        if (kb + 2 < nfull) RX_STEP(x2, w2, kb + 2);
+        if (kb < nfull) RX_STEP(x0, w0, c0, kb);
+        if (kb + 1 < nfull) RX_STEP(x1, w1, c1, kb + 1);
+        if (kb + 2 < nfull) RX_STEP(x2, w2, c2, kb + 2);
     }
 #undef RX_STEP
-    if (klen > nfull * XB) {
-        // ragged last block: element-wise loads, zero past the slice
-        const int k0 = nfull * XB;
+    if (!Q4 && klen > nfull * KB) {
+        // ragged last block (bf16 W only; a 4-bit K is whole blocks):
+        // element-wise loads, zero past the slice
+        const int k0 = nfull * KB;
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
             const int v = tid + NT * p;
@@ -465,9 +277,9 @@ __global__ __launch_bounds__(NW * 64) void k_rows_gemm_x(RowsGemmArgs a) {
         for (int p = 0; p < WPT; ++p) {
             const int v = tid + NT * p;
             const int valid = min(8, max(0, klen - k0 - (v % PPR) * 8));
-            w0[p] = __builtin_bit_cast(u32x4, ld8_guard(wp[p] + k0, valid));
+            w0[p] = __builtin_bit_cast(u32x4, ld8_guard((const bf16*)wp[p] + k0, valid));
         }
-        store(x0, w0, nfull & 1);
+        store(x0, w0, 0.f, nfull & 1);
         __syncthreads();
         mma(nfull & 1);
     }
@@ -1161,9 +973,9 @@ hipError_t launch_rows_gemm(const PoolDev& P, const RowsPlan& R, const void* x, 
     a.S = R.S;
     a.kslice = R.kslice;
     dim3 grid((unsigned)(R.tiles_m * R.tiles_n * R.S));
-    if (q4) hipLaunchKernelGGL((k_rows_gemm<true, 4, 64, 4>), grid, dim3(256), 0, stream, a);
-    else if (R.shape == 1) hipLaunchKernelGGL((k_rows_gemm_x<8, 128>), grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL((k_rows_gemm_x<4, 64>), grid, dim3(256), 0, stream, a);
+    if (q4) hipLaunchKernelGGL((k_rows_gemm_x<true, 4, 64, 128>), grid, dim3(256), 0, stream, a);
+    else if (R.shape == 1) hipLaunchKernelGGL((k_rows_gemm_x<false, 8, 128, 64>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((k_rows_gemm_x<false, 4, 64, 64>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
