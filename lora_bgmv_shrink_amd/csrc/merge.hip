@@ -50,7 +50,7 @@ __device__ __forceinline__ Piece piece_of(int tid, int p) {
 // next tile's W pieces are requested before the current tile is worked on,
 // so W reads stay in flight across tiles.
 template <bool OUT_IN>
-__global__ __launch_bounds__(MG_THREADS) void k_merge_bf16(PoolDev P, int32_t adapter, float sign,
+__global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void k_merge_bf16(PoolDev P, int32_t adapter, float sign,
                                                             bf16* __restrict__ W, int64_t ldw, int32_t tiles_c,
                                                             int32_t n_tiles) {
     constexpr int NC = OUT_IN ? MG_ROWS : MG_COLS;   // c values per tile
@@ -128,16 +128,31 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge_bf16(PoolDev P, int32_t ad
         }
         // B_a[j][c] for the tile's c range -> sBt[c - c0][j] (16-byte pieces
         // of B rows, transposed on the way in); ranks past r are 0
+        // (whole pieces requested together, without a branch, before any is
+        // stored: a load-then-store loop waited one round trip per piece)
         const int c0 = OUT_IN ? row0 : col0;
         constexpr int BPR = NC / 8;   // pieces per B row
-        for (int idx = tid; idx < 64 * BPR; idx += MG_THREADS) {
+        constexpr int BPT = 64 * BPR / MG_THREADS;
+        uint4 bv[BPT];
+        bool bw[BPT];
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            const int idx = tid + q * MG_THREADS;
+            const int j = idx / BPR;
+            const int c = (idx - j * BPR) * 8;
+            bw[q] = j < r && c0 + c + 8 <= d_out && P.vec_b;
+            bv[q] = *(const uint4*)(bw[q] ? Ba + (int64_t)j * d_out + c0 + c : Ba);
+        }
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            const int idx = tid + q * MG_THREADS;
             const int j = idx / BPR;
             const int c = (idx - j * BPR) * 8;
             union { uint4 u; bf16 e[8]; } v;
-            const bf16* src = Ba + (int64_t)j * d_out + c0 + c;
-            if (j < r && c0 + c + 8 <= d_out && P.vec_b) {
-                v.u = *(const uint4*)src;
+            if (bw[q]) {
+                v.u = bv[q];
             } else {
+                const bf16* src = Ba + (int64_t)j * d_out + c0 + c;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v.e[e] = (j < r && c0 + c + e < d_out) ? src[e] : (bf16)0;
             }
