@@ -620,9 +620,9 @@ def bench_serving(torch, args):
     batch): distinct
     adapters per step (the cost driver), cache hit rate, queue waits in
     steps (overall and for the less popular half of the adapters), and the
-    GPU time of the last 64 batches the loop formed, graph-replayed, against
-    the base-only decode of the same rows and W (adapter overhead
-    fraction)."""
+    GPU time of the last 64 batches the loop formed, graph-replayed over
+    eight copies of W in turn, against the base-only decode of the same rows
+    and weights (adapter overhead fraction)."""
     from lora_bgmv_shrink_amd import binding as b
     from lora_bgmv_shrink_amd import workloads as wl
 
@@ -684,12 +684,17 @@ def bench_serving(torch, args):
         ys = [torch.empty((len(sl), d), dtype=torch.bfloat16, device=dev) for sl in last]
         ws = torch.zeros(b.lora_layer_workspace(pool, rows_max, b.LORA_MODE_BGMV), dtype=torch.uint8, device=dev)
         wsb = torch.zeros(b.lora_decode_workspace(pool, rows_max, False), dtype=torch.uint8, device=dev)
-        g_lora = capture(torch, lambda: [b.lora_layer_apply(pool, x[:len(sl)], W, ii, w_layout=b.LORA_W_OUT_IN,
+        # batch i runs on weight copy i % 8: eight 33.5 MB copies outgrow the
+        # 256 MB last-level cache, so each batch reads its W from HBM as a
+        # layer of a real model would (one W would stay cached across batches)
+        Ws = [W] + [W.clone() for _ in range(7)]
+        g_lora = capture(torch, lambda: [b.lora_layer_apply(pool, x[:len(sl)], Ws[i % 8], ii,
+                                                            w_layout=b.LORA_W_OUT_IN,
                                                             mode=b.LORA_MODE_BGMV, y=yy, ws=ws)
-                                         for sl, ii, yy in zip(last, ids_l, ys)])
-        g_base = capture(torch, lambda: [(b.lora_decode_stream(pool, x[:len(sl)], W, ii, wsb, False),
+                                         for i, (sl, ii, yy) in enumerate(zip(last, ids_l, ys))])
+        g_base = capture(torch, lambda: [(b.lora_decode_stream(pool, x[:len(sl)], Ws[i % 8], ii, wsb, False),
                                           b.lora_decode_finish(pool, ii, wsb, yy, False))
-                                         for sl, ii, yy in zip(last, ids_l, ys)])
+                                         for i, (sl, ii, yy) in enumerate(zip(last, ids_l, ys))])
         lora_us = time_graph(torch, g_lora, 20) / len(last) * 1e6
         base_us = time_graph(torch, g_base, 20) / len(last) * 1e6
         hits = st["hits"] - stats0["hits"]

@@ -294,12 +294,13 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
         for (size_t i = 1; i < sa.size(); ++i)
             if (sa[i].first < sa[i - 1].second || sb[i].first < sb[i - 1].second) return LORA_E_INVALID;
     }
-    bool vec_a = true, vec_b = ((int64_t)d_out * eb) % 16 == 0, stream_ok = true;
+    bool vec_a = true, vec_b = ((int64_t)d_out * eb) % 16 == 0, stream_ok = true, vec_rank = true;
     const int ve = 16 / eb;
     for (int32_t u = 0; u < n_adapters; ++u) {
         vec_a = vec_a && (ao[u] * eb) % 16 == 0;
         vec_b = vec_b && (bo[u] * eb) % 16 == 0;
         stream_ok = stream_ok && rk[u] % ve == 0 && (512 * ve) % rk[u] == 0;
+        vec_rank = vec_rank && rk[u] % ve == 0;
     }
 
     const size_t o_ranks = 0;
@@ -341,6 +342,7 @@ lora_status_t lora_pool_create(lora_pool_t* out, lora_layout_t layout, lora_dtyp
     p->dev.vec_a = vec_a ? 1 : 0;
     p->dev.vec_b = vec_b ? 1 : 0;
     p->dev.stream_ok = stream_ok ? 1 : 0;
+    p->dev.vec_rank = vec_rank ? 1 : 0;
     p->dev.uniform = layout == LORA_LAYOUT_UNIFORM ? 1 : 0;
     *out = p;
     return LORA_OK;

@@ -372,6 +372,7 @@ lora_status_t lora_cache_create(lora_cache_t* out, lora_dtype_t dtype, int32_t n
         q->dev.vec_a = 1;   // blocks start 256-byte aligned
         q->dev.vec_b = ((int64_t)d_out[p] * c->eb) % 16 == 0 ? 1 : 0;
         q->dev.stream_ok = stream_ok ? 1 : 0;
+        q->dev.vec_rank = stream_ok ? 1 : 0;   // taken ranks are whole 16-byte pieces
         c->pools.push_back(q);
     }
     *out = c;

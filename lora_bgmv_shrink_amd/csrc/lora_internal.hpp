@@ -36,6 +36,7 @@ struct PoolDev {
     int32_t vec_a;       // every A block starts 16-byte aligned
     int32_t vec_b;       // every B block 16-byte aligned and d_out*elem % 16 == 0
     int32_t stream_ok;   // every rank r: r*elem % 16 == 0 and (512*16/elem) % r == 0
+    int32_t vec_rank = 0;   // every rank r: r*elem % 16 == 0 (rows of A are whole 16-byte pieces)
     // the uniform layout: every rank is r_max and adapter u's blocks start at
     // u * d_in * r_max (A) and u * r_max * d_out (B), so kernels whose path
     // waits on them form the rank and A offset without a table load
@@ -44,6 +45,14 @@ struct PoolDev {
 __device__ __forceinline__ int pool_rank(const PoolDev& P, int u) { return P.uniform ? P.r_max : P.ranks[u]; }
 __device__ __forceinline__ int64_t pool_a_off(const PoolDev& P, int u) {
     return P.uniform ? (int64_t)u * P.d_in * P.r_max : P.a_off[u];
+}
+
+// eight bf16 from p, those at or past `valid` read as zero (no access)
+__device__ __forceinline__ bf16x8_t ld8_guard(const bf16* p, int valid) {
+    union { bf16x8_t v; bf16 e[8]; } u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u.e[e] = (e < valid) ? p[e] : (bf16)0;
+    return u.v;
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }

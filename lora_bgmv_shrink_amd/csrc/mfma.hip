@@ -19,6 +19,7 @@
 //   bf16: v_mfma_f32_16x16x32_bf16, lane l supplies row l%16, k (l/16)*8..+8
 //   fp32: v_mfma_f32_16x16x4_f32,   lane l supplies row l%16, k l/16
 //   output: lane l holds rows (l/16)*4 + 0..3 of column l%16.
+#include <atomic>
 #include <climits>
 
 #include "lora_internal.hpp"
@@ -1352,31 +1353,324 @@ __global__ __launch_bounds__(C::NT) void k_sgmv_shrink(PoolDev P, const typename
 
 // t[row][j] = sum over slices (in order) of part[slice][row][j], and the
 // K-extension operand s * t (bf16 hi | lo blocks, or fp32) for the row.
+// Thread = (row, 4 columns); the slices' 16-byte pieces are requested four
+// at a time before any is added.  S_dev (when set) holds the slice count
+// the shrink launch chose on the device; S is then its upper bound.
 template <typename T>
 __global__ __launch_bounds__(256) void k_shrink_reduce(PoolDev P, const float* __restrict__ part, int32_t S,
                                                        int32_t n_rows, const int32_t* __restrict__ ids,
                                                        float* __restrict__ t, int64_t ldt,
-                                                       T* __restrict__ t_ext, int64_t lde) {
+                                                       T* __restrict__ t_ext, int64_t lde,
+                                                       const int32_t* __restrict__ S_dev = nullptr) {
     const int idx = blockIdx.x * 256 + threadIdx.x;
-    const int row = idx >> 6;
-    const int col = idx & 63;
+    const int row = idx >> 4;
+    const int c0 = (idx & 15) * 4;
     if (row >= n_rows) return;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += part[((int64_t)s * n_rows + row) * 64 + col];
-    if (col < P.r_max) t[(int64_t)row * ldt + col] = v;
+    if (S_dev) S = min(S, *S_dev);
+    const f32x4_t* pp = (const f32x4_t*)(part + (int64_t)row * 64 + c0);
+    const int64_t sstride = (int64_t)n_rows * 16;   // one slice, in 16-byte pieces
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 4) {
+        f32x4_t q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = pp[(int64_t)min(s0 + j, S - 1) * sstride];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (s0 + j < S) v += q[j];
+    }
     const int ext_rank_cols = EXT_RANKS * ((P.r_max + EXT_RANKS - 1) / EXT_RANKS);
-    if (!t_ext || col >= ext_rank_cols) return;
-    const int a = ids[row];
-    const float sv = id_ok(a, P.n_adapters) ? P.scales[a] * v : 0.f;
-    T* er = t_ext + (int64_t)row * lde;
-    if constexpr (sizeof(T) == 2) {
-        const int e = col / EXT_RANKS;
-        const int jj = col - e * EXT_RANKS;
-        const bf16 hi = f32_to_bf16(sv);
-        er[e * 64 + jj] = (T)hi;
-        er[e * 64 + 32 + jj] = (T)f32_to_bf16(sv - to_f32(hi));
-    } else {
-        er[col] = (T)sv;
+    const int a = t_ext ? ids[row] : -1;
+    const float sc = id_ok(a, P.n_adapters) ? P.scales[a] : 0.f;
+    T* er = t_ext ? t_ext + (int64_t)row * lde : nullptr;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+        const int col = c0 + e4;
+        if (col < P.r_max) t[(int64_t)row * ldt + col] = v[e4];
+        if (!er || col >= ext_rank_cols) continue;
+        const float sv = sc * v[e4];
+        if constexpr (sizeof(T) == 2) {
+            const int e = col / EXT_RANKS;
+            const int jj = col - e * EXT_RANKS;
+            const bf16 hi = f32_to_bf16(sv);
+            er[e * 64 + jj] = (T)hi;
+            er[e * 64 + 32 + jj] = (T)f32_to_bf16(sv - to_f32(hi));
+        } else {
+            er[col] = (T)sv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// SGMV shrink for long segments: bf16 pools whose ranks are multiples of 8
+// ---------------------------------------------------------------------------
+//
+// part[slice][row][0:64] = x[row, K slice] A_u[K slice, 0:64] over segment
+// tiles of 32 NW rows ("Serving multiple LoRAs: segmented matrix multiplies
+// and adapter scheduling", section "Not merging the weights, computing in
+// batches": a segment's shrink is one small matrix product).  The shrink of
+// a prefill batch reads x once and each A_u once per tile, so it is a
+// stream of x; everything here is arranged to keep many bytes of x in
+// flight per CU:
+//   - NW waves, each 32 rows x 64 ranks of 16x16x32 bf16 MFMAs;
+//   - K-blocks of 64 go through a RING-deep register ring (block kb + RING
+//     is requested as soon as block kb is in LDS) into two LDS stages, one
+//     barrier per block;
+//   - x is staged [row][k] (whole 128-byte lines per load);
+//   - A_u's rows kbeg .. kbeg + 63 are one contiguous run of 64 r elements,
+//     copied as they lie ([k][n], whole lines) into a [k][64] LDS block
+//     whose 32-byte units are XOR-swizzled per row, and read as MFMA
+//     operands with the LDS transpose read: lane i of a 16-lane group
+//     points at row k0 + i / 4, columns n0 + 4 (i % 4) .. + 3 and receives
+//     column n0 + i of rows k0 .. k0 + 3, so no transpose happens on the
+//     way in.  The swizzle (unit ^= (k & 3) ^ ((k >> 3) & 1)) puts the rows
+//     one transpose read touches in distinct banks;
+//   - the grid is the number of workgroups the GPU holds at once; every
+//     workgroup counts the batch's tiles T (from the segment descriptor)
+//     and takes the same slice count S = min(s_max, grid / T), so the
+//     T x S (tile, slice) items fill the GPU once whatever the segments;
+//     workgroup 0 stores S for the reduce pass.
+// Ranks past r are exact zeros in part (the LDS columns past r are zeroed).
+constexpr int SX_KB = 64;
+constexpr int SX_LDK = SX_KB + 8;                       // x rows padded by 16 bytes
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+struct ShrinkXArgs {
+    const bf16* x;
+    int64_t ldx;
+    const int32_t* perm;
+    const int32_t* seg_ids;
+    const int32_t* seg_off;
+    const int32_t* n_seg;
+    float* part;        // [s_max][n_rows][64]
+    int32_t* s_used;    // the slice count chosen (read by the reduce pass)
+    int32_t n_rows;
+    int32_t s_max;
+};
+
+// element offset of (k, n) in a swizzled [64][64] A block
+__device__ __forceinline__ int sx_a_at(int k, int n) {
+    return k * 64 + ((((n >> 4) ^ (k & 3) ^ ((k >> 3) & 1))) << 4) + (n & 15);
+}
+
+// NW waves of 32 rows (tile of 32 NW rows); a RING-deep register ring.
+template <int NW, int RING>
+__global__ __launch_bounds__(NW * 64) void k_sgmv_shrink_x(PoolDev P, ShrinkXArgs a) {
+    constexpr int BM = 32 * NW;
+    constexpr int NT = 64 * NW;
+    constexpr int XPT = BM * (SX_KB / 8) / NT;     // 16-byte x pieces per thread per block
+    constexpr int APT = SX_KB * 8 / NT;            // 16-byte A pieces per thread per block (r = 64)
+    static_assert(XPT * NT == BM * SX_KB / 8 && APT * NT == SX_KB * 8 && APT >= 1, "blocks do not split evenly");
+    static_assert(RING >= 2 && RING <= 8, "register ring of 2 to 8 blocks");
+    __shared__ __attribute__((aligned(16))) bf16 sX[2][BM * SX_LDK];
+    __shared__ __attribute__((aligned(16))) bf16 sA[2][SX_KB * 64];
+    __shared__ int sRow[BM];
+    __shared__ int sInfo[4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15;
+    const int G = gridDim.x;
+    const int n_seg = *a.n_seg;
+
+    if (wave == 0) {
+        int tot = 0;
+        for (int s0 = 0; s0 < n_seg; s0 += 64) {
+            const int s = s0 + lane;
+            const int c = s < n_seg ? (a.seg_off[s + 1] - a.seg_off[s] + BM - 1) / BM : 0;
+            tot += __shfl(wave_incl_scan(c, lane), 63, 64);
+        }
+        if (lane == 0) sInfo[0] = tot;
+    }
+    __syncthreads();
+    const int T = __builtin_amdgcn_readfirstlane(sInfo[0]);
+    const int S0 = max(1, min(a.s_max, G / max(T, 1)));
+    const int kslice = ((P.d_in + S0 - 1) / S0 + SX_KB - 1) / SX_KB * SX_KB;
+    const int S = (P.d_in + kslice - 1) / kslice;   // every slice non-empty
+    if (blockIdx.x == 0 && tid == 0) *a.s_used = S;
+
+    // lane constants of the transpose reads: group g = lane / 16 takes k
+    // rows g * 8 .. g * 8 + 7 of each 32-deep step (reads of rows + 0..3 and
+    // + 4..7); the swizzle of those rows is (lr / 4) ^ (g & 1)
+    const int g = lane >> 4;
+    const int a_lane = (g * 8 + (lr >> 2)) * 64 + (lr & 3) * 4;
+    const int a_sw = (lr >> 2) ^ (g & 1);
+
+    for (int item = blockIdx.x; item < T * S; item += G) {
+        const int tile = item / S;
+        const int ks = item - tile * S;
+        __syncthreads();   // the previous item is done with sRow, sInfo and both stages
+        if (wave == 0) {
+            int s = 0, c = 0;
+            find_seg_tile(a.seg_off, n_seg, BM, tile, lane, s, c);
+            if (lane == 0) {
+                sInfo[1] = s;
+                sInfo[2] = c;
+            }
+        }
+        __syncthreads();
+        const int s = __builtin_amdgcn_readfirstlane(sInfo[1]);
+        const int row0 = a.seg_off[s] + __builtin_amdgcn_readfirstlane(sInfo[2]) * BM;
+        const int cnt = min(BM, a.seg_off[s + 1] - row0);
+        const int u = a.seg_ids[s];
+        if (tid < BM) sRow[tid] = tid < cnt ? a.perm[row0 + tid] : -1;
+        float* out = a.part + (int64_t)ks * a.n_rows * 64;
+        if (!id_ok(u, P.n_adapters)) {
+            __syncthreads();
+            for (int idx = tid; idx < cnt * 64; idx += NT) out[(int64_t)sRow[idx >> 6] * 64 + (idx & 63)] = 0.f;
+            continue;
+        }
+        const int r = pool_rank(P, u);
+        const bf16* Au = (const bf16*)P.A + pool_a_off(P, u);
+        const int kbeg = ks * kslice;
+        const int klen = min(P.d_in, kbeg + kslice) - kbeg;
+        const int nfull = klen / SX_KB;
+        // the item walks its whole blocks from a tile-dependent start (fixed
+        // per tile, so the sum order is too): tiles that run side by side
+        // read different columns of their rows at any moment
+        const int rot = nfull > 0 ? (tile * 3) % nfull : 0;
+        // LDS columns past r hold zeros for the whole item (no block writes them)
+        if (r < 64) {
+            const int w = 64 - r;
+            for (int idx = tid; idx < 2 * SX_KB * w; idx += NT) {
+                const int st = idx / (SX_KB * w);
+                const int rem = idx - st * SX_KB * w;
+                const int k = rem / w;
+                sA[st][sx_a_at(k, r + rem - k * w)] = 0;
+            }
+        }
+        __syncthreads();   // sRow
+
+        // piece v = tid + NT p: x row v / 8, k-piece v % 8; A element 8 v of
+        // the block's run (row 8 v / r, column 8 v % r), valid for v < 8 r
+        const bf16* xp[XPT];
+        int xs[XPT];
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            const int v = tid + NT * p;
+            const int m = v >> 3;
+            const int gr = sRow[m] >= 0 ? sRow[m] : sRow[0];   // rows past cnt read row 0 (never stored)
+            xp[p] = a.x + (int64_t)gr * a.ldx + kbeg + (v & 7) * 8;
+            xs[p] = m * SX_LDK + (v & 7) * 8;
+        }
+        const bf16* ap[APT];
+        int as[APT];
+        bool aok[APT];
+#pragma unroll
+        for (int p = 0; p < APT; ++p) {
+            const int v = tid + NT * p;
+            aok[p] = v < 8 * r;
+            const int e = aok[p] ? 8 * v : 0;
+            const int k = e / r;
+            ap[p] = Au + (int64_t)kbeg * r + e;
+            as[p] = sx_a_at(k, e - k * r);
+        }
+        const int64_t ablk = (int64_t)SX_KB * r;   // elements of A per block
+
+        u32x4_t xr[RING][XPT], ar[RING][APT];
+        f32x4_t acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        auto load = [&](u32x4_t (&dx)[XPT], u32x4_t (&da)[APT], int kb) __attribute__((always_inline)) {
+            kb += rot;
+            kb -= kb >= nfull ? nfull : 0;
+#pragma unroll
+            for (int p = 0; p < XPT; ++p) dx[p] = *(const u32x4_t*)(xp[p] + kb * SX_KB);
+#pragma unroll
+            for (int p = 0; p < APT; ++p) da[p] = *(const u32x4_t*)(ap[p] + kb * ablk);
+        };
+        auto store = [&](const u32x4_t (&dx)[XPT], const u32x4_t (&da)[APT], int st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int p = 0; p < XPT; ++p) *(u32x4_t*)(sX[st] + xs[p]) = dx[p];
+#pragma unroll
+            for (int p = 0; p < APT; ++p)
+                if (aok[p]) *(u32x4_t*)(sA[st] + as[p]) = da[p];
+        };
+        auto mma = [&](int st) __attribute__((always_inline)) {
+            const bf16* sx = sX[st] + (wave * 32 + lr) * SX_LDK + (lane >> 4) * 8;
+            const bf16* sa = sA[st] + a_lane;
+#pragma unroll
+            for (int h = 0; h < SX_KB / 32; ++h) {
+                bf16x8_t xa[2], b[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) xa[i] = *(const bf16x8_t*)(sx + i * 16 * SX_LDK + h * 32);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16* q = sa + h * 32 * 64 + ((j ^ a_sw) << 4);
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)q);
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(q + 4 * 64));
+                    b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        };
+        // one block: registers -> LDS stage kb & 1 (last read by block
+        // kb - 2, which every wave finished before the barrier of block
+        // kb - 1), then block kb + RING into the freed registers (past the
+        // last whole block: that block again, from cache, never stored), then
+        // the MFMAs.  Ring slot q holds the blocks kb with kb % RING == q.
+        auto step = [&](u32x4_t (&dx)[XPT], u32x4_t (&da)[APT], int kb, int last) __attribute__((always_inline)) {
+            store(dx, da, kb & 1);
+            __syncthreads();
+            load(dx, da, min(kb + RING, last));
+            mma(kb & 1);
+        };
+        if (nfull > 0) {
+            const int last = nfull - 1;
+#pragma unroll
+            for (int q = 0; q < RING; ++q) load(xr[q], ar[q], min(q, last));
+            int kb = 0;
+            for (; kb + RING <= nfull; kb += RING) {
+#pragma unroll
+                for (int q = 0; q < RING; ++q) step(xr[q], ar[q], kb + q, last);
+            }
+#pragma unroll
+            for (int q = 0; q < RING - 1; ++q)
+                if (kb + q < nfull) step(xr[q], ar[q], kb + q, last);
+        }
+        if (klen > nfull * SX_KB) {
+            // ragged last block: x element-wise up to klen, A rows past it zero
+            const int k0 = nfull * SX_KB;
+            const int rows = klen - k0;
+#pragma unroll
+            for (int p = 0; p < XPT; ++p) {
+                const int v = tid + NT * p;
+                const int valid = min(8, max(0, rows - (v & 7) * 8));
+                xr[0][p] = __builtin_bit_cast(u32x4_t, ld8_guard(xp[p] + k0, valid));
+            }
+#pragma unroll
+            for (int p = 0; p < APT; ++p) {
+                const int v = tid + NT * p;
+                const bool in = aok[p] && (8 * v) / r < rows;
+                ar[0][p] = in ? *(const u32x4_t*)(ap[p] + nfull * ablk) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+            store(xr[0], ar[0], nfull & 1);
+            __syncthreads();
+            mma(nfull & 1);
+        }
+
+        // lane l holds rows (l / 16) * 4 + q of column l % 16 of each block
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = wave * 32 + i * 16 + (lane >> 4) * 4 + q;
+                if (m >= cnt) continue;
+                float* o = out + (int64_t)sRow[m] * 64 + lr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j * 16] = acc[i][j][q];
+            }
     }
 }
 
@@ -1864,8 +2158,47 @@ int32_t sgmv_shrink_slices(const PoolDev& P, int32_t n_rows) {
 }
 
 size_t sgmv_shrink_part_bytes(const PoolDev& P, int32_t n_rows) {
+    // the slices' partial sums, then (k_sgmv_shrink_x) the slice count it chose
     const int32_t S = sgmv_shrink_slices(P, n_rows);
-    return S > 1 ? align_up((size_t)S * n_rows * 64 * 4, 256) : 0;
+    return S > 1 ? align_up((size_t)S * n_rows * 64 * 4, 256) + 256 : 0;
+}
+
+// k_sgmv_shrink_x launch shape: 8 waves (256-row tiles), a 4-block ring (6 measured no faster).
+constexpr int SX_NW = 8, SX_RING = 4;
+
+// Workgroups of k_sgmv_shrink_x the current device holds at once.
+static int shrink_x_slots() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_sgmv_shrink_x<SX_NW, SX_RING>, SX_NW * 64, 0) !=
+            hipSuccess)
+            per = 0;
+        v = std::max(1, cus) * std::max(1, per);
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// k_sgmv_shrink_x takes bf16 pools whose A blocks are 16-byte aligned and
+// whose ranks are multiples of 8, when the K split is on.
+static hipError_t run_shrink_x(const PoolDev& P, const void* x, int64_t ldx, const lora_segments_t* seg,
+                               int32_t n_rows, int32_t n_bins, float* t, int64_t ldt, void* t_ext, int64_t lde,
+                               const int32_t* ids, float* part, hipStream_t stream) {
+    const int32_t s_max = sgmv_shrink_slices(P, n_rows);
+    int32_t* s_used = (int32_t*)((uint8_t*)part + align_up((size_t)s_max * n_rows * 64 * 4, 256));
+    const int64_t items = seg_tiles(n_rows, n_bins, 32 * SX_NW) * s_max;
+    const int G = (int)std::max<int64_t>(1, std::min<int64_t>(shrink_x_slots(), items));
+    ShrinkXArgs a{(const bf16*)x, ldx, seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, part, s_used, n_rows, s_max};
+    hipLaunchKernelGGL((k_sgmv_shrink_x<SX_NW, SX_RING>), dim3((unsigned)G), dim3(SX_NW * 64), 0, stream, P, a);
+    dim3 rgrid((unsigned)ceil_div((int64_t)n_rows * 16, 256));
+    hipLaunchKernelGGL(k_shrink_reduce<bf16>, rgrid, dim3(256), 0, stream, P, (const float*)part, s_max, n_rows,
+                       ids, t, ldt, (bf16*)t_ext, lde, (const int32_t*)s_used);
+    return hipGetLastError();
 }
 
 template <class C, typename T>
@@ -1883,7 +2216,7 @@ static hipError_t run_shrink(const PoolDev& P, const void* x, int64_t ldx, const
     hipLaunchKernelGGL(k_sgmv_shrink<C>, grid, dim3(C::NT), 0, stream, P, (const T*)x, ldx, seg->perm,
                        seg->seg_ids, seg->seg_off, seg->n_seg, t, ldt, (T*)t_ext, lde, pt, n_rows, ks_len);
     if (pt) {
-        dim3 rgrid((unsigned)ceil_div((int64_t)n_rows * 64, 256));
+        dim3 rgrid((unsigned)ceil_div((int64_t)n_rows * 16, 256));
         hipLaunchKernelGGL(k_shrink_reduce<T>, rgrid, dim3(256), 0, stream, P, (const float*)pt, S, n_rows, ids,
                            t, ldt, (T*)t_ext, lde);
     }
@@ -1894,8 +2227,11 @@ hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, 
                               const lora_segments_t* seg, int32_t n_rows, int32_t n_bins, float* t,
                               int64_t ldt, bool, hipStream_t stream, void* t_ext, int64_t lde,
                               const int32_t* ids, float* part) {
-    if (dt == LORA_BF16)
+    if (dt == LORA_BF16) {
+        if (part && P.vec_a && P.vec_rank && sgmv_shrink_slices(P, n_rows) > 1)
+            return run_shrink_x(P, x, ldx, seg, n_rows, n_bins, t, ldt, t_ext, lde, ids, part, stream);
         return run_shrink<ShrinkB, bf16>(P, x, ldx, seg, n_rows, n_bins, t, ldt, t_ext, lde, ids, part, stream);
+    }
     return run_shrink<ShrinkF, float>(P, x, ldx, seg, n_rows, n_bins, t, ldt, t_ext, lde, ids, part, stream);
 }
 

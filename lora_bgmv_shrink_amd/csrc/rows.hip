@@ -75,13 +75,6 @@ __device__ __forceinline__ int xcd_tile(int b, int G) {
     return xc * q + min(xc, rem) + local;
 }
 
-__device__ __forceinline__ bf16x8_t ld8_guard(const bf16* p, int valid) {
-    union { bf16x8_t v; bf16 e[8]; } u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u.e[e] = (e < valid) ? p[e] : (bf16)0;
-    return u.v;
-}
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Eight signed 4-bit values (element e in bits 4e .. 4e+3) as exact bf16.

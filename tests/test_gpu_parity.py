@@ -181,6 +181,49 @@ def test_sgmv_shrink_split_and_unsplit(ranks, split):
             assert np.all(tn[i, int(p.pool.ranks[a]):] == 0)
 
 
+@pytest.mark.parametrize("case", [
+    # long runs at rank 64 (prefill-like), whole K-blocks
+    dict(seed=31, d_in=4096, n_adapters=5, ranks=64, layout=wl.UNIFORM,
+         runs=[700, 1, 530, 129, 128, 2, 300]),
+    # ranks that are multiples of 8 but not powers of two, a ragged K tail
+    # (2104 = 32 x 64 + 56) and base-only rows inside the runs
+    dict(seed=32, d_in=2104, n_adapters=6, ranks=[8, 24, 64, 40, 16, 56], layout=wl.RAGGED,
+         runs=[260, 3, 129, 1, 400, 77, 64]),
+    # hundreds of short runs over 600 adapters: more tiles than workgroups
+    # the GPU holds, so workgroups take several tiles of different ranks
+    dict(seed=33, d_in=2048, n_adapters=600, ranks=([8, 16, 32, 64, 24] * 120), layout=wl.RAGGED,
+         runs=None, n_rows=2000),
+])
+def test_sgmv_shrink_long_segments(case):
+    """The split-K SGMV shrink on pools whose ranks are multiples of 8 (the
+    transpose-read kernel): t matches the oracle, columns past each rank and
+    base-only rows are exactly 0, a repeated call is bit-identical, and the
+    unsplit shrink (ws = NULL, other kernel) agrees within the tolerance."""
+    say(f"sgmv shrink, long segments: seed {case['seed']} d_in {case['d_in']}")
+    b = binding()
+    w = wl.small_batch(seed=case["seed"], n_rows=case.get("n_rows", 200), d_in=case["d_in"], d_out=128,
+                       n_adapters=case["n_adapters"], ranks=case["ranks"], layout=case["layout"],
+                       dtype=torch.bfloat16, device="cuda", run_lengths=case["runs"], frac_base=0.05)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    assert b.lora_sgmv_shrink_workspace(pool, w.n_rows) > 0
+    seg = b.lora_segments_build(ids, p.pool.n_adapters)
+    t = b.lora_sgmv_shrink(pool, p.x, seg, split=True)
+    t2 = b.lora_sgmv_shrink(pool, p.x, seg, split=True)
+    tu = b.lora_sgmv_shrink(pool, p.x, seg, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(t, t2)
+    o = run_oracle(w, want=("t",))
+    assert_close(t, o["t"], TOL[torch.bfloat16], "t split")
+    assert_close(tu, o["t"], TOL[torch.bfloat16], "t unsplit")
+    tn = t.cpu().numpy()
+    assert np.all(tn[w.ids == -1] == 0)
+    for i, a in enumerate(w.ids.tolist()):
+        if a >= 0:
+            assert np.all(tn[i, int(p.pool.ranks[a]):] == 0)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("mode", ["bgmv", "sgmv"])
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
