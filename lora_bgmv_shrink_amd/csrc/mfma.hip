@@ -1685,8 +1685,10 @@ __global__ __launch_bounds__(NW * 64) void k_sgmv_shrink_x(PoolDev P, ShrinkXArg
 // segment and EXP_SPAN output columns, taken 128 at a time:
 //   - the A side is s_u * t of the tile's rows as bf16 pairs (hi, lo) with
 //     hi + lo = s_u * t to about 16 significant bits, in blocks of 32 ranks
-//     laid [hi(32) | lo(32)] along K; the B side holds each rank row of B_u
-//     twice (against hi and against lo), staged transposed as [column][K];
+//     laid [hi(32) | lo(32)] along K; the B side is B_u's rank rows for
+//     the piece, staged as they lie ([rank][column], whole 256-byte rows)
+//     and read as MFMA operands with LDS transpose reads, one fragment per
+//     32 ranks serving both the hi and the lo half;
 //   - 4 waves, each 64 rows x 32 columns of 16x16x32 bf16 MFMAs;
 //   - the fp32 tile then goes through LDS so that y moves in 16-byte pieces,
 //     read and written once, rounded once.
@@ -1701,6 +1703,12 @@ constexpr int EXP_KLD = EXP_KMAX + 8;          // bf16 pitch of the staged rows 
 constexpr int EXP_CLD = EXP_COLS + 4;          // fp32 pitch of the staged output tile
 constexpr int EXP_SPAN = 512;                 // columns per workgroup, in pieces of EXP_COLS (256: slower; 1024: slower)
 
+// element offset of (rank j, column c) in the staged [64][EXP_COLS] B block:
+// 32-byte units XOR-swizzled per row so that the eight rows one half-wave's
+// transpose read touches fall in distinct banks
+__device__ __forceinline__ int exp_b_at(int j, int c) {
+    return j * EXP_COLS + ((((c >> 4) ^ ((j & 3) | (((j >> 3) & 1) << 2)))) << 4) + (c & 15);
+}
 __device__ __forceinline__ int exp_kcols(int r) { return 64 * ((r + 31) / 32); }
 
 template <typename TY>
@@ -1712,10 +1720,10 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
                                                              TY* __restrict__ y, int64_t ldy, int accumulate,
                                                              int vec_y) {
     // A [64 rows][KLD] bf16 stays for the workgroup's whole span; the second
-    // region holds B^T [128 columns][KLD] bf16 of one 128-column piece, then
-    // that piece's fp32 output tile [64][CLD]
+    // region holds B_u [64 ranks][128 columns] bf16 of one 128-column piece
+    // (swizzled), then that piece's fp32 output tile [64][CLD]
     constexpr int A_BYTES = EXP_ROWS * EXP_KLD * 2;
-    constexpr int B_BYTES = EXP_COLS * EXP_KLD * 2;
+    constexpr int B_BYTES = (EXP_KMAX / 2) * EXP_COLS * 2;
     constexpr int C_BYTES = EXP_ROWS * EXP_CLD * 4;
     constexpr int R2_BYTES = B_BYTES > C_BYTES ? B_BYTES : C_BYTES;
     __shared__ __attribute__((aligned(16))) uint8_t lds[A_BYTES + R2_BYTES];
@@ -1790,84 +1798,20 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
     const int lr = lane & 15;
     const int kq = (lane >> 4) * 8;
     const int lq = (lane >> 4) * 4;
+    // transpose-read lane constants: group g = lane / 16 reads rank rows
+    // g * 8 + lr / 4 (+ 4) of each 32-rank block, whose swizzle is
+    // (lr / 4) | ((g & 1) << 2)
+    const int b_lane = ((lane >> 4) * 8 + (lr >> 2)) * EXP_COLS + (lr & 3) * 4;
+    const int b_sw = (lr >> 2) | (((lane >> 4) & 1) << 2);
     const int span0 = blockIdx.y * EXP_SPAN;
     for (int piece = 0; piece < EXP_SPAN / EXP_COLS; ++piece) {
         const int n0 = span0 + piece * EXP_COLS;
         if (n0 >= N) break;   // uniform over the workgroup
-        if (ok) {
-            // B^T: column n, K column 64 e + h * 32 + jj holds B_u[32 e + jj][n]
-            // (both h).  Consecutive lanes take consecutive ranks of one
-            // 8-column group, so their LDS writes are consecutive halves.
-            // (whole 16-byte pieces: every load of a thread requested, without
-            // a branch, before any is stored; ragged or unaligned pieces after)
-            constexpr int BPT = (EXP_KMAX / 2) * (EXP_COLS / 8) / EXP_THREADS;
-            const int nB = (K / 2) * (EXP_COLS / 8);
-            uint4 bv[BPT];
-            bool bw[BPT];
-#pragma unroll
-            for (int q = 0; q < BPT; ++q) {
-                const int idx = tid + q * EXP_THREADS;
-                const int j = idx % (K / 2);
-                const int nc = n0 + (idx / (K / 2)) * 8;
-                bw[q] = idx < nB && j < rk && vb && nc + 8 <= N;
-                bv[q] = *(const uint4*)(bw[q] ? Bu + (int64_t)j * N + nc : Bu);
-            }
-#pragma unroll
-            for (int q = 0; q < BPT; ++q) {
-                const int idx = tid + q * EXP_THREADS;
-                if (idx >= nB) continue;
-                const int j = idx % (K / 2);
-                const int c8 = (idx / (K / 2)) * 8;
-                const int nc = n0 + c8;
-                union { uint4 u4; bf16 e[8]; } v;
-                if (bw[q]) {
-                    v.u4 = bv[q];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v.e[e] = (j < rk && nc + e < N) ? Bu[(int64_t)j * N + nc + e] : (bf16)0;
-                }
-                const int kc = (j >> 5) * 64 + (j & 31);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sB[(c8 + e) * EXP_KLD + kc] = v.e[e];
-                    sB[(c8 + e) * EXP_KLD + kc + 32] = v.e[e];
-                }
-            }
-        }
-        __syncthreads();   // A (first piece) and B^T staged
-        f32x4_t acc[4][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < K; k0 += 32) {
-            bf16x8_t a[4], bb[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(sA + (i * 16 + lr) * EXP_KLD + k0 + kq);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bb[j] = *(const bf16x8_t*)(sB + (wave * 32 + j * 16 + lr) * EXP_KLD + k0 + kq);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
-        }
-        __syncthreads();   // every wave is done with B^T before sC overwrites it
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    sC[(i * 16 + lq + q) * EXP_CLD + wave * 32 + j * 16 + lr] = acc[i][j][q];
-        __syncthreads();
         // 16 threads per row, 8 columns each: a wave moves 4 rows of 128
         // contiguous columns per pass; 16 rows per pass of the workgroup.
         // Whole 16-byte pieces of y (the usual case) are requested, for all
-        // passes, before any is used (one round trip, not one per pass);
-        // ragged or unaligned pieces go element by element.
+        // passes, before B is staged and the MFMAs run (the y round trip
+        // overlaps them); ragged or unaligned pieces go element by element.
         constexpr int NPASS = EXP_ROWS / 16;
         constexpr int YV = 8 * (int)sizeof(TY) / 16;   // 16-byte pieces per 8 columns
         const int cl = (tid & 15) * 8;
@@ -1889,6 +1833,84 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
                 for (int h = 0; h < YV; ++h) yv[pass][h] = *(const uint4*)(src + h * (16 / sizeof(TY)));
             }
         }
+        if (ok) {
+            // B_u rows 0 .. K/2 - 1, columns n0 .. n0 + 127, staged as they lie
+            // ([rank][column], rows past the rank zero) in a swizzled block
+            // read by the MFMAs with LDS transpose reads.  16 lanes move one
+            // 256-byte rank row; every load of a thread is requested, without
+            // a branch, before any is stored; ragged or unaligned pieces after.
+            constexpr int BPT = (EXP_KMAX / 2) * (EXP_COLS / 8) / EXP_THREADS;
+            const int nB = (K / 2) * (EXP_COLS / 8);
+            uint4 bv[BPT];
+            bool bw[BPT];
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                const int j = idx >> 4;
+                const int nc = n0 + (idx & 15) * 8;
+                bw[q] = idx < nB && j < rk && vb && nc + 8 <= N;
+                bv[q] = *(const uint4*)(bw[q] ? Bu + (int64_t)j * N + nc : Bu);
+            }
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                if (idx >= nB) continue;
+                const int j = idx >> 4;
+                const int c8 = (idx & 15) * 8;
+                const int nc = n0 + c8;
+                union { uint4 u4; bf16 e[8]; } v;
+                if (bw[q]) {
+                    v.u4 = bv[q];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v.e[e] = (j < rk && nc + e < N) ? Bu[(int64_t)j * N + nc + e] : (bf16)0;
+                }
+                *(uint4*)(sB + exp_b_at(j, c8)) = v.u4;
+            }
+        }
+        __syncthreads();   // A (first piece) and B staged
+        f32x4_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // per 32 ranks: the B fragments (transpose reads: lane l takes column
+        // l % 16 of its 16-column block, ranks (l / 16) * 8 .. + 7) serve both
+        // the hi and the lo half of s t
+        for (int kb = 0; kb < K / 64; ++kb) {
+            bf16x8_t bb[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16* q = sB + b_lane + kb * 32 * EXP_COLS + (((wave * 2 + j) ^ b_sw) << 4);
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)q);
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(q + 4 * EXP_COLS));
+                bb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8_t a[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a[i] = *(const bf16x8_t*)(sA + (i * 16 + lr) * EXP_KLD + kb * 64 + h * 32 + kq);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        __syncthreads();   // every wave is done with B before sC overwrites it
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sC[(i * 16 + lq + q) * EXP_CLD + wave * 32 + j * 16 + lr] = acc[i][j][q];
+        __syncthreads();
+        // y pieces of this thread (requested at the top of the piece)
 #pragma unroll
         for (int pass = 0; pass < NPASS; ++pass) {
             const int m = pass * 16 + (tid >> 4);
@@ -1918,7 +1940,300 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
                 }
             }
         }
-        __syncthreads();   // sC read before the next piece's B^T overwrites it
+        __syncthreads();   // sC read before the next piece's B overwrites it
+    }
+}
+
+// The expand for long segments: the same tiles and operands as above, run
+// as a stream.  A tile's setup (its segment, rows, rank, scale and s t) is a
+// chain of dependent loads, so the grid is the number of workgroups the GPU
+// holds at once and each workgroup streams an equal run of the batch's
+// 128-column pieces, numbered tile-major (every workgroup counts the tiles
+// from the segment descriptor); a run crosses at most a tile boundary or two.
+// XCD x (workgroups b with b % 8 == x) takes the x-th eighth of the pieces,
+// so an XCD's L2 serves one or two segments.  Within a tile, y (whole 16-byte pieces of
+// rows) and B run through register rings YR pieces deep; B and the fp32
+// output tile have LDS regions of their own, so a piece needs two barriers.
+// Requires d_out % 8 == 0 and y rows 16-byte aligned.
+template <typename TY>
+__global__ __launch_bounds__(EXP_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_sgmv_expand_t(
+    PoolDev P, const float* __restrict__ t, int64_t ldt, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ seg_ids, const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_seg_p,
+    int32_t cap, TY* __restrict__ y, int64_t ldy, int accumulate) {
+    constexpr int BPT = (EXP_KMAX / 2) * (EXP_COLS / 8) / EXP_THREADS;   // B pieces per thread
+    constexpr int NPASS = EXP_ROWS / 16;                                 // y rows per thread
+    constexpr int YV = 8 * (int)sizeof(TY) / 16;                         // 16-byte pieces per 8 columns
+    constexpr int YR = sizeof(TY) == 2 ? 3 : 2;                          // ring depth (pieces in flight)
+    __shared__ __attribute__((aligned(16))) bf16 sA[EXP_ROWS * EXP_KLD];
+    __shared__ __attribute__((aligned(16))) bf16 sB[(EXP_KMAX / 2) * EXP_COLS];
+    __shared__ __attribute__((aligned(16))) float sC[EXP_ROWS * EXP_CLD];
+    __shared__ int sRow[EXP_ROWS];
+    __shared__ int sInfo[8];
+    __shared__ SegTileCache C;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int N = P.d_out;
+    const int npieces = (N + EXP_COLS - 1) / EXP_COLS;
+    // the run boundaries and ids, once per workgroup (tile lookups then
+    // read LDS), and the batch's tile count
+    const int n_seg = seg_tile_cache_load(seg_off, seg_ids, n_seg_p, cap, tid, EXP_THREADS, C);
+    __syncthreads();
+    if (wave == 0) {
+        int tot = 0;
+        for (int s0 = 0; s0 < n_seg; s0 += 64) {
+            const int s = s0 + lane;
+            int c = 0;
+            if (s < n_seg) {
+                const int l = s < SEG_CACHE ? C.lo[s] : seg_off[s];
+                const int h = s < SEG_CACHE ? C.hi[s] : seg_off[s + 1];
+                c = (h - l + EXP_ROWS - 1) / EXP_ROWS;
+            }
+            tot += __shfl(wave_incl_scan(c, lane), 63, 64);
+        }
+        if (lane == 0) sInfo[0] = tot;
+    }
+    __syncthreads();
+    const int T = __builtin_amdgcn_readfirstlane(sInfo[0]);
+    const int G = gridDim.x;
+    const int64_t total = (int64_t)T * npieces;
+    const int xc = blockIdx.x & 7;
+    const int gx = (G + 7 - xc) / 8;                           // workgroups of this XCD
+    const int64_t x_lo = xc * total / 8, x_len = (xc + 1) * total / 8 - x_lo;
+    const int64_t lb = (int64_t)(blockIdx.x >> 3);
+    const int64_t g_beg = x_lo + lb * x_len / gx;              // this workgroup's pieces [g_beg, g_end)
+    const int64_t g_end = x_lo + (lb + 1) * x_len / gx;
+
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int lq = (lane >> 4) * 4;
+    const int b_lane = ((lane >> 4) * 8 + (lr >> 2)) * EXP_COLS + (lr & 3) * 4;
+    const int b_sw = (lr >> 2) | (((lane >> 4) & 1) << 2);
+    const int cl = (tid & 15) * 8;   // this thread's 8 columns of a piece, rows pass * 16 + tid / 16
+
+    for (int64_t gp = g_beg; gp < g_end;) {
+        const int tile = (int)(gp / npieces);
+        const int p_beg = (int)(gp - (int64_t)tile * npieces);
+        const int p_end = (int)min<int64_t>(npieces, p_beg + (g_end - gp));
+        gp += p_end - p_beg;
+        __syncthreads();   // the previous tile is done with sInfo, sRow, sA, sB and sC
+        if (wave == 0) {
+            // the tile from LDS, then its rows, B offset, rank and scale in one round trip
+            int s = 0, c = 0, lo = 0, hi = 0, id = -1;
+            seg_tile_find(C, n_seg, seg_off, seg_ids, EXP_ROWS, tile, lane, s, c, lo, hi, id);
+            const int r0 = lo + c * EXP_ROWS;
+            const int cn = min(EXP_ROWS, hi - r0);
+            const bool v = id_ok(id, P.n_adapters);
+            const int pr = lane < cn ? perm[r0 + lane] : -1;
+            const int64_t bo = v ? P.b_off[id] : 0;
+            const int rkk = v ? pool_rank(P, id) : 0;
+            const float scv = v ? P.scales[id] : 0.f;
+            sRow[lane] = pr;
+            if (lane == 0) {
+                sInfo[1] = cn;
+                sInfo[2] = v ? 1 : 0;
+                sInfo[3] = rkk;
+                sInfo[4] = (int)(bo & 0xffffffff);
+                sInfo[5] = (int)(bo >> 32);
+                sInfo[6] = __float_as_int(scv);
+            }
+        }
+        __syncthreads();
+        const int cnt = __builtin_amdgcn_readfirstlane(sInfo[1]);
+        const bool ok = __builtin_amdgcn_readfirstlane(sInfo[2]) != 0;
+        if (!ok && accumulate) continue;   // base-only rows keep their y
+        const int rk = __builtin_amdgcn_readfirstlane(sInfo[3]);
+        const int64_t b_off = ((int64_t)__builtin_amdgcn_readfirstlane(sInfo[5]) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane(sInfo[4]);
+        const int K = exp_kcols(rk);   // 0 for a base-only tile
+        const bf16* Bu = (const bf16*)P.B + b_off;
+        const bool vb = P.vec_b != 0;
+        // this thread's y rows (pass p: row p * 16 + tid / 16; past cnt: the
+        // tile's first row, read and never written)
+        int yrow[NPASS];
+        bool rin[NPASS];
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+            const int m = ps * 16 + (tid >> 4);
+            rin[ps] = m < cnt;
+            yrow[ps] = sRow[rin[ps] ? m : 0];
+        }
+        auto load_y = [&](u32x4_t (&yv)[NPASS][YV], int pc) __attribute__((always_inline)) {
+            if (!accumulate) return;
+            const int c = pc * EXP_COLS + cl;
+            const int cc = c + 8 <= N ? c : 0;   // d_out % 8 == 0: a piece is whole or past the end
+#pragma unroll
+            for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+                for (int h = 0; h < YV; ++h)
+                    yv[ps][h] = *(const u32x4_t*)(y + (int64_t)yrow[ps] * ldy + cc + h * (16 / sizeof(TY)));
+        };
+        // B_u rows 0 .. K/2 - 1 of a piece's 128 columns, 16 lanes per
+        // 256-byte rank row; whole aligned pieces only (others after, one
+        // element at a time, in store_b)
+        auto load_b = [&](u32x4_t (&bv)[BPT], int pc) __attribute__((always_inline)) {
+            const int n0 = pc * EXP_COLS;
+            int m = 0;
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                const int j = idx >> 4;
+                const int nc = n0 + (idx & 15) * 8;
+                const bool w = j < K / 2 && j < rk && vb && nc + 8 <= N;
+                bv[q] = *(const u32x4_t*)(w ? Bu + (int64_t)j * N + nc : Bu);
+                m |= w ? 1 << q : 0;
+            }
+            return m;
+        };
+        auto store_b = [&](const u32x4_t (&bv)[BPT], int bw, int pc) __attribute__((always_inline)) {
+            const int n0 = pc * EXP_COLS;
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                const int j = idx >> 4;
+                if (j >= K / 2) continue;
+                const int c8 = (idx & 15) * 8;
+                const int nc = n0 + c8;
+                union { u32x4_t u4; bf16 e[8]; } v;
+                if (bw & (1 << q)) {
+                    v.u4 = bv[q];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v.e[e] = (j < rk && nc + e < N) ? Bu[(int64_t)j * N + nc + e] : (bf16)0;
+                }
+                *(u32x4_t*)(sB + exp_b_at(j, c8)) = v.u4;
+            }
+        };
+
+        // the run's first YR pieces (in this tile) of y and first YR - 1 pieces of B are
+        // requested before s t is staged (a base-only tile has rank 0: no B
+        // piece is loaded or stored)
+        const int np = p_end - p_beg;
+        u32x4_t yr[YR][NPASS][YV];
+        u32x4_t br[YR][BPT];
+        int wb[YR];
+#pragma unroll
+        for (int q = 0; q < YR; ++q) load_y(yr[q], p_beg + min(q, np - 1));
+#pragma unroll
+        for (int q = 0; q < YR - 1; ++q) wb[q] = load_b(br[q], p_beg + min(q, np - 1));
+        if (ok) {
+            // A: row m, K column 64 e + h * 32 + jj holds the hi (h = 0) or lo
+            // (h = 1) part of s * t[m][32 e + jj] (0 past the rank and past cnt)
+            constexpr int TPT = EXP_ROWS * (EXP_KMAX / 2) / EXP_THREADS;
+            const float sc = __int_as_float(__builtin_amdgcn_readfirstlane(sInfo[6]));
+            const int nA = EXP_ROWS * (K / 2);
+            float tv[TPT];
+#pragma unroll
+            for (int q = 0; q < TPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                const int m = idx / (K / 2);
+                const int j = idx - m * (K / 2);
+                const bool in = idx < nA && m < cnt && j < rk;
+                tv[q] = t[in ? (int64_t)sRow[m] * ldt + j : 0];
+                tv[q] = in ? tv[q] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < TPT; ++q) {
+                const int idx = tid + q * EXP_THREADS;
+                if (idx < nA) {
+                    const int m = idx / (K / 2);
+                    const int j = idx - m * (K / 2);
+                    const float v = sc * tv[q];
+                    const bf16 hi = f32_to_bf16(v);
+                    const bf16 lo = f32_to_bf16(v - to_f32(hi));
+                    const int e = j >> 5;
+                    const int jj = j & 31;
+                    sA[m * EXP_KLD + e * 64 + jj] = hi;
+                    sA[m * EXP_KLD + e * 64 + 32 + jj] = lo;
+                }
+            }
+        }
+
+        // piece kk of the run (ring slot kk % YR): its B into LDS (whose
+        // last reader, the previous piece's MFMAs, every wave finished before
+        // the previous piece's second barrier), barrier, piece kk + YR - 1's
+        // B requested into the slot the previous piece freed, MFMAs, the fp32
+        // tile into sC (whose last reads, the previous piece's, every wave
+        // finished before this piece's first barrier), barrier, y added from
+        // sC and written, piece kk + YR's y requested into this slot (past
+        // the run's last piece: that piece again, never used)
+        auto step = [&](u32x4_t (&yc)[NPASS][YV], u32x4_t (&bc)[BPT], int wcur, u32x4_t (&bn)[BPT], int& wn,
+                        int kk) __attribute__((always_inline)) {
+            const int pc = p_beg + kk;
+            store_b(bc, wcur, pc);
+            __syncthreads();
+            wn = load_b(bn, p_beg + min(kk + YR - 1, np - 1));
+            f32x4_t acc[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < K / 64; ++kb) {
+                bf16x8_t bb[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const bf16* q = sB + b_lane + kb * 32 * EXP_COLS + (((wave * 2 + j) ^ b_sw) << 4);
+                    const i16x4_t lo =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)q);
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(q + 4 * EXP_COLS));
+                    bb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8_t a[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a[i] = *(const bf16x8_t*)(sA + (i * 16 + lr) * EXP_KLD + kb * 64 + h * 32 + kq);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        sC[(i * 16 + lq + q) * EXP_CLD + wave * 32 + j * 16 + lr] = acc[i][j][q];
+            __syncthreads();
+            const int nc = pc * EXP_COLS + cl;
+#pragma unroll
+            for (int ps = 0; ps < NPASS; ++ps) {
+                if (!rin[ps] || nc >= N) continue;
+                const float* cr = sC + (ps * 16 + (tid >> 4)) * EXP_CLD + cl;
+                union { u32x4_t u4[YV]; TY e[8]; } o;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = cr[e];
+                if (accumulate) {
+#pragma unroll
+                    for (int h = 0; h < YV; ++h) o.u4[h] = yc[ps][h];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] += to_f32(o.e[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o.e[e] = from_f32<TY>(v[e]);
+                TY* dst = y + (int64_t)yrow[ps] * ldy + nc;
+#pragma unroll
+                for (int h = 0; h < YV; ++h) *(u32x4_t*)(dst + h * (16 / sizeof(TY))) = o.u4[h];
+            }
+            load_y(yc, p_beg + min(kk + YR, np - 1));
+        };
+        int kk = 0;
+        for (; kk + YR <= np; kk += YR) {
+#pragma unroll
+            for (int q = 0; q < YR; ++q)
+                step(yr[q], br[q], wb[q], br[(q + YR - 1) % YR], wb[(q + YR - 1) % YR], kk + q);
+        }
+#pragma unroll
+        for (int q = 0; q < YR - 1; ++q)
+            if (kk + q < np) step(yr[q], br[q], wb[q], br[(q + YR - 1) % YR], wb[(q + YR - 1) % YR], kk + q);
     }
 }
 
@@ -2235,6 +2550,26 @@ hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, 
     return run_shrink<ShrinkF, float>(P, x, ldx, seg, n_rows, n_bins, t, ldt, t_ext, lde, ids, part, stream);
 }
 
+// Workgroups of k_sgmv_expand_t (bf16 or fp32 y) the current device holds at once.
+static int expand_t_slots(bool bf16_y) {
+    static std::atomic<int> cache[2][64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[bf16_y][dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+        const hipError_t e = bf16_y ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_sgmv_expand_t<bf16>,
+                                                                                   EXP_THREADS, 0)
+                                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_sgmv_expand_t<float>,
+                                                                                   EXP_THREADS, 0);
+        if (e != hipSuccess) per = 0;
+        v = std::max(1, cus) * std::max(1, per);
+        cache[bf16_y][dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 hipError_t launch_sgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                               const lora_segments_t* seg, int32_t n_rows, int32_t n_bins, void* y,
                               lora_dtype_t ydt, int64_t ldy, int accumulate, hipStream_t stream) {
@@ -2244,7 +2579,21 @@ hipError_t launch_sgmv_expand(const PoolDev& P, lora_dtype_t dt, const float* t,
         // 16-byte y pieces when y and its rows are 16-byte aligned
         const size_t yb = ydt == LORA_BF16 ? 2 : 4;
         const int vec_y = (((uintptr_t)y & 15u) == 0 && (ldy * (int64_t)yb) % 16 == 0) ? 1 : 0;
-        if (ydt == LORA_BF16)
+        // the streaming kernel: whole 16-byte pieces of y rows
+        const bool piece_y = P.d_out % 8 == 0 && vec_y;
+        if (piece_y) {
+            const int64_t most = (int64_t)row_tiles * ceil_div(P.d_out, EXP_COLS);   // items never exceed this
+            const int G = (int)std::max<int64_t>(1, std::min<int64_t>(expand_t_slots(ydt == LORA_BF16), most));
+            const int32_t cap = std::min<int32_t>(seg->cap, std::max<int32_t>(1, std::min<int32_t>(n_rows, n_bins)));
+            if (ydt == LORA_BF16)
+                hipLaunchKernelGGL(k_sgmv_expand_t<bf16>, dim3((unsigned)G), dim3(EXP_THREADS), 0, stream, P, t,
+                                   ldt, seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, cap, (bf16*)y, ldy,
+                                   accumulate);
+            else
+                hipLaunchKernelGGL(k_sgmv_expand_t<float>, dim3((unsigned)G), dim3(EXP_THREADS), 0, stream, P, t,
+                                   ldt, seg->perm, seg->seg_ids, seg->seg_off, seg->n_seg, cap, (float*)y, ldy,
+                                   accumulate);
+        } else if (ydt == LORA_BF16)
             hipLaunchKernelGGL(k_sgmv_expand<bf16>, grid, dim3(EXP_THREADS), 0, stream, P, t, ldt, seg->perm,
                                seg->seg_ids, seg->seg_off, seg->n_seg, (bf16*)y, ldy, accumulate, vec_y);
         else
