@@ -26,9 +26,20 @@ namespace {
 constexpr int MG_ROWS = 64;
 constexpr int MG_COLS = 128;
 constexpr int MG_THREADS = 256;
-constexpr int MG_RPAD = 64 + 8;               // bf16 pitch of the staged B^T rows
 constexpr int MG_LDT = MG_COLS + 4;           // fp32 pitch of the staged product
 constexpr int MG_PIECES = MG_ROWS * MG_COLS / 8 / MG_THREADS;   // 16-byte W pieces per thread
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// element offset of (rank j, column c) in a staged [64][NC] block of B_a:
+// 32-byte units XOR-swizzled per row so that the rows one transpose read
+// touches fall in distinct banks (NC = 128: 8 units a row, the eight rows of
+// a half-wave in distinct units; NC = 64: 4 units, two rows per 64 banks)
+template <int NC>
+__device__ __forceinline__ int mg_b_at(int j, int c) {
+    const int sw = NC == 128 ? ((j & 3) | (((j >> 3) & 1) << 2)) : ((j & 3) ^ ((j >> 3) & 1));
+    return j * NC + ((((c >> 4) ^ sw)) << 4) + (c & 15);
+}
 
 // One 16-byte W piece of the tile: stored row `row`, columns col .. col + 7.
 struct Piece {
@@ -44,7 +55,10 @@ __device__ __forceinline__ Piece piece_of(int tid, int p) {
 //   IN_OUT: L = A_a (row = k), R = B_a (col = c)
 //   OUT_IN: L = B_a^T (row = c), R = A_a^T (col = k)
 // A_a rows are j-contiguous, so its MFMA operand comes straight from global
-// memory; B_a is staged into LDS as [c][j].
+// memory.  B_a is staged into LDS as it lies ([j][c], 16-byte pieces of its
+// rows) and read as MFMA operands with the LDS transpose read (lane i of a
+// 16-lane group points at row j0 + i / 4, columns c0 + 4 (i % 4) and
+// receives column c0 + i of rows j0 .. j0 + 3).
 //
 // A workgroup walks tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...; the
 // next tile's W pieces are requested before the current tile is worked on,
@@ -54,7 +68,7 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
                                                             bf16* __restrict__ W, int64_t ldw, int32_t tiles_c,
                                                             int32_t n_tiles) {
     constexpr int NC = OUT_IN ? MG_ROWS : MG_COLS;   // c values per tile
-    __shared__ __attribute__((aligned(16))) bf16 sBt[NC * MG_RPAD];
+    __shared__ __attribute__((aligned(16))) bf16 sB[64 * NC];
     __shared__ __attribute__((aligned(16))) float sAcc[MG_ROWS * MG_LDT];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -103,8 +117,16 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         for (int e = 0; e < 8; ++e) t.e[e] = (k < d_in && j + e < r) ? Aa[(int64_t)k * r + j + e] : (bf16)0;
         return t.v;
     };
-    auto bt_frag = [&](int c_local, int j0) __attribute__((always_inline)) {
-        return *(const bf16x8_t*)(sBt + c_local * MG_RPAD + j0 + kq);
+    // transpose-read operand: columns cb .. cb + 15 of the staged block,
+    // ranks j0 + (l / 16) * 8 .. + 8
+    const int b_lane = ((lane >> 4) * 8 + (lr >> 2)) * NC + (lr & 3) * 4;
+    const int b_sw = NC == 128 ? ((lr >> 2) | (((lane >> 4) & 1) << 2)) : ((lr >> 2) ^ ((lane >> 4) & 1));
+    auto b_frag = [&](int cb, int j0) __attribute__((always_inline)) {
+        const bf16* q = sB + b_lane + j0 * NC + (((cb >> 4) ^ b_sw) << 4);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)q);
+        const i16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(q + 4 * NC));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
     uint4 wv[MG_PIECES], wn[MG_PIECES];
@@ -126,8 +148,8 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
                 Ag[st][f] = a_frag(k, st * 32);
             }
         }
-        // B_a[j][c] for the tile's c range -> sBt[c - c0][j] (16-byte pieces
-        // of B rows, transposed on the way in); ranks past r are 0
+        // B_a[j][c] for the tile's c range -> sB (16-byte pieces of B rows,
+        // as they lie); ranks past r are 0 up to the last 32-rank step
         // (whole pieces requested together, without a branch, before any is
         // stored: a load-then-store loop waited one round trip per piece)
         const int c0 = OUT_IN ? row0 : col0;
@@ -147,6 +169,7 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         for (int q = 0; q < BPT; ++q) {
             const int idx = tid + q * MG_THREADS;
             const int j = idx / BPR;
+            if (j >= 32 * steps) continue;
             const int c = (idx - j * BPR) * 8;
             union { uint4 u; bf16 e[8]; } v;
             if (bw[q]) {
@@ -156,8 +179,7 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v.e[e] = (j < r && c0 + c + e < d_out) ? src[e] : (bf16)0;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sBt[(c + e) * MG_RPAD + j] = v.e[e];
+            *(uint4*)(sB + mg_b_at<NC>(j, c)) = v.u;
         }
         __syncthreads();
 
@@ -172,9 +194,9 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
             const int j0 = st * 32;
             bf16x8_t L[2], R[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) L[i] = OUT_IN ? bt_frag(wr * 32 + i * 16 + lr, j0) : Ag[st][i];
+            for (int i = 0; i < 2; ++i) L[i] = OUT_IN ? b_frag(wr * 32 + i * 16, j0) : Ag[st][i];
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) R[jb] = OUT_IN ? Ag[st][jb] : bt_frag(wc * 64 + jb * 16 + lr, j0);
+            for (int jb = 0; jb < 4; ++jb) R[jb] = OUT_IN ? Ag[st][jb] : b_frag(wc * 64 + jb * 16, j0);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         }
 #pragma unroll
         for (int p = 0; p < MG_PIECES; ++p) wv[p] = wn[p];
-        __syncthreads();   // sBt and sAcc are rewritten for the next tile
+        __syncthreads();   // sB and sAcc are rewritten for the next tile
     }
 }
 

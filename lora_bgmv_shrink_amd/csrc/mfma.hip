@@ -1950,8 +1950,8 @@ __global__ __launch_bounds__(EXP_THREADS) void k_sgmv_expand(PoolDev P, const fl
 // holds at once and each workgroup streams an equal run of the batch's
 // 128-column pieces, numbered tile-major (every workgroup counts the tiles
 // from the segment descriptor); a run crosses at most a tile boundary or two.
-// XCD x (workgroups b with b % 8 == x) takes the x-th eighth of the pieces,
-// so an XCD's L2 serves one or two segments.  Within a tile, y (whole 16-byte pieces of
+// The runs are dealt out XCD by XCD (workgroups b with b % 8 == 0 take the
+// first runs), so an XCD's L2 serves one or two segments.  Within a tile, y (whole 16-byte pieces of
 // rows) and B run through register rings YR pieces deep; B and the fp32
 // output tile have LDS regions of their own, so a piece needs two barriers.
 // Requires d_out % 8 == 0 and y rows 16-byte aligned.
@@ -1998,12 +1998,12 @@ __global__ __launch_bounds__(EXP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
     const int T = __builtin_amdgcn_readfirstlane(sInfo[0]);
     const int G = gridDim.x;
     const int64_t total = (int64_t)T * npieces;
+    // workgroups numbered XCD by XCD (those with b % 8 == 0 first), each
+    // taking the next equal run of pieces [g_beg, g_end)
     const int xc = blockIdx.x & 7;
-    const int gx = (G + 7 - xc) / 8;                           // workgroups of this XCD
-    const int64_t x_lo = xc * total / 8, x_len = (xc + 1) * total / 8 - x_lo;
-    const int64_t lb = (int64_t)(blockIdx.x >> 3);
-    const int64_t g_beg = x_lo + lb * x_len / gx;              // this workgroup's pieces [g_beg, g_end)
-    const int64_t g_end = x_lo + (lb + 1) * x_len / gx;
+    const int64_t pos = (int64_t)xc * (G >> 3) + min(xc, G & 7) + (blockIdx.x >> 3);
+    const int64_t g_beg = pos * total / G;
+    const int64_t g_end = (pos + 1) * total / G;
 
     const int lr = lane & 15;
     const int kq = (lane >> 4) * 8;

@@ -224,6 +224,30 @@ def test_sgmv_shrink_long_segments(case):
             assert np.all(tn[i, int(p.pool.ranks[a]):] == 0)
 
 
+@pytest.mark.parametrize("n_rows,d_out", [(64, 256), (20, 128), (300, 1024)])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+def test_sgmv_expand_small_grids(n_rows, d_out, ydt):
+    """The streaming SGMV expand deals equal runs of pieces to its
+    workgroups XCD by XCD; with fewer pieces than XCDs (a grid of fewer than
+    8 workgroups) every piece must still be written.  Accumulating into a
+    random y, against the oracle."""
+    say(f"sgmv expand, small grid: {n_rows} rows -> {d_out}, y {ydt}")
+    b = binding()
+    w = wl.small_batch(seed=n_rows + d_out, n_rows=n_rows, d_in=128, d_out=d_out, n_adapters=2, ranks=[16, 64],
+                       layout=wl.RAGGED, dtype=torch.bfloat16, device="cuda", frac_base=0.0,
+                       run_lengths=[n_rows // 2, n_rows - n_rows // 2])
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    o = run_oracle(w, want=("t", "lora"))
+    t = torch.as_tensor(o["t"], dtype=torch.float32, device=DEV)
+    y0 = torch.randn(w.n_rows, p.d_out, device=DEV).to(ydt)
+    seg = b.lora_segments_build(ids, p.pool.n_adapters)
+    y = b.lora_sgmv_expand(pool, t, seg, y=y0.clone(), y_dtype=ydt, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close(y, o["lora"] + f64(y0), TOL[torch.bfloat16], f"y ({n_rows} x {d_out}, {ydt})")
+
+
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("mode", ["bgmv", "sgmv"])
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
