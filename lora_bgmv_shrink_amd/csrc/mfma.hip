@@ -1415,7 +1415,9 @@ __global__ __launch_bounds__(256) void k_shrink_reduce(PoolDev P, const float* _
 //   - K-blocks of 64 go through a RING-deep register ring (block kb + RING
 //     is requested as soon as block kb is in LDS) into two LDS stages, one
 //     barrier per block;
-//   - x is staged [row][k] (whole 128-byte lines per load);
+//   - x is staged [row][k] (whole 128-byte lines per load), with
+//     nontemporal loads: x is read once, and marked as streaming it leaves
+//     L2 to A, which every tile of a segment re-reads;
 //   - A_u's rows kbeg .. kbeg + 63 are one contiguous run of 64 r elements,
 //     copied as they lie ([k][n], whole lines) into a [k][64] LDS block
 //     whose 32-byte units are XOR-swizzled per row, and read as MFMA
@@ -1580,7 +1582,7 @@ __global__ __launch_bounds__(NW * 64) void k_sgmv_shrink_x(PoolDev P, ShrinkXArg
             kb += rot;
             kb -= kb >= nfull ? nfull : 0;
 #pragma unroll
-            for (int p = 0; p < XPT; ++p) dx[p] = *(const u32x4_t*)(xp[p] + kb * SX_KB);
+            for (int p = 0; p < XPT; ++p) dx[p] = __builtin_nontemporal_load((const u32x4_t*)(xp[p] + kb * SX_KB));
 #pragma unroll
             for (int p = 0; p < APT; ++p) da[p] = *(const u32x4_t*)(ap[p] + kb * ablk);
         };
