@@ -148,6 +148,72 @@ hipError_t run_rows(const lora_pool_s* pool, const void* x, int64_t ldx, const v
     return e;
 }
 
+// The shrink (BGMV per row, or segments and the SGMV shrink) and the fused
+// GEMM (x W plus the adapter term, y rounded once).  q4: W is 4-bit bytes
+// stored [d_out, d_in] with fp32 scales wscale [d_out][lds] (SGMV only).
+hipError_t run_fused(const lora_pool_s* pool, lora_mode_t m, const void* x, int64_t ldx, const void* W,
+                     int64_t ldw, bool w_out_in, const float* wscale, int64_t lds, const int32_t* ids,
+                     const lora_segments_t* seg, int32_t n_rows, void* y, lora_dtype_t y_dtype, int64_t ldy,
+                     void* ws, hipStream_t stream) {
+    const PoolDev& P = pool->dev;
+    const int eb = elem_bytes(pool->dtype);
+    uint8_t* base = (uint8_t*)ws;
+    float* t = (float*)base;
+    const int64_t ldt = t_stride(P.r_max);
+    void* t_ext = base + align_up((size_t)n_rows * ldt * 4, 256);
+    const int64_t lde = ext_cols(eb, P.r_max);
+    const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256) + ext_bytes(pool, n_rows);
+    hipError_t e = hipSuccess;
+    const int32_t* gemm_perm = nullptr;   // SGMV: the GEMM visits rows grouped by adapter
+    if (m == LORA_MODE_BGMV) {
+        BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
+        e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, plan, stream, t_ext, lde);
+    } else {
+        lora_segments_t own;
+        const lora_segments_t* sg = seg;
+        const SegLayout SL = seg_layout(after_t, n_rows, P.n_adapters);
+        float* part = sgmv_shrink_part_bytes(P, n_rows) ? (float*)(base + SL.end) : nullptr;
+        if (!sg) {
+            SegLayout L = SL;
+            own.perm = (int32_t*)(base + L.perm);
+            own.seg_ids = (int32_t*)(base + L.seg_ids);
+            own.seg_off = (int32_t*)(base + L.seg_off);
+            own.n_seg = (int32_t*)(base + L.n_seg);
+            own.cap = L.cap;
+            e = launch_segments(ids, n_rows, P.n_adapters, &own, P.err, stream);
+            sg = &own;
+        }
+        if (e == hipSuccess)
+            e = launch_sgmv_shrink(P, pool->dtype, x, ldx, sg, n_rows, P.n_adapters + 1, t, ldt, true,
+                                   stream, t_ext, lde, ids, part);
+        if ((int64_t)n_rows * ldx * eb < ((int64_t)1 << 31)) gemm_perm = sg->perm;
+    }
+    if (e != hipSuccess) return e;
+    GemmArgs g;
+    g.x = x;
+    g.ldx = ldx;
+    g.W = W;
+    g.ldw = ldw;
+    g.w_out_in = w_out_in ? 1 : 0;
+    g.w_q4 = wscale != nullptr;
+    g.wscale = wscale;
+    g.lds = lds;
+    g.ids = ids;
+    g.n_rows = n_rows;
+    g.t = t;
+    g.ldt = ldt;
+    g.t_ext = t_ext;
+    g.lde = lde;
+    g.y = y;
+    g.ldy = ldy;
+    g.vec_x = true;
+    g.vec_w = true;
+    g.rows_distinct = (m == LORA_MODE_BGMV);
+    g.perm = gemm_perm;
+    g.x_rows = n_rows;
+    return launch_layer_gemm(P, pool->dtype, y_dtype, g, stream);
+}
+
 lora_mode_t resolve_mode(lora_mode_t m, int32_t n_rows, int32_t n_adapters) {
     if (m != LORA_MODE_AUTO) return m;
     return (n_rows <= 64 || n_rows <= 2 * (int64_t)n_adapters) ? LORA_MODE_BGMV : LORA_MODE_SGMV;
@@ -538,58 +604,8 @@ lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx, con
         return dev_status(
             run_rows(pool, x, ldx, W, ldw, nullptr, 0, false, ids, seg, n_rows, y, y_dtype, ldy, ws, stream));
     }
-    uint8_t* base = (uint8_t*)ws;
-    float* t = (float*)base;
-    const int64_t ldt = t_stride(P.r_max);
-    void* t_ext = base + align_up((size_t)n_rows * ldt * 4, 256);
-    const int64_t lde = ext_cols(eb, P.r_max);
-    const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256) + ext_bytes(pool, n_rows);
-    hipError_t e = hipSuccess;
-    const int32_t* gemm_perm = nullptr;   // SGMV: the GEMM visits rows grouped by adapter
-    if (m == LORA_MODE_BGMV) {
-        BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
-        e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, plan, stream, t_ext, lde);
-    } else {
-        lora_segments_t own;
-        const lora_segments_t* sg = seg;
-        const SegLayout SL = seg_layout(after_t, n_rows, P.n_adapters);
-        float* part = sgmv_shrink_part_bytes(P, n_rows) ? (float*)(base + SL.end) : nullptr;
-        if (!sg) {
-            SegLayout L = SL;
-            own.perm = (int32_t*)(base + L.perm);
-            own.seg_ids = (int32_t*)(base + L.seg_ids);
-            own.seg_off = (int32_t*)(base + L.seg_off);
-            own.n_seg = (int32_t*)(base + L.n_seg);
-            own.cap = L.cap;
-            e = launch_segments(ids, n_rows, P.n_adapters, &own, P.err, stream);
-            sg = &own;
-        }
-        if (e == hipSuccess)
-            e = launch_sgmv_shrink(P, pool->dtype, x, ldx, sg, n_rows, P.n_adapters + 1, t, ldt, true,
-                                   stream, t_ext, lde, ids, part);
-        if ((int64_t)n_rows * ldx * eb < ((int64_t)1 << 31)) gemm_perm = sg->perm;
-    }
-    if (e != hipSuccess) return LORA_E_DEVICE;
-    GemmArgs g;
-    g.x = x;
-    g.ldx = ldx;
-    g.W = W;
-    g.ldw = ldw;
-    g.w_out_in = (w_layout == LORA_W_OUT_IN) ? 1 : 0;
-    g.ids = ids;
-    g.n_rows = n_rows;
-    g.t = t;
-    g.ldt = ldt;
-    g.t_ext = t_ext;
-    g.lde = lde;
-    g.y = y;
-    g.ldy = ldy;
-    g.vec_x = true;
-    g.vec_w = true;
-    g.rows_distinct = (m == LORA_MODE_BGMV);
-    g.perm = gemm_perm;
-    g.x_rows = n_rows;
-    return dev_status(launch_layer_gemm(P, pool->dtype, y_dtype, g, stream));
+    return dev_status(run_fused(pool, m, x, ldx, W, ldw, w_layout == LORA_W_OUT_IN, nullptr, 0, ids, seg, n_rows, y,
+                                y_dtype, ldy, ws, stream));
 }
 
 lora_status_t lora_layer_apply_noalloc(lora_pool_t pool, const void* x, int64_t ldx, const void* W,
@@ -779,6 +795,7 @@ lora_status_t lora_layer_q4_workspace(lora_pool_t pool, int32_t n_rows, size_t* 
         return LORA_OK;
     }
     if (pool->dev.n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
+    if (n_rows > kRowsMaxRows) return lora_layer_workspace(pool, n_rows, LORA_MODE_SGMV, bytes);
     *bytes = rows_ws_bytes(pool, n_rows, true);
     return LORA_OK;
 }
@@ -827,6 +844,9 @@ lora_status_t lora_layer_apply_q4(lora_pool_t pool, const void* x, int64_t ldx, 
         if (e == hipSuccess) e = launch_decode_finish(P, D, g, y_dtype, stream);
         return dev_status(e);
     }
+    if (n_rows > kRowsMaxRows)
+        return dev_status(run_fused(pool, LORA_MODE_SGMV, x, ldx, Wq, ldq, true, w_scale, lds, ids, seg, n_rows, y,
+                                    y_dtype, ldy, ws, stream));
     return dev_status(run_rows(pool, x, ldx, Wq, ldq, w_scale, lds, true, ids, seg, n_rows, y, y_dtype, ldy, ws,
                                stream));
 }

@@ -58,13 +58,9 @@ __device__ __forceinline__ bf16x8_t ld8_guard(const bf16* p, int valid) {
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quieted).
-__device__ __forceinline__ bf16 f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quieted).  The
+// conversion instruction (v_cvt_pk_bf16_f32 on gfx950) does exactly this.
+__device__ __forceinline__ bf16 f32_to_bf16(float f) { return __builtin_bit_cast(bf16, (__bf16)f); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
@@ -273,6 +269,11 @@ struct GemmArgs {
     // adapters.  x_rows: rows x holds (0: n_rows).  Needs x under 2 GiB.
     const int32_t* perm = nullptr;
     int32_t x_rows = 0;
+    // 4-bit W (stored [d_out, d_in], bf16 pool): W holds bytes, ldw bytes per
+    // row; wscale [d_out][lds] fp32, one scale per output and 128 inputs
+    bool w_q4 = false;
+    const float* wscale = nullptr;
+    int64_t lds = 0;
 };
 hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt,
                              const GemmArgs& g, hipStream_t stream);

@@ -569,6 +569,64 @@ struct GemmDev {
     // (null: row m); x holds x_rows addressable rows
     const int32_t* perm;
     int32_t x_rows;
+    // 4-bit W (k_layer_gemm<..., Q4>): W is bytes [d_out][ldw], the scale of
+    // inputs 128 g .. 128 g + 127 of output n is wscale[n * lds + g]
+    const float* wscale;
+    int64_t lds;
+};
+
+// Eight signed 4-bit values (element e in bits 4e .. 4e+3) times `sc`, each
+// product rounded once to bf16 (the conversion instruction takes two at a time).
+__device__ __forceinline__ uint4 widen8_q4_scaled(uint32_t w, float sc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int q0 = ((int)(w << (28 - 8 * h))) >> 28;
+        const int q1 = ((int)(w << (24 - 8 * h))) >> 28;
+        const bf16x2_t v = {(__bf16)((float)q0 * sc), (__bf16)((float)q1 * sc)};
+        o[h] = __builtin_bit_cast(uint32_t, v);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// 4-bit W rows of a tile ([d_out, d_in] storage): one BK-deep block of BN
+// rows is BN x BK/2 bytes.  A thread takes QB bytes (2 QB consecutive
+// inputs) of one row through a buffer resource over the tile's rows (rows
+// past the range read as 0), and that row's scale of the block's 128-input
+// group; it stores them to the LDS tile widened, bf16(q * scale).
+template <class C>
+struct Q4WLoader {
+    static constexpr int RB = C::BK / 2;              // bytes of a row per block
+    static constexpr int QB = C::BN * RB / C::NT;     // bytes per thread
+    static constexpr int PPR = RB / QB;               // pieces per row
+    static_assert((QB == 8 || QB == 16) && PPR * QB == RB && C::NT % PPR == 0 && 128 % C::BK == 0,
+                  "4-bit pieces of 8 or 16 bytes, one scale group per block");
+    uint32_t q[QB / 4];
+    float sc;
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t rs, int64_t ldq, const float* srow, int k0,
+                                             int tid) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+        const int voff = (int)((int64_t)(tid / PPR) * ldq) + (tid % PPR) * QB;
+        if constexpr (QB == 16) {
+            const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, k0 / 2, 0);
+            q[0] = v.x;
+            q[1] = v.y;
+            q[2] = v.z;
+            q[3] = v.w;
+        } else {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, k0 / 2, 0);
+            q[0] = v.x;
+            q[1] = v.y;
+        }
+        sc = srow[k0 >> 7];
+    }
+    __device__ __forceinline__ void store(bf16* s, int tid) const {
+        bf16* d = s + (tid / PPR) * C::LDK + (tid % PPR) * QB * 2;
+#pragma unroll
+        for (int h = 0; h < QB / 4; ++h) *(uint4*)(d + h * 8) = widen8_q4_scaled(q[h], sc);
+    }
 };
 
 // VE consecutive outputs of one row, rounded once; 8-, 16- or 32-byte
@@ -791,9 +849,12 @@ __device__ __forceinline__ void gather_epilogue(const PoolDev& P, const GemmDev&
 // shrink; rows of other adapters masked to 0)
 // and whose B side is B_u[j][n0:n0+BN] (each rank row twice for bf16, to
 // meet the hi and the lo half).  y is rounded once at the end.
-template <class C, typename TY, bool OUT_IN>
+// Q4 (with OUT_IN, bf16 x and adapters): W is 4-bit, widened into the LDS
+// tile as bf16(q * scale) (Q4WLoader); d_in is a multiple of 128.
+template <class C, typename TY, bool OUT_IN, bool Q4 = false>
 __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     using T = typename C::T;
+    static_assert(!Q4 || (OUT_IN && sizeof(T) == 2), "4-bit W: bf16, stored [d_out, d_in]");
     // K-extension only where a K-block is one t_ext block; other tile shapes
     // always take the row-wise epilogue
     constexpr bool EXT = C::BK == ext_block_cols(sizeof(T)) && C::KH == EXT_RANKS;
@@ -933,13 +994,21 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     const T* TE = (const T*)g.t_ext;
     RowLoader<C, C::BM> la;
     BLoader<C> lb;
-    RowLoader<C, C::BN> lw;   // W rows (OUT_IN) share the B register set's shape
+    // W rows (OUT_IN) share the B register set's shape; 4-bit rows their own
+    using WLoader = typename std::conditional<Q4, Q4WLoader<C>, RowLoader<C, C::BN>>::type;
+    WLoader lw;
     auto load_main = [&](int s) {
         if (g.perm) la.load(X, g.ldx, sRowA, s * C::BK, K, tid);
         else la.load_direct(X, g.ldx, m0, g.n, s * C::BK, K, tid);
-        if constexpr (OUT_IN) lw.load_direct(Wp, g.ldw, n0, N, s * C::BK, K, tid);
-        else if constexpr (sizeof(T) == 2) lb.load_trans_pairs(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
-        else lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
+        if constexpr (Q4) {
+            // not reached: a 4-bit K is whole blocks (the loop below takes them all)
+        } else if constexpr (OUT_IN) {
+            lw.load_direct(Wp, g.ldw, n0, N, s * C::BK, K, tid);
+        } else if constexpr (sizeof(T) == 2) {
+            lb.load_trans_pairs(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
+        } else {
+            lb.load_trans(Wp, g.ldw, s * C::BK, C::BK, K, n0, N, true, tid);
+        }
     };
     constexpr bool PAIRS = sizeof(T) == 2;
     auto load_ext = [&](int s) {
@@ -978,12 +1047,23 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
         const int a_base = g.perm ? 0 : m0;
         const int a_rows = g.perm ? g.x_rows : max(0, min(C::BM, g.n - m0));
         const __amdgpu_buffer_rsrc_t rs_a = rsrc(X + (int64_t)a_base * g.ldx, a_rows, g.ldx);
-        const __amdgpu_buffer_rsrc_t rs_w = rsrc(Wp + (int64_t)n0 * g.ldw, max(0, min(C::BN, N - n0)), g.ldw);
+        // W: the tile's rows (4-bit: bytes, a row of ldw bytes; the scale row
+        // of this thread's W row, clamped into W's rows)
+        const __amdgpu_buffer_rsrc_t rs_w =
+            Q4 ? rsrc((const T*)((const uint8_t*)g.W + (int64_t)n0 * g.ldw), max(0, min(C::BN, N - n0)),
+                      g.ldw / (int64_t)sizeof(T))
+               : rsrc(Wp + (int64_t)n0 * g.ldw, max(0, min(C::BN, N - n0)), g.ldw);
+        const float* srow = nullptr;
+        if constexpr (Q4) srow = g.wscale + (int64_t)min(n0 + tid / Q4WLoader<C>::PPR, N - 1) * g.lds;
         int a_off[RowLoader<C, C::BM>::NV];
         la.row_offsets(sRowA, a_base, g.ldx, (int)((int64_t)a_rows * g.ldx * (int64_t)sizeof(T)), tid, a_off);
+        auto load_w = [&](WLoader& l, int s) __attribute__((always_inline)) {
+            if constexpr (Q4) l.load_buf(rs_w, g.ldw, srow, s * C::BK, tid);
+            else l.load_buf(rs_w, g.ldw, s * C::BK, tid);
+        };
         auto load_full = [&](int s) {
             la.load_buf_off(rs_a, a_off, s * C::BK, tid);
-            lw.load_buf(rs_w, g.ldw, s * C::BK, tid);
+            load_w(lw, s);
         };
         auto step = [&](int kb) {
             T* sA = smem + (kb & 1) * C::STAGE;
@@ -999,10 +1079,10 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             // thread): two blocks in flight, in two register sets used
             // alternately (the loop is unrolled by two)
             RowLoader<C, C::BM> la2;
-            RowLoader<C, C::BN> lw2;
+            WLoader lw2;
             auto load_full2 = [&](int s) {
                 la2.load_buf_off(rs_a, a_off, s * C::BK, tid);
-                lw2.load_buf(rs_w, g.ldw, s * C::BK, tid);
+                load_w(lw2, s);
             };
             auto step2 = [&](int k) {
                 T* sA = smem + (k & 1) * C::STAGE;
@@ -2336,8 +2416,9 @@ using GemmF32 = Cfg<float, 64, 64, 32, 2, 2>;
 using ShrinkB = Cfg<bf16, 64, 64, 64, 4, 1>;
 using ShrinkF = Cfg<float, 64, 64, 32, 4, 1>;
 
-template <class C, typename TY>
+template <class C, typename TY, bool Q4 = false>
 hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
+    static_assert(!Q4 || sizeof(typename C::T) == 2, "4-bit W with bf16 tiles");
     GemmDev g;
     g.x = a.x;
     g.ldx = a.ldx;
@@ -2355,11 +2436,16 @@ hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     g.tiles_n = (int32_t)ceil_div(P.d_out, C::BN);
     g.perm = a.perm;
     g.x_rows = a.x_rows > 0 ? a.x_rows : a.n_rows;
+    g.wscale = a.wscale;
+    g.lds = a.lds;
     dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n));
-    if (a.w_out_in)
+    if constexpr (Q4) {
+        hipLaunchKernelGGL((k_layer_gemm<C, TY, true, true>), grid, dim3(C::NT), 0, stream, P, g);
+    } else if (a.w_out_in) {
         hipLaunchKernelGGL((k_layer_gemm<C, TY, true>), grid, dim3(C::NT), 0, stream, P, g);
-    else
+    } else {
         hipLaunchKernelGGL((k_layer_gemm<C, TY, false>), grid, dim3(C::NT), 0, stream, P, g);
+    }
     return hipGetLastError();
 }
 
@@ -2414,6 +2500,26 @@ GemmArgs rows_from(const GemmArgs& a, int32_t r0) {
 
 template <typename TY>
 hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream, bool tail = false) {
+    if (a.w_q4) {
+        // 4-bit W: 256x256 tiles (the row tiles past whole rounds in 128x128
+        // tiles when the last round would be mostly idle), else 128x128
+        auto tiles = [&](int bm, int bn) { return ceil_div(a.n_rows, bm) * ceil_div(P.d_out, bn); };
+        const int64_t th = tiles(GemmHuge::BM, GemmHuge::BN);
+        if (!tail && th >= 200) {
+            const int64_t tn = ceil_div(P.d_out, GemmHuge::BN);
+            const int64_t tm_h = (th / 256) * 256 / tn;
+            const int32_t r0 = (int32_t)(tm_h * GemmHuge::BM);
+            if (tm_h > 0 && r0 < a.n_rows && ceil_div(tm_h * tn, 256) < ceil_div(th, 256)) {
+                GemmArgs h = a;
+                h.n_rows = r0;
+                const hipError_t e = run_gemm<GemmHuge, TY, true>(P, h, stream);
+                if (e != hipSuccess) return e;
+                return run_gemm_bf16<TY>(P, rows_from<TY>(a, r0), stream, true);
+            }
+            return run_gemm<GemmHuge, TY, true>(P, a, stream);
+        }
+        return run_gemm<GemmBig, TY, true>(P, a, stream);
+    }
     if (a.w_out_in && a.n_rows <= 64 && !a.t_ext && !a.perm) {
         if (a.n_rows <= 16) return run_skinny<TY, 1>(P, a, stream);
         if (a.n_rows <= 32) return run_skinny<TY, 2>(P, a, stream);

@@ -156,7 +156,9 @@ def test_q4_decode_ragged_pool_fp32_y():
     (65, 1024, 776, wl.UNIFORM, 16, 30, None),                    # segment-tile path
     (300, 2048, 1032, wl.RAGGED, [8, 16, 32, 64, 1, 3, 24, 40], 8, None),
     (700, 1536, 520, wl.UNIFORM, 64, 5, [300, 7, 200, 1, 64, 65, 63]),
-    (1100, 1024, 640, wl.RAGGED, [8, 16, 32, 64] * 3, 12, [500, 1, 300, 299]),   # SGMV shrink form
+    (1100, 1024, 640, wl.RAGGED, [8, 16, 32, 64] * 3, 12, [500, 1, 300, 299]),   # fused GEMM (past 1024 rows)
+    (1500, 2048, 1000, wl.RAGGED, [1, 3, 24, 40, 64, 16], 6, [700, 2, 300, 1, 497]),   # odd ranks, ragged d_out
+    (2100, 256, 6144, wl.UNIFORM, 32, 4, [1000, 600, 500]),     # 256 x 256 tiles of the fused GEMM
 ])
 @pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float32])
 def test_q4_layer_matches_oracle(n_rows, d_in, d_out, layout, ranks, n_ad, runs, ydt):
@@ -197,6 +199,28 @@ def test_q4_layer_agrees_with_bf16_layer_on_exact_weights():
                             y_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(y4, f64(yb), 1e-4, "q4 vs bf16 layer (fp32 y)")
+
+
+def test_q4_layer_past_1024_rows_agrees_with_bf16_layer_on_exact_weights():
+    """Past 1024 rows the 4-bit weight is widened to bf16(q * scale) in the
+    fused GEMM's tiles; with power-of-two scales that widening is exact, so
+    the 4-bit layer and the bf16 SGMV layer on the dequantized weight
+    compute the same function."""
+    b = binding()
+    d_in, d_out, n = 1024, 1536, 1300
+    w = wl.small_batch(seed=16, n_rows=n, d_in=d_in, d_out=d_out, n_adapters=6, ranks=64, dtype=torch.bfloat16,
+                       device=DEV, frac_base=0.05, run_lengths=[400, 300, 1, 599])
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    Wq, sc = wl.q4_weight(9, d_in, d_out, DEV, pow2_scales=True)
+    Wd = oracle.dequant_q4(Wq.cpu().numpy(), sc.cpu().double().numpy(), d_in)
+    Wb = torch.from_numpy(Wd.T.copy()).to(torch.bfloat16).to(DEV)
+    ids = torch.as_tensor(w.ids, device=DEV)
+    y4 = b.lora_layer_apply_q4(pool, p.x, Wq, sc, ids, y_dtype=torch.float32)
+    yb = b.lora_layer_apply(pool, p.x, Wb, ids, w_layout=b.LORA_W_OUT_IN, mode=b.LORA_MODE_SGMV,
+                            y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(y4, f64(yb), 1e-4, "q4 vs bf16 SGMV layer (fp32 y)")
 
 
 def test_q4_layer_small_batch_is_the_decode_pair():
