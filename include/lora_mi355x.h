@@ -385,14 +385,17 @@ lora_status_t lora_decode_finish(lora_pool_t pool, const int32_t* ids, int32_t n
  * lora_decode_stream_q4's (signed nibbles, one fp32 scale per output and 128
  * inputs); the adapter term is the bf16 one, unchanged.
  *   1..64 rows: lora_decode_stream_q4 + lora_decode_finish;
- *   more rows: segments (built in the workspace unless `seg` is given), the
- *     shrink per segment tile (past 1024 rows the SGMV shrink), the base
- *     product over 128 x 64 tiles whose 4-bit W blocks are widened exactly
- *     to bf16 in LDS (each 128-deep block is one scale group: its sums are
- *     scaled once and added), and the finish per segment tile (base partials
- *     + s * t B_a, y rounded once).
- * The workspace (lora_layer_q4_workspace) holds fp32 base partials of
- * n_rows * d_out * 4 bytes or more.  Requires a bf16 pool, d_in % 128 == 0,
+ *   65..1024 rows: segments (built in the workspace unless `seg` is given),
+ *     the shrink per segment tile, the base product over 128 x 64 tiles whose
+ *     4-bit W blocks are widened exactly to bf16 in LDS (each 128-deep block
+ *     is one scale group: its sums are scaled once and added), and the
+ *     finish per segment tile (base partials + s * t B_a, y rounded once);
+ *     the workspace holds fp32 base partials of n_rows * d_out * 4 bytes;
+ *   more rows: lora_layer_apply's SGMV form (segments, the SGMV shrink, one
+ *     fused GEMM over 256 x 256 tiles with the adapter term in its K loop)
+ *     whose W tiles are widened to bf16(q * scale), each weight rounded once
+ *     (at most 2^-9 of its value, the precision of a bf16 base weight).
+ * lora_layer_q4_workspace sizes the workspace.  Requires a bf16 pool, d_in % 128 == 0,
  * ldq >= d_in / 2 with ldq % 16 == 0, a 16-byte aligned Wq, a 4-byte aligned
  * w_scale and lds >= d_in / 128; otherwise LORA_E_UNSUPPORTED /
  * LORA_E_INVALID.  The other rules are lora_layer_apply's. */

@@ -100,17 +100,15 @@ bool rows_ok(const lora_pool_s* pool, int32_t n_rows) {
            pool->dev.n_adapters <= kMaxAdaptersSegments;
 }
 
-// workspace of the few-hundred-row path: segments, the plan's partials and
-// tile records, and (batches past the segment-tile shrink) the SGMV shrink's
-// K-split partials
+// workspace of the few-hundred-row path: segments, then the plan's partials
+// and row records
 size_t rows_ws_bytes(const lora_pool_s* pool, int32_t n_rows, bool q4 = false) {
     const RowsPlan R = plan_rows(pool->dev, n_rows, q4);
-    size_t b = align_up(seg_layout(0, n_rows, pool->dev.n_adapters).end, 256) + R.bytes;
-    if (!R.tile_shrink) b = align_up(b, 256) + sgmv_shrink_part_bytes(pool->dev, n_rows);
-    return b;
+    return align_up(seg_layout(0, n_rows, pool->dev.n_adapters).end, 256) + R.bytes;
 }
 
-// The few-hundred-row path (also the 4-bit base above decode sizes).  seg:
+// The few-hundred-row path, up to kRowsMaxRows rows (also the 4-bit base
+// there).  seg:
 // caller's segments of these ids, or NULL (built at the start of the
 // workspace).  q4: W is 4-bit bytes with fp32 scales wscale [d_out][lds].
 hipError_t run_rows(const lora_pool_s* pool, const void* x, int64_t ldx, const void* W, int64_t ldw,
@@ -134,12 +132,6 @@ hipError_t run_rows(const lora_pool_s* pool, const void* x, int64_t ldx, const v
     uint8_t* rb = base + align_up(L.end, 256);
     float* part = (float*)(rb + R.part_off);
     float* tpart = (float*)(rb + R.tpart_off);
-    if (e == hipSuccess && !R.tile_shrink) {
-        // long batches: t from the SGMV shrink (K split into its own partials)
-        float* sp = sgmv_shrink_part_bytes(P, n_rows) ? (float*)(rb + align_up(R.bytes, 256)) : nullptr;
-        e = launch_sgmv_shrink(P, pool->dtype, x, ldx, seg, n_rows, P.n_adapters + 1, tpart, R.rtp, true, stream,
-                               nullptr, 0, ids, sp);
-    }
     if (e == hipSuccess)
         e = launch_rows_adapter(P, R, x, ldx, ids, seg, n_rows, part, tpart, y, y_dtype, ldy, stream, true, false);
     if (e == hipSuccess) e = launch_rows_gemm(P, R, x, ldx, W, ldw, wscale, lds, q4, n_rows, part, stream);

@@ -283,7 +283,6 @@ hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt
 // over the segments of lora_segments_build (rows.hip).
 struct RowsPlan {
     int32_t shape;              // tile: 0 128 x 64, 1 256 x 128
-    int32_t tile_shrink;        // shrink per segment tile (else the SGMV shrink writes t)
     int32_t tiles_m, tiles_n;
     int32_t S, kslice;          // K slices of the base product
     int32_t St, ks_len;         // K slices of the shrink

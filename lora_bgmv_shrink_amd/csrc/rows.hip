@@ -50,7 +50,6 @@ namespace lora {
 namespace {
 
 constexpr int RG_KB = 128;            // K slices are whole 128-deep groups (the 4-bit scale group)
-constexpr int kRowsTileShrinkMax = 1024;   // rows the segment-tile shrink serves
 
 struct RowsGemmArgs {
     const bf16* x;
@@ -677,222 +676,6 @@ __global__ __launch_bounds__(FS_NT) void k_seg_finish(PoolDev P, SegFinishArgs a
     }
 }
 
-// Batches past the segment-tile shrink's range (the SGMV shrink forms t; a
-// request is hundreds of rows of one adapter): the finish runs per segment
-// tile of SS_ROWS rows, whose rows share B.  Per tile, written by
-// k_tile_recs: its rows in perm, and its adapter's rank (0: base-only rows),
-// scale and B offset; valid = 0 past the last tile.
-struct TileRec {
-    int64_t b_off;
-    int32_t valid, row0, cnt, rank;
-    float scale;
-    int32_t pad;
-};
-
-struct TileFinishArgs {
-    const TileRec* tiles;
-    const int32_t* ids;
-    const int32_t* perm;
-    const float* part;    // [S][M][ldp], ldp a multiple of 4
-    int64_t ldp;
-    int32_t S;
-    const float* tpart;   // [St][M][rtp]
-    int64_t rtp;
-    int32_t St;
-    int32_t M;
-    int32_t n_chunks;     // column chunks of FS_COLS
-    void* y;
-    int64_t ldy;
-};
-
-constexpr int TF_RPW = SS_ROWS / (FS_NT / 64);   // tile rows per wave
-
-// Workgroup (segment tile, FS_COLS columns), lane l: columns c .. c + 3.
-// The tile's t (rows x rank, summed over the shrink slices in order) is
-// formed in LDS from loads requested together.  Wave w produces the tile's
-// rows w, w + 4, ...: their base partials (every K slice; SB >= S, slices
-// past S clamped and masked) are requested together (one row at a time for
-// SB > 2, to fit the registers), and each FS_RC-row chunk of B (rows past r
-// clamped; they meet t = 0) is loaded once per wave and applied to all of
-// them, the first chunk before the barrier.  VEC as in k_seg_finish.
-template <typename TY, int SB, bool VEC>
-__global__ __launch_bounds__(FS_NT) void k_tile_finish(PoolDev P, TileFinishArgs a) {
-    constexpr int RP = SB <= 2 ? TF_RPW : 1;   // rows formed together
-    __shared__ float sT[SS_ROWS][64];
-    __shared__ int sRow[SS_ROWS];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int tile = blockIdx.x / a.n_chunks;
-    const int ch = blockIdx.x - tile * a.n_chunks;
-    const TileRec* rp = a.tiles + tile;
-    if (!uload(&rp->valid, 0)) return;
-    const int row0 = uload(&rp->row0, 0);
-    const int cnt = uload(&rp->cnt, 0);
-    const int r = uload(&rp->rank, 0);
-    const float sc = uload(&rp->scale, 0);
-    const int64_t boff = uload(&rp->b_off, 0);
-    if (tid < SS_ROWS) sRow[tid] = a.perm[row0 + min(tid, cnt - 1)];
-    const int N = P.d_out;
-    const int col = ch * FS_COLS + lane * FS_VE;
-    const int cc = col < N ? col : 0;   // lanes past d_out read column 0; nothing is stored
-
-    const bf16* __restrict__ Bu = (const bf16*)P.B + boff + cc;
-    const int rr = max(r, 1);
-    uint2 bv[FS_RC];
-    auto load_b = [&](int j0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < FS_RC; ++q) {
-            const bf16* src = Bu + (int64_t)min(j0 + q, rr - 1) * N;
-            if constexpr (VEC) {
-                bv[q] = *(const uint2*)src;
-            } else {
-                union { uint2 u; bf16 e[4]; } w;
-#pragma unroll
-                for (int e = 0; e < FS_VE; ++e) w.e[e] = src[cc + e < N ? e : 0];
-                bv[q] = w.u;
-            }
-        }
-    };
-    if (r > 0) load_b(0);
-    __syncthreads();   // sRow
-    if (r > 0) {
-        // t[m][j] for the SS_ROWS x 64 pairs v = tid + FS_NT q: the slices of
-        // every pair requested together (in groups of 4), added in order
-        constexpr int PPT = SS_ROWS * 64 / FS_NT;
-        const int64_t sl = (int64_t)a.M * a.rtp;
-        float t[PPT];
-#pragma unroll
-        for (int q = 0; q < PPT; ++q) t[q] = 0.f;
-        for (int k0 = 0; k0 < a.St; k0 += 4) {
-            float tv[PPT][4];
-#pragma unroll
-            for (int q = 0; q < PPT; ++q) {
-                const int v = tid + FS_NT * q;
-                const int m = v >> 6;
-                const int j = min(v & 63, (int)a.rtp - 1);
-                const float* tp = a.tpart + (int64_t)sRow[min(m, cnt - 1)] * a.rtp + j;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tv[q][e] = tp[(int64_t)min(k0 + e, a.St - 1) * sl];
-            }
-#pragma unroll
-            for (int q = 0; q < PPT; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t[q] += (k0 + e < a.St) ? tv[q][e] : 0.f;
-        }
-#pragma unroll
-        for (int q = 0; q < PPT; ++q) {
-            const int v = tid + FS_NT * q;
-            sT[v >> 6][v & 63] = ((v & 63) < r) ? t[q] : 0.f;
-        }
-    } else if (ch == 0 && tid < cnt) {
-        if (a.ids[sRow[tid]] != -1) flag_bad_id(P.err);   // invalid ids run as base-only rows
-    }
-    __syncthreads();
-    if (col >= N) return;
-
-    const int64_t slice = (int64_t)a.M * a.ldp;
-    TY* __restrict__ Y = (TY*)a.y;
-    for (int m0 = wave; m0 < cnt; m0 += (FS_NT / 64) * RP) {
-        float pv[RP][SB][FS_VE];
-#pragma unroll
-        for (int k = 0; k < RP; ++k) {
-            const int m = min(m0 + (FS_NT / 64) * k, cnt - 1);
-            const float* prow = a.part + (int64_t)sRow[m] * a.ldp + cc;
-#pragma unroll
-            for (int s = 0; s < SB; ++s) {
-                const float* q = prow + (int64_t)min(s, a.S - 1) * slice;
-                if constexpr (VEC) {
-                    const float4 f = *(const float4*)q;
-                    pv[k][s][0] = f.x; pv[k][s][1] = f.y; pv[k][s][2] = f.z; pv[k][s][3] = f.w;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < FS_VE; ++e) pv[k][s][e] = q[cc + e < N ? e : 0];
-                }
-            }
-        }
-        float ex[RP][FS_VE];
-#pragma unroll
-        for (int k = 0; k < RP; ++k)
-#pragma unroll
-            for (int e = 0; e < FS_VE; ++e) ex[k][e] = 0.f;
-        for (int j0 = 0; j0 < r;) {
-#pragma unroll
-            for (int q = 0; q < FS_RC; ++q) {
-                union { uint2 u; bf16 e[4]; } w;
-                w.u = bv[q];
-#pragma unroll
-                for (int k = 0; k < RP; ++k) {
-                    const float tj = sT[min(m0 + (FS_NT / 64) * k, cnt - 1)][min(j0 + q, 63)];   // 0 past r
-#pragma unroll
-                    for (int e = 0; e < FS_VE; ++e) ex[k][e] += tj * to_f32(w.e[e]);
-                }
-            }
-            j0 += FS_RC;
-            if (j0 >= r) break;
-            load_b(j0);
-        }
-        if (r > FS_RC && m0 + (FS_NT / 64) * RP < cnt) load_b(0);   // the next rows start from chunk 0 again
-#pragma unroll
-        for (int k = 0; k < RP; ++k) {
-            const int m = m0 + (FS_NT / 64) * k;
-            if (m >= cnt) break;
-            float o[FS_VE];
-#pragma unroll
-            for (int e = 0; e < FS_VE; ++e) o[e] = 0.f;
-#pragma unroll
-            for (int s = 0; s < SB; ++s)
-                if (s < a.S)
-#pragma unroll
-                    for (int e = 0; e < FS_VE; ++e) o[e] += pv[k][s][e];
-#pragma unroll
-            for (int e = 0; e < FS_VE; ++e) o[e] += sc * ex[k][e];
-            TY* yr = Y + (int64_t)sRow[m] * a.ldy + col;
-            if constexpr (VEC) {
-                if constexpr (sizeof(TY) == 2) {
-                    union { uint2 u; bf16 e[4]; } w;
-#pragma unroll
-                    for (int e = 0; e < FS_VE; ++e) w.e[e] = f32_to_bf16(o[e]);
-                    *(uint2*)yr = w.u;
-                } else {
-                    *(float4*)yr = make_float4(o[0], o[1], o[2], o[3]);
-                }
-            } else {
-                for (int e = 0; e < FS_VE && col + e < N; ++e) yr[e] = from_f32<TY>(o[e]);
-            }
-        }
-    }
-}
-
-// Tile records without the segment-tile shrink (when the SGMV shrink forms
-// t): one wave per tile finds its segment and writes the record.
-__global__ __launch_bounds__(64) void k_tile_recs(PoolDev P, const int32_t* __restrict__ seg_ids,
-                                                  const int32_t* __restrict__ seg_off,
-                                                  const int32_t* __restrict__ n_seg, TileRec* __restrict__ tiles) {
-    const int lane = threadIdx.x;
-    int s = 0, c = 0;
-    const bool found = find_seg_tile(seg_off, *n_seg, SS_ROWS, blockIdx.x, lane, s, c);
-    if (lane != 0) return;
-    TileRec rec;
-    rec.pad = 0;
-    if (!found) {
-        rec.valid = 0;
-        rec.b_off = 0;
-        rec.row0 = rec.cnt = rec.rank = 0;
-        rec.scale = 0.f;
-    } else {
-        const int u = seg_ids[s];
-        const bool ok = id_ok(u, P.n_adapters);
-        rec.valid = 1;
-        rec.row0 = seg_off[s] + c * SS_ROWS;
-        rec.cnt = min(SS_ROWS, seg_off[s + 1] - rec.row0);
-        rec.b_off = ok ? P.b_off[u] : 0;
-        rec.rank = ok ? P.ranks[u] : 0;
-        rec.scale = ok ? P.scales[u] : 0.f;
-    }
-    tiles[blockIdx.x] = rec;
-}
-
 // segment tiles of SS_ROWS rows: at most one partial tile per segment on top
 // of the full ones (the grid is sized without reading the segment count)
 int64_t rows_tiles(int32_t n_rows, int32_t n_bins) {
@@ -930,15 +713,9 @@ RowsPlan plan_rows(const PoolDev& P, int32_t n_rows, bool q4) {
     R.ks_len = ks_len;
     R.St = (int32_t)ceil_div(K, ks_len);
     R.rtp = (int64_t)align_up((size_t)P.r_max, 4);
-    // batches past the segment-tile shrink's range take the SGMV shrink,
-    // which writes t itself (one slice)
-    R.tile_shrink = n_rows <= kRowsTileShrinkMax ? 1 : 0;
-    if (!R.tile_shrink) R.St = 1;
     const size_t part = align_up((size_t)R.S * n_rows * R.ldp * 4, 256);
     const size_t tpart = align_up((size_t)R.St * n_rows * R.rtp * 4, 256);
-    // row records (segment-tile shrink) or tile records (SGMV shrink)
-    const size_t recs = R.tile_shrink ? align_up((size_t)n_rows * sizeof(RowRec), 256)
-                                      : align_up((size_t)rows_tiles(n_rows, P.n_adapters + 1) * sizeof(TileRec), 256);
+    const size_t recs = align_up((size_t)n_rows * sizeof(RowRec), 256);   // the finish's row records
     R.part_off = 0;
     R.tpart_off = part;
     R.recs_off = part + tpart;
@@ -979,14 +756,7 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
     const int n_bins = P.n_adapters + 1;
     // the row records follow the t partials (RowsPlan::recs_off)
     RowRec* recs = (RowRec*)((uint8_t*)tpart + (R.recs_off - R.tpart_off));
-    if (shrink && !R.tile_shrink) {
-        // t comes from the SGMV shrink (tpart is t, one slice); only the records
-        TileRec* tiles = (TileRec*)((uint8_t*)tpart + (R.recs_off - R.tpart_off));
-        hipLaunchKernelGGL(k_tile_recs, dim3((unsigned)rows_tiles(n_rows, n_bins)), dim3(64), 0, stream, P,
-                           seg->seg_ids, seg->seg_off, seg->n_seg, tiles);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    } else if (shrink) {
+    if (shrink) {
         SegShrinkArgs s;
         s.recs = recs;
         s.ids = ids;
@@ -1009,42 +779,6 @@ hipError_t launch_rows_adapter(const PoolDev& P, const RowsPlan& R, const void* 
         hipLaunchKernelGGL(k_seg_shrink, grid, dim3(SS_NT), lds, stream, P, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-    }
-    if (finish && !R.tile_shrink) {
-        TileFinishArgs f;
-        f.tiles = (const TileRec*)((uint8_t*)tpart + (R.recs_off - R.tpart_off));
-        f.ids = ids;
-        f.perm = seg->perm;
-        f.part = part;
-        f.ldp = R.ldp;
-        f.S = R.S;
-        f.tpart = tpart;
-        f.rtp = R.rtp;
-        f.St = R.St;
-        f.M = n_rows;
-        f.n_chunks = (int32_t)ceil_div(P.d_out, FS_COLS);
-        f.y = y;
-        f.ldy = ldy;
-        dim3 grid((unsigned)(rows_tiles(n_rows, n_bins) * f.n_chunks));
-        const bool vec = P.vec_b != 0;
-#define LORA_TFIN(TY_, SB_)                                                                                \
-    do {                                                                                                   \
-        if (vec) hipLaunchKernelGGL((k_tile_finish<TY_, SB_, true>), grid, dim3(FS_NT), 0, stream, P, f);  \
-        else hipLaunchKernelGGL((k_tile_finish<TY_, SB_, false>), grid, dim3(FS_NT), 0, stream, P, f);     \
-    } while (0)
-        if (ydt == LORA_BF16) {
-            if (R.S <= 1) LORA_TFIN(bf16, 1);
-            else if (R.S <= 2) LORA_TFIN(bf16, 2);
-            else if (R.S <= 4) LORA_TFIN(bf16, 4);
-            else LORA_TFIN(bf16, 8);
-        } else {
-            if (R.S <= 1) LORA_TFIN(float, 1);
-            else if (R.S <= 2) LORA_TFIN(float, 2);
-            else if (R.S <= 4) LORA_TFIN(float, 4);
-            else LORA_TFIN(float, 8);
-        }
-#undef LORA_TFIN
-        return hipGetLastError();
     }
     if (finish) {
         SegFinishArgs f;
