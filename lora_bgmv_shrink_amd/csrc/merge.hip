@@ -30,6 +30,7 @@ constexpr int MG_LDT = MG_COLS + 4;           // fp32 pitch of the staged produc
 constexpr int MG_PIECES = MG_ROWS * MG_COLS / 8 / MG_THREADS;   // 16-byte W pieces per thread
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // element offset of (rank j, column c) in a staged [64][NC] block of B_a:
 // 32-byte units XOR-swizzled per row so that the rows one transpose read
@@ -238,6 +239,219 @@ __global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     }
 }
 
+// Whole tiles (the stored rows a multiple of 64, the stored columns of 128)
+// and 16-byte A_a and B_a pieces: the same update with no bounds branch.
+// A workgroup takes a run of consecutive tiles numbered column-major, so the
+// run keeps its stored columns, on which one operand depends (OUT_IN: A_a,
+// whose fragments stay in registers; IN_OUT: B_a, whose staged block stays
+// in LDS); the next tile's W pieces and its other operand are requested
+// before the current tile is worked on.  Every load of a tile goes out
+// unconditionally (ranks past r read rank 0 of their row; the values are
+// masked where they are used), so the loads stay in flight together and a
+// wait for one of them does not wait for the next tile's.
+template <bool OUT_IN>
+__global__ __launch_bounds__(MG_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void k_merge_bf16_run(
+    PoolDev P, int32_t adapter, float sign, bf16* __restrict__ W, int64_t ldw, int32_t tiles_r, int32_t n_tiles) {
+    constexpr int NC = OUT_IN ? MG_ROWS : MG_COLS;   // c values per tile
+    constexpr int NAF = OUT_IN ? 4 : 2;              // A_a fragments per rank step
+    constexpr int BPR = NC / 8;                      // 16-byte pieces per B_a row
+    constexpr int BPT = 64 * BPR / MG_THREADS;       // B_a pieces per thread
+    __shared__ __attribute__((aligned(16))) bf16 sB[64 * NC];
+    __shared__ __attribute__((aligned(16))) float sAcc[MG_ROWS * MG_LDT];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave >> 1;   // 32-row half of the tile
+    const int wc = wave & 1;    // 64-column half of the tile
+    const int lr = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int r = uload(P.ranks, adapter);
+    const float s = sign * uload(P.scales, adapter);
+    const bf16* Aa = (const bf16*)P.A + uload(P.a_off, adapter);
+    const bf16* Ba = (const bf16*)P.B + uload(P.b_off, adapter);
+    const int d_out = P.d_out;
+    const int steps = (r + 31) / 32;   // 32 ranks per MFMA step
+
+    auto tile_at = [&](int t, int& row0, int& col0) __attribute__((always_inline)) {
+        const int tc = t / tiles_r;
+        row0 = (t - tc * tiles_r) * MG_ROWS;
+        col0 = tc * MG_COLS;
+    };
+    auto load_w = [&](u32x4_t (&w)[MG_PIECES], int t) __attribute__((always_inline)) {
+        int row0, col0;
+        tile_at(t, row0, col0);
+#pragma unroll
+        for (int p = 0; p < MG_PIECES; ++p) {
+            const Piece q = piece_of(tid, p);
+            w[p] = *(const u32x4_t*)(W + (int64_t)(row0 + q.row) * ldw + col0 + q.col);
+        }
+    };
+    // A_a fragments of tile t: lane l takes row/column l % 16 of its block
+    // and ranks (l / 16) * 8 .. + 8 of each 32-rank step
+    auto load_a = [&](bf16x8_t (&a)[2][NAF], int t) __attribute__((always_inline)) {
+        int row0, col0;
+        tile_at(t, row0, col0);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if (st >= steps) break;
+            const int j = st * 32 + kq;
+#pragma unroll
+            for (int f = 0; f < NAF; ++f) {
+                const int k = OUT_IN ? col0 + wc * 64 + f * 16 + lr : row0 + wr * 32 + f * 16 + lr;
+                a[st][f] = *(const bf16x8_t*)(Aa + (int64_t)k * r + (j < r ? j : 0));
+            }
+        }
+    };
+    // B_a[j][c] pieces of the tile's c range, as they lie
+    auto load_b = [&](u32x4_t (&b)[BPT], int t) __attribute__((always_inline)) {
+        int row0, col0;
+        tile_at(t, row0, col0);
+        const int c0 = OUT_IN ? row0 : col0;
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            const int idx = tid + q * MG_THREADS;
+            const int j = idx / BPR;
+            const int c = (idx - j * BPR) * 8;
+            b[q] = *(const u32x4_t*)(Ba + (int64_t)(j < r ? j : 0) * d_out + c0 + c);
+        }
+    };
+    // -> sB; ranks past r are 0 up to the last 32-rank step
+    auto stage_b = [&](const u32x4_t (&b)[BPT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            const int idx = tid + q * MG_THREADS;
+            const int j = idx / BPR;
+            if (j >= 32 * steps) continue;
+            const int c = (idx - j * BPR) * 8;
+            *(u32x4_t*)(sB + mg_b_at<NC>(j, c)) = j < r ? b[q] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    // transpose-read operand: columns cb .. cb + 15 of the staged block,
+    // ranks j0 + (l / 16) * 8 .. + 8
+    const int b_lane = ((lane >> 4) * 8 + (lr >> 2)) * NC + (lr & 3) * 4;
+    const int b_sw = NC == 128 ? ((lr >> 2) | (((lane >> 4) & 1) << 2)) : ((lr >> 2) ^ ((lane >> 4) & 1));
+    auto b_frag = [&](int cb, int j0) __attribute__((always_inline)) {
+        const bf16* q = sB + b_lane + j0 * NC + (((cb >> 4) ^ b_sw) << 4);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)q);
+        const i16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(q + 4 * NC));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // the tile's product on the matrix cores into sAcc (W's layout), then
+    // W + s * product per piece, rounded once.  The A_a fragments and W
+    // pieces are made opaque where they are used, so that nothing derived
+    // from them (and no wait for them) moves up to their loads.
+    auto work_tile = [&](int row0, int col0, bf16x8_t (&a)[2][NAF], u32x4_t (&w)[MG_PIECES])
+                         __attribute__((always_inline)) {
+        f32x4_t acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) acc[i][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if (st >= steps) break;
+            const int j0 = st * 32;
+            const bool aok = j0 + kq < r;
+            bf16x8_t Am[NAF];
+#pragma unroll
+            for (int f = 0; f < NAF; ++f) {
+                bf16x8_t v = a[st][f];
+                asm volatile("" : "+v"(v));
+                Am[f] = aok ? v : bf16x8_t{};
+            }
+            bf16x8_t L[2], R[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) L[i] = OUT_IN ? b_frag(wr * 32 + i * 16, j0) : Am[i % NAF];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) R[jb] = OUT_IN ? Am[jb % NAF] : b_frag(wc * 64 + jb * 16, j0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+                    acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(L[i], R[jb], acc[i][jb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sAcc[(wr * 32 + i * 16 + (lane >> 4) * 4 + q) * MG_LDT + wc * 64 + jb * 16 + lr] = acc[i][jb][q];
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < MG_PIECES; ++p) {
+            const Piece q = piece_of(tid, p);
+            const float* pr = sAcc + q.row * MG_LDT + q.col;
+            union { u32x4_t u; bf16 e[8]; } v;
+            v.u = w[p];
+            asm volatile("" : "+v"(v.u));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v.e[e] = f32_to_bf16(to_f32(v.e[e]) + s * pr[e]);
+            *(u32x4_t*)(W + (int64_t)(row0 + q.row) * ldw + col0 + q.col) = v.u;
+        }
+    };
+
+    const int t_beg = (int)((int64_t)blockIdx.x * n_tiles / gridDim.x);
+    const int t_end = (int)((int64_t)(blockIdx.x + 1) * n_tiles / gridDim.x);
+    if (t_beg >= t_end) return;
+    u32x4_t wv[MG_PIECES], wn[MG_PIECES];
+    bf16x8_t Ag[2][NAF];
+    int held = -1;   // stored columns of the operand held along the run
+    if constexpr (OUT_IN) {
+        u32x4_t bv[BPT], bn[BPT];
+        load_w(wv, t_beg);
+        load_b(bv, t_beg);
+        for (int t = t_beg; t < t_end; ++t) {
+            int row0, col0;
+            tile_at(t, row0, col0);
+            if (col0 != held) {   // the run enters other columns: their A_a fragments
+                held = col0;
+                load_a(Ag, t);
+            }
+            // the next tile (the last tile again at the end of the run: an
+            // unconditional request keeps every wait count exact)
+            const int tn = t + 1 < t_end ? t + 1 : t;
+            load_b(bn, tn);
+            load_w(wn, tn);
+            stage_b(bv);
+            __syncthreads();
+            work_tile(row0, col0, Ag, wv);
+#pragma unroll
+            for (int p = 0; p < MG_PIECES; ++p) wv[p] = wn[p];
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) bv[q] = bn[q];
+            __syncthreads();   // sB and sAcc are rewritten for the next tile
+        }
+    } else {
+        bf16x8_t An[2][NAF];
+        load_w(wv, t_beg);
+        load_a(Ag, t_beg);
+        for (int t = t_beg; t < t_end; ++t) {
+            int row0, col0;
+            tile_at(t, row0, col0);
+            if (col0 != held) {   // the run enters other columns: their B_a block
+                held = col0;
+                u32x4_t bt[BPT];
+                load_b(bt, t);
+                stage_b(bt);
+                __syncthreads();
+            }
+            const int tn = t + 1 < t_end ? t + 1 : t;
+            load_a(An, tn);
+            load_w(wn, tn);
+            work_tile(row0, col0, Ag, wv);
+#pragma unroll
+            for (int p = 0; p < MG_PIECES; ++p) wv[p] = wn[p];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int f = 0; f < NAF; ++f) Ag[st][f] = An[st][f];
+            __syncthreads();   // sAcc (and sB at a change of columns) is rewritten for the next tile
+        }
+    }
+}
+
 // fp32: each thread updates four consecutive stored elements, summing over
 // the rank in order.
 template <bool OUT_IN>
@@ -280,9 +494,20 @@ hipError_t launch_merge(const PoolDev& P, lora_dtype_t dt, int32_t adapter, floa
         // about three workgroups per CU (the LDS of one is ~52 KiB), each
         // walking its share of the tiles
         const int tiles_c = (int)ceil_div(n_cols, MG_COLS);
-        const int64_t n_tiles = ceil_div(n_rows, MG_ROWS) * tiles_c;
+        const int tiles_r = (int)ceil_div(n_rows, MG_ROWS);
+        const int64_t n_tiles = (int64_t)tiles_r * tiles_c;
         dim3 grid((unsigned)std::min<int64_t>(n_tiles, 768));
-        if (out_in)
+        // whole tiles and 16-byte A_a and B_a pieces take the branch-free kernel
+        const bool whole_tiles =
+            n_rows % MG_ROWS == 0 && n_cols % MG_COLS == 0 && P.vec_a && P.vec_b && P.vec_rank;
+        if (whole_tiles) {
+            if (out_in)
+                hipLaunchKernelGGL(k_merge_bf16_run<true>, grid, dim3(MG_THREADS), 0, stream, P, adapter, sign,
+                                   (bf16*)W, ldw, tiles_r, (int32_t)n_tiles);
+            else
+                hipLaunchKernelGGL(k_merge_bf16_run<false>, grid, dim3(MG_THREADS), 0, stream, P, adapter, sign,
+                                   (bf16*)W, ldw, tiles_r, (int32_t)n_tiles);
+        } else if (out_in)
             hipLaunchKernelGGL(k_merge_bf16<true>, grid, dim3(MG_THREADS), 0, stream, P, adapter, sign, (bf16*)W,
                                ldw, tiles_c, (int32_t)n_tiles);
         else
