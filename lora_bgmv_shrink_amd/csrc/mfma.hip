@@ -284,7 +284,12 @@ struct RowLoader {
             reg[v] = tmp.u;
         }
     }
-    // rows whose sId differs from u load zeros (the K-extension operand)
+    // the K-extension operand: rows whose sId is u; the others read row 0,
+    // and are zeroed here (MASK) or by store_masked.  Masking at the load
+    // made the compiler wait for each load before issuing the next; the GEMM
+    // over W stored [d_in, d_out] keeps it (its 256 x 256 tile spills more
+    // with the mask at the store).
+    template <bool MASK>
     __device__ __forceinline__ void load_masked(const T* __restrict__ base, int64_t ld, const int* sRow,
                                                 const int* sId, int u, int k0, int tid) {
 #pragma unroll
@@ -295,7 +300,18 @@ struct RowLoader {
             const int k = k0 + (idx - r * VPR) * C::VE;
             const bool ok = sId[r] == u;   // implies sRow[r] >= 0
             const uint4 val = *(const uint4*)(base + (int64_t)(ok ? sRow[r] : 0) * ld + k);
-            reg[v] = ok ? val : uint4{0u, 0u, 0u, 0u};
+            reg[v] = (!MASK || ok) ? val : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+    // store, rows whose sId differs from u as zeros
+    __device__ __forceinline__ void store_masked(T* s, const int* sId, int u, int tid) const {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = tid + v * C::NT;
+            if (TOT % C::NT != 0 && idx >= TOT) break;
+            const int r = idx / VPR;
+            const int c = (idx - r * VPR) * C::VE;
+            *(uint4*)(s + r * C::LDK + c) = sId[r] == u ? reg[v] : uint4{0u, 0u, 0u, 0u};
         }
     }
     __device__ __forceinline__ void store(T* s, int tid) const {
@@ -411,9 +427,33 @@ struct BLoader {
         cv = rest % T_VPR;
         p = lo + PF * (rest / T_VPR);
     }
+    // SPLIT: whole vectors (the usual case) go through a branch-free loop of
+    // their own.  A bounds branch around each load made the compiler wait for
+    // each load before issuing the next; the K-extension blocks of the GEMM
+    // over W stored [d_out, d_in] take SPLIT.  The GEMM over W stored
+    // [d_in, d_out] keeps the per-piece form: its 256 x 256 tile spills more
+    // with SPLIT.
+    template <bool SPLIT = false>
     __device__ __forceinline__ void load_trans_pairs(const T* __restrict__ base, int64_t ld, int j0, int kwrap,
                                                      int kmax, int n0, int N, bool vec, int tid) {
         const bool full = vec && n0 + C::BN <= N;
+        if (SPLIT && full) {
+#pragma unroll
+            for (int v = 0; v < P_NV; ++v) {
+                const int idx = tid + v * C::NT;
+                if (P_TOT % C::NT != 0 && idx >= P_TOT) break;
+                int p, cv;
+                pair_piece(idx, p, cv);
+                const int n = n0 + cv * VE;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = j0 + (2 * p + h) % kwrap;
+                    // a row at or past kmax reads row j0; the A side is exactly zero there
+                    reg[2 * v + h] = *(const uint4*)(base + (int64_t)(k < kmax ? k : j0) * ld + n);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int v = 0; v < P_NV; ++v) {
             const int idx = tid + v * C::NT;
@@ -423,10 +463,8 @@ struct BLoader {
             const int n = n0 + cv * VE;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int kr = 2 * p + h;
-                const int k = j0 + kr % kwrap;
+                const int k = j0 + (2 * p + h) % kwrap;
                 if (full) {
-                    // a row at or past kmax reads row j0; the A side is exactly zero there
                     reg[2 * v + h] = *(const uint4*)(base + (int64_t)(k < kmax ? k : j0) * ld + n);
                 } else {
                     union { uint4 u; T e[VE]; } tmp;
@@ -1015,9 +1053,10 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
         const int code = sExt[s];
         const int u = code >> 1;
         const int e = code & 1;
-        la.load_masked(TE, g.lde, sRowA, sId, u, e * C::BK, tid);
+        la.template load_masked<!OUT_IN>(TE, g.lde, sRowA, sId, u, e * C::BK, tid);
         if constexpr (PAIRS)
-            lb.load_trans_pairs((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
+            lb.template load_trans_pairs<OUT_IN>((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0,
+                                                 N, P.vec_b, tid);
         else
             lb.load_trans((const T*)P.B + P.b_off[u], N, e * C::KH, C::KH, P.ranks[u], n0, N, P.vec_b, tid);
     };
@@ -1148,7 +1187,8 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             const int kb = nk + e;
             T* sA = smem + (kb & 1) * C::STAGE;
             T* sB = sA + C::A_ELEMS;
-            la.store(sA, tid);
+            if constexpr (OUT_IN) la.store_masked(sA, sId, sExt[e] >> 1, tid);
+            else la.store(sA, tid);
             store_trans(sB);
             __syncthreads();
             if (e + 1 < n_ext) load_ext(e + 1);
