@@ -157,6 +157,7 @@ hipError_t run_fused(const lora_pool_s* pool, lora_mode_t m, const void* x, int6
     const size_t after_t = align_up((size_t)n_rows * ldt * 4, 256) + ext_bytes(pool, n_rows);
     hipError_t e = hipSuccess;
     const int32_t* gemm_perm = nullptr;   // SGMV: the GEMM visits rows grouped by adapter
+    size_t end = after_t;                  // end of this mode's layout; the GEMM's split partials follow
     if (m == LORA_MODE_BGMV) {
         BgmvShrinkPlan plan = plan_bgmv_shrink(P, eb, n_rows);
         e = launch_bgmv_shrink(P, pool->dtype, x, ldx, ids, n_rows, t, ldt, plan, stream, t_ext, lde);
@@ -165,6 +166,7 @@ hipError_t run_fused(const lora_pool_s* pool, lora_mode_t m, const void* x, int6
         const lora_segments_t* sg = seg;
         const SegLayout SL = seg_layout(after_t, n_rows, P.n_adapters);
         float* part = sgmv_shrink_part_bytes(P, n_rows) ? (float*)(base + SL.end) : nullptr;
+        end = SL.end + sgmv_shrink_part_bytes(P, n_rows);
         if (!sg) {
             SegLayout L = SL;
             own.perm = (int32_t*)(base + L.perm);
@@ -203,6 +205,10 @@ hipError_t run_fused(const lora_pool_s* pool, lora_mode_t m, const void* x, int6
     g.rows_distinct = (m == LORA_MODE_BGMV);
     g.perm = gemm_perm;
     g.x_rows = n_rows;
+    if (pool->dtype == LORA_BF16) {
+        g.split_bytes = layer_gemm_split_bytes(P, n_rows);
+        g.split_part = g.split_bytes ? (float*)(base + align_up(end, 256)) : nullptr;
+    }
     return launch_layer_gemm(P, pool->dtype, y_dtype, g, stream);
 }
 
@@ -528,9 +534,12 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
     if (!mode_ok(mode)) return LORA_E_INVALID;
     const lora_mode_t m = resolve_mode(mode, n_rows, pool->dev.n_adapters);
     size_t off = align_up((size_t)n_rows * t_stride(pool->dev.r_max) * 4, 256) + ext_bytes(pool, n_rows);
+    // the fused GEMM's K-split partial sums follow the layout of either mode
+    const size_t split = pool->dtype == LORA_BF16 ? layer_gemm_split_bytes(pool->dev, n_rows) : 0;
     if (m == LORA_MODE_BGMV) {
         // the W layout is not known here: room for the few-hundred-row path
         // (W stored [d_out, d_in]) and for the fused GEMM (either layout)
+        if (split) off = align_up(off, 256) + split;
         if (rows_ok(pool, n_rows)) off = std::max(off, rows_ws_bytes(pool, n_rows));
         if (decode_ok(pool, n_rows))
             off = std::max(off, decode_ws_bytes(pool->dev, n_rows, plan_decode(pool->dev, n_rows, true)));
@@ -538,6 +547,7 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
         if (pool->dev.n_adapters > kMaxAdaptersSegments) return LORA_E_UNSUPPORTED;
         off = seg_layout(off, n_rows, pool->dev.n_adapters).end;
         off += sgmv_shrink_part_bytes(pool->dev, n_rows);   // split-K partial sums of the shrink
+        if (split) off = align_up(off, 256) + split;
     }
     *bytes = std::max<size_t>(off, 256);
     return LORA_OK;

@@ -231,6 +231,9 @@ hipError_t launch_sgmv_shrink(const PoolDev& P, lora_dtype_t dt, const void* x, 
                               float* part = nullptr);
 int32_t sgmv_shrink_slices(const PoolDev& P, int32_t n_rows);
 size_t sgmv_shrink_part_bytes(const PoolDev& P, int32_t n_rows);
+// workspace for the K split of the layer GEMM's 128x128 launches (bf16 pool,
+// W stored [d_out, d_in]); 0 when no launch of this batch is split
+size_t layer_gemm_split_bytes(const PoolDev& P, int32_t n_rows);
 // t_ext from an existing t (rows with invalid ids or -1 are left alone)
 hipError_t launch_make_t_ext(const PoolDev& P, lora_dtype_t dt, const float* t, int64_t ldt,
                              const int32_t* ids, int32_t n_rows, void* t_ext, int64_t lde,
@@ -272,6 +275,10 @@ struct GemmArgs {
     // 4-bit W (stored [d_out, d_in], bf16 pool): W holds bytes, ldw bytes per
     // row; wscale [d_out][lds] fp32, one scale per output and 128 inputs
     bool w_q4 = false;
+    // room for the fp32 partial sums of a K split of the 128x128 launches
+    // (layer_gemm_split_bytes); null: no split
+    float* split_part = nullptr;
+    size_t split_bytes = 0;
     const float* wscale = nullptr;
     int64_t lds = 0;
 };

@@ -611,6 +611,13 @@ struct GemmDev {
     // inputs 128 g .. 128 g + 127 of output n is wscale[n * lds + g]
     const float* wscale;
     int64_t lds;
+    // split K (part non-null): workgroup b takes K slice b / (tiles_m *
+    // tiles_n) of kslice K-blocks and writes its fp32 partial product
+    // (base only) to part[slice][tile row][ldp]; a finish launch adds the
+    // slices and the adapter term
+    float* part;
+    int64_t ldp;
+    int32_t kslice;
 };
 
 // Eight signed 4-bit values (element e in bits 4e .. 4e+3) times `sc`, each
@@ -917,7 +924,12 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     // XCD-aware order: consecutive workgroups land on different XCDs, so give
     // each XCD a contiguous run of tiles, then raster in groups of 8 row-tiles.
     int b = blockIdx.x;
-    const int T_all = gridDim.x;
+    int ks = 0;
+    const int T_all = g.part ? g.tiles_m * g.tiles_n : (int)gridDim.x;
+    if (g.part) {
+        ks = b / T_all;
+        b -= ks * T_all;
+    }
     const int T8 = T_all & ~7;
     if (b < T8) b = (b & 7) * (T8 >> 3) + (b >> 3);
     constexpr int GM = 8;
@@ -1022,7 +1034,10 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
         if (tid == C::BM - 1) sNExt = before + nb;
         __syncthreads();
     }
-    const int nk = (K + C::BK - 1) / C::BK;
+    const int nk_all = (K + C::BK - 1) / C::BK;
+    // this workgroup's K-blocks (all of them without a K split)
+    const int kbeg = g.part ? ks * g.kslice : 0;
+    const int nk = g.part ? min(nk_all, kbeg + g.kslice) : nk_all;
     const int total = nk + sNExt;
 
     Acc<C> acc;
@@ -1069,7 +1084,7 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
     if constexpr (OUT_IN) {
         // whole K-blocks in a branch-free loop (both operands K-contiguous);
         // the last whole block and a ragged tail block after it
-        const int nkf = K / C::BK;
+        const int nkf = min(K / C::BK, nk);
         // buffer resources over the tile's rows (raw, 16-byte pieces); their
         // fields are workgroup-uniform, said so with readfirstlane so that the
         // loads take the descriptor from scalar registers directly
@@ -1112,7 +1127,7 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             __syncthreads();
             return sA;
         };
-        int kb = 0;
+        int kb = kbeg;
         if constexpr (C::NT <= 256 || (C::BM + C::BN) * C::BK * (int)sizeof(T) <= 64 * C::NT) {
             // registers to spare (4 waves, or at most 64 staged bytes a
             // thread): two blocks in flight, in two register sets used
@@ -1130,9 +1145,9 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
                 __syncthreads();
                 return sA;
             };
-            if (nkf >= 2) {
-                load_full(0);
-                load_full2(1);
+            if (nkf - kb >= 2) {
+                load_full(kb);
+                load_full2(kb + 1);
                 for (; kb + 3 < nkf; kb += 2) {
                     T* sA = step(kb);
                     load_full(kb + 2);
@@ -1150,12 +1165,12 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
                 mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
                 ++kb;
             } else {
-                if (nkf > 0) load_full(0);
-                else load_main(0);
+                if (kb < nkf) load_full(kb);
+                else load_main(kb);
             }
         } else {
-            if (nkf > 0) load_full(0);
-            else load_main(0);
+            if (kb < nkf) load_full(kb);
+            else load_main(kb);
             for (; kb + 1 < nkf; ++kb) {
                 T* sA = step(kb);
                 load_full(kb + 1);
@@ -1168,8 +1183,8 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
             mma_block<C>(acc, sA, sA + C::A_ELEMS, wm, wn, lane);
         }
     } else {
-        load_main(0);
-        for (int kb = 0; kb < nk; ++kb) {
+        load_main(kbeg);
+        for (int kb = kbeg; kb < nk; ++kb) {
             T* sA = smem + (kb & 1) * C::STAGE;
             T* sB = sA + C::A_ELEMS;
             la.store(sA, tid);
@@ -1196,6 +1211,23 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
         }
     }
 
+    if (g.part) {
+        // this K slice's fp32 partial product, by tile row, for the finish
+        float* pp = g.part + (int64_t)ks * g.n * g.ldp;
+        const int lcp = lane % C::BLK;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int col = n0 + wn * C::WTN + j * C::BLK + lcp;
+#pragma unroll
+                for (int q = 0; q < C::M::NACC; ++q) {
+                    const int m = m0 + wm * C::WTM + i * C::BLK + C::M::row(lane, q);
+                    if (m < g.n && col < N) pp[(int64_t)m * g.ldp + col] = acc.v[i][j][q];
+                }
+            }
+        return;
+    }
     if (gather) {
         __syncthreads();   // every wave is done with the LDS stages
         gather_epilogue<C, TY>(P, g, acc, (float*)smem, sRec, sRowA, n0, wm, wn, wave, lane);
@@ -1215,6 +1247,106 @@ __global__ __launch_bounds__(C::NT) void k_layer_gemm(PoolDev P, GemmDev g) {
                 if (row >= 0 && col < N) Y[(int64_t)row * g.ldy + col] = from_f32<TY>(acc.v[i][j][q]);
             }
         }
+}
+
+// Finish of a split-K launch: workgroup (tile row m, 256 columns), lane l
+// columns c .. c + 3:
+//     y[row] = sum over slices (in order) of part[slice][m] + s_a * t[row] B_a,
+// row = perm[m] (or m), a = ids[row], y rounded once.  The partial sums go
+// out first (they need nothing), then, once the row's adapter is known, its
+// t values (into LDS) and B rows; rank rows past r read row 0 again and meet
+// t = 0.
+struct SplitFinishArgs {
+    const float* part;      // [S][n][ldp]
+    int64_t ldp;
+    int32_t S;
+    int32_t n;
+    const int32_t* perm;    // tile row -> row, or null
+    const int32_t* ids;     // by row
+    const float* t;         // [row][ldt], unscaled x A
+    int64_t ldt;
+    void* y;
+    int64_t ldy;
+};
+constexpr int SF_SLICES = 8;   // K slices of a split launch at most
+constexpr int SF_RCHUNK = 16;  // rank rows of B requested together
+
+template <typename TY>
+__global__ __launch_bounds__(64) void k_gemm_split_finish(PoolDev P, SplitFinishArgs f) {
+    __shared__ float st[64];
+    const int lane = threadIdx.x;
+    const int N = P.d_out;
+    const int nch = (N + 255) / 256;
+    const int m = blockIdx.x / nch;
+    const int c0 = (blockIdx.x - m * nch) * 256 + lane * 4;
+    const bool in = c0 < N;
+    const int cc = in ? c0 : 0;   // columns past d_out read column 0 and are not stored
+    const bool vec = (N & 3) == 0;
+    float4 u[SF_SLICES];
+#pragma unroll
+    for (int q = 0; q < SF_SLICES; ++q) {
+        const float* pp = f.part + ((int64_t)(q < f.S ? q : 0) * f.n + m) * f.ldp + cc;
+        if (vec) {
+            u[q] = *(const float4*)pp;
+        } else {
+            u[q].x = pp[0];
+            u[q].y = cc + 1 < N ? pp[1] : 0.f;
+            u[q].z = cc + 2 < N ? pp[2] : 0.f;
+            u[q].w = cc + 3 < N ? pp[3] : 0.f;
+        }
+    }
+    const int row = f.perm ? f.perm[m] : m;
+    const int a = f.ids[row];
+    const bool ok = id_ok(a, P.n_adapters);
+    const int r = ok ? uload(P.ranks, a) : 0;
+    const int64_t boff = ok ? uload(P.b_off, a) : 0;
+    const float sc = ok ? uload(P.scales, a) : 0.f;
+    if (lane < r) st[lane] = f.t[(int64_t)row * f.ldt + lane];
+    const bf16* Bu = (const bf16*)P.B + boff + cc;
+    const bool vb = P.vec_b != 0;
+    uint2 bv[SF_RCHUNK];
+    auto load_b = [&](int j0) {
+#pragma unroll
+        for (int q = 0; q < SF_RCHUNK; ++q) {
+            const int j = j0 + q;
+            if (vb) {
+                bv[q] = *(const uint2*)(Bu + (int64_t)(j < r ? j : 0) * N);
+            } else {
+                union { uint2 u; bf16 e[4]; } w;
+                for (int e = 0; e < 4; ++e) w.e[e] = (j < r && cc + e < N) ? Bu[(int64_t)j * N + e] : (bf16)0;
+                bv[q] = w.u;
+            }
+        }
+    };
+    if (r > 0) load_b(0);
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < SF_SLICES; ++q)
+        if (q < f.S) {
+            v[0] += u[q].x; v[1] += u[q].y; v[2] += u[q].z; v[3] += u[q].w;
+        }
+    __syncthreads();
+    if (!in) return;
+    if (r > 0) {
+        float e4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j0 = 0;;) {
+#pragma unroll
+            for (int q = 0; q < SF_RCHUNK; ++q) {
+                const float tj = (j0 + q < r) ? st[j0 + q] : 0.f;
+                union { uint2 u; bf16 e[4]; } w;
+                w.u = bv[q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) e4[e] += tj * to_f32(w.e[e]);
+            }
+            j0 += SF_RCHUNK;
+            if (j0 >= r) break;
+            load_b(j0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += sc * e4[e];
+    }
+    const bool vec_y = ((f.ldy * (int64_t)sizeof(TY)) & 15) == 0 && ((uintptr_t)f.y & 15) == 0;
+    store_row_piece<TY, 4>((TY*)f.y + (int64_t)row * f.ldy + c0, v, N - c0, vec_y);
 }
 
 // ---------------------------------------------------------------------------
@@ -2456,10 +2588,16 @@ using GemmF32 = Cfg<float, 64, 64, 32, 2, 2>;
 using ShrinkB = Cfg<bf16, 64, 64, 64, 4, 1>;
 using ShrinkF = Cfg<float, 64, 64, 32, 4, 1>;
 
+// part non-null: a K split into S slices of kslice K-blocks, base product
+// only, fp32 partial sums into part (see GemmDev)
 template <class C, typename TY, bool Q4 = false>
-hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
+hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream, float* part = nullptr,
+                    int64_t ldp = 0, int S = 1, int kslice = 0) {
     static_assert(!Q4 || sizeof(typename C::T) == 2, "4-bit W with bf16 tiles");
     GemmDev g;
+    g.part = part;
+    g.ldp = ldp;
+    g.kslice = kslice;
     g.x = a.x;
     g.ldx = a.ldx;
     g.W = a.W;
@@ -2478,7 +2616,11 @@ hipError_t run_gemm(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
     g.x_rows = a.x_rows > 0 ? a.x_rows : a.n_rows;
     g.wscale = a.wscale;
     g.lds = a.lds;
-    dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n));
+    if (part) {   // the base product alone; the finish adds the adapter term
+        g.t = nullptr;
+        g.t_ext = nullptr;
+    }
+    dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n * (part ? S : 1)));
     if constexpr (Q4) {
         hipLaunchKernelGGL((k_layer_gemm<C, TY, true, true>), grid, dim3(C::NT), 0, stream, P, g);
     } else if (a.w_out_in) {
@@ -2538,6 +2680,82 @@ GemmArgs rows_from(const GemmArgs& a, int32_t r0) {
     return b;
 }
 
+// K slices for a 128x128 launch of n_rows rows (1: no split).  With fewer
+// tiles than CUs and a long K, each workgroup walks all of K one block at a
+// time, about a microsecond a block whatever the tile size (the 2,218-row
+// mixed batch: its k and v projections and the rows past the 256x256 rounds
+// took 130-400 us each).  The split takes the slice count that minimises
+// (rounds of one workgroup per CU) x (K-blocks per slice), plus two blocks'
+// worth per slice for the partial sums, each slice at least 16 blocks deep.
+int gemm_big_slices(const PoolDev& P, int32_t n_rows) {
+    const int64_t T = ceil_div(n_rows, GemmBig::BM) * ceil_div(P.d_out, GemmBig::BN);
+    const int64_t nk = ceil_div(P.d_in, GemmBig::BK);
+    if (T >= 256 || nk < 32) return 1;
+    int best = 1;
+    int64_t best_cost = ceil_div(T, 256) * nk;
+    for (int S = 2; S <= SF_SLICES && nk / S >= 16; ++S) {
+        const int64_t cost = ceil_div(T * S, 256) * ceil_div(nk, S) + 2 * S;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = S;
+        }
+    }
+    return best;
+}
+
+size_t gemm_big_split_bytes(const PoolDev& P, int32_t n_rows) {
+    const int S = gemm_big_slices(P, n_rows);
+    return S > 1 ? align_up((size_t)S * n_rows * align_up((size_t)P.d_out, 4) * 4, 256) : 0;
+}
+
+// Rows of the 256x256 launch when the rows past its whole rounds take a
+// second launch (0: one launch)
+int32_t huge_head_rows(const PoolDev& P, int32_t n_rows) {
+    auto tiles = [&](int bm, int bn) { return ceil_div(n_rows, bm) * ceil_div(P.d_out, bn); };
+    const int64_t th = tiles(GemmHuge::BM, GemmHuge::BN);
+    const int64_t tn = ceil_div(P.d_out, GemmHuge::BN);
+    const int64_t tm_h = (th / 256) * 256 / tn;
+    const int32_t r0 = (int32_t)(tm_h * GemmHuge::BM);
+    if (tm_h > 0 && r0 < n_rows) {
+        const double rounds = (double)ceil_div(th, 256);
+        const double rounds_h = (double)ceil_div(tm_h * tn, 256);
+        const double tail_rounds =
+            0.35 * (double)ceil_div(ceil_div(n_rows - r0, GemmBig::BM) * ceil_div(P.d_out, GemmBig::BN), 256);
+        if (rounds_h + tail_rounds < rounds - 0.25) return r0;
+    }
+    return 0;
+}
+
+// 128x128 tiles, K split when gemm_big_slices says so and the caller gave
+// room for the partial sums (W stored [d_out, d_in], bf16 W): the split
+// launch computes x W alone, the finish adds the slices and s t B_a
+template <typename TY>
+hipError_t run_gemm_big(const PoolDev& P, const GemmArgs& a, hipStream_t stream) {
+    const int S = (a.split_part && a.w_out_in && !a.w_q4 && a.t) ? gemm_big_slices(P, a.n_rows) : 1;
+    if (S < 2 || gemm_big_split_bytes(P, a.n_rows) > a.split_bytes) return run_gemm<GemmBig, TY>(P, a, stream);
+    const int nk = (int)ceil_div(P.d_in, GemmBig::BK);
+    const int kslice = (nk + S - 1) / S;
+    const int Sr = (nk + kslice - 1) / kslice;   // every slice non-empty
+    const int64_t ldp = (int64_t)align_up((size_t)P.d_out, 4);
+    hipError_t e = run_gemm<GemmBig, TY>(P, a, stream, a.split_part, ldp, Sr, kslice);
+    if (e != hipSuccess) return e;
+    SplitFinishArgs f;
+    f.part = a.split_part;
+    f.ldp = ldp;
+    f.S = Sr;
+    f.n = a.n_rows;
+    f.perm = a.perm;
+    f.ids = a.ids;
+    f.t = a.t;
+    f.ldt = a.ldt;
+    f.y = a.y;
+    f.ldy = a.ldy;
+    const int nch = (int)ceil_div(P.d_out, 256);
+    hipLaunchKernelGGL(k_gemm_split_finish<TY>, dim3((unsigned)((int64_t)a.n_rows * nch)), dim3(64), 0, stream, P,
+                       f);
+    return hipGetLastError();
+}
+
 template <typename TY>
 hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream, bool tail = false) {
     if (a.w_q4) {
@@ -2573,27 +2791,19 @@ hipError_t run_gemm_bf16(const PoolDev& P, const GemmArgs& a, hipStream_t stream
         // round would be mostly idle, the row tiles that fill whole rounds
         // take the 256x256 launch and the remaining rows a launch of 128x128
         // tiles (a quarter of the work each).
-        const int64_t tn = ceil_div(P.d_out, GemmHuge::BN);
-        const int64_t tm_h = (th / 256) * 256 / tn;
-        const int32_t r0 = (int32_t)(tm_h * GemmHuge::BM);
-        if (tm_h > 0 && r0 < a.n_rows) {
-            const double rounds = (double)ceil_div(th, 256);
-            const double rounds_h = (double)ceil_div(tm_h * tn, 256);
-            const double tail_rounds =
-                0.35 * (double)ceil_div(ceil_div(a.n_rows - r0, GemmBig::BM) * ceil_div(P.d_out, GemmBig::BN), 256);
-            if (rounds_h + tail_rounds < rounds - 0.25) {
-                GemmArgs h = a;
-                h.n_rows = r0;
-                const hipError_t e = run_gemm<GemmHuge, TY>(P, h, stream);
-                if (e != hipSuccess) return e;
-                return run_gemm_bf16<TY>(P, rows_from<TY>(a, r0), stream, true);
-            }
+        const int32_t r0 = huge_head_rows(P, a.n_rows);
+        if (r0 > 0) {
+            GemmArgs h = a;
+            h.n_rows = r0;
+            const hipError_t e = run_gemm<GemmHuge, TY>(P, h, stream);
+            if (e != hipSuccess) return e;
+            return run_gemm_bf16<TY>(P, rows_from<TY>(a, r0), stream, true);
         }
         return run_gemm<GemmHuge, TY>(P, a, stream);
     }
     // 128x128 tiles from 96 of them: fewer workgroups than CUs, but a
     // 128x128 tile moves half the x and W bytes per flop of a 64x64 tile
-    if (tiles(GemmBig::BM, GemmBig::BN) >= (tail ? 64 : 96)) return run_gemm<GemmBig, TY>(P, a, stream);
+    if (tiles(GemmBig::BM, GemmBig::BN) >= (tail ? 64 : 96)) return run_gemm_big<TY>(P, a, stream);
     if (a.w_out_in && (!a.t_ext || (a.t && a.rows_distinct))) return run_gemm<GemmMed, TY>(P, a, stream);
     if (tiles(GemmMid::BM, GemmMid::BN) >= 128 || a.n_rows > 32) return run_gemm<GemmMid, TY>(P, a, stream);
     return run_gemm<GemmSmall, TY>(P, a, stream);
@@ -2606,6 +2816,21 @@ hipError_t launch_layer_gemm(const PoolDev& P, lora_dtype_t dt, lora_dtype_t ydt
     if (dt == LORA_BF16)
         return ydt == LORA_BF16 ? run_gemm_bf16<bf16>(P, a, stream) : run_gemm_bf16<float>(P, a, stream);
     return ydt == LORA_BF16 ? run_gemm<GemmF32, bf16>(P, a, stream) : run_gemm<GemmF32, float>(P, a, stream);
+}
+
+size_t layer_gemm_split_bytes(const PoolDev& P, int32_t n_rows) {
+    // the 128x128 launch that run_gemm_bf16 may split: all rows, or the rows
+    // past the 256x256 rounds
+    if (n_rows <= 0) return 0;
+    auto tiles = [&](int32_t rows, int bm, int bn) { return ceil_div(rows, bm) * ceil_div(P.d_out, bn); };
+    if (tiles(n_rows, GemmHuge::BM, GemmHuge::BN) >= 200) {
+        const int32_t r0 = huge_head_rows(P, n_rows);
+        if (r0 <= 0) return 0;
+        const int32_t rest = n_rows - r0;
+        if (tiles(rest, GemmHuge::BM, GemmHuge::BN) >= 200) return 0;
+        return tiles(rest, GemmBig::BM, GemmBig::BN) >= 64 ? gemm_big_split_bytes(P, rest) : 0;
+    }
+    return tiles(n_rows, GemmBig::BM, GemmBig::BN) >= 96 ? gemm_big_split_bytes(P, n_rows) : 0;
 }
 
 static int64_t seg_tiles(int32_t n_rows, int32_t n_bins, int bm) {

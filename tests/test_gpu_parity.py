@@ -610,6 +610,57 @@ def test_rows_path(case):
     assert torch.equal(y, y2), "run-to-run bits"
 
 
+# The fused layer's 128x128 launches with few tiles and a long K run split K
+# (fp32 partial sums, then a finish that adds them and s t B_a): all rows of
+# a 1,536-row batch (1,024 x 2,048 -> 1,024 columns, two slices), and the 170
+# rows past the 256x256 rounds of a 2,218-row batch (8,192 columns, two slices),
+# in SGMV (rows visited grouped by adapter) and BGMV order, against the oracle.
+SPLIT_CASES = [
+    # n_rows, d_in, d_out, rows checked: "all" or "tail" (past the 256x256 rounds)
+    (1536, 2048, 1024, "all"),
+    (2218, 2048, 8192, "tail"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}" for c in SPLIT_CASES])
+def test_layer_split_k_launches(case):
+    n, d_in, d_out, which = case
+    say(f"split-K layer launches: {n} x {d_in} -> {d_out}, rows {which}")
+    b = binding()
+    rng = np.random.default_rng(n + d_out)
+    n_ad = 12
+    w = wl.small_batch(seed=n, n_rows=n, device=DEV, dtype=torch.bfloat16, d_in=d_in, d_out=d_out,
+                       n_adapters=n_ad, layout=wl.RAGGED, ranks=RAGGED_RANKS, frac_base=0.0,
+                       scale=np.linspace(-2.0, 2.0, n_ad).astype(np.float32))
+    w = wl.Workload(w.name, w.dtype, _rows_ids("runs", n, n_ad, rng), w.projections)
+    p = w.projections[0]
+    pool = pool_of(p.pool)
+    ids = ids_dev(w)
+    Ws = w_stored(p.W, b.LORA_W_OUT_IN)
+    seg = b.lora_segments_build(ids, n_ad)
+    torch.cuda.synchronize()
+    if which == "all":
+        rows = np.arange(n)
+        cols = None
+    else:
+        # rows in the order each mode visits them: SGMV by segments, BGMV as given
+        perm = seg.perm[:n].cpu().numpy()
+        tail_sgmv = perm[2048:]
+        tail_bgmv = np.arange(2048, n)
+        rows = np.unique(np.concatenate([tail_sgmv, tail_bgmv, rng.choice(2048, 16, replace=False)]))
+        cols = sorted(set(rng.choice(d_out, 160, replace=False).tolist()) | {0, d_out - 1})
+    o = run_oracle(w, rows=rows.tolist(), cols=cols, threads=0)
+    for mode in (b.LORA_MODE_SGMV, b.LORA_MODE_BGMV):
+        for ydt in (torch.bfloat16, torch.float32):
+            y = b.lora_layer_apply(pool, p.x, Ws, ids, w_layout=b.LORA_W_OUT_IN, mode=mode, y_dtype=ydt,
+                                   seg=seg if mode == b.LORA_MODE_SGMV else None)
+            torch.cuda.synchronize()
+            ys = y[torch.as_tensor(rows, device=y.device)]
+            if cols is not None:
+                ys = ys[:, cols]
+            assert_close(ys, o["y"], TOL[torch.bfloat16], f"y mode {mode} {ydt}")
+
+
 def test_rows_path_invalid_ids():
     say("few-hundred-row path: invalid ids flagged and run as base-only rows")
     b = binding()
