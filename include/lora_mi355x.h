@@ -264,7 +264,10 @@ lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t
  *    Segments are built in the workspace unless `seg` is given.
  *   x [n_rows, ldx]; W per w_layout with leading dimension ldw; y [n_rows,
  *   ldy] of y_dtype.  `seg` may be NULL (SGMV builds segments in the
- *   workspace) or a descriptor already built for these ids.
+ *   workspace) or a descriptor already built for these ids by
+ *   lora_segments_build; any other content is undefined behaviour (the
+ *   kernels gather x and scatter t and y through perm, and not every kernel
+ *   checks its entries).
  *   mode AUTO picks BGMV when n_rows <= 64 or n_rows <= 2 * n_adapters
  *   (segments would mostly hold one or two rows) and SGMV otherwise. */
 lora_status_t lora_layer_apply(lora_pool_t pool, const void* x, int64_t ldx,

@@ -1262,6 +1262,7 @@ struct SplitFinishArgs {
     int32_t S;
     int32_t n;
     const int32_t* perm;    // tile row -> row, or null
+    int32_t x_rows;         // rows of ids, t and y; a perm entry outside them skips the tile row
     const int32_t* ids;     // by row
     const float* t;         // [row][ldt], unscaled x A
     int64_t ldt;
@@ -1296,6 +1297,7 @@ __global__ __launch_bounds__(64) void k_gemm_split_finish(PoolDev P, SplitFinish
         }
     }
     const int row = f.perm ? f.perm[m] : m;
+    if (row < 0 || row >= f.x_rows) return;   // the GEMM skipped it too (whole workgroup, before the barrier)
     const int a = f.ids[row];
     const bool ok = id_ok(a, P.n_adapters);
     const int r = ok ? uload(P.ranks, a) : 0;
@@ -2745,6 +2747,7 @@ hipError_t run_gemm_big(const PoolDev& P, const GemmArgs& a, hipStream_t stream)
     f.S = Sr;
     f.n = a.n_rows;
     f.perm = a.perm;
+    f.x_rows = a.x_rows > 0 ? a.x_rows : a.n_rows;
     f.ids = a.ids;
     f.t = a.t;
     f.ldt = a.ldt;
