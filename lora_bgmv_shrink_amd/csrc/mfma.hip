@@ -118,6 +118,10 @@ __device__ __forceinline__ void mma_block(Acc<C>& acc, const typename C::T* sA,
     const T* pa = sA + (wm * C::WTM + lr) * C::LDK + kq;
     const T* pb = sB + (wn * C::WTN + lr) * C::LDK + kq;
     typename M::frag a[NA][C::FM], b[2][C::FN];
+    // the wave in its MFMA block issues ahead of a wave of the same SIMD that
+    // is loading or storing the next block (prefill and mixed batches 0.4-1.5%
+    // faster)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) a[0][i] = M::ld(pa + i * C::BLK * C::LDK);
 #pragma unroll
@@ -153,6 +157,7 @@ __device__ __forceinline__ void mma_block(Acc<C>& acc, const typename C::T* sA,
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // K-contiguous rows -> LDS [row][k].  sRow[r] is the source row or -1.
