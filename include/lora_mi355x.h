@@ -240,7 +240,10 @@ lora_status_t lora_sgmv_expand(lora_pool_t pool, const float* t, int64_t ldt,
 /* Workspace bytes for lora_layer_apply.  The W layout is not an argument,
  * so for BGMV batches of 65..1024 rows of a bf16 pool the size covers the
  * few-hundred-row form (W stored [d_out, d_in]): segments, fp32 base
- * partials (S * n_rows * d_out * 4 bytes, S <= 8 K slices) and t partials. */
+ * partials (S * n_rows * d_out * 4 bytes, S <= 8 K slices) and t partials.
+ * For a bf16 pool it also covers the fp32 K-slice partials of a tiled GEMM
+ * launch that splits K (a 128x128 launch of few tiles over a long K, W
+ * stored [d_out, d_in]), whatever the W layout and y dtype of the call. */
 lora_status_t lora_layer_workspace(lora_pool_t pool, int32_t n_rows, lora_mode_t mode,
                                    size_t* bytes);
 
